@@ -1,0 +1,207 @@
+/*
+ * mm_ssd.h -- C ABI of the Matryoshka-sliced selective-scan library
+ * (libmmssd.so, HIP kernels for gfx950 / MI355X).
+ *
+ * What it computes.  The hot path of the MatMamba block ("MatMamba: A
+ * Matryoshka State Space Model", the paragraph that splits the Mamba2 block
+ * into an input projection, a causal 1-D convolution of kernel size 4 over the
+ * concatenated x, B and C streams, a chunk + selective scan (SSM) with
+ * learnable per-head A and D, and an output projection):
+ *   - the causal depthwise conv1d (kernel 4) with SiLU over [x | B | C];
+ *   - the selective scan over the first h_i heads of a nested sub-block
+ *         H_t = exp(dt_t*A_h) * H_{t-1} + dt_t * x_t (outer) B_t   (d_head x d_state)
+ *         y_t = H_t . C_t + D_h * x_t
+ *     (the block's display equations did not survive on that page; this is
+ *     the Mamba2 reading, with one real scalar A_h and D_h per head and
+ *     Euler-discretised input; the Mamba page's Sampling Rule states that the
+ *     state is updated with input-dependent discretised parameters);
+ *   - the single-token recurrent decode step (Mamba page, Strengths:
+ *     linear-time recurrent inference without a KV cache).
+ * Matryoshka slicing ("MatMamba", nesting paragraph): a sub-block M_i with
+ * width m_i uses d_i = e*m_i inner channels and h_i = d_i/d_head heads, i.e.
+ * the prefixes W[0:d_i] and A[0:h_i] of the full block's parameters; B and C
+ * are d_state-sized, shared by all heads and never sliced.
+ *
+ * Conventions shared by every entry point.
+ *   - Pointers are device pointers unless stated; sizes are element counts.
+ *   - Rows are tokens (or sequences, for decode): row index = b*seqlen + t.
+ *     A row stride (in elements) lets the caller pass a view into a wider
+ *     buffer, e.g. the x, B and C column ranges of the conv output; only the
+ *     active prefix of each row is read or written, so nothing is copied to
+ *     run a slice.  Unit stride inside a row.
+ *   - Alignment: every row start must be 16-byte aligned (base pointer and
+ *     row stride), except dt, which is read element-wise.
+ *   - dtype (MM_F32 or MM_BF16) is the storage type of the token streams
+ *     (x, dt, B, C, y, conv input/output).  A, D, conv weights and every state
+ *     are fp32.  All arithmetic is fp32; bf16 stores round to nearest even.
+ *   - Ownership: the caller owns every buffer.  The library allocates no
+ *     memory, keeps no pointer after returning and holds no mutable global
+ *     state; scratch memory comes in through `workspace`.  Calls are
+ *     asynchronous on `stream` (a hipStream_t; NULL = the null stream); buffers
+ *     must stay valid until the stream has passed the call.  No entry point
+ *     synchronises the host, so calls may be captured into a HIP graph.
+ *   - Errors: every entry point returns MM_OK (0) or a negative MM_ERR_* code.
+ *     All host-checkable preconditions are checked before anything is
+ *     enqueued, so a failing call has no side effects.  No C++ exception
+ *     crosses this boundary.  mm_status_string() names a code.
+ *   - Concurrent calls on different streams must not write the same buffers.
+ */
+#ifndef MM_SSD_H
+#define MM_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MM_ABI_VERSION 1
+
+enum mm_status {
+  MM_OK = 0,
+  MM_ERR_NULL = -1,        /* a required pointer is NULL */
+  MM_ERR_SHAPE = -2,       /* a size or stride is out of range or inconsistent */
+  MM_ERR_SLICE = -3,       /* Matryoshka width/heads invalid (no integer head count, or out of range) */
+  MM_ERR_DTYPE = -4,       /* unknown dtype code */
+  MM_ERR_UNSUPPORTED = -5, /* valid request this build does not implement (e.g. ngroups != 1) */
+  MM_ERR_ALIGN = -6,       /* a row start is not 16-byte aligned */
+  MM_ERR_WORKSPACE = -7,   /* workspace missing or smaller than the size query returned */
+  MM_ERR_HIP = -8          /* the HIP runtime reported an error (launch failure) */
+};
+
+enum mm_dtype { MM_F32 = 0, MM_BF16 = 1 };
+
+/* Version of this ABI (MM_ABI_VERSION). */
+int mm_abi_version(void);
+
+/* Static, NUL-terminated name of a status code; never NULL. */
+const char* mm_status_string(int status);
+
+/*
+ * Matryoshka slice resolution ("MatMamba", nesting and Mix'n'Match
+ * paragraphs): e = d_inner/d_model, d_i = e*m, h = d_i/d_head.
+ * Errors: MM_ERR_NULL if heads_out is NULL; MM_ERR_SHAPE if a dimension is
+ * not positive or d_inner is not a multiple of d_model; MM_ERR_SLICE unless
+ * 0 < m <= d_model and d_i is a multiple of d_head.  Host only.
+ */
+int mm_heads_for_dim(int64_t d_model, int64_t d_inner, int64_t d_head,
+                     int64_t m, int64_t* heads_out);
+
+/*
+ * Causal depthwise conv1d, kernel 4, then SiLU, over the concatenated
+ * [x | B | C] channels ("MatMamba", block paragraph: conv weights are the
+ * concatenation W_conv_x, W_conv_B, W_conv_C; sigma = SiLU).  For every active
+ * channel c and token t:
+ *     out[t,c] = SiLU(bias[c] + sum_{k=0..3} w[c*4+k] * in[t-3+k, c])
+ * with in[tau<0, c] taken from conv_state (or 0 when conv_state is NULL).
+ *
+ *   xbc_in   (batch*seqlen rows, in_row_stride) dtype; channels
+ *            [0, d_inner) = x, then ngroups*d_state B, then ngroups*d_state C.
+ *   xbc_out  (batch*seqlen rows, out_row_stride) dtype, same channel layout;
+ *            must not overlap xbc_in.  Inactive channels are not written.
+ *   w        (conv_dim, 4) fp32, conv_dim = d_inner + 2*ngroups*d_state;
+ *            tap 3 multiplies the current token.
+ *   bias     (conv_dim) fp32, or NULL for none.
+ *   conv_state (batch, 3, conv_dim) fp32 or NULL: state[b][k][c] is the input
+ *            3-k tokens before the first token (k=0 oldest).  Read as history,
+ *            then overwritten in place with the last three inputs of the
+ *            sequence (active channels only).
+ *   Active channels of sequence b: c < h_b*d_head (the x slice, W_conv_x[0:d_i])
+ *   and every B/C channel; h_b = n_heads_active, or, when heads_active_per_seq
+ *   (device int32, batch entries) is given, min(heads_active_per_seq[b],
+ *   n_heads_active) clamped at 0.
+ * Preconditions: 1 <= batch <= 65535, seqlen >= 1; d_inner = n_heads*d_head
+ * for some n_heads >= 1; 1 <= n_heads_active <= n_heads; ngroups >= 1;
+ * d_head, d_state multiples of 8; row strides >= conv_dim; w 16-byte aligned.
+ */
+int mm_conv1d_silu(const void* xbc_in, int64_t in_row_stride,
+                   void* xbc_out, int64_t out_row_stride,
+                   const float* w, const float* bias, float* conv_state,
+                   int64_t batch, int64_t seqlen, int64_t d_inner,
+                   int64_t d_head, int64_t d_state, int64_t ngroups,
+                   int64_t n_heads_active, const int32_t* heads_active_per_seq,
+                   int dtype, void* stream);
+
+/*
+ * Bytes of device workspace mm_ssd_forward needs for these sizes (may be 0).
+ * Same argument meaning and errors as mm_ssd_forward.  Host only.
+ */
+int mm_ssd_forward_workspace_size(int64_t batch, int64_t seqlen,
+                                  int64_t n_heads, int64_t d_head,
+                                  int64_t d_state, int64_t ngroups,
+                                  int64_t n_heads_active, int64_t chunk,
+                                  int dtype, size_t* bytes_out);
+
+/*
+ * Chunked selective scan (SSD) over heads [0, n_heads_active) ("MatMamba",
+ * block paragraph: chunk + selective scan; nesting paragraph: A[0:h_i]).
+ * The sequence is cut into chunks of `chunk` tokens (the last may be
+ * shorter); inside a chunk the output is the masked, decayed quadratic form
+ * (C B^T o L) (dt x) plus the decayed contribution of the state entering the
+ * chunk; states are passed from chunk to chunk.  The result equals the
+ * token-by-token recurrence up to rounding and does not depend on `chunk`.
+ *
+ *   x   (batch*seqlen rows, x_row_stride) dtype: row = n_heads*d_head values,
+ *       head-major; the first n_heads_active*d_head are read.
+ *   dt  (rows, dt_row_stride) dtype: per-head step size after any bias and
+ *       softplus (> 0); the first n_heads_active entries are read.
+ *   A   (n_heads) fp32, D (n_heads) fp32 or NULL (= 0); prefixes read.
+ *   B, C (rows, b_row_stride / c_row_stride) dtype: ngroups*d_state values.
+ *   y   (rows, y_row_stride) dtype: the first n_heads_active*d_head values of
+ *       each row are written; the rest of the row is untouched.
+ *   initial_state (batch, n_heads, d_head, d_state) fp32 or NULL (= 0).
+ *   final_state   same layout or NULL; active heads written.  It may alias
+ *       initial_state (state chaining in place).
+ *   chunk: 16, 32, 64, 128 or 256.
+ *   workspace: device memory of at least mm_ssd_forward_workspace_size()
+ *       bytes (may be NULL if that is 0), not used concurrently by another call.
+ * Preconditions: 1 <= batch <= 65535, seqlen >= 1, n_heads <= 65535;
+ * 1 <= n_heads_active <= n_heads; ngroups == 1 (MM_ERR_UNSUPPORTED otherwise); (d_head, d_state) one of
+ * (32,16), (64,64), (64,128); strides >= the row lengths above; with MM_F32
+ * storage, chunk <= 128 when d_state = 128.
+ */
+int mm_ssd_forward(const void* x, int64_t x_row_stride,
+                   const void* dt, int64_t dt_row_stride,
+                   const float* A,
+                   const void* B, int64_t b_row_stride,
+                   const void* C, int64_t c_row_stride,
+                   const float* D,
+                   void* y, int64_t y_row_stride,
+                   const float* initial_state, float* final_state,
+                   int64_t batch, int64_t seqlen, int64_t n_heads,
+                   int64_t d_head, int64_t d_state, int64_t ngroups,
+                   int64_t n_heads_active, int64_t chunk, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode token for every sequence of the batch (Mamba page, Strengths:
+ * linear-time recurrent inference), in place on `state`, for heads
+ * [0, h_b) of sequence b (h_b as in mm_conv1d_silu):
+ *     H <- exp(dt*A_h) * H + dt * x_t (outer) B_t ;  y_t = H . C_t + D_h * x_t
+ *   state (batch, n_heads, d_head, d_state) fp32, read and written.
+ *   x_t (batch rows, x_row_stride) dtype: n_heads*d_head values per row.
+ *   dt_t (batch rows, dt_row_stride) dtype: n_heads values (post-softplus).
+ *   B_t, C_t (batch rows, b_row_stride / c_row_stride) dtype: ngroups*d_state.
+ *   A, D: as in mm_ssd_forward.  y_t (batch rows, y_row_stride) dtype.
+ * Inactive heads' state and y_t are untouched.  Preconditions:
+ * 1 <= batch <= 65535; 1 <= n_heads_active <= n_heads; ngroups == 1;
+ * d_state one of 16, 32, 64, 128, 256; d_head >= 1; state 16-byte aligned.
+ */
+int mm_ssd_step(float* state,
+                const void* x_t, int64_t x_row_stride,
+                const void* dt_t, int64_t dt_row_stride,
+                const float* A,
+                const void* B_t, int64_t b_row_stride,
+                const void* C_t, int64_t c_row_stride,
+                const float* D,
+                void* y_t, int64_t y_row_stride,
+                int64_t batch, int64_t n_heads, int64_t d_head,
+                int64_t d_state, int64_t ngroups, int64_t n_heads_active,
+                const int32_t* heads_active_per_seq, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MM_SSD_H */

@@ -1,0 +1,265 @@
+"""Python binding of libmmssd.so (C ABI in include/mm_ssd.h).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, passes their data pointers, row strides and the current HIP
+stream to the C entry point of the same name, and raises on a non-zero
+status.  Outputs and the workspace are allocated with torch (device memory is
+plumbing here); every step of the computation runs in the HIP kernels.
+
+There is no fallback: if the shared library is missing the call raises.
+Build it with ``python -m selective_state_space_12_amd._build`` (or
+``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmmssd.so")
+
+MM_OK = 0
+MM_F32 = 0
+MM_BF16 = 1
+STATUS = {
+    0: "MM_OK", -1: "MM_ERR_NULL", -2: "MM_ERR_SHAPE", -3: "MM_ERR_SLICE",
+    -4: "MM_ERR_DTYPE", -5: "MM_ERR_UNSUPPORTED", -6: "MM_ERR_ALIGN",
+    -7: "MM_ERR_WORKSPACE", -8: "MM_ERR_HIP",
+}
+
+_lock = threading.Lock()
+_lib = None
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_int = ctypes.c_int
+
+
+class MMError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmmssd.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with "
+                    "`python -m selective_state_space_12_amd._build`")
+            L = ctypes.CDLL(LIB_PATH)
+            L.mm_abi_version.argtypes = []
+            L.mm_abi_version.restype = _int
+            L.mm_status_string.argtypes = [_int]
+            L.mm_status_string.restype = ctypes.c_char_p
+            L.mm_heads_for_dim.argtypes = [_i64, _i64, _i64, _i64, ctypes.POINTER(_i64)]
+            L.mm_heads_for_dim.restype = _int
+            L.mm_conv1d_silu.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i64,
+                                         _i64, _i64, _i64, _i64, _i64, _vp, _int, _vp]
+            L.mm_conv1d_silu.restype = _int
+            L.mm_ssd_forward_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64,
+                                                        _i64, _i64, _int,
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+            L.mm_ssd_forward_workspace_size.restype = _int
+            L.mm_ssd_forward.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
+                                         _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                         _i64, _i64, _i64, _int, _vp, ctypes.c_size_t, _vp]
+            L.mm_ssd_forward.restype = _int
+            L.mm_ssd_step.argtypes = [_vp, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64,
+                                      _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                      _vp, _int, _vp]
+            L.mm_ssd_step.restype = _int
+            _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MM_OK:
+        msg = lib().mm_status_string(status).decode()
+        raise MMError(fn, status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MM_F32
+    if t.dtype == torch.bfloat16:
+        return MM_BF16
+    raise TypeError(f"unsupported storage dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _row_stride(t: torch.Tensor, name: str, inner: Tuple[int, ...]) -> int:
+    """Token-row stride of a (batch, seqlen, *inner) view whose inner block is
+    contiguous and whose batches are seqlen rows apart."""
+    if t.dim() != 2 + len(inner) or tuple(t.shape[2:]) != tuple(inner):
+        raise ValueError(f"{name}: expected shape (batch, seqlen, {inner}), got {tuple(t.shape)}")
+    expect = 1
+    for d in range(t.dim() - 1, 1, -1):
+        if t.shape[d] > 1 and t.stride(d) != expect:
+            raise ValueError(f"{name}: inner dimensions must be contiguous")
+        expect *= t.shape[d]
+    rs = t.stride(1) if t.shape[1] > 1 else (t.stride(0) if t.shape[0] > 1 else expect)
+    if t.shape[0] > 1 and t.shape[1] > 1 and t.stride(0) != t.shape[1] * t.stride(1):
+        raise ValueError(f"{name}: batches must be seqlen rows apart")
+    return rs
+
+
+def abi_version() -> int:
+    return lib().mm_abi_version()
+
+
+def heads_for_dim(d_model: int, d_inner: int, d_head: int, m: int) -> int:
+    """h_i for Matryoshka width m (raises MMError on an invalid width)."""
+    out = _i64(0)
+    _check("mm_heads_for_dim", lib().mm_heads_for_dim(d_model, d_inner, d_head, m, ctypes.byref(out)))
+    return out.value
+
+
+def conv1d_silu(xbc: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                conv_state: Optional[torch.Tensor] = None, *, d_inner: int, d_head: int,
+                d_state: int, ngroups: int = 1, n_heads_active: Optional[int] = None,
+                heads_per_seq: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal depthwise conv (kernel 4) + SiLU on xbc (batch, seqlen, conv_dim)
+    -> out (same layout; only active channels written).  conv_state
+    (batch, 3, conv_dim) fp32 is read and updated in place."""
+    conv_dim = d_inner + 2 * ngroups * d_state
+    batch, seqlen = xbc.shape[0], xbc.shape[1]
+    n_heads = d_inner // d_head
+    h_act = n_heads if n_heads_active is None else int(n_heads_active)
+    if out is None:
+        out = torch.empty((batch, seqlen, conv_dim), dtype=xbc.dtype, device=xbc.device)
+    if out.dtype != xbc.dtype:
+        raise TypeError("out must have the input's dtype")
+    rs_in = _row_stride(xbc, "xbc", (conv_dim,))
+    rs_out = _row_stride(out, "out", (conv_dim,))
+    if w.dtype != torch.float32 or not w.is_contiguous() or w.numel() != conv_dim * 4:
+        raise ValueError("w must be a contiguous fp32 (conv_dim, 4) tensor")
+    if conv_state is not None and (conv_state.dtype != torch.float32 or not conv_state.is_contiguous()
+                                   or tuple(conv_state.shape) != (batch, 3, conv_dim)):
+        raise ValueError("conv_state must be a contiguous fp32 (batch, 3, conv_dim) tensor")
+    if heads_per_seq is not None and (heads_per_seq.dtype != torch.int32 or not heads_per_seq.is_contiguous()):
+        raise ValueError("heads_per_seq must be a contiguous int32 tensor")
+    st = lib().mm_conv1d_silu(_ptr(xbc), rs_in, _ptr(out), rs_out, _ptr(w), _ptr(bias),
+                              _ptr(conv_state), batch, seqlen, d_inner, d_head, d_state,
+                              ngroups, h_act, _ptr(heads_per_seq), _dtype_code(xbc), _stream())
+    _check("mm_conv1d_silu", st)
+    return out
+
+
+def ssd_forward_workspace_size(batch: int, seqlen: int, n_heads: int, d_head: int,
+                               d_state: int, ngroups: int, n_heads_active: int, chunk: int,
+                               dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    code = MM_F32 if dtype == torch.float32 else MM_BF16
+    _check("mm_ssd_forward_workspace_size",
+           lib().mm_ssd_forward_workspace_size(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                               n_heads_active, chunk, code, ctypes.byref(out)))
+    return out.value
+
+
+def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                C: torch.Tensor, D: Optional[torch.Tensor] = None, *,
+                n_heads_active: Optional[int] = None, chunk: int = 256,
+                initial_state: Optional[torch.Tensor] = None,
+                final_state: Optional[torch.Tensor] = None,
+                y: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Chunked selective scan over heads [0, n_heads_active).
+
+    x (batch, seqlen, n_heads, d_head), dt (batch, seqlen, n_heads),
+    B, C (batch, seqlen, ngroups, d_state) -- each may be a strided view
+    whose token rows are wider (e.g. column ranges of the conv output).
+    Returns y: the given buffer (batch, seqlen, n_heads, d_head) with the
+    active prefix written, or a new (batch, seqlen, n_heads_active, d_head)
+    tensor.  final_state (batch, n_heads, d_head, d_state) fp32, if given, is
+    written for the active heads."""
+    batch, seqlen, n_heads, d_head = x.shape
+    if B.dim() == 3:
+        B = B.unsqueeze(2)
+        C = C.unsqueeze(2)
+    ngroups, d_state = B.shape[2], B.shape[3]
+    h_act = n_heads if n_heads_active is None else int(n_heads_active)
+    if y is None:
+        y = torch.empty((batch, seqlen, h_act, d_head), dtype=x.dtype, device=x.device)
+    code = _dtype_code(x)
+    for name, t in (("dt", dt), ("B", B), ("C", C), ("y", y)):
+        if t.dtype != x.dtype:
+            raise TypeError(f"{name} must have x's dtype")
+    xs = _row_stride(x, "x", (n_heads, d_head))
+    ys = _row_stride(y, "y", (y.shape[2], d_head))
+    dts = _row_stride(dt, "dt", (n_heads,))
+    bs = _row_stride(B, "B", (ngroups, d_state))
+    cs = _row_stride(C, "C", (ngroups, d_state))
+    for name, t in (("A", A), ("D", D), ("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 tensor")
+    need = ssd_forward_workspace_size(batch, seqlen, n_heads, d_head, d_state, ngroups, h_act,
+                                      chunk, x.dtype)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().mm_ssd_forward(_ptr(x), xs, _ptr(dt), dts, _ptr(A), _ptr(B), bs, _ptr(C), cs,
+                              _ptr(D), _ptr(y), ys, _ptr(initial_state), _ptr(final_state),
+                              batch, seqlen, n_heads, d_head, d_state, ngroups, h_act, chunk,
+                              code, _ptr(workspace), wbytes, _stream())
+    _check("mm_ssd_forward", st)
+    return y
+
+
+def ssd_step(state: torch.Tensor, x_t: torch.Tensor, dt_t: torch.Tensor, A: torch.Tensor,
+             B_t: torch.Tensor, C_t: torch.Tensor, D: Optional[torch.Tensor] = None, *,
+             n_heads_active: Optional[int] = None,
+             heads_per_seq: Optional[torch.Tensor] = None,
+             y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode token, in place on state (batch, n_heads, d_head, d_state)
+    fp32.  x_t (batch, n_heads, d_head), dt_t (batch, n_heads),
+    B_t, C_t (batch, ngroups, d_state) -- rows may be strided.  Returns y_t
+    (batch, n_heads, d_head); inactive heads are left untouched."""
+    batch, n_heads, d_head, d_state = state.shape
+    if B_t.dim() == 2:
+        B_t = B_t.unsqueeze(1)
+        C_t = C_t.unsqueeze(1)
+    ngroups = B_t.shape[1]
+    h_act = n_heads if n_heads_active is None else int(n_heads_active)
+    if y is None:
+        y = torch.empty((batch, n_heads, d_head), dtype=x_t.dtype, device=x_t.device)
+    if state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError("state must be a contiguous fp32 tensor")
+
+    def rows(t, name, inner):
+        if tuple(t.shape[1:]) != tuple(inner):
+            raise ValueError(f"{name}: expected (batch, {inner}), got {tuple(t.shape)}")
+        expect = 1
+        for d in range(t.dim() - 1, 0, -1):
+            if t.shape[d] > 1 and t.stride(d) != expect:
+                raise ValueError(f"{name}: inner dimensions must be contiguous")
+            expect *= t.shape[d]
+        return t.stride(0) if t.shape[0] > 1 else expect
+
+    xs = rows(x_t, "x_t", (n_heads, d_head))
+    ys = rows(y, "y", (n_heads, d_head))
+    dts = rows(dt_t, "dt_t", (n_heads,))
+    bs = rows(B_t, "B_t", (ngroups, d_state))
+    cs = rows(C_t, "C_t", (ngroups, d_state))
+    if heads_per_seq is not None and (heads_per_seq.dtype != torch.int32 or not heads_per_seq.is_contiguous()):
+        raise ValueError("heads_per_seq must be a contiguous int32 tensor")
+    st = lib().mm_ssd_step(_ptr(state), _ptr(x_t), xs, _ptr(dt_t), dts, _ptr(A), _ptr(B_t), bs,
+                           _ptr(C_t), cs, _ptr(D), _ptr(y), ys, batch, n_heads, d_head, d_state,
+                           ngroups, h_act, _ptr(heads_per_seq), _dtype_code(x_t), _stream())
+    _check("mm_ssd_step", st)
+    return y

@@ -1,0 +1,162 @@
+// C ABI entry points of libmmssd.so (declared in include/mm_ssd.h): validate
+// on the host, then enqueue the gfx950 kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include "../../include/mm_ssd.h"
+#include "kernels.h"
+#include "validate.h"
+
+using namespace mmssd;
+
+namespace {
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MM_OK : MM_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int mm_abi_version(void) { return MM_ABI_VERSION; }
+
+const char* mm_status_string(int status) {
+  switch (status) {
+    case MM_OK: return "MM_OK";
+    case MM_ERR_NULL: return "MM_ERR_NULL: a required pointer is NULL";
+    case MM_ERR_SHAPE: return "MM_ERR_SHAPE: a size or stride is out of range or inconsistent";
+    case MM_ERR_SLICE: return "MM_ERR_SLICE: Matryoshka width or active head count is invalid";
+    case MM_ERR_DTYPE: return "MM_ERR_DTYPE: unknown dtype code";
+    case MM_ERR_UNSUPPORTED: return "MM_ERR_UNSUPPORTED: valid request not implemented by this build";
+    case MM_ERR_ALIGN: return "MM_ERR_ALIGN: a row start is not 16-byte aligned";
+    case MM_ERR_WORKSPACE: return "MM_ERR_WORKSPACE: workspace missing or too small";
+    case MM_ERR_HIP: return "MM_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown mm_status code";
+  }
+}
+
+int mm_heads_for_dim(int64_t d_model, int64_t d_inner, int64_t d_head, int64_t m,
+                     int64_t* heads_out) {
+  const int st = validate_heads_for_dim(d_model, d_inner, d_head, m, heads_out);
+  if (st != MM_OK) return st;
+  *heads_out = (d_inner / d_model) * m / d_head;
+  return MM_OK;
+}
+
+int mm_conv1d_silu(const void* xbc_in, int64_t in_row_stride, void* xbc_out,
+                   int64_t out_row_stride, const float* w, const float* bias,
+                   float* conv_state, int64_t batch, int64_t seqlen, int64_t d_inner,
+                   int64_t d_head, int64_t d_state, int64_t ngroups,
+                   int64_t n_heads_active, const int32_t* heads_active_per_seq,
+                   int dtype, void* stream) {
+  const int st = validate_conv(xbc_in, in_row_stride, xbc_out, out_row_stride, w, bias,
+                               conv_state, batch, seqlen, d_inner, d_head, d_state, ngroups,
+                               n_heads_active, dtype);
+  if (st != MM_OK) return st;
+  ConvArgs a;
+  a.in = xbc_in;
+  a.in_stride = in_row_stride;
+  a.out = xbc_out;
+  a.out_stride = out_row_stride;
+  a.w = w;
+  a.bias = bias;
+  a.conv_state = conv_state;
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.d_inner = d_inner;
+  a.d_head = d_head;
+  a.bc_dim = 2 * ngroups * d_state;
+  a.heads_cap = (int)n_heads_active;
+  a.heads_per_seq = heads_active_per_seq;
+  return hip_status(launch_conv1d_silu(a, dtype, as_stream(stream)));
+}
+
+int mm_ssd_forward_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
+                                  int64_t d_head, int64_t d_state, int64_t ngroups,
+                                  int64_t n_heads_active, int64_t chunk, int dtype,
+                                  size_t* bytes_out) {
+  if (!bytes_out) return MM_ERR_NULL;
+  const int st = validate_ssd_shape(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                    n_heads_active, chunk, dtype);
+  if (st != MM_OK) return st;
+  *bytes_out = fwd_workspace_bytes(batch, seqlen, n_heads_active, d_head, d_state, chunk);
+  return MM_OK;
+}
+
+int mm_ssd_forward(const void* x, int64_t x_row_stride, const void* dt,
+                   int64_t dt_row_stride, const float* A, const void* B,
+                   int64_t b_row_stride, const void* C, int64_t c_row_stride,
+                   const float* D, void* y, int64_t y_row_stride,
+                   const float* initial_state, float* final_state, int64_t batch,
+                   int64_t seqlen, int64_t n_heads, int64_t d_head, int64_t d_state,
+                   int64_t ngroups, int64_t n_heads_active, int64_t chunk, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate_ssd_forward(x, x_row_stride, dt, dt_row_stride, A, B, b_row_stride, C,
+                                c_row_stride, y, y_row_stride, initial_state, final_state,
+                                batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                n_heads_active, chunk, dtype);
+  if (st != MM_OK) return st;
+  const size_t need = fwd_workspace_bytes(batch, seqlen, n_heads_active, d_head, d_state, chunk);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MM_ERR_WORKSPACE;
+  if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return MM_ERR_ALIGN;
+  FwdArgs a;
+  a.x = x;
+  a.xs = x_row_stride;
+  a.dt = dt;
+  a.dts = dt_row_stride;
+  a.A = A;
+  a.B = B;
+  a.bs = b_row_stride;
+  a.C = C;
+  a.cs = c_row_stride;
+  a.D = D;
+  a.y = y;
+  a.ys = y_row_stride;
+  a.h0 = initial_state;
+  a.hT = final_state;
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.n_heads = (int)n_heads;
+  a.d_head = (int)d_head;
+  a.d_state = (int)d_state;
+  a.heads = (int)n_heads_active;
+  a.chunk = (int)chunk;
+  return hip_status(launch_ssd_forward(a, dtype, workspace, as_stream(stream)));
+}
+
+int mm_ssd_step(float* state, const void* x_t, int64_t x_row_stride, const void* dt_t,
+                int64_t dt_row_stride, const float* A, const void* B_t,
+                int64_t b_row_stride, const void* C_t, int64_t c_row_stride,
+                const float* D, void* y_t, int64_t y_row_stride, int64_t batch,
+                int64_t n_heads, int64_t d_head, int64_t d_state, int64_t ngroups,
+                int64_t n_heads_active, const int32_t* heads_active_per_seq, int dtype,
+                void* stream) {
+  const int st = validate_ssd_step(state, x_t, x_row_stride, dt_t, dt_row_stride, A, B_t,
+                                   b_row_stride, C_t, c_row_stride, y_t, y_row_stride,
+                                   batch, n_heads, d_head, d_state, ngroups, n_heads_active,
+                                   dtype);
+  if (st != MM_OK) return st;
+  StepArgs a;
+  a.state = state;
+  a.x = x_t;
+  a.xs = x_row_stride;
+  a.dt = dt_t;
+  a.dts = dt_row_stride;
+  a.A = A;
+  a.B = B_t;
+  a.bs = b_row_stride;
+  a.C = C_t;
+  a.cs = c_row_stride;
+  a.D = D;
+  a.y = y_t;
+  a.ys = y_row_stride;
+  a.batch = batch;
+  a.n_heads = (int)n_heads;
+  a.d_head = (int)d_head;
+  a.d_state = (int)d_state;
+  a.heads_cap = (int)n_heads_active;
+  a.heads_per_seq = heads_active_per_seq;
+  return hip_status(launch_ssd_step(a, dtype, as_stream(stream)));
+}
+
+}  // extern "C"

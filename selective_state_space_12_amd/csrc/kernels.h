@@ -1,0 +1,80 @@
+// Host-side launchers of the gfx950 kernels.  Arguments have been validated by
+// the C ABI layer (abi.cpp) before any of these is called; each returns a
+// hipError_t from the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace mmssd {
+
+struct ConvArgs {
+  const void* in;
+  int64_t in_stride;
+  void* out;
+  int64_t out_stride;
+  const float* w;
+  const float* bias;
+  float* conv_state;
+  int64_t batch, seqlen, d_inner, d_head, bc_dim;  // bc_dim = 2*ngroups*d_state
+  int heads_cap;                                    // n_heads_active
+  const int32_t* heads_per_seq;                     // device, nullable
+};
+
+hipError_t launch_conv1d_silu(const ConvArgs& a, int dtype, hipStream_t s);
+
+struct StepArgs {
+  float* state;
+  const void* x;
+  int64_t xs;
+  const void* dt;
+  int64_t dts;
+  const float* A;
+  const void* B;
+  int64_t bs;
+  const void* C;
+  int64_t cs;
+  const float* D;
+  void* y;
+  int64_t ys;
+  int64_t batch;
+  int n_heads, d_head, d_state;
+  int heads_cap;
+  const int32_t* heads_per_seq;
+};
+
+hipError_t launch_ssd_step(const StepArgs& a, int dtype, hipStream_t s);
+
+struct FwdArgs {
+  const void* x;
+  int64_t xs;
+  const void* dt;
+  int64_t dts;
+  const float* A;
+  const void* B;
+  int64_t bs;
+  const void* C;
+  int64_t cs;
+  const float* D;
+  void* y;
+  int64_t ys;
+  const float* h0;
+  float* hT;
+  int64_t batch, seqlen;
+  int n_heads, d_head, d_state, heads;
+  int chunk;
+};
+
+// How a scan call is cut: chunks per sequence, segments per sequence and
+// chunks per segment (every segment but the last holds seg_chunks chunks).
+void fwd_plan(int64_t batch, int64_t seqlen, int64_t heads, int64_t chunk, int* nchunks,
+              int* nseg, int* seg_chunks);
+// Device workspace the plan needs (segment states and decays), 0 if none.
+size_t fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
+                           int64_t d_head, int64_t d_state, int64_t chunk);
+
+hipError_t launch_ssd_forward(const FwdArgs& a, int dtype, void* workspace, hipStream_t s);
+
+}  // namespace mmssd

@@ -1,0 +1,172 @@
+// Host-side argument validation (see validate.h).
+#include "validate.h"
+
+#include <cstdint>
+
+namespace mmssd {
+
+namespace {
+
+// Largest element count accepted for any single dimension product; keeps all
+// index arithmetic far from int64 overflow.
+constexpr int64_t kMaxElems = int64_t(1) << 46;
+
+bool pos(int64_t v) { return v > 0 && v < kMaxElems; }
+
+bool mul_ok(int64_t a, int64_t b) { return a > 0 && b > 0 && a <= kMaxElems / b; }
+
+// Supported (d_head, d_state) pairs of the chunked-scan kernel.
+bool scan_shape_supported(int64_t P, int64_t N) {
+  return (P == 32 && N == 16) || (P == 64 && N == 64) || (P == 64 && N == 128);
+}
+
+bool chunk_supported(int64_t q) {
+  return q == 16 || q == 32 || q == 64 || q == 128 || q == 256;
+}
+
+}  // namespace
+
+bool rows_aligned(const void* p, int64_t stride, int64_t elem) {
+  return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((stride * elem) % 16 == 0);
+}
+
+int validate_heads_for_dim(int64_t d_model, int64_t d_inner, int64_t d_head,
+                           int64_t m, const int64_t* heads_out) {
+  if (!heads_out) return MM_ERR_NULL;
+  if (!pos(d_model) || !pos(d_inner) || !pos(d_head)) return MM_ERR_SHAPE;
+  if (d_inner % d_model != 0) return MM_ERR_SHAPE;
+  if (m <= 0 || m > d_model) return MM_ERR_SLICE;
+  const int64_t e = d_inner / d_model;
+  if ((e * m) % d_head != 0) return MM_ERR_SLICE;
+  return MM_OK;
+}
+
+int validate_conv(const void* xbc_in, int64_t in_row_stride, const void* xbc_out,
+                  int64_t out_row_stride, const float* w, const float* bias,
+                  const float* conv_state, int64_t batch,
+                  int64_t seqlen, int64_t d_inner, int64_t d_head,
+                  int64_t d_state, int64_t ngroups, int64_t n_heads_active,
+                  int dtype) {
+  if (!xbc_in || !xbc_out || !w) return MM_ERR_NULL;
+  const int64_t el = dtype_bytes(dtype);
+  if (el == 0) return MM_ERR_DTYPE;
+  if (!pos(batch) || !pos(seqlen) || !pos(d_inner) || !pos(d_head) ||
+      !pos(d_state) || !pos(ngroups))
+    return MM_ERR_SHAPE;
+  if (d_inner % d_head != 0) return MM_ERR_SHAPE;
+  if (d_head % 8 != 0 || d_state % 8 != 0) return MM_ERR_UNSUPPORTED;
+  const int64_t n_heads = d_inner / d_head;
+  if (n_heads_active < 1 || n_heads_active > n_heads) return MM_ERR_SLICE;
+  if (!mul_ok(ngroups, d_state)) return MM_ERR_SHAPE;
+  const int64_t conv_dim = d_inner + 2 * ngroups * d_state;
+  if (in_row_stride < conv_dim || out_row_stride < conv_dim) return MM_ERR_SHAPE;
+  if (!mul_ok(batch, seqlen) || !mul_ok(batch * seqlen, in_row_stride) ||
+      !mul_ok(batch * seqlen, out_row_stride))
+    return MM_ERR_SHAPE;
+  if (batch > kMaxGridYZ) return MM_ERR_SHAPE;
+  if (!rows_aligned(xbc_in, in_row_stride, el) || !rows_aligned(xbc_out, out_row_stride, el))
+    return MM_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(w) % 16 != 0) return MM_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(bias) % 4 != 0 || reinterpret_cast<uintptr_t>(conv_state) % 4 != 0)
+    return MM_ERR_ALIGN;
+  // The output must not overlap the input (the window reads neighbours).
+  const uintptr_t i0 = reinterpret_cast<uintptr_t>(xbc_in);
+  const uintptr_t i1 = i0 + uintptr_t(((batch * seqlen - 1) * in_row_stride + conv_dim) * el);
+  const uintptr_t o0 = reinterpret_cast<uintptr_t>(xbc_out);
+  const uintptr_t o1 = o0 + uintptr_t(((batch * seqlen - 1) * out_row_stride + conv_dim) * el);
+  if (i0 < o1 && o0 < i1) return MM_ERR_SHAPE;
+  return MM_OK;
+}
+
+int validate_ssd_shape(int64_t batch, int64_t seqlen, int64_t n_heads,
+                       int64_t d_head, int64_t d_state, int64_t ngroups,
+                       int64_t n_heads_active, int64_t chunk, int dtype) {
+  if (dtype_bytes(dtype) == 0) return MM_ERR_DTYPE;
+  if (!pos(batch) || !pos(seqlen) || !pos(n_heads) || !pos(d_head) ||
+      !pos(d_state) || !pos(ngroups) || !pos(chunk))
+    return MM_ERR_SHAPE;
+  if (n_heads_active < 1 || n_heads_active > n_heads) return MM_ERR_SLICE;
+  if (n_heads % ngroups != 0) return MM_ERR_SHAPE;
+  if (batch > kMaxGridYZ || n_heads > kMaxGridYZ) return MM_ERR_SHAPE;
+  if (ngroups != 1) return MM_ERR_UNSUPPORTED;
+  if (!scan_shape_supported(d_head, d_state)) return MM_ERR_UNSUPPORTED;
+  if (!chunk_supported(chunk)) return MM_ERR_UNSUPPORTED;
+  // fp32 tiles of a 256-token chunk with d_state 128 exceed one CU's LDS.
+  if (dtype == MM_F32 && d_state == 128 && chunk > 128) return MM_ERR_UNSUPPORTED;
+  if (!mul_ok(batch, seqlen) || !mul_ok(n_heads, d_head) ||
+      !mul_ok(batch * seqlen, n_heads * d_head) || !mul_ok(batch * n_heads, d_head * d_state))
+    return MM_ERR_SHAPE;
+  return MM_OK;
+}
+
+int validate_ssd_forward(const void* x, int64_t x_row_stride, const void* dt,
+                         int64_t dt_row_stride, const float* A, const void* B,
+                         int64_t b_row_stride, const void* C,
+                         int64_t c_row_stride, const void* y,
+                         int64_t y_row_stride, const float* initial_state,
+                         const float* final_state, int64_t batch, int64_t seqlen,
+                         int64_t n_heads, int64_t d_head, int64_t d_state,
+                         int64_t ngroups, int64_t n_heads_active, int64_t chunk,
+                         int dtype) {
+  if (!x || !dt || !A || !B || !C || !y) return MM_ERR_NULL;
+  int st = validate_ssd_shape(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                              n_heads_active, chunk, dtype);
+  if (st != MM_OK) return st;
+  const int64_t el = dtype_bytes(dtype);
+  const int64_t xw = n_heads * d_head;
+  const int64_t bw = ngroups * d_state;
+  if (x_row_stride < xw || y_row_stride < xw || dt_row_stride < n_heads ||
+      b_row_stride < bw || c_row_stride < bw)
+    return MM_ERR_SHAPE;
+  const int64_t rows = batch * seqlen;
+  if (!mul_ok(rows, x_row_stride) || !mul_ok(rows, y_row_stride) ||
+      !mul_ok(rows, dt_row_stride) || !mul_ok(rows, b_row_stride) ||
+      !mul_ok(rows, c_row_stride))
+    return MM_ERR_SHAPE;
+  if (!rows_aligned(x, x_row_stride, el) || !rows_aligned(y, y_row_stride, el) ||
+      !rows_aligned(B, b_row_stride, el) || !rows_aligned(C, c_row_stride, el))
+    return MM_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(dt) % el != 0) return MM_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(initial_state) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(final_state) % 4 != 0)
+    return MM_ERR_ALIGN;
+  return MM_OK;
+}
+
+int validate_ssd_step(const float* state, const void* x_t, int64_t x_row_stride,
+                      const void* dt_t, int64_t dt_row_stride, const float* A,
+                      const void* B_t, int64_t b_row_stride, const void* C_t,
+                      int64_t c_row_stride, const void* y_t,
+                      int64_t y_row_stride, int64_t batch, int64_t n_heads,
+                      int64_t d_head, int64_t d_state, int64_t ngroups,
+                      int64_t n_heads_active, int dtype) {
+  if (!state || !x_t || !dt_t || !A || !B_t || !C_t || !y_t) return MM_ERR_NULL;
+  const int64_t el = dtype_bytes(dtype);
+  if (el == 0) return MM_ERR_DTYPE;
+  if (!pos(batch) || !pos(n_heads) || !pos(d_head) || !pos(d_state) || !pos(ngroups))
+    return MM_ERR_SHAPE;
+  if (n_heads_active < 1 || n_heads_active > n_heads) return MM_ERR_SLICE;
+  if (n_heads % ngroups != 0) return MM_ERR_SHAPE;
+  if (batch > kMaxGridYZ) return MM_ERR_SHAPE;
+  if (ngroups != 1) return MM_ERR_UNSUPPORTED;
+  if (d_state != 16 && d_state != 32 && d_state != 64 && d_state != 128 && d_state != 256)
+    return MM_ERR_UNSUPPORTED;
+  const int64_t xw = n_heads * d_head;
+  const int64_t bw = ngroups * d_state;
+  if (x_row_stride < xw || y_row_stride < xw || dt_row_stride < n_heads ||
+      b_row_stride < bw || c_row_stride < bw)
+    return MM_ERR_SHAPE;
+  if (!mul_ok(batch, x_row_stride) || !mul_ok(batch, y_row_stride) ||
+      !mul_ok(batch, dt_row_stride) || !mul_ok(batch, b_row_stride) ||
+      !mul_ok(batch, c_row_stride) || !mul_ok(batch * n_heads, d_head * d_state))
+    return MM_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(state) % 16 != 0) return MM_ERR_ALIGN;
+  if (!rows_aligned(B_t, b_row_stride, el) || !rows_aligned(C_t, c_row_stride, el))
+    return MM_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(x_t) % el != 0 || reinterpret_cast<uintptr_t>(y_t) % el != 0 ||
+      reinterpret_cast<uintptr_t>(dt_t) % el != 0)
+    return MM_ERR_ALIGN;
+  return MM_OK;
+}
+
+}  // namespace mmssd

@@ -1,0 +1,59 @@
+// Host-side argument validation for the C ABI in include/mm_ssd.h.
+//
+// Pure C++ with no HIP calls, so it is also built with g++ (and sanitizers) on
+// machines without a GPU.  Every function returns MM_OK or the MM_ERR_* code
+// the header documents; nothing is enqueued before these checks pass.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/mm_ssd.h"
+
+namespace mmssd {
+
+// Grid dimensions y and z of a launch are limited to this many blocks.
+constexpr int64_t kMaxGridYZ = 65535;
+
+// Sizes of one element of a token-stream dtype, 0 if unknown.
+inline int64_t dtype_bytes(int dtype) {
+  return dtype == MM_F32 ? 4 : dtype == MM_BF16 ? 2 : 0;
+}
+
+// True when p is 16-byte aligned and stride*elem keeps every row aligned.
+bool rows_aligned(const void* p, int64_t stride, int64_t elem);
+
+int validate_heads_for_dim(int64_t d_model, int64_t d_inner, int64_t d_head,
+                           int64_t m, const int64_t* heads_out);
+
+int validate_conv(const void* xbc_in, int64_t in_row_stride, const void* xbc_out,
+                  int64_t out_row_stride, const float* w, const float* bias,
+                  const float* conv_state, int64_t batch,
+                  int64_t seqlen, int64_t d_inner, int64_t d_head,
+                  int64_t d_state, int64_t ngroups, int64_t n_heads_active,
+                  int dtype);
+
+// Shape-only part of the scan checks (used by the workspace query too).
+int validate_ssd_shape(int64_t batch, int64_t seqlen, int64_t n_heads,
+                       int64_t d_head, int64_t d_state, int64_t ngroups,
+                       int64_t n_heads_active, int64_t chunk, int dtype);
+
+int validate_ssd_forward(const void* x, int64_t x_row_stride, const void* dt,
+                         int64_t dt_row_stride, const float* A, const void* B,
+                         int64_t b_row_stride, const void* C,
+                         int64_t c_row_stride, const void* y,
+                         int64_t y_row_stride, const float* initial_state,
+                         const float* final_state, int64_t batch, int64_t seqlen,
+                         int64_t n_heads, int64_t d_head, int64_t d_state,
+                         int64_t ngroups, int64_t n_heads_active, int64_t chunk,
+                         int dtype);
+
+int validate_ssd_step(const float* state, const void* x_t, int64_t x_row_stride,
+                      const void* dt_t, int64_t dt_row_stride, const float* A,
+                      const void* B_t, int64_t b_row_stride, const void* C_t,
+                      int64_t c_row_stride, const void* y_t,
+                      int64_t y_row_stride, int64_t batch, int64_t n_heads,
+                      int64_t d_head, int64_t d_state, int64_t ngroups,
+                      int64_t n_heads_active, int dtype);
+
+}  // namespace mmssd

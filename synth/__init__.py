@@ -139,7 +139,8 @@ def xbc_inputs(w: Workload, batch: Optional[int] = None,
                seqlen: Optional[int] = None, salt: int = 0,
                with_state: bool = False) -> Dict[str, torch.Tensor]:
     """Raw conv input (b, l, conv_dim) ~ N(0,1) in the storage dtype, its
-    weights, and optionally a conv state (b, conv_dim, 3) ~ N(0,1) fp32."""
+    weights, and optionally a conv state (b, 3, conv_dim) ~ N(0,1) fp32
+    (oldest tap first)."""
     b = batch or w.batch
     l = seqlen or w.seqlen
     out = {
@@ -147,7 +148,7 @@ def xbc_inputs(w: Workload, batch: Optional[int] = None,
         "w": draw_conv_w(w),
     }
     if with_state:
-        out["conv_state"] = _normal((b, w.conv_dim, 3), _gen(w, _CS0, salt))
+        out["conv_state"] = _normal((b, 3, w.conv_dim), _gen(w, _CS0, salt))
     return out
 
 

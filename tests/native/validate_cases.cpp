@@ -1,0 +1,97 @@
+// Host-only checks of the C ABI's argument validation, built with g++ and
+// AddressSanitizer/UBSan by tests/test_abi_cpu.py (no HIP, no GPU).  Every
+// case states the status code include/mm_ssd.h documents for it.
+#include <cstdint>
+#include <cstdio>
+
+#include "../../selective_state_space_12_amd/csrc/validate.h"
+
+using namespace mmssd;
+
+static int failures = 0;
+
+static void expect(const char* name, int got, int want) {
+  if (got != want) {
+    std::printf("FAIL %s: got %d want %d\n", name, got, want);
+    ++failures;
+  } else {
+    std::printf("ok   %s\n", name);
+  }
+}
+
+int main() {
+  // fake, 16-byte aligned addresses: validation never dereferences them
+  const void* P = reinterpret_cast<const void*>(uintptr_t(0x100000));
+  const void* P2 = reinterpret_cast<const void*>(uintptr_t(0x1000000000ull));
+  const float* F = reinterpret_cast<const float*>(uintptr_t(0x200000));
+  const void* MIS = reinterpret_cast<const void*>(uintptr_t(0x100008));
+  int64_t h = 0;
+
+  // slice resolution (nesting / Mix'n'Match rule)
+  expect("heads ok", validate_heads_for_dim(2048, 4096, 64, 256, &h), MM_OK);
+  expect("heads null", validate_heads_for_dim(2048, 4096, 64, 256, nullptr), MM_ERR_NULL);
+  expect("heads m=0", validate_heads_for_dim(2048, 4096, 64, 0, &h), MM_ERR_SLICE);
+  expect("heads m>d", validate_heads_for_dim(2048, 4096, 64, 2049, &h), MM_ERR_SLICE);
+  expect("heads non-integer", validate_heads_for_dim(2048, 4096, 64, 100, &h), MM_ERR_SLICE);
+  expect("heads e not integer", validate_heads_for_dim(3, 4, 2, 1, &h), MM_ERR_SHAPE);
+  expect("heads d_head<=0", validate_heads_for_dim(2048, 4096, 0, 256, &h), MM_ERR_SHAPE);
+
+  // conv: 4096 + 256 channels, bf16
+  const int64_t cd = 4352;
+  expect("conv ok", validate_conv(P, cd, P2, cd, F, nullptr, nullptr, 4, 8192, 4096, 64, 128, 1, 64, MM_BF16), MM_OK);
+  expect("conv null in", validate_conv(nullptr, cd, P2, cd, F, nullptr, nullptr, 4, 8192, 4096, 64, 128, 1, 64, MM_BF16), MM_ERR_NULL);
+  expect("conv null w", validate_conv(P, cd, P2, cd, nullptr, nullptr, nullptr, 4, 8192, 4096, 64, 128, 1, 64, MM_BF16), MM_ERR_NULL);
+  expect("conv dtype", validate_conv(P, cd, P2, cd, F, nullptr, nullptr, 4, 8192, 4096, 64, 128, 1, 64, 9), MM_ERR_DTYPE);
+  expect("conv heads 0", validate_conv(P, cd, P2, cd, F, nullptr, nullptr, 4, 8192, 4096, 64, 128, 1, 0, MM_BF16), MM_ERR_SLICE);
+  expect("conv heads > n", validate_conv(P, cd, P2, cd, F, nullptr, nullptr, 4, 8192, 4096, 64, 128, 1, 65, MM_BF16), MM_ERR_SLICE);
+  expect("conv stride short", validate_conv(P, cd - 8, P2, cd, F, nullptr, nullptr, 4, 8192, 4096, 64, 128, 1, 64, MM_BF16), MM_ERR_SHAPE);
+  expect("conv misaligned", validate_conv(MIS, cd, P2, cd, F, nullptr, nullptr, 4, 8192, 4096, 64, 128, 1, 64, MM_BF16), MM_ERR_ALIGN);
+  expect("conv stride misaligned", validate_conv(P, cd + 1, P2, cd, F, nullptr, nullptr, 4, 8192, 4096, 64, 128, 1, 64, MM_BF16), MM_ERR_ALIGN);
+  expect("conv overlap", validate_conv(P, cd, P, cd, F, nullptr, nullptr, 1, 2, 4096, 64, 128, 1, 64, MM_BF16), MM_ERR_SHAPE);
+  expect("conv d_head%8", validate_conv(P, 40, P2, 40, F, nullptr, nullptr, 1, 2, 12, 4, 8, 1, 1, MM_F32), MM_ERR_UNSUPPORTED);
+  expect("conv batch 0", validate_conv(P, cd, P2, cd, F, nullptr, nullptr, 0, 8192, 4096, 64, 128, 1, 64, MM_BF16), MM_ERR_SHAPE);
+  expect("conv batch > grid", validate_conv(P, cd, P2, cd, F, nullptr, nullptr, 70000, 1, 4096, 64, 128, 1, 64, MM_BF16), MM_ERR_SHAPE);
+
+  // scan forward: x/y rows 4096 wide, B/C 128 wide, dt 64 wide
+  auto fwd = [&](const void* x, int64_t xs, const void* dt, int64_t dts, const float* A,
+                 const void* B, int64_t bs, const void* C, int64_t cs, const void* y, int64_t ys,
+                 int64_t batch, int64_t seqlen, int64_t nh, int64_t P_, int64_t N_, int64_t G,
+                 int64_t ha, int64_t q, int dt_code) {
+    return validate_ssd_forward(x, xs, dt, dts, A, B, bs, C, cs, y, ys, nullptr, nullptr, batch,
+                                seqlen, nh, P_, N_, G, ha, q, dt_code);
+  };
+  expect("fwd ok", fwd(P, 4096, P, 64, F, P, 128, P, 128, P2, 4096, 4, 8192, 64, 64, 128, 1, 64, 256, MM_BF16), MM_OK);
+  expect("fwd ok strided", fwd(P, 4352, P, 64, F, P, 4352, P, 4352, P2, 4096, 4, 8192, 64, 64, 128, 1, 8, 256, MM_BF16), MM_OK);
+  expect("fwd null A", fwd(P, 4096, P, 64, nullptr, P, 128, P, 128, P2, 4096, 4, 8192, 64, 64, 128, 1, 64, 256, MM_BF16), MM_ERR_NULL);
+  expect("fwd dtype", fwd(P, 4096, P, 64, F, P, 128, P, 128, P2, 4096, 4, 8192, 64, 64, 128, 1, 64, 256, 2), MM_ERR_DTYPE);
+  expect("fwd heads 0", fwd(P, 4096, P, 64, F, P, 128, P, 128, P2, 4096, 4, 8192, 64, 64, 128, 1, 0, 256, MM_BF16), MM_ERR_SLICE);
+  expect("fwd heads > n", fwd(P, 4096, P, 64, F, P, 128, P, 128, P2, 4096, 4, 8192, 64, 64, 128, 1, 65, 256, MM_BF16), MM_ERR_SLICE);
+  expect("fwd ngroups 2", fwd(P, 4096, P, 64, F, P, 256, P, 256, P2, 4096, 4, 8192, 64, 64, 128, 2, 64, 256, MM_BF16), MM_ERR_UNSUPPORTED);
+  expect("fwd chunk 48", fwd(P, 4096, P, 64, F, P, 128, P, 128, P2, 4096, 4, 8192, 64, 64, 128, 1, 64, 48, MM_BF16), MM_ERR_UNSUPPORTED);
+  expect("fwd shape (48,128)", fwd(P, 3072, P, 64, F, P, 128, P, 128, P2, 3072, 4, 8192, 64, 48, 128, 1, 64, 256, MM_BF16), MM_ERR_UNSUPPORTED);
+  expect("fwd fp32 chunk 256 N=128", fwd(P, 4096, P, 64, F, P, 128, P, 128, P2, 4096, 4, 8192, 64, 64, 128, 1, 64, 256, MM_F32), MM_ERR_UNSUPPORTED);
+  expect("fwd x stride short", fwd(P, 4088, P, 64, F, P, 128, P, 128, P2, 4096, 4, 8192, 64, 64, 128, 1, 64, 256, MM_BF16), MM_ERR_SHAPE);
+  expect("fwd dt stride short", fwd(P, 4096, P, 63, F, P, 128, P, 128, P2, 4096, 4, 8192, 64, 64, 128, 1, 64, 256, MM_BF16), MM_ERR_SHAPE);
+  expect("fwd B misaligned", fwd(P, 4096, P, 64, F, MIS, 128, P, 128, P2, 4096, 4, 8192, 64, 64, 128, 1, 64, 256, MM_BF16), MM_ERR_ALIGN);
+  expect("fwd y stride misaligned", fwd(P, 4096, P, 64, F, P, 128, P, 128, P2, 4100, 4, 8192, 64, 64, 128, 1, 64, 256, MM_BF16), MM_ERR_ALIGN);
+  expect("fwd seqlen 0", fwd(P, 4096, P, 64, F, P, 128, P, 128, P2, 4096, 4, 0, 64, 64, 128, 1, 64, 256, MM_BF16), MM_ERR_SHAPE);
+  expect("fwd huge", fwd(P, 4096, P, 64, F, P, 128, P, 128, P2, 4096, int64_t(1) << 40, 1 << 20, 64, 64, 128, 1, 64, 256, MM_BF16), MM_ERR_SHAPE);
+  expect("fwd shape only ok", validate_ssd_shape(1, 256, 4, 32, 16, 1, 4, 64, MM_F32), MM_OK);
+
+  // decode step
+  auto step = [&](const float* st, int64_t batch, int64_t nh, int64_t P_, int64_t N_, int64_t G,
+                  int64_t ha, int dt_code, const void* B) {
+    return validate_ssd_step(st, P, nh * P_, P, nh, F, B, G * N_, P, G * N_, P2, nh * P_, batch, nh,
+                             P_, N_, G, ha, dt_code);
+  };
+  expect("step ok", step(F, 256, 64, 64, 128, 1, 64, MM_F32, P), MM_OK);
+  expect("step null state", step(nullptr, 256, 64, 64, 128, 1, 64, MM_F32, P), MM_ERR_NULL);
+  expect("step heads 0", step(F, 256, 64, 64, 128, 1, 0, MM_F32, P), MM_ERR_SLICE);
+  expect("step N=96", step(F, 256, 64, 64, 96, 1, 64, MM_F32, P), MM_ERR_UNSUPPORTED);
+  expect("step ngroups 2", step(F, 256, 64, 64, 128, 2, 64, MM_F32, P), MM_ERR_UNSUPPORTED);
+  expect("step B misaligned", step(F, 256, 64, 64, 128, 1, 64, MM_F32, MIS), MM_ERR_ALIGN);
+  expect("step dtype", step(F, 256, 64, 64, 128, 1, 64, 5, P), MM_ERR_DTYPE);
+
+  std::printf("%d failure(s)\n", failures);
+  return failures == 0 ? 0 : 1;
+}

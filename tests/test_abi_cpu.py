@@ -1,0 +1,128 @@
+"""CPU checks of the C ABI: the shared library loads and exports every entry
+point include/mm_ssd.h declares; host-only entry points answer; argument
+validation returns the documented codes (g++ build under ASan/UBSan).  No
+kernel is launched here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mm_ssd.h")
+LIB = os.path.join(ROOT, "selective_state_space_12_amd", "libmmssd.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mm_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from selective_state_space_12_amd import _build
+        _build.build(verbose=False)
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for fn in ("mm_conv1d_silu", "mm_ssd_forward", "mm_ssd_step", "mm_ssd_forward_workspace_size",
+               "mm_heads_for_dim", "mm_status_string", "mm_abi_version"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings(lib):
+    lib.mm_abi_version.restype = ctypes.c_int
+    assert lib.mm_abi_version() == 1
+    lib.mm_status_string.restype = ctypes.c_char_p
+    lib.mm_status_string.argtypes = [ctypes.c_int]
+    names = [lib.mm_status_string(c).decode() for c in range(0, -9, -1)]
+    assert names[0] == "MM_OK"
+    for code, prefix in zip(range(-1, -9, -1), ["MM_ERR_NULL", "MM_ERR_SHAPE", "MM_ERR_SLICE",
+                                                "MM_ERR_DTYPE", "MM_ERR_UNSUPPORTED", "MM_ERR_ALIGN",
+                                                "MM_ERR_WORKSPACE", "MM_ERR_HIP"]):
+        assert lib.mm_status_string(code).decode().startswith(prefix)
+    assert lib.mm_status_string(12345)
+
+
+def test_heads_for_dim_matches_slice_rule(lib):
+    """MatMamba nesting paragraph: h_i = e*m_i/d_head for every trained and
+    interpolated width; invalid widths are rejected."""
+    import synth
+    f = lib.mm_heads_for_dim
+    f.argtypes = [ctypes.c_int64] * 4 + [ctypes.POINTER(ctypes.c_int64)]
+    out = ctypes.c_int64()
+    for w in synth.WORKLOADS.values():
+        for m in w.slices:
+            assert f(w.d_model, w.d_inner, w.d_head, m, ctypes.byref(out)) == 0
+            assert out.value == w.heads(m)
+    assert f(2048, 4096, 64, 100, ctypes.byref(out)) == -3
+    assert f(2048, 4096, 64, 0, ctypes.byref(out)) == -3
+    assert f(2048, 4096, 64, 4096, ctypes.byref(out)) == -3
+    assert f(2048, 4096, 64, 256, None) == -1
+
+
+def test_workspace_query(lib):
+    f = lib.mm_ssd_forward_workspace_size
+    f.argtypes = [ctypes.c_int64] * 8 + [ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    out = ctypes.c_size_t()
+    # one long sequence, few heads: split into segments -> non-zero workspace
+    assert f(1, 131072, 32, 64, 128, 1, 8, 256, 1, ctypes.byref(out)) == 0
+    assert out.value > 0
+    assert f(1, 131072, 32, 64, 128, 1, 8, 48, 1, ctypes.byref(out)) == -5
+    assert f(1, 131072, 32, 64, 128, 2, 8, 256, 1, ctypes.byref(out)) == -5
+
+
+def _no_gpu():
+    return not os.path.exists("/dev/kfd")
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake device pointers are only passed where no GPU exists")
+def test_entry_points_reject_before_enqueueing(lib):
+    """Every failing call returns its status before touching the GPU (these
+    pointers are fake; a launch would fail loudly here)."""
+    P = 0x100000
+    lib.mm_ssd_forward.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    args = [P, 4096, P, 64, P, P, 128, P, 128, None, P, 4096, None, None,
+            4, 8192, 64, 64, 128, 1, 64, 256, 1, None, 0, None]
+    types = [ctypes.c_void_p, i64, ctypes.c_void_p, i64, ctypes.c_void_p, ctypes.c_void_p, i64,
+             ctypes.c_void_p, i64, ctypes.c_void_p, ctypes.c_void_p, i64, ctypes.c_void_p,
+             ctypes.c_void_p, i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.mm_ssd_forward.argtypes = types
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return lib.mm_ssd_forward(*a)
+
+    assert call(a0=None) == -1          # x NULL
+    assert call(a22=7) == -4            # dtype
+    assert call(a20=0) == -3            # n_heads_active 0
+    assert call(a19=2, a6=256, a8=256) == -5  # ngroups 2
+    assert call(a21=100) == -5          # chunk
+    assert call(a1=4095) == -2          # x row stride too short
+    assert call(a5=P + 8) == -6         # B misaligned
+
+
+def test_validation_cases_under_sanitizers(tmp_path):
+    src = os.path.join(ROOT, "tests", "native", "validate_cases.cpp")
+    val = os.path.join(ROOT, "selective_state_space_12_amd", "csrc", "validate.cpp")
+    exe = str(tmp_path / "validate_cases")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-Wall", "-Wextra", "-o", exe, src, val]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    res = subprocess.run([exe], capture_output=True, text=True)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "0 failure(s)" in res.stdout
