@@ -142,10 +142,12 @@ int mm_ssd_forward_workspace_size(int64_t batch, int64_t seqlen,
  * chunk; states are passed from chunk to chunk.  The result equals the
  * token-by-token recurrence up to rounding and does not depend on `chunk`.
  *
- *   x   (batch*seqlen rows, x_row_stride) dtype: row = n_heads*d_head values,
- *       head-major; the first n_heads_active*d_head are read.
+ *   x   (batch*seqlen rows, x_row_stride) dtype: head-major rows of d_head
+ *       values per head; the first n_heads_active*d_head are read, so a row
+ *       may hold just the active heads (x_row_stride >= n_heads_active*d_head).
  *   dt  (rows, dt_row_stride) dtype: per-head step size after any bias and
  *       softplus (> 0); the first n_heads_active entries are read.
+ *   n_heads sizes A, D, initial_state and final_state (the full block).
  *   A   (n_heads) fp32, D (n_heads) fp32 or NULL (= 0); prefixes read.
  *   B, C (rows, b_row_stride / c_row_stride) dtype: ngroups*d_state values.
  *   y   (rows, y_row_stride) dtype: the first n_heads_active*d_head values of

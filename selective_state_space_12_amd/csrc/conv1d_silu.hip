@@ -71,23 +71,33 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
     }
   }
 
-  for (int t = t0; t < t1; ++t) {
-    const Vec16<T> u = load16(in + (row0 + t) * in_stride + c);
-    Vec16<T> o;
+  // tokens in groups of kGroup: issue the group's loads, then compute and store
+  constexpr int kGroup = 8;
+  for (int tg = t0; tg < t1; tg += kGroup) {
+    Vec16<T> u[kGroup];
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const float ut = to_f32(u.v[j]);
-      float pre = bv[j];
-      pre = fmaf(wk[0][j], h[0][j], pre);
-      pre = fmaf(wk[1][j], h[1][j], pre);
-      pre = fmaf(wk[2][j], h[2][j], pre);
-      pre = fmaf(wk[3][j], ut, pre);
-      o.v[j] = from_f32<T>(pre / (1.0f + __expf(-pre)));
-      h[0][j] = h[1][j];
-      h[1][j] = h[2][j];
-      h[2][j] = ut;
+    for (int i = 0; i < kGroup; ++i)
+      if (tg + i < t1) u[i] = load16(in + (row0 + tg + i) * in_stride + c);
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      if (tg + i < t1) {
+        Vec16<T> o;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const float ut = to_f32(u[i].v[j]);
+          float pre = bv[j];
+          pre = fmaf(wk[0][j], h[0][j], pre);
+          pre = fmaf(wk[1][j], h[1][j], pre);
+          pre = fmaf(wk[2][j], h[2][j], pre);
+          pre = fmaf(wk[3][j], ut, pre);
+          o.v[j] = from_f32<T>(pre / (1.0f + __expf(-pre)));
+          h[0][j] = h[1][j];
+          h[1][j] = h[2][j];
+          h[2][j] = ut;
+        }
+        store16(out + (row0 + tg + i) * out_stride + c, o);
+      }
     }
-    store16(out + (row0 + t) * out_stride + c, o);
   }
 
   // Single run per sequence: this thread read the old state, so it may

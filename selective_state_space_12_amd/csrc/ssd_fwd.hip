@@ -39,9 +39,10 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-// Aim for at least this many workgroups (two per CU of the 256-CU part).
+// Aim for at least this many workgroups (one per CU of the 256-CU part: the
+// chunk tiles take most of a CU's LDS).
 #ifndef MMSSD_TARGET_UNITS
-#define MMSSD_TARGET_UNITS 512
+#define MMSSD_TARGET_UNITS 256
 #endif
 
 struct FwdK {
@@ -62,34 +63,38 @@ struct FwdK {
   float* seg_state;  // (batch, heads, nseg, P, N) fp32, or null
   float* seg_decay;  // (batch, heads, nseg) log2 decay of each segment
   int64_t seqlen;
-  int n_heads, heads, Q, QA, nseg, seg_chunks, nchunks;
+  int n_heads, heads, nseg, seg_chunks, nchunks;
 };
 
 template <typename T> constexpr int pad16() { return 16 / (int)sizeof(T); }
 
-template <typename T, int P, int N>
+template <typename T, int P, int N, int Q>
 struct Layout {
-  static constexpr int BP = N + pad16<T>();  // row pitch of B tile (elements)
-  static constexpr int HP = N + pad16<T>();  // row pitch of the operand copy of H
-  __host__ __device__ static int XP(int QA) { return QA + pad16<T>(); }
-  __host__ __device__ static size_t bytes(int QA) {
-    return (size_t)QA * BP * sizeof(T) + (size_t)P * XP(QA) * sizeof(T) +
-           (size_t)P * HP * sizeof(T) + 3 * (size_t)QA * sizeof(float);
-  }
+  static constexpr int QA = Q < 32 ? 32 : Q;  // rows allocated (whole 32-wide column blocks)
+  static constexpr int BP = N + pad16<T>();   // row pitch of the B tile (elements)
+  static constexpr int HP = N + pad16<T>();   // row pitch of the operand copy of H
+  static constexpr int XP = QA + pad16<T>();  // row pitch of the transposed x tile
+  static constexpr size_t bytes = (size_t)QA * BP * sizeof(T) + (size_t)P * XP * sizeof(T) +
+                                  (size_t)P * HP * sizeof(T) + 3 * (size_t)QA * sizeof(float);
 };
 
-template <typename T, int P, int N, bool OUT>
+template <typename T, int P, int N, int Q, bool OUT>
 __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
-  using L = Layout<T, P, N>;
+  using L = Layout<T, P, N, Q>;
   constexpr int TP = P / 16, TN = N / 16, NTILE = TP * TN;
   constexpr int TPW = NTILE >= kWaves ? NTILE / kWaves : 1;  // state tiles per wave
   static_assert(NTILE < kWaves || NTILE % kWaves == 0, "state tiles must split evenly");
   static_assert(TP % TPW == 0, "a wave's state tiles share one column block");
   constexpr int NKB = (N + 31) / 32;  // K=32 slices over d_state
   constexpr int VB = 16 / (int)sizeof(T);
+  constexpr int QA = L::QA, XP = L::XP;
+  constexpr int NBV = (QA * (N / VB) + kThreads - 1) / kThreads;  // B vectors per thread
+  constexpr int NXV = (QA * (P / VB) + kThreads - 1) / kThreads;  // x vectors per thread
+  constexpr int kRBW = 2;                                          // row blocks per wave (Q <= 256)
+  constexpr int E = (QA + 63) / 64;                                // dt values per lane of wave 0
+  constexpr int RB = Q / 16;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const int Q = k.Q, QA = k.QA, XP = L::XP(QA);
   T* Bs = reinterpret_cast<T*>(smem);
   T* XT = Bs + (size_t)QA * L::BP;
   T* Hs = XT + (size_t)P * XP;
@@ -109,6 +114,11 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Ah2 = k.A[h] * kLog2e;
   const float Dh = k.D ? k.D[h] : 0.0f;
+
+  // 16-row output blocks of this wave, dealt in snake order for balance
+  int rb[kRBW];
+#pragma unroll
+  for (int i = 0; i < kRBW; ++i) rb[i] = (i & 1) ? i * kWaves + kWaves - 1 - wave : i * kWaves + wave;
 
   // ---- state tiles owned by this wave: H[pt*16 + g*4 + i][nt*16 + r16] ----
   const int tile0 = wave * TPW;
@@ -130,26 +140,92 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
         hacc[t][i] = (hin && owns) ? hin[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] : 0.0f;
   }
 
+  // ---- registers holding the next chunk's inputs (loaded during compute) ----
+  Vec16<T> pb[NBV], px[NXV];
+  float pdt[E];
+  Frag8<T> cfa[NKB];  // C of this wave's first row block, loaded one step ahead
+
+  // Loads are unconditional (rows past the end of the sequence are clamped to
+  // its last row); the commit below zeroes them, so no lane branches here.
+  auto prefetch = [&](int c) {
+    const int64_t row0 = rowb + (int64_t)c * Q;
+    const int last = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q) - 1;
+#pragma unroll
+    for (int v = 0; v < NBV; ++v) {
+      const int idx = tid + v * kThreads;
+      const int s = min(idx / (N / VB), last), col = (idx % (N / VB)) * VB;
+      pb[v] = load16(Bp + (row0 + s) * k.bs + col);
+    }
+    // x: consecutive lanes take consecutive tokens (same 16-byte column
+    // group), so the transposed LDS writes of a wave hit distinct banks
+#pragma unroll
+    for (int v = 0; v < NXV; ++v) {
+      const int idx = tid + v * kThreads;
+      const int s = min(idx % QA, last), p0 = ((idx / QA) % (P / VB)) * VB;
+      px[v] = load16(Xp + (row0 + s) * k.xs + (int64_t)h * P + p0);
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int s = min(lane * E + e, last);
+        pdt[e] = to_f32(DTp[(row0 + s) * k.dts + h]);
+      }
+    }
+  };
+
+  // C fragments of one 16-row block: lane holds C[t0 + r16][kb*32 + g*8 + j]
+  auto load_c = [&](int c, int r, Frag8<T> (&cf)[NKB]) {
+    const int64_t row0 = rowb + (int64_t)c * Q;
+    const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
+    const int trow = r * 16 + r16;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int n = kb * 32 + g * 8;
+      if (r < RB && trow < len && n < N) frag_load8(cf[kb], Cp + (row0 + trow) * k.cs + n);
+      else frag_zero(cf[kb]);
+    }
+  };
+
   const int c_begin = seg * k.seg_chunks;
   const int c_end = min(c_begin + k.seg_chunks, k.nchunks);
   float lam_seg = 0.0f;
+  if (c_begin < c_end) {
+    prefetch(c_begin);
+    if (OUT) load_c(c_begin, rb[0], cfa);
+  }
 
   for (int c = c_begin; c < c_end; ++c) {
     const int64_t t_base = (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, k.seqlen - t_base);
     const int64_t row0 = rowb + t_base;
 
-    // ---- phase L: dt + decay cumsum (wave 0), B and x tiles, operand copy of H
+    // ---- phase L: prefetched tiles -> LDS (rows >= len zeroed), decay cumsum,
+    // operand copy of H
+#pragma unroll
+    for (int v = 0; v < NBV; ++v) {
+      const int idx = tid + v * kThreads;
+      if (idx < QA * (N / VB)) {
+        const int s = idx / (N / VB), col = (idx % (N / VB)) * VB;
+        store16(Bs + s * L::BP + col, s < len ? pb[v] : zero16<T>());
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NXV; ++v) {
+      const int idx = tid + v * kThreads;
+      if (idx < QA * (P / VB)) {
+        const int s = idx % QA, p0 = (idx / QA) * VB;
+        const Vec16<T> xv = s < len ? px[v] : zero16<T>();
+#pragma unroll
+        for (int j = 0; j < VB; ++j) XT[(p0 + j) * XP + s] = xv.v[j];
+      }
+    }
     if (wave == 0) {
-      constexpr int kMaxE = 4;  // QA <= 256
-      const int E = (QA + 63) / 64;
-      float d[kMaxE], pre[kMaxE];
+      float pre[E];
       float run = 0.0f;
 #pragma unroll
-      for (int e = 0; e < kMaxE; ++e) {
-        const int s = lane * E + e;
-        d[e] = (e < E && s < len) ? to_f32(DTp[(row0 + s) * k.dts + h]) : 0.0f;
-        run += d[e] * Ah2;
+      for (int e = 0; e < E; ++e) {
+        if (lane * E + e >= len) pdt[e] = 0.0f;
+        run += pdt[e] * Ah2;
         pre[e] = run;
       }
       float incl = run;
@@ -161,26 +237,15 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
       const float excl = incl - run;
       const float lend = __shfl(incl, 63);
 #pragma unroll
-      for (int e = 0; e < kMaxE; ++e) {
+      for (int e = 0; e < E; ++e) {
         const int s = lane * E + e;
-        if (e < E && s < QA) {
+        if (s < QA) {
           const float lv = excl + pre[e];
           lam[s] = lv;
-          dtv[s] = d[e];
-          wsc[s] = exp2f(lend - lv) * d[e];
+          dtv[s] = pdt[e];
+          wsc[s] = __builtin_amdgcn_exp2f(lend - lv) * pdt[e];
         }
       }
-    }
-    for (int idx = tid; idx < QA * (N / VB); idx += kThreads) {
-      const int s = idx / (N / VB), col = (idx % (N / VB)) * VB;
-      const Vec16<T> v = s < len ? load16(Bp + (row0 + s) * k.bs + col) : zero16<T>();
-      store16(Bs + s * L::BP + col, v);
-    }
-    for (int idx = tid; idx < QA * (P / VB); idx += kThreads) {
-      const int s = idx / (P / VB), p0 = (idx % (P / VB)) * VB;
-      const Vec16<T> v = s < len ? load16(Xp + (row0 + s) * k.xs + (int64_t)h * P + p0) : zero16<T>();
-#pragma unroll
-      for (int j = 0; j < VB; ++j) XT[(p0 + j) * XP + s] = v.v[j];
     }
     if (OUT && owns) {
 #pragma unroll
@@ -191,127 +256,141 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
     }
     __syncthreads();
 
-    // ---- phase R: outputs of this chunk, 16-row blocks in snake order ----
-    if (OUT) {
-      const int RB = Q / 16;
-      for (int it = 0; it * kWaves < RB; ++it) {
-        const int base = it * kWaves;
-        const int r = (it & 1) ? base + kWaves - 1 - wave : base + wave;
-        const int t0 = r * 16;
-        if (r >= RB || t0 >= len) continue;
-        const int trow = t0 + r16;  // this lane's row of C and of the masked product
+    // next chunk's loads are in flight while this chunk computes
+    if (c + 1 < c_end) prefetch(c + 1);
 
-        Frag8<T> cf[NKB];
+    // ---- phase R: outputs of this chunk ----
+    auto row_block = [&](const int r, const Frag8<T> (&cf)[NKB]) {
+      const int t0 = r * 16;
+      if (r >= RB || t0 >= len) return;
+      const int trow = t0 + r16;  // this lane's row of the masked product
+
+      // Y_off = exp(Lambda_t) * C_t . H_prev
+      f32x4 acc[TP];
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) {
+        acc[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           const int n = kb * 32 + g * 8;
-          if (trow < len && n < N) frag_load8(cf[kb], Cp + (row0 + trow) * k.cs + n);
-          else frag_zero(cf[kb]);
-        }
-
-        // Y_off = exp(Lambda_t) * C_t . H_prev
-        f32x4 acc[TP];
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          acc[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            const int n = kb * 32 + g * 8;
-            Frag8<T> hf;
-            if (n < N) frag_load8(hf, Hs + (pt * 16 + r16) * L::HP + n);
-            else frag_zero(hf);
-            acc[pt] = mma(cf[kb], hf, acc[pt]);
-          }
-        }
-        {
-          float sc[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sc[i] = exp2f(lam[t0 + g * 4 + i]);
-#pragma unroll
-          for (int pt = 0; pt < TP; ++pt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[pt][i] *= sc[i];
-        }
-
-        // Y_diag: (G o L) (x) over the causal 32-wide column blocks
-        const float lam_t = lam[trow];
-        const int nsb = (t0 + 15) / 32 + 1;
-        for (int sb = 0; sb < nsb; ++sb) {
-          const int s0 = sb * 32;
-          f32x4 g0 = {0.0f, 0.0f, 0.0f, 0.0f}, g1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            const int n = kb * 32 + g * 8;
-            Frag8<T> b0, b1;
-            if (n < N) {
-              frag_load8(b0, Bs + (s0 + r16) * L::BP + n);
-              frag_load8(b1, Bs + (s0 + 16 + r16) * L::BP + n);
-            } else {
-              frag_zero(b0);
-              frag_zero(b1);
-            }
-            g0 = mma(b0, cf[kb], g0);  // G^T[s0 + g*4 + i][trow]
-            g1 = mma(b1, cf[kb], g1);  // G^T[s0 + 16 + g*4 + i][trow]
-          }
-          Frag8<T> mf;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int sj = s0 + (j < 4 ? g * 4 + j : 16 + g * 4 + (j - 4));
-            const float gv = j < 4 ? g0[j] : g1[j - 4];
-            float v = 0.0f;
-            if (sj <= trow) v = gv * exp2f(lam_t - lam[sj]) * dtv[sj];
-            frag_set(mf, j, v);
-          }
-#pragma unroll
-          for (int pt = 0; pt < TP; ++pt) {
-            const T* xr = XT + (pt * 16 + r16) * XP + s0 + g * 4;
-            Frag8<T> xf;
-            frag_load4x2(xf, xr, xr + 16);
-            acc[pt] = mma(mf, xf, acc[pt]);
-          }
-        }
-
-        // epilogue: + D x, round, store the head's slice of each token row
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          const int p = pt * 16 + r16;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = t0 + g * 4 + i;
-            if (t < len) {
-              const float xv = to_f32(XT[p * XP + t]);
-              Yp[(row0 + t) * k.ys + (int64_t)h * P + p] = from_f32<T>(acc[pt][i] + Dh * xv);
-            }
-          }
+          Frag8<T> hf;
+          if (n < N) frag_load8(hf, Hs + (pt * 16 + r16) * L::HP + n);
+          else frag_zero(hf);
+          acc[pt] = mma(cf[kb], hf, acc[pt]);
         }
       }
+      {
+        float sc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sc[q] = __builtin_amdgcn_exp2f(lam[t0 + g * 4 + q]);
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[pt][q] *= sc[q];
+      }
+
+      // Y_diag: (G o L) (x) over the causal 32-wide column blocks
+      const float lam_t = lam[trow];
+      const int nsb = (t0 + 15) / 32 + 1;
+#pragma unroll 1
+      for (int sb = 0; sb < nsb; ++sb) {
+        const int s0 = sb * 32;
+        f32x4 g0 = {0.0f, 0.0f, 0.0f, 0.0f}, g1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int n = kb * 32 + g * 8;
+          Frag8<T> b0, b1;
+          if (n < N) {
+            frag_load8(b0, Bs + (s0 + r16) * L::BP + n);
+            frag_load8(b1, Bs + (s0 + 16 + r16) * L::BP + n);
+          } else {
+            frag_zero(b0);
+            frag_zero(b1);
+          }
+          g0 = mma(b0, cf[kb], g0);  // G^T[s0 + g*4 + q][trow]
+          g1 = mma(b1, cf[kb], g1);  // G^T[s0 + 16 + g*4 + q][trow]
+        }
+        // masked decay: M[t][s] = G[t][s] * exp2(lam_t - lam_s) * dt_s for s <= t;
+        // column blocks before the diagonal one need no mask
+        const f32x4 la = *reinterpret_cast<const f32x4*>(lam + s0 + g * 4);
+        const f32x4 lb = *reinterpret_cast<const f32x4*>(lam + s0 + 16 + g * 4);
+        const f32x4 da = *reinterpret_cast<const f32x4*>(dtv + s0 + g * 4);
+        const f32x4 db = *reinterpret_cast<const f32x4*>(dtv + s0 + 16 + g * 4);
+        Frag8<T> mf;
+        if (sb + 1 < nsb) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            frag_set(mf, j, g0[j] * __builtin_amdgcn_exp2f(lam_t - la[j]) * da[j]);
+            frag_set(mf, j + 4, g1[j] * __builtin_amdgcn_exp2f(lam_t - lb[j]) * db[j]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int sa = s0 + g * 4 + j, sbb = sa + 16;
+            frag_set(mf, j, sa <= trow ? g0[j] * __builtin_amdgcn_exp2f(lam_t - la[j]) * da[j] : 0.0f);
+            frag_set(mf, j + 4, sbb <= trow ? g1[j] * __builtin_amdgcn_exp2f(lam_t - lb[j]) * db[j] : 0.0f);
+          }
+        }
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) {
+          const T* xr = XT + (pt * 16 + r16) * XP + s0 + g * 4;
+          Frag8<T> xf;
+          frag_load4x2(xf, xr, xr + 16);
+          acc[pt] = mma(mf, xf, acc[pt]);
+        }
+      }
+
+      // epilogue: + D x, round, store the head's slice of each token row
+      T* ybase = Yp + (row0 + t0 + g * 4) * k.ys + (int64_t)h * P + r16;
+      const bool full = t0 + 16 <= len;
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) {
+        // x[t0 + g*4 + q][p] for q = 0..3: four consecutive entries of XT's row p
+        Frag8<T> xq;
+        const T* xrow = XT + (pt * 16 + r16) * XP + t0 + g * 4;
+        frag_load4x2(xq, xrow, xrow);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (full || t0 + g * 4 + q < len)
+            ybase[q * k.ys + pt * 16] = from_f32<T>(acc[pt][q] + Dh * to_f32(xq.v[q]));
+        }
+      }
+    };
+    if (OUT) {
+      static_assert(kRBW == 2, "two row blocks per wave");
+      Frag8<T> cfb[NKB];
+      load_c(c, rb[1], cfb);  // in flight while the first row block computes
+      row_block(rb[0], cfa);
+      row_block(rb[1], cfb);
+      if (c + 1 < c_end) load_c(c + 1, rb[0], cfa);  // in flight across phase U
     }
 
     // ---- phase U: H <- exp(Lambda_end) H + (w o x)^T B, w_s = exp(Lambda_end - Lambda_s) dt_s
     const float lend = lam[QA - 1];
     lam_seg += lend;
     if (owns) {
-      const float dec = exp2f(lend);
+      const float dec = __builtin_amdgcn_exp2f(lend);
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hacc[t][i] *= dec;
+        for (int q = 0; q < 4; ++q) hacc[t][q] *= dec;
       const int nsbu = (len + 31) / 32;
+#pragma unroll 1
       for (int sb = 0; sb < nsbu; ++sb) {
         const int s0 = sb * 32 + g * 8;
+        // B operand (k = s, n): the decay weight w_s is folded in here, once
+        // per column block, so the x operand is a plain tile read
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(wsc + s0);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wsc + s0 + 4);
         Frag8<T> bfv;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bfv.v[j] = Bs[(s0 + j) * L::BP + nt * 16 + r16];
-        float wj[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) wj[j] = wsc[s0 + j];
+        for (int j = 0; j < 8; ++j)
+          frag_set(bfv, j, to_f32(Bs[(s0 + j) * L::BP + nt * 16 + r16]) * (j < 4 ? w0[j] : w1[j - 4]));
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-          Frag8<T> xf, af;
+          Frag8<T> xf;
           frag_load8(xf, XT + ((pt0 + t) * 16 + r16) * XP + s0);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) frag_set(af, j, to_f32(xf.v[j]) * wj[j]);
-          hacc[t] = mma(af, bfv, hacc[t]);
+          hacc[t] = mma(xf, bfv, hacc[t]);
         }
       }
     }
@@ -330,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hout[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] = hacc[t][i];
+      for (int q = 0; q < 4; ++q) hout[((pt0 + t) * 16 + g * 4 + q) * N + nt * 16 + r16] = hacc[t][q];
   }
 }
 
@@ -354,26 +433,25 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(float* __restrict__ se
   }
 }
 
-template <typename T, int P, int N>
+template <typename T, int P, int N, int Q>
 hipError_t launch_shape(const FwdArgs& a, void* ws, hipStream_t s) {
-  using L = Layout<T, P, N>;
+  using L = Layout<T, P, N, Q>;
   FwdK k;
   k.x = a.x; k.xs = a.xs; k.dt = a.dt; k.dts = a.dts; k.A = a.A;
   k.B = a.B; k.bs = a.bs; k.C = a.C; k.cs = a.cs; k.D = a.D;
   k.y = a.y; k.ys = a.ys; k.h0 = a.h0; k.hT = a.hT;
   k.seqlen = a.seqlen; k.n_heads = a.n_heads; k.heads = a.heads;
-  k.Q = a.chunk; k.QA = a.chunk < 32 ? 32 : a.chunk;
-  fwd_plan(a.batch, a.seqlen, a.heads, a.chunk, &k.nchunks, &k.nseg, &k.seg_chunks);
+  fwd_plan(a.batch, a.seqlen, a.heads, Q, &k.nchunks, &k.nseg, &k.seg_chunks);
   k.seg_state = nullptr;
   k.seg_decay = nullptr;
   if (k.nseg > 1) {
     k.seg_state = static_cast<float*>(ws);
     k.seg_decay = k.seg_state + (size_t)a.batch * a.heads * k.nseg * P * N;
   }
-  const size_t lds = L::bytes(k.QA);
+  const size_t lds = L::bytes;
   hipError_t e;
   if (k.nseg > 1) {
-    auto pre = ssd_chunk_kernel<T, P, N, false>;
+    auto pre = ssd_chunk_kernel<T, P, N, Q, false>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(pre),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -383,7 +461,7 @@ hipError_t launch_shape(const FwdArgs& a, void* ws, hipStream_t s) {
                        k.seg_state, k.seg_decay, a.h0, a.n_heads, a.heads, k.nseg, P * N);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  auto main_k = ssd_chunk_kernel<T, P, N, true>;
+  auto main_k = ssd_chunk_kernel<T, P, N, Q, true>;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(main_k),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -391,11 +469,26 @@ hipError_t launch_shape(const FwdArgs& a, void* ws, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int P, int N>
+hipError_t launch_chunk(const FwdArgs& a, void* ws, hipStream_t s) {
+  switch (a.chunk) {
+    case 16: return launch_shape<T, P, N, 16>(a, ws, s);
+    case 32: return launch_shape<T, P, N, 32>(a, ws, s);
+    case 64: return launch_shape<T, P, N, 64>(a, ws, s);
+    case 128: return launch_shape<T, P, N, 128>(a, ws, s);
+    case 256:
+      // fp32 tiles of 256 tokens with d_state 128 do not fit one CU's LDS
+      if constexpr (sizeof(T) == 4 && N == 128) return hipErrorInvalidValue;
+      else return launch_shape<T, P, N, 256>(a, ws, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T>
 hipError_t launch_typed(const FwdArgs& a, void* ws, hipStream_t s) {
-  if (a.d_head == 32 && a.d_state == 16) return launch_shape<T, 32, 16>(a, ws, s);
-  if (a.d_head == 64 && a.d_state == 64) return launch_shape<T, 64, 64>(a, ws, s);
-  if (a.d_head == 64 && a.d_state == 128) return launch_shape<T, 64, 128>(a, ws, s);
+  if (a.d_head == 32 && a.d_state == 16) return launch_chunk<T, 32, 16>(a, ws, s);
+  if (a.d_head == 64 && a.d_state == 64) return launch_chunk<T, 64, 64>(a, ws, s);
+  if (a.d_head == 64 && a.d_state == 128) return launch_chunk<T, 64, 128>(a, ws, s);
   return hipErrorInvalidValue;
 }
 

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(
     int P, int heads_cap, const int32_t* __restrict__ heads_per_seq) {
   constexpr int N = LPR * 4;
   constexpr int kRowsPerPass = kStepThreads / LPR;
-  constexpr int kUnroll = 4;
+  constexpr int kUnroll = 8;  // state rows in flight per thread
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   if (h >= clamp_heads(heads_per_seq, b, heads_cap)) return;

@@ -113,9 +113,10 @@ int validate_ssd_forward(const void* x, int64_t x_row_stride, const void* dt,
                               n_heads_active, chunk, dtype);
   if (st != MM_OK) return st;
   const int64_t el = dtype_bytes(dtype);
-  const int64_t xw = n_heads * d_head;
+  // only the active prefix of each token row is read or written
+  const int64_t xw = n_heads_active * d_head;
   const int64_t bw = ngroups * d_state;
-  if (x_row_stride < xw || y_row_stride < xw || dt_row_stride < n_heads ||
+  if (x_row_stride < xw || y_row_stride < xw || dt_row_stride < n_heads_active ||
       b_row_stride < bw || c_row_stride < bw)
     return MM_ERR_SHAPE;
   const int64_t rows = batch * seqlen;
@@ -151,9 +152,9 @@ int validate_ssd_step(const float* state, const void* x_t, int64_t x_row_stride,
   if (ngroups != 1) return MM_ERR_UNSUPPORTED;
   if (d_state != 16 && d_state != 32 && d_state != 64 && d_state != 128 && d_state != 256)
     return MM_ERR_UNSUPPORTED;
-  const int64_t xw = n_heads * d_head;
+  const int64_t xw = n_heads_active * d_head;
   const int64_t bw = ngroups * d_state;
-  if (x_row_stride < xw || y_row_stride < xw || dt_row_stride < n_heads ||
+  if (x_row_stride < xw || y_row_stride < xw || dt_row_stride < n_heads_active ||
       b_row_stride < bw || c_row_stride < bw)
     return MM_ERR_SHAPE;
   if (!mul_ok(batch, x_row_stride) || !mul_ok(batch, y_row_stride) ||
