@@ -1,0 +1,381 @@
+"""Benchmark of the Matryoshka-sliced conv1d + selective-scan hot path on one GPU.
+
+One step = the prefill path of the 1.4B-scale block on one batch of seeded
+synthetic input resident in HBM: causal conv1d (kernel 4) + SiLU over the
+[x | B | C] stream (b=4, l=8192, 4352 channels, bf16), then the chunked
+selective scan on strided views of the conv output (64 heads of 64, d_state
+128, chunk 256, full width m=2048).  ``value`` is tokens/s of that step.
+
+Also reported on the same JSON line:
+  - ``roofline``: the scan kernel's algorithmic HBM bytes per launch divided by
+    its own duration (HIP events around each scan launch inside the timed
+    steps, on the stream it runs on), against MI355X's 8 TB/s;
+  - ``slices``: scan-only tokens/s and HBM fraction at every Matryoshka width;
+  - ``decode``: the recurrent decode step (conv state roll + scan step) for a
+    batch of 256 sequences at mixed widths, 1024 tokens captured in a HIP graph;
+  - ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample
+    of the same workload, scaled to the step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ssd_scan_1p4b_m2048.json")
+SCAN_SRC = os.path.join(ROOT, "selective_state_space_12_amd", "csrc", "ssd_fwd.hip")
+
+
+COPY_BYTES = 1 << 30
+
+
+def _pmc_per_dispatch(dirname: str, counter: str, kernel_substr: str, min_grid: int = 0):
+    """Mean value (KiB) of a counter over the dispatches of one kernel, from a
+    rocprofv3 --output-format csv counter_collection file."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row.get("Counter_Name") != counter or kernel_substr not in row.get("Kernel_Name", ""):
+                continue
+            if int(row.get("Grid_Size", 0)) < min_grid:
+                continue
+            key = (f, row.get("Dispatch_Id"))
+            vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernel '{kernel_substr}' under {dirname}")
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def summarize_pmc(scan_fetch, scan_write, copy_fetch, copy_write):
+    """HBM bytes per scan launch: FETCH_SIZE + WRITE_SIZE of the scan kernel,
+    each scaled by what the same counter reads for a copy of known size."""
+    sf, nsf = _pmc_per_dispatch(scan_fetch, "FETCH_SIZE", "ssd_chunk_kernel")
+    sw, nsw = _pmc_per_dispatch(scan_write, "WRITE_SIZE", "ssd_chunk_kernel")
+    # the calibration copy is the only large copy dispatch of its run
+    cf, _ = _pmc_per_dispatch(copy_fetch, "FETCH_SIZE", "copyBuffer", min_grid=1 << 16)
+    cw, _ = _pmc_per_dispatch(copy_write, "WRITE_SIZE", "copyBuffer", min_grid=1 << 16)
+    kf = COPY_BYTES / (cf * 1024.0)
+    kw = COPY_BYTES / (cw * 1024.0)
+    total = sf * 1024.0 * kf + sw * 1024.0 * kw
+    import synth
+    w = synth.WORKLOADS["1.4b"]
+    alg = scan_bytes(w.batch * w.seqlen, w.n_heads, w.d_head, w.d_state, 2)
+    rec = {"kernel": "ssd_chunk_kernel<bf16, 64, 128, 256, main>",
+           "workload": "1.4B-scale scan, b=4 l=8192, 64 heads, chunk 256, inputs as in bench.py",
+           "kernel_source_sha256_16": src_hash(),
+           "fetch_kib_per_dispatch": sf, "write_kib_per_dispatch": sw,
+           "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+                                "fetch_scale": kf, "write_scale": kw},
+           "hbm_bytes_per_launch": total, "alg_bytes_per_launch": alg,
+           "traffic_over_alg": total / alg, "dispatches": [nsf, nsw]}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(rec))
+
+
+def scan_bytes(tokens: int, heads: int, P: int, N: int, elem: int) -> int:
+    """Algorithmic HBM bytes of one scan call: x and y of the active heads,
+    B and C, and dt of the active heads (A, D negligible)."""
+    return tokens * (2 * heads * P * elem + 2 * N * elem + heads * elem)
+
+
+def conv_bytes(tokens: int, channels: int, elem: int) -> int:
+    return tokens * channels * elem * 2
+
+
+def decode_bytes(heads_per_seq, P: int, N: int, d_inner: int) -> int:
+    """Per decode step: fp32 state read+write of active heads, conv state
+    read+write and xbc input of active channels, dt and y (fp32)."""
+    tot = 0
+    for h in heads_per_seq:
+        ch = h * P + 2 * N
+        tot += h * P * N * 4 * 2 + ch * 3 * 4 * 2 + ch * 4 * 2 + h * 4 + h * P * 4
+    return tot
+
+
+def src_hash() -> str:
+    return hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per scan launch measured with rocprofv3 (FETCH_SIZE and
+    WRITE_SIZE, calibrated on a copy kernel), if taken on this kernel source."""
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != src_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-slices", action="store_true")
+    ap.add_argument("--mode", choices=["step", "scan", "copy"], default="step",
+                    help="scan: only the full-width scan (for counter runs); "
+                         "copy: a 1 GiB device copy that calibrates the HBM byte counters")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("SCAN_FETCH", "SCAN_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc output dirs (csv); writes the traffic record under profiles/")
+    args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the scan shards by batch and head with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_12_amd as mm
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS["1.4b"]
+    b, l, H, P, N = w.batch, w.seqlen, w.n_heads, w.d_head, w.d_state
+    tokens = b * l
+    elem = 2
+    print(f"# generating inputs for {w.name}: b={b} l={l} conv_dim={w.conv_dim}", file=sys.stderr, flush=True)
+    xi = synth.xbc_inputs(w)
+    xbc_raw = xi["xbc"].to(dev)
+    conv_w = xi["w"].to(dev)
+    dt = synth.pipeline_dt(w).to(dev)
+    A = synth.draw_A(w).to(dev)
+    D = synth.draw_D(w).to(dev)
+    del xi
+    xbc = torch.empty_like(xbc_raw)
+    y = torch.empty((b, l, H, P), dtype=w.dtype, device=dev)
+    xv = xbc[..., :w.d_inner].view(b, l, H, P)
+    Bv = xbc[..., w.d_inner:w.d_inner + N].unsqueeze(2)
+    Cv = xbc[..., w.d_inner + N:].unsqueeze(2)
+    ws_bytes = mm.ssd_forward_workspace_size(b, l, H, P, N, 1, H, w.chunk, w.dtype)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def scan(heads):
+        mm.ssd_forward(xv, dt, A, Bv, Cv, D, n_heads_active=heads, chunk=w.chunk, y=y,
+                       workspace=ws)
+
+    def conv(heads):
+        mm.conv1d_silu(xbc_raw, conv_w, None, None, d_inner=w.d_inner, d_head=P,
+                       d_state=N, n_heads_active=heads, out=xbc)
+
+    if args.mode == "scan":  # counter runs: the full-width scan alone
+        conv(H)
+        for _ in range(args.warmup + args.steps):
+            scan(H)
+        torch.cuda.synchronize()
+        print(f"# scan-only: {args.warmup + args.steps} launches", file=sys.stderr)
+        return
+    if args.mode == "copy":  # counter calibration: a plain copy of known size
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy: {args.warmup + args.steps} x {COPY_BYTES} bytes", file=sys.stderr)
+        return
+
+    # ---- the step: conv + scan at full width --------------------------------
+    for _ in range(args.warmup):
+        conv(H)
+        scan(H)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        conv(H)
+        ev[i][0].record(stream)
+        scan(H)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    scan_ms = sorted(a.elapsed_time(z) for a, z in ev)
+    scan_avg_ms = sum(scan_ms) / len(scan_ms)
+    value = tokens / (ms_step * 1e-3)
+
+    alg = scan_bytes(tokens, H, P, N, elem)
+    achieved = alg / (scan_avg_ms * 1e-3) / 1e9
+    traffic = load_traffic()
+
+    out = {
+        "metric": "SSD scan tokens/s per Matryoshka slice; % of MI355X MFMA/HBM roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) xBC stream, log-uniform dt in [1e-3, 1e-1]; no dataset)",
+        "config": {"workload": "1.4B-scale MatMamba block prefill: conv1d(k=4)+SiLU then chunked "
+                               "selective scan, b=4 l=8192 d_model=2048 d_inner=4096 64 heads x 64, "
+                               "d_state=128, chunk=256, slice m=2048 (64 heads)",
+                   "global_batch": b, "seq_len": l, "parallelism": "single GPU"},
+        "roofline": {"kernel": "ssd_chunk_kernel (scan)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "alg_bytes_per_launch": alg, "avg_launch_ms": scan_avg_ms},
+    }
+
+    # ---- every Matryoshka width, scan only -----------------------------------
+    if not args.no_slices:
+        slices = {}
+        for m in w.slices:
+            h = w.heads(m)
+            for _ in range(3):
+                scan(h)
+            torch.cuda.synchronize()
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            reps = 10
+            s0.record(stream)
+            for _ in range(reps):
+                scan(h)
+            s1.record(stream)
+            torch.cuda.synchronize()
+            t = s0.elapsed_time(s1) / reps
+            ab = scan_bytes(tokens, h, P, N, elem)
+            slices[str(m)] = {"heads": h, "scan_ms": t, "tokens_per_s": tokens / (t * 1e-3),
+                              "hbm_frac": ab / (t * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+        # conv alone at full width
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(10):
+            conv(H)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        tc = c0.elapsed_time(c1) / 10
+        cb = conv_bytes(tokens, w.conv_dim, elem)
+        out["slices"] = slices
+        out["conv"] = {"ms": tc, "hbm_frac": cb / (tc * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+
+    # ---- decode: conv state roll + scan step, 1024 tokens in a HIP graph -----
+    if not args.no_decode:
+        out["decode"] = bench_decode(torch, mm, synth, dev)
+
+    # ---- CPU baseline: the oracle on a bounded sample --------------------------
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w)
+
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(torch, mm, synth, dev):
+    d = synth.WORKLOADS["decode"]
+    bsz, H, P, N, cd = d.batch, d.n_heads, d.d_head, d.d_state, d.conv_dim
+    pool = synth.decode_pool(d, pool=64)
+    xbc_t = pool["xbc_t"].to(dev)          # (64, b, cd) fp32
+    dt_t = pool["dt_t"].to(dev)            # (64, b, H)
+    hv_cpu = synth.decode_heads(d)
+    hv = hv_cpu.to(dev)
+    A = synth.draw_A(d).to(dev)
+    D = synth.draw_D(d).to(dev)
+    cw = synth.draw_conv_w(d).to(dev)
+    state = torch.zeros((bsz, H, P, N), device=dev)
+    cstate = torch.zeros((bsz, 3, cd), device=dev)
+    u = torch.empty((bsz, 1, cd), device=dev)
+    yt = torch.empty((bsz, H, P), device=dev)
+
+    def one(k):
+        mm.conv1d_silu(xbc_t[k].unsqueeze(1), cw, None, cstate, d_inner=d.d_inner, d_head=P,
+                       d_state=N, n_heads_active=H, heads_per_seq=hv, out=u)
+        u2 = u[:, 0]
+        mm.ssd_step(state, u2[:, :d.d_inner].view(bsz, H, P), dt_t[k], A,
+                    u2[:, d.d_inner:d.d_inner + N], u2[:, d.d_inner + N:], D,
+                    n_heads_active=H, heads_per_seq=hv, y=yt)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for k in range(4):
+            one(k)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(64):
+            one(k)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = d.steps // 64
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    steps = reps * 64
+    per_step_us = ms * 1e3 / steps
+    by = decode_bytes(hv_cpu.tolist(), P, N, d.d_inner)
+    return {"workload": "decode: batch 256, 64 heads x 64 x 128 fp32 state, slices "
+                        "round-robin {16,32,64} heads, 1024 tokens in a HIP graph",
+            "tokens_per_s": bsz * steps / (ms * 1e-3), "us_per_step": per_step_us,
+            "bytes_per_step": by, "hbm_frac": by / (per_step_us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+
+
+def cpu_baseline(w):
+    """The fp64 oracle as it stands, on the host cores, over one full step of the
+    same workload (conv over all 4352 channels, then the scan for all 64 heads
+    of the 4 sequences of 8192 tokens) -- about 86 GFLOP of fp64 work."""
+    import oracle
+    import synth
+
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    b, l, H, P, N = w.batch, w.seqlen, w.n_heads, w.d_head, w.d_state
+    xi = synth.xbc_inputs(w)
+    u = xi["xbc"].double().numpy()
+    cw = xi["w"].double().numpy()
+    dt = synth.pipeline_dt(w).double().numpy()
+    A = synth.draw_A(w).double().numpy()
+    D = synth.draw_D(w).double().numpy()
+    del xi
+    oracle.build()
+    t0 = time.perf_counter()
+    xo, _ = oracle.conv1d_silu(u, cw, None, None, d_inner=w.d_inner, d_head=P)
+    t1 = time.perf_counter()
+    del u
+    x = xo[..., :w.d_inner].reshape(b, l, H, P)
+    Bm = xo[..., w.d_inner:w.d_inner + N]
+    Cm = xo[..., w.d_inner + N:]
+    oracle.ssd_forward(x, dt, A, Bm, Cm, D, return_state=False)
+    t2 = time.perf_counter()
+    return {"value": b * l / (t2 - t0), "unit": "tokens/s", "cores": int(os.environ["OMP_NUM_THREADS"]),
+            "kind": "oracle",
+            "sample": f"one full step (b={b}, l={l}): fp64 conv {t1 - t0:.1f}s + scan {t2 - t1:.1f}s "
+                      f"on {os.environ['OMP_NUM_THREADS']} threads"}
+
+
+if __name__ == "__main__":
+    main()

@@ -39,6 +39,7 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
+constexpr int kXcds = 8;  // accelerator complex dies of the MI355X, each with its own L2
 // Aim for at least this many workgroups (one per CU of the 256-CU part: the
 // chunk tiles take most of a CU's LDS).
 #ifndef MMSSD_TARGET_UNITS
@@ -75,7 +76,7 @@ struct Layout {
   static constexpr int HP = N + pad16<T>();   // row pitch of the operand copy of H
   static constexpr int XP = QA + pad16<T>();  // row pitch of the transposed x tile
   static constexpr size_t bytes = (size_t)QA * BP * sizeof(T) + (size_t)P * XP * sizeof(T) +
-                                  (size_t)P * HP * sizeof(T) + 3 * (size_t)QA * sizeof(float);
+                                  (size_t)P * HP * sizeof(T) + 4 * (size_t)QA * sizeof(float);
 };
 
 template <typename T, int P, int N, int Q, bool OUT>
@@ -101,8 +102,17 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
   float* lam = reinterpret_cast<float*>(Hs + (size_t)P * L::HP);
   float* dtv = lam + QA;
   float* wsc = dtv + QA;
+  float* efac = wsc + QA;
 
-  const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // XCD-aware unit mapping: workgroups are dealt round-robin to the 8 XCDs in
+  // dispatch order, so give each XCD a contiguous block of (sequence, head,
+  // segment) units -- heads that share a sequence's B and C tiles then share
+  // one XCD's L2.
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int total = gx * gy * gridDim.z;
+  const int pid = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int uid = total % kXcds == 0 ? (pid % kXcds) * (total / kXcds) + pid / kXcds : pid;
+  const int seg = uid % gx, h = (uid / gx) % gy, b = uid / (gx * gy);
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int r16 = lane % 16, g = lane / 16;
 
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
   // ---- registers holding the next chunk's inputs (loaded during compute) ----
   Vec16<T> pb[NBV], px[NXV];
   float pdt[E];
-  Frag8<T> cfa[NKB];  // C of this wave's first row block, loaded one step ahead
+  Frag8<T> cfa[NKB], cfb[NKB];  // C of this wave's two row blocks, loaded a chunk ahead
 
   // Loads are unconditional (rows past the end of the sequence are clamped to
   // its last row); the commit below zeroes them, so no lane branches here.
@@ -191,7 +201,10 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
   float lam_seg = 0.0f;
   if (c_begin < c_end) {
     prefetch(c_begin);
-    if (OUT) load_c(c_begin, rb[0], cfa);
+    if (OUT) {
+      load_c(c_begin, rb[0], cfa);
+      load_c(c_begin, rb[1], cfb);
+    }
   }
 
   for (int c = c_begin; c < c_end; ++c) {
@@ -246,6 +259,16 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
           wsc[s] = __builtin_amdgcn_exp2f(lend - lv) * pdt[e];
         }
       }
+      // efac_s = exp2(lam_e - lam_s) dt_s with e the last token of s's
+      // 32-wide column block (token s | 31, held by lane (s|31)/E, slot E-1)
+      static_assert(32 % E == 0, "a column block spans whole lanes");
+      const float lane_last = excl + pre[E - 1];
+      const float lam_blk_end = __shfl(lane_last, lane | (32 / E - 1));
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int s = lane * E + e;
+        if (s < QA) efac[s] = __builtin_amdgcn_exp2f(lam_blk_end - (excl + pre[e])) * pdt[e];
+      }
     }
     if (OUT && owns) {
 #pragma unroll
@@ -259,113 +282,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
     // next chunk's loads are in flight while this chunk computes
     if (c + 1 < c_end) prefetch(c + 1);
 
-    // ---- phase R: outputs of this chunk ----
-    auto row_block = [&](const int r, const Frag8<T> (&cf)[NKB]) {
-      const int t0 = r * 16;
-      if (r >= RB || t0 >= len) return;
-      const int trow = t0 + r16;  // this lane's row of the masked product
-
-      // Y_off = exp(Lambda_t) * C_t . H_prev
-      f32x4 acc[TP];
-#pragma unroll
-      for (int pt = 0; pt < TP; ++pt) {
-        acc[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const int n = kb * 32 + g * 8;
-          Frag8<T> hf;
-          if (n < N) frag_load8(hf, Hs + (pt * 16 + r16) * L::HP + n);
-          else frag_zero(hf);
-          acc[pt] = mma(cf[kb], hf, acc[pt]);
-        }
-      }
-      {
-        float sc[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sc[q] = __builtin_amdgcn_exp2f(lam[t0 + g * 4 + q]);
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[pt][q] *= sc[q];
-      }
-
-      // Y_diag: (G o L) (x) over the causal 32-wide column blocks
-      const float lam_t = lam[trow];
-      const int nsb = (t0 + 15) / 32 + 1;
-#pragma unroll 1
-      for (int sb = 0; sb < nsb; ++sb) {
-        const int s0 = sb * 32;
-        f32x4 g0 = {0.0f, 0.0f, 0.0f, 0.0f}, g1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const int n = kb * 32 + g * 8;
-          Frag8<T> b0, b1;
-          if (n < N) {
-            frag_load8(b0, Bs + (s0 + r16) * L::BP + n);
-            frag_load8(b1, Bs + (s0 + 16 + r16) * L::BP + n);
-          } else {
-            frag_zero(b0);
-            frag_zero(b1);
-          }
-          g0 = mma(b0, cf[kb], g0);  // G^T[s0 + g*4 + q][trow]
-          g1 = mma(b1, cf[kb], g1);  // G^T[s0 + 16 + g*4 + q][trow]
-        }
-        // masked decay: M[t][s] = G[t][s] * exp2(lam_t - lam_s) * dt_s for s <= t;
-        // column blocks before the diagonal one need no mask
-        const f32x4 la = *reinterpret_cast<const f32x4*>(lam + s0 + g * 4);
-        const f32x4 lb = *reinterpret_cast<const f32x4*>(lam + s0 + 16 + g * 4);
-        const f32x4 da = *reinterpret_cast<const f32x4*>(dtv + s0 + g * 4);
-        const f32x4 db = *reinterpret_cast<const f32x4*>(dtv + s0 + 16 + g * 4);
-        Frag8<T> mf;
-        if (sb + 1 < nsb) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            frag_set(mf, j, g0[j] * __builtin_amdgcn_exp2f(lam_t - la[j]) * da[j]);
-            frag_set(mf, j + 4, g1[j] * __builtin_amdgcn_exp2f(lam_t - lb[j]) * db[j]);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int sa = s0 + g * 4 + j, sbb = sa + 16;
-            frag_set(mf, j, sa <= trow ? g0[j] * __builtin_amdgcn_exp2f(lam_t - la[j]) * da[j] : 0.0f);
-            frag_set(mf, j + 4, sbb <= trow ? g1[j] * __builtin_amdgcn_exp2f(lam_t - lb[j]) * db[j] : 0.0f);
-          }
-        }
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          const T* xr = XT + (pt * 16 + r16) * XP + s0 + g * 4;
-          Frag8<T> xf;
-          frag_load4x2(xf, xr, xr + 16);
-          acc[pt] = mma(mf, xf, acc[pt]);
-        }
-      }
-
-      // epilogue: + D x, round, store the head's slice of each token row
-      T* ybase = Yp + (row0 + t0 + g * 4) * k.ys + (int64_t)h * P + r16;
-      const bool full = t0 + 16 <= len;
-#pragma unroll
-      for (int pt = 0; pt < TP; ++pt) {
-        // x[t0 + g*4 + q][p] for q = 0..3: four consecutive entries of XT's row p
-        Frag8<T> xq;
-        const T* xrow = XT + (pt * 16 + r16) * XP + t0 + g * 4;
-        frag_load4x2(xq, xrow, xrow);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (full || t0 + g * 4 + q < len)
-            ybase[q * k.ys + pt * 16] = from_f32<T>(acc[pt][q] + Dh * to_f32(xq.v[q]));
-        }
-      }
-    };
-    if (OUT) {
-      static_assert(kRBW == 2, "two row blocks per wave");
-      Frag8<T> cfb[NKB];
-      load_c(c, rb[1], cfb);  // in flight while the first row block computes
-      row_block(rb[0], cfa);
-      row_block(rb[1], cfb);
-      if (c + 1 < c_end) load_c(c + 1, rb[0], cfa);  // in flight across phase U
-    }
-
     // ---- phase U: H <- exp(Lambda_end) H + (w o x)^T B, w_s = exp(Lambda_end - Lambda_s) dt_s
+    // (registers only; the outputs below use the operand copy of H_prev in LDS)
     const float lend = lam[QA - 1];
     lam_seg += lend;
     if (owns) {
@@ -394,6 +312,276 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
         }
       }
     }
+    // ---- phase R: outputs of this chunk ----
+    // Lane holds G^T[s0 + g*4 + q][t] (gA) and G^T[s0 + 16 + g*4 + q][t] (gB)
+    // for its row t; the masked decay turns them into the A operand of M . x.
+    // Column blocks left of the diagonal use the factored decay
+    //   exp2(lam_t - lam_s) dt_s = exp2(lam_t - lam_e) * efac_s,
+    //   efac_s = exp2(lam_e - lam_s) dt_s,  e = last token of the block,
+    // both factors <= 1 when A < 0; the diagonal block uses the direct form.
+    auto build_m = [&](const f32x4& gA, const f32x4& gB, int s0, int trow, float lam_t,
+                       bool diag) {
+      Frag8<T> mf;
+      if (!diag) {
+        const float et = __builtin_amdgcn_exp2f(lam_t - lam[s0 + 31]);
+        const f32x4 ea = *reinterpret_cast<const f32x4*>(efac + s0 + g * 4);
+        const f32x4 eb = *reinterpret_cast<const f32x4*>(efac + s0 + 16 + g * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          frag_set(mf, j, gA[j] * ea[j] * et);
+          frag_set(mf, j + 4, gB[j] * eb[j] * et);
+        }
+      } else {
+        const f32x4 la = *reinterpret_cast<const f32x4*>(lam + s0 + g * 4);
+        const f32x4 lb = *reinterpret_cast<const f32x4*>(lam + s0 + 16 + g * 4);
+        const f32x4 da = *reinterpret_cast<const f32x4*>(dtv + s0 + g * 4);
+        const f32x4 db = *reinterpret_cast<const f32x4*>(dtv + s0 + 16 + g * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int sa = s0 + g * 4 + j;
+          frag_set(mf, j, sa <= trow ? gA[j] * __builtin_amdgcn_exp2f(lam_t - la[j]) * da[j] : 0.0f);
+          frag_set(mf, j + 4,
+                   sa + 16 <= trow ? gB[j] * __builtin_amdgcn_exp2f(lam_t - lb[j]) * db[j] : 0.0f);
+        }
+      }
+      return mf;
+    };
+    // B operand rows s0 + r16 and s0 + 16 + r16 of K-slice kb (d_state)
+    auto load_bpair = [&](int s0, int kb, Frag8<T>& b0, Frag8<T>& b1) {
+      const int n = kb * 32 + g * 8;
+      if (n < N) {
+        frag_load8(b0, Bs + (s0 + r16) * L::BP + n);
+        frag_load8(b1, Bs + (s0 + 16 + r16) * L::BP + n);
+      } else {
+        frag_zero(b0);
+        frag_zero(b1);
+      }
+    };
+    auto load_xpair = [&](int s0, int pt, Frag8<T>& xf) {
+      const T* xr = XT + (pt * 16 + r16) * XP + s0 + g * 4;
+      frag_load4x2(xf, xr, xr + 16);
+    };
+    // epilogue: + D x, round, store the head's slice of each token row
+    auto store_rows = [&](const f32x4 (&acc)[TP], int t0, bool full) {
+      T* ybase = Yp + (row0 + t0 + g * 4) * k.ys + (int64_t)h * P + r16;
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) {
+        // x[t0 + g*4 + q][p] for q = 0..3: four consecutive entries of XT's row p
+        Frag8<T> xq;
+        const T* xrow = XT + (pt * 16 + r16) * XP + t0 + g * 4;
+        frag_load4x2(xq, xrow, xrow);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (full || t0 + g * 4 + q < len)
+            ybase[q * k.ys + pt * 16] = from_f32<T>(acc[pt][q] + Dh * to_f32(xq.v[q]));
+        }
+      }
+    };
+    auto scale_rows = [&](f32x4 (&acc)[TP], int t0) {
+      const f32x4 la = *reinterpret_cast<const f32x4*>(lam + t0 + g * 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float sq = __builtin_amdgcn_exp2f(la[q]);
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) acc[pt][q] *= sq;
+      }
+    };
+
+    if (OUT && len == Q && (RB == 16 || RB == 8)) {
+      // Full chunk: every wave owns RB/8 row blocks, no bounds tests.
+      constexpr bool kTwo = RB == 16;
+      const int t00 = rb[0] * 16, t01 = rb[1] * 16;
+      const int nsb0 = rb[0] / 2 + 1, nsb1 = rb[1] / 2 + 1;  // column blocks through the diagonal
+      const float lt0 = lam[t00 + r16];
+      const float lt1 = kTwo ? lam[t01 + r16] : 0.0f;
+      f32x4 acc0[TP], acc1[TP];
+      // Y_off = exp(Lambda_t) * C_t . H_prev
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) {
+        acc0[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        acc1[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int n = kb * 32 + g * 8;
+          Frag8<T> hf;
+          if (n < N) frag_load8(hf, Hs + (pt * 16 + r16) * L::HP + n);
+          else frag_zero(hf);
+          acc0[pt] = mma(cfa[kb], hf, acc0[pt]);
+          if (kTwo) acc1[pt] = mma(cfb[kb], hf, acc1[pt]);
+        }
+      }
+      scale_rows(acc0, t00);
+      if (kTwo) scale_rows(acc1, t01);
+      // Y_diag over column blocks; both row blocks share each B and x fragment
+      auto step = [&](int sb, bool both, bool diag0, bool diag1) {
+        const int s0 = sb * 32;
+        f32x4 g0A = {0, 0, 0, 0}, g0B = {0, 0, 0, 0}, g1A = {0, 0, 0, 0}, g1B = {0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          Frag8<T> b0, b1;
+          load_bpair(s0, kb, b0, b1);
+          if (both) {
+            g0A = mma(b0, cfa[kb], g0A);
+            g0B = mma(b1, cfa[kb], g0B);
+          }
+          g1A = mma(b0, cfb[kb], g1A);
+          g1B = mma(b1, cfb[kb], g1B);
+        }
+        Frag8<T> m0, m1;
+        if (both) m0 = build_m(g0A, g0B, s0, t00 + r16, lt0, diag0);
+        m1 = build_m(g1A, g1B, s0, t01 + r16, lt1, diag1);
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) {
+          Frag8<T> xf;
+          load_xpair(s0, pt, xf);
+          if (both) acc0[pt] = mma(m0, xf, acc0[pt]);
+          acc1[pt] = mma(m1, xf, acc1[pt]);
+        }
+      };
+      if (kTwo) {
+        int sb = 0;
+#pragma unroll 1
+        for (; sb < nsb0 - 1; ++sb) step(sb, true, false, false);
+        step(sb++, true, true, false);
+#pragma unroll 1
+        for (; sb < nsb1 - 1; ++sb) step(sb, false, false, false);
+        step(sb, false, false, true);
+        store_rows(acc0, t00, true);
+        store_rows(acc1, t01, true);
+      } else {
+        // one row block per wave
+        int sb = 0;
+#pragma unroll 1
+        for (; sb < nsb0 - 1; ++sb) {
+          const int s0 = sb * 32;
+          f32x4 gA = {0, 0, 0, 0}, gB = {0, 0, 0, 0};
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            Frag8<T> b0, b1;
+            load_bpair(s0, kb, b0, b1);
+            gA = mma(b0, cfa[kb], gA);
+            gB = mma(b1, cfa[kb], gB);
+          }
+          const Frag8<T> m = build_m(gA, gB, s0, t00 + r16, lt0, false);
+#pragma unroll
+          for (int pt = 0; pt < TP; ++pt) {
+            Frag8<T> xf;
+            load_xpair(s0, pt, xf);
+            acc0[pt] = mma(m, xf, acc0[pt]);
+          }
+        }
+        {
+          const int s0 = sb * 32;
+          f32x4 gA = {0, 0, 0, 0}, gB = {0, 0, 0, 0};
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            Frag8<T> b0, b1;
+            load_bpair(s0, kb, b0, b1);
+            gA = mma(b0, cfa[kb], gA);
+            gB = mma(b1, cfa[kb], gB);
+          }
+          const Frag8<T> m = build_m(gA, gB, s0, t00 + r16, lt0, true);
+#pragma unroll
+          for (int pt = 0; pt < TP; ++pt) {
+            Frag8<T> xf;
+            load_xpair(s0, pt, xf);
+            acc0[pt] = mma(m, xf, acc0[pt]);
+          }
+        }
+        store_rows(acc0, t00, true);
+      }
+      if (c + 1 < c_end) {  // in flight across the next commit and state update
+        load_c(c + 1, rb[0], cfa);
+        load_c(c + 1, rb[1], cfb);
+      }
+    } else if (OUT) {
+      // Generic path: ragged last chunk or fewer row blocks than waves.
+      const int t00 = rb[0] * 16, t01 = rb[1] * 16;
+      const bool v0 = rb[0] < RB && t00 < len;  // wave-uniform
+      const bool v1 = rb[1] < RB && t01 < len;
+      f32x4 acc0[TP], acc1[TP];
+
+      // Y_off = exp(Lambda_t) * C_t . H_prev
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) {
+        acc0[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        acc1[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int n = kb * 32 + g * 8;
+          Frag8<T> hf;
+          if (n < N) frag_load8(hf, Hs + (pt * 16 + r16) * L::HP + n);
+          else frag_zero(hf);
+          if (v0) acc0[pt] = mma(cfa[kb], hf, acc0[pt]);
+          if (v1) acc1[pt] = mma(cfb[kb], hf, acc1[pt]);
+        }
+      }
+      {
+        const f32x4 la0 = v0 ? *reinterpret_cast<const f32x4*>(lam + t00 + g * 4) : f32x4{0, 0, 0, 0};
+        const f32x4 la1 = v1 ? *reinterpret_cast<const f32x4*>(lam + t01 + g * 4) : f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float s0q = __builtin_amdgcn_exp2f(la0[q]), s1q = __builtin_amdgcn_exp2f(la1[q]);
+#pragma unroll
+          for (int pt = 0; pt < TP; ++pt) {
+            acc0[pt][q] *= s0q;
+            acc1[pt][q] *= s1q;
+          }
+        }
+      }
+
+      // Y_diag over causal 32-wide column blocks
+      const int nsb0 = v0 ? t00 / 32 + 1 : 0;  // column blocks up to the diagonal
+      const int nsb1 = v1 ? t01 / 32 + 1 : 0;
+      const int nsbm = nsb0 > nsb1 ? nsb0 : nsb1;
+      const float lt0 = lam[t00 + r16 < QA ? t00 + r16 : QA - 1];
+      const float lt1 = lam[t01 + r16 < QA ? t01 + r16 : QA - 1];
+#pragma unroll 1
+      for (int sb = 0; sb < nsbm; ++sb) {
+        const int s0 = sb * 32;
+        const bool a0 = sb < nsb0, a1 = sb < nsb1;  // wave-uniform
+        f32x4 g0A = {0, 0, 0, 0}, g0B = {0, 0, 0, 0}, g1A = {0, 0, 0, 0}, g1B = {0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int n = kb * 32 + g * 8;
+          Frag8<T> b0, b1;
+          if (n < N) {
+            frag_load8(b0, Bs + (s0 + r16) * L::BP + n);
+            frag_load8(b1, Bs + (s0 + 16 + r16) * L::BP + n);
+          } else {
+            frag_zero(b0);
+            frag_zero(b1);
+          }
+          if (a0) {
+            g0A = mma(b0, cfa[kb], g0A);
+            g0B = mma(b1, cfa[kb], g0B);
+          }
+          if (a1) {
+            g1A = mma(b0, cfb[kb], g1A);
+            g1B = mma(b1, cfb[kb], g1B);
+          }
+        }
+        Frag8<T> m0, m1;
+        if (a0) m0 = build_m(g0A, g0B, s0, t00 + r16, lt0, sb + 1 == nsb0);
+        if (a1) m1 = build_m(g1A, g1B, s0, t01 + r16, lt1, sb + 1 == nsb1);
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) {
+          const T* xr = XT + (pt * 16 + r16) * XP + s0 + g * 4;
+          Frag8<T> xf;
+          frag_load4x2(xf, xr, xr + 16);
+          if (a0) acc0[pt] = mma(m0, xf, acc0[pt]);
+          if (a1) acc1[pt] = mma(m1, xf, acc1[pt]);
+        }
+      }
+
+      if (v0) store_rows(acc0, t00, t00 + 16 <= len);
+      if (v1) store_rows(acc1, t01, t01 + 16 <= len);
+      if (c + 1 < c_end) {  // in flight across the next commit and state update
+        load_c(c + 1, rb[0], cfa);
+        load_c(c + 1, rb[1], cfb);
+      }
+    }
+
     __syncthreads();
   }
 
