@@ -18,8 +18,16 @@ namespace mmssd {
 
 namespace {
 
-constexpr int kConvThreads = 128;
+constexpr int kConvThreads = 64;
 constexpr int kTokensPerRun = 32;
+
+// SiLU(v) = v * sigmoid(v) = v / (1 + exp(-v)), with the hardware exp2 and
+// reciprocal (about 1 ulp each): an IEEE division here made the kernel
+// VALU-bound below the HBM rate.  Large |v| saturates correctly (exp2 -> inf,
+// rcp(inf) -> 0).
+__device__ __forceinline__ float silu(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
+}
 
 template <typename T>
 __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
@@ -72,7 +80,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
   }
 
   // tokens in groups of kGroup: issue the group's loads, then compute and store
-  constexpr int kGroup = 8;
+  constexpr int kGroup = 4;
   for (int tg = t0; tg < t1; tg += kGroup) {
     Vec16<T> u[kGroup];
 #pragma unroll
@@ -90,7 +98,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
           pre = fmaf(wk[1][j], h[1][j], pre);
           pre = fmaf(wk[2][j], h[2][j], pre);
           pre = fmaf(wk[3][j], ut, pre);
-          o.v[j] = from_f32<T>(pre / (1.0f + __expf(-pre)));
+          o.v[j] = from_f32<T>(silu(pre));
           h[0][j] = h[1][j];
           h[1][j] = h[2][j];
           h[2][j] = ut;
