@@ -134,6 +134,20 @@ int mm_ssd_forward_workspace_size(int64_t batch, int64_t seqlen,
                                   int dtype, size_t* bytes_out);
 
 /*
+ * Number of sequence segments mm_ssd_forward cuts each sequence into for
+ * these sizes (>= 1; with several, segment end states are chained through
+ * the workspace).  Two calls with the same count and the same tile length
+ * round identically on a shared head, so sub-block outputs then equal the
+ * first heads of the full block bit for bit ("MatMamba", nesting paragraph).
+ * Same argument meaning and errors as mm_ssd_forward.  Host only.
+ */
+int mm_ssd_forward_segments(int64_t batch, int64_t seqlen,
+                            int64_t n_heads, int64_t d_head,
+                            int64_t d_state, int64_t ngroups,
+                            int64_t n_heads_active, int64_t chunk,
+                            int dtype, int* nseg_out);
+
+/*
  * Chunked selective scan (SSD) over heads [0, n_heads_active) ("MatMamba",
  * block paragraph: chunk + selective scan; nesting paragraph: A[0:h_i]).
  * The sequence is cut into chunks of `chunk` tokens (the last may be
@@ -155,7 +169,10 @@ int mm_ssd_forward_workspace_size(int64_t batch, int64_t seqlen,
  *   initial_state (batch, n_heads, d_head, d_state) fp32 or NULL (= 0).
  *   final_state   same layout or NULL; active heads written.  It may alias
  *       initial_state (state chaining in place).
- *   chunk: 16, 32, 64, 128 or 256.
+ *   chunk: 16, 32, 64, 128 or 256.  With MM_BF16 storage, d_head 64 and
+ *       d_state 128, chunks of 128 and 256 tokens are evaluated in tiles of
+ *       128 (the chunked form is exact for any chunk length; only rounding
+ *       can differ from a single 256-token block).
  *   workspace: device memory of at least mm_ssd_forward_workspace_size()
  *       bytes (may be NULL if that is 0), not used concurrently by another call.
  * Preconditions: 1 <= batch <= 65535, seqlen >= 1, n_heads <= 65535;

@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
                                                         _i64, _i64, _int,
                                                         ctypes.POINTER(ctypes.c_size_t)]
             L.mm_ssd_forward_workspace_size.restype = _int
+            L.mm_ssd_forward_segments.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                                  _i64, _int, ctypes.POINTER(_int)]
+            L.mm_ssd_forward_segments.restype = _int
             L.mm_ssd_forward.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
                                          _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                          _i64, _i64, _i64, _int, _vp, ctypes.c_size_t, _vp]
@@ -169,6 +172,17 @@ def ssd_forward_workspace_size(batch: int, seqlen: int, n_heads: int, d_head: in
     _check("mm_ssd_forward_workspace_size",
            lib().mm_ssd_forward_workspace_size(batch, seqlen, n_heads, d_head, d_state, ngroups,
                                                n_heads_active, chunk, code, ctypes.byref(out)))
+    return out.value
+
+
+def ssd_forward_segments(batch: int, seqlen: int, n_heads: int, d_head: int, d_state: int,
+                         ngroups: int, n_heads_active: int, chunk: int,
+                         dtype: torch.dtype) -> int:
+    out = _int(0)
+    code = MM_F32 if dtype == torch.float32 else MM_BF16
+    _check("mm_ssd_forward_segments",
+           lib().mm_ssd_forward_segments(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                         n_heads_active, chunk, code, ctypes.byref(out)))
     return out.value
 
 

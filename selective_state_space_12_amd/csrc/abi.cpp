@@ -79,7 +79,18 @@ int mm_ssd_forward_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads
   const int st = validate_ssd_shape(batch, seqlen, n_heads, d_head, d_state, ngroups,
                                     n_heads_active, chunk, dtype);
   if (st != MM_OK) return st;
-  *bytes_out = fwd_workspace_bytes(batch, seqlen, n_heads_active, d_head, d_state, chunk);
+  *bytes_out = fwd_workspace_bytes(batch, seqlen, n_heads_active, d_head, d_state, chunk, dtype);
+  return MM_OK;
+}
+
+int mm_ssd_forward_segments(int64_t batch, int64_t seqlen, int64_t n_heads, int64_t d_head,
+                            int64_t d_state, int64_t ngroups, int64_t n_heads_active,
+                            int64_t chunk, int dtype, int* nseg_out) {
+  if (!nseg_out) return MM_ERR_NULL;
+  const int st = validate_ssd_shape(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                    n_heads_active, chunk, dtype);
+  if (st != MM_OK) return st;
+  *nseg_out = fwd_segments(batch, seqlen, n_heads_active, d_head, d_state, chunk, dtype);
   return MM_OK;
 }
 
@@ -96,7 +107,7 @@ int mm_ssd_forward(const void* x, int64_t x_row_stride, const void* dt,
                                 batch, seqlen, n_heads, d_head, d_state, ngroups,
                                 n_heads_active, chunk, dtype);
   if (st != MM_OK) return st;
-  const size_t need = fwd_workspace_bytes(batch, seqlen, n_heads_active, d_head, d_state, chunk);
+  const size_t need = fwd_workspace_bytes(batch, seqlen, n_heads_active, d_head, d_state, chunk, dtype);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MM_ERR_WORKSPACE;
   if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return MM_ERR_ALIGN;
   FwdArgs a;

@@ -71,9 +71,20 @@ struct FwdArgs {
 // chunks per segment (every segment but the last holds seg_chunks chunks).
 void fwd_plan(int64_t batch, int64_t seqlen, int64_t heads, int64_t chunk, int* nchunks,
               int* nseg, int* seg_chunks);
-// Device workspace the plan needs (segment states and decays), 0 if none.
+// Device workspace a scan call needs, 0 if none: segment states and decays
+// of the plan and, on the bf16 d_head-64 d_state-128 path, the per-tile G and
+// B^T fragments.
 size_t fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
-                           int64_t d_head, int64_t d_state, int64_t chunk);
+                           int64_t d_head, int64_t d_state, int64_t chunk, int dtype);
+
+// Segments per sequence of a scan call (the plan of the path it takes).
+int fwd_segments(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
+                 int64_t d_state, int64_t chunk, int dtype);
+
+// bf16, d_head 64, d_state 128, chunk 128 or 256 (ssd_fwd_bf16.hip).
+bool bf16_path(int64_t d_head, int64_t d_state, int64_t chunk, int dtype);
+size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads);
+hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* workspace, hipStream_t s);
 
 hipError_t launch_ssd_forward(const FwdArgs& a, int dtype, void* workspace, hipStream_t s);
 

@@ -157,11 +157,16 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
 
   // Loads are unconditional (rows past the end of the sequence are clamped to
   // its last row); the commit below zeroes them, so no lane branches here.
-  auto prefetch = [&](int c) {
+  // A chunk's loads are issued in kParts portions spread over the previous
+  // chunk's compute: every CU runs the same program, so issuing them in one
+  // burst saturates HBM for microseconds and then leaves it idle.
+  constexpr int kParts = 3;
+  auto prefetch = [&](int c, int part) {
     const int64_t row0 = rowb + (int64_t)c * Q;
     const int last = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q) - 1;
 #pragma unroll
     for (int v = 0; v < NBV; ++v) {
+      if (v % kParts != part) continue;
       const int idx = tid + v * kThreads;
       const int s = min(idx / (N / VB), last), col = (idx % (N / VB)) * VB;
       pb[v] = load16(Bp + (row0 + s) * k.bs + col);
@@ -170,11 +175,12 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
     // group), so the transposed LDS writes of a wave hit distinct banks
 #pragma unroll
     for (int v = 0; v < NXV; ++v) {
+      if (v % kParts != part) continue;
       const int idx = tid + v * kThreads;
       const int s = min(idx % QA, last), p0 = ((idx / QA) % (P / VB)) * VB;
       px[v] = load16(Xp + (row0 + s) * k.xs + (int64_t)h * P + p0);
     }
-    if (wave == 0) {
+    if (wave == 0 && part == 0) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int s = min(lane * E + e, last);
@@ -200,7 +206,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
   const int c_end = min(c_begin + k.seg_chunks, k.nchunks);
   float lam_seg = 0.0f;
   if (c_begin < c_end) {
-    prefetch(c_begin);
+#pragma unroll
+    for (int part = 0; part < kParts; ++part) prefetch(c_begin, part);
     if (OUT) {
       load_c(c_begin, rb[0], cfa);
       load_c(c_begin, rb[1], cfb);
@@ -280,7 +287,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
     __syncthreads();
 
     // next chunk's loads are in flight while this chunk computes
-    if (c + 1 < c_end) prefetch(c + 1);
+    const bool more = c + 1 < c_end;
+    if (more) prefetch(c + 1, 0);  // parts 1 and 2 follow the state update and Y_off
 
     // ---- phase U: H <- exp(Lambda_end) H + (w o x)^T B, w_s = exp(Lambda_end - Lambda_s) dt_s
     // (registers only; the outputs below use the operand copy of H_prev in LDS)
@@ -311,6 +319,10 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
           hacc[t] = mma(xf, bfv, hacc[t]);
         }
       }
+    }
+    if (more) {
+      prefetch(c + 1, 1);
+      if (!OUT) prefetch(c + 1, 2);
     }
     // ---- phase R: outputs of this chunk ----
     // Lane holds G^T[s0 + g*4 + q][t] (gA) and G^T[s0 + 16 + g*4 + q][t] (gB)
@@ -412,6 +424,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
       }
       scale_rows(acc0, t00);
       if (kTwo) scale_rows(acc1, t01);
+      if (more) prefetch(c + 1, 2);
       // Y_diag over column blocks; both row blocks share each B and x fragment
       auto step = [&](int sb, bool both, bool diag0, bool diag1) {
         const int s0 = sb * 32;
@@ -495,6 +508,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
         load_c(c + 1, rb[1], cfb);
       }
     } else if (OUT) {
+      if (more) prefetch(c + 1, 2);
       // Generic path: ragged last chunk or fewer row blocks than waves.
       const int t00 = rb[0] * 16, t01 = rb[1] * 16;
       const bool v0 = rb[0] < RB && t00 < len;  // wave-uniform
@@ -695,8 +709,17 @@ void fwd_plan(int64_t batch, int64_t seqlen, int64_t heads, int64_t chunk, int* 
   *nseg = (int)((nc + per - 1) / per);
 }
 
+int fwd_segments(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
+                 int64_t d_state, int64_t chunk, int dtype) {
+  const int64_t q = bf16_path(d_head, d_state, chunk, dtype) ? 128 : chunk;
+  int nc, nseg, per;
+  fwd_plan(batch, seqlen, heads, q, &nc, &nseg, &per);
+  return nseg;
+}
+
 size_t fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
-                           int64_t d_state, int64_t chunk) {
+                           int64_t d_state, int64_t chunk, int dtype) {
+  if (bf16_path(d_head, d_state, chunk, dtype)) return bf16_workspace_bytes(batch, seqlen, heads);
   int nc, nseg, per;
   fwd_plan(batch, seqlen, heads, chunk, &nc, &nseg, &per);
   if (nseg <= 1) return 0;
@@ -704,6 +727,7 @@ size_t fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t
 }
 
 hipError_t launch_ssd_forward(const FwdArgs& a, int dtype, void* ws, hipStream_t s) {
+  if (bf16_path(a.d_head, a.d_state, a.chunk, dtype)) return launch_ssd_forward_bf16(a, ws, s);
   if (dtype == MM_BF16) return launch_typed<bf16>(a, ws, s);
   return launch_typed<float>(a, ws, s);
 }

@@ -80,6 +80,25 @@ def test_workspace_query(lib):
     assert out.value > 0
     assert f(1, 131072, 32, 64, 128, 1, 8, 48, 1, ctypes.byref(out)) == -5
     assert f(1, 131072, 32, 64, 128, 2, 8, 256, 1, ctypes.byref(out)) == -5
+    # fp32, 256 (sequence, head) units: one segment, nothing to stage
+    assert f(4, 8192, 64, 64, 128, 1, 64, 128, 0, ctypes.byref(out)) == 0
+    assert out.value == 0
+    # bf16 d_head 64 d_state 128: per-tile G and B^T fragments, 52 KB per tile
+    assert f(4, 8192, 64, 64, 128, 1, 64, 256, 1, ctypes.byref(out)) == 0
+    assert out.value == 4 * 64 * 52 * 1024
+
+
+def test_segments_query(lib):
+    f = lib.mm_ssd_forward_segments
+    f.argtypes = [ctypes.c_int64] * 8 + [ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    n = ctypes.c_int()
+    assert f(4, 8192, 64, 64, 128, 1, 64, 256, 1, ctypes.byref(n)) == 0 and n.value == 1
+    # 4 x 8 units at 64 tiles each: split so that about 256 workgroups run
+    assert f(4, 8192, 64, 64, 128, 1, 8, 256, 1, ctypes.byref(n)) == 0 and n.value == 8
+    assert f(1, 131072, 32, 64, 128, 1, 8, 256, 1, ctypes.byref(n)) == 0 and n.value == 32
+    assert f(1, 100, 4, 32, 16, 1, 4, 64, 0, ctypes.byref(n)) == 0 and n.value == 2
+    assert f(1, 100, 4, 32, 16, 1, 4, 64, 0, None) == -1
+    assert f(1, 100, 4, 32, 16, 1, 4, 48, 0, ctypes.byref(n)) == -5
 
 
 def _no_gpu():

@@ -164,16 +164,17 @@ def test_scan_long_context_full_length_sampled():
 
 # ------------------------------------------------------------- invariants ----
 def _plan_is_single_segment(w, batch, seqlen, heads, chunk):
-    return mm.ssd_forward_workspace_size(batch, seqlen, w.n_heads, w.d_head, w.d_state, 1, heads,
-                                         chunk, w.dtype) == 0
+    return mm.ssd_forward_segments(batch, seqlen, w.n_heads, w.d_head, w.d_state, 1, heads,
+                                   chunk, w.dtype) == 1
 
 
 def test_nesting_bitwise_when_plans_match():
     """Sub-block M_i == first h_i heads of M_g, bit for bit, whenever both
-    calls cut the sequence the same way: one chunk (every slice), and a
-    multi-chunk batch wide enough that neither call splits into segments."""
+    calls cut the sequence the same way: one (ragged) tile for every slice,
+    and a multi-tile batch wide enough that neither call splits into
+    segments."""
     w = B14
-    cases = [(4, 256, [8, 16, 32, 64]), (8, 1000, [32, 64])]
+    cases = [(4, 120, [8, 16, 32, 64]), (8, 1000, [32, 64])]
     for b, l, hs in cases:
         inp = synth.forward_inputs(w, batch=b, seqlen=l, with_state=True)
         say(f"nesting 1.4b-shaped bf16 b={b} l={l}")
