@@ -10,15 +10,17 @@
 // chunked form is exact at any chunk length, so only rounding differs).
 //
 // MI355X design:
-//  - chunk_gram_kernel forms, once per (sequence, tile) and for every head,
-//    the causal blocks of G = C B^T and the tiles of B^T, already in the
-//    register order of the MFMA operands that consume them (1 KB per wave
-//    load, fully coalesced).  With one B/C group all heads share them, so the
-//    C.B^T contraction leaves the per-head kernel.
-//  - ssd_bf16_kernel: one workgroup of 8 waves walks the tiles of one
-//    (sequence, head, segment).  Waves 0-3 produce outputs, waves 4-7 own the
-//    fp32 state in MFMA accumulators and stage x; one wave of each kind
-//    shares a SIMD, so the output MFMAs overlap the state update and staging.
+//  - tile_prep_kernel forms, once per (sequence, tile) and for every head,
+//    the causal blocks of G = C B^T and the tiles of B^T and C, already in
+//    the register order of the MFMA operands that consume them (1 KB per wave
+//    load, fully coalesced), and a head-major copy of dt.  With one B/C group
+//    all heads share them, so the C.B^T contraction leaves the per-head
+//    kernel and every per-tile load is a few whole cache lines.
+//  - ssd_bf16_kernel: one workgroup of 16 waves walks the tiles of one
+//    (sequence, head, segment).  Eight waves produce outputs (one 16-token
+//    block each), four own the fp32 state in MFMA accumulators, four stage x
+//    and the decay cumsums; every SIMD runs waves of all three kinds, so the
+//    output MFMAs overlap the state update and the staging.
 //  - x is transposed by an MFMA against a 0/1 selector (exact), which leaves
 //    four consecutive tokens per lane: three scaled copies (plain, block
 //    decay, end decay) go to LDS with 8-byte writes.
@@ -28,6 +30,8 @@
 //    Horner form (one scalar per block), so G enters the MFMA unscaled.  The
 //    diagonal block takes the direct masked form, with D folded into the
 //    diagonal of the mask.
+//  - output rows are dealt to the A operand in an order that leaves each lane
+//    eight consecutive channels of a token, stored as one 16-byte write;
 //  - LDS tiles are double-buffered and the decay cumsums triple-buffered, so
 //    each tile costs one workgroup barrier.
 #include "device_common.h"
@@ -50,15 +54,22 @@ constexpr int kNBW = kNB / 4;  // state column blocks per state wave
 constexpr int kXP = kQ + 8;    // LDS row pitch (elements) of the transposed x copies
 constexpr int kHP = kN + 8;    // LDS row pitch (elements) of the operand copy of H
 constexpr int kXcds = 8;
+// 16 waves, four per SIMD: 0-7 outputs (one 16-token block each; waves w and
+// w+4 share a SIMD and take blocks whose causal work adds up the same), 8-11
+// state update, 12-15 x staging and decay cumsums.
+constexpr int kThreads = 16 * 64;
+static_assert(kHP == kXP, "x copies and the H copy share one swizzled row layout");
 
 // G fragments (tb, k) exist for the 32-token blocks k <= tb/2 (causal,
 // diagonal block included), numbered tb-major.
 __host__ __device__ constexpr int gbase(int tb) {
   return (tb / 2) * (tb / 2 + 1) + (tb & 1) * (tb / 2 + 1);
 }
-constexpr int kNG = gbase(kTB);           // 20
-constexpr int kNFR = kNG + kNB * kSB;     // fragments per (sequence, tile): 52
-constexpr size_t kFragBytes = 64 * 16;    // one wave-wide fragment
+constexpr int kNG = gbase(kTB);                  // G fragments: 20
+constexpr int kBT0 = kNG;                        // first B^T fragment (nb, ks): kNB * kSB
+constexpr int kC0 = kBT0 + kNB * kSB;            // first C fragment (tb, kb): kTB * kKB
+constexpr int kNFR = kC0 + kTB * kKB;            // fragments per (sequence, tile): 84
+constexpr size_t kFragBytes = 64 * 16;           // one wave-wide fragment
 
 constexpr size_t kXTile = (size_t)kP * kXP * sizeof(bf16);
 constexpr size_t kHTile = (size_t)kP * kHP * sizeof(bf16);
@@ -78,59 +89,123 @@ __device__ __forceinline__ Frag8<bf16> as_frag(uint4 u) {
 __device__ __forceinline__ Frag8<bf16> lds_frag(const bf16* p) {
   return as_frag(*reinterpret_cast<const uint4*>(p));
 }
+// Element offset of (row, col) in a [64][kXP] LDS tile, col a multiple of 8.
+// The 16-byte chunks of rows 8-15 of every 16 rows are XOR-ed with 4: the
+// A-operand row orders used below (rows r and r + 8 read by lanes of the
+// same 8-lane group) then hit distinct banks, and natural row orders stay
+// conflict-free.
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * kXP + (col ^ (((row >> 3) & 1) << 5));
+}
+
+// Lane value moved by a DPP pattern; lanes with no source (or outside the
+// row mask) read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xf, false));
+}
 
 // ---------------------------------------------------------------------------
-// Per (sequence, tile): G fragments and B^T fragments.
-//   G fragment (tb, k): lane (r, g) holds G[tb*16 + r][k*32 + g*8 + j], j < 8
-//   B^T fragment (nb, ks): lane (r, g) holds B[ks*32 + g*8 + j][nb*16 + r]
-// Rows past the end of the sequence repeat its last row (finite values that
-// the scan multiplies by dt = 0 or never stores).
-__global__ __launch_bounds__(256) void chunk_gram_kernel(const bf16* __restrict__ Bp, int64_t bs,
-                                                         const bf16* __restrict__ Cp, int64_t cs,
-                                                         uint4* __restrict__ frags, int64_t seqlen,
-                                                         int ntiles) {
-  __shared__ __align__(16) bf16 Bt[kQ][kN + 8];
-  const int c = blockIdx.x, b = blockIdx.y;
+// Per (sequence, tile), shared by every head:
+//   G fragment (tb, k):    lane (r, g) holds G[tb*16 + r][k*32 + g*8 + j], j < 8
+//   B^T fragment (np, e, ks): lane (r, g) holds B[ks*32 + g*8 + j][n] with
+//                          n = np*32 + (r/4)*8 + e*4 + r%4 (so the state
+//                          update leaves lane (p, g) eight consecutive n)
+//   C fragment (tb, kb):   lane (r, g) holds C[tb*16 + r][kb*32 + g*8 + j]
+// and, per head, dt of the tile's tokens as one contiguous row (dtT).  Rows
+// past the end of the sequence repeat its last row (finite values that the
+// scan multiplies by dt = 0 or never stores).  blockIdx.z selects the part
+// (0..4: four G fragments each, one per wave; 5: B^T; 6: C and dt), so seven
+// small workgroups share a tile.
+__global__ __launch_bounds__(256) void tile_prep_kernel(const bf16* __restrict__ Bp, int64_t bs,
+                                                        const bf16* __restrict__ Cp, int64_t cs,
+                                                        const bf16* __restrict__ dtp, int64_t dts,
+                                                        uint4* __restrict__ frags,
+                                                        bf16* __restrict__ dtT, int64_t seqlen,
+                                                        int ntiles, int heads) {
+  __shared__ __align__(16) bf16 sh[kQ * (kN + 8)];
+  const int c = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
   const int64_t row0 = (int64_t)b * seqlen + (int64_t)c * kQ;
   const int last = (int)min((int64_t)kQ, seqlen - (int64_t)c * kQ) - 1;
   uint4* out = frags + ((int64_t)b * ntiles + c) * kNFR * 64;
 
-  for (int v = tid; v < kQ * (kN / 8); v += 256) {
-    const int s = v / (kN / 8), col = (v % (kN / 8)) * 8;
-    *reinterpret_cast<uint4*>(&Bt[s][col]) =
-        *reinterpret_cast<const uint4*>(Bp + (row0 + min(s, last)) * bs + col);
-  }
-
-  // G^T tiles: A operand row m takes B row k*32 + (m/4)*8 + m%4 (tile a) or
-  // that + 4 (tile b), B operand column n is C row tb*16 + n, so output slot
-  // i of lane (r, g) is G[tb*16 + r][k*32 + g*8 + i] (a) and [.. + 4 + i] (b).
-  for (int f = wave; f < kNG; f += 4) {
-    int tb = 0;
-    while (gbase(tb + 1) <= f) ++tb;
-    const int k = f - gbase(tb);
-    const int sa = k * 32 + (r16 >> 2) * 8 + (r16 & 3);
-    const int t = min(tb * 16 + r16, last);
-    f32x4 da = {0, 0, 0, 0}, db = {0, 0, 0, 0};
+  constexpr int kGParts = kNG / 4;
+  static_assert(kNG % 4 == 0, "G fragments split over 4-wave workgroups");
+  if (part < kGParts) {
+    // G^T tiles: A operand row m takes B row k*32 + (m/4)*8 + m%4 (tile a) or
+    // that + 4 (tile b), B operand column n is C row tb*16 + n, so output slot
+    // i of lane (r, g) is G[tb*16 + r][k*32 + g*8 + i] (a) and [.. + 4 + i] (b).
+    {
+      const int f = part * 4 + wave;
+      int tb = 0;
+      while (gbase(tb + 1) <= f) ++tb;
+      const int k = f - gbase(tb);
+      const int sa = k * 32 + (r16 >> 2) * 8 + (r16 & 3);
+      const bf16* ba = Bp + (row0 + min(sa, last)) * bs + g * 8;
+      const bf16* bb = Bp + (row0 + min(sa + 4, last)) * bs + g * 8;
+      const bf16* cr = Cp + (row0 + min(tb * 16 + r16, last)) * cs + g * 8;
+      f32x4 da = {0, 0, 0, 0}, db = {0, 0, 0, 0};
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) {
-      const int n = kb * 32 + g * 8;
-      const Frag8<bf16> a0 = lds_frag(&Bt[min(sa, last)][n]);
-      const Frag8<bf16> a1 = lds_frag(&Bt[min(sa + 4, last)][n]);
-      const Frag8<bf16> cb = as_frag(*reinterpret_cast<const uint4*>(Cp + (row0 + t) * cs + n));
-      da = mma(a0, cb, da);
-      db = mma(a1, cb, db);
+      for (int kb = 0; kb < kKB; ++kb) {
+        const Frag8<bf16> a0 = as_frag(*reinterpret_cast<const uint4*>(ba + kb * 32));
+        const Frag8<bf16> a1 = as_frag(*reinterpret_cast<const uint4*>(bb + kb * 32));
+        const Frag8<bf16> cb = as_frag(*reinterpret_cast<const uint4*>(cr + kb * 32));
+        da = mma(a0, cb, da);
+        db = mma(a1, cb, db);
+      }
+      const uint2 lo = pack4(da), hi = pack4(db);
+      out[f * 64 + lane] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
-    const uint2 lo = pack4(da), hi = pack4(db);
-    out[f * 64 + lane] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-  }
-  __syncthreads();
-  for (int f = wave; f < kNB * kSB; f += 4) {
-    const int nb = f / kSB, ks = f % kSB;
-    bf16x8 v;
+  } else if (part == kGParts) {
+    bf16 (*Bt)[kN + 8] = reinterpret_cast<bf16 (*)[kN + 8]>(sh);
+    for (int v = tid; v < kQ * (kN / 8); v += 256) {
+      const int s = v / (kN / 8), col = (v % (kN / 8)) * 8;
+      *reinterpret_cast<uint4*>(&Bt[s][col]) =
+          *reinterpret_cast<const uint4*>(Bp + (row0 + min(s, last)) * bs + col);
+    }
+    __syncthreads();
+    for (int f = wave; f < kNB * kSB; f += 4) {
+      const int npe = f / kSB, ks = f % kSB;  // npe = np*2 + e
+      const int n = (npe >> 1) * 32 + (r16 >> 2) * 8 + (npe & 1) * 4 + (r16 & 3);
+      bf16x8 v;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = Bt[ks * 32 + g * 8 + j][nb * 16 + r16];
-    out[(kNG + f) * 64 + lane] = __builtin_bit_cast(uint4, v);
+      for (int j = 0; j < 8; ++j) v[j] = Bt[ks * 32 + g * 8 + j][n];
+      out[(kBT0 + f) * 64 + lane] = __builtin_bit_cast(uint4, v);
+    }
+  } else {
+    for (int f = wave; f < kTB * kKB; f += 4) {
+      const int tb = f / kKB, kb = f % kKB;
+      const int t = min(tb * 16 + r16, last);
+      out[(kC0 + f) * 64 + lane] =
+          *reinterpret_cast<const uint4*>(Cp + (row0 + t) * cs + kb * 32 + g * 8);
+    }
+    // dt, 64 heads at a time: [token][head] -> LDS -> [head][token]
+    bf16 (*Dt)[kQ + 2] = reinterpret_cast<bf16 (*)[kQ + 2]>(sh);
+    bf16* dto = dtT + ((int64_t)b * ntiles + c) * heads * kQ;
+    for (int h0 = 0; h0 < heads; h0 += 64) {
+      const int nh = min(64, heads - h0);
+      __syncthreads();
+      // thread: head h0 + tid%64, tokens tid/64 + 4i; all 32 loads in flight
+      const int hh = tid & 63;
+      bf16 v[kQ / 4];
+#pragma unroll
+      for (int i = 0; i < kQ / 4; ++i) {
+        const int s = (tid >> 6) + 4 * i;
+        v[i] = dtp[(row0 + min(s, last)) * dts + h0 + min(hh, nh - 1)];
+      }
+      if (hh < nh) {
+#pragma unroll
+        for (int i = 0; i < kQ / 4; ++i) Dt[hh][(tid >> 6) + 4 * i] = v[i];
+      }
+      __syncthreads();
+      for (int v = tid; v < nh * (kQ / 2); v += 256) {
+        const int hh = v / (kQ / 2), s2 = v % (kQ / 2);
+        *reinterpret_cast<uint32_t*>(dto + (int64_t)(h0 + hh) * kQ + 2 * s2) =
+            *reinterpret_cast<const uint32_t*>(&Dt[hh][2 * s2]);
+      }
+    }
   }
 }
 
@@ -148,6 +223,7 @@ struct BK {
   const float* h0;
   float* hT;
   const uint4* frags;
+  const bf16* dtT;
   float* seg_state;
   float* seg_decay;
   int64_t seqlen;
@@ -155,40 +231,39 @@ struct BK {
 };
 
 // ---------------------------------------------------------------------------
-// Output waves (OUT only).  Wave y produces the 16-token blocks tb0 = y and
-// tb1 = 7 - y (equal causal work per wave) for all 64 channels of the head.
-// Output tiles are held transposed, D[p][t]: lane (r, g) holds
-// y[tb*16 + r][pb*16 + g*4 + i], four consecutive channels of one token.
-template <int L0>
-__device__ void output_waves(const BK& k, unsigned char* smem, int b, int h, int c0, int c1,
-                             int y) {
-  constexpr int L1 = kSB - 1 - L0;  // off-diagonal 32-token blocks of tb1
+// Output waves (OUT only).  Each produces one 16-token block tb of every tile
+// for all 64 channels of the head; L = tb/2 is the number of 32-token blocks
+// left of its diagonal block.  Output tiles are held transposed, D[m][t]:
+// row m of tile pb = 2a + e is channel a*32 + (m/4)*8 + e*4 + m%4, so lane
+// (r, g) holds channels a*32 + g*8 + e*4 + i of token tb*16 + r: tiles 2a and
+// 2a+1 together give it eight consecutive channels, one 16-byte store.
+template <int L>
+__device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int c0, int c1,
+                            int tb) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
-  const int tb0 = y, tb1 = kTB - 1 - y;
   const bf16* xbuf = reinterpret_cast<const bf16*>(smem);
   const bf16* hbuf = xbuf + 2 * 3 * kP * kXP;
   const float* dbuf = reinterpret_cast<const float*>(hbuf + 2 * kP * kHP);
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Dh = k.D ? k.D[h] : 0.0f;
+  const int t = tb * 16 + r16;  // this lane's token within a tile
 
-  Frag8<bf16> cf[2][kKB];
-  Frag8<bf16> gf0[L0 + 1], gf1[L1 + 1];
-  auto load_c = [&](int c) {
-    const int64_t r0 = rowb + (int64_t)c * kQ;
-    const int last = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ) - 1;
-    const int t0 = min(tb0 * 16 + r16, last), t1 = min(tb1 * 16 + r16, last);
+  // A-operand row (channel) of this lane in tile pb
+  int prow[kPB];
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) {
-      cf[0][kb] = as_frag(*reinterpret_cast<const uint4*>(k.C + (r0 + t0) * k.cs + kb * 32 + g * 8));
-      cf[1][kb] = as_frag(*reinterpret_cast<const uint4*>(k.C + (r0 + t1) * k.cs + kb * 32 + g * 8));
-    }
+  for (int pb = 0; pb < kPB; ++pb) prow[pb] = (pb >> 1) * 32 + (r16 >> 2) * 8 + (pb & 1) * 4 + (r16 & 3);
+
+  Frag8<bf16> cf[kKB];
+  Frag8<bf16> gf[L + 1];
+  auto load_c = [&](int c) {
+    const uint4* f = k.frags + (((int64_t)b * k.ntiles + c) * kNFR + kC0 + tb * kKB) * 64 + lane;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) cf[kb] = as_frag(f[kb * 64]);
   };
   auto load_g = [&](int c) {
-    const uint4* f = k.frags + ((int64_t)b * k.ntiles + c) * kNFR * 64 + lane;
+    const uint4* f = k.frags + (((int64_t)b * k.ntiles + c) * kNFR + gbase(tb)) * 64 + lane;
 #pragma unroll
-    for (int q = 0; q <= L0; ++q) gf0[q] = as_frag(f[(gbase(tb0) + q) * 64]);
-#pragma unroll
-    for (int q = 0; q <= L1; ++q) gf1[q] = as_frag(f[(gbase(tb1) + q) * 64]);
+    for (int q = 0; q <= L; ++q) gf[q] = as_frag(f[q * 64]);
   };
 
   load_c(c0);
@@ -205,21 +280,45 @@ __device__ void output_waves(const BK& k, unsigned char* smem, int b, int h, int
     const float* lam = dbuf + (c % 3) * kDec;
     const float* dtv = lam + kQ;
 
-    f32x4 acc[2][kPB];
+    f32x4 acc[kPB];
 #pragma unroll
-    for (int pb = 0; pb < kPB; ++pb) acc[0][pb] = acc[1][pb] = f32x4{0, 0, 0, 0};
+    for (int pb = 0; pb < kPB; ++pb) acc[pb] = f32x4{0, 0, 0, 0};
+
+    // Diagonal block: M[t][s] = G[t][s] exp2(lam_t - lam_s) dt_s for s <= t,
+    // plus D on s == t (the skip term D x_t).  Built in two halves dealt
+    // between the Y_off MFMAs below (independent VALU work).
+    const float lt = lam[t];
+    Frag8<bf16> m;
+    auto mask4 = [&](int j0) {
+      const int sb = L * 32 + g * 8 + j0;
+      const f32x4 ls = *reinterpret_cast<const f32x4*>(lam + sb);
+      const f32x4 ds = *reinterpret_cast<const f32x4*>(dtv + sb);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s = sb + j;
+        float v = static_cast<float>(gf[L].v[j0 + j]) * __builtin_amdgcn_exp2f(lt - ls[j]) * ds[j];
+        v = s <= t ? v : 0.0f;
+        v = s == t ? v + Dh : v;
+        m.v[j0 + j] = static_cast<bf16>(v);
+      }
+    };
 
     // Y_off before scaling: D[p][t] = sum_n H_prev[p][n] C[t][n]
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
-        const Frag8<bf16> hf = lds_frag(Hs + (pb * 16 + r16) * kHP + kb * 32 + g * 8);
-        acc[0][pb] = mma(hf, cf[0][kb], acc[0][pb]);
-        acc[1][pb] = mma(hf, cf[1][kb], acc[1][pb]);
+        const Frag8<bf16> hf = lds_frag(Hs + swz(prow[pb], kb * 32 + g * 8));
+        acc[pb] = mma(hf, cf[kb], acc[pb]);
       }
+      if (kb == 1) mask4(0);
+      if (kb == 3) mask4(4);
     }
-    if (c + 1 < c1) load_c(c + 1);
+    // Prefetches are unconditional (the last tile reloads itself): with a
+    // fixed number of loads per iteration the compiler's vmcnt waits stay
+    // exact instead of draining loads that were just issued.
+    const int cn = min(c + 1, c1 - 1);
+    load_c(cn);
 
     // Off-diagonal blocks in Horner form.  Before block q the accumulator is
     // referred to the end e(q-1) of the previous block (the tile start for
@@ -227,86 +326,49 @@ __device__ void output_waves(const BK& k, unsigned char* smem, int b, int h, int
     // block's own terms carry exp2(lam[e(q)] - lam_s) dt_s inside x (XE).
     float prev = 0.0f;
 #pragma unroll
-    for (int q = 0; q < L1; ++q) {
+    for (int q = 0; q < L; ++q) {
       const float eq = lam[q * 32 + 31];
       const float r = __builtin_amdgcn_exp2f(eq - prev);
       prev = eq;
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
-        const Frag8<bf16> xe = lds_frag(XE + (pb * 16 + r16) * kXP + q * 32 + g * 8);
-        acc[1][pb] = mma(xe, gf1[q], acc[1][pb] * r);
-        if (q < L0) acc[0][pb] = mma(xe, gf0[q], acc[0][pb] * r);
+        const Frag8<bf16> xe = lds_frag(XE + swz(prow[pb], q * 32 + g * 8));
+        acc[pb] = mma(xe, gf[q], acc[pb] * r);
       }
     }
-    // from the last block end to each token: exp2(lam_t - lam[e(L-1)]) <= 1
-    const int t0 = tb0 * 16 + r16, t1 = tb1 * 16 + r16;
-    const float lt0 = lam[t0], lt1 = lam[t1];
-    const float s0 = __builtin_amdgcn_exp2f(lt0 - (L0 > 0 ? lam[(L0 - 1) * 32 + 31] : 0.0f));
-    const float s1 = __builtin_amdgcn_exp2f(lt1 - lam[(L1 - 1) * 32 + 31]);
+    // from the last block end (tile start if none) to the token: <= 1
+    const float sc = __builtin_amdgcn_exp2f(lt - prev);
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb) {
-      acc[0][pb] *= s0;
-      acc[1][pb] *= s1;
+      const Frag8<bf16> xt = lds_frag(XT + swz(prow[pb], L * 32 + g * 8));
+      acc[pb] = mma(xt, m, acc[pb] * sc);
     }
 
-    // Diagonal block: M[t][s] = G[t][s] exp2(lam_t - lam_s) dt_s for s <= t,
-    // plus D on s == t (the skip term D x_t).
-    auto diag = [&](f32x4 (&a)[kPB], const Frag8<bf16>& gfr, int q, int t, float lt) {
-      const int sb = q * 32 + g * 8;
-      const f32x4 la0 = *reinterpret_cast<const f32x4*>(lam + sb);
-      const f32x4 la1 = *reinterpret_cast<const f32x4*>(lam + sb + 4);
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(dtv + sb);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(dtv + sb + 4);
-      Frag8<bf16> m;
+    if (t < len) {
+      bf16* yb = k.y + (r0 + t) * k.ys + (int64_t)h * kP + g * 8;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int s = sb + j;
-        const float ls = j < 4 ? la0[j] : la1[j - 4];
-        const float ds = j < 4 ? d0[j] : d1[j - 4];
-        float v = static_cast<float>(gfr.v[j]) * __builtin_amdgcn_exp2f(lt - ls) * ds;
-        v = s <= t ? v : 0.0f;
-        v = s == t ? v + Dh : v;
-        m.v[j] = static_cast<bf16>(v);
+      for (int a = 0; a < 2; ++a) {
+        const uint2 lo = pack4(acc[2 * a]), hi = pack4(acc[2 * a + 1]);
+        *reinterpret_cast<uint4*>(yb + a * 32) = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
-#pragma unroll
-      for (int pb = 0; pb < kPB; ++pb) {
-        const Frag8<bf16> xt = lds_frag(XT + (pb * 16 + r16) * kXP + sb);
-        a[pb] = mma(xt, m, a[pb]);
-      }
-    };
-    diag(acc[0], gf0[L0], L0, t0, lt0);
-    diag(acc[1], gf1[L1], L1, t1, lt1);
-    if (c + 1 < c1) load_g(c + 1);
-
-    bf16* yb = k.y + (int64_t)h * kP + g * 4;
-    if (t0 < len) {
-#pragma unroll
-      for (int pb = 0; pb < kPB; ++pb)
-        *reinterpret_cast<uint2*>(yb + (r0 + t0) * k.ys + pb * 16) = pack4(acc[0][pb]);
     }
-    if (t1 < len) {
-#pragma unroll
-      for (int pb = 0; pb < kPB; ++pb)
-        *reinterpret_cast<uint2*>(yb + (r0 + t1) * k.ys + pb * 16) = pack4(acc[1][pb]);
-    }
+    load_g(cn);
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// State waves.  Wave u owns the state columns nb = 2u, 2u+1 for all rows:
-// H^T tiles D[n][p], lane (r, g) holds H[pb*16 + r][nb*16 + g*4 + i].  It
-// stages x rows 32u..32u+31 of each tile, and wave 4 (u = 0) also forms the
-// decay cumsums two tiles ahead.
+// State waves.  Wave u owns the state columns n in [32u, 32u + 32) for all
+// rows: H^T tiles D[m][p] (e = 0, 1), lane (r, g) holds
+// H[pb*16 + r][32u + g*8 + e*4 + i], eight consecutive columns over the two
+// tiles (the B^T fragments deal their rows in that order).
 template <bool OUT>
 __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int seg, int c0,
                             int c1, int u) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
-  bf16* xbuf = reinterpret_cast<bf16*>(smem);
-  bf16* hbuf = xbuf + 2 * 3 * kP * kXP;
-  float* dbuf = reinterpret_cast<float*>(hbuf + 2 * kP * kHP);
-  const int64_t rowb = (int64_t)b * k.seqlen;
-  const float Ah2 = k.A[h] * kLog2e;
+  const bf16* xbuf = reinterpret_cast<const bf16*>(smem);
+  bf16* hbuf = reinterpret_cast<bf16*>(smem) + 2 * 3 * kP * kXP;
+  const float* dbuf = reinterpret_cast<const float*>(hbuf + 2 * kP * kHP);
 
   f32x4 hacc[kNBW][kPB];
   {
@@ -318,144 +380,43 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
         hin = k.h0 + ((int64_t)b * k.n_heads + h) * (kP * kN);
     }
 #pragma unroll
-    for (int j = 0; j < kNBW; ++j)
+    for (int e = 0; e < kNBW; ++e)
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb)
-        hacc[j][pb] = hin ? *reinterpret_cast<const f32x4*>(
-                                hin + (pb * 16 + r16) * kN + (u * kNBW + j) * 16 + g * 4)
+        hacc[e][pb] = hin ? *reinterpret_cast<const f32x4*>(
+                                hin + (pb * 16 + r16) * kN + u * 32 + g * 8 + e * 4)
                           : f32x4{0, 0, 0, 0};
   }
-
-  // 0/1 selectors: Sel_j[k][n] = (k == j*16 + n), so X . Sel_j picks 16 of the
-  // 32 channels of a row block and returns them transposed.
-  Frag8<bf16> sel[2];
-#pragma unroll
-  for (int js = 0; js < 2; ++js)
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-      sel[js].v[jj] = static_cast<bf16>(g * 8 + jj == js * 16 + r16 ? 1.0f : 0.0f);
-
-  uint4 xr[2][2];  // x rows (2u + a)*16 + r, channels pc*32 + g*8 .. +7
-  auto load_x = [&](int c) {
-    const int64_t r0 = rowb + (int64_t)c * kQ;
-    const int last = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ) - 1;
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int s = min((2 * u + a) * 16 + r16, last);
-#pragma unroll
-      for (int pc = 0; pc < 2; ++pc)
-        xr[a][pc] = *reinterpret_cast<const uint4*>(k.x + (r0 + s) * k.xs + (int64_t)h * kP +
-                                                     pc * 32 + g * 8);
-    }
-  };
   Frag8<bf16> bt[kNBW][kSB];
-  auto load_bt = [&](int c) {
-    const uint4* f = k.frags + (((int64_t)b * k.ntiles + c) * kNFR + kNG) * 64 + lane;
+  auto load_bt = [&](int c, int ks) {  // one 32-token slice of this wave's B^T columns
+    const uint4* f = k.frags + (((int64_t)b * k.ntiles + c) * kNFR + kBT0) * 64 + lane;
 #pragma unroll
-    for (int j = 0; j < kNBW; ++j)
-#pragma unroll
-      for (int ks = 0; ks < kSB; ++ks) bt[j][ks] = as_frag(f[((u * kNBW + j) * kSB + ks) * 64]);
-  };
-  float dtr[2];  // wave 4: dt of tokens 2*lane, 2*lane + 1
-  auto load_dt = [&](int c) {
-    const int64_t r0 = rowb + (int64_t)c * kQ;
-    const int len = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int s = 2 * lane + e;
-      dtr[e] = s < len ? static_cast<float>(k.dt[(r0 + s) * k.dts + h]) : 0.0f;
-    }
-  };
-  // Lambda (inclusive cumsum of dt*A, log2 units), dt, block-end factor
-  // exp2(Lambda_e - Lambda_s) dt_s and end factor exp2(Lambda_end - Lambda_s) dt_s.
-  auto make_dec = [&](int buf) {
-    float* d = dbuf + buf * kDec;
-    const float v0 = dtr[0] * Ah2, v1 = dtr[1] * Ah2;
-    float incl = v0 + v1;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    const float l0 = incl - v1, l1 = incl;
-    const float lend = __shfl(incl, 63);
-    const float lblk = __shfl(incl, lane | 15);  // tokens 32q..32q+31 sit in lanes 16q..16q+15
-    *reinterpret_cast<float2*>(d + 2 * lane) = make_float2(l0, l1);
-    *reinterpret_cast<float2*>(d + kQ + 2 * lane) = make_float2(dtr[0], dtr[1]);
-    *reinterpret_cast<float2*>(d + 2 * kQ + 2 * lane) =
-        make_float2(__builtin_amdgcn_exp2f(lblk - l0) * dtr[0], __builtin_amdgcn_exp2f(lblk - l1) * dtr[1]);
-    *reinterpret_cast<float2*>(d + 3 * kQ + 2 * lane) =
-        make_float2(__builtin_amdgcn_exp2f(lend - l0) * dtr[0], __builtin_amdgcn_exp2f(lend - l1) * dtr[1]);
-    return lend;
-  };
-  // x tile -> LDS: plain (OUT), block-end scaled (OUT) and end scaled copies,
-  // each transposed to [channel][token].
-  auto commit = [&](int xb, int db) {
-    const float* d = dbuf + db * kDec;
-    bf16* XT = xbuf + (xb * 3 + 0) * kP * kXP;
-    bf16* XE = xbuf + (xb * 3 + 1) * kP * kXP;
-    bf16* XW = xbuf + (xb * 3 + 2) * kP * kXP;
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int s0 = (2 * u + a) * 16 + g * 4;
-      const f32x4 e4 = *reinterpret_cast<const f32x4*>(d + 2 * kQ + s0);
-      const f32x4 w4 = *reinterpret_cast<const f32x4*>(d + 3 * kQ + s0);
-#pragma unroll
-      for (int pc = 0; pc < 2; ++pc) {
-        const Frag8<bf16> xa = as_frag(xr[a][pc]);
-#pragma unroll
-        for (int js = 0; js < 2; ++js) {
-          // lane (r, g): x[s0 + i][pc*32 + js*16 + r], i = 0..3
-          const f32x4 v = mma(xa, sel[js], f32x4{0, 0, 0, 0});
-          const int p = pc * 32 + js * 16 + r16;
-          if (OUT) {
-            *reinterpret_cast<uint2*>(XT + p * kXP + s0) = pack4(v);
-            *reinterpret_cast<uint2*>(XE + p * kXP + s0) = pack4(v * e4);
-          }
-          *reinterpret_cast<uint2*>(XW + p * kXP + s0) = pack4(v * w4);
-        }
-      }
-    }
+    for (int j = 0; j < kNBW; ++j) bt[j][ks] = as_frag(f[((u * kNBW + j) * kSB + ks) * 64]);
   };
   auto write_hs = [&](int buf) {
     bf16* Hs = hbuf + buf * kP * kHP;
 #pragma unroll
-    for (int j = 0; j < kNBW; ++j)
-#pragma unroll
-      for (int pb = 0; pb < kPB; ++pb)
-        *reinterpret_cast<uint2*>(Hs + (pb * 16 + r16) * kHP + (u * kNBW + j) * 16 + g * 4) =
-            pack4(hacc[j][pb]);
+    for (int pb = 0; pb < kPB; ++pb) {
+      const uint2 lo = pack4(hacc[0][pb]), hi = pack4(hacc[1][pb]);
+      *reinterpret_cast<uint4*>(Hs + swz(pb * 16 + r16, u * 32 + g * 8)) =
+          make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
   };
 
-  const bool dec_wave = u == 0;
-  float lam_seg = 0.0f;
-  load_x(c0);
-  load_bt(c0);
-  if (dec_wave) {
-    load_dt(c0);
-    lam_seg += make_dec(c0 % 3);
-    if (c0 + 1 < c1) {
-      load_dt(c0 + 1);
-      lam_seg += make_dec((c0 + 1) % 3);
-    }
-    if (c0 + 2 < c1) load_dt(c0 + 2);
-  }
+  // The same loads in the same order every iteration (tile index clamped to
+  // the last tile), and the prologue ends with that sequence, so the
+  // compiler's vmcnt waits stay exact.
+  const int cl = c1 - 1;
   if (OUT) write_hs(c0 & 1);
-  __syncthreads();
-  commit(c0 & 1, c0 % 3);
-  if (c0 + 1 < c1) load_x(c0 + 1);
-  __syncthreads();
+#pragma unroll
+  for (int ks = 0; ks < kSB; ++ks) load_bt(c0, ks);
+  __syncthreads();  // decay cumsums of the first tiles
+  __syncthreads();  // x copies of the first tile
 
   for (int c = c0; c < c1; ++c) {
-    if (c + 1 < c1) {
-      commit((c + 1) & 1, (c + 1) % 3);
-      if (c + 2 < c1) load_x(c + 2);
-    }
-    if (dec_wave && c + 2 < c1) {
-      lam_seg += make_dec((c + 2) % 3);
-      if (c + 3 < c1) load_dt(c + 3);
-    }
-    // H <- exp2(Lambda_end) H + (B^T)(w o x): A operand B^T rows, B operand the end-scaled x
+    // H <- exp2(Lambda_end) H + (B^T)(w o x): A operand B^T rows, B operand
+    // the end-scaled x; each B^T slice is reloaded for the next tile as soon
+    // as its MFMAs are issued.
     const float* d = dbuf + (c % 3) * kDec;
     const float dec = __builtin_amdgcn_exp2f(d[kQ - 1]);
     const bf16* XW = xbuf + ((c & 1) * 3 + 2) * kP * kXP;
@@ -467,15 +428,13 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
     for (int ks = 0; ks < kSB; ++ks) {
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
-        const Frag8<bf16> xw = lds_frag(XW + (pb * 16 + r16) * kXP + ks * 32 + g * 8);
+        const Frag8<bf16> xw = lds_frag(XW + swz(pb * 16 + r16, ks * 32 + g * 8));
 #pragma unroll
         for (int j = 0; j < kNBW; ++j) hacc[j][pb] = mma(bt[j][ks], xw, hacc[j][pb]);
       }
+      load_bt(min(c + 1, cl), ks);
     }
-    if (c + 1 < c1) {
-      if (OUT) write_hs((c + 1) & 1);
-      load_bt(c + 1);
-    }
+    if (OUT && c + 1 < c1) write_hs((c + 1) & 1);
     __syncthreads();
   }
 
@@ -484,20 +443,157 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
     if (k.hT && seg == k.nseg - 1) hout = k.hT + ((int64_t)b * k.n_heads + h) * (kP * kN);
   } else {
     hout = k.seg_state + (((int64_t)b * k.heads + h) * k.nseg + seg) * (kP * kN);
-    if (dec_wave && lane == 0) k.seg_decay[((int64_t)b * k.heads + h) * k.nseg + seg] = lam_seg;
   }
   if (hout) {
 #pragma unroll
-    for (int j = 0; j < kNBW; ++j)
+    for (int e = 0; e < kNBW; ++e)
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb)
-        *reinterpret_cast<f32x4*>(hout + (pb * 16 + r16) * kN + (u * kNBW + j) * 16 + g * 4) =
-            hacc[j][pb];
+        *reinterpret_cast<f32x4*>(hout + (pb * 16 + r16) * kN + u * 32 + g * 8 + e * 4) =
+            hacc[e][pb];
   }
 }
 
+// ---------------------------------------------------------------------------
+// Stage waves.  Wave v stages x rows 32v..32v+31 of each tile into the three
+// transposed LDS copies one tile ahead; wave 8 (v = 0) also forms the decay
+// cumsums two tiles ahead.
 template <bool OUT>
-__global__ __launch_bounds__(512) void ssd_bf16_kernel(BK k) {
+__device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int seg, int c0,
+                            int c1, int v) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+  bf16* xbuf = reinterpret_cast<bf16*>(smem);
+  float* dbuf = reinterpret_cast<float*>(xbuf + 2 * 3 * kP * kXP + 2 * kP * kHP);
+  const int64_t rowb = (int64_t)b * k.seqlen;
+  const float Ah2 = k.A[h] * kLog2e;
+
+  // 0/1 selectors: Sel_j[k][n] = (k == j*16 + n), so X . Sel_j picks 16 of the
+  // 32 channels of a row block and returns them transposed.
+  Frag8<bf16> sel[2];
+#pragma unroll
+  for (int js = 0; js < 2; ++js)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      sel[js].v[jj] = static_cast<bf16>(g * 8 + jj == js * 16 + r16 ? 1.0f : 0.0f);
+
+  // x rows 32v + (r/4)*8 + e*4 + r%4 (A-operand row r of transpose e),
+  // channels pc*32 + g*8 .. +7: the transposes then leave lane (p, g) the
+  // eight consecutive tokens 32v + g*8 .. +7.
+  uint4 xr[2][2];
+  auto load_x = [&](int c) {
+    const int64_t r0 = rowb + (int64_t)c * kQ;
+    const int last = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ) - 1;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int s = min(v * 32 + (r16 >> 2) * 8 + a * 4 + (r16 & 3), last);
+#pragma unroll
+      for (int pc = 0; pc < 2; ++pc)
+        xr[a][pc] = *reinterpret_cast<const uint4*>(k.x + (r0 + s) * k.xs + (int64_t)h * kP +
+                                                     pc * 32 + g * 8);
+    }
+  };
+  // dt of tokens 2*lane, 2*lane + 1 of a tile (head-major copy), kept raw
+  // until make_dec (a conversion here would make the wave wait for the load)
+  uint32_t dtr_raw;
+  auto load_dt = [&](int c) {
+    dtr_raw = reinterpret_cast<const uint32_t*>(
+        k.dtT + (((int64_t)b * k.ntiles + c) * k.heads + h) * kQ)[lane];
+  };
+  // Lambda (inclusive cumsum of dt*A, log2 units), dt, block-end factor
+  // exp2(Lambda_e - Lambda_s) dt_s and end factor exp2(Lambda_end - Lambda_s) dt_s
+  // of tile c (dt = 0 past the end of the sequence).
+  auto make_dec = [&](int c, int buf) {
+    const int len = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ);
+    float dtr[2];
+    dtr[0] = 2 * lane < len ? __builtin_bit_cast(float, dtr_raw << 16) : 0.0f;
+    dtr[1] = 2 * lane + 1 < len ? __builtin_bit_cast(float, dtr_raw & 0xffff0000u) : 0.0f;
+    float* d = dbuf + buf * kDec;
+    const float v0 = dtr[0] * Ah2, v1 = dtr[1] * Ah2;
+    // inclusive scan over the wave with DPP row shifts and row broadcasts
+    float incl = v0 + v1;
+    incl += dpp_f<0x111, 0xf>(incl);  // row_shr:1
+    incl += dpp_f<0x112, 0xf>(incl);  // row_shr:2
+    incl += dpp_f<0x114, 0xf>(incl);  // row_shr:4
+    incl += dpp_f<0x118, 0xf>(incl);  // row_shr:8
+    incl += dpp_f<0x142, 0xa>(incl);  // row_bcast:15 into rows 1 and 3
+    incl += dpp_f<0x143, 0xc>(incl);  // row_bcast:31 into rows 2 and 3
+    const float l0 = incl - v1, l1 = incl;
+    const float lend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
+    // tokens 32q..32q+31 sit in lanes 16q..16q+15: the block end is lane 16q+15
+    const float e0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 15));
+    const float e1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 31));
+    const float e2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 47));
+    const int row = lane >> 4;
+    const float lblk = row == 0 ? e0 : row == 1 ? e1 : row == 2 ? e2 : lend;
+    *reinterpret_cast<float2*>(d + 2 * lane) = make_float2(l0, l1);
+    *reinterpret_cast<float2*>(d + kQ + 2 * lane) = make_float2(dtr[0], dtr[1]);
+    *reinterpret_cast<float2*>(d + 2 * kQ + 2 * lane) =
+        make_float2(__builtin_amdgcn_exp2f(lblk - l0) * dtr[0], __builtin_amdgcn_exp2f(lblk - l1) * dtr[1]);
+    *reinterpret_cast<float2*>(d + 3 * kQ + 2 * lane) =
+        make_float2(__builtin_amdgcn_exp2f(lend - l0) * dtr[0], __builtin_amdgcn_exp2f(lend - l1) * dtr[1]);
+    return lend;
+  };
+  // x tile -> LDS: plain (OUT), block-end scaled (OUT) and end scaled copies,
+  // each transposed to [channel][token], 16-byte writes.
+  auto commit = [&](int xb, int db) {
+    const float* d = dbuf + db * kDec;
+    bf16* XT = xbuf + (xb * 3 + 0) * kP * kXP;
+    bf16* XE = xbuf + (xb * 3 + 1) * kP * kXP;
+    bf16* XW = xbuf + (xb * 3 + 2) * kP * kXP;
+    const int s0 = v * 32 + g * 8;
+    const f32x4 ea = *reinterpret_cast<const f32x4*>(d + 2 * kQ + s0);
+    const f32x4 eb = *reinterpret_cast<const f32x4*>(d + 2 * kQ + s0 + 4);
+    const f32x4 wa = *reinterpret_cast<const f32x4*>(d + 3 * kQ + s0);
+    const f32x4 wb = *reinterpret_cast<const f32x4*>(d + 3 * kQ + s0 + 4);
+    auto pack8 = [](const f32x4& lo, const f32x4& hi) {
+      const uint2 a = pack4(lo), b2 = pack4(hi);
+      return make_uint4(a.x, a.y, b2.x, b2.y);
+    };
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pc = q >> 1, js = q & 1;
+      // lane (r, g): x[s0 + e*4 + i][pc*32 + js*16 + r] in va (e = 0), vb (e = 1)
+      const f32x4 va = mma(as_frag(xr[0][pc]), sel[js], f32x4{0, 0, 0, 0});
+      const f32x4 vb = mma(as_frag(xr[1][pc]), sel[js], f32x4{0, 0, 0, 0});
+      const int off = swz(pc * 32 + js * 16 + r16, s0);
+      if (OUT) {
+        *reinterpret_cast<uint4*>(XT + off) = pack8(va, vb);
+        *reinterpret_cast<uint4*>(XE + off) = pack8(va * ea, vb * eb);
+      }
+      *reinterpret_cast<uint4*>(XW + off) = pack8(va * wa, vb * wb);
+    }
+  };
+
+  // The same loads in the same order every iteration (x, dt; tile indices
+  // clamped to the last tile), and the prologue ends with that sequence, so
+  // the compiler's vmcnt waits stay exact.  Only wave 8 uses the dt values.
+  const bool dec_wave = v == 0;
+  const int cl = c1 - 1;
+  float lam_seg = 0.0f;
+  load_x(c0);
+  load_dt(c0);
+  if (dec_wave) lam_seg += make_dec(c0, c0 % 3);
+  load_dt(min(c0 + 1, cl));
+  if (dec_wave && c0 + 1 < c1) lam_seg += make_dec(c0 + 1, (c0 + 1) % 3);
+  __syncthreads();
+  commit(c0 & 1, c0 % 3);
+  load_x(min(c0 + 1, cl));
+  load_dt(min(c0 + 2, cl));
+  __syncthreads();
+
+  for (int c = c0; c < c1; ++c) {
+    if (c + 1 < c1) commit((c + 1) & 1, (c + 1) % 3);
+    load_x(min(c + 2, cl));
+    if (dec_wave && c + 2 < c1) lam_seg += make_dec(c + 2, (c + 2) % 3);
+    load_dt(min(c + 3, cl));
+    __syncthreads();
+  }
+  if (!OUT && dec_wave && lane == 0)
+    k.seg_decay[((int64_t)b * k.heads + h) * k.nseg + seg] = lam_seg;
+}
+
+template <bool OUT>
+__global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(BK k) {
   extern __shared__ __align__(16) unsigned char smem[];
   // XCD-aware unit mapping: consecutive workgroups go to different XCDs, so
   // give each XCD a contiguous block of (sequence, head, segment) units; the
@@ -512,11 +608,18 @@ __global__ __launch_bounds__(512) void ssd_bf16_kernel(BK k) {
   if (c0 >= c1) return;  // whole workgroup
   // wave index as a scalar, so the role branch below is uniform per wave
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave >= 4) {
-    state_waves<OUT>(k, smem, b, h, seg, c0, c1, wave - 4);
+  if (wave >= 12) {
+    stage_waves<OUT>(k, smem, b, h, seg, c0, c1, wave - 12);
+  } else if (wave >= 8) {
+    state_waves<OUT>(k, smem, b, h, seg, c0, c1, wave - 8);
   } else if (OUT) {
-    if (wave < 2) output_waves<0>(k, smem, b, h, c0, c1, wave);
-    else output_waves<1>(k, smem, b, h, c0, c1, wave);
+    const int tb = wave < 4 ? wave : kTB + 3 - wave;  // 0 1 2 3 7 6 5 4
+    switch (tb >> 1) {
+      case 0: output_wave<0>(k, smem, b, h, c0, c1, tb); break;
+      case 1: output_wave<1>(k, smem, b, h, c0, c1, tb); break;
+      case 2: output_wave<2>(k, smem, b, h, c0, c1, tb); break;
+      default: output_wave<3>(k, smem, b, h, c0, c1, tb); break;
+    }
   } else {
     // no outputs in the prepass: keep the barrier count of the state waves
     for (int i = 0; i < c1 - c0 + 2; ++i) __syncthreads();
@@ -547,6 +650,11 @@ size_t frag_region_bytes(int64_t batch, int64_t seqlen) {
   const size_t bytes = (size_t)(batch * nt) * kNFR * kFragBytes;
   return (bytes + 255) & ~(size_t)255;
 }
+size_t dt_region_bytes(int64_t batch, int64_t seqlen, int64_t heads) {
+  const int64_t nt = (seqlen + kQ - 1) / kQ;
+  const size_t bytes = (size_t)(batch * nt * heads) * kQ * sizeof(bf16);
+  return (bytes + 255) & ~(size_t)255;
+}
 
 }  // namespace
 
@@ -557,7 +665,7 @@ bool bf16_path(int64_t d_head, int64_t d_state, int64_t chunk, int dtype) {
 size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads) {
   int nt, nseg, per;
   fwd_plan(batch, seqlen, heads, kQ, &nt, &nseg, &per);
-  size_t bytes = frag_region_bytes(batch, seqlen);
+  size_t bytes = frag_region_bytes(batch, seqlen) + dt_region_bytes(batch, seqlen, heads);
   if (nseg > 1) bytes += (size_t)(batch * heads * nseg) * (size_t)(kP * kN + 1) * sizeof(float);
   return bytes;
 }
@@ -573,17 +681,21 @@ hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
   k.h0 = a.h0; k.hT = a.hT;
   k.seqlen = a.seqlen; k.n_heads = a.n_heads; k.heads = a.heads;
   fwd_plan(a.batch, a.seqlen, a.heads, kQ, &k.ntiles, &k.nseg, &k.seg_chunks);
-  uint4* frags = static_cast<uint4*>(ws);
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  uint4* frags = reinterpret_cast<uint4*>(wsb);
+  bf16* dtT = reinterpret_cast<bf16*>(wsb + frag_region_bytes(a.batch, a.seqlen));
   k.frags = frags;
+  k.dtT = dtT;
   k.seg_state = nullptr;
   k.seg_decay = nullptr;
   if (k.nseg > 1) {
-    k.seg_state = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) +
-                                           frag_region_bytes(a.batch, a.seqlen));
+    k.seg_state = reinterpret_cast<float*>(wsb + frag_region_bytes(a.batch, a.seqlen) +
+                                           dt_region_bytes(a.batch, a.seqlen, a.heads));
     k.seg_decay = k.seg_state + (size_t)a.batch * a.heads * k.nseg * kP * kN;
   }
-  hipLaunchKernelGGL(chunk_gram_kernel, dim3(k.ntiles, (unsigned)a.batch), dim3(256), 0, s,
-                     static_cast<const bf16*>(a.B), a.bs, k.C, a.cs, frags, a.seqlen, k.ntiles);
+  hipLaunchKernelGGL(tile_prep_kernel, dim3(k.ntiles, (unsigned)a.batch, kNG / 4 + 2), dim3(256), 0, s,
+                     static_cast<const bf16*>(a.B), a.bs, k.C, a.cs, k.dt, a.dts, frags, dtT,
+                     a.seqlen, k.ntiles, a.heads);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (k.nseg > 1) {
@@ -591,7 +703,7 @@ hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(pre),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(pre, dim3(k.nseg - 1, a.heads, (unsigned)a.batch), dim3(512), kLds, s, k);
+    hipLaunchKernelGGL(pre, dim3(k.nseg - 1, a.heads, (unsigned)a.batch), dim3(kThreads), kLds, s, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(seg_combine_bf16_kernel, dim3(a.heads, (unsigned)a.batch), dim3(256), 0, s,
                        k.seg_state, k.seg_decay, a.h0, a.n_heads, a.heads, k.nseg);
@@ -601,7 +713,7 @@ hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(main_k),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(main_k, dim3(k.nseg, a.heads, (unsigned)a.batch), dim3(512), kLds, s, k);
+  hipLaunchKernelGGL(main_k, dim3(k.nseg, a.heads, (unsigned)a.batch), dim3(kThreads), kLds, s, k);
   return hipGetLastError();
 }
 

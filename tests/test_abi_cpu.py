@@ -83,9 +83,10 @@ def test_workspace_query(lib):
     # fp32, 256 (sequence, head) units: one segment, nothing to stage
     assert f(4, 8192, 64, 64, 128, 1, 64, 128, 0, ctypes.byref(out)) == 0
     assert out.value == 0
-    # bf16 d_head 64 d_state 128: per-tile G and B^T fragments, 52 KB per tile
+    # bf16 d_head 64 d_state 128: per 128-token tile, G, B^T and C fragments
+    # (84 KB, shared by the heads) and a head-major dt row per active head
     assert f(4, 8192, 64, 64, 128, 1, 64, 256, 1, ctypes.byref(out)) == 0
-    assert out.value == 4 * 64 * 52 * 1024
+    assert out.value == 4 * 64 * (84 * 1024 + 64 * 128 * 2)
 
 
 def test_segments_query(lib):

@@ -149,6 +149,24 @@ def test_scan_long_context_segments(m):
     assert e_y < TOL[torch.bfloat16] and e_h < TOL[torch.bfloat16]
 
 
+def test_scan_more_than_64_heads_segmented():
+    """A block wider than the 130M one (96 heads of 64, 80 active): the
+    per-tile dt staging runs over the heads in groups of 64, and the few
+    (sequence, head) units split a ragged 3-tile sequence into segments."""
+    import dataclasses
+    w = dataclasses.replace(M130, d_model=3072, d_inner=6144)
+    h = 80
+    inp = synth.forward_inputs(w, batch=1, seqlen=300, with_state=True)
+    assert mm.ssd_forward_segments(1, 300, w.n_heads, 64, 128, 1, h, 256, w.dtype) > 1
+    say(f"scan bf16 wide block: {w.n_heads} heads, {h} active, l=300")
+    y, hT = run_forward(inp, h, 256)
+    sample = [0, 63, 64, 79]
+    yr, hr = oracle_forward(inp, h, head_idx=sample)
+    e_y, e_h = rel_l2(y[:, :, sample], yr), rel_l2(hT[:, sample], hr)
+    say(f"  rel_l2 y={e_y:.3e} state={e_h:.3e}")
+    assert e_y < TOL[torch.bfloat16] and e_h < TOL[torch.bfloat16]
+
+
 def test_scan_long_context_full_length_sampled():
     w = LONG
     h = w.heads(256)
