@@ -51,14 +51,12 @@ constexpr int kPB = kP / 16;   // 16-wide d_head blocks
 constexpr int kNB = kN / 16;   // 16-wide d_state blocks
 constexpr int kKB = kN / 32;   // K=32 slices over d_state
 constexpr int kNBW = kNB / 4;  // state column blocks per state wave
-constexpr int kXP = kQ + 8;    // LDS row pitch (elements) of the transposed x copies
 constexpr int kHP = kN + 8;    // LDS row pitch (elements) of the operand copy of H
 constexpr int kXcds = 8;
 // 16 waves, four per SIMD: 0-7 outputs (one 16-token block each; waves w and
 // w+4 share a SIMD and take blocks whose causal work adds up the same), 8-11
 // state update, 12-15 x staging and decay cumsums.
 constexpr int kThreads = 16 * 64;
-static_assert(kHP == kXP, "x copies and the H copy share one swizzled row layout");
 
 // G fragments (tb, k) exist for the 32-token blocks k <= tb/2 (causal,
 // diagonal block included), numbered tb-major.
@@ -71,10 +69,13 @@ constexpr int kC0 = kBT0 + kNB * kSB;            // first C fragment (tb, kb): k
 constexpr int kNFR = kC0 + kTB * kKB;            // fragments per (sequence, tile): 84
 constexpr size_t kFragBytes = 64 * 16;           // one wave-wide fragment
 
-constexpr size_t kXTile = (size_t)kP * kXP * sizeof(bf16);
+constexpr int kXE = kQ * kP;  // elements of one x tile in LDS ([token][column], 128 B rows)
+// Per buffer three x tiles: plain (diagonal blocks), scaled by the block-end
+// factor (off-diagonal blocks) and by the end factor (state update).
+constexpr int kXBuf = 3 * kXE;
 constexpr size_t kHTile = (size_t)kP * kHP * sizeof(bf16);
 constexpr size_t kDec = 4 * kQ;  // floats: Lambda, dt, block-end factor, end factor
-constexpr size_t kLds = 2 * 3 * kXTile + 2 * kHTile + 3 * kDec * sizeof(float);
+constexpr size_t kLds = 2 * kXBuf * sizeof(bf16) + 2 * kHTile + 3 * kDec * sizeof(float);
 
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -89,13 +90,60 @@ __device__ __forceinline__ Frag8<bf16> as_frag(uint4 u) {
 __device__ __forceinline__ Frag8<bf16> lds_frag(const bf16* p) {
   return as_frag(*reinterpret_cast<const uint4*>(p));
 }
-// Element offset of (row, col) in a [64][kXP] LDS tile, col a multiple of 8.
-// The 16-byte chunks of rows 8-15 of every 16 rows are XOR-ed with 4: the
-// A-operand row orders used below (rows r and r + 8 read by lanes of the
-// same 8-lane group) then hit distinct banks, and natural row orders stay
-// conflict-free.
+// Element offset of (row, col) in the [64][kHP] LDS copy of H, col a
+// multiple of 8.  The 16-byte chunks of rows 8-15 of every 16 rows are XOR-ed
+// with 4: the A-operand row orders used below (rows r and r + 8 read by lanes
+// of the same 8-lane group) then hit distinct banks, and natural row orders
+// stay conflict-free.
 __device__ __forceinline__ int swz(int row, int col) {
-  return row * kXP + (col ^ (((row >> 3) & 1) << 5));
+  return row * kHP + (col ^ (((row >> 3) & 1) << 5));
+}
+
+// Channel held at column c of an operand tile: tile pb = c/16, row m = c%16
+// is channel (pb/2)*32 + (m/4)*8 + (pb%2)*4 + m%4.  Output tiles 2a and 2a+1
+// then leave a lane eight consecutive channels (one 16-byte store).
+__device__ __forceinline__ int chan(int pb, int m) {
+  return (pb >> 1) * 32 + (m >> 2) * 8 + (pb & 1) * 4 + (m & 3);
+}
+
+// x tile in LDS: row s (token) holds the 64 channels in column order
+// (column c = channel chan(c/16, c%16)), 8 chunks of 16 bytes per 128-byte
+// row, chunk index XOR-ed with 2*(s%4).  Element offset of (s, chunk, half):
+__device__ __forceinline__ int xoff(int s, int chunk, int half) {
+  return s * kP + ((chunk ^ ((s & 3) << 1)) << 3) + half * 4;
+}
+
+// MFMA operand of 8 consecutive tokens sb..sb+7 (sb = block start + g*8) for
+// columns pb*16 + r of the x tile, read with two LDS transpose loads: within
+// each 16-lane group, lane i receives element i%4 of the 8 bytes that lane
+// 4k + i/4 addresses, for k = 0..3.  Lane src therefore addresses token
+// sb + src/4 (+4 for the second load), columns pb*16 + 4*(src%4) .. +3.
+// The XOR of the chunk index makes the four rows of a group hit 32 distinct
+// banks.
+typedef short short4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ Frag8<bf16> x_frag(const bf16* X, int sb, int pb, int lane) {
+  const int src = lane & 15;
+  const int chunk = 2 * pb + ((src & 3) >> 1), half = src & 1;
+  const int s1 = sb + (src >> 2);
+  typedef __attribute__((address_space(3))) short4v lds_short4;
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4*)(const_cast<bf16*>(X) + xoff(s1, chunk, half)));
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4*)(const_cast<bf16*>(X) + xoff(s1 + 4, chunk, half)));
+  Frag8<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return f;
+}
+
+// f[j] *= sc[j] for the 8 operand values of a fragment (rounded back to bf16)
+__device__ __forceinline__ Frag8<bf16> scale8(const Frag8<bf16>& f, const f32x4& a, const f32x4& b) {
+  Frag8<bf16> r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r.v[j] = static_cast<bf16>(static_cast<float>(f.v[j]) * a[j]);
+    r.v[j + 4] = static_cast<bf16>(static_cast<float>(f.v[j + 4]) * b[j]);
+  }
+  return r;
 }
 
 // Lane value moved by a DPP pattern; lanes with no source (or outside the
@@ -242,7 +290,7 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
                             int tb) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
   const bf16* xbuf = reinterpret_cast<const bf16*>(smem);
-  const bf16* hbuf = xbuf + 2 * 3 * kP * kXP;
+  const bf16* hbuf = xbuf + 2 * kXBuf;
   const float* dbuf = reinterpret_cast<const float*>(hbuf + 2 * kP * kHP);
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Dh = k.D ? k.D[h] : 0.0f;
@@ -251,7 +299,7 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
   // A-operand row (channel) of this lane in tile pb
   int prow[kPB];
 #pragma unroll
-  for (int pb = 0; pb < kPB; ++pb) prow[pb] = (pb >> 1) * 32 + (r16 >> 2) * 8 + (pb & 1) * 4 + (r16 & 3);
+  for (int pb = 0; pb < kPB; ++pb) prow[pb] = chan(pb, r16);
 
   Frag8<bf16> cf[kKB];
   Frag8<bf16> gf[L + 1];
@@ -275,8 +323,8 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
     const int len = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ);
     const int64_t r0 = rowb + (int64_t)c * kQ;
     const bf16* Hs = hbuf + (c & 1) * kP * kHP;
-    const bf16* XT = xbuf + ((c & 1) * 3 + 0) * kP * kXP;
-    const bf16* XE = xbuf + ((c & 1) * 3 + 1) * kP * kXP;
+    const bf16* XT = xbuf + (c & 1) * kXBuf;
+    const bf16* XE = XT + kXE;
     const float* lam = dbuf + (c % 3) * kDec;
     const float* dtv = lam + kQ;
 
@@ -332,16 +380,16 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
       prev = eq;
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
-        const Frag8<bf16> xe = lds_frag(XE + swz(prow[pb], q * 32 + g * 8));
-        acc[pb] = mma(xe, gf[q], acc[pb] * r);
+        const Frag8<bf16> xf = x_frag(XE, q * 32 + g * 8, pb, lane);
+        acc[pb] = mma(xf, gf[q], acc[pb] * r);
       }
     }
     // from the last block end (tile start if none) to the token: <= 1
     const float sc = __builtin_amdgcn_exp2f(lt - prev);
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb) {
-      const Frag8<bf16> xt = lds_frag(XT + swz(prow[pb], L * 32 + g * 8));
-      acc[pb] = mma(xt, m, acc[pb] * sc);
+      const Frag8<bf16> xf = x_frag(XT, L * 32 + g * 8, pb, lane);
+      acc[pb] = mma(xf, m, acc[pb] * sc);
     }
 
     if (t < len) {
@@ -360,14 +408,14 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
 // ---------------------------------------------------------------------------
 // State waves.  Wave u owns the state columns n in [32u, 32u + 32) for all
 // rows: H^T tiles D[m][p] (e = 0, 1), lane (r, g) holds
-// H[pb*16 + r][32u + g*8 + e*4 + i], eight consecutive columns over the two
+// H[chan(pb, r)][32u + g*8 + e*4 + i], eight consecutive columns over the two
 // tiles (the B^T fragments deal their rows in that order).
 template <bool OUT>
 __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int seg, int c0,
                             int c1, int u) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
   const bf16* xbuf = reinterpret_cast<const bf16*>(smem);
-  bf16* hbuf = reinterpret_cast<bf16*>(smem) + 2 * 3 * kP * kXP;
+  bf16* hbuf = reinterpret_cast<bf16*>(smem) + 2 * kXBuf;
   const float* dbuf = reinterpret_cast<const float*>(hbuf + 2 * kP * kHP);
 
   f32x4 hacc[kNBW][kPB];
@@ -384,7 +432,7 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb)
         hacc[e][pb] = hin ? *reinterpret_cast<const f32x4*>(
-                                hin + (pb * 16 + r16) * kN + u * 32 + g * 8 + e * 4)
+                                hin + chan(pb, r16) * kN + u * 32 + g * 8 + e * 4)
                           : f32x4{0, 0, 0, 0};
   }
   Frag8<bf16> bt[kNBW][kSB];
@@ -398,7 +446,7 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb) {
       const uint2 lo = pack4(hacc[0][pb]), hi = pack4(hacc[1][pb]);
-      *reinterpret_cast<uint4*>(Hs + swz(pb * 16 + r16, u * 32 + g * 8)) =
+      *reinterpret_cast<uint4*>(Hs + swz(chan(pb, r16), u * 32 + g * 8)) =
           make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
   };
@@ -414,12 +462,12 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
   __syncthreads();  // x copies of the first tile
 
   for (int c = c0; c < c1; ++c) {
-    // H <- exp2(Lambda_end) H + (B^T)(w o x): A operand B^T rows, B operand
-    // the end-scaled x; each B^T slice is reloaded for the next tile as soon
-    // as its MFMAs are issued.
+    // H <- exp2(Lambda_end) H + B^T (w o x): A operand B^T rows, B operand
+    // the end-scaled x (transposed LDS reads); each B^T slice is reloaded for
+    // the next tile as soon as its MFMAs are issued.
     const float* d = dbuf + (c % 3) * kDec;
     const float dec = __builtin_amdgcn_exp2f(d[kQ - 1]);
-    const bf16* XW = xbuf + ((c & 1) * 3 + 2) * kP * kXP;
+    const bf16* XW = xbuf + (c & 1) * kXBuf + 2 * kXE;
 #pragma unroll
     for (int j = 0; j < kNBW; ++j)
 #pragma unroll
@@ -428,9 +476,9 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
     for (int ks = 0; ks < kSB; ++ks) {
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
-        const Frag8<bf16> xw = lds_frag(XW + swz(pb * 16 + r16, ks * 32 + g * 8));
+        const Frag8<bf16> xf = x_frag(XW, ks * 32 + g * 8, pb, lane);
 #pragma unroll
-        for (int j = 0; j < kNBW; ++j) hacc[j][pb] = mma(bt[j][ks], xw, hacc[j][pb]);
+        for (int j = 0; j < kNBW; ++j) hacc[j][pb] = mma(bt[j][ks], xf, hacc[j][pb]);
       }
       load_bt(min(c + 1, cl), ks);
     }
@@ -449,47 +497,66 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
     for (int e = 0; e < kNBW; ++e)
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb)
-        *reinterpret_cast<f32x4*>(hout + (pb * 16 + r16) * kN + u * 32 + g * 8 + e * 4) =
+        *reinterpret_cast<f32x4*>(hout + chan(pb, r16) * kN + u * 32 + g * 8 + e * 4) =
             hacc[e][pb];
   }
 }
 
 // ---------------------------------------------------------------------------
-// Stage waves.  Wave v stages x rows 32v..32v+31 of each tile into the three
-// transposed LDS copies one tile ahead; wave 8 (v = 0) also forms the decay
-// cumsums two tiles ahead.
+// Stage waves.  Wave v copies tokens 32v..32v+31 of each tile into the three
+// LDS x tiles (plain, times the block-end factor, times the end factor) one
+// tile ahead (layout at xoff); wave 12 (v = 0) also forms the decay cumsums
+// two tiles ahead.
 template <bool OUT>
 __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int seg, int c0,
                             int c1, int v) {
-  const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x & 63;
   bf16* xbuf = reinterpret_cast<bf16*>(smem);
-  float* dbuf = reinterpret_cast<float*>(xbuf + 2 * 3 * kP * kXP + 2 * kP * kHP);
+  float* dbuf = reinterpret_cast<float*>(xbuf + 2 * kXBuf + 2 * kP * kHP);
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Ah2 = k.A[h] * kLog2e;
 
-  // 0/1 selectors: Sel_j[k][n] = (k == j*16 + n), so X . Sel_j picks 16 of the
-  // 32 channels of a row block and returns them transposed.
-  Frag8<bf16> sel[2];
-#pragma unroll
-  for (int js = 0; js < 2; ++js)
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-      sel[js].v[jj] = static_cast<bf16>(g * 8 + jj == js * 16 + r16 ? 1.0f : 0.0f);
-
-  // x rows 32v + (r/4)*8 + e*4 + r%4 (A-operand row r of transpose e),
-  // channels pc*32 + g*8 .. +7: the transposes then leave lane (p, g) the
-  // eight consecutive tokens 32v + g*8 .. +7.
-  uint4 xr[2][2];
+  // load i: token 32v + 8i + lane/8, channels 8*(lane%8) .. +7 (16 bytes)
+  uint4 xr[4];
   auto load_x = [&](int c) {
     const int64_t r0 = rowb + (int64_t)c * kQ;
     const int last = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ) - 1;
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int s = min(v * 32 + (r16 >> 2) * 8 + a * 4 + (r16 & 3), last);
+    for (int i = 0; i < 4; ++i) {
+      const int s = min(v * 32 + i * 8 + (lane >> 3), last);
+      xr[i] = *reinterpret_cast<const uint4*>(k.x + (r0 + s) * k.xs + (int64_t)h * kP + (lane & 7) * 8);
+    }
+  };
+  // channels a*32 + j*8 + e*4 + (0..3) sit at columns (2a + e)*16 + 4j + (0..3)
+  auto commit = [&](int xb, int db) {
+    bf16* XT = xbuf + xb * kXBuf;
+    const float* d = dbuf + db * kDec;
+    const int q = lane & 7, a = q >> 2, j = q & 3;
+    auto scaled = [](const uint4& u, float f) {
+      const bf16x8 x = __builtin_bit_cast(bf16x8, u);
+      f32x4 lo, hi;
 #pragma unroll
-      for (int pc = 0; pc < 2; ++pc)
-        xr[a][pc] = *reinterpret_cast<const uint4*>(k.x + (r0 + s) * k.xs + (int64_t)h * kP +
-                                                     pc * 32 + g * 8);
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = static_cast<float>(x[e]) * f;
+        hi[e] = static_cast<float>(x[e + 4]) * f;
+      }
+      const uint2 pl = pack4(lo), ph = pack4(hi);
+      return make_uint4(pl.x, pl.y, ph.x, ph.y);
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = v * 32 + i * 8 + (lane >> 3);
+      const int o0 = xoff(s, 4 * a + (j >> 1), j & 1), o1 = xoff(s, 4 * a + 2 + (j >> 1), j & 1);
+      const uint4 xe = scaled(xr[i], d[2 * kQ + s]);
+      const uint4 xw = scaled(xr[i], d[3 * kQ + s]);
+      if (OUT) {
+        *reinterpret_cast<uint2*>(XT + o0) = make_uint2(xr[i].x, xr[i].y);
+        *reinterpret_cast<uint2*>(XT + o1) = make_uint2(xr[i].z, xr[i].w);
+        *reinterpret_cast<uint2*>(XT + kXE + o0) = make_uint2(xe.x, xe.y);
+        *reinterpret_cast<uint2*>(XT + kXE + o1) = make_uint2(xe.z, xe.w);
+      }
+      *reinterpret_cast<uint2*>(XT + 2 * kXE + o0) = make_uint2(xw.x, xw.y);
+      *reinterpret_cast<uint2*>(XT + 2 * kXE + o1) = make_uint2(xw.z, xw.w);
     }
   };
   // dt of tokens 2*lane, 2*lane + 1 of a tile (head-major copy), kept raw
@@ -533,40 +600,10 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
         make_float2(__builtin_amdgcn_exp2f(lend - l0) * dtr[0], __builtin_amdgcn_exp2f(lend - l1) * dtr[1]);
     return lend;
   };
-  // x tile -> LDS: plain (OUT), block-end scaled (OUT) and end scaled copies,
-  // each transposed to [channel][token], 16-byte writes.
-  auto commit = [&](int xb, int db) {
-    const float* d = dbuf + db * kDec;
-    bf16* XT = xbuf + (xb * 3 + 0) * kP * kXP;
-    bf16* XE = xbuf + (xb * 3 + 1) * kP * kXP;
-    bf16* XW = xbuf + (xb * 3 + 2) * kP * kXP;
-    const int s0 = v * 32 + g * 8;
-    const f32x4 ea = *reinterpret_cast<const f32x4*>(d + 2 * kQ + s0);
-    const f32x4 eb = *reinterpret_cast<const f32x4*>(d + 2 * kQ + s0 + 4);
-    const f32x4 wa = *reinterpret_cast<const f32x4*>(d + 3 * kQ + s0);
-    const f32x4 wb = *reinterpret_cast<const f32x4*>(d + 3 * kQ + s0 + 4);
-    auto pack8 = [](const f32x4& lo, const f32x4& hi) {
-      const uint2 a = pack4(lo), b2 = pack4(hi);
-      return make_uint4(a.x, a.y, b2.x, b2.y);
-    };
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int pc = q >> 1, js = q & 1;
-      // lane (r, g): x[s0 + e*4 + i][pc*32 + js*16 + r] in va (e = 0), vb (e = 1)
-      const f32x4 va = mma(as_frag(xr[0][pc]), sel[js], f32x4{0, 0, 0, 0});
-      const f32x4 vb = mma(as_frag(xr[1][pc]), sel[js], f32x4{0, 0, 0, 0});
-      const int off = swz(pc * 32 + js * 16 + r16, s0);
-      if (OUT) {
-        *reinterpret_cast<uint4*>(XT + off) = pack8(va, vb);
-        *reinterpret_cast<uint4*>(XE + off) = pack8(va * ea, vb * eb);
-      }
-      *reinterpret_cast<uint4*>(XW + off) = pack8(va * wa, vb * wb);
-    }
-  };
 
   // The same loads in the same order every iteration (x, dt; tile indices
   // clamped to the last tile), and the prologue ends with that sequence, so
-  // the compiler's vmcnt waits stay exact.  Only wave 8 uses the dt values.
+  // the compiler's vmcnt waits stay exact.  Only wave 12 uses the dt values.
   const bool dec_wave = v == 0;
   const int cl = c1 - 1;
   float lam_seg = 0.0f;
