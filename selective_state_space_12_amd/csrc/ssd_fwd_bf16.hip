@@ -163,96 +163,96 @@ __device__ __forceinline__ float dpp_f(float v) {
 //   C fragment (tb, kb):   lane (r, g) holds C[tb*16 + r][kb*32 + g*8 + j]
 // and, per head, dt of the tile's tokens as one contiguous row (dtT).  Rows
 // past the end of the sequence repeat its last row (finite values that the
-// scan multiplies by dt = 0 or never stores).  blockIdx.z selects the part
-// (0..4: four G fragments each, one per wave; 5: B^T; 6: C and dt), so seven
-// small workgroups share a tile.
-__global__ __launch_bounds__(256) void tile_prep_kernel(const bf16* __restrict__ Bp, int64_t bs,
+// scan multiplies by dt = 0 or never stores).  One workgroup per tile stages
+// the B and C rows in LDS with whole-row loads and forms every fragment from
+// there.
+constexpr int kBCP = kN + 8;  // LDS row pitch (elements) of the staged B and C rows
+constexpr size_t kPrepLds = 2 * (size_t)kQ * kBCP * sizeof(bf16) + 64 * (kQ + 2) * sizeof(bf16);
+
+__global__ __launch_bounds__(512) void tile_prep_kernel(const bf16* __restrict__ Bp, int64_t bs,
                                                         const bf16* __restrict__ Cp, int64_t cs,
                                                         const bf16* __restrict__ dtp, int64_t dts,
                                                         uint4* __restrict__ frags,
                                                         bf16* __restrict__ dtT, int64_t seqlen,
                                                         int ntiles, int heads) {
-  __shared__ __align__(16) bf16 sh[kQ * (kN + 8)];
-  const int c = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
+  extern __shared__ __align__(16) unsigned char psm[];
+  bf16 (*Bs)[kBCP] = reinterpret_cast<bf16 (*)[kBCP]>(psm);
+  bf16 (*Cs)[kBCP] = reinterpret_cast<bf16 (*)[kBCP]>(psm + (size_t)kQ * kBCP * sizeof(bf16));
+  bf16 (*Dt)[kQ + 2] = reinterpret_cast<bf16 (*)[kQ + 2]>(psm + 2 * (size_t)kQ * kBCP * sizeof(bf16));
+  const int c = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
   const int64_t row0 = (int64_t)b * seqlen + (int64_t)c * kQ;
   const int last = (int)min((int64_t)kQ, seqlen - (int64_t)c * kQ) - 1;
   uint4* out = frags + ((int64_t)b * ntiles + c) * kNFR * 64;
 
-  constexpr int kGParts = kNG / 4;
-  static_assert(kNG % 4 == 0, "G fragments split over 4-wave workgroups");
-  if (part < kGParts) {
-    // G^T tiles: A operand row m takes B row k*32 + (m/4)*8 + m%4 (tile a) or
-    // that + 4 (tile b), B operand column n is C row tb*16 + n, so output slot
-    // i of lane (r, g) is G[tb*16 + r][k*32 + g*8 + i] (a) and [.. + 4 + i] (b).
-    {
-      const int f = part * 4 + wave;
-      int tb = 0;
-      while (gbase(tb + 1) <= f) ++tb;
-      const int k = f - gbase(tb);
-      const int sa = k * 32 + (r16 >> 2) * 8 + (r16 & 3);
-      const bf16* ba = Bp + (row0 + min(sa, last)) * bs + g * 8;
-      const bf16* bb = Bp + (row0 + min(sa + 4, last)) * bs + g * 8;
-      const bf16* cr = Cp + (row0 + min(tb * 16 + r16, last)) * cs + g * 8;
-      f32x4 da = {0, 0, 0, 0}, db = {0, 0, 0, 0};
+  for (int v = tid; v < kQ * (kN / 8); v += 512) {
+    const int s = v / (kN / 8), col = (v % (kN / 8)) * 8;
+    const int64_t r = row0 + min(s, last);
+    *reinterpret_cast<uint4*>(&Bs[s][col]) = *reinterpret_cast<const uint4*>(Bp + r * bs + col);
+    *reinterpret_cast<uint4*>(&Cs[s][col]) = *reinterpret_cast<const uint4*>(Cp + r * cs + col);
+  }
+  __syncthreads();
+
+  // G^T tiles: A operand row m takes B row k*32 + (m/4)*8 + m%4 (tile a) or
+  // that + 4 (tile b), B operand column n is C row tb*16 + n, so output slot
+  // i of lane (r, g) is G[tb*16 + r][k*32 + g*8 + i] (a) and [.. + 4 + i] (b).
+  for (int f = wave; f < kNG; f += 8) {
+    int tb = 0;
+    while (gbase(tb + 1) <= f) ++tb;
+    const int k = f - gbase(tb);
+    const int sa = k * 32 + (r16 >> 2) * 8 + (r16 & 3);
+    f32x4 da = {0, 0, 0, 0}, db = {0, 0, 0, 0};
 #pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) {
-        const Frag8<bf16> a0 = as_frag(*reinterpret_cast<const uint4*>(ba + kb * 32));
-        const Frag8<bf16> a1 = as_frag(*reinterpret_cast<const uint4*>(bb + kb * 32));
-        const Frag8<bf16> cb = as_frag(*reinterpret_cast<const uint4*>(cr + kb * 32));
-        da = mma(a0, cb, da);
-        db = mma(a1, cb, db);
-      }
-      const uint2 lo = pack4(da), hi = pack4(db);
-      out[f * 64 + lane] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    for (int kb = 0; kb < kKB; ++kb) {
+      const int n = kb * 32 + g * 8;
+      da = mma(lds_frag(&Bs[sa][n]), lds_frag(&Cs[tb * 16 + r16][n]), da);
+      db = mma(lds_frag(&Bs[sa + 4][n]), lds_frag(&Cs[tb * 16 + r16][n]), db);
     }
-  } else if (part == kGParts) {
-    bf16 (*Bt)[kN + 8] = reinterpret_cast<bf16 (*)[kN + 8]>(sh);
-    for (int v = tid; v < kQ * (kN / 8); v += 256) {
-      const int s = v / (kN / 8), col = (v % (kN / 8)) * 8;
-      *reinterpret_cast<uint4*>(&Bt[s][col]) =
-          *reinterpret_cast<const uint4*>(Bp + (row0 + min(s, last)) * bs + col);
+    const uint2 lo = pack4(da), hi = pack4(db);
+    out[f * 64 + lane] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+  // B^T fragments with LDS transpose loads: within each 16-lane group lane i
+  // receives element i%4 of the 8 bytes lane 4k + i/4 addresses (k = 0..3),
+  // so lane src addresses row ks*32 + g*8 + src/4 (+4), columns
+  // np*32 + (src%4)*8 + e*4 .. +3.
+  typedef __attribute__((address_space(3))) short4v lds_short4;
+  for (int f = wave; f < kNB * kSB; f += 8) {
+    const int npe = f / kSB, ks = f % kSB;  // npe = np*2 + e
+    const int src = lane & 15;
+    const int col = (npe >> 1) * 32 + (src & 3) * 8 + (npe & 1) * 4;
+    const int s1 = ks * 32 + g * 8 + (src >> 2);
+    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)&Bs[s1][col]);
+    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)&Bs[s1 + 4][col]);
+    out[(kBT0 + f) * 64 + lane] =
+        __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  for (int f = wave; f < kTB * kKB; f += 8) {
+    const int tb = f / kKB, kb = f % kKB;
+    out[(kC0 + f) * 64 + lane] = *reinterpret_cast<const uint4*>(&Cs[tb * 16 + r16][kb * 32 + g * 8]);
+  }
+
+  // dt, 64 heads at a time: [token][head] -> LDS -> [head][token]
+  bf16* dto = dtT + ((int64_t)b * ntiles + c) * heads * kQ;
+  for (int h0 = 0; h0 < heads; h0 += 64) {
+    const int nh = min(64, heads - h0);
+    // thread: head h0 + tid%64, tokens tid/64 + 8i; all 16 loads in flight
+    const int hh = tid & 63;
+    bf16 v[kQ / 8];
+#pragma unroll
+    for (int i = 0; i < kQ / 8; ++i) {
+      const int s = (tid >> 6) + 8 * i;
+      v[i] = dtp[(row0 + min(s, last)) * dts + h0 + min(hh, nh - 1)];
+    }
+    __syncthreads();  // previous group's rows have been written out
+    if (hh < nh) {
+#pragma unroll
+      for (int i = 0; i < kQ / 8; ++i) Dt[hh][(tid >> 6) + 8 * i] = v[i];
     }
     __syncthreads();
-    for (int f = wave; f < kNB * kSB; f += 4) {
-      const int npe = f / kSB, ks = f % kSB;  // npe = np*2 + e
-      const int n = (npe >> 1) * 32 + (r16 >> 2) * 8 + (npe & 1) * 4 + (r16 & 3);
-      bf16x8 v;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = Bt[ks * 32 + g * 8 + j][n];
-      out[(kBT0 + f) * 64 + lane] = __builtin_bit_cast(uint4, v);
-    }
-  } else {
-    for (int f = wave; f < kTB * kKB; f += 4) {
-      const int tb = f / kKB, kb = f % kKB;
-      const int t = min(tb * 16 + r16, last);
-      out[(kC0 + f) * 64 + lane] =
-          *reinterpret_cast<const uint4*>(Cp + (row0 + t) * cs + kb * 32 + g * 8);
-    }
-    // dt, 64 heads at a time: [token][head] -> LDS -> [head][token]
-    bf16 (*Dt)[kQ + 2] = reinterpret_cast<bf16 (*)[kQ + 2]>(sh);
-    bf16* dto = dtT + ((int64_t)b * ntiles + c) * heads * kQ;
-    for (int h0 = 0; h0 < heads; h0 += 64) {
-      const int nh = min(64, heads - h0);
-      __syncthreads();
-      // thread: head h0 + tid%64, tokens tid/64 + 4i; all 32 loads in flight
-      const int hh = tid & 63;
-      bf16 v[kQ / 4];
-#pragma unroll
-      for (int i = 0; i < kQ / 4; ++i) {
-        const int s = (tid >> 6) + 4 * i;
-        v[i] = dtp[(row0 + min(s, last)) * dts + h0 + min(hh, nh - 1)];
-      }
-      if (hh < nh) {
-#pragma unroll
-        for (int i = 0; i < kQ / 4; ++i) Dt[hh][(tid >> 6) + 4 * i] = v[i];
-      }
-      __syncthreads();
-      for (int v = tid; v < nh * (kQ / 2); v += 256) {
-        const int hh = v / (kQ / 2), s2 = v % (kQ / 2);
-        *reinterpret_cast<uint32_t*>(dto + (int64_t)(h0 + hh) * kQ + 2 * s2) =
-            *reinterpret_cast<const uint32_t*>(&Dt[hh][2 * s2]);
-      }
+    for (int v2 = tid; v2 < nh * (kQ / 2); v2 += 512) {
+      const int hr = v2 / (kQ / 2), s2 = v2 % (kQ / 2);
+      *reinterpret_cast<uint32_t*>(dto + (int64_t)(h0 + hr) * kQ + 2 * s2) =
+          *reinterpret_cast<const uint32_t*>(&Dt[hr][2 * s2]);
     }
   }
 }
@@ -663,21 +663,37 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(BK k) {
   }
 }
 
-// Chains segment states (same as the general path).
+// Chains segment states: slot s receives the state entering segment s,
+//   H_in[0] = h0, H_in[s+1] = exp2(decay_s) H_in[s] + S_s,
+// where slot s held the local end state S_s written by the prepass.  One
+// thread per state element; the slot loads of eight segments are issued
+// together.
 __global__ __launch_bounds__(256) void seg_combine_bf16_kernel(float* __restrict__ seg_state,
                                                                const float* __restrict__ seg_decay,
                                                                const float* __restrict__ h0,
                                                                int n_heads, int heads, int nseg) {
   constexpr int PN = kP * kN;
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
   const int64_t unit = (int64_t)b * heads + h;
-  for (int e = threadIdx.x; e < PN; e += 256) {
-    float H = h0 ? h0[((int64_t)b * n_heads + h) * PN + e] : 0.0f;
-    for (int s = 0; s < nseg; ++s) {
-      float* slot = seg_state + (unit * nseg + s) * PN + e;
-      const float S = s < nseg - 1 ? *slot : 0.0f;
-      *slot = H;
-      if (s < nseg - 1) H = exp2f(seg_decay[unit * nseg + s]) * H + S;
+  float H = h0 ? h0[((int64_t)b * n_heads + h) * PN + e] : 0.0f;
+  float* base = seg_state + unit * nseg * PN + e;
+  const float* dec = seg_decay + unit * nseg;
+  constexpr int kU = 8;
+  for (int s0 = 0; s0 < nseg; s0 += kU) {
+    float S[kU];
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const int sg = s0 + i;
+      S[i] = sg < nseg - 1 ? base[(int64_t)sg * PN] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const int sg = s0 + i;
+      if (sg < nseg) {
+        base[(int64_t)sg * PN] = H;
+        if (sg < nseg - 1) H = exp2f(dec[sg]) * H + S[i];
+      }
     }
   }
 }
@@ -730,11 +746,13 @@ hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
                                            dt_region_bytes(a.batch, a.seqlen, a.heads));
     k.seg_decay = k.seg_state + (size_t)a.batch * a.heads * k.nseg * kP * kN;
   }
-  hipLaunchKernelGGL(tile_prep_kernel, dim3(k.ntiles, (unsigned)a.batch, kNG / 4 + 2), dim3(256), 0, s,
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(tile_prep_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPrepLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tile_prep_kernel, dim3(k.ntiles, (unsigned)a.batch), dim3(512), kPrepLds, s,
                      static_cast<const bf16*>(a.B), a.bs, k.C, a.cs, k.dt, a.dts, frags, dtT,
                      a.seqlen, k.ntiles, a.heads);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (k.nseg > 1) {
     auto pre = ssd_bf16_kernel<false>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(pre),
@@ -742,8 +760,9 @@ hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pre, dim3(k.nseg - 1, a.heads, (unsigned)a.batch), dim3(kThreads), kLds, s, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(seg_combine_bf16_kernel, dim3(a.heads, (unsigned)a.batch), dim3(256), 0, s,
-                       k.seg_state, k.seg_decay, a.h0, a.n_heads, a.heads, k.nseg);
+    static_assert((kP * kN) % 256 == 0, "state elements split over 256-thread blocks");
+    hipLaunchKernelGGL(seg_combine_bf16_kernel, dim3(kP * kN / 256, a.heads, (unsigned)a.batch),
+                       dim3(256), 0, s, k.seg_state, k.seg_decay, a.h0, a.n_heads, a.heads, k.nseg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   auto main_k = ssd_bf16_kernel<true>;
