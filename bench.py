@@ -7,9 +7,11 @@ selective scan on strided views of the conv output (64 heads of 64, d_state
 128, chunk 256, full width m=2048).  ``value`` is tokens/s of that step.
 
 Also reported on the same JSON line:
-  - ``roofline``: the scan kernel's algorithmic HBM bytes per launch divided by
-    its own duration (HIP events around each scan launch inside the timed
-    steps, on the stream it runs on), against MI355X's 8 TB/s;
+  - ``roofline``: the scan call's algorithmic HBM bytes divided by its own
+    duration (HIP events around each scan call inside the timed steps, on the
+    stream it runs on), against MI355X's 8 TB/s.  A scan call is two kernels:
+    tile_prep_kernel (per-tile C.B^T, B^T and C fragments and head-major dt,
+    shared by the heads) and ssd_bf16_kernel (the scan itself);
   - ``slices``: scan-only tokens/s and HBM fraction at every Matryoshka width;
   - ``decode``: the recurrent decode step (conv state roll + scan step) for a
     batch of 256 sequences at mixed widths, 1024 tokens captured in a HIP graph;
@@ -32,7 +34,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ssd_scan_1p4b_m2048.json")
-SCAN_SRC = os.path.join(ROOT, "selective_state_space_12_amd", "csrc", "ssd_fwd.hip")
+SCAN_SRC = os.path.join(ROOT, "selective_state_space_12_amd", "csrc", "ssd_fwd_bf16.hip")
+SCAN_KERNELS = ("tile_prep_kernel", "ssd_bf16_kernel")  # the two kernels of one scan call
 
 
 COPY_BYTES = 1 << 30
@@ -58,10 +61,18 @@ def _pmc_per_dispatch(dirname: str, counter: str, kernel_substr: str, min_grid: 
 
 
 def summarize_pmc(scan_fetch, scan_write, copy_fetch, copy_write):
-    """HBM bytes per scan launch: FETCH_SIZE + WRITE_SIZE of the scan kernel,
-    each scaled by what the same counter reads for a copy of known size."""
-    sf, nsf = _pmc_per_dispatch(scan_fetch, "FETCH_SIZE", "ssd_chunk_kernel")
-    sw, nsw = _pmc_per_dispatch(scan_write, "WRITE_SIZE", "ssd_chunk_kernel")
+    """HBM bytes per scan call: FETCH_SIZE + WRITE_SIZE of its two kernels
+    (mean per dispatch of each, summed), each counter scaled by what it reads
+    for a copy of known size."""
+    sf = sw = 0.0
+    nsf, nsw = [], []
+    for kname in SCAN_KERNELS:
+        f1, n1 = _pmc_per_dispatch(scan_fetch, "FETCH_SIZE", kname)
+        w1, n2 = _pmc_per_dispatch(scan_write, "WRITE_SIZE", kname)
+        sf += f1
+        sw += w1
+        nsf.append(n1)
+        nsw.append(n2)
     # the calibration copy is the only large copy dispatch of its run
     cf, _ = _pmc_per_dispatch(copy_fetch, "FETCH_SIZE", "copyBuffer", min_grid=1 << 16)
     cw, _ = _pmc_per_dispatch(copy_write, "WRITE_SIZE", "copyBuffer", min_grid=1 << 16)
@@ -71,7 +82,7 @@ def summarize_pmc(scan_fetch, scan_write, copy_fetch, copy_write):
     import synth
     w = synth.WORKLOADS["1.4b"]
     alg = scan_bytes(w.batch * w.seqlen, w.n_heads, w.d_head, w.d_state, 2)
-    rec = {"kernel": "ssd_chunk_kernel<bf16, 64, 128, 256, main>",
+    rec = {"kernel": "scan call: tile_prep_kernel + ssd_bf16_kernel<true> (bf16, d_head 64, d_state 128, 128-token tiles)",
            "workload": "1.4B-scale scan, b=4 l=8192, 64 heads, chunk 256, inputs as in bench.py",
            "kernel_source_sha256_16": src_hash(),
            "fetch_kib_per_dispatch": sf, "write_kib_per_dispatch": sw,
@@ -237,9 +248,10 @@ def main():
         "data": "synthetic (seeded N(0,1) xBC stream, log-uniform dt in [1e-3, 1e-1]; no dataset)",
         "config": {"workload": "1.4B-scale MatMamba block prefill: conv1d(k=4)+SiLU then chunked "
                                "selective scan, b=4 l=8192 d_model=2048 d_inner=4096 64 heads x 64, "
-                               "d_state=128, chunk=256, slice m=2048 (64 heads)",
+                               "d_state=128, chunk=256 (evaluated as two 128-token tiles), "
+                               "slice m=2048 (64 heads)",
                    "global_batch": b, "seq_len": l, "parallelism": "single GPU"},
-        "roofline": {"kernel": "ssd_chunk_kernel (scan)", "bound": "hbm",
+        "roofline": {"kernel": "scan call (tile_prep_kernel + ssd_bf16_kernel)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "alg_bytes_per_launch": alg, "avg_launch_ms": scan_avg_ms},

@@ -34,6 +34,9 @@
 //    eight consecutive channels of a token, stored as one 16-byte write;
 //  - LDS tiles are double-buffered and the decay cumsums triple-buffered, so
 //    each tile costs one workgroup barrier.
+#include <atomic>
+#include <utility>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "../../include/mm_ssd.h"
@@ -185,6 +188,17 @@ __global__ __launch_bounds__(512) void tile_prep_kernel(const bf16* __restrict__
   const int last = (int)min((int64_t)kQ, seqlen - (int64_t)c * kQ) - 1;
   uint4* out = frags + ((int64_t)b * ntiles + c) * kNFR * 64;
 
+  // dt of heads h0 .. h0+63: thread takes head h0 + tid%64, tokens tid/64 + 8i
+  const int hh = tid & 63;
+  bf16 dv[kQ / 8];
+  auto load_dt = [&](int h0, int nh) {
+#pragma unroll
+    for (int i = 0; i < kQ / 8; ++i) {
+      const int s = (tid >> 6) + 8 * i;
+      dv[i] = dtp[(row0 + min(s, last)) * dts + h0 + min(hh, nh - 1)];
+    }
+  };
+  load_dt(0, min(64, heads));
   for (int v = tid; v < kQ * (kN / 8); v += 512) {
     const int s = v / (kN / 8), col = (v % (kN / 8)) * 8;
     const int64_t r = row0 + min(s, last);
@@ -235,18 +249,11 @@ __global__ __launch_bounds__(512) void tile_prep_kernel(const bf16* __restrict__
   bf16* dto = dtT + ((int64_t)b * ntiles + c) * heads * kQ;
   for (int h0 = 0; h0 < heads; h0 += 64) {
     const int nh = min(64, heads - h0);
-    // thread: head h0 + tid%64, tokens tid/64 + 8i; all 16 loads in flight
-    const int hh = tid & 63;
-    bf16 v[kQ / 8];
-#pragma unroll
-    for (int i = 0; i < kQ / 8; ++i) {
-      const int s = (tid >> 6) + 8 * i;
-      v[i] = dtp[(row0 + min(s, last)) * dts + h0 + min(hh, nh - 1)];
-    }
+    if (h0 > 0) load_dt(h0, nh);
     __syncthreads();  // previous group's rows have been written out
     if (hh < nh) {
 #pragma unroll
-      for (int i = 0; i < kQ / 8; ++i) Dt[hh][(tid >> 6) + 8 * i] = v[i];
+      for (int i = 0; i < kQ / 8; ++i) Dt[hh][(tid >> 6) + 8 * i] = dv[i];
     }
     __syncthreads();
     for (int v2 = tid; v2 < nh * (kQ / 2); v2 += 512) {
@@ -516,7 +523,12 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Ah2 = k.A[h] * kLog2e;
 
-  // load i: token 32v + 8i + lane/8, channels 8*(lane%8) .. +7 (16 bytes)
+  // Lane: LDS chunk pc = lane%8 (columns 8pc .. 8pc+7) of tokens
+  // 32v + 8i + lane/8.  Those columns hold the channels cb .. cb+3 and
+  // cb+8 .. cb+11 with cb = (pc/4)*32 + (pc%2)*16 + ((pc/2)%2)*4 (see chan),
+  // loaded as two 8-byte pieces and written as one 16-byte chunk.
+  const int pc = lane & 7;
+  const int cb = (pc >> 2) * 32 + (pc & 1) * 16 + ((pc >> 1) & 1) * 4;
   uint4 xr[4];
   auto load_x = [&](int c) {
     const int64_t r0 = rowb + (int64_t)c * kQ;
@@ -524,14 +536,15 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = min(v * 32 + i * 8 + (lane >> 3), last);
-      xr[i] = *reinterpret_cast<const uint4*>(k.x + (r0 + s) * k.xs + (int64_t)h * kP + (lane & 7) * 8);
+      const bf16* src = k.x + (r0 + s) * k.xs + (int64_t)h * kP + cb;
+      const uint2 lo = *reinterpret_cast<const uint2*>(src);
+      const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+      xr[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
   };
-  // channels a*32 + j*8 + e*4 + (0..3) sit at columns (2a + e)*16 + 4j + (0..3)
   auto commit = [&](int xb, int db) {
     bf16* XT = xbuf + xb * kXBuf;
     const float* d = dbuf + db * kDec;
-    const int q = lane & 7, a = q >> 2, j = q & 3;
     auto scaled = [](const uint4& u, float f) {
       const bf16x8 x = __builtin_bit_cast(bf16x8, u);
       f32x4 lo, hi;
@@ -546,17 +559,12 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = v * 32 + i * 8 + (lane >> 3);
-      const int o0 = xoff(s, 4 * a + (j >> 1), j & 1), o1 = xoff(s, 4 * a + 2 + (j >> 1), j & 1);
-      const uint4 xe = scaled(xr[i], d[2 * kQ + s]);
-      const uint4 xw = scaled(xr[i], d[3 * kQ + s]);
+      const int o = xoff(s, pc, 0);
       if (OUT) {
-        *reinterpret_cast<uint2*>(XT + o0) = make_uint2(xr[i].x, xr[i].y);
-        *reinterpret_cast<uint2*>(XT + o1) = make_uint2(xr[i].z, xr[i].w);
-        *reinterpret_cast<uint2*>(XT + kXE + o0) = make_uint2(xe.x, xe.y);
-        *reinterpret_cast<uint2*>(XT + kXE + o1) = make_uint2(xe.z, xe.w);
+        *reinterpret_cast<uint4*>(XT + o) = xr[i];
+        *reinterpret_cast<uint4*>(XT + kXE + o) = scaled(xr[i], d[2 * kQ + s]);
       }
-      *reinterpret_cast<uint2*>(XT + 2 * kXE + o0) = make_uint2(xw.x, xw.y);
-      *reinterpret_cast<uint2*>(XT + 2 * kXE + o1) = make_uint2(xw.z, xw.w);
+      *reinterpret_cast<uint4*>(XT + 2 * kXE + o) = scaled(xr[i], d[3 * kQ + s]);
     }
   };
   // dt of tokens 2*lane, 2*lane + 1 of a tile (head-major copy), kept raw
@@ -723,6 +731,27 @@ size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads) {
   return bytes;
 }
 
+// hipFuncSetAttribute for the three kernels that need more than 64 KB of LDS,
+// once per device (bit d of the mask).
+hipError_t set_lds_attributes() {
+  static std::atomic<unsigned long long> done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = dev < 64 ? 1ull << dev : 0ull;
+  if (bit && (done.load() & bit)) return hipSuccess;
+  const std::pair<const void*, size_t> attrs[] = {
+      {reinterpret_cast<const void*>(tile_prep_kernel), kPrepLds},
+      {reinterpret_cast<const void*>(ssd_bf16_kernel<false>), kLds},
+      {reinterpret_cast<const void*>(ssd_bf16_kernel<true>), kLds}};
+  for (const auto& fa : attrs) {
+    e = hipFuncSetAttribute(fa.first, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fa.second);
+    if (e != hipSuccess) return e;
+  }
+  done.fetch_or(bit);
+  return hipSuccess;
+}
+
 hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
   BK k;
   k.x = static_cast<const bf16*>(a.x); k.xs = a.xs;
@@ -746,8 +775,7 @@ hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
                                            dt_region_bytes(a.batch, a.seqlen, a.heads));
     k.seg_decay = k.seg_state + (size_t)a.batch * a.heads * k.nseg * kP * kN;
   }
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(tile_prep_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPrepLds);
+  hipError_t e = set_lds_attributes();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(tile_prep_kernel, dim3(k.ntiles, (unsigned)a.batch), dim3(512), kPrepLds, s,
                      static_cast<const bf16*>(a.B), a.bs, k.C, a.cs, k.dt, a.dts, frags, dtT,
@@ -755,9 +783,6 @@ hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (k.nseg > 1) {
     auto pre = ssd_bf16_kernel<false>;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(pre),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pre, dim3(k.nseg - 1, a.heads, (unsigned)a.batch), dim3(kThreads), kLds, s, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     static_assert((kP * kN) % 256 == 0, "state elements split over 256-thread blocks");
@@ -766,9 +791,6 @@ hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   auto main_k = ssd_bf16_kernel<true>;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(main_k),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(main_k, dim3(k.nseg, a.heads, (unsigned)a.batch), dim3(kThreads), kLds, s, k);
   return hipGetLastError();
 }
