@@ -21,9 +21,9 @@
 //    block each), four own the fp32 state in MFMA accumulators, four stage x
 //    and the decay cumsums; every SIMD runs waves of all three kinds, so the
 //    output MFMAs overlap the state update and the staging.
-//  - x is transposed by an MFMA against a 0/1 selector (exact), which leaves
-//    four consecutive tokens per lane: three scaled copies (plain, block
-//    decay, end decay) go to LDS with 8-byte writes.
+//  - x stays token-major in LDS: the staging waves write three copies (plain,
+//    times the block-end decay, times the end decay) with 16-byte writes, and
+//    the MFMA waves read them as operands with LDS transpose loads.
 //  - off-diagonal 32-token blocks factor the decay as
 //    exp(Lambda_t - Lambda_e) * exp(Lambda_e - Lambda_s) dt_s (e = block end,
 //    both factors <= 1); the first factor is applied to the accumulator in
