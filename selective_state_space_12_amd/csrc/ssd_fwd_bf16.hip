@@ -54,7 +54,6 @@ constexpr int kPB = kP / 16;   // 16-wide d_head blocks
 constexpr int kNB = kN / 16;   // 16-wide d_state blocks
 constexpr int kKB = kN / 32;   // K=32 slices over d_state
 constexpr int kNBW = kNB / 4;  // state column blocks per state wave
-constexpr int kHP = kN + 8;    // LDS row pitch (elements) of the operand copy of H
 constexpr int kXcds = 8;
 // 16 waves, four per SIMD: 0-7 outputs (one 16-token block each; waves w and
 // w+4 share a SIMD and take blocks whose causal work adds up the same), 8-11
@@ -72,15 +71,22 @@ constexpr int kC0 = kBT0 + kNB * kSB;            // first C fragment (tb, kb): k
 constexpr int kNFR = kC0 + kTB * kKB;            // fragments per (sequence, tile): 84
 constexpr size_t kFragBytes = 64 * 16;           // one wave-wide fragment
 
-constexpr int kXE = kQ * kP;  // elements of one x tile in LDS ([token][column], 128 B rows)
-// Per buffer three x tiles: plain (diagonal blocks), scaled by the block-end
-// factor (off-diagonal blocks) and by the end factor (state update).
-constexpr int kXBuf = 3 * kXE;
-constexpr size_t kHTile = (size_t)kP * kHP * sizeof(bf16);
-constexpr size_t kDec = 4 * kQ;  // floats: Lambda, dt, block-end factor, end factor
-constexpr size_t kLds = 2 * kXBuf * sizeof(bf16) + 2 * kHTile + 3 * kDec * sizeof(float);
+// The x tiles and the bf16 copy of H live in LDS as MFMA operand fragments,
+// lane-major (16 bytes per lane, 1 KB per fragment), so every operand read is
+// one conflict-free linear 16-byte load:
+//   x fragment (q, pb):   lane (r, g) holds x[q*32 + g*8 + j][column pb*16 + r]
+//   H fragment (pb, kb):  lane (r, g) holds H[chan(pb, r)][kb*32 + g*8 + j]
+constexpr int kXE = kQ * kP;   // elements of one x tile (16 fragments)
+// Per buffer two x tiles: plain (diagonal blocks) and scaled by the block-end
+// factor (off-diagonal blocks and the state update).
+constexpr int kXBuf = 2 * kXE;
+constexpr int kHF = kP * kN;   // elements of the operand copy of H (16 fragments)
+constexpr int kStg = kQ * kP;  // raw token-major rows, 32 per staging wave
+constexpr size_t kDec = 3 * kQ;  // floats: Lambda, dt, block-end factor
+constexpr size_t kLds = (size_t)(2 * kXBuf + 2 * kHF + kStg) * sizeof(bf16) + 3 * kDec * sizeof(float);
 
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint2 pack4(f32x4 v) {
   return __builtin_bit_cast(uint2, __builtin_convertvector(v, bf16x4));
@@ -93,14 +99,8 @@ __device__ __forceinline__ Frag8<bf16> as_frag(uint4 u) {
 __device__ __forceinline__ Frag8<bf16> lds_frag(const bf16* p) {
   return as_frag(*reinterpret_cast<const uint4*>(p));
 }
-// Element offset of (row, col) in the [64][kHP] LDS copy of H, col a
-// multiple of 8.  The 16-byte chunks of rows 8-15 of every 16 rows are XOR-ed
-// with 4: the A-operand row orders used below (rows r and r + 8 read by lanes
-// of the same 8-lane group) then hit distinct banks, and natural row orders
-// stay conflict-free.
-__device__ __forceinline__ int swz(int row, int col) {
-  return row * kHP + (col ^ (((row >> 3) & 1) << 5));
-}
+// Element offset of a lane's 16 bytes of fragment f in a fragment-ordered tile
+__device__ __forceinline__ int foff(int f, int lane) { return (f * 64 + lane) * 8; }
 
 // Channel held at column c of an operand tile: tile pb = c/16, row m = c%16
 // is channel (pb/2)*32 + (m/4)*8 + (pb%2)*4 + m%4.  Output tiles 2a and 2a+1
@@ -109,30 +109,27 @@ __device__ __forceinline__ int chan(int pb, int m) {
   return (pb >> 1) * 32 + (m >> 2) * 8 + (pb & 1) * 4 + (m & 3);
 }
 
-// x tile in LDS: row s (token) holds the 64 channels in column order
-// (column c = channel chan(c/16, c%16)), 8 chunks of 16 bytes per 128-byte
-// row, chunk index XOR-ed with 2*(s%4).  Element offset of (s, chunk, half):
-__device__ __forceinline__ int xoff(int s, int chunk, int half) {
-  return s * kP + ((chunk ^ ((s & 3) << 1)) << 3) + half * 4;
-}
+// Raw rows staged by a staging wave: row s (token) holds the head's 64
+// channels in natural order, 8 chunks of 16 bytes per 128-byte row, chunk
+// index XOR-ed with s%8.  Element offset of (s, chunk):
+__device__ __forceinline__ int soff(int s, int chunk) { return s * kP + ((chunk ^ (s & 7)) << 3); }
 
-// MFMA operand of 8 consecutive tokens sb..sb+7 (sb = block start + g*8) for
-// columns pb*16 + r of the x tile, read with two LDS transpose loads: within
-// each 16-lane group, lane i receives element i%4 of the 8 bytes that lane
-// 4k + i/4 addresses, for k = 0..3.  Lane src therefore addresses token
-// sb + src/4 (+4 for the second load), columns pb*16 + 4*(src%4) .. +3.
-// The XOR of the chunk index makes the four rows of a group hit 32 distinct
-// banks.
+// Operand fragment of 8 consecutive staged tokens sb..sb+7 for the channels
+// chan(pb, r), read with two LDS transpose loads: within each 16-lane group,
+// lane i receives element i%4 of the 8 bytes that lane 4k + i/4 addresses,
+// for k = 0..3.  Lane src therefore addresses token sb + src/4 (+4 for the
+// second load) at the four channels chan(pb, 4*(src%4)) .. +3, which are
+// consecutive: (pb/2)*32 + (src%4)*8 + (pb%2)*4.
 typedef short short4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ Frag8<bf16> x_frag(const bf16* X, int sb, int pb, int lane) {
+__device__ __forceinline__ Frag8<bf16> stg_frag(const bf16* S, int sb, int pb, int lane) {
   const int src = lane & 15;
-  const int chunk = 2 * pb + ((src & 3) >> 1), half = src & 1;
+  const int chunk = (pb >> 1) * 4 + (src & 3), half = (pb & 1) * 4;
   const int s1 = sb + (src >> 2);
   typedef __attribute__((address_space(3))) short4v lds_short4;
   const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_short4*)(const_cast<bf16*>(X) + xoff(s1, chunk, half)));
+      (lds_short4*)(const_cast<bf16*>(S) + soff(s1, chunk) + half));
   const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_short4*)(const_cast<bf16*>(X) + xoff(s1 + 4, chunk, half)));
+      (lds_short4*)(const_cast<bf16*>(S) + soff(s1 + 4, chunk) + half));
   Frag8<bf16> f;
   f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   return f;
@@ -298,15 +295,10 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
   const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
   const bf16* xbuf = reinterpret_cast<const bf16*>(smem);
   const bf16* hbuf = xbuf + 2 * kXBuf;
-  const float* dbuf = reinterpret_cast<const float*>(hbuf + 2 * kP * kHP);
+  const float* dbuf = reinterpret_cast<const float*>(hbuf + 2 * kHF + kStg);
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Dh = k.D ? k.D[h] : 0.0f;
   const int t = tb * 16 + r16;  // this lane's token within a tile
-
-  // A-operand row (channel) of this lane in tile pb
-  int prow[kPB];
-#pragma unroll
-  for (int pb = 0; pb < kPB; ++pb) prow[pb] = chan(pb, r16);
 
   Frag8<bf16> cf[kKB];
   Frag8<bf16> gf[L + 1];
@@ -329,7 +321,7 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
   for (int c = c0; c < c1; ++c) {
     const int len = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ);
     const int64_t r0 = rowb + (int64_t)c * kQ;
-    const bf16* Hs = hbuf + (c & 1) * kP * kHP;
+    const bf16* Hs = hbuf + (c & 1) * kHF;
     const bf16* XT = xbuf + (c & 1) * kXBuf;
     const bf16* XE = XT + kXE;
     const float* lam = dbuf + (c % 3) * kDec;
@@ -363,7 +355,7 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
     for (int kb = 0; kb < kKB; ++kb) {
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
-        const Frag8<bf16> hf = lds_frag(Hs + swz(prow[pb], kb * 32 + g * 8));
+        const Frag8<bf16> hf = lds_frag(Hs + foff(pb * kKB + kb, lane));
         acc[pb] = mma(hf, cf[kb], acc[pb]);
       }
       if (kb == 1) mask4(0);
@@ -387,7 +379,7 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
       prev = eq;
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
-        const Frag8<bf16> xf = x_frag(XE, q * 32 + g * 8, pb, lane);
+        const Frag8<bf16> xf = lds_frag(XE + foff(q * kPB + pb, lane));
         acc[pb] = mma(xf, gf[q], acc[pb] * r);
       }
     }
@@ -395,7 +387,7 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
     const float sc = __builtin_amdgcn_exp2f(lt - prev);
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb) {
-      const Frag8<bf16> xf = x_frag(XT, L * 32 + g * 8, pb, lane);
+      const Frag8<bf16> xf = lds_frag(XT + foff(L * kPB + pb, lane));
       acc[pb] = mma(xf, m, acc[pb] * sc);
     }
 
@@ -423,7 +415,7 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
   const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
   const bf16* xbuf = reinterpret_cast<const bf16*>(smem);
   bf16* hbuf = reinterpret_cast<bf16*>(smem) + 2 * kXBuf;
-  const float* dbuf = reinterpret_cast<const float*>(hbuf + 2 * kP * kHP);
+  const float* dbuf = reinterpret_cast<const float*>(hbuf + 2 * kHF + kStg);
 
   f32x4 hacc[kNBW][kPB];
   {
@@ -448,13 +440,13 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
 #pragma unroll
     for (int j = 0; j < kNBW; ++j) bt[j][ks] = as_frag(f[((u * kNBW + j) * kSB + ks) * 64]);
   };
+  // this wave's columns are exactly the H fragments (pb, kb = u)
   auto write_hs = [&](int buf) {
-    bf16* Hs = hbuf + buf * kP * kHP;
+    bf16* Hs = hbuf + buf * kHF;
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb) {
       const uint2 lo = pack4(hacc[0][pb]), hi = pack4(hacc[1][pb]);
-      *reinterpret_cast<uint4*>(Hs + swz(chan(pb, r16), u * 32 + g * 8)) =
-          make_uint4(lo.x, lo.y, hi.x, hi.y);
+      *reinterpret_cast<uint4*>(Hs + foff(pb * kKB + u, lane)) = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
   };
 
@@ -469,23 +461,26 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
   __syncthreads();  // x copies of the first tile
 
   for (int c = c0; c < c1; ++c) {
-    // H <- exp2(Lambda_end) H + B^T (w o x): A operand B^T rows, B operand
-    // the end-scaled x (transposed LDS reads); each B^T slice is reloaded for
-    // the next tile as soon as its MFMAs are issued.
+    // H <- exp2(Lambda_end) H + sum_s exp2(Lambda_end - Lambda_s) dt_s x_s B_s^T
+    // in Horner form over the four 32-token blocks: the state is moved from
+    // the previous block end (tile start for the first) to the end e(q) of
+    // block q by exp2(lam[e(q)] - lam[e(q-1)]) <= 1, then block q adds B^T
+    // times the x copy scaled by exp2(lam[e(q)] - lam_s) dt_s (the copy the
+    // output waves use).  A operand B^T rows, B operand x; each B^T slice is
+    // reloaded for the next tile as soon as its MFMAs are issued.
     const float* d = dbuf + (c % 3) * kDec;
-    const float dec = __builtin_amdgcn_exp2f(d[kQ - 1]);
-    const bf16* XW = xbuf + (c & 1) * kXBuf + 2 * kXE;
-#pragma unroll
-    for (int j = 0; j < kNBW; ++j)
-#pragma unroll
-      for (int pb = 0; pb < kPB; ++pb) hacc[j][pb] *= dec;
+    const bf16* XE = xbuf + (c & 1) * kXBuf + kXE;
+    float prev = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < kSB; ++ks) {
+      const float e = d[ks * 32 + 31];
+      const float rq = __builtin_amdgcn_exp2f(e - prev);
+      prev = e;
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
-        const Frag8<bf16> xf = x_frag(XW, ks * 32 + g * 8, pb, lane);
+        const Frag8<bf16> xf = lds_frag(XE + foff(ks * kPB + pb, lane));
 #pragma unroll
-        for (int j = 0; j < kNBW; ++j) hacc[j][pb] = mma(bt[j][ks], xf, hacc[j][pb]);
+        for (int j = 0; j < kNBW; ++j) hacc[j][pb] = mma(bt[j][ks], xf, hacc[j][pb] * rq);
       }
       load_bt(min(c + 1, cl), ks);
     }
@@ -510,61 +505,63 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
 }
 
 // ---------------------------------------------------------------------------
-// Stage waves.  Wave v copies tokens 32v..32v+31 of each tile into the three
-// LDS x tiles (plain, times the block-end factor, times the end factor) one
-// tile ahead (layout at xoff); wave 12 (v = 0) also forms the decay cumsums
-// two tiles ahead.
+// Stage waves.  Wave v turns tokens 32v..32v+31 of each tile, one tile ahead,
+// into the x fragments (v, pb) of both LDS x tiles (plain and times the
+// block-end factor): its raw rows go to its own staging rows (layout at soff)
+// and come back transposed, as operand fragments, from LDS transpose loads.
+// All four also form the decay cumsum two tiles ahead (a few DPP steps) and
+// waves 12, 13, 14 write its three arrays.
 template <bool OUT>
 __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int seg, int c0,
                             int c1, int v) {
   const int lane = threadIdx.x & 63;
   bf16* xbuf = reinterpret_cast<bf16*>(smem);
-  float* dbuf = reinterpret_cast<float*>(xbuf + 2 * kXBuf + 2 * kP * kHP);
+  bf16* stg = xbuf + 2 * kXBuf + 2 * kHF + v * 32 * kP;  // this wave's 32 raw rows
+  float* dbuf = reinterpret_cast<float*>(xbuf + 2 * kXBuf + 2 * kHF + kStg);
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Ah2 = k.A[h] * kLog2e;
 
-  // Lane: LDS chunk pc = lane%8 (columns 8pc .. 8pc+7) of tokens
-  // 32v + 8i + lane/8.  Those columns hold the channels cb .. cb+3 and
-  // cb+8 .. cb+11 with cb = (pc/4)*32 + (pc%2)*16 + ((pc/2)%2)*4 (see chan),
-  // loaded as two 8-byte pieces and written as one 16-byte chunk.
+  // Lane: channels 8*(lane%8) .. +7 (chunk lane%8) of tokens 32v + 8i + lane/8,
+  // one 16-byte load each (eight lanes read a whole 128-byte row).  x is read
+  // once: nontemporal loads (measured 6% faster on the whole kernel).
+  // (four named registers, not an array: the array was placed in scratch)
   const int pc = lane & 7;
-  const int cb = (pc >> 2) * 32 + (pc & 1) * 16 + ((pc >> 1) & 1) * 4;
-  uint4 xr[4];
+  uint4 xr0, xr1, xr2, xr3;
   auto load_x = [&](int c) {
     const int64_t r0 = rowb + (int64_t)c * kQ;
     const int last = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ) - 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    auto row = [&](int i) {
       const int s = min(v * 32 + i * 8 + (lane >> 3), last);
-      const bf16* src = k.x + (r0 + s) * k.xs + (int64_t)h * kP + cb;
-      const uint2 lo = *reinterpret_cast<const uint2*>(src);
-      const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
-      xr[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    }
+      return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                                           k.x + (r0 + s) * k.xs + (int64_t)h * kP + pc * 8)));
+    };
+    xr0 = row(0);
+    xr1 = row(1);
+    xr2 = row(2);
+    xr3 = row(3);
   };
+  // Raw rows out, fragments back (LDS operations of one wave complete in
+  // order, so the transpose loads see the rows just written), then the plain
+  // fragments and the ones scaled by exp2(lam[e] - lam_s) dt_s, e the end of
+  // the token's 32-token block (lane (r, g) holds tokens 32v + g*8 + j).
   auto commit = [&](int xb, int db) {
     bf16* XT = xbuf + xb * kXBuf;
     const float* d = dbuf + db * kDec;
-    auto scaled = [](const uint4& u, float f) {
-      const bf16x8 x = __builtin_bit_cast(bf16x8, u);
-      f32x4 lo, hi;
+    *reinterpret_cast<uint4*>(stg + soff(0 + (lane >> 3), pc)) = xr0;
+    *reinterpret_cast<uint4*>(stg + soff(8 + (lane >> 3), pc)) = xr1;
+    *reinterpret_cast<uint4*>(stg + soff(16 + (lane >> 3), pc)) = xr2;
+    *reinterpret_cast<uint4*>(stg + soff(24 + (lane >> 3), pc)) = xr3;
+    Frag8<bf16> f[kPB];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo[e] = static_cast<float>(x[e]) * f;
-        hi[e] = static_cast<float>(x[e + 4]) * f;
-      }
-      const uint2 pl = pack4(lo), ph = pack4(hi);
-      return make_uint4(pl.x, pl.y, ph.x, ph.y);
-    };
+    for (int pb = 0; pb < kPB; ++pb) f[pb] = stg_frag(stg, (lane >> 4) * 8, pb, lane);
+    const float* ef = d + 2 * kQ + v * 32 + (lane >> 4) * 8;
+    const f32x4 e0 = *reinterpret_cast<const f32x4*>(ef);
+    const f32x4 e1 = *reinterpret_cast<const f32x4*>(ef + 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = v * 32 + i * 8 + (lane >> 3);
-      const int o = xoff(s, pc, 0);
-      if (OUT) {
-        *reinterpret_cast<uint4*>(XT + o) = xr[i];
-        *reinterpret_cast<uint4*>(XT + kXE + o) = scaled(xr[i], d[2 * kQ + s]);
-      }
-      *reinterpret_cast<uint4*>(XT + 2 * kXE + o) = scaled(xr[i], d[3 * kQ + s]);
+    for (int pb = 0; pb < kPB; ++pb) {
+      if (OUT) *reinterpret_cast<uint4*>(XT + foff(v * kPB + pb, lane)) = __builtin_bit_cast(uint4, f[pb].v);
+      *reinterpret_cast<uint4*>(XT + kXE + foff(v * kPB + pb, lane)) =
+          __builtin_bit_cast(uint4, scale8(f[pb], e0, e1).v);
     }
   };
   // dt of tokens 2*lane, 2*lane + 1 of a tile (head-major copy), kept raw
@@ -574,9 +571,9 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
     dtr_raw = reinterpret_cast<const uint32_t*>(
         k.dtT + (((int64_t)b * k.ntiles + c) * k.heads + h) * kQ)[lane];
   };
-  // Lambda (inclusive cumsum of dt*A, log2 units), dt, block-end factor
-  // exp2(Lambda_e - Lambda_s) dt_s and end factor exp2(Lambda_end - Lambda_s) dt_s
-  // of tile c (dt = 0 past the end of the sequence).
+  // Lambda (inclusive cumsum of dt*A, log2 units), dt and block-end factor
+  // exp2(Lambda_e - Lambda_s) dt_s of tile c (dt = 0 past the end of the
+  // sequence).
   auto make_dec = [&](int c, int buf) {
     const int len = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ);
     float dtr[2];
@@ -600,26 +597,27 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
     const float e2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 47));
     const int row = lane >> 4;
     const float lblk = row == 0 ? e0 : row == 1 ? e1 : row == 2 ? e2 : lend;
-    *reinterpret_cast<float2*>(d + 2 * lane) = make_float2(l0, l1);
-    *reinterpret_cast<float2*>(d + kQ + 2 * lane) = make_float2(dtr[0], dtr[1]);
-    *reinterpret_cast<float2*>(d + 2 * kQ + 2 * lane) =
-        make_float2(__builtin_amdgcn_exp2f(lblk - l0) * dtr[0], __builtin_amdgcn_exp2f(lblk - l1) * dtr[1]);
-    *reinterpret_cast<float2*>(d + 3 * kQ + 2 * lane) =
-        make_float2(__builtin_amdgcn_exp2f(lend - l0) * dtr[0], __builtin_amdgcn_exp2f(lend - l1) * dtr[1]);
+    if (v == 0) {
+      *reinterpret_cast<float2*>(d + 2 * lane) = make_float2(l0, l1);
+    } else if (v == 1) {
+      *reinterpret_cast<float2*>(d + kQ + 2 * lane) = make_float2(dtr[0], dtr[1]);
+    } else if (v == 2) {
+      *reinterpret_cast<float2*>(d + 2 * kQ + 2 * lane) =
+          make_float2(__builtin_amdgcn_exp2f(lblk - l0) * dtr[0], __builtin_amdgcn_exp2f(lblk - l1) * dtr[1]);
+    }
     return lend;
   };
 
   // The same loads in the same order every iteration (x, dt; tile indices
   // clamped to the last tile), and the prologue ends with that sequence, so
-  // the compiler's vmcnt waits stay exact.  Only wave 12 uses the dt values.
-  const bool dec_wave = v == 0;
+  // the compiler's vmcnt waits stay exact.
   const int cl = c1 - 1;
   float lam_seg = 0.0f;
   load_x(c0);
   load_dt(c0);
-  if (dec_wave) lam_seg += make_dec(c0, c0 % 3);
+  lam_seg += make_dec(c0, c0 % 3);
   load_dt(min(c0 + 1, cl));
-  if (dec_wave && c0 + 1 < c1) lam_seg += make_dec(c0 + 1, (c0 + 1) % 3);
+  if (c0 + 1 < c1) lam_seg += make_dec(c0 + 1, (c0 + 1) % 3);
   __syncthreads();
   commit(c0 & 1, c0 % 3);
   load_x(min(c0 + 1, cl));
@@ -629,11 +627,11 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
   for (int c = c0; c < c1; ++c) {
     if (c + 1 < c1) commit((c + 1) & 1, (c + 1) % 3);
     load_x(min(c + 2, cl));
-    if (dec_wave && c + 2 < c1) lam_seg += make_dec(c + 2, (c + 2) % 3);
+    if (c + 2 < c1) lam_seg += make_dec(c + 2, (c + 2) % 3);
     load_dt(min(c + 3, cl));
     __syncthreads();
   }
-  if (!OUT && dec_wave && lane == 0)
+  if (!OUT && v == 0 && lane == 0)
     k.seg_decay[((int64_t)b * k.heads + h) * k.nseg + seg] = lam_seg;
 }
 
