@@ -120,6 +120,93 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
   }
 }
 
+// One token per sequence with a conv state (the decode step): a thread owns
+// one 16-byte channel group -- x groups up to the widest slice, then B and C,
+// the same channels for every sequence -- for kSeq = 16/V sequences, so its
+// weights are loaded once and the input and state loads of all its sequences
+// are in flight together; x groups beyond a sequence's slice skip it.  The
+// state rows become (u[t-2], u[t-1], u[t]).
+template <typename T, bool kBias>
+__global__ __launch_bounds__(256) void conv1d_silu_step_kernel(
+    const T* __restrict__ in, int64_t in_stride, T* __restrict__ out, int64_t out_stride,
+    const float* __restrict__ w, const float* __restrict__ bias, float* __restrict__ conv_state,
+    int batch, int d_inner, int d_head, int bc_dim, int heads_cap,
+    const int32_t* __restrict__ heads_per_seq) {
+  constexpr int V = Vec16<T>::kN;
+  constexpr int kSeq = 16 / V;
+  const int ngx_max = heads_cap * d_head / V;
+  const int cg = blockIdx.x * 256 + threadIdx.x;
+  if (cg >= ngx_max + bc_dim / V) return;
+  const bool is_x = cg < ngx_max;
+  const int c = is_x ? cg * V : d_inner + (cg - ngx_max) * V;
+  const int conv_dim = d_inner + bc_dim;
+
+  float wk[4][V];
+  float bv[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const float4 wj = *reinterpret_cast<const float4*>(w + (int64_t)(c + j) * 4);
+    wk[0][j] = wj.x;
+    wk[1][j] = wj.y;
+    wk[2][j] = wj.z;
+    wk[3][j] = wj.w;
+    bv[j] = kBias ? bias[c + j] : 0.0f;
+  }
+
+  Vec16<T> u[kSeq];
+  float hs[kSeq][3][V];
+  bool act[kSeq];
+#pragma unroll
+  for (int i = 0; i < kSeq; ++i) {
+    const int b = blockIdx.y * kSeq + i;
+    act[i] = b < batch && (!is_x || cg < clamp_heads(heads_per_seq, b, heads_cap) * d_head / V);
+    if (act[i]) {
+      u[i] = load16(in + (int64_t)b * in_stride + c);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const float* sp = conv_state + ((int64_t)b * 3 + k) * conv_dim + c;
+#pragma unroll
+        for (int j = 0; j < V; j += 4) {
+          const float4 q = *reinterpret_cast<const float4*>(sp + j);
+          hs[i][k][j] = q.x;
+          hs[i][k][j + 1] = q.y;
+          hs[i][k][j + 2] = q.z;
+          hs[i][k][j + 3] = q.w;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kSeq; ++i) {
+    if (!act[i]) continue;
+    const int b = blockIdx.y * kSeq + i;
+    Vec16<T> o;
+    float ut[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      ut[j] = to_f32(u[i].v[j]);
+      float pre = bv[j];
+      pre = fmaf(wk[0][j], hs[i][0][j], pre);
+      pre = fmaf(wk[1][j], hs[i][1][j], pre);
+      pre = fmaf(wk[2][j], hs[i][2][j], pre);
+      pre = fmaf(wk[3][j], ut[j], pre);
+      o.v[j] = from_f32<T>(silu(pre));
+    }
+    store16(out + (int64_t)b * out_stride + c, o);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      float* sp = conv_state + ((int64_t)b * 3 + k) * conv_dim + c;
+#pragma unroll
+      for (int j = 0; j < V; j += 4) {
+        const float4 q = k < 2 ? make_float4(hs[i][k + 1][j], hs[i][k + 1][j + 1], hs[i][k + 1][j + 2],
+                                             hs[i][k + 1][j + 3])
+                               : make_float4(ut[j], ut[j + 1], ut[j + 2], ut[j + 3]);
+        *reinterpret_cast<float4*>(sp + j) = q;
+      }
+    }
+  }
+}
+
 // Several runs per sequence: the new state is the last three input rows
 // (seqlen > run length >= 3), written after the conv kernel has read the old
 // state (stream order).
@@ -149,6 +236,17 @@ __global__ __launch_bounds__(kConvThreads) void conv_state_update_kernel(
 template <typename T>
 hipError_t launch_typed(const ConvArgs& a, hipStream_t s) {
   constexpr int V = Vec16<T>::kN;
+  if (a.seqlen == 1 && a.conv_state) {  // decode step
+    constexpr int kSeq = 16 / V;
+    const int groups = (int)((a.heads_cap * a.d_head + a.bc_dim) / V);
+    dim3 grid((unsigned)((groups + 255) / 256), (unsigned)((a.batch + kSeq - 1) / kSeq));
+    auto kern = a.bias ? conv1d_silu_step_kernel<T, true> : conv1d_silu_step_kernel<T, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, static_cast<const T*>(a.in), a.in_stride,
+                       static_cast<T*>(a.out), a.out_stride, a.w, a.bias, a.conv_state,
+                       (int)a.batch, (int)a.d_inner, (int)a.d_head, (int)a.bc_dim, a.heads_cap,
+                       a.heads_per_seq);
+    return hipGetLastError();
+  }
   const int max_groups = (int)((a.heads_cap * a.d_head + a.bc_dim) / V);
   // runs go on grid y (at most 65535 blocks): lengthen runs for very long sequences
   int64_t rl = (a.seqlen + 65534) / 65535;
