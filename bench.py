@@ -287,8 +287,19 @@ def main():
         torch.cuda.synchronize()
         tc = c0.elapsed_time(c1) / 10
         cb = conv_bytes(tokens, w.conv_dim, elem)
+        # practical ceiling for the same read + write traffic: a plain device copy
+        cpy = torch.empty_like(xbc_raw)
+        cpy.copy_(xbc_raw)
+        c0.record(stream)
+        for _ in range(10):
+            cpy.copy_(xbc_raw)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        tcopy = c0.elapsed_time(c1) / 10
+        del cpy
         out["slices"] = slices
-        out["conv"] = {"ms": tc, "hbm_frac": cb / (tc * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+        out["conv"] = {"ms": tc, "hbm_frac": cb / (tc * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                       "copy_same_bytes_ms": tcopy, "vs_copy": tcopy / tc}
 
     # ---- decode: conv state roll + scan step, 1024 tokens in a HIP graph -----
     if not args.no_decode:
