@@ -22,7 +22,7 @@ from typing import Dict, List, Optional
 import torch
 
 # tensor indices inside a config's seed block
-_X, _B, _C, _DT, _A, _D, _CONVW, _XBC, _H0, _CS0, _DTSTEP, _XBCSTEP = range(12)
+_X, _B, _C, _DT, _A, _D, _CONVW, _XBC, _H0, _CS0, _DTSTEP, _XBCSTEP, _CONVB = range(13)
 
 
 @dataclass(frozen=True)
@@ -110,6 +110,12 @@ def draw_D(w: Workload, n_heads: Optional[int] = None) -> torch.Tensor:
 def draw_conv_w(w: Workload) -> torch.Tensor:
     """(conv_dim, 4) fp32, 0.5 * N(0, 1); tap 3 multiplies the current token."""
     return _normal((w.conv_dim, 4), _gen(w, _CONVW), 0.5)
+
+
+def draw_conv_bias(w: Workload) -> torch.Tensor:
+    """(conv_dim,) fp32, 0.5 * N(0, 1).  The workloads run without a conv bias;
+    this draw exercises the optional bias argument."""
+    return _normal((w.conv_dim,), _gen(w, _CONVB), 0.5)
 
 
 def forward_inputs(w: Workload, batch: Optional[int] = None,

@@ -55,6 +55,38 @@ def test_conv_tiny_fp32_all_slices(seqlen, with_state):
             np.testing.assert_array_equal(gs[:, :, ina], f64(inp["conv_state"])[:, :, ina])
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("seqlen", [1, 100])
+def test_conv_with_bias_and_state(dtype, seqlen):
+    """The optional conv bias (MatMamba block paragraph: a conv layer over
+    the concatenated x, B, C channels), through the multi-token kernel and the
+    single-token decode kernel, with per-sequence widths."""
+    w = M130
+    b = 5
+    inp = synth.xbc_inputs(w, batch=b, seqlen=seqlen, with_state=True, salt=3)
+    bias = synth.draw_conv_bias(w)
+    hv = [w.heads(m) for m in (96, 768, 384, 192, 768)]
+    say(f"conv bias {dtype} l={seqlen} heads={hv}")
+    xin = inp["xbc"].to(dtype).to(DEV)
+    out = torch.full_like(xin, float("nan"))
+    cs0 = inp["conv_state"]
+    cs = cs0.to(DEV)
+    mm.conv1d_silu(xin, inp["w"].to(DEV), bias.to(DEV), cs, d_inner=w.d_inner, d_head=w.d_head,
+                   d_state=w.d_state, n_heads_active=w.n_heads,
+                   heads_per_seq=torch.tensor(hv, dtype=torch.int32, device=DEV), out=out)
+    torch.cuda.synchronize()
+    ref, st = oracle.conv1d_silu(inp["xbc"].to(dtype), inp["w"], bias, conv_state_to_oracle(cs0),
+                                 d_inner=w.d_inner, d_head=w.d_head, heads_active=hv)
+    got, gs, want_s = f64(out), f64(cs), conv_state_from_oracle(st)
+    for bb, h in enumerate(hv):
+        act = np.r_[0:h * w.d_head, w.d_inner:w.conv_dim]
+        ina = np.r_[h * w.d_head:w.d_inner]
+        assert oracle.rel_l2(got[bb][..., act], ref[bb][..., act]) < TOL[dtype]
+        assert np.isnan(got[bb][..., ina]).all()
+        np.testing.assert_allclose(gs[bb][:, act], want_s[bb][:, act], rtol=0, atol=0)
+        np.testing.assert_array_equal(gs[bb][:, ina], f64(cs0)[bb][:, ina])
+
+
 def test_conv_bf16_per_sequence_slices_and_long_run():
     w = M130
     b, l = 3, 300
