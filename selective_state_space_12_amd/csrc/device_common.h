@@ -34,6 +34,15 @@ __device__ __forceinline__ Vec16<T> load16(const T* p) {
   return r;
 }
 
+// For data read exactly once (a streamed input): a nontemporal load.
+template <typename T>
+__device__ __forceinline__ Vec16<T> load16_once(const T* p) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  Vec16<T> r;
+  *reinterpret_cast<u32x4_t*>(r.v) = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return r;
+}
+
 template <typename T>
 __device__ __forceinline__ void store16(T* p, const Vec16<T>& r) {
   *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(r.v);

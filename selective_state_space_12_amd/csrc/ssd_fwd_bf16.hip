@@ -199,8 +199,11 @@ __global__ __launch_bounds__(512) void tile_prep_kernel(const bf16* __restrict__
   for (int v = tid; v < kQ * (kN / 8); v += 512) {
     const int s = v / (kN / 8), col = (v % (kN / 8)) * 8;
     const int64_t r = row0 + min(s, last);
-    *reinterpret_cast<uint4*>(&Bs[s][col]) = *reinterpret_cast<const uint4*>(Bp + r * bs + col);
-    *reinterpret_cast<uint4*>(&Cs[s][col]) = *reinterpret_cast<const uint4*>(Cp + r * cs + col);
+    // B and C rows are read once here (nontemporal: prep 12.0 vs 13.7 us)
+    *reinterpret_cast<u32x4*>(&Bs[s][col]) =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Bp + r * bs + col));
+    *reinterpret_cast<u32x4*>(&Cs[s][col]) =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cp + r * cs + col));
   }
   __syncthreads();
 
