@@ -167,7 +167,10 @@ __device__ __forceinline__ float dpp_f(float v) {
 // the B and C rows in LDS with whole-row loads and forms every fragment from
 // there.
 constexpr int kBCP = kN + 8;  // LDS row pitch (elements) of the staged B and C rows
-constexpr size_t kPrepLds = 2 * (size_t)kQ * kBCP * sizeof(bf16) + 64 * (kQ + 2) * sizeof(bf16);
+// B and C rows; the dt transpose buffer reuses the C rows once the G and C
+// fragments are out (68 KB: two workgroups per CU)
+constexpr size_t kPrepLds = 2 * (size_t)kQ * kBCP * sizeof(bf16);
+static_assert(64 * (kQ + 2) <= kQ * kBCP, "dt buffer fits in the C rows");
 
 __global__ __launch_bounds__(512) void tile_prep_kernel(const bf16* __restrict__ Bp, int64_t bs,
                                                         const bf16* __restrict__ Cp, int64_t cs,
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(512) void tile_prep_kernel(const bf16* __restrict__
   extern __shared__ __align__(16) unsigned char psm[];
   bf16 (*Bs)[kBCP] = reinterpret_cast<bf16 (*)[kBCP]>(psm);
   bf16 (*Cs)[kBCP] = reinterpret_cast<bf16 (*)[kBCP]>(psm + (size_t)kQ * kBCP * sizeof(bf16));
-  bf16 (*Dt)[kQ + 2] = reinterpret_cast<bf16 (*)[kQ + 2]>(psm + 2 * (size_t)kQ * kBCP * sizeof(bf16));
+  bf16 (*Dt)[kQ + 2] = reinterpret_cast<bf16 (*)[kQ + 2]>(psm + (size_t)kQ * kBCP * sizeof(bf16));
   const int c = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
   const int64_t row0 = (int64_t)b * seqlen + (int64_t)c * kQ;
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(512) void tile_prep_kernel(const bf16* __restrict__
   for (int h0 = 0; h0 < heads; h0 += 64) {
     const int nh = min(64, heads - h0);
     if (h0 > 0) load_dt(h0, nh);
-    __syncthreads();  // previous group's rows have been written out
+    __syncthreads();  // C rows (aliased) consumed / previous group's rows written out
     if (hh < nh) {
 #pragma unroll
       for (int i = 0; i < kQ / 8; ++i) Dt[hh][(tid >> 6) + 8 * i] = dv[i];
@@ -642,13 +645,14 @@ template <bool OUT>
 __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(BK k) {
   extern __shared__ __align__(16) unsigned char smem[];
   // XCD-aware unit mapping: consecutive workgroups go to different XCDs, so
-  // give each XCD a contiguous block of (sequence, head, segment) units; the
-  // heads of a sequence then share one L2 for the G and B^T fragments.
+  // give each XCD a contiguous block of units numbered head fastest; the heads
+  // that walk the same tiles (same sequence and segment) then share one L2 for
+  // the fragments.
   const int gx = gridDim.x, gy = gridDim.y;
   const int total = gx * gy * gridDim.z;
   const int pid = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
   const int uid = total % kXcds == 0 ? (pid % kXcds) * (total / kXcds) + pid / kXcds : pid;
-  const int seg = uid % gx, h = (uid / gx) % gy, b = uid / (gx * gy);
+  const int h = uid % gy, seg = (uid / gy) % gx, b = uid / (gx * gy);
   const int c0 = seg * k.seg_chunks;
   const int c1 = min(c0 + k.seg_chunks, k.ntiles);
   if (c0 >= c1) return;  // whole workgroup
