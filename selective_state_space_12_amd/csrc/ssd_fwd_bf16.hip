@@ -572,19 +572,19 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
   };
   // dt of tokens 2*lane, 2*lane + 1 of a tile (head-major copy), kept raw
   // until make_dec (a conversion here would make the wave wait for the load)
-  uint32_t dtr_raw;
-  auto load_dt = [&](int c) {
-    dtr_raw = reinterpret_cast<const uint32_t*>(
+  auto load_dt = [&](int c) -> uint32_t {
+    return reinterpret_cast<const uint32_t*>(
         k.dtT + (((int64_t)b * k.ntiles + c) * k.heads + h) * kQ)[lane];
   };
+  uint32_t dtr_raw;
   // Lambda (inclusive cumsum of dt*A, log2 units), dt and block-end factor
   // exp2(Lambda_e - Lambda_s) dt_s of tile c (dt = 0 past the end of the
   // sequence).
-  auto make_dec = [&](int c, int buf) {
+  auto make_dec = [&](int c, int buf, uint32_t raw) {
     const int len = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ);
     float dtr[2];
-    dtr[0] = 2 * lane < len ? __builtin_bit_cast(float, dtr_raw << 16) : 0.0f;
-    dtr[1] = 2 * lane + 1 < len ? __builtin_bit_cast(float, dtr_raw & 0xffff0000u) : 0.0f;
+    dtr[0] = 2 * lane < len ? __builtin_bit_cast(float, raw << 16) : 0.0f;
+    dtr[1] = 2 * lane + 1 < len ? __builtin_bit_cast(float, raw & 0xffff0000u) : 0.0f;
     float* d = dbuf + buf * kDec;
     const float v0 = dtr[0] * Ah2, v1 = dtr[1] * Ah2;
     // inclusive scan over the wave with DPP row shifts and row broadcasts
@@ -620,21 +620,20 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
   const int cl = c1 - 1;
   float lam_seg = 0.0f;
   load_x(c0);
-  load_dt(c0);
-  lam_seg += make_dec(c0, c0 % 3);
-  load_dt(min(c0 + 1, cl));
-  if (c0 + 1 < c1) lam_seg += make_dec(c0 + 1, (c0 + 1) % 3);
+  const uint32_t dt0 = load_dt(c0), dt1 = load_dt(min(c0 + 1, cl));  // both in flight
+  lam_seg += make_dec(c0, c0 % 3, dt0);
+  if (c0 + 1 < c1) lam_seg += make_dec(c0 + 1, (c0 + 1) % 3, dt1);
   __syncthreads();
   commit(c0 & 1, c0 % 3);
   load_x(min(c0 + 1, cl));
-  load_dt(min(c0 + 2, cl));
+  dtr_raw = load_dt(min(c0 + 2, cl));
   __syncthreads();
 
   for (int c = c0; c < c1; ++c) {
     if (c + 1 < c1) commit((c + 1) & 1, (c + 1) % 3);
     load_x(min(c + 2, cl));
-    if (c + 2 < c1) lam_seg += make_dec(c + 2, (c + 2) % 3);
-    load_dt(min(c + 3, cl));
+    if (c + 2 < c1) lam_seg += make_dec(c + 2, (c + 2) % 3, dtr_raw);
+    dtr_raw = load_dt(min(c + 3, cl));
     __syncthreads();
   }
   if (!OUT && v == 0 && lane == 0)
