@@ -21,15 +21,18 @@
 //    block each), four own the fp32 state in MFMA accumulators, four stage x
 //    and the decay cumsums; every SIMD runs waves of all three kinds, so the
 //    output MFMAs overlap the state update and the staging.
-//  - x stays token-major in LDS: the staging waves write three copies (plain,
-//    times the block-end decay, times the end decay) with 16-byte writes, and
-//    the MFMA waves read them as operands with LDS transpose loads.
+//  - x and the bf16 copy of H live in LDS as MFMA operand fragments
+//    (lane-major, 16 bytes per lane), so every operand read is a linear,
+//    conflict-free 16-byte load.  Each staging wave transposes its 32 tokens
+//    once per tile (raw rows to LDS, LDS transpose loads back) and writes two
+//    x copies: plain, and times the block-end decay.
 //  - off-diagonal 32-token blocks factor the decay as
 //    exp(Lambda_t - Lambda_e) * exp(Lambda_e - Lambda_s) dt_s (e = block end,
 //    both factors <= 1); the first factor is applied to the accumulator in
 //    Horner form (one scalar per block), so G enters the MFMA unscaled.  The
-//    diagonal block takes the direct masked form, with D folded into the
-//    diagonal of the mask.
+//    state update uses the same block-scaled copy with the same Horner
+//    factors on its accumulators.  The diagonal block takes the direct masked
+//    form, with D folded into the diagonal of the mask.
 //  - output rows are dealt to the A operand in an order that leaves each lane
 //    eight consecutive channels of a token, stored as one 16-byte write;
 //  - LDS tiles are double-buffered and the decay cumsums triple-buffered, so
