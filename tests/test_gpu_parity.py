@@ -146,6 +146,24 @@ def test_scan_130m_bf16_all_slices_ragged(chunk):
         assert torch.isnan(y[:, :, h:]).all() and torch.isnan(hT[:, h:]).all()
 
 
+@pytest.mark.parametrize("seqlen", [1, 2, 127, 128, 129, 255, 257, 383])
+def test_scan_bf16_tile_boundaries(seqlen):
+    """The bf16 d_head 64 / d_state 128 path at lengths around its 128-token
+    tiles: one sequence, so few (sequence, head) units and the call splits
+    into one-tile segments (prepass + combine); one head and all heads; chunk
+    128 and 256; initial and final states; heads beyond the slice untouched."""
+    w = M130
+    inp = synth.forward_inputs(w, batch=1, seqlen=seqlen, with_state=True, salt=5)
+    for h in (1, w.n_heads):
+        yr, hr = oracle_forward(inp, h)
+        for chunk in (128, 256):
+            say(f"scan bf16 tile boundaries l={seqlen} heads={h} chunk={chunk}")
+            y, hT = run_forward(inp, h, chunk, y_fill=float("nan"))
+            e_y, e_h = rel_l2(y[:, :, :h], yr), rel_l2(hT[:, :h], hr)
+            assert e_y < TOL[torch.bfloat16] and e_h < TOL[torch.bfloat16], (e_y, e_h)
+            assert torch.isnan(y[:, :, h:]).all() and torch.isnan(hT[:, h:]).all()
+
+
 @pytest.mark.parametrize("m", [256, 2048])
 def test_scan_1p4b_full_size_sampled(m):
     """Full 1.4B-scale call (b=4, l=8192) in the benchmark's launch
