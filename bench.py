@@ -13,6 +13,7 @@ Also reported on the same JSON line:
     tile_prep_kernel (per-tile C.B^T, B^T and C fragments and head-major dt,
     shared by the heads) and ssd_bf16_kernel (the scan itself);
   - ``slices``: scan-only tokens/s and HBM fraction at every Matryoshka width;
+  - ``configs``: the same for the 130M-scale and long-context workloads;
   - ``decode``: the recurrent decode step (conv state roll + scan step) for a
     batch of 256 sequences at mixed widths, 1024 tokens captured in a HIP graph;
   - ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample
@@ -146,6 +147,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-slices", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the scan-only timings of the 130M and long-context workloads")
     ap.add_argument("--mode", choices=["step", "scan", "copy"], default="step",
                     help="scan: only the full-width scan (for counter runs); "
                          "copy: a 1 GiB device copy that calibrates the HBM byte counters")
@@ -308,6 +311,12 @@ def main():
         out["conv"] = {"ms": tc, "hbm_frac": cb / (tc * 1e-3) / (HBM_PEAK_GBS * 1e9),
                        "copy_same_bytes_ms": tcopy, "vs_copy": tcopy / tc}
 
+    # ---- the other bf16 workloads, scan only, every slice ----------------------
+    if not args.no_configs:
+        del xbc_raw, xbc, xv, Bv, Cv, y, ws
+        torch.cuda.empty_cache()
+        out["configs"] = bench_configs(torch, mm, synth, dev)
+
     # ---- decode: conv state roll + scan step, 1024 tokens in a HIP graph -----
     if not args.no_decode:
         out["decode"] = bench_decode(torch, mm, synth, dev)
@@ -317,6 +326,51 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w)
 
     print(json.dumps(out), flush=True)
+
+
+def bench_configs(torch, mm, synth, dev):
+    """Scan-only tokens/s and HBM fraction at every slice of the 130M-scale
+    (b=8, l=2048, 24 heads) and long-context (b=1, l=131072, 32 heads)
+    workloads: dense seeded inputs (x, dt, B, C as separate tensors), no initial
+    state, HIP events around 10 calls after 3 warmup calls."""
+    res = {}
+    for name in ("130m", "long"):
+        w = synth.WORKLOADS[name]
+        print(f"# generating inputs for {name}: b={w.batch} l={w.seqlen}", file=sys.stderr, flush=True)
+        inp = synth.forward_inputs(w)
+        d = {k: v.to(dev) for k, v in inp.items()}
+        del inp
+        y = torch.empty_like(d["x"])
+        tokens = w.batch * w.seqlen
+        per = {}
+        for m in w.slices:
+            h = w.heads(m)
+            need = mm.ssd_forward_workspace_size(w.batch, w.seqlen, w.n_heads, w.d_head, w.d_state,
+                                                 1, h, w.chunk, w.dtype)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+            def call():
+                mm.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], n_heads_active=h,
+                               chunk=w.chunk, y=y, workspace=ws)
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record()
+            for _ in range(10):
+                call()
+            s1.record()
+            torch.cuda.synchronize()
+            t = s0.elapsed_time(s1) / 10
+            ab = scan_bytes(tokens, h, w.d_head, w.d_state, 2)
+            per[str(m)] = {"heads": h, "scan_ms": t, "tokens_per_s": tokens / (t * 1e-3),
+                           "hbm_frac": ab / (t * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+            del ws
+        res[name] = {"batch": w.batch, "seq_len": w.seqlen, "n_heads": w.n_heads, "slices": per}
+        del d, y
+        torch.cuda.empty_cache()
+    return res
 
 
 def bench_decode(torch, mm, synth, dev):

@@ -84,6 +84,12 @@ int fwd_segments(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
 // bf16, d_head 64, d_state 128, chunk 128 or 256 (ssd_fwd_bf16.hip).
 bool bf16_path(int64_t d_head, int64_t d_state, int64_t chunk, int dtype);
 size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads);
+// The bf16 path's cut (128-token tiles): the segment count that minimises an
+// estimate of the call's time in tile-walk units, counting workgroup rounds
+// of one workgroup per CU, the per-walk start-up and the prepass and combine
+// that a split adds.
+void fwd_plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int* ntiles, int* nseg,
+                   int* seg_tiles);
 hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* workspace, hipStream_t s);
 
 hipError_t launch_ssd_forward(const FwdArgs& a, int dtype, void* workspace, hipStream_t s);

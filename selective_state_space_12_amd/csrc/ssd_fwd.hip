@@ -711,9 +711,11 @@ void fwd_plan(int64_t batch, int64_t seqlen, int64_t heads, int64_t chunk, int* 
 
 int fwd_segments(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
                  int64_t d_state, int64_t chunk, int dtype) {
-  const int64_t q = bf16_path(d_head, d_state, chunk, dtype) ? 128 : chunk;
   int nc, nseg, per;
-  fwd_plan(batch, seqlen, heads, q, &nc, &nseg, &per);
+  if (bf16_path(d_head, d_state, chunk, dtype))
+    fwd_plan_bf16(batch, seqlen, heads, &nc, &nseg, &per);
+  else
+    fwd_plan(batch, seqlen, heads, chunk, &nc, &nseg, &per);
   return nseg;
 }
 

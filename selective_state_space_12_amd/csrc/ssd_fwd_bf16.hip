@@ -730,9 +730,38 @@ bool bf16_path(int64_t d_head, int64_t d_state, int64_t chunk, int dtype) {
   return dtype == MM_BF16 && d_head == kP && d_state == kN && (chunk == 128 || chunk == 256);
 }
 
+void fwd_plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int* ntiles, int* nseg,
+                   int* seg_tiles) {
+  // Cost in units of one tile step of a workgroup (about 2.7 us on MI355X):
+  // each round of up to kCus workgroups costs its walk plus ~2.5 tiles of
+  // start-up (first loads from HBM, state in, pipeline fill and drain); the
+  // prepass walks at about half the main kernel's rate per tile; the combine
+  // and the two extra launches add ~3 tiles.
+  constexpr int64_t kCus = 256;
+  const int64_t n = (seqlen + kQ - 1) / kQ;
+  const int64_t units = batch * heads;
+  int64_t best_per = n > 0 ? n : 1, best_seg = 1;
+  double best = 1e300;
+  for (int64_t want = 1; want <= n; ++want) {
+    const int64_t per = (n + want - 1) / want;
+    const int64_t seg = (n + per - 1) / per;
+    if (seg != want) continue;  // the same cut as a smaller count
+    const int64_t r_main = (units * seg + kCus - 1) / kCus;
+    double cost = (double)r_main * ((double)per + 2.5);
+    if (seg > 1) {
+      const int64_t r_pre = (units * (seg - 1) + kCus - 1) / kCus;
+      cost += (double)r_pre * (0.5 * (double)per + 2.5) + 3.0;
+    }
+    if (cost < best) { best = cost; best_per = per; best_seg = seg; }
+  }
+  *ntiles = (int)n;
+  *seg_tiles = (int)best_per;
+  *nseg = (int)best_seg;
+}
+
 size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads) {
   int nt, nseg, per;
-  fwd_plan(batch, seqlen, heads, kQ, &nt, &nseg, &per);
+  fwd_plan_bf16(batch, seqlen, heads, &nt, &nseg, &per);
   size_t bytes = frag_region_bytes(batch, seqlen) + dt_region_bytes(batch, seqlen, heads);
   if (nseg > 1) bytes += (size_t)(batch * heads * nseg) * (size_t)(kP * kN + 1) * sizeof(float);
   return bytes;
@@ -769,7 +798,7 @@ hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
   k.y = static_cast<bf16*>(a.y); k.ys = a.ys;
   k.h0 = a.h0; k.hT = a.hT;
   k.seqlen = a.seqlen; k.n_heads = a.n_heads; k.heads = a.heads;
-  fwd_plan(a.batch, a.seqlen, a.heads, kQ, &k.ntiles, &k.nseg, &k.seg_chunks);
+  fwd_plan_bf16(a.batch, a.seqlen, a.heads, &k.ntiles, &k.nseg, &k.seg_chunks);
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   uint4* frags = reinterpret_cast<uint4*>(wsb);
   bf16* dtT = reinterpret_cast<bf16*>(wsb + frag_region_bytes(a.batch, a.seqlen));

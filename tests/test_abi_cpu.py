@@ -94,9 +94,14 @@ def test_segments_query(lib):
     f.argtypes = [ctypes.c_int64] * 8 + [ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     n = ctypes.c_int()
     assert f(4, 8192, 64, 64, 128, 1, 64, 256, 1, ctypes.byref(n)) == 0 and n.value == 1
-    # 4 x 8 units at 64 tiles each: split so that about 256 workgroups run
+    # bf16 path: split only where more workgroups pay for the prepass and
+    # combine.  4 x 8 units at 64 tiles each -> 8 segments (256 workgroups);
+    # 8 x 24 units at 16 tiles -> one walk (two rounds of 192 would cost more)
     assert f(4, 8192, 64, 64, 128, 1, 8, 256, 1, ctypes.byref(n)) == 0 and n.value == 8
     assert f(1, 131072, 32, 64, 128, 1, 8, 256, 1, ctypes.byref(n)) == 0 and n.value == 32
+    assert f(8, 2048, 24, 64, 128, 1, 24, 256, 1, ctypes.byref(n)) == 0 and n.value == 1
+    assert f(8, 2048, 24, 64, 128, 1, 3, 256, 1, ctypes.byref(n)) == 0 and n.value == 8
+    assert f(1, 383, 24, 64, 128, 1, 1, 128, 1, ctypes.byref(n)) == 0 and n.value == 1
     assert f(1, 100, 4, 32, 16, 1, 4, 64, 0, ctypes.byref(n)) == 0 and n.value == 2
     assert f(1, 100, 4, 32, 16, 1, 4, 64, 0, None) == -1
     assert f(1, 100, 4, 32, 16, 1, 4, 48, 0, ctypes.byref(n)) == -5

@@ -146,12 +146,35 @@ def test_scan_130m_bf16_all_slices_ragged(chunk):
         assert torch.isnan(y[:, :, h:]).all() and torch.isnan(hT[:, h:]).all()
 
 
+@pytest.mark.parametrize("seqlen", [2048, 2000])
+def test_scan_130m_full_shape_all_slices(seqlen):
+    """The 130M-scale call (b=8) at every slice in the benchmark's launch
+    configuration: 3 and 6 heads split each sequence into segments (8 of 2
+    tiles, 4 of 4 tiles), 12 and 24 heads walk it whole; at 2000 tokens the
+    last tile is ragged.  The oracle recomputes the first, middle and last
+    active head of every sequence."""
+    w = M130
+    inp = synth.forward_inputs(w, batch=8, seqlen=seqlen, with_state=True, salt=7)
+    want = {3: 8, 6: 4, 12: 1, 24: 1}
+    for m in w.slices:
+        h = w.heads(m)
+        assert mm.ssd_forward_segments(8, seqlen, w.n_heads, 64, 128, 1, h, w.chunk, w.dtype) == want[h]
+        say(f"scan 130m bf16 b=8 l={seqlen} heads={h}")
+        y, hT = run_forward(inp, h, w.chunk, y_fill=float("nan"))
+        sample = sorted({0, h // 2, h - 1})
+        yr, hr = oracle_forward(inp, h, head_idx=sample)
+        e_y, e_h = rel_l2(y[:, :, sample], yr), rel_l2(hT[:, sample], hr)
+        say(f"  heads {sample}: rel_l2 y={e_y:.3e} state={e_h:.3e}")
+        assert e_y < TOL[torch.bfloat16] and e_h < TOL[torch.bfloat16]
+        assert torch.isnan(y[:, :, h:]).all() and torch.isnan(hT[:, h:]).all()
+
+
 @pytest.mark.parametrize("seqlen", [1, 2, 127, 128, 129, 255, 257, 383])
 def test_scan_bf16_tile_boundaries(seqlen):
     """The bf16 d_head 64 / d_state 128 path at lengths around its 128-token
-    tiles: one sequence, so few (sequence, head) units and the call splits
-    into one-tile segments (prepass + combine); one head and all heads; chunk
-    128 and 256; initial and final states; heads beyond the slice untouched."""
+    tiles (one sequence, one unsplit walk per head); one head and all heads;
+    chunk 128 and 256; initial and final states; heads beyond the slice
+    untouched."""
     w = M130
     inp = synth.forward_inputs(w, batch=1, seqlen=seqlen, with_state=True, salt=5)
     for h in (1, w.n_heads):
@@ -202,13 +225,14 @@ def test_scan_long_context_segments(m):
 def test_scan_more_than_64_heads_segmented():
     """A block wider than the 130M one (96 heads of 64, 80 active): the
     per-tile dt staging runs over the heads in groups of 64, and the few
-    (sequence, head) units split a ragged 3-tile sequence into segments."""
+    (sequence, head) units split a 32-tile sequence (last tile ragged) into
+    segments of 11, 11 and 10 tiles."""
     import dataclasses
     w = dataclasses.replace(M130, d_model=3072, d_inner=6144)
     h = 80
-    inp = synth.forward_inputs(w, batch=1, seqlen=300, with_state=True)
-    assert mm.ssd_forward_segments(1, 300, w.n_heads, 64, 128, 1, h, 256, w.dtype) > 1
-    say(f"scan bf16 wide block: {w.n_heads} heads, {h} active, l=300")
+    inp = synth.forward_inputs(w, batch=1, seqlen=4000, with_state=True)
+    assert mm.ssd_forward_segments(1, 4000, w.n_heads, 64, 128, 1, h, 256, w.dtype) == 3
+    say(f"scan bf16 wide block: {w.n_heads} heads, {h} active, l=4000")
     y, hT = run_forward(inp, h, 256)
     sample = [0, 63, 64, 79]
     yr, hr = oracle_forward(inp, h, head_idx=sample)
