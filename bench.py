@@ -12,7 +12,9 @@ Also reported on the same JSON line:
     stream it runs on), against MI355X's 8 TB/s.  A scan call is two kernels:
     tile_prep_kernel (per-tile C.B^T, B^T and C fragments and head-major dt,
     shared by the heads) and ssd_bf16_kernel (the scan itself);
-  - ``slices``: scan-only tokens/s and HBM fraction at every Matryoshka width;
+  - ``slices``: scan-only tokens/s, HBM and MFMA fractions at every
+    Matryoshka width: 5 warmup calls, then 50 calls timed one by one with HIP
+    events, each after a 512 MiB write that evicts the caches; median, p10, p90;
   - ``configs``: the same for the 130M-scale and long-context workloads;
   - ``decode``: the recurrent decode step (conv state roll + scan step) for a
     batch of 256 sequences at mixed widths, 1024 tokens captured in a HIP graph;
@@ -100,6 +102,50 @@ def scan_bytes(tokens: int, heads: int, P: int, N: int, elem: int) -> int:
     """Algorithmic HBM bytes of one scan call: x and y of the active heads,
     B and C, and dt of the active heads (A, D negligible)."""
     return tokens * (2 * heads * P * elem + 2 * N * elem + heads * elem)
+
+
+def scan_flops(tokens: int, heads: int, P: int, N: int, Q: int) -> int:
+    """Algorithmic flops of one scan call, causal-counted chunked form at chunk
+    Q with one B/C group: (Q+1) N for the shared C.B^T blocks, and per head
+    (Q+1) P for the masked product with x plus 4 P N for the chunk state and
+    the inter-chunk output term."""
+    return tokens * ((Q + 1) * N + heads * ((Q + 1) * P + 4 * P * N))
+
+
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16
+FLUSH_BYTES = 512 << 20
+
+
+def timed_calls(torch, fn, flush, iters: int = 50, warmup: int = 5):
+    """Per-call HIP-event timing: ``warmup`` untimed calls, then ``iters``
+    calls each preceded by a write of ``flush`` (512 MiB, larger than the L2s
+    and the 256 MB Infinity Cache together) so that every call starts cold.
+    Returns the median, p10 and p90 in ms."""
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    torch.cuda.synchronize()
+    for i in range(iters):
+        flush.fill_(i & 0x7F)
+        ev[i][0].record()
+        fn()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(z) for a, z in ev)
+    q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
+    return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9)}
+
+
+def scan_entry(tokens, h, P, N, Q, t):
+    """JSON fields of one scan timing ``t`` (median/p10/p90 in ms)."""
+    ms = t["median"]
+    ab = scan_bytes(tokens, h, P, N, 2)
+    fl = scan_flops(tokens, h, P, N, Q)
+    return {"heads": h, "scan_ms": ms, "scan_ms_p10": t["p10"], "scan_ms_p90": t["p90"],
+            "tokens_per_s": tokens / (ms * 1e-3),
+            "hbm_frac": ab / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "mfma_frac": fl / (ms * 1e-3) / (MFMA_PEAK_TFLOPS * 1e12)}
 
 
 def conv_bytes(tokens: int, channels: int, elem: int) -> int:
@@ -268,54 +314,34 @@ def main():
     }
 
     # ---- every Matryoshka width, scan only -----------------------------------
+    flush = None
+    if not (args.no_slices and args.no_configs):
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     if not args.no_slices:
         slices = {}
         for m in w.slices:
             h = w.heads(m)
-            for _ in range(3):
-                scan(h)
-            torch.cuda.synchronize()
-            s0 = torch.cuda.Event(enable_timing=True)
-            s1 = torch.cuda.Event(enable_timing=True)
-            reps = 10
-            s0.record(stream)
-            for _ in range(reps):
-                scan(h)
-            s1.record(stream)
-            torch.cuda.synchronize()
-            t = s0.elapsed_time(s1) / reps
-            ab = scan_bytes(tokens, h, P, N, elem)
-            slices[str(m)] = {"heads": h, "scan_ms": t, "tokens_per_s": tokens / (t * 1e-3),
-                              "hbm_frac": ab / (t * 1e-3) / (HBM_PEAK_GBS * 1e9)}
-        # conv alone at full width
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        for _ in range(10):
-            conv(H)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        tc = c0.elapsed_time(c1) / 10
-        cb = conv_bytes(tokens, w.conv_dim, elem)
-        # practical ceiling for the same read + write traffic: a plain device copy
+            slices[str(m)] = scan_entry(tokens, h, P, N, w.chunk,
+                                        timed_calls(torch, lambda: scan(h), flush))
+        # conv alone at full width, and a plain device copy of the same bytes
+        # (the practical ceiling for that read + write traffic)
+        tcv = timed_calls(torch, lambda: conv(H), flush)
         cpy = torch.empty_like(xbc_raw)
-        cpy.copy_(xbc_raw)
-        c0.record(stream)
-        for _ in range(10):
-            cpy.copy_(xbc_raw)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        tcopy = c0.elapsed_time(c1) / 10
+        tcp = timed_calls(torch, lambda: cpy.copy_(xbc_raw), flush)
         del cpy
+        tc, tcopy = tcv["median"], tcp["median"]
+        cb = conv_bytes(tokens, w.conv_dim, elem)
         out["slices"] = slices
-        out["conv"] = {"ms": tc, "hbm_frac": cb / (tc * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        out["conv"] = {"ms": tc, "ms_p10": tcv["p10"], "ms_p90": tcv["p90"],
+                       "tokens_per_s": tokens / (tc * 1e-3), "gb_per_s": cb / (tc * 1e-3) / 1e9,
+                       "hbm_frac": cb / (tc * 1e-3) / (HBM_PEAK_GBS * 1e9),
                        "copy_same_bytes_ms": tcopy, "vs_copy": tcopy / tc}
 
     # ---- the other bf16 workloads, scan only, every slice ----------------------
     if not args.no_configs:
         del xbc_raw, xbc, xv, Bv, Cv, y, ws
         torch.cuda.empty_cache()
-        out["configs"] = bench_configs(torch, mm, synth, dev)
+        out["configs"] = bench_configs(torch, mm, synth, dev, flush)
 
     # ---- decode: conv state roll + scan step, 1024 tokens in a HIP graph -----
     if not args.no_decode:
@@ -328,11 +354,11 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def bench_configs(torch, mm, synth, dev):
-    """Scan-only tokens/s and HBM fraction at every slice of the 130M-scale
-    (b=8, l=2048, 24 heads) and long-context (b=1, l=131072, 32 heads)
-    workloads: dense seeded inputs (x, dt, B, C as separate tensors), no initial
-    state, HIP events around 10 calls after 3 warmup calls."""
+def bench_configs(torch, mm, synth, dev, flush):
+    """Scan-only tokens/s, HBM and MFMA fractions at every slice of the
+    130M-scale (b=8, l=2048, 24 heads) and long-context (b=1, l=131072, 32
+    heads) workloads: dense seeded inputs (x, dt, B, C as separate tensors),
+    no initial state, timed as the 1.4B slices are (``timed_calls``)."""
     res = {}
     for name in ("130m", "long"):
         w = synth.WORKLOADS[name]
@@ -352,20 +378,8 @@ def bench_configs(torch, mm, synth, dev):
             def call():
                 mm.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], n_heads_active=h,
                                chunk=w.chunk, y=y, workspace=ws)
-            for _ in range(3):
-                call()
-            torch.cuda.synchronize()
-            s0 = torch.cuda.Event(enable_timing=True)
-            s1 = torch.cuda.Event(enable_timing=True)
-            s0.record()
-            for _ in range(10):
-                call()
-            s1.record()
-            torch.cuda.synchronize()
-            t = s0.elapsed_time(s1) / 10
-            ab = scan_bytes(tokens, h, w.d_head, w.d_state, 2)
-            per[str(m)] = {"heads": h, "scan_ms": t, "tokens_per_s": tokens / (t * 1e-3),
-                           "hbm_frac": ab / (t * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+            per[str(m)] = scan_entry(tokens, h, w.d_head, w.d_state, w.chunk,
+                                     timed_calls(torch, call, flush))
             del ws
         res[name] = {"batch": w.batch, "seq_len": w.seqlen, "n_heads": w.n_heads, "slices": per}
         del d, y
