@@ -195,6 +195,43 @@ def ssd_step(state, x_t, dt_t, A, B_t, C_t, D=None, *, heads_active=None):
     return y, st
 
 
+def softplus(v):
+    """softplus(v) = log(1 + e^v), the map from the raw W_dt projection (plus
+    its bias) to the step size dt (MatMamba page, block paragraph: W_dt is one
+    of the input projections; the workloads draw dt as softplus of a Gaussian).
+    Written as log(e^0 + e^v) with numpy's logaddexp, which evaluates it
+    without overflow."""
+    return np.logaddexp(0.0, _f64(v))
+
+
+def ssd_forward_fused(xbc, w, dt, A, D=None, *, d_inner, d_head, conv_bias=None,
+                      conv_state=None, dt_bias=None, dt_softplus=False, h0=None,
+                      heads_active=None):
+    """The block's prefill path as one composition (MatMamba page, block
+    paragraph: the conv over the concatenated x, B, C streams feeds the chunk +
+    selective scan): u = conv1d_silu(xbc); x, B, C = the d_inner, d_state and
+    d_state column ranges of u; dt' = dt + dt_bias, through softplus if asked;
+    then ssd_forward.  xbc: (batch, seqlen, conv_dim) raw conv input; dt:
+    (batch, seqlen, n_heads) raw.  conv_state in this module's layout
+    (batch, conv_dim, 3).  Returns (y, h_final, new_conv_state)."""
+    xbc = _f64(xbc)
+    batch, seqlen, conv_dim = xbc.shape
+    n_heads = d_inner // d_head
+    N = (conv_dim - d_inner) // 2
+    u, new_state = conv1d_silu(xbc, w, conv_bias, conv_state, d_inner=d_inner, d_head=d_head,
+                               heads_active=heads_active)
+    x = u[:, :, :d_inner].reshape(batch, seqlen, n_heads, d_head)
+    B = u[:, :, d_inner:d_inner + N][:, :, None, :]
+    C = u[:, :, d_inner + N:d_inner + 2 * N][:, :, None, :]
+    d = _f64(dt).reshape(batch, seqlen, n_heads)
+    if dt_bias is not None:
+        d = d + _f64(dt_bias).reshape(1, 1, n_heads)
+    if dt_softplus:
+        d = softplus(d)
+    y, hf = ssd_forward(x, d, A, B, C, D, h0, heads_active=heads_active)
+    return y, hf, new_state
+
+
 def rel_l2(a, b) -> float:
     """Relative L2 distance ||a - b|| / ||b|| in fp64 (b is the reference)."""
     a = _f64(a)

@@ -324,3 +324,56 @@ def test_slice_resolution():
     for bad in (0, -32, 2049, 16, 100):
         with pytest.raises(ValueError):
             oracle.heads_for_dim(2048, 4096, 64, bad)
+
+
+def test_softplus_closed_forms():
+    """softplus(v) = log(1 + e^v): softplus(0) = ln 2, softplus(v) -
+    softplus(-v) = v (e^v = (1 + e^v)/(1 + e^-v)), softplus(v) -> v for large v
+    and -> e^v for very negative v; agrees with torch's fp64 softplus."""
+    assert abs(oracle.softplus(0.0) - math.log(2.0)) < 1e-16
+    v = np.linspace(-30.0, 30.0, 241)
+    np.testing.assert_allclose(oracle.softplus(v) - oracle.softplus(-v), v, rtol=0, atol=1e-13)
+    assert oracle.softplus(60.0) == 60.0
+    assert abs(oracle.softplus(-40.0) / math.exp(-40.0) - 1.0) < 1e-12
+    ref = torch.nn.functional.softplus(torch.from_numpy(v), beta=1.0, threshold=1000.0).numpy()
+    np.testing.assert_allclose(oracle.softplus(v), ref, rtol=1e-14, atol=1e-300)
+
+
+@pytest.mark.parametrize("softplus_on", [False, True])
+def test_fused_composition_columns_and_dt(softplus_on):
+    """The fused prefill composition takes x, B and C from the d_inner, d_state
+    and d_state column ranges of the conv output and feeds dt + dt_bias
+    (through softplus) to the scan.  With a current-token-only conv filter the
+    conv output is SiLU(u) = u * expit(u) (scipy's logistic function), so the
+    expected result is the scan on independently sliced columns; the returned
+    conv state is the last three raw inputs."""
+    import scipy.special
+    rng = np.random.default_rng(41)
+    b, l, H, P, N = 2, 9, 3, 2, 3
+    d_inner = H * P
+    cd = d_inner + 2 * N
+    u = rng.standard_normal((b, l, cd))
+    w = np.zeros((cd, 4))
+    w[:, 3] = 1.0
+    dt = rng.standard_normal((b, l, H)) - 1.0
+    dtb = rng.standard_normal(H) * 0.3
+    A = -np.exp(rng.uniform(0, math.log(16.0), H))
+    D = rng.standard_normal(H)
+    h0 = rng.standard_normal((b, H, P, N))
+    st0 = rng.standard_normal((b, cd, 3))
+    for h in (1, H):
+        y, hf, st = oracle.ssd_forward_fused(u, w, dt, A, D, d_inner=d_inner, d_head=P,
+                                             conv_state=st0, dt_bias=dtb, dt_softplus=softplus_on,
+                                             h0=h0, heads_active=h)
+        s = u * scipy.special.expit(u)
+        x = np.stack([s[:, :, k * P:(k + 1) * P] for k in range(H)], axis=2)
+        Bm = s[:, :, d_inner:d_inner + N][:, :, None, :]
+        Cm = s[:, :, d_inner + N:][:, :, None, :]
+        de = dt + dtb[None, None, :]
+        if softplus_on:
+            de = np.log1p(np.exp(de))
+        yr, hr = oracle.ssd_forward(x, de, A, Bm, Cm, D, h0, heads_active=h)
+        np.testing.assert_allclose(y[:, :, :h], yr[:, :, :h], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(hf[:, :h], hr[:, :h], rtol=1e-12, atol=1e-13)
+        act = np.r_[0:h * P, d_inner:cd]
+        np.testing.assert_array_equal(st[:, act], u[:, -3:, :].transpose(0, 2, 1)[:, act])
