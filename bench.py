@@ -2,19 +2,25 @@
 
 One step = the prefill path of the 1.4B-scale block on one batch of seeded
 synthetic input resident in HBM: causal conv1d (kernel 4) + SiLU over the
-[x | B | C] stream (b=4, l=8192, 4352 channels, bf16), then the chunked
-selective scan on strided views of the conv output (64 heads of 64, d_state
-128, chunk 256, full width m=2048).  ``value`` is tokens/s of that step.
+[x | B | C] stream (b=4, l=8192, 4352 channels, bf16), the dt of the
+workload, and the chunked selective scan (64 heads of 64, d_state 128, chunk
+256, full width m=2048), as one fused call (mm_ssd_forward_fused: the conv
+runs inside the scan kernels and its output never reaches HBM).  ``value`` is
+tokens/s of that step.
 
 Also reported on the same JSON line:
-  - ``roofline``: the scan call's algorithmic HBM bytes divided by its own
-    duration (HIP events around each scan call inside the timed steps, on the
-    stream it runs on), against MI355X's 8 TB/s.  A scan call is two kernels:
-    tile_prep_kernel (per-tile C.B^T, B^T and C fragments and head-major dt,
-    shared by the heads) and ssd_bf16_kernel (the scan itself);
-  - ``slices``: scan-only tokens/s, HBM and MFMA fractions at every
+  - ``roofline``: the fused call's algorithmic HBM bytes (raw x, B, C, dt in;
+    y out) divided by its own duration (HIP events around each call inside
+    the timed steps, on the stream it runs on), against MI355X's 8 TB/s.  A
+    fused call is two kernels: tile_prep_kernel (per tile, shared by the
+    heads: conv of B and C, C.B^T, B^T and C fragments, head-major dt) and
+    ssd_bf16_kernel (conv of x and the scan);
+  - ``unfused``: the same step as two calls, mm_conv1d_silu into a buffer and
+    mm_ssd_forward on strided views of it;
+  - ``slices``: the fused call's tokens/s, HBM and MFMA fractions at every
     Matryoshka width: 5 warmup calls, then 50 calls timed one by one with HIP
-    events, each after a 512 MiB write that evicts the caches; median, p10, p90;
+    events, each after a 512 MiB write that evicts the caches; median, p10,
+    p90; ``scan_slices``: the same for the scan call alone on the conv output;
   - ``configs``: the same for the 130M-scale and long-context workloads;
   - ``decode``: the recurrent decode step (conv state roll + scan step) for a
     batch of 256 sequences at mixed widths, 1024 tokens captured in a HIP graph;
@@ -36,9 +42,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ssd_scan_1p4b_m2048.json")
-SCAN_SRC = os.path.join(ROOT, "selective_state_space_12_amd", "csrc", "ssd_fwd_bf16.hip")
-SCAN_KERNELS = ("tile_prep_kernel", "ssd_bf16_kernel")  # the two kernels of one scan call
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_prefill_1p4b_m2048.json")
+SCAN_SRCS = [os.path.join(ROOT, "selective_state_space_12_amd", "csrc", f)
+             for f in ("ssd_fwd_bf16.hip", "device_common.h")]
+SCAN_KERNELS = ("tile_prep_kernel", "ssd_bf16_kernel")  # the two kernels of one call
 
 
 COPY_BYTES = 1 << 30
@@ -64,9 +71,9 @@ def _pmc_per_dispatch(dirname: str, counter: str, kernel_substr: str, min_grid: 
 
 
 def summarize_pmc(scan_fetch, scan_write, copy_fetch, copy_write):
-    """HBM bytes per scan call: FETCH_SIZE + WRITE_SIZE of its two kernels
-    (mean per dispatch of each, summed), each counter scaled by what it reads
-    for a copy of known size."""
+    """HBM bytes per fused prefill call (``--mode fused`` runs): FETCH_SIZE +
+    WRITE_SIZE of its two kernels (mean per dispatch of each, summed), each
+    counter scaled by what it reads for a copy of known size."""
     sf = sw = 0.0
     nsf, nsw = [], []
     for kname in SCAN_KERNELS:
@@ -85,8 +92,9 @@ def summarize_pmc(scan_fetch, scan_write, copy_fetch, copy_write):
     import synth
     w = synth.WORKLOADS["1.4b"]
     alg = scan_bytes(w.batch * w.seqlen, w.n_heads, w.d_head, w.d_state, 2)
-    rec = {"kernel": "scan call: tile_prep_kernel + ssd_bf16_kernel<true> (bf16, d_head 64, d_state 128, 128-token tiles)",
-           "workload": "1.4B-scale scan, b=4 l=8192, 64 heads, chunk 256, inputs as in bench.py",
+    rec = {"kernel": "fused prefill call: tile_prep_kernel<true> + ssd_bf16_kernel<true, true> "
+                     "(conv + scan, bf16, d_head 64, d_state 128, 128-token tiles)",
+           "workload": "1.4B-scale prefill, b=4 l=8192, 64 heads, chunk 256, inputs as in bench.py",
            "kernel_source_sha256_16": src_hash(),
            "fetch_kib_per_dispatch": sf, "write_kib_per_dispatch": sw,
            "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
@@ -163,10 +171,10 @@ def decode_bytes(heads_per_seq, P: int, N: int, d_inner: int) -> int:
 
 
 def src_hash() -> str:
-    """Hash of the scan kernel source with comments and blank space removed, so
-    a record of measured traffic stays valid across comment-only edits."""
+    """Hash of the scan kernel sources with comments and blank space removed,
+    so a record of measured traffic stays valid across comment-only edits."""
     import re
-    text = open(SCAN_SRC).read()
+    text = "".join(open(f).read() for f in SCAN_SRCS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
     text = re.sub(r"\s+", " ", text)
@@ -174,7 +182,7 @@ def src_hash() -> str:
 
 
 def load_traffic():
-    """HBM bytes per scan launch measured with rocprofv3 (FETCH_SIZE and
+    """HBM bytes per fused call measured with rocprofv3 (FETCH_SIZE and
     WRITE_SIZE, calibrated on a copy kernel), if taken on this kernel source."""
     try:
         d = json.load(open(TRAFFIC_FILE))
@@ -195,9 +203,10 @@ def main():
     ap.add_argument("--no-slices", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the scan-only timings of the 130M and long-context workloads")
-    ap.add_argument("--mode", choices=["step", "scan", "copy"], default="step",
-                    help="scan: only the full-width scan (for counter runs); "
-                         "copy: a 1 GiB device copy that calibrates the HBM byte counters")
+    ap.add_argument("--mode", choices=["step", "fused", "scan", "copy"], default="step",
+                    help="fused / scan: only the full-width fused call / scan call (for "
+                         "counter runs); copy: a 1 GiB device copy that calibrates the HBM "
+                         "byte counters")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("SCAN_FETCH", "SCAN_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="rocprofv3 --pmc output dirs (csv); writes the traffic record under profiles/")
     args = ap.parse_args()
@@ -234,7 +243,15 @@ def main():
     Cv = xbc[..., w.d_inner + N:].unsqueeze(2)
     ws_bytes = mm.ssd_forward_workspace_size(b, l, H, P, N, 1, H, w.chunk, w.dtype)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    wsf_bytes = mm.ssd_forward_fused_workspace_size(b, l, H, P, N, 1, H, w.chunk, w.dtype)
+    wsf = torch.empty(max(wsf_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+
+    def fused(heads):
+        # dt is the workload's step size as given (after softplus), so no
+        # bias and no softplus here
+        mm.ssd_forward_fused(xbc_raw, conv_w, dt, A, D, d_head=P, d_state=N,
+                             n_heads_active=heads, chunk=w.chunk, y=y, workspace=wsf)
 
     def scan(heads):
         mm.ssd_forward(xv, dt, A, Bv, Cv, D, n_heads_active=heads, chunk=w.chunk, y=y,
@@ -251,6 +268,12 @@ def main():
         torch.cuda.synchronize()
         print(f"# scan-only: {args.warmup + args.steps} launches", file=sys.stderr)
         return
+    if args.mode == "fused":  # counter runs: the full-width fused call alone
+        for _ in range(args.warmup + args.steps):
+            fused(H)
+        torch.cuda.synchronize()
+        print(f"# fused-only: {args.warmup + args.steps} launches", file=sys.stderr)
+        return
     if args.mode == "copy":  # counter calibration: a plain copy of known size
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -261,32 +284,48 @@ def main():
         print(f"# copy: {args.warmup + args.steps} x {COPY_BYTES} bytes", file=sys.stderr)
         return
 
-    # ---- the step: conv + scan at full width --------------------------------
-    for _ in range(args.warmup):
+    def timed_steps(step, inner=None):
+        """W warmup steps, then K steps back to back between two events;
+        with ``inner``, HIP events also bracket that part of each step."""
+        for _ in range(args.warmup):
+            step(inner)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(args.steps):
+            step(ev[i])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        part = [a.elapsed_time(z) for a, z in ev]
+        return t0.elapsed_time(t1) / args.steps, sum(part) / len(part)
+
+    def fused_step(evs):
+        if evs:
+            evs[0].record(stream)
+        fused(H)
+        if evs:
+            evs[1].record(stream)
+
+    def two_call_step(evs):
         conv(H)
+        if evs:
+            evs[0].record(stream)
         scan(H)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        conv(H)
-        ev[i][0].record(stream)
-        scan(H)
-        ev[i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    scan_ms = sorted(a.elapsed_time(z) for a, z in ev)
-    scan_avg_ms = sum(scan_ms) / len(scan_ms)
+        if evs:
+            evs[1].record(stream)
+
+    # ---- the step: the fused call at full width --------------------------------
+    ms_step, fused_avg_ms = timed_steps(fused_step)
     value = tokens / (ms_step * 1e-3)
+    # ---- the same step as two calls (conv into a buffer, then the scan) --------
+    ms_two, scan_avg_ms = timed_steps(two_call_step)
 
     alg = scan_bytes(tokens, H, P, N, elem)
-    achieved = alg / (scan_avg_ms * 1e-3) / 1e9
+    achieved = alg / (fused_avg_ms * 1e-3) / 1e9
     traffic = load_traffic()
 
     out = {
@@ -302,15 +341,18 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) xBC stream, log-uniform dt in [1e-3, 1e-1]; no dataset)",
-        "config": {"workload": "1.4B-scale MatMamba block prefill: conv1d(k=4)+SiLU then chunked "
-                               "selective scan, b=4 l=8192 d_model=2048 d_inner=4096 64 heads x 64, "
-                               "d_state=128, chunk=256 (evaluated as two 128-token tiles), "
-                               "slice m=2048 (64 heads)",
+        "config": {"workload": "1.4B-scale MatMamba block prefill: conv1d(k=4)+SiLU and chunked "
+                               "selective scan in one fused call, b=4 l=8192 d_model=2048 "
+                               "d_inner=4096 64 heads x 64, d_state=128, chunk=256 (evaluated as "
+                               "two 128-token tiles), slice m=2048 (64 heads)",
                    "global_batch": b, "seq_len": l, "parallelism": "single GPU"},
-        "roofline": {"kernel": "scan call (tile_prep_kernel + ssd_bf16_kernel)", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "roofline": {"kernel": "fused prefill call (tile_prep_kernel + ssd_bf16_kernel, conv fused)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "alg_bytes_per_launch": alg, "avg_launch_ms": scan_avg_ms},
+                     "alg_bytes_per_launch": alg, "avg_launch_ms": fused_avg_ms},
+        "unfused": {"ms_per_step": ms_two, "tokens_per_s": tokens / (ms_two * 1e-3),
+                    "scan_ms": scan_avg_ms,
+                    "scan_hbm_frac": alg / (scan_avg_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)},
     }
 
     # ---- every Matryoshka width, scan only -----------------------------------
@@ -318,11 +360,14 @@ def main():
     if not (args.no_slices and args.no_configs):
         flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     if not args.no_slices:
-        slices = {}
+        slices, scan_slices = {}, {}
+        conv(H)
         for m in w.slices:
             h = w.heads(m)
             slices[str(m)] = scan_entry(tokens, h, P, N, w.chunk,
-                                        timed_calls(torch, lambda: scan(h), flush))
+                                        timed_calls(torch, lambda: fused(h), flush))
+            scan_slices[str(m)] = scan_entry(tokens, h, P, N, w.chunk,
+                                             timed_calls(torch, lambda: scan(h), flush))
         # conv alone at full width, and a plain device copy of the same bytes
         # (the practical ceiling for that read + write traffic)
         tcv = timed_calls(torch, lambda: conv(H), flush)
@@ -332,6 +377,7 @@ def main():
         tc, tcopy = tcv["median"], tcp["median"]
         cb = conv_bytes(tokens, w.conv_dim, elem)
         out["slices"] = slices
+        out["scan_slices"] = scan_slices
         out["conv"] = {"ms": tc, "ms_p10": tcv["p10"], "ms_p90": tcv["p90"],
                        "tokens_per_s": tokens / (tc * 1e-3), "gb_per_s": cb / (tc * 1e-3) / 1e9,
                        "hbm_frac": cb / (tc * 1e-3) / (HBM_PEAK_GBS * 1e9),
@@ -339,7 +385,7 @@ def main():
 
     # ---- the other bf16 workloads, scan only, every slice ----------------------
     if not args.no_configs:
-        del xbc_raw, xbc, xv, Bv, Cv, y, ws
+        del xbc_raw, xbc, xv, Bv, Cv, y, ws, wsf
         torch.cuda.empty_cache()
         out["configs"] = bench_configs(torch, mm, synth, dev, flush)
 

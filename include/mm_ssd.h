@@ -194,6 +194,58 @@ int mm_ssd_forward(const void* x, int64_t x_row_stride,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace mm_ssd_forward_fused needs for these sizes (may
+ * be 0).  Same argument meaning and errors as mm_ssd_forward_fused.  Host only.
+ */
+int mm_ssd_forward_fused_workspace_size(int64_t batch, int64_t seqlen,
+                                        int64_t n_heads, int64_t d_head,
+                                        int64_t d_state, int64_t ngroups,
+                                        int64_t n_heads_active, int64_t chunk,
+                                        int dtype, size_t* bytes_out);
+
+/*
+ * The prefill path of the block in one call ("MatMamba", block paragraph:
+ * the conv over the concatenated x, B and C streams feeds the chunk +
+ * selective scan; W_dt is one of the input projections): exactly
+ *     u = mm_conv1d_silu(xbc, conv_w, conv_bias, conv_state)   (active channels)
+ *     dt' = softplus(dt + dt_bias) if dt_softplus else dt + dt_bias
+ *     y = mm_ssd_forward(x = u[:, 0:d_inner], dt', A, B = u[:, d_inner:d_inner+N],
+ *                        C = u[:, d_inner+N:], D, initial_state, final_state)
+ * with the conv output and dt' rounded to the storage dtype as if stored, but
+ * without writing them: for MM_BF16 storage, d_head 64, d_state 128 and chunk
+ * 128/256 the conv and the dt transform run inside the scan kernels, and only
+ * y (and the final state) reach memory; other shapes stage them in the
+ * workspace.  softplus(v) = log(1 + exp(v)).
+ *
+ *   xbc  (batch*seqlen rows, xbc_row_stride) dtype: the raw conv input, the
+ *        layout of mm_conv1d_silu's xbc_in with d_inner = n_heads*d_head; the
+ *        x slice of the first n_heads_active heads and all B, C channels are
+ *        read.  Must not overlap y.
+ *   conv_w (conv_dim, 4) fp32, 16-byte aligned; conv_bias (conv_dim) or NULL.
+ *   conv_state (batch, 3, conv_dim) fp32 or NULL: as in mm_conv1d_silu, read
+ *        as history, then overwritten with the last three raw inputs (active
+ *        channels) after every read of it.
+ *   dt   (rows, dt_row_stride) dtype: the raw per-head dt (before bias and
+ *        softplus); dt_bias (n_heads) fp32 or NULL (= 0); dt_softplus 0 or 1.
+ *   A, D, y, initial_state, final_state, chunk, workspace: as in
+ *        mm_ssd_forward (workspace sized by mm_ssd_forward_fused_workspace_size).
+ * Preconditions: those of mm_ssd_forward for the scan sizes, and
+ * xbc_row_stride >= conv_dim; dt_softplus not 0 or 1 gives MM_ERR_SHAPE.
+ */
+int mm_ssd_forward_fused(const void* xbc, int64_t xbc_row_stride,
+                         const float* conv_w, const float* conv_bias,
+                         float* conv_state,
+                         const void* dt, int64_t dt_row_stride,
+                         const float* dt_bias, int dt_softplus,
+                         const float* A, const float* D,
+                         void* y, int64_t y_row_stride,
+                         const float* initial_state, float* final_state,
+                         int64_t batch, int64_t seqlen, int64_t n_heads,
+                         int64_t d_head, int64_t d_state, int64_t ngroups,
+                         int64_t n_heads_active, int64_t chunk, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decode token for every sequence of the batch (Mamba page, Strengths:
  * linear-time recurrent inference), in place on `state`, for heads
  * [0, h_b) of sequence b (h_b as in mm_conv1d_silu):

@@ -75,6 +75,15 @@ def lib() -> ctypes.CDLL:
                                          _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                          _i64, _i64, _i64, _int, _vp, ctypes.c_size_t, _vp]
             L.mm_ssd_forward.restype = _int
+            L.mm_ssd_forward_fused_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64,
+                                                              _i64, _i64, _int,
+                                                              ctypes.POINTER(ctypes.c_size_t)]
+            L.mm_ssd_forward_fused_workspace_size.restype = _int
+            L.mm_ssd_forward_fused.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _int, _vp,
+                                               _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64,
+                                               _i64, _i64, _i64, _i64, _int, _vp, ctypes.c_size_t,
+                                               _vp]
+            L.mm_ssd_forward_fused.restype = _int
             L.mm_ssd_step.argtypes = [_vp, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64,
                                       _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                       _vp, _int, _vp]
@@ -232,6 +241,69 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
                               batch, seqlen, n_heads, d_head, d_state, ngroups, h_act, chunk,
                               code, _ptr(workspace), wbytes, _stream())
     _check("mm_ssd_forward", st)
+    return y
+
+
+def ssd_forward_fused_workspace_size(batch: int, seqlen: int, n_heads: int, d_head: int,
+                                     d_state: int, ngroups: int, n_heads_active: int, chunk: int,
+                                     dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    code = MM_F32 if dtype == torch.float32 else MM_BF16
+    _check("mm_ssd_forward_fused_workspace_size",
+           lib().mm_ssd_forward_fused_workspace_size(batch, seqlen, n_heads, d_head, d_state,
+                                                     ngroups, n_heads_active, chunk, code,
+                                                     ctypes.byref(out)))
+    return out.value
+
+
+def ssd_forward_fused(xbc: torch.Tensor, conv_w: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
+                      D: Optional[torch.Tensor] = None, *, d_head: int, d_state: int,
+                      ngroups: int = 1, conv_bias: Optional[torch.Tensor] = None,
+                      conv_state: Optional[torch.Tensor] = None,
+                      dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = False,
+                      n_heads_active: Optional[int] = None, chunk: int = 256,
+                      initial_state: Optional[torch.Tensor] = None,
+                      final_state: Optional[torch.Tensor] = None,
+                      y: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Conv1d (kernel 4) + SiLU, dt transform and chunked scan in one call, on
+    the raw conv input xbc (batch, seqlen, conv_dim) with conv_dim =
+    n_heads*d_head + 2*ngroups*d_state; dt (batch, seqlen, n_heads) is the raw
+    dt (dt_bias added, then softplus if dt_softplus).  conv_state
+    (batch, 3, conv_dim) fp32, if given, is read and rolled in place.  Returns
+    y as ssd_forward does."""
+    batch, seqlen, n_heads = dt.shape
+    conv_dim = n_heads * d_head + 2 * ngroups * d_state
+    h_act = n_heads if n_heads_active is None else int(n_heads_active)
+    if y is None:
+        y = torch.empty((batch, seqlen, h_act, d_head), dtype=xbc.dtype, device=xbc.device)
+    code = _dtype_code(xbc)
+    for name, t in (("dt", dt), ("y", y)):
+        if t.dtype != xbc.dtype:
+            raise TypeError(f"{name} must have xbc's dtype")
+    xs = _row_stride(xbc, "xbc", (conv_dim,))
+    ys = _row_stride(y, "y", (y.shape[2], d_head))
+    dts = _row_stride(dt, "dt", (n_heads,))
+    if conv_w.dtype != torch.float32 or not conv_w.is_contiguous() or conv_w.numel() != conv_dim * 4:
+        raise ValueError("conv_w must be a contiguous fp32 (conv_dim, 4) tensor")
+    if conv_state is not None and (conv_state.dtype != torch.float32 or not conv_state.is_contiguous()
+                                   or tuple(conv_state.shape) != (batch, 3, conv_dim)):
+        raise ValueError("conv_state must be a contiguous fp32 (batch, 3, conv_dim) tensor")
+    for name, t in (("A", A), ("D", D), ("conv_bias", conv_bias), ("dt_bias", dt_bias),
+                    ("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 tensor")
+    need = ssd_forward_fused_workspace_size(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                            h_act, chunk, xbc.dtype)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=xbc.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().mm_ssd_forward_fused(_ptr(xbc), xs, _ptr(conv_w), _ptr(conv_bias), _ptr(conv_state),
+                                    _ptr(dt), dts, _ptr(dt_bias), int(bool(dt_softplus)), _ptr(A),
+                                    _ptr(D), _ptr(y), ys, _ptr(initial_state), _ptr(final_state),
+                                    batch, seqlen, n_heads, d_head, d_state, ngroups, h_act, chunk,
+                                    code, _ptr(workspace), wbytes, _stream())
+    _check("mm_ssd_forward_fused", st)
     return y
 
 

@@ -135,6 +135,63 @@ int mm_ssd_forward(const void* x, int64_t x_row_stride, const void* dt,
   return hip_status(launch_ssd_forward(a, dtype, workspace, as_stream(stream)));
 }
 
+int mm_ssd_forward_fused_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
+                                        int64_t d_head, int64_t d_state, int64_t ngroups,
+                                        int64_t n_heads_active, int64_t chunk, int dtype,
+                                        size_t* bytes_out) {
+  if (!bytes_out) return MM_ERR_NULL;
+  const int st = validate_ssd_shape(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                    n_heads_active, chunk, dtype);
+  if (st != MM_OK) return st;
+  *bytes_out = fused_workspace_bytes(batch, seqlen, n_heads, n_heads_active, d_head, d_state,
+                                     chunk, dtype);
+  return MM_OK;
+}
+
+int mm_ssd_forward_fused(const void* xbc, int64_t xbc_row_stride, const float* conv_w,
+                         const float* conv_bias, float* conv_state, const void* dt,
+                         int64_t dt_row_stride, const float* dt_bias, int dt_softplus,
+                         const float* A, const float* D, void* y, int64_t y_row_stride,
+                         const float* initial_state, float* final_state, int64_t batch,
+                         int64_t seqlen, int64_t n_heads, int64_t d_head, int64_t d_state,
+                         int64_t ngroups, int64_t n_heads_active, int64_t chunk, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate_ssd_forward_fused(xbc, xbc_row_stride, conv_w, conv_bias, conv_state, dt,
+                                      dt_row_stride, dt_bias, dt_softplus, A, y, y_row_stride,
+                                      initial_state, final_state, batch, seqlen, n_heads,
+                                      d_head, d_state, ngroups, n_heads_active, chunk, dtype);
+  if (st != MM_OK) return st;
+  const size_t need = fused_workspace_bytes(batch, seqlen, n_heads, n_heads_active, d_head,
+                                            d_state, chunk, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MM_ERR_WORKSPACE;
+  if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return MM_ERR_ALIGN;
+  FusedCall f;
+  f.xbc = xbc;
+  f.xbcs = xbc_row_stride;
+  f.conv_w = conv_w;
+  f.conv_bias = conv_bias;
+  f.conv_state = conv_state;
+  f.dt = dt;
+  f.dts = dt_row_stride;
+  f.dt_bias = dt_bias;
+  f.softplus = dt_softplus;
+  f.A = A;
+  f.D = D;
+  f.y = y;
+  f.ys = y_row_stride;
+  f.h0 = initial_state;
+  f.hT = final_state;
+  f.batch = batch;
+  f.seqlen = seqlen;
+  f.n_heads = (int)n_heads;
+  f.d_head = (int)d_head;
+  f.d_state = (int)d_state;
+  f.heads = (int)n_heads_active;
+  f.chunk = (int)chunk;
+  f.dtype = dtype;
+  return hip_status(launch_ssd_forward_fused(f, workspace, as_stream(stream)));
+}
+
 int mm_ssd_step(float* state, const void* x_t, int64_t x_row_stride, const void* dt_t,
                 int64_t dt_row_stride, const float* A, const void* B_t,
                 int64_t b_row_stride, const void* C_t, int64_t c_row_stride,

@@ -22,14 +22,6 @@ namespace {
 constexpr int kConvThreads = 64;
 constexpr int kTokensPerRun = 32;
 
-// SiLU(v) = v * sigmoid(v) = v / (1 + exp(-v)), with the hardware exp2 and
-// reciprocal (about 1 ulp each): an IEEE division here made the kernel
-// VALU-bound below the HBM rate.  Large |v| saturates correctly (exp2 -> inf,
-// rcp(inf) -> 0).
-__device__ __forceinline__ float silu(float v) {
-  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
-}
-
 template <typename T>
 __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
     const T* __restrict__ in, int64_t in_stride, T* __restrict__ out,

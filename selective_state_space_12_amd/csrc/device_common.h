@@ -14,6 +14,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e), converts exp(v) to exp2(v*log2e)
 
+// SiLU(v) = v * sigmoid(v) = v / (1 + exp(-v)), with the hardware exp2 and
+// reciprocal (about 1 ulp each): an IEEE division made the conv kernel
+// VALU-bound below the HBM rate.  Large |v| saturates correctly (exp2 -> inf,
+// rcp(inf) -> 0).  Every kernel that applies the conv uses this one form, so
+// a fused conv rounds exactly as the standalone one.
+__device__ __forceinline__ float silu(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
+}
+
+// softplus(v) = log(1 + exp(v)); above 20 it equals v in fp32.
+__device__ __forceinline__ float softplus(float v) { return v > 20.0f ? v : log1pf(expf(v)); }
+
 // ---- scalar conversions -------------------------------------------------
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }

@@ -81,6 +81,18 @@ size_t fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
 int fwd_segments(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
                  int64_t d_state, int64_t chunk, int dtype);
 
+// Conv and dt parameters of a fused scan call (raw conv input in, the conv
+// and the dt transform applied on the way into the scan).
+struct FuseArgs {
+  const float* w = nullptr;        // (conv_dim, 4) conv weights, tap 3 = current token
+  const float* bias = nullptr;     // (conv_dim) or NULL
+  float* state = nullptr;          // (batch, 3, conv_dim) conv history or NULL (zeros)
+  const float* dt_bias = nullptr;  // (n_heads) or NULL
+  int64_t conv_dim = 0;
+  int d_inner = 0;
+  int softplus = 0;                // dt = softplus(dt + dt_bias) if set, else dt + dt_bias
+};
+
 // bf16, d_head 64, d_state 128, chunk 128 or 256 (ssd_fwd_bf16.hip).
 bool bf16_path(int64_t d_head, int64_t d_state, int64_t chunk, int dtype);
 size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads);
@@ -91,7 +103,37 @@ size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads);
 void fwd_plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int* ntiles, int* nseg,
                    int* seg_tiles);
 hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* workspace, hipStream_t s);
+// The same with the conv and dt transform fused in: a.x, a.B, a.C are the raw
+// conv input's x, B and C columns and a.dt the raw dt.  The conv state, if
+// any, is read, not updated (the caller rolls it afterwards).
+hipError_t launch_ssd_forward_bf16_fused(const FwdArgs& a, const FuseArgs& fu, void* workspace,
+                                         hipStream_t s);
 
 hipError_t launch_ssd_forward(const FwdArgs& a, int dtype, void* workspace, hipStream_t s);
+
+// A fused prefill call (fused.hip): raw [x | B | C] conv input rows in, the
+// conv + SiLU and the dt transform applied on the way into the scan.
+struct FusedCall {
+  const void* xbc;
+  int64_t xbcs;
+  const float* conv_w;
+  const float* conv_bias;
+  float* conv_state;
+  const void* dt;
+  int64_t dts;
+  const float* dt_bias;
+  int softplus;
+  const float* A;
+  const float* D;
+  void* y;
+  int64_t ys;
+  const float* h0;
+  float* hT;
+  int64_t batch, seqlen;
+  int n_heads, d_head, d_state, heads, chunk, dtype;
+};
+size_t fused_workspace_bytes(int64_t batch, int64_t seqlen, int64_t n_heads, int64_t heads,
+                             int64_t d_head, int64_t d_state, int64_t chunk, int dtype);
+hipError_t launch_ssd_forward_fused(const FusedCall& f, void* workspace, hipStream_t s);
 
 }  // namespace mmssd

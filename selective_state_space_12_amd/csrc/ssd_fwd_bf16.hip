@@ -84,7 +84,10 @@ constexpr int kXE = kQ * kP;   // elements of one x tile (16 fragments)
 // factor (off-diagonal blocks and the state update).
 constexpr int kXBuf = 2 * kXE;
 constexpr int kHF = kP * kN;   // elements of the operand copy of H (16 fragments)
-constexpr int kStg = kQ * kP;  // raw token-major rows, 32 per staging wave
+// Raw token-major rows per staging wave: 4 rows before its 32 tokens (the
+// conv window of a fused call) and the 32 rows themselves.
+constexpr int kStgRows = 4 + 32;
+constexpr int kStg = 4 * kStgRows * kP;
 constexpr size_t kDec = 3 * kQ;  // floats: Lambda, dt, block-end factor
 constexpr size_t kLds = (size_t)(2 * kXBuf + 2 * kHF + kStg) * sizeof(bf16) + 3 * kDec * sizeof(float);
 
@@ -112,27 +115,29 @@ __device__ __forceinline__ int chan(int pb, int m) {
   return (pb >> 1) * 32 + (m >> 2) * 8 + (pb & 1) * 4 + (m & 3);
 }
 
-// Raw rows staged by a staging wave: row s (token) holds the head's 64
-// channels in natural order, 8 chunks of 16 bytes per 128-byte row, chunk
-// index XOR-ed with s%8.  Element offset of (s, chunk):
+// Raw rows staged by a staging wave: row s holds the head's 64 channels of
+// one token in natural order (token s - 4 of the wave's 32), 8 chunks of 16
+// bytes per 128-byte row, chunk index XOR-ed with s%8.  Element offset of
+// (s, chunk):
 __device__ __forceinline__ int soff(int s, int chunk) { return s * kP + ((chunk ^ (s & 7)) << 3); }
 
-// Operand fragment of 8 consecutive staged tokens sb..sb+7 for the channels
-// chan(pb, r), read with two LDS transpose loads: within each 16-lane group,
-// lane i receives element i%4 of the 8 bytes that lane 4k + i/4 addresses,
-// for k = 0..3.  Lane src therefore addresses token sb + src/4 (+4 for the
-// second load) at the four channels chan(pb, 4*(src%4)) .. +3, which are
-// consecutive: (pb/2)*32 + (src%4)*8 + (pb%2)*4.
+// Four consecutive staged rows sb..sb+3 for the channel chan(pb, r), read
+// with one LDS transpose load: within each 16-lane group, lane i receives
+// element i%4 of the 8 bytes that lane 4k + i/4 addresses, for k = 0..3.
+// Lane src therefore addresses row sb + src/4 at the four channels
+// chan(pb, 4*(src%4)) .. +3, which are consecutive:
+// (pb/2)*32 + (src%4)*8 + (pb%2)*4.
 typedef short short4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ Frag8<bf16> stg_frag(const bf16* S, int sb, int pb, int lane) {
+__device__ __forceinline__ short4v stg_rows4(const bf16* S, int sb, int pb, int lane) {
   const int src = lane & 15;
   const int chunk = (pb >> 1) * 4 + (src & 3), half = (pb & 1) * 4;
-  const int s1 = sb + (src >> 2);
   typedef __attribute__((address_space(3))) short4v lds_short4;
-  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_short4*)(const_cast<bf16*>(S) + soff(s1, chunk) + half));
-  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_short4*)(const_cast<bf16*>(S) + soff(s1 + 4, chunk) + half));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4*)(const_cast<bf16*>(S) + soff(sb + (src >> 2), chunk) + half));
+}
+// Operand fragment of the 8 staged rows sb..sb+7 (two transpose loads).
+__device__ __forceinline__ Frag8<bf16> stg_frag(const bf16* S, int sb, int pb, int lane) {
+  const short4v lo = stg_rows4(S, sb, pb, lane), hi = stg_rows4(S, sb + 4, pb, lane);
   Frag8<bf16> f;
   f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   return f;
@@ -169,22 +174,31 @@ __device__ __forceinline__ float dpp_f(float v) {
 // scan multiplies by dt = 0 or never stores).  One workgroup per tile stages
 // the B and C rows in LDS with whole-row loads and forms every fragment from
 // there.
+//
+// Fused calls (raw conv input, FUSED): the workgroup also stages the three
+// rows before the tile and applies the causal conv (kernel 4) + SiLU to the
+// B and C channels in LDS, in the same fp32 operation order and rounding as
+// the conv kernel, and turns raw dt into dt = softplus(dt + dt_bias) (or
+// dt + dt_bias), rounded to bf16 as a stored dt would be.
 constexpr int kBCP = kN + 8;  // LDS row pitch (elements) of the staged B and C rows
+constexpr int kBCRows = kQ + 3;  // the tile's rows and, for a fused call, three before it
 // B and C rows; the dt transpose buffer reuses the C rows once the G and C
-// fragments are out (68 KB: two workgroups per CU)
-constexpr size_t kPrepLds = 2 * (size_t)kQ * kBCP * sizeof(bf16);
+// fragments are out (71 KB: two workgroups per CU)
+constexpr size_t kPrepLds = 2 * (size_t)kBCRows * kBCP * sizeof(bf16);
 static_assert(64 * (kQ + 2) <= kQ * kBCP, "dt buffer fits in the C rows");
 
-__global__ __launch_bounds__(512) void tile_prep_kernel(const bf16* __restrict__ Bp, int64_t bs,
+// (at most 128 VGPRs: two workgroups per CU)
+template <bool FUSED>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void tile_prep_kernel(const bf16* __restrict__ Bp, int64_t bs,
                                                         const bf16* __restrict__ Cp, int64_t cs,
                                                         const bf16* __restrict__ dtp, int64_t dts,
                                                         uint4* __restrict__ frags,
                                                         bf16* __restrict__ dtT, int64_t seqlen,
-                                                        int ntiles, int heads) {
+                                                        int ntiles, int heads, FuseArgs cv) {
   extern __shared__ __align__(16) unsigned char psm[];
   bf16 (*Bs)[kBCP] = reinterpret_cast<bf16 (*)[kBCP]>(psm);
-  bf16 (*Cs)[kBCP] = reinterpret_cast<bf16 (*)[kBCP]>(psm + (size_t)kQ * kBCP * sizeof(bf16));
-  bf16 (*Dt)[kQ + 2] = reinterpret_cast<bf16 (*)[kQ + 2]>(psm + (size_t)kQ * kBCP * sizeof(bf16));
+  bf16 (*Cs)[kBCP] = reinterpret_cast<bf16 (*)[kBCP]>(psm + (size_t)kBCRows * kBCP * sizeof(bf16));
+  bf16 (*Dt)[kQ + 2] = reinterpret_cast<bf16 (*)[kQ + 2]>(psm + (size_t)kBCRows * kBCP * sizeof(bf16));
   const int c = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
   const int64_t row0 = (int64_t)b * seqlen + (int64_t)c * kQ;
@@ -195,23 +209,89 @@ __global__ __launch_bounds__(512) void tile_prep_kernel(const bf16* __restrict__
   const int hh = tid & 63;
   bf16 dv[kQ / 8];
   auto load_dt = [&](int h0, int nh) {
+    const int hd = h0 + min(hh, nh - 1);
 #pragma unroll
     for (int i = 0; i < kQ / 8; ++i) {
       const int s = (tid >> 6) + 8 * i;
-      dv[i] = dtp[(row0 + min(s, last)) * dts + h0 + min(hh, nh - 1)];
+      dv[i] = dtp[(row0 + min(s, last)) * dts + hd];
+    }
+    if (FUSED) {
+      const float db = cv.dt_bias ? cv.dt_bias[hd] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < kQ / 8; ++i) {
+        const float d = static_cast<float>(dv[i]) + db;
+        dv[i] = static_cast<bf16>(cv.softplus ? softplus(d) : d);
+      }
     }
   };
-  load_dt(0, min(64, heads));
-  for (int v = tid; v < kQ * (kN / 8); v += 512) {
-    const int s = v / (kN / 8), col = (v % (kN / 8)) * 8;
-    const int64_t r = row0 + min(s, last);
-    // B and C rows are read once here (nontemporal: prep 12.0 vs 13.7 us)
-    *reinterpret_cast<u32x4*>(&Bs[s][col]) =
-        __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Bp + r * bs + col));
-    *reinterpret_cast<u32x4*>(&Cs[s][col]) =
-        __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cp + r * cs + col));
+  if (!FUSED) load_dt(0, min(64, heads));  // in flight during the row loads
+  // Row sr of Bs/Cs holds token sr - kH of the tile (kH = 3 before the conv of
+  // a fused call, 0 otherwise); the rows before the sequence start are 0 (a
+  // given conv state enters the conv below in fp32).
+  constexpr int kH = FUSED ? 3 : 0;
+  for (int v = tid; v < (kQ + kH) * (kN / 8); v += 512) {
+    const int sr = v / (kN / 8), col = (v % (kN / 8)) * 8;
+    const int s = sr - kH;
+    u32x4 bq = {0u, 0u, 0u, 0u}, cq = {0u, 0u, 0u, 0u};
+    if (s >= 0 || c > 0) {
+      const int64_t r = row0 + (s >= 0 ? min(s, last) : s);
+      // B and C rows are read once here (nontemporal: prep 12.0 vs 13.7 us)
+      bq = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Bp + r * bs + col));
+      cq = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cp + r * cs + col));
+    }
+    *reinterpret_cast<u32x4*>(&Bs[sr][col]) = bq;
+    *reinterpret_cast<u32x4*>(&Cs[sr][col]) = cq;
   }
   __syncthreads();
+  if (FUSED) {
+    // Thread: matrix m (B, C), 8 channels (group cg), 8 tokens (run).  It
+    // takes its three history rows into registers, then (after a barrier, as
+    // the previous run's thread overwrites them) turns each of its 8 raw rows
+    // into the conv output in place: row sr = token sr - 3.
+    const int m = tid >> 8, run = (tid >> 4) & 15, cg = tid & 15;
+    bf16 (*S)[kBCP] = m ? Cs : Bs;
+    const int64_t ch = cv.d_inner + m * kN + cg * 8;
+    float wk[4][8], bv[8], hs[3][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 wj = *reinterpret_cast<const float4*>(cv.w + (ch + j) * 4);
+      wk[0][j] = wj.x; wk[1][j] = wj.y; wk[2][j] = wj.z; wk[3][j] = wj.w;
+      bv[j] = cv.bias ? cv.bias[ch + j] : 0.0f;
+    }
+    const bool from_state = c == 0 && run == 0 && cv.state;
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        hs[k][j] = from_state ? cv.state[((int64_t)b * 3 + k) * cv.conv_dim + ch + j]
+                              : static_cast<float>(S[run * 8 + k][cg * 8 + j]);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bf16x8* row = reinterpret_cast<bf16x8*>(&S[run * 8 + 3 + i][cg * 8]);
+      const bf16x8 u = *row;
+      bf16x8 ov;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float ut = static_cast<float>(u[j]);
+        float pre = bv[j];
+        pre = fmaf(wk[0][j], hs[0][j], pre);
+        pre = fmaf(wk[1][j], hs[1][j], pre);
+        pre = fmaf(wk[2][j], hs[2][j], pre);
+        pre = fmaf(wk[3][j], ut, pre);
+        ov[j] = static_cast<bf16>(silu(pre));
+        hs[0][j] = hs[1][j];
+        hs[1][j] = hs[2][j];
+        hs[2][j] = ut;
+      }
+      *row = ov;
+    }
+    __syncthreads();
+  }
+  // token s of the tile at row s from here on
+  Bs += kH;
+  Cs += kH;
+  if (FUSED) load_dt(0, min(64, heads));  // (after the conv: registers)
 
   // G^T tiles: A operand row m takes B row k*32 + (m/4)*8 + m%4 (tile a) or
   // that + 4 (tile b), B operand column n is C row tb*16 + n, so output slot
@@ -287,6 +367,12 @@ struct BK {
   const bf16* dtT;
   float* seg_state;
   float* seg_decay;
+  // fused calls: x is the raw conv input of the x channels; the staging
+  // waves apply the conv (weights cw, bias cbias, history cstate)
+  const float* cw;
+  const float* cbias;
+  const float* cstate;
+  int64_t conv_dim;
   int64_t seqlen;
   int n_heads, heads, nseg, seg_chunks, ntiles;
 };
@@ -518,14 +604,18 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
 // into the x fragments (v, pb) of both LDS x tiles (plain and times the
 // block-end factor): its raw rows go to its own staging rows (layout at soff)
 // and come back transposed, as operand fragments, from LDS transpose loads.
+// In a fused call the wave also stages the 4 rows before its tokens and
+// applies the causal conv (kernel 4) + SiLU to the transposed fragments, where
+// each lane holds 8 consecutive tokens of one channel: the same fp32
+// operation order and rounding as the conv kernel.
 // All four also form the decay cumsum two tiles ahead (a few DPP steps) and
 // waves 12, 13, 14 write its three arrays.
-template <bool OUT>
+template <bool OUT, bool FUSED>
 __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int seg, int c0,
                             int c1, int v) {
   const int lane = threadIdx.x & 63;
   bf16* xbuf = reinterpret_cast<bf16*>(smem);
-  bf16* stg = xbuf + 2 * kXBuf + 2 * kHF + v * 32 * kP;  // this wave's 32 raw rows
+  bf16* stg = xbuf + 2 * kXBuf + 2 * kHF + v * kStgRows * kP;  // this wave's staged rows
   float* dbuf = reinterpret_cast<float*>(xbuf + 2 * kXBuf + 2 * kHF + kStg);
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Ah2 = k.A[h] * kLog2e;
@@ -535,7 +625,9 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
   // once: nontemporal loads (measured 6% faster on the whole kernel).
   // (four named registers, not an array: the array was placed in scratch)
   const int pc = lane & 7;
-  uint4 xr0, xr1, xr2, xr3;
+  // rows r0..r3 (tokens 32v + 8i + lane/8) and, fused, the halo row
+  struct XSet { uint4 r0, r1, r2, r3, h; };
+  XSet xs;
   auto load_x = [&](int c) {
     const int64_t r0 = rowb + (int64_t)c * kQ;
     const int last = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ) - 1;
@@ -544,25 +636,84 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
       return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
                                            k.x + (r0 + s) * k.xs + (int64_t)h * kP + pc * 8)));
     };
-    xr0 = row(0);
-    xr1 = row(1);
-    xr2 = row(2);
-    xr3 = row(3);
+    xs.r0 = row(0);
+    xs.r1 = row(1);
+    xs.r2 = row(2);
+    xs.r3 = row(3);
+    if (FUSED) {
+      // the 4 tokens before the wave's first (lanes 32-63 repeat lanes 0-31);
+      // before the sequence start: 0 (a conv state enters in fp32 below)
+      const int s = v * 32 - 4 + ((lane >> 3) & 3);
+      xs.h = make_uint4(0u, 0u, 0u, 0u);
+      if (s >= 0 || c > 0)
+        xs.h = *reinterpret_cast<const uint4*>(k.x + (r0 + (s >= 0 ? min(s, last) : s)) * k.xs +
+                                               (int64_t)h * kP + pc * 8);
+    }
   };
+  // conv weights and bias of the lane's channels h*64 + chan(pb, r)
+  f32x4 cwk[kPB];
+  float cbv[kPB];
+  if (FUSED) {
+#pragma unroll
+    for (int pb = 0; pb < kPB; ++pb) {
+      const int64_t ch = (int64_t)h * kP + chan(pb, lane & 15);
+      cwk[pb] = *reinterpret_cast<const f32x4*>(k.cw + ch * 4);
+      cbv[pb] = k.cbias ? k.cbias[ch] : 0.0f;
+    }
+  }
   // Raw rows out, fragments back (LDS operations of one wave complete in
   // order, so the transpose loads see the rows just written), then the plain
   // fragments and the ones scaled by exp2(lam[e] - lam_s) dt_s, e the end of
   // the token's 32-token block (lane (r, g) holds tokens 32v + g*8 + j).
-  auto commit = [&](int xb, int db) {
-    bf16* XT = xbuf + xb * kXBuf;
-    const float* d = dbuf + db * kDec;
-    *reinterpret_cast<uint4*>(stg + soff(0 + (lane >> 3), pc)) = xr0;
-    *reinterpret_cast<uint4*>(stg + soff(8 + (lane >> 3), pc)) = xr1;
-    *reinterpret_cast<uint4*>(stg + soff(16 + (lane >> 3), pc)) = xr2;
-    *reinterpret_cast<uint4*>(stg + soff(24 + (lane >> 3), pc)) = xr3;
+  auto commit = [&](int c) {
+    bf16* XT = xbuf + (c & 1) * kXBuf;
+    const float* d = dbuf + (c % 3) * kDec;
+    *reinterpret_cast<uint4*>(stg + soff(4 + (lane >> 3), pc)) = xs.r0;
+    *reinterpret_cast<uint4*>(stg + soff(12 + (lane >> 3), pc)) = xs.r1;
+    *reinterpret_cast<uint4*>(stg + soff(20 + (lane >> 3), pc)) = xs.r2;
+    *reinterpret_cast<uint4*>(stg + soff(28 + (lane >> 3), pc)) = xs.r3;
+    if (FUSED && lane < 32) *reinterpret_cast<uint4*>(stg + soff(lane >> 3, pc)) = xs.h;
     Frag8<bf16> f[kPB];
 #pragma unroll
-    for (int pb = 0; pb < kPB; ++pb) f[pb] = stg_frag(stg, (lane >> 4) * 8, pb, lane);
+    for (int pb = 0; pb < kPB; ++pb) f[pb] = stg_frag(stg, 4 + (lane >> 4) * 8, pb, lane);
+    if (FUSED) {
+      // lanes holding a sequence's first tokens take the history from the
+      // conv state in fp32 (loaded here: once per sequence)
+      const bool first = c == 0 && v == 0 && (lane >> 4) == 0 && k.cstate;
+      const float* hist = first ? k.cstate + (int64_t)b * 3 * k.conv_dim + (int64_t)h * kP : nullptr;
+#pragma unroll
+      for (int pb = 0; pb < kPB; ++pb) {
+        // tokens -4..-1 as bf16 pairs: a bf16 is the high half of its fp32,
+        // so the three taps are word 0's high half and word 1's two halves
+        // (element extraction through a bf16 bit_cast of the short vector
+        // was lowered to element 0 for all three)
+        const uint2 hw = __builtin_bit_cast(uint2, stg_rows4(stg, (lane >> 4) * 8, pb, lane));
+        float h0 = __builtin_bit_cast(float, hw.x & 0xffff0000u);
+        float h1 = __builtin_bit_cast(float, hw.y << 16);
+        float h2 = __builtin_bit_cast(float, hw.y & 0xffff0000u);
+        const int ch = chan(pb, lane & 15);
+        if (first) {
+          h0 = hist[ch];
+          h1 = hist[k.conv_dim + ch];
+          h2 = hist[2 * k.conv_dim + ch];
+        }
+        const f32x4 wk = cwk[pb];
+        const float bias = cbv[pb];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float ut = static_cast<float>(f[pb].v[j]);
+          float pre = bias;
+          pre = fmaf(wk[0], h0, pre);
+          pre = fmaf(wk[1], h1, pre);
+          pre = fmaf(wk[2], h2, pre);
+          pre = fmaf(wk[3], ut, pre);
+          f[pb].v[j] = static_cast<bf16>(silu(pre));
+          h0 = h1;
+          h1 = h2;
+          h2 = ut;
+        }
+      }
+    }
     const float* ef = d + 2 * kQ + v * 32 + (lane >> 4) * 8;
     const f32x4 e0 = *reinterpret_cast<const f32x4*>(ef);
     const f32x4 e1 = *reinterpret_cast<const f32x4*>(ef + 4);
@@ -627,13 +778,13 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
   lam_seg += make_dec(c0, c0 % 3, dt0);
   if (c0 + 1 < c1) lam_seg += make_dec(c0 + 1, (c0 + 1) % 3, dt1);
   __syncthreads();
-  commit(c0 & 1, c0 % 3);
+  commit(c0);
   load_x(min(c0 + 1, cl));
   dtr_raw = load_dt(min(c0 + 2, cl));
   __syncthreads();
 
   for (int c = c0; c < c1; ++c) {
-    if (c + 1 < c1) commit((c + 1) & 1, (c + 1) % 3);
+    if (c + 1 < c1) commit(c + 1);
     load_x(min(c + 2, cl));
     if (c + 2 < c1) lam_seg += make_dec(c + 2, (c + 2) % 3, dtr_raw);
     dtr_raw = load_dt(min(c + 3, cl));
@@ -643,7 +794,7 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
     k.seg_decay[((int64_t)b * k.heads + h) * k.nseg + seg] = lam_seg;
 }
 
-template <bool OUT>
+template <bool OUT, bool FUSED>
 __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(BK k) {
   extern __shared__ __align__(16) unsigned char smem[];
   // XCD-aware unit mapping: consecutive workgroups go to different XCDs, so
@@ -661,7 +812,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(BK k) {
   // wave index as a scalar, so the role branch below is uniform per wave
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave >= 12) {
-    stage_waves<OUT>(k, smem, b, h, seg, c0, c1, wave - 12);
+    stage_waves<OUT, FUSED>(k, smem, b, h, seg, c0, c1, wave - 12);
   } else if (wave >= 8) {
     state_waves<OUT>(k, smem, b, h, seg, c0, c1, wave - 8);
   } else if (OUT) {
@@ -767,7 +918,7 @@ size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads) {
   return bytes;
 }
 
-// hipFuncSetAttribute for the three kernels that need more than 64 KB of LDS,
+// hipFuncSetAttribute for the kernels that need more than 64 KB of LDS,
 // once per device (bit d of the mask).
 hipError_t set_lds_attributes() {
   static std::atomic<unsigned long long> done{0};
@@ -777,9 +928,12 @@ hipError_t set_lds_attributes() {
   const unsigned long long bit = dev < 64 ? 1ull << dev : 0ull;
   if (bit && (done.load() & bit)) return hipSuccess;
   const std::pair<const void*, size_t> attrs[] = {
-      {reinterpret_cast<const void*>(tile_prep_kernel), kPrepLds},
-      {reinterpret_cast<const void*>(ssd_bf16_kernel<false>), kLds},
-      {reinterpret_cast<const void*>(ssd_bf16_kernel<true>), kLds}};
+      {reinterpret_cast<const void*>(tile_prep_kernel<false>), kPrepLds},
+      {reinterpret_cast<const void*>(tile_prep_kernel<true>), kPrepLds},
+      {reinterpret_cast<const void*>(ssd_bf16_kernel<false, false>), kLds},
+      {reinterpret_cast<const void*>(ssd_bf16_kernel<true, false>), kLds},
+      {reinterpret_cast<const void*>(ssd_bf16_kernel<false, true>), kLds},
+      {reinterpret_cast<const void*>(ssd_bf16_kernel<true, true>), kLds}};
   for (const auto& fa : attrs) {
     e = hipFuncSetAttribute(fa.first, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fa.second);
     if (e != hipSuccess) return e;
@@ -788,7 +942,8 @@ hipError_t set_lds_attributes() {
   return hipSuccess;
 }
 
-hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
+template <bool FUSED>
+hipError_t launch_bf16(const FwdArgs& a, const FuseArgs& fu, void* ws, hipStream_t s) {
   BK k;
   k.x = static_cast<const bf16*>(a.x); k.xs = a.xs;
   k.dt = static_cast<const bf16*>(a.dt); k.dts = a.dts;
@@ -797,6 +952,7 @@ hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
   k.D = a.D;
   k.y = static_cast<bf16*>(a.y); k.ys = a.ys;
   k.h0 = a.h0; k.hT = a.hT;
+  k.cw = fu.w; k.cbias = fu.bias; k.cstate = fu.state; k.conv_dim = fu.conv_dim;
   k.seqlen = a.seqlen; k.n_heads = a.n_heads; k.heads = a.heads;
   fwd_plan_bf16(a.batch, a.seqlen, a.heads, &k.ntiles, &k.nseg, &k.seg_chunks);
   unsigned char* wsb = static_cast<unsigned char*>(ws);
@@ -813,12 +969,12 @@ hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
   }
   hipError_t e = set_lds_attributes();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tile_prep_kernel, dim3(k.ntiles, (unsigned)a.batch), dim3(512), kPrepLds, s,
-                     static_cast<const bf16*>(a.B), a.bs, k.C, a.cs, k.dt, a.dts, frags, dtT,
-                     a.seqlen, k.ntiles, a.heads);
+  hipLaunchKernelGGL(tile_prep_kernel<FUSED>, dim3(k.ntiles, (unsigned)a.batch), dim3(512),
+                     kPrepLds, s, static_cast<const bf16*>(a.B), a.bs, k.C, a.cs, k.dt, a.dts,
+                     frags, dtT, a.seqlen, k.ntiles, a.heads, fu);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (k.nseg > 1) {
-    auto pre = ssd_bf16_kernel<false>;
+    auto pre = ssd_bf16_kernel<false, FUSED>;
     hipLaunchKernelGGL(pre, dim3(k.nseg - 1, a.heads, (unsigned)a.batch), dim3(kThreads), kLds, s, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     static_assert((kP * kN) % 256 == 0, "state elements split over 256-thread blocks");
@@ -826,9 +982,18 @@ hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
                        dim3(256), 0, s, k.seg_state, k.seg_decay, a.h0, a.n_heads, a.heads, k.nseg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  auto main_k = ssd_bf16_kernel<true>;
+  auto main_k = ssd_bf16_kernel<true, FUSED>;
   hipLaunchKernelGGL(main_k, dim3(k.nseg, a.heads, (unsigned)a.batch), dim3(kThreads), kLds, s, k);
   return hipGetLastError();
+}
+
+hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* ws, hipStream_t s) {
+  return launch_bf16<false>(a, FuseArgs{}, ws, s);
+}
+
+hipError_t launch_ssd_forward_bf16_fused(const FwdArgs& a, const FuseArgs& fu, void* ws,
+                                         hipStream_t s) {
+  return launch_bf16<true>(a, fu, ws, s);
 }
 
 }  // namespace mmssd

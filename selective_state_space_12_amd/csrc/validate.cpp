@@ -134,6 +134,44 @@ int validate_ssd_forward(const void* x, int64_t x_row_stride, const void* dt,
   return MM_OK;
 }
 
+int validate_ssd_forward_fused(const void* xbc, int64_t xbc_row_stride, const float* conv_w,
+                               const float* conv_bias, const float* conv_state, const void* dt,
+                               int64_t dt_row_stride, const float* dt_bias, int dt_softplus,
+                               const float* A, const void* y, int64_t y_row_stride,
+                               const float* initial_state, const float* final_state,
+                               int64_t batch, int64_t seqlen, int64_t n_heads, int64_t d_head,
+                               int64_t d_state, int64_t ngroups, int64_t n_heads_active,
+                               int64_t chunk, int dtype) {
+  if (!xbc || !conv_w || !dt || !A || !y) return MM_ERR_NULL;
+  int st = validate_ssd_shape(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                              n_heads_active, chunk, dtype);
+  if (st != MM_OK) return st;
+  if (dt_softplus != 0 && dt_softplus != 1) return MM_ERR_SHAPE;
+  const int64_t el = dtype_bytes(dtype);
+  const int64_t conv_dim = n_heads * d_head + 2 * ngroups * d_state;
+  const int64_t xw = n_heads_active * d_head;
+  if (xbc_row_stride < conv_dim || y_row_stride < xw || dt_row_stride < n_heads_active)
+    return MM_ERR_SHAPE;
+  const int64_t rows = batch * seqlen;
+  if (!mul_ok(rows, xbc_row_stride) || !mul_ok(rows, y_row_stride) ||
+      !mul_ok(rows, dt_row_stride))
+    return MM_ERR_SHAPE;
+  if (!rows_aligned(xbc, xbc_row_stride, el) || !rows_aligned(y, y_row_stride, el))
+    return MM_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(dt) % el != 0) return MM_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(conv_w) % 16 != 0) return MM_ERR_ALIGN;
+  const void* f32s[] = {conv_bias, conv_state, dt_bias, initial_state, final_state};
+  for (const void* p : f32s)
+    if (reinterpret_cast<uintptr_t>(p) % 4 != 0) return MM_ERR_ALIGN;
+  // y must not overlap the conv input (the scan reads its rows while storing y).
+  const uintptr_t i0 = reinterpret_cast<uintptr_t>(xbc);
+  const uintptr_t i1 = i0 + uintptr_t(((rows - 1) * xbc_row_stride + conv_dim) * el);
+  const uintptr_t o0 = reinterpret_cast<uintptr_t>(y);
+  const uintptr_t o1 = o0 + uintptr_t(((rows - 1) * y_row_stride + xw) * el);
+  if (i0 < o1 && o0 < i1) return MM_ERR_SHAPE;
+  return MM_OK;
+}
+
 int validate_ssd_step(const float* state, const void* x_t, int64_t x_row_stride,
                       const void* dt_t, int64_t dt_row_stride, const float* A,
                       const void* B_t, int64_t b_row_stride, const void* C_t,

@@ -48,6 +48,15 @@ int validate_ssd_forward(const void* x, int64_t x_row_stride, const void* dt,
                          int64_t ngroups, int64_t n_heads_active, int64_t chunk,
                          int dtype);
 
+int validate_ssd_forward_fused(const void* xbc, int64_t xbc_row_stride, const float* conv_w,
+                               const float* conv_bias, const float* conv_state, const void* dt,
+                               int64_t dt_row_stride, const float* dt_bias, int dt_softplus,
+                               const float* A, const void* y, int64_t y_row_stride,
+                               const float* initial_state, const float* final_state,
+                               int64_t batch, int64_t seqlen, int64_t n_heads, int64_t d_head,
+                               int64_t d_state, int64_t ngroups, int64_t n_heads_active,
+                               int64_t chunk, int dtype);
+
 int validate_ssd_step(const float* state, const void* x_t, int64_t x_row_stride,
                       const void* dt_t, int64_t dt_row_stride, const float* A,
                       const void* B_t, int64_t b_row_stride, const void* C_t,

@@ -22,7 +22,7 @@ from typing import Dict, List, Optional
 import torch
 
 # tensor indices inside a config's seed block
-_X, _B, _C, _DT, _A, _D, _CONVW, _XBC, _H0, _CS0, _DTSTEP, _XBCSTEP, _CONVB = range(13)
+_X, _B, _C, _DT, _A, _D, _CONVW, _XBC, _H0, _CS0, _DTSTEP, _XBCSTEP, _CONVB, _DTRAW, _DTB = range(15)
 
 
 @dataclass(frozen=True)
@@ -164,6 +164,21 @@ def pipeline_dt(w: Workload, batch: Optional[int] = None,
     b = batch or w.batch
     l = seqlen or w.seqlen
     return _dt((b, l, w.n_heads), w, _gen(w, _DT, salt + 1)).to(w.dtype)
+
+
+def raw_dt(w: Workload, batch: Optional[int] = None, seqlen: Optional[int] = None,
+           salt: int = 0) -> torch.Tensor:
+    """Raw dt (b, l, H) before bias and softplus, N(0,1) - 4 in the storage
+    dtype: through softplus with no bias it follows the softplus(N(0,1) - 4)
+    recipe of the workloads."""
+    b = batch or w.batch
+    l = seqlen or w.seqlen
+    return (_normal((b, l, w.n_heads), _gen(w, _DTRAW, salt)) - 4.0).to(w.dtype)
+
+
+def draw_dt_bias(w: Workload) -> torch.Tensor:
+    """(n_heads,) fp32, 0.5 * N(0, 1): exercises the optional dt bias."""
+    return _normal((w.n_heads,), _gen(w, _DTB), 0.5)
 
 
 def decode_pool(w: Workload, pool: int = 64, batch: Optional[int] = None,
