@@ -2,25 +2,23 @@
 
 One step = the prefill path of the 1.4B-scale block on one batch of seeded
 synthetic input resident in HBM: causal conv1d (kernel 4) + SiLU over the
-[x | B | C] stream (b=4, l=8192, 4352 channels, bf16), the dt of the
-workload, and the chunked selective scan (64 heads of 64, d_state 128, chunk
-256, full width m=2048), as one fused call (mm_ssd_forward_fused: the conv
-runs inside the scan kernels and its output never reaches HBM).  ``value`` is
-tokens/s of that step.
+[x | B | C] stream (b=4, l=8192, 4352 channels, bf16), then the chunked
+selective scan on strided views of the conv output (64 heads of 64, d_state
+128, chunk 256, full width m=2048).  ``value`` is tokens/s of that step.
 
 Also reported on the same JSON line:
-  - ``roofline``: the fused call's algorithmic HBM bytes (raw x, B, C, dt in;
-    y out) divided by its own duration (HIP events around each call inside
-    the timed steps, on the stream it runs on), against MI355X's 8 TB/s.  A
-    fused call is two kernels: tile_prep_kernel (per tile, shared by the
-    heads: conv of B and C, C.B^T, B^T and C fragments, head-major dt) and
-    ssd_bf16_kernel (conv of x and the scan);
-  - ``unfused``: the same step as two calls, mm_conv1d_silu into a buffer and
-    mm_ssd_forward on strided views of it;
-  - ``slices``: the fused call's tokens/s, HBM and MFMA fractions at every
+  - ``roofline``: the scan call's algorithmic HBM bytes divided by its own
+    duration (HIP events around each scan call inside the timed steps, on the
+    stream it runs on), against MI355X's 8 TB/s.  A scan call is two kernels:
+    tile_prep_kernel (per-tile C.B^T, B^T and C fragments and head-major dt,
+    shared by the heads) and ssd_bf16_kernel (the scan itself);
+  - ``fused``: the same step as one fused call (mm_ssd_forward_fused: the conv
+    runs inside the scan kernels, its output never reaches HBM), with its own
+    HBM fraction and measured traffic;
+  - ``slices``: the scan call's tokens/s, HBM and MFMA fractions at every
     Matryoshka width: 5 warmup calls, then 50 calls timed one by one with HIP
     events, each after a 512 MiB write that evicts the caches; median, p10,
-    p90; ``scan_slices``: the same for the scan call alone on the conv output;
+    p90; ``fused_slices``: the same for the fused call;
   - ``configs``: the same for the 130M-scale and long-context workloads;
   - ``decode``: the recurrent decode step (conv state roll + scan step) for a
     batch of 256 sequences at mixed widths, 1024 tokens captured in a HIP graph;
@@ -42,7 +40,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_prefill_1p4b_m2048.json")
+TRAFFIC_FILES = {"scan": os.path.join(ROOT, "profiles", "traffic_ssd_scan_1p4b_m2048.json"),
+                 "fused": os.path.join(ROOT, "profiles", "traffic_fused_prefill_1p4b_m2048.json")}
 SCAN_SRCS = [os.path.join(ROOT, "selective_state_space_12_amd", "csrc", f)
              for f in ("ssd_fwd_bf16.hip", "device_common.h")]
 SCAN_KERNELS = ("tile_prep_kernel", "ssd_bf16_kernel")  # the two kernels of one call
@@ -70,10 +69,11 @@ def _pmc_per_dispatch(dirname: str, counter: str, kernel_substr: str, min_grid: 
     return sum(vals.values()) / len(vals), len(vals)
 
 
-def summarize_pmc(scan_fetch, scan_write, copy_fetch, copy_write):
-    """HBM bytes per fused prefill call (``--mode fused`` runs): FETCH_SIZE +
-    WRITE_SIZE of its two kernels (mean per dispatch of each, summed), each
-    counter scaled by what it reads for a copy of known size."""
+def summarize_pmc(which, scan_fetch, scan_write, copy_fetch, copy_write):
+    """HBM bytes per scan call or fused prefill call (``which``: counter runs
+    of ``--mode scan`` / ``--mode fused``): FETCH_SIZE + WRITE_SIZE of its two
+    kernels (mean per dispatch of each, summed), each counter scaled by what
+    it reads for a copy of known size."""
     sf = sw = 0.0
     nsf, nsw = [], []
     for kname in SCAN_KERNELS:
@@ -92,8 +92,10 @@ def summarize_pmc(scan_fetch, scan_write, copy_fetch, copy_write):
     import synth
     w = synth.WORKLOADS["1.4b"]
     alg = scan_bytes(w.batch * w.seqlen, w.n_heads, w.d_head, w.d_state, 2)
-    rec = {"kernel": "fused prefill call: tile_prep_kernel<true> + ssd_bf16_kernel<true, true> "
-                     "(conv + scan, bf16, d_head 64, d_state 128, 128-token tiles)",
+    rec = {"kernel": ("fused prefill call: tile_prep_kernel<true> + ssd_bf16_kernel<true, true> "
+                      "(conv + scan" if which == "fused" else
+                      "scan call: tile_prep_kernel<false> + ssd_bf16_kernel<true, false> (scan") +
+                     ", bf16, d_head 64, d_state 128, 128-token tiles)",
            "workload": "1.4B-scale prefill, b=4 l=8192, 64 heads, chunk 256, inputs as in bench.py",
            "kernel_source_sha256_16": src_hash(),
            "fetch_kib_per_dispatch": sf, "write_kib_per_dispatch": sw,
@@ -101,8 +103,8 @@ def summarize_pmc(scan_fetch, scan_write, copy_fetch, copy_write):
                                 "fetch_scale": kf, "write_scale": kw},
            "hbm_bytes_per_launch": total, "alg_bytes_per_launch": alg,
            "traffic_over_alg": total / alg, "dispatches": [nsf, nsw]}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    os.makedirs(os.path.dirname(TRAFFIC_FILES[which]), exist_ok=True)
+    json.dump(rec, open(TRAFFIC_FILES[which], "w"), indent=1)
     print(json.dumps(rec))
 
 
@@ -181,11 +183,11 @@ def src_hash() -> str:
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per fused call measured with rocprofv3 (FETCH_SIZE and
+def load_traffic(which):
+    """HBM bytes per scan / fused call measured with rocprofv3 (FETCH_SIZE and
     WRITE_SIZE, calibrated on a copy kernel), if taken on this kernel source."""
     try:
-        d = json.load(open(TRAFFIC_FILE))
+        d = json.load(open(TRAFFIC_FILES[which]))
     except (OSError, ValueError):
         return None
     if d.get("kernel_source_sha256_16") != src_hash():
@@ -207,8 +209,10 @@ def main():
                     help="fused / scan: only the full-width fused call / scan call (for "
                          "counter runs); copy: a 1 GiB device copy that calibrates the HBM "
                          "byte counters")
-    ap.add_argument("--summarize-pmc", nargs=4, metavar=("SCAN_FETCH", "SCAN_WRITE", "COPY_FETCH", "COPY_WRITE"),
-                    help="rocprofv3 --pmc output dirs (csv); writes the traffic record under profiles/")
+    ap.add_argument("--summarize-pmc", nargs=5,
+                    metavar=("WHICH", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="WHICH = scan or fused, then rocprofv3 --pmc output dirs (csv); writes "
+                         "the traffic record under profiles/")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
@@ -318,15 +322,15 @@ def main():
         if evs:
             evs[1].record(stream)
 
-    # ---- the step: the fused call at full width --------------------------------
-    ms_step, fused_avg_ms = timed_steps(fused_step)
+    # ---- the step: conv + scan at full width ------------------------------------
+    ms_step, scan_avg_ms = timed_steps(two_call_step)
     value = tokens / (ms_step * 1e-3)
-    # ---- the same step as two calls (conv into a buffer, then the scan) --------
-    ms_two, scan_avg_ms = timed_steps(two_call_step)
+    # ---- the same step as one fused call ------------------------------------------
+    ms_fused, fused_avg_ms = timed_steps(fused_step)
 
     alg = scan_bytes(tokens, H, P, N, elem)
-    achieved = alg / (fused_avg_ms * 1e-3) / 1e9
-    traffic = load_traffic()
+    achieved = alg / (scan_avg_ms * 1e-3) / 1e9
+    traffic = load_traffic("scan")
 
     out = {
         "metric": "SSD scan tokens/s per Matryoshka slice; % of MI355X MFMA/HBM roofline",
@@ -341,18 +345,19 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) xBC stream, log-uniform dt in [1e-3, 1e-1]; no dataset)",
-        "config": {"workload": "1.4B-scale MatMamba block prefill: conv1d(k=4)+SiLU and chunked "
-                               "selective scan in one fused call, b=4 l=8192 d_model=2048 "
-                               "d_inner=4096 64 heads x 64, d_state=128, chunk=256 (evaluated as "
-                               "two 128-token tiles), slice m=2048 (64 heads)",
+        "config": {"workload": "1.4B-scale MatMamba block prefill: conv1d(k=4)+SiLU then chunked "
+                               "selective scan, b=4 l=8192 d_model=2048 d_inner=4096 64 heads x 64, "
+                               "d_state=128, chunk=256 (evaluated as two 128-token tiles), "
+                               "slice m=2048 (64 heads)",
                    "global_batch": b, "seq_len": l, "parallelism": "single GPU"},
-        "roofline": {"kernel": "fused prefill call (tile_prep_kernel + ssd_bf16_kernel, conv fused)",
-                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "roofline": {"kernel": "scan call (tile_prep_kernel + ssd_bf16_kernel)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "alg_bytes_per_launch": alg, "avg_launch_ms": fused_avg_ms},
-        "unfused": {"ms_per_step": ms_two, "tokens_per_s": tokens / (ms_two * 1e-3),
-                    "scan_ms": scan_avg_ms,
-                    "scan_hbm_frac": alg / (scan_avg_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)},
+                     "alg_bytes_per_launch": alg, "avg_launch_ms": scan_avg_ms},
+        "fused": {"ms_per_step": ms_fused, "tokens_per_s": tokens / (ms_fused * 1e-3),
+                  "call_ms": fused_avg_ms,
+                  "hbm_frac": alg / (fused_avg_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                  "traffic": load_traffic("fused")},
     }
 
     # ---- every Matryoshka width, scan only -----------------------------------
@@ -360,14 +365,14 @@ def main():
     if not (args.no_slices and args.no_configs):
         flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     if not args.no_slices:
-        slices, scan_slices = {}, {}
+        slices, fused_slices = {}, {}
         conv(H)
         for m in w.slices:
             h = w.heads(m)
             slices[str(m)] = scan_entry(tokens, h, P, N, w.chunk,
-                                        timed_calls(torch, lambda: fused(h), flush))
-            scan_slices[str(m)] = scan_entry(tokens, h, P, N, w.chunk,
-                                             timed_calls(torch, lambda: scan(h), flush))
+                                        timed_calls(torch, lambda: scan(h), flush))
+            fused_slices[str(m)] = scan_entry(tokens, h, P, N, w.chunk,
+                                              timed_calls(torch, lambda: fused(h), flush))
         # conv alone at full width, and a plain device copy of the same bytes
         # (the practical ceiling for that read + write traffic)
         tcv = timed_calls(torch, lambda: conv(H), flush)
@@ -377,7 +382,7 @@ def main():
         tc, tcopy = tcv["median"], tcp["median"]
         cb = conv_bytes(tokens, w.conv_dim, elem)
         out["slices"] = slices
-        out["scan_slices"] = scan_slices
+        out["fused_slices"] = fused_slices
         out["conv"] = {"ms": tc, "ms_p10": tcv["p10"], "ms_p90": tcv["p90"],
                        "tokens_per_s": tokens / (tc * 1e-3), "gb_per_s": cb / (tc * 1e-3) / 1e9,
                        "hbm_frac": cb / (tc * 1e-3) / (HBM_PEAK_GBS * 1e9),
