@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the Matryoshka-sliced conv1d+SiLU and selective scan.
+"""fp64 CPU oracle for the Matryoshka-sliced conv1d+SiLU, selective scan and
+gated RMSNorm epilogue.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no
@@ -62,6 +63,8 @@ def _load():
             lib.oracle_ssd_step.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i64, i64,
                                             i64, i64, i64, ip]
             lib.oracle_ssd_step.restype = None
+            lib.oracle_gated_rmsnorm.argtypes = [dp, dp, dp, ctypes.c_double, dp, i64, i64]
+            lib.oracle_gated_rmsnorm.restype = None
             _lib = lib
     return _lib
 
@@ -230,6 +233,25 @@ def ssd_forward_fused(xbc, w, dt, A, D=None, *, d_inner, d_head, conv_bias=None,
         d = softplus(d)
     y, hf = ssd_forward(x, d, A, B, C, D, h0, heads_active=heads_active)
     return y, hf, new_state
+
+
+def gated_rmsnorm(y, z, w, eps, *, d):
+    """Gated RMSNorm over the first d channels of each token (MatMamba page,
+    block paragraph: sigma = SiLU gates the scan output with z, Norm =
+    RMSNorm; gate before norm, the Mamba2 order):
+    out = (y * SiLU(z)) * w / sqrt(mean((y * SiLU(z))^2) + eps).
+    y, z: (..., >= d) -- the first d channels are used; w: (>= d,).  Returns
+    (..., d) fp64."""
+    lib = _load()
+    y = _f64(y)
+    z = _f64(z)
+    lead = y.shape[:-1]
+    yy = np.ascontiguousarray(y[..., :d].reshape(-1, d))
+    zz = np.ascontiguousarray(z[..., :d].reshape(-1, d))
+    ww = np.ascontiguousarray(_f64(w).reshape(-1)[:d])
+    out = np.empty_like(yy)
+    lib.oracle_gated_rmsnorm(_ptr(yy), _ptr(zz), _ptr(ww), float(eps), _ptr(out), yy.shape[0], d)
+    return out.reshape(*lead, d)
 
 
 def rel_l2(a, b) -> float:

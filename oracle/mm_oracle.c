@@ -170,3 +170,30 @@ void oracle_ssd_step(double* state, const double* x_t, const double* dt_t,
     }
   }
 }
+
+/*
+ * Gated RMSNorm over the first d channels of each token row (the output side
+ * of the MatMamba block paragraph: sigma = SiLU gates the scan output with z,
+ * Norm = RMSNorm; the display equation is lost, and the gate is read as
+ * applied before the norm, as in the Mamba2 block):
+ *   g_c   = y_c * SiLU(z_c),              c < d
+ *   out_c = g_c * w_c / sqrt(mean_{c<d} g_c^2 + eps)
+ * y, z, out: rows x d (row-major, unit stride); w: d.
+ */
+void oracle_gated_rmsnorm(const double* y, const double* z, const double* w, double eps,
+                          double* out, int64_t rows, int64_t d) {
+  #pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const double* yr = y + r * d;
+    const double* zr = z + r * d;
+    double* o = out + r * d;
+    double ss = 0.0;
+    for (int64_t c = 0; c < d; ++c) {
+      const double g = yr[c] * silu(zr[c]);
+      o[c] = g;
+      ss += g * g;
+    }
+    const double inv = 1.0 / sqrt(ss / (double)d + eps);
+    for (int64_t c = 0; c < d; ++c) o[c] = o[c] * inv * w[c];
+  }
+}

@@ -377,3 +377,30 @@ def test_fused_composition_columns_and_dt(softplus_on):
         np.testing.assert_allclose(hf[:, :h], hr[:, :h], rtol=1e-12, atol=1e-13)
         act = np.r_[0:h * P, d_inner:cd]
         np.testing.assert_array_equal(st[:, act], u[:, -3:, :].transpose(0, 2, 1)[:, act])
+
+
+def test_gated_rmsnorm_against_torch_and_order():
+    """Gated RMSNorm over the first d channels: against torch's rms_norm of
+    y * silu(z) (fp64); the gate comes before the norm, so with w = 1 and
+    eps = 0 every output row has mean square exactly 1 (a norm applied before
+    the gate would not); z large makes the gate the identity times z, so the
+    result is the plain RMSNorm of y; channels past d never matter."""
+    rng = np.random.default_rng(51)
+    rows, width, d = 7, 24, 16
+    y = rng.standard_normal((rows, width))
+    z = rng.standard_normal((rows, width)) * 2
+    w = rng.standard_normal(width)
+    eps = 1e-5
+    out = oracle.gated_rmsnorm(y, z, w, eps, d=d)
+    g = torch.from_numpy(y[:, :d]) * torch.nn.functional.silu(torch.from_numpy(z[:, :d]))
+    ref = torch.nn.functional.rms_norm(g, (d,), weight=torch.from_numpy(w[:d]), eps=eps).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-14)
+    unit = oracle.gated_rmsnorm(y, z, np.ones(width), 0.0, d=d)
+    np.testing.assert_allclose((unit ** 2).mean(axis=1), 1.0, rtol=1e-13)
+    big = oracle.gated_rmsnorm(y, np.full_like(z, 40.0), np.ones(width), 0.0, d=d)
+    plain = y[:, :d] / np.sqrt((y[:, :d] ** 2).mean(axis=1, keepdims=True))
+    np.testing.assert_allclose(big, plain, rtol=1e-13)
+    y2, z2 = y.copy(), z.copy()
+    y2[:, d:] = 1e9
+    z2[:, d:] = -1e9
+    np.testing.assert_array_equal(oracle.gated_rmsnorm(y2, z2, w, eps, d=d), out)
