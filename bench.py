@@ -20,6 +20,8 @@ Also reported on the same JSON line:
     events, each after a 512 MiB write that evicts the caches; median, p10,
     p90; ``fused_slices``: the same for the fused call;
   - ``configs``: the same for the 130M-scale and long-context workloads;
+  - ``gated_rmsnorm``: the gated RMSNorm epilogue (y * SiLU(z), RMSNorm over
+    d_i) on the 1.4B-scale rows at every width, timed as the slices are;
   - ``decode``: the recurrent decode step (conv state roll + scan step) for a
     batch of 256 sequences at mixed widths, 1024 tokens captured in a HIP graph;
   - ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample
@@ -387,6 +389,24 @@ def main():
                        "tokens_per_s": tokens / (tc * 1e-3), "gb_per_s": cb / (tc * 1e-3) / 1e9,
                        "hbm_frac": cb / (tc * 1e-3) / (HBM_PEAK_GBS * 1e9),
                        "copy_same_bytes_ms": tcopy, "vs_copy": tcopy / tc}
+
+    # ---- gated RMSNorm epilogue on the same rows, every width -------------------
+    if not args.no_slices:
+        gi = synth.gate_inputs(w)
+        gy, gz, gw = gi["y"].to(dev), gi["z"].to(dev), gi["w"].to(dev)
+        del gi
+        gout = torch.empty_like(gy)
+        norm = {}
+        for m in w.slices:
+            d_i = w.heads(m) * P
+            t = timed_calls(torch, lambda: mm.gated_rmsnorm(gy, gz, gw, 1e-5, d=d_i, out=gout[..., :d_i]),
+                            flush)
+            nb = 3 * tokens * d_i * elem
+            norm[str(m)] = {"d": d_i, "ms": t["median"], "ms_p10": t["p10"], "ms_p90": t["p90"],
+                            "gb_per_s": nb / (t["median"] * 1e-3) / 1e9,
+                            "hbm_frac": nb / (t["median"] * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+        out["gated_rmsnorm"] = norm
+        del gy, gz, gw, gout
 
     # ---- the other bf16 workloads, scan only, every slice ----------------------
     if not args.no_configs:

@@ -246,6 +246,26 @@ int mm_ssd_forward_fused(const void* xbc, int64_t xbc_row_stride,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Gated RMSNorm epilogue over the first d channels of each token row
+ * ("MatMamba", block paragraph: the scan output is gated by sigma(z), sigma =
+ * SiLU, and normalised by Norm = RMSNorm; the gate is read as applied before
+ * the norm, the Mamba2 order):
+ *     g_c = y_c * SiLU(z_c),   out_c = g_c * w_c / sqrt(mean_{c<d} g_c^2 + eps)
+ * With a Matryoshka slice, d = d_i and w is read as its prefix w[0:d_i].
+ *   y, z, out (rows, row strides) dtype: the first d values of each row are
+ *        read (y, z) or written (out); out may be y itself (same pointer and
+ *        stride), no other overlap with y or z.
+ *   w    (>= d) fp32, 16-byte aligned.   eps >= 0 and finite.
+ * Preconditions: rows >= 1, d >= 1 (both < 2^31); d a multiple of 8
+ * (MM_ERR_UNSUPPORTED otherwise); row strides >= d; rows 16-byte aligned.
+ */
+int mm_gated_rmsnorm(const void* y, int64_t y_row_stride,
+                     const void* z, int64_t z_row_stride,
+                     const float* w, float eps,
+                     void* out, int64_t out_row_stride,
+                     int64_t rows, int64_t d, int dtype, void* stream);
+
+/*
  * One decode token for every sequence of the batch (Mamba page, Strengths:
  * linear-time recurrent inference), in place on `state`, for heads
  * [0, h_b) of sequence b (h_b as in mm_conv1d_silu):

@@ -84,6 +84,9 @@ def lib() -> ctypes.CDLL:
                                                _i64, _i64, _i64, _i64, _int, _vp, ctypes.c_size_t,
                                                _vp]
             L.mm_ssd_forward_fused.restype = _int
+            L.mm_gated_rmsnorm.argtypes = [_vp, _i64, _vp, _i64, _vp, ctypes.c_float, _vp, _i64,
+                                           _i64, _i64, _int, _vp]
+            L.mm_gated_rmsnorm.restype = _int
             L.mm_ssd_step.argtypes = [_vp, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64,
                                       _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                       _vp, _int, _vp]
@@ -305,6 +308,48 @@ def ssd_forward_fused(xbc: torch.Tensor, conv_w: torch.Tensor, dt: torch.Tensor,
                                     code, _ptr(workspace), wbytes, _stream())
     _check("mm_ssd_forward_fused", st)
     return y
+
+
+def gated_rmsnorm(y: torch.Tensor, z: torch.Tensor, w: torch.Tensor, eps: float = 1e-5, *,
+                  d: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out = (y * SiLU(z)) * w / sqrt(mean((y * SiLU(z))^2) + eps) over the
+    first d channels of every row.  y, z: (..., width) with contiguous rows of
+    width >= d (views of wider rows allowed: the rows may be strided); w fp32.
+    Returns out (..., d) (or writes the given out, which may be y)."""
+    width = y.shape[-1]
+    d = width if d is None else int(d)
+
+    def rows_of(t, name):
+        """(rows, row stride) of a (..., width) tensor whose leading
+        dimensions collapse to evenly strided rows of unit-stride values."""
+        if t.shape[-1] < d or (t.shape[-1] > 1 and t.stride(-1) != 1):
+            raise ValueError(f"{name}: rows must be unit-stride with at least d={d} values")
+        if t.dim() == 1:
+            return 1, t.shape[-1]
+        rs = t.stride(-2)
+        for k in range(t.dim() - 3, -1, -1):
+            if t.shape[k] > 1 and t.stride(k) != t.stride(k + 1) * t.shape[k + 1]:
+                raise ValueError(f"{name}: leading dimensions must collapse to evenly strided rows")
+        n = 1
+        for v in t.shape[:-1]:
+            n *= v
+        return n, (rs if n > 1 else t.shape[-1])
+
+    rows, ys = rows_of(y, "y")
+    rz, zs = rows_of(z, "z")
+    if rz != rows or z.dtype != y.dtype:
+        raise ValueError("z must have y's rows and dtype")
+    if out is None:
+        out = torch.empty(tuple(y.shape[:-1]) + (d,), dtype=y.dtype, device=y.device)
+    ro, os_ = rows_of(out, "out")
+    if ro != rows or out.dtype != y.dtype:
+        raise ValueError("out must have y's rows and dtype")
+    if w.dtype != torch.float32 or not w.is_contiguous() or w.numel() < d:
+        raise ValueError("w must be a contiguous fp32 tensor of at least d values")
+    st = lib().mm_gated_rmsnorm(_ptr(y), ys, _ptr(z), zs, _ptr(w), float(eps), _ptr(out), os_,
+                                rows, d, _dtype_code(y), _stream())
+    _check("mm_gated_rmsnorm", st)
+    return out
 
 
 def ssd_step(state: torch.Tensor, x_t: torch.Tensor, dt_t: torch.Tensor, A: torch.Tensor,

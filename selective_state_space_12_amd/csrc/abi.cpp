@@ -192,6 +192,26 @@ int mm_ssd_forward_fused(const void* xbc, int64_t xbc_row_stride, const float* c
   return hip_status(launch_ssd_forward_fused(f, workspace, as_stream(stream)));
 }
 
+int mm_gated_rmsnorm(const void* y, int64_t y_row_stride, const void* z, int64_t z_row_stride,
+                     const float* w, float eps, void* out, int64_t out_row_stride, int64_t rows,
+                     int64_t d, int dtype, void* stream) {
+  const int st = validate_gated_rmsnorm(y, y_row_stride, z, z_row_stride, w, eps, out,
+                                        out_row_stride, rows, d, dtype);
+  if (st != MM_OK) return st;
+  NormArgs a;
+  a.y = y;
+  a.ys = y_row_stride;
+  a.z = z;
+  a.zs = z_row_stride;
+  a.w = w;
+  a.eps = eps;
+  a.out = out;
+  a.os = out_row_stride;
+  a.rows = rows;
+  a.d = d;
+  return hip_status(launch_gated_rmsnorm(a, dtype, as_stream(stream)));
+}
+
 int mm_ssd_step(float* state, const void* x_t, int64_t x_row_stride, const void* dt_t,
                 int64_t dt_row_stride, const float* A, const void* B_t,
                 int64_t b_row_stride, const void* C_t, int64_t c_row_stride,

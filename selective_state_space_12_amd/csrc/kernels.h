@@ -111,6 +111,20 @@ hipError_t launch_ssd_forward_bf16_fused(const FwdArgs& a, const FuseArgs& fu, v
 
 hipError_t launch_ssd_forward(const FwdArgs& a, int dtype, void* workspace, hipStream_t s);
 
+// Gated RMSNorm epilogue (gated_rmsnorm.hip): rows of y and z, d channels.
+struct NormArgs {
+  const void* y;
+  int64_t ys;
+  const void* z;
+  int64_t zs;
+  const float* w;
+  float eps;
+  void* out;
+  int64_t os;
+  int64_t rows, d;
+};
+hipError_t launch_gated_rmsnorm(const NormArgs& a, int dtype, hipStream_t s);
+
 // A fused prefill call (fused.hip): raw [x | B | C] conv input rows in, the
 // conv + SiLU and the dt transform applied on the way into the scan.
 struct FusedCall {

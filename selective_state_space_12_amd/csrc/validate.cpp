@@ -2,6 +2,7 @@
 #include "validate.h"
 
 #include <cstdint>
+#include <utility>
 
 namespace mmssd {
 
@@ -169,6 +170,34 @@ int validate_ssd_forward_fused(const void* xbc, int64_t xbc_row_stride, const fl
   const uintptr_t o0 = reinterpret_cast<uintptr_t>(y);
   const uintptr_t o1 = o0 + uintptr_t(((rows - 1) * y_row_stride + xw) * el);
   if (i0 < o1 && o0 < i1) return MM_ERR_SHAPE;
+  return MM_OK;
+}
+
+int validate_gated_rmsnorm(const void* y, int64_t y_row_stride, const void* z,
+                           int64_t z_row_stride, const float* w, float eps, const void* out,
+                           int64_t out_row_stride, int64_t rows, int64_t d, int dtype) {
+  if (!y || !z || !w || !out) return MM_ERR_NULL;
+  const int64_t el = dtype_bytes(dtype);
+  if (el == 0) return MM_ERR_DTYPE;
+  if (!pos(rows) || !pos(d) || rows > INT32_MAX || d > INT32_MAX) return MM_ERR_SHAPE;
+  if (d % 8 != 0) return MM_ERR_UNSUPPORTED;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return MM_ERR_SHAPE;  // rejects NaN and inf too
+  if (y_row_stride < d || z_row_stride < d || out_row_stride < d) return MM_ERR_SHAPE;
+  if (!mul_ok(rows, y_row_stride) || !mul_ok(rows, z_row_stride) || !mul_ok(rows, out_row_stride))
+    return MM_ERR_SHAPE;
+  if (!rows_aligned(y, y_row_stride, el) || !rows_aligned(z, z_row_stride, el) ||
+      !rows_aligned(out, out_row_stride, el))
+    return MM_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(w) % 16 != 0) return MM_ERR_ALIGN;
+  // out may be y itself (same rows); any other overlap with y or z is refused
+  auto span = [&](const void* p, int64_t stride) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return std::pair<uintptr_t, uintptr_t>(a, a + uintptr_t(((rows - 1) * stride + d) * el));
+  };
+  const auto o = span(out, out_row_stride), yy = span(y, y_row_stride), zz = span(z, z_row_stride);
+  const bool same_as_y = out == y && out_row_stride == y_row_stride;
+  if (!same_as_y && o.first < yy.second && yy.first < o.second) return MM_ERR_SHAPE;
+  if (o.first < zz.second && zz.first < o.second) return MM_ERR_SHAPE;
   return MM_OK;
 }
 

@@ -57,6 +57,10 @@ int validate_ssd_forward_fused(const void* xbc, int64_t xbc_row_stride, const fl
                                int64_t d_state, int64_t ngroups, int64_t n_heads_active,
                                int64_t chunk, int dtype);
 
+int validate_gated_rmsnorm(const void* y, int64_t y_row_stride, const void* z,
+                           int64_t z_row_stride, const float* w, float eps, const void* out,
+                           int64_t out_row_stride, int64_t rows, int64_t d, int dtype);
+
 int validate_ssd_step(const float* state, const void* x_t, int64_t x_row_stride,
                       const void* dt_t, int64_t dt_row_stride, const float* A,
                       const void* B_t, int64_t b_row_stride, const void* C_t,

@@ -22,7 +22,7 @@ from typing import Dict, List, Optional
 import torch
 
 # tensor indices inside a config's seed block
-_X, _B, _C, _DT, _A, _D, _CONVW, _XBC, _H0, _CS0, _DTSTEP, _XBCSTEP, _CONVB, _DTRAW, _DTB = range(15)
+_X, _B, _C, _DT, _A, _D, _CONVW, _XBC, _H0, _CS0, _DTSTEP, _XBCSTEP, _CONVB, _DTRAW, _DTB, _Z, _NW, _YN = range(18)
 
 
 @dataclass(frozen=True)
@@ -179,6 +179,20 @@ def raw_dt(w: Workload, batch: Optional[int] = None, seqlen: Optional[int] = Non
 def draw_dt_bias(w: Workload) -> torch.Tensor:
     """(n_heads,) fp32, 0.5 * N(0, 1): exercises the optional dt bias."""
     return _normal((w.n_heads,), _gen(w, _DTB), 0.5)
+
+
+def gate_inputs(w: Workload, batch: Optional[int] = None, seqlen: Optional[int] = None,
+                salt: int = 0) -> Dict[str, torch.Tensor]:
+    """Inputs of the gated RMSNorm epilogue: a scan output stand-in y and the
+    gate z, both (b, l, d_inner) ~ N(0,1) in the storage dtype, and the norm
+    weight (d_inner,) = 1 + 0.1 * N(0,1) fp32."""
+    b = batch or w.batch
+    l = seqlen or w.seqlen
+    return {
+        "y": _normal((b, l, w.d_inner), _gen(w, _YN, salt)).to(w.dtype),
+        "z": _normal((b, l, w.d_inner), _gen(w, _Z, salt)).to(w.dtype),
+        "w": 1.0 + _normal((w.d_inner,), _gen(w, _NW), 0.1),
+    }
 
 
 def decode_pool(w: Workload, pool: int = 64, batch: Optional[int] = None,

@@ -92,6 +92,39 @@ int main() {
   expect("step B misaligned", step(F, 256, 64, 64, 128, 1, 64, MM_F32, MIS), MM_ERR_ALIGN);
   expect("step dtype", step(F, 256, 64, 64, 128, 1, 64, 5, P), MM_ERR_DTYPE);
 
+  // fused prefill call: raw xBC rows (4352 channels) at P, y at P2
+  auto fused = [&](const void* xbc, int64_t xs, const float* cw, const float* cst, int sp,
+                   const void* y, int64_t heads, int64_t chunk, int dt_code) {
+    return validate_ssd_forward_fused(xbc, xs, cw, nullptr, cst, P, 64, nullptr, sp, F, y, 4096,
+                                      nullptr, nullptr, 4, 8192, 64, 64, 128, 1, heads, chunk,
+                                      dt_code);
+  };
+  const float* FMIS = reinterpret_cast<const float*>(uintptr_t(0x200004));
+  expect("fused ok", fused(P, cd, F, F, 1, P2, 64, 256, MM_BF16), MM_OK);
+  expect("fused null conv w", fused(P, cd, nullptr, F, 1, P2, 64, 256, MM_BF16), MM_ERR_NULL);
+  expect("fused stride < conv_dim", fused(P, cd - 8, F, F, 1, P2, 64, 256, MM_BF16), MM_ERR_SHAPE);
+  expect("fused softplus flag 2", fused(P, cd, F, F, 2, P2, 64, 256, MM_BF16), MM_ERR_SHAPE);
+  expect("fused conv w misaligned", fused(P, cd, FMIS, F, 1, P2, 64, 256, MM_BF16), MM_ERR_ALIGN);
+  expect("fused y over xbc", fused(P, cd, F, F, 1, P, 64, 256, MM_BF16), MM_ERR_SHAPE);
+  expect("fused heads 0", fused(P, cd, F, F, 1, P2, 0, 256, MM_BF16), MM_ERR_SLICE);
+  expect("fused chunk 48", fused(P, cd, F, F, 1, P2, 64, 48, MM_BF16), MM_ERR_UNSUPPORTED);
+
+  // gated RMSNorm: 32768 rows of 4096, y at P, z at P2, out at P3
+  const void* P3 = reinterpret_cast<const void*>(uintptr_t(0x4000000000ull));
+  auto norm = [&](const void* y, const void* z, const void* o, int64_t os, const float* w, float eps,
+                  int64_t d, int dt_code) {
+    return validate_gated_rmsnorm(y, 4096, z, 4096, w, eps, o, os, 32768, d, dt_code);
+  };
+  expect("norm ok", norm(P, P2, P3, 4096, F, 1e-5f, 4096, MM_BF16), MM_OK);
+  expect("norm in place", norm(P, P2, P, 4096, F, 1e-5f, 4096, MM_BF16), MM_OK);
+  expect("norm out over y, other stride", norm(P, P2, P, 4104, F, 1e-5f, 4096, MM_BF16), MM_ERR_SHAPE);
+  expect("norm out over z", norm(P, P2, P2, 4096, F, 1e-5f, 4096, MM_BF16), MM_ERR_SHAPE);
+  expect("norm d % 8", norm(P, P2, P3, 4096, F, 1e-5f, 4092, MM_BF16), MM_ERR_UNSUPPORTED);
+  expect("norm eps < 0", norm(P, P2, P3, 4096, F, -1.0f, 4096, MM_BF16), MM_ERR_SHAPE);
+  expect("norm w misaligned", norm(P, P2, P3, 4096, FMIS, 1e-5f, 4096, MM_BF16), MM_ERR_ALIGN);
+  expect("norm null z", norm(P, nullptr, P3, 4096, F, 1e-5f, 4096, MM_BF16), MM_ERR_NULL);
+  expect("norm dtype", norm(P, P2, P3, 4096, F, 1e-5f, 4096, 9), MM_ERR_DTYPE);
+
   std::printf("%d failure(s)\n", failures);
   return failures == 0 ? 0 : 1;
 }
