@@ -20,6 +20,9 @@ Also reported on the same JSON line:
     events, each after a 512 MiB write that evicts the caches; median, p10,
     p90; ``fused_slices``: the same for the fused call;
   - ``configs``: the same for the 130M-scale and long-context workloads;
+  - ``mixed``: the scan with a width per sequence (mm_ssd_forward_mixed),
+    widths round-robin {512, 1024, 2048} over the 4 sequences, against the
+    same batch run at the widest width;
   - ``gated_rmsnorm``: the gated RMSNorm epilogue (y * SiLU(z), RMSNorm over
     d_i) on the 1.4B-scale rows at every width, timed as the slices are;
   - ``decode``: the recurrent decode step (conv state roll + scan step) for a
@@ -389,6 +392,23 @@ def main():
                        "tokens_per_s": tokens / (tc * 1e-3), "gb_per_s": cb / (tc * 1e-3) / 1e9,
                        "hbm_frac": cb / (tc * 1e-3) / (HBM_PEAK_GBS * 1e9),
                        "copy_same_bytes_ms": tcopy, "vs_copy": tcopy / tc}
+
+    # ---- a width per sequence: widths round-robin {512, 1024, 2048} ----------------
+    if not args.no_slices:
+        hps = [w.heads(w.slices[1 + (i % 3)]) for i in range(b)]
+        wsm = torch.empty(max(mm.ssd_forward_mixed_workspace_size(b, l, H, P, N, 1, hps, w.chunk,
+                                                                  w.dtype), 1),
+                          dtype=torch.uint8, device=dev)
+        tmix = timed_calls(torch, lambda: mm.ssd_forward_mixed(
+            xv, dt, A, Bv, Cv, D, heads_per_seq=hps, chunk=w.chunk, y=y, workspace=wsm), flush)
+        tmax = timed_calls(torch, lambda: scan(max(hps)), flush)
+        mb = sum(scan_bytes(l, h, P, N, elem) for h in hps)
+        out["mixed"] = {"heads_per_seq": hps, "scan_ms": tmix["median"],
+                        "scan_ms_p10": tmix["p10"], "scan_ms_p90": tmix["p90"],
+                        "tokens_per_s": tokens / (tmix["median"] * 1e-3),
+                        "hbm_frac": mb / (tmix["median"] * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                        "widest_for_all_ms": tmax["median"]}
+        del wsm
 
     # ---- gated RMSNorm epilogue on the same rows, every width -------------------
     if not args.no_slices:

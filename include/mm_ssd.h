@@ -194,6 +194,50 @@ int mm_ssd_forward(const void* x, int64_t x_row_stride,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace mm_ssd_forward_mixed needs for these sizes and
+ * per-sequence widths (may be 0).  Same argument meaning and errors as
+ * mm_ssd_forward_mixed.  Host only.
+ */
+int mm_ssd_forward_mixed_workspace_size(int64_t batch, int64_t seqlen,
+                                        int64_t n_heads, int64_t d_head,
+                                        int64_t d_state, int64_t ngroups,
+                                        const int32_t* heads_per_seq,
+                                        int64_t chunk, int dtype,
+                                        size_t* bytes_out);
+
+/*
+ * mm_ssd_forward with a width per sequence ("MatMamba", deployment
+ * paragraph: input-adaptive sub-model selection, a larger slice for a harder
+ * input; here each sequence of the batch runs its own slice): sequence b runs heads
+ * [0, heads_per_seq[b]) with the prefixes A[0:h_b], D[0:h_b] and its
+ * initial/final state heads; every other head's y and state is untouched.
+ * Results for sequence b equal a mm_ssd_forward call at n_heads_active = h_b
+ * up to rounding (bit for bit when both calls cut the sequence into the same
+ * segments).
+ *   heads_per_seq: HOST array of batch int32 values in [1, n_heads], read
+ *       during the call (the launch carries them; no device table).  Only
+ *       the active (sequence, head) units are scheduled, and the segment
+ *       split is planned for their count.
+ *   Every other argument as in mm_ssd_forward, with the row strides checked
+ *   against the widest sequence.
+ * Preconditions: those of mm_ssd_forward; batch <= 256 (MM_ERR_UNSUPPORTED
+ * otherwise); MM_ERR_SLICE for an entry outside [1, n_heads]; MM_ERR_NULL if
+ * heads_per_seq is NULL.
+ */
+int mm_ssd_forward_mixed(const void* x, int64_t x_row_stride,
+                         const void* dt, int64_t dt_row_stride,
+                         const float* A,
+                         const void* B, int64_t b_row_stride,
+                         const void* C, int64_t c_row_stride,
+                         const float* D,
+                         void* y, int64_t y_row_stride,
+                         const float* initial_state, float* final_state,
+                         int64_t batch, int64_t seqlen, int64_t n_heads,
+                         int64_t d_head, int64_t d_state, int64_t ngroups,
+                         const int32_t* heads_per_seq, int64_t chunk, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace mm_ssd_forward_fused needs for these sizes (may
  * be 0).  Same argument meaning and errors as mm_ssd_forward_fused.  Host only.
  */

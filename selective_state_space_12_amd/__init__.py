@@ -84,6 +84,14 @@ def lib() -> ctypes.CDLL:
                                                _i64, _i64, _i64, _i64, _int, _vp, ctypes.c_size_t,
                                                _vp]
             L.mm_ssd_forward_fused.restype = _int
+            L.mm_ssd_forward_mixed_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64,
+                                                              _vp, _i64, _int,
+                                                              ctypes.POINTER(ctypes.c_size_t)]
+            L.mm_ssd_forward_mixed_workspace_size.restype = _int
+            L.mm_ssd_forward_mixed.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
+                                               _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                               _i64, _vp, _i64, _int, _vp, ctypes.c_size_t, _vp]
+            L.mm_ssd_forward_mixed.restype = _int
             L.mm_gated_rmsnorm.argtypes = [_vp, _i64, _vp, _i64, _vp, ctypes.c_float, _vp, _i64,
                                            _i64, _i64, _int, _vp]
             L.mm_gated_rmsnorm.restype = _int
@@ -244,6 +252,72 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
                               batch, seqlen, n_heads, d_head, d_state, ngroups, h_act, chunk,
                               code, _ptr(workspace), wbytes, _stream())
     _check("mm_ssd_forward", st)
+    return y
+
+
+def _host_heads(heads_per_seq, batch: int):
+    """Per-sequence head counts as a host int32 array (kept alive by the caller)."""
+    if len(heads_per_seq) != batch:
+        raise ValueError(f"heads_per_seq must have {batch} entries")
+    return (ctypes.c_int32 * batch)(*[int(v) for v in heads_per_seq])
+
+
+def ssd_forward_mixed_workspace_size(batch: int, seqlen: int, n_heads: int, d_head: int,
+                                     d_state: int, ngroups: int, heads_per_seq, chunk: int,
+                                     dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    code = MM_F32 if dtype == torch.float32 else MM_BF16
+    hp = _host_heads(heads_per_seq, batch)
+    _check("mm_ssd_forward_mixed_workspace_size",
+           lib().mm_ssd_forward_mixed_workspace_size(batch, seqlen, n_heads, d_head, d_state,
+                                                     ngroups, ctypes.cast(hp, ctypes.c_void_p),
+                                                     chunk, code, ctypes.byref(out)))
+    return out.value
+
+
+def ssd_forward_mixed(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                      C: torch.Tensor, D: Optional[torch.Tensor] = None, *, heads_per_seq,
+                      chunk: int = 256, initial_state: Optional[torch.Tensor] = None,
+                      final_state: Optional[torch.Tensor] = None,
+                      y: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ssd_forward with a width per sequence: sequence b runs heads
+    [0, heads_per_seq[b]) (a list or CPU tensor of ints).  Returns y
+    (batch, seqlen, n_heads, d_head) -- the given buffer, or a new one whose
+    inactive heads are uninitialised."""
+    batch, seqlen, n_heads, d_head = x.shape
+    if B.dim() == 3:
+        B = B.unsqueeze(2)
+        C = C.unsqueeze(2)
+    ngroups, d_state = B.shape[2], B.shape[3]
+    hps = [int(v) for v in (heads_per_seq.tolist() if torch.is_tensor(heads_per_seq)
+                            else heads_per_seq)]
+    hp = _host_heads(hps, batch)
+    if y is None:
+        y = torch.empty((batch, seqlen, n_heads, d_head), dtype=x.dtype, device=x.device)
+    code = _dtype_code(x)
+    for name, t in (("dt", dt), ("B", B), ("C", C), ("y", y)):
+        if t.dtype != x.dtype:
+            raise TypeError(f"{name} must have x's dtype")
+    xs = _row_stride(x, "x", (n_heads, d_head))
+    ys = _row_stride(y, "y", (y.shape[2], d_head))
+    dts = _row_stride(dt, "dt", (n_heads,))
+    bs = _row_stride(B, "B", (ngroups, d_state))
+    cs = _row_stride(C, "C", (ngroups, d_state))
+    for name, t in (("A", A), ("D", D), ("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 tensor")
+    need = ssd_forward_mixed_workspace_size(batch, seqlen, n_heads, d_head, d_state, ngroups, hps,
+                                            chunk, x.dtype)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().mm_ssd_forward_mixed(_ptr(x), xs, _ptr(dt), dts, _ptr(A), _ptr(B), bs, _ptr(C), cs,
+                                    _ptr(D), _ptr(y), ys, _ptr(initial_state), _ptr(final_state),
+                                    batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                    ctypes.cast(hp, ctypes.c_void_p), chunk, code, _ptr(workspace),
+                                    wbytes, _stream())
+    _check("mm_ssd_forward_mixed", st)
     return y
 
 

@@ -135,6 +135,69 @@ int mm_ssd_forward(const void* x, int64_t x_row_stride, const void* dt,
   return hip_status(launch_ssd_forward(a, dtype, workspace, as_stream(stream)));
 }
 
+int mm_ssd_forward_mixed_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
+                                        int64_t d_head, int64_t d_state, int64_t ngroups,
+                                        const int32_t* heads_per_seq, int64_t chunk, int dtype,
+                                        size_t* bytes_out) {
+  if (!bytes_out) return MM_ERR_NULL;
+  int64_t mx = 0;
+  int st = validate_heads_per_seq(heads_per_seq, batch, n_heads, &mx);
+  if (st != MM_OK) return st;
+  st = validate_ssd_shape(batch, seqlen, n_heads, d_head, d_state, ngroups, mx, chunk, dtype);
+  if (st != MM_OK) return st;
+  int64_t units = 0;
+  for (int64_t b = 0; b < batch; ++b) units += heads_per_seq[b];
+  *bytes_out = fwd_workspace_bytes(batch, seqlen, mx, d_head, d_state, chunk, dtype, units);
+  return MM_OK;
+}
+
+int mm_ssd_forward_mixed(const void* x, int64_t x_row_stride, const void* dt,
+                         int64_t dt_row_stride, const float* A, const void* B,
+                         int64_t b_row_stride, const void* C, int64_t c_row_stride,
+                         const float* D, void* y, int64_t y_row_stride,
+                         const float* initial_state, float* final_state, int64_t batch,
+                         int64_t seqlen, int64_t n_heads, int64_t d_head, int64_t d_state,
+                         int64_t ngroups, const int32_t* heads_per_seq, int64_t chunk, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t mx = 0;
+  int st = validate_heads_per_seq(heads_per_seq, batch, n_heads, &mx);
+  if (st != MM_OK) return st;
+  st = validate_ssd_forward(x, x_row_stride, dt, dt_row_stride, A, B, b_row_stride, C,
+                            c_row_stride, y, y_row_stride, initial_state, final_state, batch,
+                            seqlen, n_heads, d_head, d_state, ngroups, mx, chunk, dtype);
+  if (st != MM_OK) return st;
+  int64_t units = 0;
+  for (int64_t b = 0; b < batch; ++b) units += heads_per_seq[b];
+  const size_t need =
+      fwd_workspace_bytes(batch, seqlen, mx, d_head, d_state, chunk, dtype, units);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MM_ERR_WORKSPACE;
+  if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return MM_ERR_ALIGN;
+  FwdArgs a;
+  a.x = x;
+  a.xs = x_row_stride;
+  a.dt = dt;
+  a.dts = dt_row_stride;
+  a.A = A;
+  a.B = B;
+  a.bs = b_row_stride;
+  a.C = C;
+  a.cs = c_row_stride;
+  a.D = D;
+  a.y = y;
+  a.ys = y_row_stride;
+  a.h0 = initial_state;
+  a.hT = final_state;
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.n_heads = (int)n_heads;
+  a.d_head = (int)d_head;
+  a.d_state = (int)d_state;
+  a.heads = (int)mx;
+  a.chunk = (int)chunk;
+  a.heads_per_seq = heads_per_seq;
+  return hip_status(launch_ssd_forward(a, dtype, workspace, as_stream(stream)));
+}
+
 int mm_ssd_forward_fused_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
                                         int64_t d_head, int64_t d_state, int64_t ngroups,
                                         int64_t n_heads_active, int64_t chunk, int dtype,

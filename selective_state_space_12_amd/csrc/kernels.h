@@ -47,6 +47,30 @@ struct StepArgs {
 
 hipError_t launch_ssd_step(const StepArgs& a, int dtype, hipStream_t s);
 
+// Per-sequence slices of a scan call (input-adaptive widths: each sequence
+// runs its own slice): the active (sequence, head) units, numbered sequence-major, with
+// start[b] the first unit of sequence b (start[batch] = units).  Passed by
+// value to the kernels, so a mixed call needs no device-side table.
+constexpr int kMaxMixedBatch = 256;
+struct UnitMap {
+  int mixed = 0;  // 0: every sequence runs the call's `heads`
+  int batch = 0;
+  int units = 0;
+  int start[kMaxMixedBatch + 1] = {};
+};
+
+// Sequence and head of unit u (mixed maps; start[] is nondecreasing).
+__host__ __device__ inline void unit_to_bh(const UnitMap& m, int u, int* b, int* h) {
+  int lo = 0, hi = m.batch;  // start[lo] <= u < start[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (m.start[mid] <= u) lo = mid;
+    else hi = mid;
+  }
+  *b = lo;
+  *h = u - m.start[lo];
+}
+
 struct FwdArgs {
   const void* x;
   int64_t xs;
@@ -63,23 +87,30 @@ struct FwdArgs {
   const float* h0;
   float* hT;
   int64_t batch, seqlen;
-  int n_heads, d_head, d_state, heads;
+  int n_heads, d_head, d_state, heads;  // heads: active heads (the widest sequence's, if mixed)
   int chunk;
+  const int32_t* heads_per_seq = nullptr;  // host array (batch entries) for a mixed call
 };
+
+// The unit map of a call (mixed when a.heads_per_seq is set).
+UnitMap make_unit_map(const FwdArgs& a);
 
 // How a scan call is cut: chunks per sequence, segments per sequence and
 // chunks per segment (every segment but the last holds seg_chunks chunks).
+// `units` overrides batch * heads as the count of active (sequence, head)
+// units (a mixed call); 0 keeps it.
 void fwd_plan(int64_t batch, int64_t seqlen, int64_t heads, int64_t chunk, int* nchunks,
-              int* nseg, int* seg_chunks);
+              int* nseg, int* seg_chunks, int64_t units = 0);
 // Device workspace a scan call needs, 0 if none: segment states and decays
 // of the plan and, on the bf16 d_head-64 d_state-128 path, the per-tile G and
 // B^T fragments.
 size_t fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
-                           int64_t d_head, int64_t d_state, int64_t chunk, int dtype);
+                           int64_t d_head, int64_t d_state, int64_t chunk, int dtype,
+                           int64_t units = 0);
 
 // Segments per sequence of a scan call (the plan of the path it takes).
 int fwd_segments(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
-                 int64_t d_state, int64_t chunk, int dtype);
+                 int64_t d_state, int64_t chunk, int dtype, int64_t units = 0);
 
 // Conv and dt parameters of a fused scan call (raw conv input in, the conv
 // and the dt transform applied on the way into the scan).
@@ -95,13 +126,13 @@ struct FuseArgs {
 
 // bf16, d_head 64, d_state 128, chunk 128 or 256 (ssd_fwd_bf16.hip).
 bool bf16_path(int64_t d_head, int64_t d_state, int64_t chunk, int dtype);
-size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads);
+size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t units = 0);
 // The bf16 path's cut (128-token tiles): the segment count that minimises an
 // estimate of the call's time in tile-walk units, counting workgroup rounds
 // of one workgroup per CU, the per-walk start-up and the prepass and combine
 // that a split adds.
 void fwd_plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int* ntiles, int* nseg,
-                   int* seg_tiles);
+                   int* seg_tiles, int64_t units = 0);
 hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* workspace, hipStream_t s);
 // The same with the conv and dt transform fused in: a.x, a.B, a.C are the raw
 // conv input's x, B and C columns and a.dt the raw dt.  The conv state, if

@@ -65,6 +65,7 @@ struct FwdK {
   float* seg_decay;  // (batch, heads, nseg) log2 decay of each segment
   int64_t seqlen;
   int n_heads, heads, nseg, seg_chunks, nchunks;
+  UnitMap um;  // mixed: heads of sequence b = um.start[b+1] - um.start[b]
 };
 
 template <typename T> constexpr int pad16() { return 16 / (int)sizeof(T); }
@@ -113,6 +114,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
   const int pid = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
   const int uid = total % kXcds == 0 ? (pid % kXcds) * (total / kXcds) + pid / kXcds : pid;
   const int seg = uid % gx, h = (uid / gx) % gy, b = uid / (gx * gy);
+  if (k.um.mixed && h >= k.um.start[b + 1] - k.um.start[b]) return;  // whole workgroup
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int r16 = lane % 16, g = lane / 16;
 
@@ -621,8 +623,10 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(FwdK k) {
 __global__ __launch_bounds__(256) void seg_combine_kernel(float* __restrict__ seg_state,
                                                           const float* __restrict__ seg_decay,
                                                           const float* __restrict__ h0,
-                                                          int n_heads, int heads, int nseg, int PN) {
+                                                          int n_heads, int heads, int nseg, int PN,
+                                                          UnitMap um) {
   const int h = blockIdx.x, b = blockIdx.y;
+  if (um.mixed && h >= um.start[b + 1] - um.start[b]) return;
   const int64_t unit = (int64_t)b * heads + h;
   for (int e = threadIdx.x; e < PN; e += 256) {
     float H = h0 ? h0[((int64_t)b * n_heads + h) * PN + e] : 0.0f;
@@ -643,7 +647,9 @@ hipError_t launch_shape(const FwdArgs& a, void* ws, hipStream_t s) {
   k.B = a.B; k.bs = a.bs; k.C = a.C; k.cs = a.cs; k.D = a.D;
   k.y = a.y; k.ys = a.ys; k.h0 = a.h0; k.hT = a.hT;
   k.seqlen = a.seqlen; k.n_heads = a.n_heads; k.heads = a.heads;
-  fwd_plan(a.batch, a.seqlen, a.heads, Q, &k.nchunks, &k.nseg, &k.seg_chunks);
+  k.um = make_unit_map(a);
+  fwd_plan(a.batch, a.seqlen, a.heads, Q, &k.nchunks, &k.nseg, &k.seg_chunks,
+           k.um.mixed ? k.um.units : 0);
   k.seg_state = nullptr;
   k.seg_decay = nullptr;
   if (k.nseg > 1) {
@@ -660,7 +666,7 @@ hipError_t launch_shape(const FwdArgs& a, void* ws, hipStream_t s) {
     hipLaunchKernelGGL(pre, dim3(k.nseg - 1, a.heads, (unsigned)a.batch), dim3(kThreads), lds, s, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(seg_combine_kernel, dim3(a.heads, (unsigned)a.batch), dim3(256), 0, s,
-                       k.seg_state, k.seg_decay, a.h0, a.n_heads, a.heads, k.nseg, P * N);
+                       k.seg_state, k.seg_decay, a.h0, a.n_heads, a.heads, k.nseg, P * N, k.um);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   auto main_k = ssd_chunk_kernel<T, P, N, Q, true>;
@@ -696,10 +702,21 @@ hipError_t launch_typed(const FwdArgs& a, void* ws, hipStream_t s) {
 
 }  // namespace
 
+UnitMap make_unit_map(const FwdArgs& a) {
+  UnitMap m;
+  if (!a.heads_per_seq) return m;
+  m.mixed = 1;
+  m.batch = (int)a.batch;
+  m.start[0] = 0;
+  for (int b = 0; b < m.batch; ++b) m.start[b + 1] = m.start[b] + a.heads_per_seq[b];
+  m.units = m.start[m.batch];
+  return m;
+}
+
 void fwd_plan(int64_t batch, int64_t seqlen, int64_t heads, int64_t chunk, int* nchunks,
-              int* nseg, int* seg_chunks) {
+              int* nseg, int* seg_chunks, int64_t units_in) {
   const int64_t nc = (seqlen + chunk - 1) / chunk;
-  const int64_t units = batch * heads;
+  const int64_t units = units_in > 0 ? units_in : batch * heads;
   int64_t want = (MMSSD_TARGET_UNITS + units - 1) / units;
   if (want > nc) want = nc;
   if (want < 1) want = 1;
@@ -710,20 +727,21 @@ void fwd_plan(int64_t batch, int64_t seqlen, int64_t heads, int64_t chunk, int* 
 }
 
 int fwd_segments(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
-                 int64_t d_state, int64_t chunk, int dtype) {
+                 int64_t d_state, int64_t chunk, int dtype, int64_t units) {
   int nc, nseg, per;
   if (bf16_path(d_head, d_state, chunk, dtype))
-    fwd_plan_bf16(batch, seqlen, heads, &nc, &nseg, &per);
+    fwd_plan_bf16(batch, seqlen, heads, &nc, &nseg, &per, units);
   else
-    fwd_plan(batch, seqlen, heads, chunk, &nc, &nseg, &per);
+    fwd_plan(batch, seqlen, heads, chunk, &nc, &nseg, &per, units);
   return nseg;
 }
 
 size_t fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
-                           int64_t d_state, int64_t chunk, int dtype) {
-  if (bf16_path(d_head, d_state, chunk, dtype)) return bf16_workspace_bytes(batch, seqlen, heads);
+                           int64_t d_state, int64_t chunk, int dtype, int64_t units) {
+  if (bf16_path(d_head, d_state, chunk, dtype))
+    return bf16_workspace_bytes(batch, seqlen, heads, units);
   int nc, nseg, per;
-  fwd_plan(batch, seqlen, heads, chunk, &nc, &nseg, &per);
+  fwd_plan(batch, seqlen, heads, chunk, &nc, &nseg, &per, units);
   if (nseg <= 1) return 0;
   return (size_t)(batch * heads * nseg) * (size_t)(d_head * d_state + 1) * sizeof(float);
 }

@@ -375,6 +375,9 @@ struct BK {
   int64_t conv_dim;
   int64_t seqlen;
   int n_heads, heads, nseg, seg_chunks, ntiles;
+  // mixed calls: the grid is (segments x active units) on x, units numbered
+  // sequence-major (heads of one sequence adjacent)
+  UnitMap um;
 };
 
 // ---------------------------------------------------------------------------
@@ -805,7 +808,15 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(BK k) {
   const int total = gx * gy * gridDim.z;
   const int pid = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
   const int uid = total % kXcds == 0 ? (pid % kXcds) * (total / kXcds) + pid / kXcds : pid;
-  const int h = uid % gy, seg = (uid / gy) % gx, b = uid / (gx * gy);
+  int h, seg, b;
+  if (k.um.mixed) {
+    seg = uid / k.um.units;
+    unit_to_bh(k.um, uid % k.um.units, &b, &h);
+  } else {
+    h = uid % gy;
+    seg = (uid / gy) % gx;
+    b = uid / (gx * gy);
+  }
   const int c0 = seg * k.seg_chunks;
   const int c1 = min(c0 + k.seg_chunks, k.ntiles);
   if (c0 >= c1) return;  // whole workgroup
@@ -837,10 +848,12 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(BK k) {
 __global__ __launch_bounds__(256) void seg_combine_bf16_kernel(float* __restrict__ seg_state,
                                                                const float* __restrict__ seg_decay,
                                                                const float* __restrict__ h0,
-                                                               int n_heads, int heads, int nseg) {
+                                                               int n_heads, int heads, int nseg,
+                                                               UnitMap um) {
   constexpr int PN = kP * kN;
   const int e = blockIdx.x * 256 + threadIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  int h = blockIdx.y, b = blockIdx.z;
+  if (um.mixed) unit_to_bh(um, blockIdx.y, &b, &h);
   const int64_t unit = (int64_t)b * heads + h;
   float H = h0 ? h0[((int64_t)b * n_heads + h) * PN + e] : 0.0f;
   float* base = seg_state + unit * nseg * PN + e;
@@ -882,7 +895,7 @@ bool bf16_path(int64_t d_head, int64_t d_state, int64_t chunk, int dtype) {
 }
 
 void fwd_plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int* ntiles, int* nseg,
-                   int* seg_tiles) {
+                   int* seg_tiles, int64_t units_in) {
   // Cost in units of one tile step of a workgroup (about 2.7 us on MI355X):
   // each round of up to kCus workgroups costs its walk plus ~2.5 tiles of
   // start-up (first loads from HBM, state in, pipeline fill and drain); the
@@ -890,7 +903,7 @@ void fwd_plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int* ntiles, in
   // and the two extra launches add ~3 tiles.
   constexpr int64_t kCus = 256;
   const int64_t n = (seqlen + kQ - 1) / kQ;
-  const int64_t units = batch * heads;
+  const int64_t units = units_in > 0 ? units_in : batch * heads;
   int64_t best_per = n > 0 ? n : 1, best_seg = 1;
   double best = 1e300;
   for (int64_t want = 1; want <= n; ++want) {
@@ -910,9 +923,9 @@ void fwd_plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int* ntiles, in
   *nseg = (int)best_seg;
 }
 
-size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads) {
+size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t units) {
   int nt, nseg, per;
-  fwd_plan_bf16(batch, seqlen, heads, &nt, &nseg, &per);
+  fwd_plan_bf16(batch, seqlen, heads, &nt, &nseg, &per, units);
   size_t bytes = frag_region_bytes(batch, seqlen) + dt_region_bytes(batch, seqlen, heads);
   if (nseg > 1) bytes += (size_t)(batch * heads * nseg) * (size_t)(kP * kN + 1) * sizeof(float);
   return bytes;
@@ -954,7 +967,10 @@ hipError_t launch_bf16(const FwdArgs& a, const FuseArgs& fu, void* ws, hipStream
   k.h0 = a.h0; k.hT = a.hT;
   k.cw = fu.w; k.cbias = fu.bias; k.cstate = fu.state; k.conv_dim = fu.conv_dim;
   k.seqlen = a.seqlen; k.n_heads = a.n_heads; k.heads = a.heads;
-  fwd_plan_bf16(a.batch, a.seqlen, a.heads, &k.ntiles, &k.nseg, &k.seg_chunks);
+  k.um = make_unit_map(a);
+  fwd_plan_bf16(a.batch, a.seqlen, a.heads, &k.ntiles, &k.nseg, &k.seg_chunks,
+                k.um.mixed ? k.um.units : 0);
+  if (k.um.mixed && k.um.units == 0) return hipSuccess;  // no active head anywhere
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   uint4* frags = reinterpret_cast<uint4*>(wsb);
   bf16* dtT = reinterpret_cast<bf16*>(wsb + frag_region_bytes(a.batch, a.seqlen));
@@ -975,15 +991,21 @@ hipError_t launch_bf16(const FwdArgs& a, const FuseArgs& fu, void* ws, hipStream
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (k.nseg > 1) {
     auto pre = ssd_bf16_kernel<false, FUSED>;
-    hipLaunchKernelGGL(pre, dim3(k.nseg - 1, a.heads, (unsigned)a.batch), dim3(kThreads), kLds, s, k);
+    const dim3 gpre = k.um.mixed ? dim3((unsigned)((k.nseg - 1) * k.um.units))
+                                 : dim3(k.nseg - 1, a.heads, (unsigned)a.batch);
+    hipLaunchKernelGGL(pre, gpre, dim3(kThreads), kLds, s, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     static_assert((kP * kN) % 256 == 0, "state elements split over 256-thread blocks");
-    hipLaunchKernelGGL(seg_combine_bf16_kernel, dim3(kP * kN / 256, a.heads, (unsigned)a.batch),
-                       dim3(256), 0, s, k.seg_state, k.seg_decay, a.h0, a.n_heads, a.heads, k.nseg);
+    const dim3 gcomb = k.um.mixed ? dim3(kP * kN / 256, (unsigned)k.um.units)
+                                  : dim3(kP * kN / 256, a.heads, (unsigned)a.batch);
+    hipLaunchKernelGGL(seg_combine_bf16_kernel, gcomb, dim3(256), 0, s, k.seg_state, k.seg_decay,
+                       a.h0, a.n_heads, a.heads, k.nseg, k.um);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   auto main_k = ssd_bf16_kernel<true, FUSED>;
-  hipLaunchKernelGGL(main_k, dim3(k.nseg, a.heads, (unsigned)a.batch), dim3(kThreads), kLds, s, k);
+  const dim3 gmain = k.um.mixed ? dim3((unsigned)(k.nseg * k.um.units))
+                                : dim3(k.nseg, a.heads, (unsigned)a.batch);
+  hipLaunchKernelGGL(main_k, gmain, dim3(kThreads), kLds, s, k);
   return hipGetLastError();
 }
 

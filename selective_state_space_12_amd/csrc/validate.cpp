@@ -135,6 +135,21 @@ int validate_ssd_forward(const void* x, int64_t x_row_stride, const void* dt,
   return MM_OK;
 }
 
+int validate_heads_per_seq(const int32_t* heads_per_seq, int64_t batch, int64_t n_heads,
+                           int64_t* max_heads) {
+  if (!heads_per_seq || !max_heads) return MM_ERR_NULL;
+  if (!pos(batch) || !pos(n_heads)) return MM_ERR_SHAPE;
+  if (batch > 256) return MM_ERR_UNSUPPORTED;
+  int64_t mx = 0;
+  for (int64_t b = 0; b < batch; ++b) {
+    const int64_t h = heads_per_seq[b];
+    if (h < 1 || h > n_heads) return MM_ERR_SLICE;
+    if (h > mx) mx = h;
+  }
+  *max_heads = mx;
+  return MM_OK;
+}
+
 int validate_ssd_forward_fused(const void* xbc, int64_t xbc_row_stride, const float* conv_w,
                                const float* conv_bias, const float* conv_state, const void* dt,
                                int64_t dt_row_stride, const float* dt_bias, int dt_softplus,

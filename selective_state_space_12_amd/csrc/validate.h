@@ -48,6 +48,11 @@ int validate_ssd_forward(const void* x, int64_t x_row_stride, const void* dt,
                          int64_t ngroups, int64_t n_heads_active, int64_t chunk,
                          int dtype);
 
+// Per-sequence head counts of a mixed scan call (host array): batch <= 256
+// entries, each in [1, n_heads].  On success *max_heads is the widest.
+int validate_heads_per_seq(const int32_t* heads_per_seq, int64_t batch, int64_t n_heads,
+                           int64_t* max_heads);
+
 int validate_ssd_forward_fused(const void* xbc, int64_t xbc_row_stride, const float* conv_w,
                                const float* conv_bias, const float* conv_state, const void* dt,
                                int64_t dt_row_stride, const float* dt_bias, int dt_softplus,

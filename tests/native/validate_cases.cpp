@@ -125,6 +125,18 @@ int main() {
   expect("norm null z", norm(P, nullptr, P3, 4096, F, 1e-5f, 4096, MM_BF16), MM_ERR_NULL);
   expect("norm dtype", norm(P, P2, P3, 4096, F, 1e-5f, 4096, 9), MM_ERR_DTYPE);
 
+  // per-sequence widths of a mixed scan call
+  {
+    int64_t mx = 0;
+    const int32_t ok4[4] = {16, 64, 32, 64}, zero[2] = {0, 3}, wide[2] = {3, 65};
+    expect("mixed ok", validate_heads_per_seq(ok4, 4, 64, &mx), MM_OK);
+    expect("mixed widest", (int)mx, 64);
+    expect("mixed null", validate_heads_per_seq(nullptr, 4, 64, &mx), MM_ERR_NULL);
+    expect("mixed 0 heads", validate_heads_per_seq(zero, 2, 64, &mx), MM_ERR_SLICE);
+    expect("mixed > n_heads", validate_heads_per_seq(wide, 2, 64, &mx), MM_ERR_SLICE);
+    expect("mixed batch 257", validate_heads_per_seq(ok4, 257, 64, &mx), MM_ERR_UNSUPPORTED);
+  }
+
   std::printf("%d failure(s)\n", failures);
   return failures == 0 ? 0 : 1;
 }
