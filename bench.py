@@ -527,10 +527,56 @@ def bench_decode(torch, mm, synth, dev):
     steps = reps * 64
     per_step_us = ms * 1e3 / steps
     by = decode_bytes(hv_cpu.tolist(), P, N, d.d_inner)
+    # speculative decoding at full width (64 heads, every sequence): verify 4
+    # draft tokens in one pass over the states (conv of the 4 tokens on a copy
+    # of the conv state, then mm_ssd_step_multi with no state write), commit
+    # each sequence's accepted prefix (mm_ssd_step_multi in place with the
+    # accepted counts, mm_conv_state_advance), against 4 single steps
+    kd = 4
+    xk = xbc_t[:kd].permute(1, 0, 2).contiguous()
+    dk = dt_t[:kd].permute(1, 0, 2).contiguous()
+    uk = torch.empty_like(xk)
+    yk = torch.empty((bsz, kd, H, P), device=dev)
+    cs_v = cstate.clone()
+    acc = torch.randint(0, kd + 1, (bsz,), generator=torch.Generator().manual_seed(5),
+                        dtype=torch.int32).to(dev)
+    di = d.d_inner
+
+    def verify():
+        cs_v.copy_(cstate)
+        mm.conv1d_silu(xk, cw, None, cs_v, d_inner=di, d_head=P, d_state=N, n_heads_active=H,
+                       out=uk)
+        mm.ssd_step_multi(state, uk[..., :di].view(bsz, kd, H, P), dk, A, uk[..., di:di + N],
+                          uk[..., di + N:], D, state_out=None, y=yk)
+
+    def commit():
+        mm.ssd_step_multi(state, uk[..., :di].view(bsz, kd, H, P), dk, A, uk[..., di:di + N],
+                          uk[..., di + N:], D, state_out=state, tokens_per_seq=acc, y=yk)
+        mm.conv_state_advance(cstate, xk, d_inner=di, d_head=P, d_state=N, tokens_per_seq=acc)
+
+    def four_steps():
+        for t in range(kd):
+            mm.ssd_step(state, uk[:, t, :di].view(bsz, H, P), dk[:, t], A, uk[:, t, di:di + N],
+                        uk[:, t, di + N:], D, y=yt)
+
+    def timed(fn, reps=20):
+        for _ in range(3):
+            fn()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    v_us, c_us, s_us = timed(verify), timed(commit), timed(four_steps)
     return {"workload": "decode: batch 256, 64 heads x 64 x 128 fp32 state, slices "
                         "round-robin {16,32,64} heads, 1024 tokens in a HIP graph",
             "tokens_per_s": bsz * steps / (ms * 1e-3), "us_per_step": per_step_us,
-            "bytes_per_step": by, "hbm_frac": by / (per_step_us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+            "bytes_per_step": by, "hbm_frac": by / (per_step_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+            "spec_decode": {"draft_tokens": kd, "heads": H, "verify_us": v_us, "commit_us": c_us,
+                            "four_single_steps_us": s_us,
+                            "verify_plus_commit_vs_steps": s_us / (v_us + c_us)}}
 
 
 def cpu_baseline(w):

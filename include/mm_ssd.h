@@ -335,6 +335,54 @@ int mm_ssd_step(float* state,
                 int64_t d_state, int64_t ngroups, int64_t n_heads_active,
                 const int32_t* heads_active_per_seq, int dtype, void* stream);
 
+/*
+ * ntok tokens per sequence in one pass over the states, for nested-draft
+ * speculative decoding ("MatMamba", deployment paragraph: a smaller nested
+ * slice drafts tokens that the larger model verifies).  For each active
+ * (sequence b, head h) -- h < h_b as in mm_ssd_step -- the state is read once
+ * from state_in, the sequence's first n_b tokens are applied in order with
+ * exactly mm_ssd_step's arithmetic (so the results equal n_b single steps bit
+ * for bit), y is written for those tokens, and the advanced state is written
+ * to state_out.  n_b = ntok, or tokens_per_seq[b] clamped to [0, ntok].
+ * Verify a draft with state_out = NULL (outputs only); commit its accepted
+ * prefix with state_out = state_in and tokens_per_seq = the accepted counts.
+ *   state_in (batch, n_heads, d_head, d_state) fp32; state_out the same
+ *       layout, equal to state_in, NULL, or not overlapping it.
+ *   x, dt, B, C, y: token rows, row b*ntok + t for token t of sequence b
+ *       (otherwise as in mm_ssd_step); rows past n_b are neither read nor
+ *       written.
+ *   heads_active_per_seq, tokens_per_seq: device int32 (batch) or NULL.
+ * Preconditions: those of mm_ssd_step; 1 <= ntok <= 64; d_head * d_state
+ * <= 8192 (MM_ERR_UNSUPPORTED otherwise).
+ */
+int mm_ssd_step_multi(const float* state_in, float* state_out,
+                      const void* x, int64_t x_row_stride,
+                      const void* dt, int64_t dt_row_stride,
+                      const float* A,
+                      const void* B, int64_t b_row_stride,
+                      const void* C, int64_t c_row_stride,
+                      const float* D,
+                      void* y, int64_t y_row_stride,
+                      int64_t batch, int64_t ntok, int64_t n_heads, int64_t d_head,
+                      int64_t d_state, int64_t ngroups, int64_t n_heads_active,
+                      const int32_t* heads_active_per_seq,
+                      const int32_t* tokens_per_seq, int dtype, void* stream);
+
+/*
+ * Conv state of each sequence advanced by its first n_b raw conv inputs
+ * (rows b*ntok + t of xbc; n_b = ntok, or tokens_per_seq[b] clamped to
+ * [0, ntok]): the new state is the last three of (old state, those inputs),
+ * for the active channels (x slice of n_heads_active heads, then every B and
+ * C channel) -- the commit half of mm_conv1d_silu's state update, for a
+ * draft's accepted prefix.  conv_state (batch, 3, conv_dim) fp32 in place.
+ * Preconditions: 1 <= ntok <= 64, batch <= 65535, d_inner a multiple of
+ * d_head, 1 <= n_heads_active <= d_inner / d_head, xbc_row_stride >= conv_dim.
+ */
+int mm_conv_state_advance(float* conv_state, const void* xbc, int64_t xbc_row_stride,
+                          int64_t batch, int64_t ntok, const int32_t* tokens_per_seq,
+                          int64_t d_inner, int64_t d_head, int64_t d_state, int64_t ngroups,
+                          int64_t n_heads_active, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -92,6 +92,13 @@ def lib() -> ctypes.CDLL:
                                                _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                                _i64, _vp, _i64, _int, _vp, ctypes.c_size_t, _vp]
             L.mm_ssd_forward_mixed.restype = _int
+            L.mm_ssd_step_multi.argtypes = [_vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp,
+                                            _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                            _i64, _i64, _vp, _vp, _int, _vp]
+            L.mm_ssd_step_multi.restype = _int
+            L.mm_conv_state_advance.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
+                                                _i64, _i64, _int, _vp]
+            L.mm_conv_state_advance.restype = _int
             L.mm_gated_rmsnorm.argtypes = [_vp, _i64, _vp, _i64, _vp, ctypes.c_float, _vp, _i64,
                                            _i64, _i64, _int, _vp]
             L.mm_gated_rmsnorm.restype = _int
@@ -424,6 +431,72 @@ def gated_rmsnorm(y: torch.Tensor, z: torch.Tensor, w: torch.Tensor, eps: float 
                                 rows, d, _dtype_code(y), _stream())
     _check("mm_gated_rmsnorm", st)
     return out
+
+
+def _dev_i32(t: Optional[torch.Tensor], name: str):
+    if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or t.device.type != "cuda"):
+        raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    return _ptr(t)
+
+
+def ssd_step_multi(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
+                   B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None, *,
+                   state_out: Optional[torch.Tensor] = None,
+                   n_heads_active: Optional[int] = None,
+                   heads_per_seq: Optional[torch.Tensor] = None,
+                   tokens_per_seq: Optional[torch.Tensor] = None,
+                   y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ntok decode tokens per sequence in one pass over the states.  x
+    (batch, ntok, n_heads, d_head), dt (batch, ntok, n_heads), B, C
+    (batch, ntok, [ngroups,] d_state).  state (batch, n_heads, d_head,
+    d_state) fp32 is read; the advanced state goes to state_out (pass the
+    state itself to update it in place; None: outputs only).  Returns y
+    (batch, ntok, n_heads, d_head); rows past a sequence's token count and
+    inactive heads are left untouched."""
+    batch, n_heads, d_head, d_state = state.shape
+    ntok = x.shape[1]
+    if B.dim() == 3:
+        B = B.unsqueeze(2)
+        C = C.unsqueeze(2)
+    ngroups = B.shape[2]
+    h_act = n_heads if n_heads_active is None else int(n_heads_active)
+    if y is None:
+        y = torch.empty((batch, ntok, n_heads, d_head), dtype=x.dtype, device=x.device)
+    for name, t in (("state", state), ("state_out", state_out)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 tensor")
+    xs = _row_stride(x, "x", (n_heads, d_head))
+    ys = _row_stride(y, "y", (n_heads, d_head))
+    dts = _row_stride(dt, "dt", (n_heads,))
+    bs = _row_stride(B, "B", (ngroups, d_state))
+    cs = _row_stride(C, "C", (ngroups, d_state))
+    st = lib().mm_ssd_step_multi(_ptr(state), _ptr(state_out), _ptr(x), xs, _ptr(dt), dts, _ptr(A),
+                                 _ptr(B), bs, _ptr(C), cs, _ptr(D), _ptr(y), ys, batch, ntok,
+                                 n_heads, d_head, d_state, ngroups, h_act,
+                                 _dev_i32(heads_per_seq, "heads_per_seq"),
+                                 _dev_i32(tokens_per_seq, "tokens_per_seq"), _dtype_code(x),
+                                 _stream())
+    _check("mm_ssd_step_multi", st)
+    return y
+
+
+def conv_state_advance(conv_state: torch.Tensor, xbc: torch.Tensor, *, d_inner: int, d_head: int,
+                       d_state: int, ngroups: int = 1, n_heads_active: Optional[int] = None,
+                       tokens_per_seq: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """conv_state (batch, 3, conv_dim) fp32 advanced in place by each
+    sequence's first tokens of xbc (batch, ntok, conv_dim) raw conv input."""
+    batch, ntok = xbc.shape[0], xbc.shape[1]
+    conv_dim = d_inner + 2 * ngroups * d_state
+    if conv_state.dtype != torch.float32 or not conv_state.is_contiguous() or \
+            tuple(conv_state.shape) != (batch, 3, conv_dim):
+        raise ValueError("conv_state must be a contiguous fp32 (batch, 3, conv_dim) tensor")
+    xs = _row_stride(xbc, "xbc", (conv_dim,))
+    h_act = d_inner // d_head if n_heads_active is None else int(n_heads_active)
+    st = lib().mm_conv_state_advance(_ptr(conv_state), _ptr(xbc), xs, batch, ntok,
+                                     _dev_i32(tokens_per_seq, "tokens_per_seq"), d_inner, d_head,
+                                     d_state, ngroups, h_act, _dtype_code(xbc), _stream())
+    _check("mm_conv_state_advance", st)
+    return conv_state
 
 
 def ssd_step(state: torch.Tensor, x_t: torch.Tensor, dt_t: torch.Tensor, A: torch.Tensor,

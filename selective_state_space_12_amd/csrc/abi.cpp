@@ -275,6 +275,66 @@ int mm_gated_rmsnorm(const void* y, int64_t y_row_stride, const void* z, int64_t
   return hip_status(launch_gated_rmsnorm(a, dtype, as_stream(stream)));
 }
 
+int mm_ssd_step_multi(const float* state_in, float* state_out, const void* x, int64_t x_row_stride,
+                      const void* dt, int64_t dt_row_stride, const float* A, const void* B,
+                      int64_t b_row_stride, const void* C, int64_t c_row_stride, const float* D,
+                      void* y, int64_t y_row_stride, int64_t batch, int64_t ntok,
+                      int64_t n_heads, int64_t d_head, int64_t d_state, int64_t ngroups,
+                      int64_t n_heads_active, const int32_t* heads_active_per_seq,
+                      const int32_t* tokens_per_seq, int dtype, void* stream) {
+  const int st = validate_ssd_step_multi(state_in, state_out, x, x_row_stride, dt, dt_row_stride,
+                                         A, B, b_row_stride, C, c_row_stride, y, y_row_stride,
+                                         batch, ntok, n_heads, d_head, d_state, ngroups,
+                                         n_heads_active, dtype);
+  if (st != MM_OK) return st;
+  StepMultiArgs a;
+  a.state_in = state_in;
+  a.state_out = state_out;
+  a.x = x;
+  a.xs = x_row_stride;
+  a.dt = dt;
+  a.dts = dt_row_stride;
+  a.A = A;
+  a.B = B;
+  a.bs = b_row_stride;
+  a.C = C;
+  a.cs = c_row_stride;
+  a.D = D;
+  a.y = y;
+  a.ys = y_row_stride;
+  a.batch = batch;
+  a.n_heads = (int)n_heads;
+  a.d_head = (int)d_head;
+  a.d_state = (int)d_state;
+  a.heads_cap = (int)n_heads_active;
+  a.heads_per_seq = heads_active_per_seq;
+  a.ntok = (int)ntok;
+  a.tokens_per_seq = tokens_per_seq;
+  return hip_status(launch_ssd_step_multi(a, dtype, as_stream(stream)));
+}
+
+int mm_conv_state_advance(float* conv_state, const void* xbc, int64_t xbc_row_stride,
+                          int64_t batch, int64_t ntok, const int32_t* tokens_per_seq,
+                          int64_t d_inner, int64_t d_head, int64_t d_state, int64_t ngroups,
+                          int64_t n_heads_active, int dtype, void* stream) {
+  const int st = validate_conv_state_advance(conv_state, xbc, xbc_row_stride, batch, ntok,
+                                             d_inner, d_head, d_state, ngroups, n_heads_active,
+                                             dtype);
+  if (st != MM_OK) return st;
+  ConvAdvanceArgs a;
+  a.conv_state = conv_state;
+  a.xbc = xbc;
+  a.xbcs = xbc_row_stride;
+  a.batch = batch;
+  a.ntok = (int)ntok;
+  a.tokens_per_seq = tokens_per_seq;
+  a.conv_dim = d_inner + 2 * ngroups * d_state;
+  a.xw = (int)(n_heads_active * d_head);
+  a.d_inner = (int)d_inner;
+  a.bc_dim = (int)(2 * ngroups * d_state);
+  return hip_status(launch_conv_state_advance(a, dtype, as_stream(stream)));
+}
+
 int mm_ssd_step(float* state, const void* x_t, int64_t x_row_stride, const void* dt_t,
                 int64_t dt_row_stride, const float* A, const void* B_t,
                 int64_t b_row_stride, const void* C_t, int64_t c_row_stride,

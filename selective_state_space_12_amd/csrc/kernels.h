@@ -47,6 +47,44 @@ struct StepArgs {
 
 hipError_t launch_ssd_step(const StepArgs& a, int dtype, hipStream_t s);
 
+// ntok tokens per sequence in one pass over the states (ssd_step.hip).
+struct StepMultiArgs {
+  const float* state_in;
+  float* state_out;  // may equal state_in, or NULL for outputs only
+  const void* x;
+  int64_t xs;
+  const void* dt;
+  int64_t dts;
+  const float* A;
+  const void* B;
+  int64_t bs;
+  const void* C;
+  int64_t cs;
+  const float* D;
+  void* y;
+  int64_t ys;
+  int64_t batch;
+  int n_heads, d_head, d_state;
+  int heads_cap;
+  const int32_t* heads_per_seq;   // device, nullable
+  int ntok;
+  const int32_t* tokens_per_seq;  // device, nullable
+};
+hipError_t launch_ssd_step_multi(const StepMultiArgs& a, int dtype, hipStream_t s);
+
+// Conv state advanced by each sequence's first tokens (ssd_step.hip).
+struct ConvAdvanceArgs {
+  float* conv_state;
+  const void* xbc;
+  int64_t xbcs;
+  int64_t batch;
+  int ntok;
+  const int32_t* tokens_per_seq;  // device, nullable
+  int64_t conv_dim;
+  int xw, d_inner, bc_dim;
+};
+hipError_t launch_conv_state_advance(const ConvAdvanceArgs& a, int dtype, hipStream_t s);
+
 // Per-sequence slices of a scan call (input-adaptive widths: each sequence
 // runs its own slice): the active (sequence, head) units, numbered sequence-major, with
 // start[b] the first unit of sequence b (start[batch] = units).  Passed by

@@ -87,6 +87,209 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(
   }
 }
 
+// k tokens per sequence in one pass over the states (speculative decoding:
+// verify a draft, then commit its accepted prefix): each workgroup reads its
+// (head, sequence) state once, applies the sequence's first ntok_b tokens in
+// order with exactly the single-step arithmetic, writes y for those tokens
+// and, when state_out is given, the advanced state (nontemporal stores; the
+// state read when ntok_b = 0).  Token t of sequence b is row b*k + t of x,
+// dt, B, C and y.  All rows of a workgroup's state fit in one pass
+// (P <= rows per pass x kUnroll), which the launch checks.  The per-token dot
+// products bound it (a 5-step butterfly per state row and token; loading all
+// tokens' inputs up front measured no faster), so up to 8 tokens the partial
+// sums are kept per token and reduced together: log2(k) stages that split
+// the tokens between partner lanes, then the remaining stages once.
+template <typename T, int LPR, int KMAX>  // KMAX > 0: tokens' dot products reduced together
+__global__ __launch_bounds__(kStepThreads) void ssd_steps_kernel(
+    const float* __restrict__ state_in, float* state_out, const T* __restrict__ x, int64_t xs,
+    const T* __restrict__ dt, int64_t dts, const float* __restrict__ A,
+    const T* __restrict__ Bt, int64_t bs, const T* __restrict__ Ct, int64_t cs,
+    const float* __restrict__ D, T* __restrict__ y, int64_t ys, int n_heads, int P,
+    int heads_cap, const int32_t* __restrict__ heads_per_seq, int k,
+    const int32_t* __restrict__ tokens_per_seq) {
+  constexpr int N = LPR * 4;
+  constexpr int kRowsPerPass = kStepThreads / LPR;
+  constexpr int kUnroll = 8;
+  static_assert(KMAX == 0 || (KMAX <= LPR && (KMAX & (KMAX - 1)) == 0), "tokens per lane group");
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  if (h >= clamp_heads(heads_per_seq, b, heads_cap)) return;
+  int ntok = k;
+  if (tokens_per_seq) ntok = min(max(tokens_per_seq[b], 0), k);
+
+  const int lane_in_row = threadIdx.x % LPR;
+  const int row_in_pass = threadIdx.x / LPR;
+  const int n0 = lane_in_row * 4;
+  const float Ah = A[h];
+  const float Dh = D ? D[h] : 0.0f;
+  const int64_t soff = ((int64_t)b * n_heads + h) * (int64_t)P * N;
+
+  f32x4 s[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int p = u * kRowsPerPass + row_in_pass;
+    if (p < P) s[u] = *reinterpret_cast<const f32x4*>(state_in + soff + (int64_t)p * N + n0);
+  }
+  auto load_tok = [&](int t, float (&bv)[4], float (&cv)[4], float& dtv, float (&xv)[kUnroll]) {
+    const int64_t row = (int64_t)b * k + t;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bv[j] = to_f32(Bt[row * bs + n0 + j]);
+      cv[j] = to_f32(Ct[row * cs + n0 + j]);
+    }
+    dtv = to_f32(dt[row * dts + h]);
+    const T* xrow = x + row * xs + (int64_t)h * P;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int p = u * kRowsPerPass + row_in_pass;
+      xv[u] = p < P ? to_f32(xrow[p]) : 0.0f;
+    }
+  };
+  // one token's update with the single step's arithmetic, in its order; the
+  // lane's part of y's dot product for each row
+  auto update = [&](float dtv, const float (&bv)[4], const float (&cv)[4],
+                    const float (&xv)[kUnroll], float (&part)[kUnroll]) {
+    const float alpha = exp2f(dtv * Ah * kLog2e);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float xd = dtv * xv[u];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[u][j] = fmaf(alpha, s[u][j], xd * bv[j]);
+      part[u] = s[u][0] * cv[0] + s[u][1] * cv[1] + s[u][2] * cv[2] + s[u][3] * cv[3];
+    }
+  };
+  if constexpr (KMAX > 0) {
+    // Token loop with local partial sums only, then one butterfly per row for
+    // all KMAX tokens: the first log2(KMAX) stages each hand half of a lane's
+    // tokens to its partner (the lane keeps the other half, adding the
+    // partner's value of the same token), the rest are the usual stages.
+    // Every sum adds the same operands in the same order as a single step.
+    float part[KMAX][kUnroll], xs0[KMAX][kUnroll];
+#pragma unroll
+    for (int t = 0; t < KMAX; ++t) {
+      float bv[4], cv[4], dtv = 0.0f, xv[kUnroll];
+      if (t < ntok) {
+        load_tok(t, bv, cv, dtv, xv);
+        update(dtv, bv, cv, xv, part[t]);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) xs0[t][u] = xv[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) part[t][u] = xs0[t][u] = 0.0f;
+      }
+    }
+    int tok = 0;  // token whose sum this lane ends up holding
+#pragma unroll
+    for (int cnt = KMAX, off = LPR / 2; cnt > 1; cnt >>= 1, off >>= 1) {
+      const int half = cnt / 2;
+      const bool hi = (lane_in_row & off) != 0;
+      if (hi) tok += half;
+#pragma unroll
+      for (int i = 0; i < half; ++i)
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const float mine = hi ? part[i + half][u] : part[i][u];
+          const float send = hi ? part[i][u] : part[i + half][u];
+          part[i][u] = mine + __shfl_xor(send, off, LPR);
+        }
+    }
+#pragma unroll
+    for (int off = LPR / (2 * KMAX); off >= 1; off >>= 1)
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) part[0][u] += __shfl_xor(part[0][u], off, LPR);
+    if ((lane_in_row & (LPR / KMAX - 1)) == 0 && tok < ntok) {
+      T* yrow = y + ((int64_t)b * k + tok) * ys + (int64_t)h * P;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int p = u * kRowsPerPass + row_in_pass;
+        float xv = 0.0f;
+#pragma unroll
+        for (int t = 0; t < KMAX; ++t) xv = t == tok ? xs0[t][u] : xv;
+        if (p < P) yrow[p] = from_f32<T>(part[0][u] + Dh * xv);
+      }
+    }
+  } else {
+    for (int t = 0; t < ntok; ++t) {
+      float bv[4], cv[4], dtv, xv[kUnroll], part[kUnroll];
+      load_tok(t, bv, cv, dtv, xv);
+      update(dtv, bv, cv, xv, part);
+      T* yrow = y + ((int64_t)b * k + t) * ys + (int64_t)h * P;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int p = u * kRowsPerPass + row_in_pass;
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) part[u] += __shfl_xor(part[u], m, LPR);
+        if (lane_in_row == 0 && p < P) yrow[p] = from_f32<T>(part[u] + Dh * xv[u]);
+      }
+    }
+  }
+  if (state_out) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int p = u * kRowsPerPass + row_in_pass;
+      if (p < P)
+        __builtin_nontemporal_store(s[u], reinterpret_cast<f32x4*>(state_out + soff + (int64_t)p * N + n0));
+    }
+  }
+}
+
+template <typename T, int LPR, int KMAX>
+void launch_multi_k(const StepMultiArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)a.heads_cap, (unsigned)a.batch);
+  hipLaunchKernelGGL((ssd_steps_kernel<T, LPR, KMAX>), grid, dim3(kStepThreads), 0, s, a.state_in,
+                     a.state_out, static_cast<const T*>(a.x), a.xs, static_cast<const T*>(a.dt),
+                     a.dts, a.A, static_cast<const T*>(a.B), a.bs, static_cast<const T*>(a.C),
+                     a.cs, a.D, static_cast<T*>(a.y), a.ys, a.n_heads, a.d_head, a.heads_cap,
+                     a.heads_per_seq, a.ntok, a.tokens_per_seq);
+}
+
+template <typename T, int LPR>
+hipError_t launch_multi_lpr(const StepMultiArgs& a, hipStream_t s) {
+  constexpr int kRowsMax = (kStepThreads / LPR) * 8;
+  if (a.d_head > kRowsMax) return hipErrorInvalidValue;
+  if (a.ntok <= 2 && LPR >= 2) launch_multi_k<T, LPR, 2>(a, s);
+  else if (a.ntok <= 4 && LPR >= 4) launch_multi_k<T, LPR, 4>(a, s);
+  else if (a.ntok <= 8 && LPR >= 8) launch_multi_k<T, LPR, (LPR >= 8 ? 8 : 1)>(a, s);
+  else launch_multi_k<T, LPR, 0>(a, s);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_multi_typed(const StepMultiArgs& a, hipStream_t s) {
+  switch (a.d_state) {
+    case 16: return launch_multi_lpr<T, 4>(a, s);
+    case 32: return launch_multi_lpr<T, 8>(a, s);
+    case 64: return launch_multi_lpr<T, 16>(a, s);
+    case 128: return launch_multi_lpr<T, 32>(a, s);
+    case 256: return launch_multi_lpr<T, 64>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// conv_state[b] advanced by the sequence's first ntok_b raw inputs (rows
+// b*k + t of xbc): the new state is the last three of (old state, those
+// inputs), active channels only (x slice of heads_cap heads, then B and C).
+template <typename T>
+__global__ __launch_bounds__(256) void conv_state_advance_kernel(
+    float* __restrict__ cstate, const T* __restrict__ xbc, int64_t xbcs, int k,
+    const int32_t* __restrict__ tokens_per_seq, int64_t conv_dim, int xw, int d_inner,
+    int bc_dim) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= xw + bc_dim) return;
+  const int64_t c = i < xw ? i : d_inner + (i - xw);
+  const int ntok = tokens_per_seq ? min(max(tokens_per_seq[b], 0), k) : k;
+  float* sp = cstate + (int64_t)b * 3 * conv_dim + c;
+  float v[3];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const int t = ntok - 3 + q;  // token index; below 0: the old state's slot t + 3
+    v[q] = t >= 0 ? to_f32(xbc[((int64_t)b * k + t) * xbcs + c]) : sp[(t + 3) * conv_dim];
+  }
+#pragma unroll
+  for (int q = 0; q < 3; ++q) sp[q * conv_dim] = v[q];
+}
+
 template <typename T, int LPR>
 hipError_t launch_lpr(const StepArgs& a, hipStream_t s) {
   dim3 grid((unsigned)a.heads_cap, (unsigned)a.batch);
@@ -115,6 +318,25 @@ hipError_t launch_typed(const StepArgs& a, hipStream_t s) {
 hipError_t launch_ssd_step(const StepArgs& a, int dtype, hipStream_t s) {
   if (dtype == MM_BF16) return launch_typed<bf16>(a, s);
   return launch_typed<float>(a, s);
+}
+
+hipError_t launch_ssd_step_multi(const StepMultiArgs& a, int dtype, hipStream_t s) {
+  if (dtype == MM_BF16) return launch_multi_typed<bf16>(a, s);
+  return launch_multi_typed<float>(a, s);
+}
+
+hipError_t launch_conv_state_advance(const ConvAdvanceArgs& a, int dtype, hipStream_t s) {
+  const int active = a.xw + a.bc_dim;
+  dim3 grid((unsigned)((active + 255) / 256), (unsigned)a.batch);
+  if (dtype == MM_BF16)
+    hipLaunchKernelGGL(conv_state_advance_kernel<bf16>, grid, dim3(256), 0, s, a.conv_state,
+                       static_cast<const bf16*>(a.xbc), a.xbcs, a.ntok, a.tokens_per_seq,
+                       a.conv_dim, a.xw, a.d_inner, a.bc_dim);
+  else
+    hipLaunchKernelGGL(conv_state_advance_kernel<float>, grid, dim3(256), 0, s, a.conv_state,
+                       static_cast<const float*>(a.xbc), a.xbcs, a.ntok, a.tokens_per_seq,
+                       a.conv_dim, a.xw, a.d_inner, a.bc_dim);
+  return hipGetLastError();
 }
 
 }  // namespace mmssd

@@ -216,6 +216,59 @@ int validate_gated_rmsnorm(const void* y, int64_t y_row_stride, const void* z,
   return MM_OK;
 }
 
+int validate_ssd_step_multi(const float* state_in, const float* state_out, const void* x_t,
+                            int64_t x_row_stride, const void* dt_t, int64_t dt_row_stride,
+                            const float* A, const void* B_t, int64_t b_row_stride,
+                            const void* C_t, int64_t c_row_stride, const void* y_t,
+                            int64_t y_row_stride, int64_t batch, int64_t ntok, int64_t n_heads,
+                            int64_t d_head, int64_t d_state, int64_t ngroups,
+                            int64_t n_heads_active, int dtype) {
+  if (ntok < 1 || ntok > 64) return MM_ERR_SHAPE;
+  if (!pos(batch) || !mul_ok(batch, ntok)) return MM_ERR_SHAPE;
+  // the state shape and alignment with batch sequences
+  int st = validate_ssd_step(state_in, x_t, x_row_stride, dt_t, dt_row_stride, A, B_t,
+                             b_row_stride, C_t, c_row_stride, y_t, y_row_stride, batch, n_heads,
+                             d_head, d_state, ngroups, n_heads_active, dtype);
+  if (st != MM_OK) return st;
+  // the token streams have batch * ntok rows
+  if (!mul_ok(batch * ntok, x_row_stride) || !mul_ok(batch * ntok, y_row_stride) ||
+      !mul_ok(batch * ntok, dt_row_stride) || !mul_ok(batch * ntok, b_row_stride) ||
+      !mul_ok(batch * ntok, c_row_stride))
+    return MM_ERR_SHAPE;
+  if (d_head * d_state > 8192) return MM_ERR_UNSUPPORTED;  // one pass over a state
+  if (reinterpret_cast<uintptr_t>(state_out) % 16 != 0) return MM_ERR_ALIGN;
+  if (state_out && state_out != state_in) {
+    const uintptr_t i0 = reinterpret_cast<uintptr_t>(state_in);
+    const uintptr_t bytes = uintptr_t(batch * n_heads * d_head * d_state) * sizeof(float);
+    const uintptr_t o0 = reinterpret_cast<uintptr_t>(state_out);
+    if (i0 < o0 + bytes && o0 < i0 + bytes) return MM_ERR_SHAPE;
+  }
+  return MM_OK;
+}
+
+int validate_conv_state_advance(const float* conv_state, const void* xbc, int64_t xbc_row_stride,
+                                int64_t batch, int64_t ntok, int64_t d_inner, int64_t d_head,
+                                int64_t d_state, int64_t ngroups, int64_t n_heads_active,
+                                int dtype) {
+  if (!conv_state || !xbc) return MM_ERR_NULL;
+  const int64_t el = dtype_bytes(dtype);
+  if (el == 0) return MM_ERR_DTYPE;
+  if (ntok < 1 || ntok > 64) return MM_ERR_SHAPE;
+  if (!pos(batch) || !pos(d_inner) || !pos(d_head) || !pos(d_state) || !pos(ngroups))
+    return MM_ERR_SHAPE;
+  if (batch > kMaxGridYZ || d_inner % d_head != 0) return MM_ERR_SHAPE;
+  const int64_t n_heads = d_inner / d_head;
+  if (n_heads_active < 1 || n_heads_active > n_heads) return MM_ERR_SLICE;
+  if (!mul_ok(ngroups, d_state)) return MM_ERR_SHAPE;
+  const int64_t conv_dim = d_inner + 2 * ngroups * d_state;
+  if (xbc_row_stride < conv_dim || !mul_ok(batch, ntok) || !mul_ok(batch * ntok, xbc_row_stride) ||
+      !mul_ok(batch * 3, conv_dim))
+    return MM_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(xbc) % el != 0 || reinterpret_cast<uintptr_t>(conv_state) % 4 != 0)
+    return MM_ERR_ALIGN;
+  return MM_OK;
+}
+
 int validate_ssd_step(const float* state, const void* x_t, int64_t x_row_stride,
                       const void* dt_t, int64_t dt_row_stride, const float* A,
                       const void* B_t, int64_t b_row_stride, const void* C_t,

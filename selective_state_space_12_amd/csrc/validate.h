@@ -66,6 +66,23 @@ int validate_gated_rmsnorm(const void* y, int64_t y_row_stride, const void* z,
                            int64_t z_row_stride, const float* w, float eps, const void* out,
                            int64_t out_row_stride, int64_t rows, int64_t d, int dtype);
 
+// mm_ssd_step_multi: the checks of validate_ssd_step for the states (batch
+// sequences) and for batch * ntok token rows, plus 1 <= ntok <= 64, d_head
+// within one state pass (d_head * d_state <= 8192) and state_out equal to
+// state_in, NULL, or disjoint from it.
+int validate_ssd_step_multi(const float* state_in, const float* state_out, const void* x_t,
+                            int64_t x_row_stride, const void* dt_t, int64_t dt_row_stride,
+                            const float* A, const void* B_t, int64_t b_row_stride,
+                            const void* C_t, int64_t c_row_stride, const void* y_t,
+                            int64_t y_row_stride, int64_t batch, int64_t ntok, int64_t n_heads,
+                            int64_t d_head, int64_t d_state, int64_t ngroups,
+                            int64_t n_heads_active, int dtype);
+
+int validate_conv_state_advance(const float* conv_state, const void* xbc, int64_t xbc_row_stride,
+                                int64_t batch, int64_t ntok, int64_t d_inner, int64_t d_head,
+                                int64_t d_state, int64_t ngroups, int64_t n_heads_active,
+                                int dtype);
+
 int validate_ssd_step(const float* state, const void* x_t, int64_t x_row_stride,
                       const void* dt_t, int64_t dt_row_stride, const float* A,
                       const void* B_t, int64_t b_row_stride, const void* C_t,
