@@ -137,6 +137,33 @@ int main() {
     expect("mixed batch 257", validate_heads_per_seq(ok4, 257, 64, &mx), MM_ERR_UNSUPPORTED);
   }
 
+  // multi-token decode step: 256 sequences x 4 tokens, 64 heads x 64 x 128
+  {
+    float* S2 = reinterpret_cast<float*>(uintptr_t(0x8000000000ull));
+    auto multi = [&](const float* out, int64_t ntok, int64_t P_, int64_t N_) {
+      return validate_ssd_step_multi(F, out, P, 64 * P_, P, 64, F, P, N_, P, N_, P2, 64 * P_, 256,
+                                     ntok, 64, P_, N_, 1, 64, MM_F32);
+    };
+    expect("multi ok", multi(nullptr, 4, 64, 128), MM_OK);
+    expect("multi in place", multi(F, 4, 64, 128), MM_OK);
+    expect("multi separate out", multi(S2, 4, 64, 128), MM_OK);
+    expect("multi out overlaps in", multi(F + 4, 4, 64, 128), MM_ERR_SHAPE);
+    expect("multi ntok 0", multi(nullptr, 0, 64, 128), MM_ERR_SHAPE);
+    expect("multi ntok 65", multi(nullptr, 65, 64, 128), MM_ERR_SHAPE);
+    expect("multi state too big for a pass", multi(nullptr, 4, 128, 128), MM_ERR_UNSUPPORTED);
+    expect("conv advance ok",
+           validate_conv_state_advance(F, P, cd, 256, 4, 4096, 64, 128, 1, 64, MM_F32), MM_OK);
+    expect("conv advance stride",
+           validate_conv_state_advance(F, P, cd - 4, 256, 4, 4096, 64, 128, 1, 64, MM_F32),
+           MM_ERR_SHAPE);
+    expect("conv advance heads",
+           validate_conv_state_advance(F, P, cd, 256, 4, 4096, 64, 128, 1, 65, MM_F32),
+           MM_ERR_SLICE);
+    expect("conv advance null",
+           validate_conv_state_advance(nullptr, P, cd, 256, 4, 4096, 64, 128, 1, 64, MM_F32),
+           MM_ERR_NULL);
+  }
+
   std::printf("%d failure(s)\n", failures);
   return failures == 0 ? 0 : 1;
 }
