@@ -14,7 +14,9 @@ results.  Every function states the passage it follows.
 
 Pins: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (brute force, closed forms, textbook routines,
-invariants) -- see the docstrings there.
+invariants) and, for the backward functions, ``tests/test_oracle_backward_pins.py``
+(finite differences of the pinned forward functions, a one-token closed form)
+-- see the docstrings there.
 """
 from __future__ import annotations
 
@@ -65,6 +67,10 @@ def _load():
             lib.oracle_ssd_step.restype = None
             lib.oracle_gated_rmsnorm.argtypes = [dp, dp, dp, ctypes.c_double, dp, i64, i64]
             lib.oracle_gated_rmsnorm.restype = None
+            lib.oracle_ssd_backward.argtypes = [dp] * 16 + [i64] * 6 + [ip]
+            lib.oracle_ssd_backward.restype = None
+            lib.oracle_conv1d_silu_backward.argtypes = [dp] * 9 + [i64] * 5 + [ip]
+            lib.oracle_conv1d_silu_backward.restype = None
             _lib = lib
     return _lib
 
@@ -196,6 +202,85 @@ def ssd_step(state, x_t, dt_t, A, B_t, C_t, D=None, *, heads_active=None):
                         _ptr(C_t), _ptr(D), _ptr(y), batch, n_heads, P, N, ngroups,
                         hv.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
     return y, st
+
+
+def ssd_backward(x, dt, A, B, C, D=None, h0=None, dy=None, dhT=None, *, heads_active=None):
+    """Gradients of L = sum(dy * y) + sum(dhT * h_final) for ssd_forward, by
+    reverse-mode differentiation of the recurrence token by token (the joint
+    training of the nested sub-blocks, MatMamba page, training paragraph,
+    needs the backward pass of every granularity; the chain rule is written
+    out in ``mm_oracle.c``).  Shapes as ssd_forward; dy like y, dhT like the
+    final state (None = 0).  Returns a dict with dx, ddt (NaN for inactive
+    heads), dA, dD (n_heads; NaN for heads active in no sequence), dB, dC
+    (batch, seqlen, ngroups, N; summed over the active heads of the group) and
+    dh0 (batch, n_heads, P, N; NaN for inactive heads)."""
+    lib = _load()
+    x = _f64(x)
+    batch, seqlen, n_heads, P = x.shape
+    dt = _f64(dt).reshape(batch, seqlen, n_heads)
+    B = _f64(B)
+    C = _f64(C)
+    if B.ndim == 3:
+        B = B[:, :, None, :]
+        C = C[:, :, None, :]
+    ngroups, N = B.shape[2], B.shape[3]
+    if n_heads % ngroups:
+        raise ValueError("n_heads must be a multiple of ngroups")
+    A = _f64(A).reshape(n_heads)
+    D = _f64(D)
+    if D is not None:
+        D = D.reshape(n_heads)
+    h0 = _f64(h0)
+    if h0 is not None:
+        h0 = h0.reshape(batch, n_heads, P, N)
+    dy = _f64(dy).reshape(batch, seqlen, n_heads, P)
+    dhT = _f64(dhT)
+    if dhT is not None:
+        dhT = dhT.reshape(batch, n_heads, P, N)
+    hv = _heads_vec(heads_active, batch, n_heads)
+    out = {
+        "dx": np.full((batch, seqlen, n_heads, P), np.nan),
+        "ddt": np.full((batch, seqlen, n_heads), np.nan),
+        "dA": np.full(n_heads, np.nan),
+        "dB": np.empty((batch, seqlen, ngroups, N)),
+        "dC": np.empty((batch, seqlen, ngroups, N)),
+        "dD": np.full(n_heads, np.nan),
+        "dh0": np.full((batch, n_heads, P, N), np.nan),
+    }
+    lib.oracle_ssd_backward(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+                            _ptr(dy), _ptr(dhT), _ptr(out["dx"]), _ptr(out["ddt"]),
+                            _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                            _ptr(out["dh0"]), batch, seqlen, n_heads, P, N, ngroups,
+                            hv.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    return out
+
+
+def conv1d_silu_backward(u, w, dout, bias=None, conv_state=None, *, d_inner, d_head,
+                         heads_active=None):
+    """Gradients of L = sum(dout * conv1d_silu(u)) (the returned new conv state
+    is not differentiated): du (batch, seqlen, conv_dim; NaN outside the
+    slice), dw (conv_dim, 4) and dbias (conv_dim) summed over the sequences in
+    which each channel is active (NaN for channels active in none), dstate
+    (batch, conv_dim, 3) for the given initial conv state (None without one).
+    Chain rule in ``mm_oracle.c``."""
+    lib = _load()
+    u = _f64(u)
+    batch, seqlen, conv_dim = u.shape
+    n_heads = d_inner // d_head
+    hv = _heads_vec(heads_active, batch, n_heads)
+    w = _f64(w).reshape(conv_dim, 4)
+    bias = _f64(bias)
+    st = None if conv_state is None else _f64(conv_state).reshape(batch, conv_dim, 3)
+    dout = _f64(dout).reshape(batch, seqlen, conv_dim)
+    du = np.full_like(u, np.nan)
+    dw = np.full((conv_dim, 4), np.nan)
+    db = np.full(conv_dim, np.nan)
+    dst = None if st is None else np.full((batch, conv_dim, 3), np.nan)
+    lib.oracle_conv1d_silu_backward(_ptr(u), _ptr(w), _ptr(bias), _ptr(st), _ptr(dout),
+                                    _ptr(du), _ptr(dw), _ptr(db), _ptr(dst), batch, seqlen,
+                                    conv_dim, d_inner, d_head,
+                                    hv.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    return {"du": du, "dw": dw, "dbias": db, "dstate": dst}
 
 
 def softplus(v):

@@ -43,6 +43,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 /* SiLU(v) = v * sigmoid(v), the nonlinearity the MatMamba block paragraph
  * names after the convolution. */
@@ -195,5 +196,206 @@ void oracle_gated_rmsnorm(const double* y, const double* z, const double* w, dou
     }
     const double inv = 1.0 / sqrt(ss / (double)d + eps);
     for (int64_t c = 0; c < d; ++c) o[c] = o[c] * inv * w[c];
+  }
+}
+
+/*
+ * Reverse-mode gradient of oracle_ssd_forward (the recurrence above, for
+ * training the nested sub-blocks jointly: MatMamba page, training paragraph,
+ * where the loss sums the outputs of every granularity and the gradients of
+ * the shared weights add up).  Given the cotangents dy of y and dhT of the
+ * final state (nullable = 0), with L = sum dy.y + sum dhT.h_final, the chain
+ * rule taken token by token backwards gives, with Gs = dL/dH_t accumulated:
+ *     Gs      += dy_t (outer) C_t                   (H_t feeds y_t)
+ *     dC_t    += H_t^T dy_t                         (summed over the group's heads)
+ *     dx_t     = dt_t Gs B_t + D_h dy_t
+ *     dB_t    += dt_t Gs^T x_t                      (summed over the group's heads)
+ *     ddt_t    = <Gs, A_h a_t H_{t-1} + x_t (outer) B_t>,   a_t = exp(dt_t A_h)
+ *     dA_h    += <Gs, dt_t a_t H_{t-1}>             (summed over sequences)
+ *     dD_h    += dy_t . x_t                         (summed over sequences)
+ *     Gs       = a_t Gs                             (now dL/dH_{t-1})
+ * and dh0 = Gs after the first token.  The forward states H_t of a unit are
+ * kept (seqlen + 1 of them) and walked backwards.
+ *
+ * Only active heads are read or written in dx, ddt, dh0; dA, dD (n_heads) are
+ * written for the heads active in at least one sequence; dB, dC (batch,
+ * seqlen, ngroups, N) are overwritten everywhere (0 where no head of the
+ * group is active).  dD, dh0 nullable.
+ */
+void oracle_ssd_backward(const double* x, const double* dt, const double* A,
+                         const double* B, const double* C, const double* D,
+                         const double* h0, const double* dy, const double* dhT,
+                         double* dx, double* ddt, double* dA, double* dB, double* dC,
+                         double* dD, double* dh0, int64_t batch, int64_t seqlen,
+                         int64_t n_heads, int64_t P, int64_t N, int64_t ngroups,
+                         const int64_t* heads_active) {
+  const int64_t heads_per_group = n_heads / ngroups;
+  const int64_t PN = P * N;
+  double* dA_bh = (double*)calloc((size_t)(batch * n_heads), sizeof(double));
+  double* dD_bh = (double*)calloc((size_t)(batch * n_heads), sizeof(double));
+  for (int64_t i = 0; i < batch * seqlen * ngroups * N; ++i) {
+    dB[i] = 0.0;
+    dC[i] = 0.0;
+  }
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t h = 0; h < n_heads; ++h) {
+      if (h >= heads_active[b]) continue;
+      const int64_t g = h / heads_per_group;
+      const int64_t unit = b * n_heads + h;
+      /* Hs[t+1] = state after token t; Hs[0] = initial state */
+      double* Hs = (double*)malloc((size_t)((seqlen + 1) * PN) * sizeof(double));
+      double* Gs = (double*)malloc((size_t)PN * sizeof(double));
+      for (int64_t i = 0; i < PN; ++i) Hs[i] = h0 ? h0[unit * PN + i] : 0.0;
+      for (int64_t t = 0; t < seqlen; ++t) {
+        const int64_t row = b * seqlen + t;
+        const double* xt = x + (row * n_heads + h) * P;
+        const double* Bt = B + (row * ngroups + g) * N;
+        const double d = dt[row * n_heads + h];
+        const double a = exp(d * A[h]);
+        const double* Hp = Hs + t * PN;
+        double* Hn = Hs + (t + 1) * PN;
+        for (int64_t p = 0; p < P; ++p)
+          for (int64_t n = 0; n < N; ++n)
+            Hn[p * N + n] = a * Hp[p * N + n] + d * xt[p] * Bt[n];
+      }
+      for (int64_t i = 0; i < PN; ++i) Gs[i] = dhT ? dhT[unit * PN + i] : 0.0;
+      const double Dh = D ? D[h] : 0.0;
+      double dA_acc = 0.0, dD_acc = 0.0;
+      for (int64_t t = seqlen - 1; t >= 0; --t) {
+        const int64_t row = b * seqlen + t;
+        const double* xt = x + (row * n_heads + h) * P;
+        const double* dyt = dy + (row * n_heads + h) * P;
+        const double* Bt = B + (row * ngroups + g) * N;
+        const double* Ct = C + (row * ngroups + g) * N;
+        double* dBt = dB + (row * ngroups + g) * N;
+        double* dCt = dC + (row * ngroups + g) * N;
+        const double d = dt[row * n_heads + h];
+        const double a = exp(d * A[h]);
+        const double* Hcur = Hs + (t + 1) * PN;
+        const double* Hprev = Hs + t * PN;
+        for (int64_t p = 0; p < P; ++p)
+          for (int64_t n = 0; n < N; ++n) Gs[p * N + n] += dyt[p] * Ct[n];
+        for (int64_t n = 0; n < N; ++n) {
+          double sc = 0.0, sb = 0.0;
+          for (int64_t p = 0; p < P; ++p) {
+            sc += Hcur[p * N + n] * dyt[p];
+            sb += Gs[p * N + n] * xt[p];
+          }
+#pragma omp atomic
+          dCt[n] += sc;
+#pragma omp atomic
+          dBt[n] += d * sb;
+        }
+        double sdt = 0.0, sda = 0.0;
+        for (int64_t p = 0; p < P; ++p) {
+          double gb = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            const double gv = Gs[p * N + n];
+            gb += gv * Bt[n];
+            sda += gv * Hprev[p * N + n];
+            sdt += gv * xt[p] * Bt[n];
+          }
+          dx[(row * n_heads + h) * P + p] = d * gb + Dh * dyt[p];
+          dD_acc += dyt[p] * xt[p];
+        }
+        /* d/d(dt) of a*Hprev + dt*x(outer)B, and d/dA of a = exp(dt*A) */
+        ddt[row * n_heads + h] = A[h] * a * sda + sdt;
+        dA_acc += d * a * sda;
+        for (int64_t i = 0; i < PN; ++i) Gs[i] *= a;
+      }
+      dA_bh[unit] = dA_acc;
+      dD_bh[unit] = dD_acc;
+      if (dh0)
+        for (int64_t i = 0; i < PN; ++i) dh0[unit * PN + i] = Gs[i];
+      free(Hs);
+      free(Gs);
+    }
+  }
+  for (int64_t h = 0; h < n_heads; ++h) {
+    int any = 0;
+    double sa = 0.0, sd = 0.0;
+    for (int64_t b = 0; b < batch; ++b) {
+      if (h >= heads_active[b]) continue;
+      any = 1;
+      sa += dA_bh[b * n_heads + h];
+      sd += dD_bh[b * n_heads + h];
+    }
+    if (!any) continue;
+    dA[h] = sa;
+    if (dD) dD[h] = sd;
+  }
+  free(dA_bh);
+  free(dD_bh);
+}
+
+/*
+ * Reverse-mode gradient of oracle_conv1d_silu for the cotangent dout of its
+ * output (the new conv state it returns is not differentiated).  With
+ * pre[t,c] as above and SiLU'(v) = s (1 + v (1 - s)), s = 1 / (1 + exp(-v)):
+ *     dpre[t,c]   = dout[t,c] SiLU'(pre[t,c])
+ *     du[tau,c]   = sum_k w[c,k] dpre[tau+3-k, c]     (0 <= tau+3-k < seqlen)
+ *     dw[c,k]    += sum_t dpre[t,c] u[t-3+k, c]        (u[<0] from the state or 0)
+ *     dbias[c]   += sum_t dpre[t,c]
+ *     dstate[c,j] = sum_k w[c,k] dpre[j-k, c]           (input u[j-3], j = 0..2)
+ * summed over the sequences in which channel c is active.  du and dstate are
+ * written for the active channels only; dw, dbias for channels active in at
+ * least one sequence.  bias, conv_state, dbias, dstate nullable (dstate
+ * needs conv_state's layout (batch, conv_dim, 3)).
+ */
+void oracle_conv1d_silu_backward(const double* u, const double* w, const double* bias,
+                                 const double* conv_state, const double* dout, double* du,
+                                 double* dw, double* dbias, double* dstate, int64_t batch,
+                                 int64_t seqlen, int64_t conv_dim, int64_t d_inner,
+                                 int64_t d_head, const int64_t* heads_active) {
+#pragma omp parallel for schedule(static)
+  for (int64_t c = 0; c < conv_dim; ++c) {
+    double* dpre = (double*)malloc((size_t)(seqlen > 0 ? seqlen : 1) * sizeof(double));
+    double sw[4] = {0.0, 0.0, 0.0, 0.0}, sbias = 0.0;
+    int any = 0;
+    for (int64_t b = 0; b < batch; ++b) {
+      if (c < d_inner && c >= heads_active[b] * d_head) continue;
+      any = 1;
+      double hist[3] = {0.0, 0.0, 0.0};
+      if (conv_state)
+        for (int k = 0; k < 3; ++k) hist[k] = conv_state[(b * conv_dim + c) * 3 + k];
+      for (int64_t t = 0; t < seqlen; ++t) {
+        double win[4];
+        for (int k = 0; k < 4; ++k) {
+          const int64_t tau = t - 3 + k;
+          win[k] = tau >= 0 ? u[(b * seqlen + tau) * conv_dim + c] : hist[tau + 3];
+        }
+        double pre = bias ? bias[c] : 0.0;
+        for (int k = 0; k < 4; ++k) pre += w[c * 4 + k] * win[k];
+        const double s = 1.0 / (1.0 + exp(-pre));
+        const double dp = dout[(b * seqlen + t) * conv_dim + c] * s * (1.0 + pre * (1.0 - s));
+        dpre[t] = dp;
+        for (int k = 0; k < 4; ++k) sw[k] += dp * win[k];
+        sbias += dp;
+      }
+      for (int64_t tau = 0; tau < seqlen; ++tau) {
+        double acc = 0.0;
+        for (int k = 0; k < 4; ++k) {
+          const int64_t t = tau + 3 - k;
+          if (t < seqlen) acc += w[c * 4 + k] * dpre[t];
+        }
+        du[(b * seqlen + tau) * conv_dim + c] = acc;
+      }
+      if (dstate) {
+        for (int j = 0; j < 3; ++j) {
+          double acc = 0.0;
+          for (int k = 0; k < 4; ++k) {
+            const int64_t t = j - k;
+            if (t >= 0 && t < seqlen) acc += w[c * 4 + k] * dpre[t];
+          }
+          dstate[(b * conv_dim + c) * 3 + j] = acc;
+        }
+      }
+    }
+    if (any) {
+      for (int k = 0; k < 4; ++k) dw[c * 4 + k] = sw[k];
+      if (dbias) dbias[c] = sbias;
+    }
+    free(dpre);
   }
 }
