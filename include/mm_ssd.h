@@ -383,6 +383,68 @@ int mm_conv_state_advance(float* conv_state, const void* xbc, int64_t xbc_row_st
                           int64_t d_inner, int64_t d_head, int64_t d_state, int64_t ngroups,
                           int64_t n_heads_active, int dtype, void* stream);
 
+/*
+ * Bytes of device workspace mm_ssd_backward needs: the state before every
+ * 64-token chunk and the final state of each active (sequence, head), in the
+ * storage dtype.  Same argument meaning and errors as mm_ssd_backward.
+ * Host only.
+ */
+int mm_ssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
+                                   int64_t d_head, int64_t d_state, int64_t ngroups,
+                                   int64_t n_heads_active, int dtype, size_t* bytes_out);
+
+/*
+ * Backward pass of mm_ssd_forward ("MatMamba", training paragraph: the
+ * nested granularities are trained jointly, one forward pass each, their
+ * gradients accumulated for a single parameter update).  Given the
+ * cotangents dy of y and dfinal_state of the final state, computes the
+ * gradients of L = sum(dy * y) + sum(dfinal_state * final_state) for the
+ * first n_heads_active heads:
+ *   x, dt, A, B, C, D, initial_state: the forward call's inputs, same layouts
+ *       and prefixes (D NULL = 0, initial_state NULL = 0).
+ *   dy (rows, dy_row_stride) dtype: first n_heads_active*d_head values read.
+ *   dfinal_state (batch, n_heads, d_head, d_state) fp32 or NULL (= 0).
+ *   dx (rows, dx_row_stride) dtype: first n_heads_active*d_head values of
+ *       each row written, the rest untouched.
+ *   ddt (rows, ddt_row_stride) dtype: first n_heads_active entries written.
+ *   dA (n_heads) fp32: first n_heads_active entries (sums over the batch).
+ *   dB, dC (rows, db_row_stride / dc_row_stride) fp32: ngroups*d_state
+ *       values per row, the sum over the active heads.
+ *   dD (n_heads) fp32 or NULL: first n_heads_active entries.
+ *   dinitial_state (batch, n_heads, d_head, d_state) fp32 or NULL: active
+ *       heads written.
+ *   accumulate: 0 overwrites the outputs above; 1 adds into them (the
+ *       joint training's accumulation over granularities: call once per
+ *       granularity with its n_heads_active and the cotangents of its pass).
+ *   workspace: at least mm_ssd_backward_workspace_size() bytes, 16-byte
+ *       aligned, not used concurrently by another call.
+ * dB, dC, dA and dD are sums formed with fp32 atomics, so their last bits can
+ * differ between runs; dx, ddt and dinitial_state are deterministic.
+ * Preconditions: those of mm_ssd_forward except chunk (the backward cuts
+ * 64-token chunks itself); (d_head, d_state) = (64, 64) or (64, 128) with
+ * MM_BF16, (32, 16) with MM_F32 (MM_ERR_UNSUPPORTED otherwise); row strides
+ * >= the row lengths above; dt, ddt aligned to their element, fp32 arrays to
+ * 4 bytes, token rows to 16 bytes (MM_ERR_ALIGN); accumulate 0 or 1 and no
+ * output overlapping an input or another output (MM_ERR_SHAPE).
+ */
+int mm_ssd_backward(const void* x, int64_t x_row_stride,
+                    const void* dt, int64_t dt_row_stride,
+                    const float* A,
+                    const void* B, int64_t b_row_stride,
+                    const void* C, int64_t c_row_stride,
+                    const float* D, const float* initial_state,
+                    const void* dy, int64_t dy_row_stride, const float* dfinal_state,
+                    void* dx, int64_t dx_row_stride,
+                    void* ddt, int64_t ddt_row_stride,
+                    float* dA,
+                    float* dB, int64_t db_row_stride,
+                    float* dC, int64_t dc_row_stride,
+                    float* dD, float* dinitial_state,
+                    int64_t batch, int64_t seqlen, int64_t n_heads,
+                    int64_t d_head, int64_t d_state, int64_t ngroups,
+                    int64_t n_heads_active, int dtype, int accumulate,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

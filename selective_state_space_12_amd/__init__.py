@@ -106,6 +106,14 @@ def lib() -> ctypes.CDLL:
                                       _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                       _vp, _int, _vp]
             L.mm_ssd_step.restype = _int
+            L.mm_ssd_backward_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                                         _int, ctypes.POINTER(ctypes.c_size_t)]
+            L.mm_ssd_backward_workspace_size.restype = _int
+            L.mm_ssd_backward.argtypes = ([_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
+                                           _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _vp,
+                                           _i64, _vp, _i64, _vp, _vp] + [_i64] * 7
+                                          + [_int, _int, _vp, ctypes.c_size_t, _vp])
+            L.mm_ssd_backward.restype = _int
             _lib = L
     return _lib
 
@@ -260,6 +268,94 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
                               code, _ptr(workspace), wbytes, _stream())
     _check("mm_ssd_forward", st)
     return y
+
+
+def ssd_backward_workspace_size(batch: int, seqlen: int, n_heads: int, d_head: int,
+                                d_state: int, ngroups: int, n_heads_active: int,
+                                dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    code = MM_F32 if dtype == torch.float32 else MM_BF16
+    _check("mm_ssd_backward_workspace_size",
+           lib().mm_ssd_backward_workspace_size(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                                n_heads_active, code, ctypes.byref(out)))
+    return out.value
+
+
+def ssd_backward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                 C: torch.Tensor, D: Optional[torch.Tensor], dy: torch.Tensor, *,
+                 n_heads_active: Optional[int] = None,
+                 initial_state: Optional[torch.Tensor] = None,
+                 dfinal_state: Optional[torch.Tensor] = None,
+                 grads: Optional[dict] = None, accumulate: bool = False,
+                 want_dD: bool = True, want_dinitial: bool = False,
+                 workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of sum(dy * y) + sum(dfinal_state * final_state) for
+    ssd_forward over heads [0, n_heads_active).  Inputs as ssd_forward; dy
+    like y (batch, seqlen, n_heads or n_heads_active, d_head).  Returns a dict
+    of dx, ddt (x's dtype, shaped like x and dt: inactive heads of a new
+    tensor are uninitialised), dA, dD (n_heads fp32), dB, dC (batch, seqlen,
+    ngroups, d_state fp32) and dinitial_state (batch, n_heads, d_head,
+    d_state fp32) if asked.  `grads` may hold any of these buffers to write
+    (or, with accumulate=True, add) into."""
+    batch, seqlen, n_heads, d_head = x.shape
+    if B.dim() == 3:
+        B = B.unsqueeze(2)
+        C = C.unsqueeze(2)
+    ngroups, d_state = B.shape[2], B.shape[3]
+    h_act = n_heads if n_heads_active is None else int(n_heads_active)
+    code = _dtype_code(x)
+    dev = x.device
+    g = dict(grads or {})
+    if "dx" not in g:
+        g["dx"] = torch.empty((batch, seqlen, n_heads, d_head), dtype=x.dtype, device=dev)
+    if "ddt" not in g:
+        g["ddt"] = torch.empty((batch, seqlen, n_heads), dtype=x.dtype, device=dev)
+    for k, shape in (("dA", (n_heads,)), ("dB", (batch, seqlen, ngroups, d_state)),
+                     ("dC", (batch, seqlen, ngroups, d_state))):
+        if k not in g:
+            g[k] = torch.empty(shape, dtype=torch.float32, device=dev)
+    if want_dD and "dD" not in g:
+        g["dD"] = torch.empty(n_heads, dtype=torch.float32, device=dev)
+    if want_dinitial and "dinitial_state" not in g:
+        g["dinitial_state"] = torch.empty((batch, n_heads, d_head, d_state), dtype=torch.float32,
+                                          device=dev)
+    for name, t in (("dt", dt), ("B", B), ("C", C), ("dy", dy), ("dx", g["dx"]),
+                    ("ddt", g["ddt"])):
+        if t.dtype != x.dtype:
+            raise TypeError(f"{name} must have x's dtype")
+    xs = _row_stride(x, "x", (n_heads, d_head))
+    dys = _row_stride(dy, "dy", (dy.shape[2], d_head))
+    dxs = _row_stride(g["dx"], "dx", (g["dx"].shape[2], d_head))
+    dts = _row_stride(dt, "dt", (n_heads,))
+    ddts = _row_stride(g["ddt"], "ddt", (g["ddt"].shape[2],))
+    bs = _row_stride(B, "B", (ngroups, d_state))
+    cs = _row_stride(C, "C", (ngroups, d_state))
+    dbs = _row_stride(g["dB"], "dB", (ngroups, d_state))
+    dcs = _row_stride(g["dC"], "dC", (ngroups, d_state))
+    for name, t in (("A", A), ("D", D), ("initial_state", initial_state),
+                    ("dfinal_state", dfinal_state), ("dA", g["dA"]), ("dB", g["dB"]),
+                    ("dC", g["dC"]), ("dD", g.get("dD")), ("dinitial_state", g.get("dinitial_state"))):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be fp32")
+    for name, t in (("A", A), ("D", D), ("initial_state", initial_state),
+                    ("dfinal_state", dfinal_state), ("dA", g["dA"]), ("dD", g.get("dD")),
+                    ("dinitial_state", g.get("dinitial_state"))):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    need = ssd_backward_workspace_size(batch, seqlen, n_heads, d_head, d_state, ngroups, h_act,
+                                       x.dtype)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib().mm_ssd_backward(_ptr(x), xs, _ptr(dt), dts, _ptr(A), _ptr(B), bs, _ptr(C), cs,
+                               _ptr(D), _ptr(initial_state), _ptr(dy), dys, _ptr(dfinal_state),
+                               _ptr(g["dx"]), dxs, _ptr(g["ddt"]), ddts, _ptr(g["dA"]),
+                               _ptr(g["dB"]), dbs, _ptr(g["dC"]), dcs, _ptr(g.get("dD")),
+                               _ptr(g.get("dinitial_state")), batch, seqlen, n_heads, d_head,
+                               d_state, ngroups, h_act, code, int(bool(accumulate)),
+                               _ptr(workspace), wbytes, _stream())
+    _check("mm_ssd_backward", st)
+    return g
 
 
 def _host_heads(heads_per_seq, batch: int):

@@ -335,6 +335,73 @@ int mm_conv_state_advance(float* conv_state, const void* xbc, int64_t xbc_row_st
   return hip_status(launch_conv_state_advance(a, dtype, as_stream(stream)));
 }
 
+int mm_ssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
+                                   int64_t d_head, int64_t d_state, int64_t ngroups,
+                                   int64_t n_heads_active, int dtype, size_t* bytes_out) {
+  if (!bytes_out) return MM_ERR_NULL;
+  const int st = validate_ssd_backward_shape(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                             n_heads_active, dtype);
+  if (st != MM_OK) return st;
+  *bytes_out = bwd_workspace_bytes(batch, seqlen, n_heads_active, d_head, d_state, dtype);
+  return MM_OK;
+}
+
+int mm_ssd_backward(const void* x, int64_t x_row_stride, const void* dt, int64_t dt_row_stride,
+                    const float* A, const void* B, int64_t b_row_stride, const void* C,
+                    int64_t c_row_stride, const float* D, const float* initial_state,
+                    const void* dy, int64_t dy_row_stride, const float* dfinal_state, void* dx,
+                    int64_t dx_row_stride, void* ddt, int64_t ddt_row_stride, float* dA,
+                    float* dB, int64_t db_row_stride, float* dC, int64_t dc_row_stride,
+                    float* dD, float* dinitial_state, int64_t batch, int64_t seqlen,
+                    int64_t n_heads, int64_t d_head, int64_t d_state, int64_t ngroups,
+                    int64_t n_heads_active, int dtype, int accumulate, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const int st = validate_ssd_backward(
+      x, x_row_stride, dt, dt_row_stride, A, B, b_row_stride, C, c_row_stride, D, initial_state,
+      dy, dy_row_stride, dfinal_state, dx, dx_row_stride, ddt, ddt_row_stride, dA, dB,
+      db_row_stride, dC, dc_row_stride, dD, dinitial_state, batch, seqlen, n_heads, d_head,
+      d_state, ngroups, n_heads_active, dtype, accumulate);
+  if (st != MM_OK) return st;
+  const size_t need = bwd_workspace_bytes(batch, seqlen, n_heads_active, d_head, d_state, dtype);
+  if (!workspace || workspace_bytes < need) return MM_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return MM_ERR_ALIGN;
+  BwdArgs a;
+  a.x = x;
+  a.xs = x_row_stride;
+  a.dt = dt;
+  a.dts = dt_row_stride;
+  a.A = A;
+  a.B = B;
+  a.bs = b_row_stride;
+  a.C = C;
+  a.cs = c_row_stride;
+  a.D = D;
+  a.h0 = initial_state;
+  a.dy = dy;
+  a.dys = dy_row_stride;
+  a.dhT = dfinal_state;
+  a.dx = dx;
+  a.dxs = dx_row_stride;
+  a.ddt = ddt;
+  a.ddts = ddt_row_stride;
+  a.dA = dA;
+  a.dB = dB;
+  a.dbs = db_row_stride;
+  a.dC = dC;
+  a.dcs = dc_row_stride;
+  a.dD = dD;
+  a.dh0 = dinitial_state;
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.n_heads = (int)n_heads;
+  a.d_head = (int)d_head;
+  a.d_state = (int)d_state;
+  a.heads = (int)n_heads_active;
+  a.dtype = dtype;
+  a.accumulate = accumulate;
+  return hip_status(launch_ssd_backward(a, workspace, as_stream(stream)));
+}
+
 int mm_ssd_step(float* state, const void* x_t, int64_t x_row_stride, const void* dt_t,
                 int64_t dt_row_stride, const float* A, const void* B_t,
                 int64_t b_row_stride, const void* C_t, int64_t c_row_stride,

@@ -219,4 +219,41 @@ size_t fused_workspace_bytes(int64_t batch, int64_t seqlen, int64_t n_heads, int
                              int64_t d_head, int64_t d_state, int64_t chunk, int dtype);
 hipError_t launch_ssd_forward_fused(const FusedCall& f, void* workspace, hipStream_t s);
 
+// Scan backward (ssd_bwd.hip): gradients of L = sum dy.y + sum dhT.h_final.
+struct BwdArgs {
+  const void* x;
+  int64_t xs;
+  const void* dt;
+  int64_t dts;
+  const float* A;
+  const void* B;
+  int64_t bs;
+  const void* C;
+  int64_t cs;
+  const float* D;
+  const float* h0;
+  const void* dy;
+  int64_t dys;
+  const float* dhT;
+  void* dx;
+  int64_t dxs;
+  void* ddt;
+  int64_t ddts;
+  float* dA;
+  float* dB;
+  int64_t dbs;
+  float* dC;
+  int64_t dcs;
+  float* dD;
+  float* dh0;
+  int64_t batch, seqlen;
+  int n_heads, d_head, d_state, heads, dtype, accumulate;
+};
+bool bwd_shape_supported(int64_t d_head, int64_t d_state, int dtype);
+// Workspace: the state before every 64-token chunk and the final state, per
+// active (sequence, head), in the storage type.
+size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
+                           int64_t d_state, int dtype);
+hipError_t launch_ssd_backward(const BwdArgs& a, void* workspace, hipStream_t s);
+
 }  // namespace mmssd

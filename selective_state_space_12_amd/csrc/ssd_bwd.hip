@@ -1,0 +1,815 @@
+// Chunked selective scan (SSD) backward over the first `heads` heads.
+//
+// "MatMamba: A Matryoshka State Space Model", training paragraph: the nested
+// granularities are trained jointly, one forward pass per granularity with
+// the gradients of the shared weights accumulated, and a single backward
+// pass; a sub-block uses A[0:h_i] and the first h_i heads of x (nesting
+// paragraph).  This file is the backward pass of the scan of one granularity:
+// given the cotangents dy (and dhT of the final state) it produces dx, ddt,
+// dA, dB, dC, dD and dh0 of L = sum dy.y + sum dhT.h_final, and can add them
+// into existing gradients so that the granularities' passes accumulate.
+//
+// Chunk algebra (chunk of Q tokens, Lambda_t = sum_{r<=t} dt_r A inclusive,
+// e = last token, Gc = dL/dH at the chunk's end, Hp = state before it):
+//   g_s   = sum_{t>=s} exp(Lambda_t - Lambda_s) dy_t C_t^T + exp(Lambda_e - Lambda_s) Gc
+//           (dL/dH_s, never formed; every term below is a product with it)
+//   u_s   = g_s B_s = sum_{t>=s} exp(..)(C_t . B_s) dy_t + exp(..) Gc B_s        (P)
+//   dx_s  = dt_s u_s + D dy_s,     ddt_s = x_s . u_s + A da_s
+//   dB_s  = dt_s g_s^T x_s = dt_s [sum_{t>=s} exp(..)(dy_t . x_s) C_t + exp(..) Gc^T x_s]
+//   dC_t  = h_t^T dy_t = exp(Lambda_t) Hp^T dy_t + sum_{s<=t} exp(..) dt_s (dy_t . x_s) B_s
+//   dGp   = exp(Lambda_e) Gc + sum_t exp(Lambda_t) dy_t C_t^T       (carried to the chunk before)
+// and, differentiating the exponents, dLambda_t =
+//     exp(Lambda_t) dy_t . Hp C_t                                  (off-diagonal output)
+//   + sum_{s<=t} W[t,s] - sum_{t'>=t} W[t',t]                      (diagonal block)
+//   - dt_t exp(Lambda_e - Lambda_t) x_t^T Gc B_t + [t = e] <Gc, H_e> (the chunk's end state)
+// with W[t,s] = exp(Lambda_t - Lambda_s)(C_t . B_s) dt_s (dy_t . x_s); then
+// da_r = sum_{t>=r} dLambda_t, ddt_r gets A da_r, dA_h = sum_r dt_r da_r.
+//
+// MI355X design (gfx950, 64-wide waves, 16x16x32 bf16 / 16x16x4 fp32 MFMA):
+//  - bwd_state_kernel: one workgroup per (sequence, head) walks the chunks
+//    forward with the fp32 state in MFMA accumulators and stores the state
+//    before every chunk (and the final one) in the storage type to the
+//    workspace: the backward walk needs them in reverse order.
+//  - bwd_chunk_kernel: one workgroup of 8 waves per (sequence, head) walks the
+//    chunks backwards with dL/dH (P x N fp32) in accumulators.  Per chunk the
+//    x, dy, B, C rows are staged in LDS in token-major form plus the
+//    transposed copies the K = token products need, Hp (from the workspace)
+//    and the bf16/fp32 operand copies of Gc.  Waves 0-3 own one 16-token
+//    s-block each (dx, dB, the column sums of W), waves 4-7 one 16-token
+//    t-block each (dC, the first dLambda term); the causal work of an
+//    s-block grows as that of the matching t-block shrinks, and wave w and
+//    w+4 share a SIMD.  Every wave updates its tiles of dL/dH.  The Q x Q
+//    products are formed transposed where needed so that their accumulators
+//    are directly the A operand of the next product (the masked decay applied
+//    in registers), as in the forward kernel.
+//  - dB and dC are sums over heads: fp32 atomics into the caller's buffers
+//    (zeroed by a fill kernel unless the call accumulates); dA and dD are sums
+//    over sequences, one atomic per workgroup.
+#include "device_common.h"
+#include "kernels.h"
+#include "../../include/mm_ssd.h"
+
+namespace mmssd {
+
+namespace {
+
+constexpr int kBQ = 64;  // tokens per backward chunk
+constexpr int kBWaves = 8;
+constexpr int kBThreads = kBWaves * 64;
+constexpr int kXcds = 8;
+
+struct BwdK {
+  const void* x;
+  int64_t xs;
+  const void* dt;
+  int64_t dts;
+  const float* A;
+  const void* B;
+  int64_t bs;
+  const void* C;
+  int64_t cs;
+  const float* D;
+  const float* h0;
+  const void* dy;
+  int64_t dys;
+  const float* dhT;
+  void* dx;
+  int64_t dxs;
+  void* ddt;
+  int64_t ddts;
+  float* dA;
+  float* dB;
+  int64_t dbs;
+  float* dC;
+  int64_t dcs;
+  float* dD;
+  float* dh0;
+  void* hst;  // (batch, heads, nchunks + 1, P, N) storage type
+  int64_t seqlen;
+  int n_heads, heads, nchunks, accumulate;
+};
+
+template <typename T> constexpr int bpad() { return 16 / (int)sizeof(T); }
+
+// (sequence, head) of this workgroup: consecutive units on one XCD so that
+// the heads of a sequence share its B and C rows in that XCD's L2.
+__device__ __forceinline__ void unit_of(int heads, int* b, int* h) {
+  const int total = gridDim.x;
+  const int pid = blockIdx.x;
+  const int uid = total % kXcds == 0 ? (pid % kXcds) * (total / kXcds) + pid / kXcds : pid;
+  *b = uid / heads;
+  *h = uid % heads;
+}
+
+// Eight consecutive elements at p[k0..k0+7] when k0 < K, else zeros.
+template <typename T>
+__device__ __forceinline__ void frag_row(Frag8<T>& f, const T* p, int k0, int K) {
+  if (k0 < K) frag_load8(f, p + k0);
+  else frag_zero(f);
+}
+
+// Same, every element multiplied by s.
+template <typename T>
+__device__ __forceinline__ void frag_row_scaled(Frag8<T>& f, const T* p, int k0, int K, float s) {
+  if (k0 < K) {
+    Frag8<T> r;
+    frag_load8(r, p + k0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) frag_set(f, j, to_f32(r.v[j]) * s);
+  } else {
+    frag_zero(f);
+  }
+}
+
+// Inclusive cumsum of dt*A*log2(e) over the chunk (wave 0, one token per
+// lane; tokens >= len take dt = 0 so Lambda stays at its end value).
+__device__ __forceinline__ float chunk_cumsum(float a, int lane) {
+  float incl = a;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  return incl;
+}
+
+template <typename T, int P, int N>
+struct StateLds {
+  static constexpr int TQ = kBQ + bpad<T>();  // pitch of the transposed x and B rows
+  static constexpr size_t bytes = (size_t)(P + N) * TQ * sizeof(T) + 2 * kBQ * sizeof(float);
+};
+
+// Forward walk storing the state before every chunk and the final state.
+template <typename T, int P, int N>
+__global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
+  using L = StateLds<T, P, N>;
+  constexpr int Q = kBQ, TQ = L::TQ;
+  constexpr int TP = P / 16, TN = N / 16, NTILE = TP * TN;
+  constexpr int TPW = NTILE >= kBWaves ? NTILE / kBWaves : 1;
+  static_assert(NTILE < kBWaves || NTILE % kBWaves == 0, "state tiles must split evenly");
+  static_assert(TP % TPW == 0, "a wave's state tiles share one column block");
+  constexpr int VB = 16 / (int)sizeof(T);
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* XT = reinterpret_cast<T*>(smem);
+  T* BT = XT + P * TQ;
+  float* lam = reinterpret_cast<float*>(BT + N * TQ);
+  float* wsc = lam + Q;
+
+  int b, h;
+  unit_of(k.heads, &b, &h);
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int r16 = lane % 16, g = lane / 16;
+  const T* __restrict__ Xp = static_cast<const T*>(k.x);
+  const T* __restrict__ DTp = static_cast<const T*>(k.dt);
+  const T* __restrict__ Bp = static_cast<const T*>(k.B);
+  T* __restrict__ Hst = static_cast<T*>(k.hst) + ((int64_t)b * k.heads + h) * (k.nchunks + 1) * (P * N);
+  const int64_t rowb = (int64_t)b * k.seqlen;
+  const float Ah2 = k.A[h] * kLog2e;
+
+  const int tile0 = wave * TPW;
+  const bool owns = tile0 < NTILE;
+  const int nt = tile0 / TP, pt0 = tile0 % TP;
+  f32x4 hacc[TPW];
+  const float* hin = k.h0 ? k.h0 + ((int64_t)b * k.n_heads + h) * (P * N) : nullptr;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      hacc[t][i] = (hin && owns) ? hin[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] : 0.0f;
+
+  auto store_state = [&](int c) {
+    if (!owns) return;
+    T* dst = Hst + (int64_t)c * (P * N);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dst[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] = from_f32<T>(hacc[t][i]);
+  };
+
+  for (int c = 0; c < k.nchunks; ++c) {
+    const int64_t row0 = rowb + (int64_t)c * Q;
+    const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
+    store_state(c);
+    // x^T and B^T: consecutive lanes take consecutive tokens (distinct banks)
+    for (int idx = tid; idx < Q * (P / VB); idx += kBThreads) {
+      const int s = idx % Q, p0 = (idx / Q) * VB;
+      const Vec16<T> v = s < len ? load16(Xp + (row0 + s) * k.xs + (int64_t)h * P + p0) : zero16<T>();
+#pragma unroll
+      for (int j = 0; j < VB; ++j) XT[(p0 + j) * TQ + s] = v.v[j];
+    }
+    for (int idx = tid; idx < Q * (N / VB); idx += kBThreads) {
+      const int s = idx % Q, n0 = (idx / Q) * VB;
+      const Vec16<T> v = s < len ? load16(Bp + (row0 + s) * k.bs + n0) : zero16<T>();
+#pragma unroll
+      for (int j = 0; j < VB; ++j) BT[(n0 + j) * TQ + s] = v.v[j];
+    }
+    if (wave == 0) {
+      const float d = lane < len ? to_f32(DTp[(row0 + lane) * k.dts + h]) : 0.0f;
+      const float lv = chunk_cumsum(d * Ah2, lane);
+      const float le = __shfl(lv, 63);
+      lam[lane] = lv;
+      wsc[lane] = __builtin_amdgcn_exp2f(le - lv) * d;
+    }
+    __syncthreads();
+    if (owns) {
+      const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hacc[t][i] *= dec;
+#pragma unroll
+      for (int ks = 0; ks < Q / 32; ++ks) {
+        const int s0 = ks * 32 + g * 8;
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(wsc + s0);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wsc + s0 + 4);
+        Frag8<T> bf;
+        frag_load8(bf, BT + (nt * 16 + r16) * TQ + s0);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          Frag8<T> xr, xf;
+          frag_load8(xr, XT + ((pt0 + t) * 16 + r16) * TQ + s0);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) frag_set(xf, j, to_f32(xr.v[j]) * (j < 4 ? w0[j] : w1[j - 4]));
+          hacc[t] = mma(xf, bf, hacc[t]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  store_state(k.nchunks);
+}
+
+template <typename T, int P, int N>
+struct ChunkLds {
+  static constexpr int NP = P + bpad<T>();   // token-major x and dy rows
+  static constexpr int NN = N + bpad<T>();   // token-major B and C rows, Gc rows (p-major)
+  static constexpr int TQ = kBQ + bpad<T>(); // transposed dy, B, C rows
+  static constexpr int TP2 = P + bpad<T>();  // Gc^T and Hp^T rows (n-major)
+  static constexpr size_t elems = (size_t)2 * kBQ * NP + (size_t)P * TQ + (size_t)2 * kBQ * NN +
+                                  (size_t)2 * N * TQ + (size_t)P * NN + (size_t)2 * N * TP2;
+  static constexpr int kFloats = 12 * kBQ + kBWaves;
+  static constexpr size_t bytes = elems * sizeof(T) + kFloats * sizeof(float);
+};
+
+template <typename T>
+__device__ __forceinline__ void grad_store(T* p, float v, int accumulate) {
+  *p = from_f32<T>(accumulate ? to_f32(*p) + v : v);
+}
+
+template <typename T, int P, int N>
+__global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
+  using L = ChunkLds<T, P, N>;
+  constexpr int Q = kBQ, NP = L::NP, NN = L::NN, TQ = L::TQ, TP2 = L::TP2;
+  constexpr int TP = P / 16, TN = N / 16, NTILE = TP * TN;
+  constexpr int TPW = NTILE >= kBWaves ? NTILE / kBWaves : 1;
+  constexpr int NKB = (N + 31) / 32;  // K=32 slices over d_state
+  constexpr int PKB = P / 32;         // K=32 slices over d_head
+  constexpr int VB = 16 / (int)sizeof(T);
+  constexpr int NBLK = Q / 16;        // 16-token blocks per chunk
+  static_assert(NBLK == 4, "four s-blocks and four t-blocks, one per wave");
+  static_assert(P % 32 == 0, "d_head is a whole number of K=32 slices");
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* Xn = reinterpret_cast<T*>(smem);  // [Q][NP]
+  T* Yn = Xn + Q * NP;                 // dy [Q][NP]
+  T* YT = Yn + Q * NP;                 // dy^T [P][TQ]
+  T* Bn = YT + P * TQ;                 // [Q][NN]
+  T* Cn = Bn + Q * NN;                 // [Q][NN]
+  T* BT = Cn + Q * NN;                 // [N][TQ]
+  T* CT = BT + N * TQ;                 // [N][TQ]
+  T* Gs = CT + N * TQ;                 // Gc [P][NN]
+  T* GT = Gs + P * NN;                 // Gc^T [N][TP2]
+  T* HT = GT + N * TP2;                // Hp^T [N][TP2]
+  float* lam = reinterpret_cast<float*>(HT + N * TP2);  // log2-scaled Lambda
+  float* dtv = lam + Q;
+  float* eL = dtv + Q;    // exp(Lambda_t)
+  float* sc = eL + Q;     // exp(Lambda_e - Lambda_s)
+  float* rpart = sc + Q;  // sum_s W[t,s] over each s-block: [4][Q]
+  float* csum = rpart + 4 * Q;  // sum_t W[t,s]
+  float* esum = csum + Q; // dt_s exp(..) x_s^T Gc B_s
+  float* t1 = esum + Q;   // exp(Lambda_t) dy_t . Hp C_t
+  float* expl = t1 + Q;   // x_s . u_s
+  float* hgw = expl + Q;  // <Gc, H_e> over each wave's tiles: [8]
+
+  int b, h;
+  unit_of(k.heads, &b, &h);
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int r16 = lane % 16, g = lane / 16;
+  const T* __restrict__ Xp = static_cast<const T*>(k.x);
+  const T* __restrict__ DTp = static_cast<const T*>(k.dt);
+  const T* __restrict__ Bp = static_cast<const T*>(k.B);
+  const T* __restrict__ Cp = static_cast<const T*>(k.C);
+  const T* __restrict__ DYp = static_cast<const T*>(k.dy);
+  T* __restrict__ DXp = static_cast<T*>(k.dx);
+  T* __restrict__ DDTp = static_cast<T*>(k.ddt);
+  const T* __restrict__ Hst =
+      static_cast<const T*>(k.hst) + ((int64_t)b * k.heads + h) * (k.nchunks + 1) * (P * N);
+  const int64_t rowb = (int64_t)b * k.seqlen;
+  const float Ah = k.A[h];
+  const float Ah2 = Ah * kLog2e;
+  const float Dh = k.D ? k.D[h] : 0.0f;
+
+  // tiles of dL/dH owned by this wave: G[pt*16 + g*4 + i][nt*16 + r16]
+  const int tile0 = wave * TPW;
+  const bool owns = tile0 < NTILE;
+  const int nt = tile0 / TP, pt0 = tile0 % TP;
+  f32x4 gacc[TPW];
+  {
+    const float* gin = k.dhT ? k.dhT + ((int64_t)b * k.n_heads + h) * (P * N) : nullptr;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        gacc[t][i] = (gin && owns) ? gin[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] : 0.0f;
+  }
+  float da_acc = 0.0f;  // wave 0: sum_r dt_r da_r of this lane's tokens
+  float dd_acc = 0.0f;  // waves 0-3: sum dy . x over this lane's entries
+
+  for (int c = k.nchunks - 1; c >= 0; --c) {
+    const int64_t row0 = rowb + (int64_t)c * Q;
+    const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
+
+    // ---- stage: token rows (zero past len), transposed copies, Hp^T, Gc ----
+    for (int idx = tid; idx < Q * (P / VB); idx += kBThreads) {
+      const int s = idx % Q, p0 = (idx / Q) * VB;
+      Vec16<T> xv = zero16<T>(), yv = zero16<T>();
+      if (s < len) {
+        xv = load16(Xp + (row0 + s) * k.xs + (int64_t)h * P + p0);
+        yv = load16(DYp + (row0 + s) * k.dys + (int64_t)h * P + p0);
+      }
+      store16(Xn + s * NP + p0, xv);
+      store16(Yn + s * NP + p0, yv);
+#pragma unroll
+      for (int j = 0; j < VB; ++j) YT[(p0 + j) * TQ + s] = yv.v[j];
+    }
+    for (int idx = tid; idx < Q * (N / VB); idx += kBThreads) {
+      const int s = idx % Q, n0 = (idx / Q) * VB;
+      Vec16<T> bv = zero16<T>(), cv = zero16<T>();
+      if (s < len) {
+        bv = load16(Bp + (row0 + s) * k.bs + n0);
+        cv = load16(Cp + (row0 + s) * k.cs + n0);
+      }
+      store16(Bn + s * NN + n0, bv);
+      store16(Cn + s * NN + n0, cv);
+#pragma unroll
+      for (int j = 0; j < VB; ++j) {
+        BT[(n0 + j) * TQ + s] = bv.v[j];
+        CT[(n0 + j) * TQ + s] = cv.v[j];
+      }
+    }
+    {
+      const T* hp = Hst + (int64_t)c * (P * N);
+      for (int idx = tid; idx < P * (N / VB); idx += kBThreads) {
+        const int p = idx % P, n0 = (idx / P) * VB;
+        const Vec16<T> v = load16(hp + p * N + n0);
+#pragma unroll
+        for (int j = 0; j < VB; ++j) HT[(n0 + j) * TP2 + p] = v.v[j];
+      }
+    }
+    if (owns) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int p = (pt0 + t) * 16 + g * 4 + i, n = nt * 16 + r16;
+          const T v = from_f32<T>(gacc[t][i]);
+          Gs[p * NN + n] = v;
+          GT[n * TP2 + p] = v;
+        }
+    }
+    if (wave == 0) {
+      const float d = lane < len ? to_f32(DTp[(row0 + lane) * k.dts + h]) : 0.0f;
+      const float lv = chunk_cumsum(d * Ah2, lane);
+      const float le = __shfl(lv, 63);
+      lam[lane] = lv;
+      dtv[lane] = d;
+      eL[lane] = __builtin_amdgcn_exp2f(lv);
+      sc[lane] = __builtin_amdgcn_exp2f(le - lv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rpart[j * Q + lane] = 0.0f;
+      if (lane < kBWaves) hgw[lane] = 0.0f;
+    }
+    __syncthreads();
+
+    if (wave < NBLK) {
+      // ---- s-side: rows s of one 16-token block: dx, dB, column sums ----
+      const int sb = wave, s0 = sb * 16;
+      const int srow = s0 + r16;  // A-operand row of this lane
+      const float scs = sc[srow];
+      f32x4 au[TP], ab[TN];
+#pragma unroll
+      for (int i = 0; i < TP; ++i) au[i] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < TN; ++i) ab[i] = f32x4{0, 0, 0, 0};
+      // end-state terms: u += exp(..) B_s Gc^T,  dB-part += exp(..) x_s Gc
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        Frag8<T> bf;
+        frag_row_scaled(bf, Bn + srow * NN, kb * 32 + g * 8, N, scs);
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) {
+          Frag8<T> gf;
+          frag_row(gf, Gs + (pt * 16 + r16) * NN, kb * 32 + g * 8, N);
+          au[pt] = mma(bf, gf, au[pt]);
+        }
+      }
+#pragma unroll
+      for (int kp = 0; kp < PKB; ++kp) {
+        Frag8<T> xf;
+        frag_row_scaled(xf, Xn + srow * NP, kp * 32 + g * 8, P, scs);
+#pragma unroll
+        for (int n2 = 0; n2 < TN; ++n2) {
+          Frag8<T> gf;
+          frag_load8(gf, GT + (n2 * 16 + r16) * TP2 + kp * 32 + g * 8);
+          ab[n2] = mma(xf, gf, ab[n2]);
+        }
+      }
+      // esum_s = dt_s sum_n ab[s][n] B[s][n]  (rows s = s0 + 4g + i)
+      {
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = s0 + g * 4 + i;
+          float v = 0.0f;
+#pragma unroll
+          for (int n2 = 0; n2 < TN; ++n2) v += ab[n2][i] * to_f32(Bn[s * NN + n2 * 16 + r16]);
+          e[i] = v;
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) e[i] += __shfl_xor(e[i], off);
+        if (r16 == 0)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) esum[s0 + g * 4 + i] = e[i] * dtv[s0 + g * 4 + i];
+      }
+      // diagonal-block terms over t-block pairs (2ip, 2ip+1) with t >= s
+      const float lam_s = lam[srow], dt_s = dtv[srow];
+      float csum_l = 0.0f;
+#pragma unroll 1
+      for (int ip = sb / 2; ip < NBLK / 2; ++ip) {
+        const int ta = 2 * ip, tb = 2 * ip + 1;
+        const bool doa = ta >= sb;  // block ta has t >= s somewhere (wave-uniform)
+        f32x4 gA = {0, 0, 0, 0}, gB = {0, 0, 0, 0}, qA = {0, 0, 0, 0}, qB = {0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          Frag8<T> bs, ca, cb;
+          frag_row(bs, Bn + srow * NN, kb * 32 + g * 8, N);
+          frag_row(cb, Cn + (tb * 16 + r16) * NN, kb * 32 + g * 8, N);
+          gB = mma(cb, bs, gB);
+          if (doa) {
+            frag_row(ca, Cn + (ta * 16 + r16) * NN, kb * 32 + g * 8, N);
+            gA = mma(ca, bs, gA);
+          }
+        }
+#pragma unroll
+        for (int kp = 0; kp < PKB; ++kp) {
+          Frag8<T> xs, ya, yb;
+          frag_load8(xs, Xn + srow * NP + kp * 32 + g * 8);
+          frag_load8(yb, Yn + (tb * 16 + r16) * NP + kp * 32 + g * 8);
+          qB = mma(yb, xs, qB);
+          if (doa) {
+            frag_load8(ya, Yn + (ta * 16 + r16) * NP + kp * 32 + g * 8);
+            qA = mma(ya, xs, qA);
+          }
+        }
+        // lane: G[t][s], Q[t][s] for s = srow, t = ta*16 + 4g + i (slot i)
+        // and t = tb*16 + 4g + i (slot 4 + i)
+        Frag8<T> mf, kf;
+        float rw[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = (j < 4 ? ta : tb) * 16 + g * 4 + (j & 3);
+          const float gv = j < 4 ? gA[j] : gB[j - 4];
+          const float qv = j < 4 ? qA[j] : qB[j - 4];
+          const float dec = t >= srow ? __builtin_amdgcn_exp2f(lam[t] - lam_s) : 0.0f;
+          frag_set(mf, j, gv * dec);
+          frag_set(kf, j, qv * dec);
+          const float w = gv * qv * dec * dt_s;
+          rw[j] = w;
+          csum_l += w;
+        }
+        // row sums of W over this block's 16 s (lanes r16), per t
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) rw[j] += __shfl_xor(rw[j], off);
+        if (r16 == 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) rpart[sb * Q + (j < 4 ? ta : tb) * 16 + g * 4 + (j & 3)] = rw[j];
+        }
+        // u += M^T dy  (k = t in the slot order above), dB-part += K^T C
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) {
+          Frag8<T> yf;
+          const T* yr = YT + (pt * 16 + r16) * TQ;
+          frag_load4x2(yf, yr + ta * 16 + g * 4, yr + tb * 16 + g * 4);
+          au[pt] = mma(mf, yf, au[pt]);
+        }
+#pragma unroll
+        for (int n2 = 0; n2 < TN; ++n2) {
+          Frag8<T> cf;
+          const T* cr = CT + (n2 * 16 + r16) * TQ;
+          frag_load4x2(cf, cr + ta * 16 + g * 4, cr + tb * 16 + g * 4);
+          ab[n2] = mma(kf, cf, ab[n2]);
+        }
+      }
+      // column sums: over the 4 t-slots of each group, then the 4 groups
+      csum_l += __shfl_xor(csum_l, 16);
+      csum_l += __shfl_xor(csum_l, 32);
+      if (g == 0) csum[srow] = csum_l;
+      // epilogue: dx = dt_s u + D dy, x_s . u_s, dy . x, dB atomics
+      float ex[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = s0 + g * 4 + i;
+        const float dts = dtv[s];
+        const bool live = s < len;
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) {
+          const int p = pt * 16 + r16;
+          const float xv = to_f32(Xn[s * NP + p]), yv = to_f32(Yn[s * NP + p]);
+          ex[i] += xv * au[pt][i];
+          dd_acc += xv * yv;
+          if (live)
+            grad_store(DXp + (row0 + s) * k.dxs + (int64_t)h * P + p, dts * au[pt][i] + Dh * yv,
+                       k.accumulate);
+        }
+        if (live) {
+#pragma unroll
+          for (int n2 = 0; n2 < TN; ++n2)
+            unsafeAtomicAdd(k.dB + (row0 + s) * k.dbs + n2 * 16 + r16, dts * ab[n2][i]);
+        }
+      }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ex[i] += __shfl_xor(ex[i], off);
+      if (r16 == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) expl[s0 + g * 4 + i] = ex[i];
+    } else {
+      // ---- t-side: rows t of one 16-token block: dC and the Hp term ----
+      const int tb = wave - NBLK, t0 = tb * 16;
+      const int trow = t0 + r16;
+      const float lam_t = lam[trow];
+      f32x4 ac[TN];
+#pragma unroll
+      for (int i = 0; i < TN; ++i) ac[i] = f32x4{0, 0, 0, 0};
+      // off-diagonal output term: exp(Lambda_t) dy_t Hp
+#pragma unroll
+      for (int kp = 0; kp < PKB; ++kp) {
+        Frag8<T> yf;
+        frag_row_scaled(yf, Yn + trow * NP, kp * 32 + g * 8, P, eL[trow]);
+#pragma unroll
+        for (int n2 = 0; n2 < TN; ++n2) {
+          Frag8<T> hf;
+          frag_load8(hf, HT + (n2 * 16 + r16) * TP2 + kp * 32 + g * 8);
+          ac[n2] = mma(yf, hf, ac[n2]);
+        }
+      }
+      {
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + g * 4 + i;
+          float v = 0.0f;
+#pragma unroll
+          for (int n2 = 0; n2 < TN; ++n2) v += ac[n2][i] * to_f32(Cn[t * NN + n2 * 16 + r16]);
+          e[i] = v;
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) e[i] += __shfl_xor(e[i], off);
+        if (r16 == 0)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t1[t0 + g * 4 + i] = e[i];
+      }
+      // diagonal-block term over s-block pairs (2jp, 2jp+1) with s <= t
+#pragma unroll 1
+      for (int jp = 0; jp <= tb / 2; ++jp) {
+        const int sa = 2 * jp, sb2 = 2 * jp + 1;
+        const bool dob = sb2 <= tb;  // wave-uniform
+        f32x4 rA = {0, 0, 0, 0}, rB = {0, 0, 0, 0};
+#pragma unroll
+        for (int kp = 0; kp < PKB; ++kp) {
+          Frag8<T> yt, xa, xb;
+          frag_load8(yt, Yn + trow * NP + kp * 32 + g * 8);
+          frag_load8(xa, Xn + (sa * 16 + r16) * NP + kp * 32 + g * 8);
+          rA = mma(xa, yt, rA);
+          if (dob) {
+            frag_load8(xb, Xn + (sb2 * 16 + r16) * NP + kp * 32 + g * 8);
+            rB = mma(xb, yt, rB);
+          }
+        }
+        // lane: (x_s . dy_t) for t = trow, s = sa*16 + 4g + i (slot i), sb2*16 + 4g + i (slot 4+i)
+        Frag8<T> kf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int s = (j < 4 ? sa : sb2) * 16 + g * 4 + (j & 3);
+          const float rv = j < 4 ? rA[j] : rB[j - 4];
+          const float f = s <= trow ? __builtin_amdgcn_exp2f(lam_t - lam[s]) * dtv[s] : 0.0f;
+          frag_set(kf, j, rv * f);
+        }
+#pragma unroll
+        for (int n2 = 0; n2 < TN; ++n2) {
+          Frag8<T> bf;
+          const T* br = BT + (n2 * 16 + r16) * TQ;
+          frag_load4x2(bf, br + sa * 16 + g * 4, br + sb2 * 16 + g * 4);
+          ac[n2] = mma(kf, bf, ac[n2]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + g * 4 + i;
+        if (t < len) {
+#pragma unroll
+          for (int n2 = 0; n2 < TN; ++n2)
+            unsafeAtomicAdd(k.dC + (row0 + t) * k.dcs + n2 * 16 + r16, ac[n2][i]);
+        }
+      }
+    }
+
+    // ---- every wave: <Gc, H_e> over its tiles, then dGp ----
+    if (owns) {
+      const T* he = Hst + (int64_t)(c + 1) * (P * N);
+      float dot = 0.0f;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dot += gacc[t][i] * to_f32(he[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16]);
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) dot += __shfl_xor(dot, off);
+      if (lane == 0) hgw[wave] = dot;
+      const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gacc[t][i] *= dec;
+#pragma unroll
+      for (int ks = 0; ks < Q / 32; ++ks) {
+        const int tq = ks * 32 + g * 8;
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(eL + tq);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(eL + tq + 4);
+        Frag8<T> cf;
+        frag_load8(cf, CT + (nt * 16 + r16) * TQ + tq);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          Frag8<T> yr, yf;
+          frag_load8(yr, YT + ((pt0 + t) * 16 + r16) * TQ + tq);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) frag_set(yf, j, to_f32(yr.v[j]) * (j < 4 ? e0[j] : e1[j - 4]));
+          gacc[t] = mma(yf, cf, gacc[t]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- wave 0: dLambda -> da (suffix sum) -> ddt, dA ----
+    if (wave == 0) {
+      const int t = lane;
+      // fixed summation order: the result does not depend on wave timing
+      float dl = t1[t] + (((rpart[t] + rpart[Q + t]) + rpart[2 * Q + t]) + rpart[3 * Q + t]) -
+                 csum[t] - esum[t];
+      if (t == Q - 1) {
+        float hg = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kBWaves; ++j) hg += hgw[j];
+        dl += hg;
+      }
+      // suffix sum over t' >= t
+      float suf = dl;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float v = __shfl_down(suf, off);
+        if (lane + off < 64) suf += v;
+      }
+      if (t < len) {
+        grad_store(DDTp + (row0 + t) * k.ddts + h, expl[t] + Ah * suf, k.accumulate);
+        da_acc += dtv[t] * suf;
+      }
+    }
+    // wave 0 rewrites lam/dtv/eL/sc/rpart/hgw only after its own reads above;
+    // every other array is rewritten after the next barrier
+  }
+
+  // ---- per-unit results: dh0, dA, dD ----
+  if (k.dh0 && owns) {
+    float* dst = k.dh0 + ((int64_t)b * k.n_heads + h) * (P * N);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float* q = dst + ((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16;
+        *q = k.accumulate ? *q + gacc[t][i] : gacc[t][i];
+      }
+  }
+  if (wave == 0) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) da_acc += __shfl_xor(da_acc, off);
+    if (lane == 0) unsafeAtomicAdd(k.dA + h, da_acc);
+  }
+  if (k.dD && wave < NBLK) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) dd_acc += __shfl_xor(dd_acc, off);
+    if (lane == 0) unsafeAtomicAdd(k.dD + h, dd_acc);
+  }
+}
+
+// rows x width fp32 values at p (row stride ld) set to zero
+__global__ __launch_bounds__(256) void zero_rows_kernel(float* p, int64_t ld, int width, int64_t rows) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * width) return;
+  p[(i / width) * ld + i % width] = 0.0f;
+}
+
+void zero_rows(float* p, int64_t ld, int width, int64_t rows, hipStream_t s) {
+  const int64_t n = rows * width;
+  if (n == 0) return;
+  hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, ld,
+                     width, rows);
+}
+
+template <typename T, int P, int N>
+hipError_t launch_shape(const BwdK& k, int64_t batch, hipStream_t s) {
+  const unsigned units = (unsigned)(batch * k.heads);
+  const size_t lds1 = StateLds<T, P, N>::bytes, lds2 = ChunkLds<T, P, N>::bytes;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_state_kernel<T, P, N>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
+  if (e != hipSuccess) return e;
+  static_assert(ChunkLds<T, P, N>::bytes <= 160 * 1024, "chunk tiles fit one CU's LDS");
+  hipLaunchKernelGGL((bwd_state_kernel<T, P, N>), dim3(units), dim3(kBThreads), lds1, s, k);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N>), dim3(units), dim3(kBThreads), lds2, s, k);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_shape_supported(int64_t d_head, int64_t d_state, int dtype) {
+  if (dtype == MM_BF16) return d_head == 64 && (d_state == 64 || d_state == 128);
+  return d_head == 32 && d_state == 16;
+}
+
+size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
+                           int64_t d_state, int dtype) {
+  const int64_t nchunks = (seqlen + kBQ - 1) / kBQ;
+  const size_t el = dtype == MM_BF16 ? 2 : 4;
+  return (size_t)(batch * heads) * (size_t)(nchunks + 1) * (size_t)(d_head * d_state) * el;
+}
+
+hipError_t launch_ssd_backward(const BwdArgs& a, void* workspace, hipStream_t s) {
+  BwdK k;
+  k.x = a.x;
+  k.xs = a.xs;
+  k.dt = a.dt;
+  k.dts = a.dts;
+  k.A = a.A;
+  k.B = a.B;
+  k.bs = a.bs;
+  k.C = a.C;
+  k.cs = a.cs;
+  k.D = a.D;
+  k.h0 = a.h0;
+  k.dy = a.dy;
+  k.dys = a.dys;
+  k.dhT = a.dhT;
+  k.dx = a.dx;
+  k.dxs = a.dxs;
+  k.ddt = a.ddt;
+  k.ddts = a.ddts;
+  k.dA = a.dA;
+  k.dB = a.dB;
+  k.dbs = a.dbs;
+  k.dC = a.dC;
+  k.dcs = a.dcs;
+  k.dD = a.dD;
+  k.dh0 = a.dh0;
+  k.hst = workspace;
+  k.seqlen = a.seqlen;
+  k.n_heads = a.n_heads;
+  k.heads = a.heads;
+  k.nchunks = (int)((a.seqlen + kBQ - 1) / kBQ);
+  k.accumulate = a.accumulate;
+  if (!a.accumulate) {
+    const int64_t rows = a.batch * a.seqlen;
+    zero_rows(a.dB, a.dbs, a.d_state, rows, s);
+    zero_rows(a.dC, a.dcs, a.d_state, rows, s);
+    zero_rows(a.dA, a.heads, a.heads, 1, s);
+    if (a.dD) zero_rows(a.dD, a.heads, a.heads, 1, s);
+  }
+  if (a.dtype == MM_BF16) {
+    if (a.d_state == 128) return launch_shape<bf16, 64, 128>(k, a.batch, s);
+    return launch_shape<bf16, 64, 64>(k, a.batch, s);
+  }
+  return launch_shape<float, 32, 16>(k, a.batch, s);
+}
+
+}  // namespace mmssd

@@ -21,6 +21,20 @@ bool scan_shape_supported(int64_t P, int64_t N) {
   return (P == 32 && N == 16) || (P == 64 && N == 64) || (P == 64 && N == 128);
 }
 
+// Shapes of the scan backward: its LDS tiles (x, dy, B, C with their
+// transposes, dL/dH and the chunk's start state) fit one CU for these.
+bool bwd_supported(int64_t P, int64_t N, int dtype) {
+  if (dtype == MM_BF16) return P == 64 && (N == 64 || N == 128);
+  return P == 32 && N == 16;
+}
+
+// [p, p + bytes) and [q, q + bytes2) share a byte (NULL never overlaps).
+bool ranges_overlap(const void* p, int64_t bytes, const void* q, int64_t bytes2) {
+  if (!p || !q) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
+  return a0 < b0 + uintptr_t(bytes2) && b0 < a0 + uintptr_t(bytes);
+}
+
 bool chunk_supported(int64_t q) {
   return q == 16 || q == 32 || q == 64 || q == 128 || q == 256;
 }
@@ -302,6 +316,73 @@ int validate_ssd_step(const float* state, const void* x_t, int64_t x_row_stride,
   if (reinterpret_cast<uintptr_t>(x_t) % el != 0 || reinterpret_cast<uintptr_t>(y_t) % el != 0 ||
       reinterpret_cast<uintptr_t>(dt_t) % el != 0)
     return MM_ERR_ALIGN;
+  return MM_OK;
+}
+
+int validate_ssd_backward_shape(int64_t batch, int64_t seqlen, int64_t n_heads, int64_t d_head,
+                                int64_t d_state, int64_t ngroups, int64_t n_heads_active,
+                                int dtype) {
+  const int st = validate_ssd_shape(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                    n_heads_active, 64, dtype);
+  if (st != MM_OK) return st;
+  return bwd_supported(d_head, d_state, dtype) ? MM_OK : MM_ERR_UNSUPPORTED;
+}
+
+int validate_ssd_backward(const void* x, int64_t x_row_stride, const void* dt,
+                          int64_t dt_row_stride, const float* A, const void* B,
+                          int64_t b_row_stride, const void* C, int64_t c_row_stride,
+                          const float* D, const float* initial_state, const void* dy,
+                          int64_t dy_row_stride, const float* dfinal_state, const void* dx,
+                          int64_t dx_row_stride, const void* ddt, int64_t ddt_row_stride,
+                          const float* dA, const float* dB, int64_t db_row_stride,
+                          const float* dC, int64_t dc_row_stride, const float* dD,
+                          const float* dinitial_state, int64_t batch, int64_t seqlen,
+                          int64_t n_heads, int64_t d_head, int64_t d_state, int64_t ngroups,
+                          int64_t n_heads_active, int dtype, int accumulate) {
+  if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC) return MM_ERR_NULL;
+  const int st = validate_ssd_backward_shape(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                             n_heads_active, dtype);
+  if (st != MM_OK) return st;
+  if (accumulate != 0 && accumulate != 1) return MM_ERR_SHAPE;
+  const int64_t el = dtype_bytes(dtype);
+  const int64_t xw = n_heads_active * d_head, hw = n_heads_active, bw = ngroups * d_state;
+  if (x_row_stride < xw || dy_row_stride < xw || dx_row_stride < xw || dt_row_stride < hw ||
+      ddt_row_stride < hw || b_row_stride < bw || c_row_stride < bw || db_row_stride < bw ||
+      dc_row_stride < bw)
+    return MM_ERR_SHAPE;
+  const int64_t rows = batch * seqlen;
+  const int64_t strides[] = {x_row_stride, dy_row_stride, dx_row_stride, dt_row_stride,
+                             ddt_row_stride, b_row_stride, c_row_stride, db_row_stride,
+                             dc_row_stride};
+  for (int64_t v : strides)
+    if (!mul_ok(rows, v)) return MM_ERR_SHAPE;
+  if (!rows_aligned(x, x_row_stride, el) || !rows_aligned(dy, dy_row_stride, el) ||
+      !rows_aligned(dx, dx_row_stride, el) || !rows_aligned(B, b_row_stride, el) ||
+      !rows_aligned(C, c_row_stride, el))
+    return MM_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(dt) % el != 0 || reinterpret_cast<uintptr_t>(ddt) % el != 0)
+    return MM_ERR_ALIGN;
+  const void* f32s[] = {D, initial_state, dfinal_state, dA, dB, dC, dD, dinitial_state};
+  for (const void* p : f32s)
+    if (reinterpret_cast<uintptr_t>(p) % 4 != 0) return MM_ERR_ALIGN;
+  // the written gradients must not overlap what the call reads or each other
+  auto span = [&](int64_t stride, int64_t width, int64_t e) { return ((rows - 1) * stride + width) * e; };
+  const int64_t sdx = span(dx_row_stride, xw, el), sddt = span(ddt_row_stride, hw, el);
+  const int64_t sdb = span(db_row_stride, bw, 4), sdc = span(dc_row_stride, bw, 4);
+  const int64_t sst = batch * n_heads * d_head * d_state * 4;
+  struct R { const void* p; int64_t n; };
+  const R outs[] = {{dx, sdx}, {ddt, sddt}, {dB, sdb}, {dC, sdc}, {dA, n_heads * 4},
+                    {dD, n_heads * 4}, {dinitial_state, sst}};
+  const R ins[] = {{x, span(x_row_stride, xw, el)}, {dy, span(dy_row_stride, xw, el)},
+                   {dt, span(dt_row_stride, hw, el)}, {B, span(b_row_stride, bw, el)},
+                   {C, span(c_row_stride, bw, el)}, {A, n_heads * 4}, {D, n_heads * 4},
+                   {initial_state, sst}, {dfinal_state, sst}};
+  for (const R& o : outs) {
+    for (const R& i : ins)
+      if (ranges_overlap(o.p, o.n, i.p, i.n)) return MM_ERR_SHAPE;
+    for (const R& o2 : outs)
+      if (&o2 != &o && ranges_overlap(o.p, o.n, o2.p, o2.n)) return MM_ERR_SHAPE;
+  }
   return MM_OK;
 }
 

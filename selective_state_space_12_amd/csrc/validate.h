@@ -91,4 +91,25 @@ int validate_ssd_step(const float* state, const void* x_t, int64_t x_row_stride,
                       int64_t d_head, int64_t d_state, int64_t ngroups,
                       int64_t n_heads_active, int dtype);
 
+// Shape part of the backward checks (used by its workspace query too).
+int validate_ssd_backward_shape(int64_t batch, int64_t seqlen, int64_t n_heads, int64_t d_head,
+                                int64_t d_state, int64_t ngroups, int64_t n_heads_active,
+                                int dtype);
+
+// mm_ssd_backward: the forward's checks (chunk aside) for the inputs, the
+// backward's shapes ((64, 64) and (64, 128) with bf16, (32, 16) with fp32),
+// strides and alignment of the gradients, accumulate 0 or 1, and no
+// gradient overlapping an input or another gradient.
+int validate_ssd_backward(const void* x, int64_t x_row_stride, const void* dt,
+                          int64_t dt_row_stride, const float* A, const void* B,
+                          int64_t b_row_stride, const void* C, int64_t c_row_stride,
+                          const float* D, const float* initial_state, const void* dy,
+                          int64_t dy_row_stride, const float* dfinal_state, const void* dx,
+                          int64_t dx_row_stride, const void* ddt, int64_t ddt_row_stride,
+                          const float* dA, const float* dB, int64_t db_row_stride,
+                          const float* dC, int64_t dc_row_stride, const float* dD,
+                          const float* dinitial_state, int64_t batch, int64_t seqlen,
+                          int64_t n_heads, int64_t d_head, int64_t d_state, int64_t ngroups,
+                          int64_t n_heads_active, int dtype, int accumulate);
+
 }  // namespace mmssd

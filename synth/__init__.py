@@ -22,7 +22,8 @@ from typing import Dict, List, Optional
 import torch
 
 # tensor indices inside a config's seed block
-_X, _B, _C, _DT, _A, _D, _CONVW, _XBC, _H0, _CS0, _DTSTEP, _XBCSTEP, _CONVB, _DTRAW, _DTB, _Z, _NW, _YN = range(18)
+(_X, _B, _C, _DT, _A, _D, _CONVW, _XBC, _H0, _CS0, _DTSTEP, _XBCSTEP, _CONVB, _DTRAW, _DTB, _Z, _NW,
+ _YN, _DY, _DHT, _DOUT) = range(21)
 
 
 @dataclass(frozen=True)
@@ -139,6 +140,29 @@ def forward_inputs(w: Workload, batch: Optional[int] = None,
     if with_state:
         out["h0"] = _normal((b, H, P, N), _gen(w, _H0, salt))
     return out
+
+
+def cotangents(w: Workload, batch: Optional[int] = None, seqlen: Optional[int] = None,
+               salt: int = 0) -> Dict[str, torch.Tensor]:
+    """Cotangents for a backward pass of the scan: dy (b, l, H, P) ~ N(0, 1)
+    in the storage dtype (the gradient arriving at y) and dhT (b, H, P, N)
+    ~ N(0, 1) fp32 (arriving at the final state)."""
+    b = batch or w.batch
+    l = seqlen or w.seqlen
+    H, P, N = w.n_heads, w.d_head, w.d_state
+    return {
+        "dy": _normal((b, l, H, P), _gen(w, _DY, salt)).to(w.dtype),
+        "dhT": _normal((b, H, P, N), _gen(w, _DHT, salt)),
+    }
+
+
+def conv_cotangent(w: Workload, batch: Optional[int] = None, seqlen: Optional[int] = None,
+                   salt: int = 0) -> torch.Tensor:
+    """Cotangent of the conv output (b, l, conv_dim) ~ N(0, 1) in the storage
+    dtype."""
+    b = batch or w.batch
+    l = seqlen or w.seqlen
+    return _normal((b, l, w.conv_dim), _gen(w, _DOUT, salt)).to(w.dtype)
 
 
 def xbc_inputs(w: Workload, batch: Optional[int] = None,

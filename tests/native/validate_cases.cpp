@@ -164,6 +164,42 @@ int main() {
            MM_ERR_NULL);
   }
 
+  // scan backward: 4 x 8192 tokens, 64 heads x 64 x 128, bf16; every output
+  // in a region of its own (inputs may share theirs)
+  {
+    auto at = [](uint64_t a) { return reinterpret_cast<float*>(uintptr_t(a)); };
+    float *dx = at(0x1000000000ull), *ddt = at(0x2000000000ull), *dB = at(0x3000000000ull),
+          *dC = at(0x4000000000ull), *dA = at(0x5000000000ull), *dD = at(0x6000000000ull),
+          *dh0 = at(0x7000000000ull);
+    auto bwd = [&](const void* dy, const void* dx_, float* dB_, float* dC_, int64_t dxs,
+                   int64_t P_, int64_t N_, int64_t ha, int dt_code, int acc) {
+      return validate_ssd_backward(P, 64 * P_, P, 64, F, P, N_, P, N_, F, nullptr, dy, 64 * P_,
+                                   nullptr, dx_, dxs, ddt, 64, dA, dB_, N_, dC_, N_, dD, dh0, 4,
+                                   8192, 64, P_, N_, 1, ha, dt_code, acc);
+    };
+    expect("bwd ok", bwd(P, dx, dB, dC, 4096, 64, 128, 64, MM_BF16, 0), MM_OK);
+    expect("bwd ok accumulate", bwd(P, dx, dB, dC, 4096, 64, 128, 8, MM_BF16, 1), MM_OK);
+    expect("bwd ok d_state 64", bwd(P, dx, dB, dC, 4096, 64, 64, 64, MM_BF16, 0), MM_OK);
+    expect("bwd null dy", bwd(nullptr, dx, dB, dC, 4096, 64, 128, 64, MM_BF16, 0), MM_ERR_NULL);
+    expect("bwd fp32 d_head 64", bwd(P, dx, dB, dC, 4096, 64, 128, 64, MM_F32, 0),
+           MM_ERR_UNSUPPORTED);
+    expect("bwd bf16 d_head 32", bwd(P, dx, dB, dC, 2048, 32, 16, 64, MM_BF16, 0),
+           MM_ERR_UNSUPPORTED);
+    expect("bwd dx over x", bwd(P, P, dB, dC, 4096, 64, 128, 64, MM_BF16, 0), MM_ERR_SHAPE);
+    expect("bwd dB over dC", bwd(P, dx, dB, dB + 64, 4096, 64, 128, 64, MM_BF16, 0),
+           MM_ERR_SHAPE);
+    expect("bwd accumulate 2", bwd(P, dx, dB, dC, 4096, 64, 128, 64, MM_BF16, 2), MM_ERR_SHAPE);
+    expect("bwd dx stride short", bwd(P, dx, dB, dC, 4088, 64, 128, 64, MM_BF16, 0),
+           MM_ERR_SHAPE);
+    expect("bwd dB misaligned", bwd(P, dx, at(0x3000000002ull), dC, 4096, 64, 128, 64, MM_BF16, 0),
+           MM_ERR_ALIGN);
+    expect("bwd heads 0", bwd(P, dx, dB, dC, 4096, 64, 128, 0, MM_BF16, 0), MM_ERR_SLICE);
+    expect("bwd shape query ok", validate_ssd_backward_shape(4, 8192, 64, 64, 128, 1, 64, MM_BF16),
+           MM_OK);
+    expect("bwd shape query fp32 64x64",
+           validate_ssd_backward_shape(4, 8192, 64, 64, 64, 1, 64, MM_F32), MM_ERR_UNSUPPORTED);
+  }
+
   std::printf("%d failure(s)\n", failures);
   return failures == 0 ? 0 : 1;
 }
