@@ -25,6 +25,9 @@ Also reported on the same JSON line:
     same batch run at the widest width;
   - ``gated_rmsnorm``: the gated RMSNorm epilogue (y * SiLU(z), RMSNorm over
     d_i) on the 1.4B-scale rows at every width, timed as the slices are;
+  - ``backward``: the scan's backward pass (mm_ssd_backward: dx, ddt, dA,
+    dB, dC, dD from the cotangent of y) on the same inputs at every width,
+    timed as the slices are, with its HBM fraction;
   - ``decode``: the recurrent decode step (conv state roll + scan step) for a
     batch of 256 sequences at mixed widths, 1024 tokens captured in a HIP graph;
   - ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample
@@ -119,6 +122,13 @@ def scan_bytes(tokens: int, heads: int, P: int, N: int, elem: int) -> int:
     return tokens * (2 * heads * P * elem + 2 * N * elem + heads * elem)
 
 
+def bwd_bytes(tokens: int, heads: int, P: int, N: int, elem: int) -> int:
+    """Algorithmic HBM bytes of one scan backward call: x, dy read and dx
+    written for the active heads, dt read and ddt written, B and C read, the
+    fp32 dB and dC written (A, D, dA, dD negligible)."""
+    return tokens * (3 * heads * P * elem + 2 * heads * elem + 2 * N * elem + 2 * N * 4)
+
+
 def scan_flops(tokens: int, heads: int, P: int, N: int, Q: int) -> int:
     """Algorithmic flops of one scan call, causal-counted chunked form at chunk
     Q with one B/C group: (Q+1) N for the shared C.B^T blocks, and per head
@@ -208,11 +218,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-slices", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the scan-only timings of the 130M and long-context workloads")
-    ap.add_argument("--mode", choices=["step", "fused", "scan", "copy"], default="step",
-                    help="fused / scan: only the full-width fused call / scan call (for "
-                         "counter runs); copy: a 1 GiB device copy that calibrates the HBM "
+    ap.add_argument("--mode", choices=["step", "fused", "scan", "backward", "copy"],
+                    default="step",
+                    help="fused / scan / backward: only the full-width fused call / scan call / "
+                         "scan backward call (for counter runs); copy: a 1 GiB device copy that calibrates the HBM "
                          "byte counters")
     ap.add_argument("--summarize-pmc", nargs=5,
                     metavar=("WHICH", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -282,6 +294,18 @@ def main():
             fused(H)
         torch.cuda.synchronize()
         print(f"# fused-only: {args.warmup + args.steps} launches", file=sys.stderr)
+        return
+    if args.mode == "backward":  # counter runs: the full-width scan backward alone
+        conv(H)
+        dy = synth.cotangents(w)["dy"].to(dev)
+        g = {"dx": torch.empty((b, l, H, P), dtype=w.dtype, device=dev),
+             "ddt": torch.empty((b, l, H), dtype=w.dtype, device=dev)}
+        bws = torch.empty(mm.ssd_backward_workspace_size(b, l, H, P, N, 1, H, w.dtype),
+                          dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup + args.steps):
+            g = mm.ssd_backward(xv, dt, A, Bv, Cv, D, dy, grads=g, workspace=bws)
+        torch.cuda.synchronize()
+        print(f"# backward-only: {args.warmup + args.steps} launches", file=sys.stderr)
         return
     if args.mode == "copy":  # counter calibration: a plain copy of known size
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -367,7 +391,7 @@ def main():
 
     # ---- every Matryoshka width, scan only -----------------------------------
     flush = None
-    if not (args.no_slices and args.no_configs):
+    if not (args.no_slices and args.no_configs and args.no_backward):
         flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     if not args.no_slices:
         slices, fused_slices = {}, {}
@@ -428,6 +452,10 @@ def main():
         out["gated_rmsnorm"] = norm
         del gy, gz, gw, gout
 
+    # ---- scan backward on the same inputs, every width ------------------------
+    if not args.no_backward:
+        out["backward"] = bench_backward(torch, mm, synth, w, dev, flush, xv, dt, A, Bv, Cv, D)
+
     # ---- the other bf16 workloads, scan only, every slice ----------------------
     if not args.no_configs:
         del xbc_raw, xbc, xv, Bv, Cv, y, ws, wsf
@@ -443,6 +471,31 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w)
 
     print(json.dumps(out), flush=True)
+
+
+def bench_backward(torch, mm, synth, w, dev, flush, xv, dt, A, Bv, Cv, D, slices=None):
+    """mm_ssd_backward at every width of the 1.4B-scale workload (dy from the
+    seeded cotangents, no final-state cotangent, gradients overwritten)."""
+    b, l, H, P, N = w.batch, w.seqlen, w.n_heads, w.d_head, w.d_state
+    tokens = b * l
+    dy = synth.cotangents(w)["dy"].to(dev)
+    g = {"dx": torch.empty((b, l, H, P), dtype=w.dtype, device=dev),
+         "ddt": torch.empty((b, l, H), dtype=w.dtype, device=dev),
+         "dA": torch.empty(H, device=dev), "dD": torch.empty(H, device=dev),
+         "dB": torch.empty((b, l, 1, N), device=dev), "dC": torch.empty((b, l, 1, N), device=dev)}
+    ws = torch.empty(mm.ssd_backward_workspace_size(b, l, H, P, N, 1, H, w.dtype),
+                     dtype=torch.uint8, device=dev)
+    res = {}
+    for m in (slices or w.slices):
+        h = w.heads(m)
+        t = timed_calls(torch, lambda: mm.ssd_backward(xv, dt, A, Bv, Cv, D, dy, n_heads_active=h,
+                                                        grads=g, workspace=ws), flush)
+        ab = bwd_bytes(tokens, h, P, N, 2)
+        res[str(m)] = {"heads": h, "ms": t["median"], "ms_p10": t["p10"], "ms_p90": t["p90"],
+                       "tokens_per_s": tokens / (t["median"] * 1e-3),
+                       "hbm_frac": ab / (t["median"] * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+    del dy, g, ws
+    return res
 
 
 def bench_configs(torch, mm, synth, dev, flush):

@@ -384,6 +384,38 @@ int mm_conv_state_advance(float* conv_state, const void* xbc, int64_t xbc_row_st
                           int64_t n_heads_active, int dtype, void* stream);
 
 /*
+ * Backward pass of mm_conv1d_silu ("MatMamba", block paragraph for the conv
+ * and SiLU, training paragraph for the joint backward pass of the nested
+ * granularities).  Given dout, the cotangent of the conv output, computes the
+ * gradients of L = sum(dout * out) for the active channels (the x slice of
+ * n_heads_active heads, then every B and C channel):
+ *   xbc_in, w, bias, conv_state: the forward call's inputs, with conv_state
+ *       holding the history it read (before its in-place update), or NULL.
+ *   dout    (rows, dout_row_stride) dtype; active channels read.
+ *   dxbc_in (rows, din_row_stride) dtype: active channels written.
+ *   dw      (conv_dim, 4) fp32: active channels' rows (sums over the batch).
+ *   dbias   (conv_dim) fp32 or NULL: active channels.
+ *   dconv_state (batch, 3, conv_dim) fp32 or NULL: gradient with respect to
+ *       the history rows (zero history when conv_state is NULL); active
+ *       channels written.
+ *   accumulate: 0 overwrites the outputs above, 1 adds into them.
+ * dw and dbias are sums formed with fp32 atomics (last bits may vary between
+ * runs).  The updated conv state the forward returns is not differentiated.
+ * Preconditions: those of mm_conv1d_silu (heads_active_per_seq aside);
+ * seqlen <= 64*65535; dout rows 16-byte aligned; fp32 outputs 4-byte aligned;
+ * accumulate 0 or 1 and no output overlapping an input or another output
+ * (MM_ERR_SHAPE).
+ */
+int mm_conv1d_silu_backward(const void* xbc_in, int64_t in_row_stride,
+                            const void* dout, int64_t dout_row_stride,
+                            void* dxbc_in, int64_t din_row_stride,
+                            const float* w, const float* bias, const float* conv_state,
+                            float* dw, float* dbias, float* dconv_state,
+                            int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_head,
+                            int64_t d_state, int64_t ngroups, int64_t n_heads_active,
+                            int dtype, int accumulate, void* stream);
+
+/*
  * Bytes of device workspace mm_ssd_backward needs: the state before every
  * 64-token chunk and the final state of each active (sequence, head), in the
  * storage dtype.  Same argument meaning and errors as mm_ssd_backward.

@@ -114,6 +114,10 @@ def lib() -> ctypes.CDLL:
                                            _i64, _vp, _i64, _vp, _vp] + [_i64] * 7
                                           + [_int, _int, _vp, ctypes.c_size_t, _vp])
             L.mm_ssd_backward.restype = _int
+            L.mm_conv1d_silu_backward.argtypes = ([_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
+                                                   _vp, _vp, _vp] + [_i64] * 7
+                                                  + [_int, _int, _vp])
+            L.mm_conv1d_silu_backward.restype = _int
             _lib = L
     return _lib
 
@@ -268,6 +272,50 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
                               code, _ptr(workspace), wbytes, _stream())
     _check("mm_ssd_forward", st)
     return y
+
+
+def conv1d_silu_backward(xbc: torch.Tensor, w: torch.Tensor, dout: torch.Tensor,
+                         bias: Optional[torch.Tensor] = None,
+                         conv_state: Optional[torch.Tensor] = None, *, d_inner: int, d_head: int,
+                         d_state: int, ngroups: int = 1, n_heads_active: Optional[int] = None,
+                         grads: Optional[dict] = None, accumulate: bool = False,
+                         want_dbias: bool = False, want_dstate: bool = False) -> dict:
+    """Gradients of sum(dout * conv1d_silu(xbc)) for the active channels:
+    dxbc (like xbc), dw (conv_dim, 4) fp32 and, if asked, dbias (conv_dim)
+    and dconv_state (batch, 3, conv_dim) fp32.  conv_state is the history the
+    forward read (its value before the forward's in-place update).  `grads`
+    may hold any of these buffers to write (or, with accumulate=True, add)
+    into."""
+    batch, seqlen, width = xbc.shape
+    conv_dim = d_inner + 2 * ngroups * d_state
+    h_act = d_inner // d_head if n_heads_active is None else int(n_heads_active)
+    dev = xbc.device
+    g = dict(grads or {})
+    if "dxbc" not in g:
+        g["dxbc"] = torch.empty((batch, seqlen, conv_dim), dtype=xbc.dtype, device=dev)
+    if "dw" not in g:
+        g["dw"] = torch.empty((conv_dim, 4), dtype=torch.float32, device=dev)
+    if want_dbias and "dbias" not in g:
+        g["dbias"] = torch.empty(conv_dim, dtype=torch.float32, device=dev)
+    if want_dstate and "dconv_state" not in g:
+        g["dconv_state"] = torch.empty((batch, 3, conv_dim), dtype=torch.float32, device=dev)
+    for name, t in (("dout", dout), ("dxbc", g["dxbc"])):
+        if t.dtype != xbc.dtype:
+            raise TypeError(f"{name} must have xbc's dtype")
+    xs = _row_stride(xbc, "xbc", (width,))
+    ds = _row_stride(dout, "dout", (dout.shape[2],))
+    gs = _row_stride(g["dxbc"], "dxbc", (g["dxbc"].shape[2],))
+    for name, t in (("w", w), ("bias", bias), ("conv_state", conv_state), ("dw", g["dw"]),
+                    ("dbias", g.get("dbias")), ("dconv_state", g.get("dconv_state"))):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 tensor")
+    st = lib().mm_conv1d_silu_backward(_ptr(xbc), xs, _ptr(dout), ds, _ptr(g["dxbc"]), gs,
+                                       _ptr(w), _ptr(bias), _ptr(conv_state), _ptr(g["dw"]),
+                                       _ptr(g.get("dbias")), _ptr(g.get("dconv_state")), batch,
+                                       seqlen, d_inner, d_head, d_state, ngroups, h_act,
+                                       _dtype_code(xbc), int(bool(accumulate)), _stream())
+    _check("mm_conv1d_silu_backward", st)
+    return g
 
 
 def ssd_backward_workspace_size(batch: int, seqlen: int, n_heads: int, d_head: int,

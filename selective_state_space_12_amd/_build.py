@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmmssd.so")
 
 HIP_SOURCES = ["conv1d_silu.hip", "ssd_step.hip", "ssd_fwd.hip", "ssd_fwd_bf16.hip", "fused.hip",
-               "gated_rmsnorm.hip", "ssd_bwd.hip"]
+               "gated_rmsnorm.hip", "ssd_bwd.hip", "conv1d_silu_bwd.hip"]
 CPP_SOURCES = ["abi.cpp", "validate.cpp"]
 ARCH = "gfx950"
 

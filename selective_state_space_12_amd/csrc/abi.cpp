@@ -335,6 +335,40 @@ int mm_conv_state_advance(float* conv_state, const void* xbc, int64_t xbc_row_st
   return hip_status(launch_conv_state_advance(a, dtype, as_stream(stream)));
 }
 
+int mm_conv1d_silu_backward(const void* xbc_in, int64_t in_row_stride, const void* dout,
+                            int64_t dout_row_stride, void* dxbc_in, int64_t din_row_stride,
+                            const float* w, const float* bias, const float* conv_state,
+                            float* dw, float* dbias, float* dconv_state, int64_t batch,
+                            int64_t seqlen, int64_t d_inner, int64_t d_head, int64_t d_state,
+                            int64_t ngroups, int64_t n_heads_active, int dtype, int accumulate,
+                            void* stream) {
+  const int st = validate_conv_backward(xbc_in, in_row_stride, dout, dout_row_stride, dxbc_in,
+                                        din_row_stride, w, bias, conv_state, dw, dbias,
+                                        dconv_state, batch, seqlen, d_inner, d_head, d_state,
+                                        ngroups, n_heads_active, dtype, accumulate);
+  if (st != MM_OK) return st;
+  ConvBwdArgs a;
+  a.in = xbc_in;
+  a.in_stride = in_row_stride;
+  a.dout = dout;
+  a.dout_stride = dout_row_stride;
+  a.din = dxbc_in;
+  a.din_stride = din_row_stride;
+  a.w = w;
+  a.bias = bias;
+  a.conv_state = conv_state;
+  a.dw = dw;
+  a.dbias = dbias;
+  a.dstate = dconv_state;
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.d_inner = d_inner;
+  a.xw = (int)(n_heads_active * d_head);
+  a.bc_dim = (int)(2 * ngroups * d_state);
+  a.accumulate = accumulate;
+  return hip_status(launch_conv1d_silu_backward(a, dtype, as_stream(stream)));
+}
+
 int mm_ssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
                                    int64_t d_head, int64_t d_state, int64_t ngroups,
                                    int64_t n_heads_active, int dtype, size_t* bytes_out) {

@@ -1,0 +1,215 @@
+// Backward pass of the causal depthwise conv1d (kernel 4) + SiLU over the
+// [x | B | C] channels ("MatMamba: A Matryoshka State Space Model", block
+// paragraph for the conv and SiLU; training paragraph for the joint backward
+// pass of the nested granularities).  With pre[t] = bias + sum_k w_k u[t-3+k]
+// and SiLU'(v) = s (1 + v (1 - s)), s = sigmoid(v):
+//   dpre[t]   = dout[t] SiLU'(pre[t])
+//   du[tau]   = sum_k w_k dpre[tau + 3 - k]       (tau = -3..-1: the conv state rows)
+//   dw_k     += sum_t dpre[t] u[t - 3 + k],  dbias += sum_t dpre[t]
+//
+// Design: HBM-bound streaming, as the forward conv.  A thread owns 16 bytes
+// of channels and a run of tokens; it slides a window of three inputs and
+// three dpre values, so du[t-3] is complete once dpre[t] is known: the run
+// reads three tokens past its end (the halo whose dpre reaches back into the
+// run) and three before it.  The run that starts at token 0 also emits the
+// conv-state rows' gradient.  dw and dbias are summed over the run in
+// registers and added with one fp32 atomic per value and run.
+#include "device_common.h"
+#include "kernels.h"
+#include "../../include/mm_ssd.h"
+
+namespace mmssd {
+
+namespace {
+
+constexpr int kThreads = 64;
+constexpr int kRun = 64;  // tokens per thread
+
+template <typename T>
+__device__ __forceinline__ void add_store16(T* p, const float (&v)[Vec16<T>::kN], int accumulate) {
+  constexpr int V = Vec16<T>::kN;
+  Vec16<T> o;
+  if (accumulate) {
+    const Vec16<T> old = load16(p);
+#pragma unroll
+    for (int j = 0; j < V; ++j) o.v[j] = from_f32<T>(to_f32(old.v[j]) + v[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; ++j) o.v[j] = from_f32<T>(v[j]);
+  }
+  store16(p, o);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void conv1d_silu_bwd_kernel(
+    const T* __restrict__ in, int64_t in_stride, const T* __restrict__ dout, int64_t dout_stride,
+    T* __restrict__ din, int64_t din_stride, const float* __restrict__ w,
+    const float* __restrict__ bias, const float* __restrict__ conv_state, float* __restrict__ dw,
+    float* __restrict__ dbias, float* __restrict__ dstate, int seqlen, int d_inner, int xw,
+    int bc_dim, int accumulate) {
+  constexpr int V = Vec16<T>::kN;
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.y * kRun;
+  const int cg = blockIdx.x * kThreads + threadIdx.x;
+  const int ngx = xw / V;
+  if (cg >= ngx + bc_dim / V || t0 >= seqlen) return;
+  const int c = cg < ngx ? cg * V : d_inner + (cg - ngx) * V;
+  const int conv_dim = d_inner + bc_dim;
+  const int t1 = min(seqlen, t0 + kRun);
+  const int tend = min(seqlen, t1 + 3);  // tokens whose dpre is needed
+
+  float wk[4][V], bv[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const float4 wj = *reinterpret_cast<const float4*>(w + (int64_t)(c + j) * 4);
+    wk[0][j] = wj.x;
+    wk[1][j] = wj.y;
+    wk[2][j] = wj.z;
+    wk[3][j] = wj.w;
+    bv[j] = bias ? bias[c + j] : 0.0f;
+  }
+  const int64_t row0 = (int64_t)b * seqlen;
+  // inputs u[t-3], u[t-2], u[t-1] and dpre[t-3], dpre[t-2], dpre[t-1]
+  float h[3][V], dp[3][V];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int tau = t0 - 3 + k;
+    if (tau >= 0) {
+      const Vec16<T> v = load16(in + (row0 + tau) * in_stride + c);
+#pragma unroll
+      for (int j = 0; j < V; ++j) h[k][j] = to_f32(v.v[j]);
+    } else if (conv_state) {
+      const float* sp = conv_state + ((int64_t)b * 3 + (tau + 3)) * conv_dim + c;
+#pragma unroll
+      for (int j = 0; j < V; ++j) h[k][j] = sp[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < V; ++j) h[k][j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) dp[k][j] = 0.0f;
+  }
+  float sw[4][V], sb[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    sb[j] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sw[k][j] = 0.0f;
+  }
+
+  // Before the run's first token the dpre window would need dpre[t0-3..t0-1],
+  // which only matter for du[t0-3..t0-1] (outside the run): the window starts
+  // at zero and nothing is emitted for those tokens, except the conv-state
+  // rows when the run starts the sequence (dpre before token 0 is zero).
+  // Tokens past the sequence end have dpre = 0.
+  constexpr int kGroup = 4;
+  for (int tg = t0; tg < t1 + 3; tg += kGroup) {
+    Vec16<T> u[kGroup], go[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i)
+      if (tg + i < tend) {
+        u[i] = load16(in + (row0 + tg + i) * in_stride + c);
+        go[i] = load16(dout + (row0 + tg + i) * dout_stride + c);
+      }
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const int t = tg + i;
+      if (t >= t1 + 3) break;
+      float dcur[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        float d = 0.0f;
+        if (t < tend) {
+          const float ut = to_f32(u[i].v[j]);
+          float pre = bv[j];
+          pre = fmaf(wk[0][j], h[0][j], pre);
+          pre = fmaf(wk[1][j], h[1][j], pre);
+          pre = fmaf(wk[2][j], h[2][j], pre);
+          pre = fmaf(wk[3][j], ut, pre);
+          const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-pre * kLog2e));
+          d = to_f32(go[i].v[j]) * s * (1.0f + pre * (1.0f - s));
+          if (t < t1) {
+            sw[0][j] = fmaf(d, h[0][j], sw[0][j]);
+            sw[1][j] = fmaf(d, h[1][j], sw[1][j]);
+            sw[2][j] = fmaf(d, h[2][j], sw[2][j]);
+            sw[3][j] = fmaf(d, ut, sw[3][j]);
+            sb[j] += d;
+          }
+          h[0][j] = h[1][j];
+          h[1][j] = h[2][j];
+          h[2][j] = ut;
+        }
+        dcur[j] = d;
+      }
+      // du[t-3] = w0 dpre[t] + w1 dpre[t-1] + w2 dpre[t-2] + w3 dpre[t-3]
+      const int tau = t - 3;
+      if (tau >= t0 || (t0 == 0 && dstate)) {
+        float g[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+          g[j] = wk[0][j] * dcur[j] + wk[1][j] * dp[2][j] + wk[2][j] * dp[1][j] + wk[3][j] * dp[0][j];
+        if (tau >= t0) {
+          add_store16(din + (row0 + tau) * din_stride + c, g, accumulate);
+        } else {  // tau = -3..-1: conv state row tau + 3 (the run starts the sequence)
+          float* sp = dstate + ((int64_t)b * 3 + (tau + 3)) * conv_dim + c;
+#pragma unroll
+          for (int j = 0; j < V; ++j) sp[j] = accumulate ? sp[j] + g[j] : g[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        dp[0][j] = dp[1][j];
+        dp[1][j] = dp[2][j];
+        dp[2][j] = dcur[j];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) unsafeAtomicAdd(dw + (int64_t)(c + j) * 4 + k, sw[k][j]);
+    if (dbias) unsafeAtomicAdd(dbias + c + j, sb[j]);
+  }
+}
+
+// n fp32 values at p set to zero; the x slice [0, xw) and the B/C channels
+// [d_inner, conv_dim) of a per-channel array (width values per channel)
+__global__ __launch_bounds__(256) void zero_channels_kernel(float* p, int width, int xw,
+                                                            int d_inner, int bc_dim) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= (xw + bc_dim) * width) return;
+  const int ch = i / width, k = i % width;
+  const int c = ch < xw ? ch : d_inner + (ch - xw);
+  p[(int64_t)c * width + k] = 0.0f;
+}
+
+template <typename T>
+void launch_typed(const ConvBwdArgs& a, hipStream_t s) {
+  constexpr int V = Vec16<T>::kN;
+  const int groups = (a.xw + a.bc_dim) / V;
+  const dim3 grid((unsigned)((groups + kThreads - 1) / kThreads),
+                  (unsigned)((a.seqlen + kRun - 1) / kRun), (unsigned)a.batch);
+  hipLaunchKernelGGL(conv1d_silu_bwd_kernel<T>, grid, dim3(kThreads), 0, s,
+                     static_cast<const T*>(a.in), a.in_stride, static_cast<const T*>(a.dout),
+                     a.dout_stride, static_cast<T*>(a.din), a.din_stride, a.w, a.bias,
+                     a.conv_state, a.dw, a.dbias, a.dstate, (int)a.seqlen, (int)a.d_inner, a.xw,
+                     a.bc_dim, a.accumulate);
+}
+
+}  // namespace
+
+hipError_t launch_conv1d_silu_backward(const ConvBwdArgs& a, int dtype, hipStream_t s) {
+  if (!a.accumulate) {
+    const int ch = a.xw + a.bc_dim;
+    hipLaunchKernelGGL(zero_channels_kernel, dim3((unsigned)((ch * 4 + 255) / 256)), dim3(256), 0,
+                       s, a.dw, 4, a.xw, (int)a.d_inner, a.bc_dim);
+    if (a.dbias)
+      hipLaunchKernelGGL(zero_channels_kernel, dim3((unsigned)((ch + 255) / 256)), dim3(256), 0,
+                         s, a.dbias, 1, a.xw, (int)a.d_inner, a.bc_dim);
+  }
+  if (dtype == MM_BF16) launch_typed<bf16>(a, s);
+  else launch_typed<float>(a, s);
+  return hipGetLastError();
+}
+
+}  // namespace mmssd

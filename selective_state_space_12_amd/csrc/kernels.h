@@ -256,4 +256,23 @@ size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t
                            int64_t d_state, int dtype);
 hipError_t launch_ssd_backward(const BwdArgs& a, void* workspace, hipStream_t s);
 
+// Conv backward (conv1d_silu_bwd.hip): gradients of sum dout * conv1d_silu(in).
+struct ConvBwdArgs {
+  const void* in;
+  int64_t in_stride;
+  const void* dout;
+  int64_t dout_stride;
+  void* din;
+  int64_t din_stride;
+  const float* w;
+  const float* bias;
+  const float* conv_state;  // (batch, 3, conv_dim) history, or NULL (zeros)
+  float* dw;
+  float* dbias;
+  float* dstate;            // (batch, 3, conv_dim) or NULL
+  int64_t batch, seqlen, d_inner;
+  int xw, bc_dim, accumulate;  // xw: active x channels
+};
+hipError_t launch_conv1d_silu_backward(const ConvBwdArgs& a, int dtype, hipStream_t s);
+
 }  // namespace mmssd

@@ -187,31 +187,57 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
         dst[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] = from_f32<T>(hacc[t][i]);
   };
 
-  for (int c = 0; c < k.nchunks; ++c) {
+  // The next chunk's x, B rows and dt are loaded into registers while this
+  // chunk's update runs (every thread's vector slots are fixed, so the
+  // loads of a chunk are all in flight at once).
+  constexpr int NXV = (Q * (P / VB) + kBThreads - 1) / kBThreads;
+  constexpr int NBV = (Q * (N / VB) + kBThreads - 1) / kBThreads;
+  Vec16<T> px[NXV], pb[NBV];
+  float pdt = 0.0f;
+  auto prefetch = [&](int c) {
     const int64_t row0 = rowb + (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
+#pragma unroll
+    for (int v = 0; v < NXV; ++v) {
+      const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
+      px[v] = (idx < Q * (P / VB) && s < len) ? load16(Xp + (row0 + s) * k.xs + (int64_t)h * P + p0)
+                                              : zero16<T>();
+    }
+#pragma unroll
+    for (int v = 0; v < NBV; ++v) {
+      const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
+      pb[v] = (idx < Q * (N / VB) && s < len) ? load16(Bp + (row0 + s) * k.bs + n0) : zero16<T>();
+    }
+    if (wave == 0) pdt = lane < len ? to_f32(DTp[(row0 + lane) * k.dts + h]) : 0.0f;
+  };
+  if (k.nchunks > 0) prefetch(0);
+
+  for (int c = 0; c < k.nchunks; ++c) {
     store_state(c);
     // x^T and B^T: consecutive lanes take consecutive tokens (distinct banks)
-    for (int idx = tid; idx < Q * (P / VB); idx += kBThreads) {
-      const int s = idx % Q, p0 = (idx / Q) * VB;
-      const Vec16<T> v = s < len ? load16(Xp + (row0 + s) * k.xs + (int64_t)h * P + p0) : zero16<T>();
 #pragma unroll
-      for (int j = 0; j < VB; ++j) XT[(p0 + j) * TQ + s] = v.v[j];
+    for (int v = 0; v < NXV; ++v) {
+      const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
+      if (idx < Q * (P / VB))
+#pragma unroll
+        for (int j = 0; j < VB; ++j) XT[(p0 + j) * TQ + s] = px[v].v[j];
     }
-    for (int idx = tid; idx < Q * (N / VB); idx += kBThreads) {
-      const int s = idx % Q, n0 = (idx / Q) * VB;
-      const Vec16<T> v = s < len ? load16(Bp + (row0 + s) * k.bs + n0) : zero16<T>();
 #pragma unroll
-      for (int j = 0; j < VB; ++j) BT[(n0 + j) * TQ + s] = v.v[j];
+    for (int v = 0; v < NBV; ++v) {
+      const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
+      if (idx < Q * (N / VB))
+#pragma unroll
+        for (int j = 0; j < VB; ++j) BT[(n0 + j) * TQ + s] = pb[v].v[j];
     }
     if (wave == 0) {
-      const float d = lane < len ? to_f32(DTp[(row0 + lane) * k.dts + h]) : 0.0f;
+      const float d = pdt;
       const float lv = chunk_cumsum(d * Ah2, lane);
       const float le = __shfl(lv, 63);
       lam[lane] = lv;
       wsc[lane] = __builtin_amdgcn_exp2f(le - lv) * d;
     }
     __syncthreads();
+    if (c + 1 < k.nchunks) prefetch(c + 1);
     if (owns) {
       const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
 #pragma unroll
@@ -248,7 +274,7 @@ struct ChunkLds {
   static constexpr int TP2 = P + bpad<T>();  // Gc^T and Hp^T rows (n-major)
   static constexpr size_t elems = (size_t)2 * kBQ * NP + (size_t)P * TQ + (size_t)2 * kBQ * NN +
                                   (size_t)2 * N * TQ + (size_t)P * NN + (size_t)2 * N * TP2;
-  static constexpr int kFloats = 12 * kBQ + kBWaves;
+  static constexpr int kFloats = 15 * kBQ + 2 * kBWaves;
   static constexpr size_t bytes = elems * sizeof(T) + kFloats * sizeof(float);
 };
 
@@ -269,6 +295,12 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
   constexpr int NBLK = Q / 16;        // 16-token blocks per chunk
   static_assert(NBLK == 4, "four s-blocks and four t-blocks, one per wave");
   static_assert(P % 32 == 0, "d_head is a whole number of K=32 slices");
+  constexpr int NXV = (Q * (P / VB) + kBThreads - 1) / kBThreads;  // x, dy vectors per thread
+  constexpr int NBV = (Q * (N / VB) + kBThreads - 1) / kBThreads;  // B, C vectors per thread
+  constexpr int NHV = (P * (N / VB) + kBThreads - 1) / kBThreads;  // Hp vectors per thread
+  constexpr int TPH = TP / 2;                  // d_head tiles per column half
+  constexpr int TNH = TN >= 2 ? TN / 2 : 1;    // d_state tiles per column half
+  static_assert(TP % 2 == 0 && (TN == 1 || TN % 2 == 0), "columns split in two halves");
 
   extern __shared__ __align__(16) unsigned char smem[];
   T* Xn = reinterpret_cast<T*>(smem);  // [Q][NP]
@@ -287,10 +319,10 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
   float* sc = eL + Q;     // exp(Lambda_e - Lambda_s)
   float* rpart = sc + Q;  // sum_s W[t,s] over each s-block: [4][Q]
   float* csum = rpart + 4 * Q;  // sum_t W[t,s]
-  float* esum = csum + Q; // dt_s exp(..) x_s^T Gc B_s
-  float* t1 = esum + Q;   // exp(Lambda_t) dy_t . Hp C_t
-  float* expl = t1 + Q;   // x_s . u_s
-  float* hgw = expl + Q;  // <Gc, H_e> over each wave's tiles: [8]
+  float* esum = csum + Q;     // dt_s exp(..) x_s^T Gc B_s, per column half: [2][Q]
+  float* t1 = esum + 2 * Q;   // exp(Lambda_t) dy_t . Hp C_t, per column half: [2][Q]
+  float* expl = t1 + 2 * Q;   // x_s . u_s, per column half: [2][Q]
+  float* hgw = expl + 2 * Q;  // <Gc, H_e> over each wave's tiles: [2][8] by chunk parity
 
   int b, h;
   unit_of(k.heads, &b, &h);
@@ -324,49 +356,83 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
         gacc[t][i] = (gin && owns) ? gin[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] : 0.0f;
   }
   float da_acc = 0.0f;  // wave 0: sum_r dt_r da_r of this lane's tokens
-  float dd_acc = 0.0f;  // waves 0-3: sum dy . x over this lane's entries
+  float dd_acc = 0.0f;  // sum dy . x over this lane's entries
 
   for (int c = k.nchunks - 1; c >= 0; --c) {
     const int64_t row0 = rowb + (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
 
-    // ---- stage: token rows (zero past len), transposed copies, Hp^T, Gc ----
-    for (int idx = tid; idx < Q * (P / VB); idx += kBThreads) {
-      const int s = idx % Q, p0 = (idx / Q) * VB;
-      Vec16<T> xv = zero16<T>(), yv = zero16<T>();
-      if (s < len) {
-        xv = load16(Xp + (row0 + s) * k.xs + (int64_t)h * P + p0);
-        yv = load16(DYp + (row0 + s) * k.dys + (int64_t)h * P + p0);
-      }
-      store16(Xn + s * NP + p0, xv);
-      store16(Yn + s * NP + p0, yv);
+    // ---- stage: every global load of the chunk first (one round trip), then
+    // token rows (zero past len), transposed copies, Hp^T and Gc into LDS ----
+    Vec16<T> vx[NXV], vy[NXV], vb[NBV], vc[NBV], vh[NHV];
 #pragma unroll
-      for (int j = 0; j < VB; ++j) YT[(p0 + j) * TQ + s] = yv.v[j];
+    for (int v = 0; v < NXV; ++v) {
+      const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
+      const bool ld = idx < Q * (P / VB) && s < len;
+      vx[v] = ld ? load16(Xp + (row0 + s) * k.xs + (int64_t)h * P + p0) : zero16<T>();
+      vy[v] = ld ? load16(DYp + (row0 + s) * k.dys + (int64_t)h * P + p0) : zero16<T>();
     }
-    for (int idx = tid; idx < Q * (N / VB); idx += kBThreads) {
-      const int s = idx % Q, n0 = (idx / Q) * VB;
-      Vec16<T> bv = zero16<T>(), cv = zero16<T>();
-      if (s < len) {
-        bv = load16(Bp + (row0 + s) * k.bs + n0);
-        cv = load16(Cp + (row0 + s) * k.cs + n0);
-      }
-      store16(Bn + s * NN + n0, bv);
-      store16(Cn + s * NN + n0, cv);
 #pragma unroll
-      for (int j = 0; j < VB; ++j) {
-        BT[(n0 + j) * TQ + s] = bv.v[j];
-        CT[(n0 + j) * TQ + s] = cv.v[j];
-      }
+    for (int v = 0; v < NBV; ++v) {
+      const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
+      const bool ld = idx < Q * (N / VB) && s < len;
+      vb[v] = ld ? load16(Bp + (row0 + s) * k.bs + n0) : zero16<T>();
+      vc[v] = ld ? load16(Cp + (row0 + s) * k.cs + n0) : zero16<T>();
     }
+    const T* hp = Hst + (int64_t)c * (P * N);
+#pragma unroll
+    for (int v = 0; v < NHV; ++v) {
+      const int idx = tid + v * kBThreads, p = idx % P, n0 = (idx / P) * VB;
+      vh[v] = idx < P * (N / VB) ? load16(hp + p * N + n0) : zero16<T>();
+    }
+    // <Gc, H_e> on this wave's tiles (H_e: the state after this chunk; gacc
+    // still holds Gc), into this chunk's half of the per-wave slots
+    float hdot = 0.0f;
     {
-      const T* hp = Hst + (int64_t)c * (P * N);
-      for (int idx = tid; idx < P * (N / VB); idx += kBThreads) {
-        const int p = idx % P, n0 = (idx / P) * VB;
-        const Vec16<T> v = load16(hp + p * N + n0);
+      const T* hn = Hst + (int64_t)(c + 1) * (P * N);
 #pragma unroll
-        for (int j = 0; j < VB; ++j) HT[(n0 + j) * TP2 + p] = v.v[j];
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          hdot += owns ? gacc[t][i] * to_f32(hn[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16])
+                       : 0.0f;
+    }
+    const float dtl = (wave == 0 && lane < len) ? to_f32(DTp[(row0 + lane) * k.dts + h]) : 0.0f;
+#pragma unroll
+    for (int v = 0; v < NXV; ++v) {
+      const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
+      if (idx < Q * (P / VB)) {
+        store16(Xn + s * NP + p0, vx[v]);
+        store16(Yn + s * NP + p0, vy[v]);
+#pragma unroll
+        for (int j = 0; j < VB; ++j) YT[(p0 + j) * TQ + s] = vy[v].v[j];
       }
     }
+#pragma unroll
+    for (int v = 0; v < NBV; ++v) {
+      const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
+      if (idx < Q * (N / VB)) {
+        store16(Bn + s * NN + n0, vb[v]);
+        store16(Cn + s * NN + n0, vc[v]);
+#pragma unroll
+        for (int j = 0; j < VB; ++j) {
+          BT[(n0 + j) * TQ + s] = vb[v].v[j];
+          CT[(n0 + j) * TQ + s] = vc[v].v[j];
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NHV; ++v) {
+      const int idx = tid + v * kBThreads, p = idx % P, n0 = (idx / P) * VB;
+      if (idx < P * (N / VB))
+#pragma unroll
+        for (int j = 0; j < VB; ++j) HT[(n0 + j) * TP2 + p] = vh[v].v[j];
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) hdot += __shfl_xor(hdot, off);
+    // two halves by chunk parity: wave 0 may still read the other chunk's
+    // half (after the last barrier) while a faster wave writes this one
+    if (lane == 0) hgw[(c & 1) * kBWaves + wave] = hdot;
     if (owns) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
@@ -379,7 +445,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
         }
     }
     if (wave == 0) {
-      const float d = lane < len ? to_f32(DTp[(row0 + lane) * k.dts + h]) : 0.0f;
+      const float d = dtl;
       const float lv = chunk_cumsum(d * Ah2, lane);
       const float le = __shfl(lv, 63);
       lam[lane] = lv;
@@ -388,262 +454,277 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
       sc[lane] = __builtin_amdgcn_exp2f(le - lv);
 #pragma unroll
       for (int j = 0; j < 4; ++j) rpart[j * Q + lane] = 0.0f;
-      if (lane < kBWaves) hgw[lane] = 0.0f;
     }
     __syncthreads();
 
-    if (wave < NBLK) {
-      // ---- s-side: rows s of one 16-token block: dx, dB, column sums ----
-      const int sb = wave, s0 = sb * 16;
-      const int srow = s0 + r16;  // A-operand row of this lane
-      const float scs = sc[srow];
-      f32x4 au[TP], ab[TN];
-#pragma unroll
-      for (int i = 0; i < TP; ++i) au[i] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < TN; ++i) ab[i] = f32x4{0, 0, 0, 0};
-      // end-state terms: u += exp(..) B_s Gc^T,  dB-part += exp(..) x_s Gc
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        Frag8<T> bf;
-        frag_row_scaled(bf, Bn + srow * NN, kb * 32 + g * 8, N, scs);
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          Frag8<T> gf;
-          frag_row(gf, Gs + (pt * 16 + r16) * NN, kb * 32 + g * 8, N);
-          au[pt] = mma(bf, gf, au[pt]);
-        }
-      }
-#pragma unroll
-      for (int kp = 0; kp < PKB; ++kp) {
-        Frag8<T> xf;
-        frag_row_scaled(xf, Xn + srow * NP, kp * 32 + g * 8, P, scs);
-#pragma unroll
-        for (int n2 = 0; n2 < TN; ++n2) {
-          Frag8<T> gf;
-          frag_load8(gf, GT + (n2 * 16 + r16) * TP2 + kp * 32 + g * 8);
-          ab[n2] = mma(xf, gf, ab[n2]);
-        }
-      }
-      // esum_s = dt_s sum_n ab[s][n] B[s][n]  (rows s = s0 + 4g + i)
+    {
+      // ---- this wave: s-block and t-block `blk`, column half `hf` (d_head
+      // tiles [pb0, pb0+TPH), d_state tiles [nb0, nb0+TNH)); the two waves of
+      // a block share its Q x Q products and split the outputs' columns ----
+      const int blk = wave % NBLK, hf = wave / NBLK;
+      const int pb0 = hf * TPH, nb0 = hf * TNH;
+      const bool nlive = nb0 < TN;  // this half has d_state tiles (wave-uniform)
+
+      // ---- s-side: rows s of the block: dx, dB, column sums of W ----
       {
-        float e[4];
+        const int s0 = blk * 16, srow = s0 + r16;  // A-operand row of this lane
+        const float scs = sc[srow];
+        f32x4 au[TPH], ab[TNH];
+#pragma unroll
+        for (int i = 0; i < TPH; ++i) au[i] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < TNH; ++i) ab[i] = f32x4{0, 0, 0, 0};
+        // end-state terms: u += exp(..) B_s Gc^T,  dB-part += exp(..) x_s Gc
+#pragma unroll 1
+        for (int kb = 0; kb < NKB; ++kb) {
+          Frag8<T> bf;
+          frag_row_scaled(bf, Bn + srow * NN, kb * 32 + g * 8, N, scs);
+#pragma unroll
+          for (int pp = 0; pp < TPH; ++pp) {
+            Frag8<T> gf;
+            frag_row(gf, Gs + ((pb0 + pp) * 16 + r16) * NN, kb * 32 + g * 8, N);
+            au[pp] = mma(bf, gf, au[pp]);
+          }
+        }
+        if (nlive) {
+#pragma unroll 1
+          for (int kp = 0; kp < PKB; ++kp) {
+            Frag8<T> xf;
+            frag_row_scaled(xf, Xn + srow * NP, kp * 32 + g * 8, P, scs);
+#pragma unroll
+            for (int nn = 0; nn < TNH; ++nn) {
+              Frag8<T> gf;
+              frag_load8(gf, GT + ((nb0 + nn) * 16 + r16) * TP2 + kp * 32 + g * 8);
+              ab[nn] = mma(xf, gf, ab[nn]);
+            }
+          }
+        }
+        // esum_s (this half) = dt_s sum_n ab[s][n] B[s][n]  (rows s = s0 + 4g + i)
+        {
+          float e[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int s = s0 + g * 4 + i;
+            float v = 0.0f;
+            if (nlive)
+#pragma unroll
+              for (int nn = 0; nn < TNH; ++nn)
+                v += ab[nn][i] * to_f32(Bn[s * NN + (nb0 + nn) * 16 + r16]);
+            e[i] = v;
+          }
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[i] += __shfl_xor(e[i], off);
+          if (r16 == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) esum[hf * Q + s0 + g * 4 + i] = e[i] * dtv[s0 + g * 4 + i];
+        }
+        // diagonal-block terms over t-block pairs (2ip, 2ip+1) with t >= s
+        const float lam_s = lam[srow], dt_s = dtv[srow];
+        float csum_l = 0.0f;
+#pragma unroll 1
+        for (int ip = blk / 2; ip < NBLK / 2; ++ip) {
+          const int ta = 2 * ip, tb = 2 * ip + 1;
+          const bool doa = ta >= blk;  // block ta has t >= s somewhere (wave-uniform)
+          f32x4 gA = {0, 0, 0, 0}, gB = {0, 0, 0, 0}, qA = {0, 0, 0, 0}, qB = {0, 0, 0, 0};
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            Frag8<T> bs, ca, cb;
+            frag_row(bs, Bn + srow * NN, kb * 32 + g * 8, N);
+            frag_row(cb, Cn + (tb * 16 + r16) * NN, kb * 32 + g * 8, N);
+            gB = mma(cb, bs, gB);
+            if (doa) {
+              frag_row(ca, Cn + (ta * 16 + r16) * NN, kb * 32 + g * 8, N);
+              gA = mma(ca, bs, gA);
+            }
+          }
+#pragma unroll
+          for (int kp = 0; kp < PKB; ++kp) {
+            Frag8<T> xs, ya, yb;
+            frag_load8(xs, Xn + srow * NP + kp * 32 + g * 8);
+            frag_load8(yb, Yn + (tb * 16 + r16) * NP + kp * 32 + g * 8);
+            qB = mma(yb, xs, qB);
+            if (doa) {
+              frag_load8(ya, Yn + (ta * 16 + r16) * NP + kp * 32 + g * 8);
+              qA = mma(ya, xs, qA);
+            }
+          }
+          // lane: G[t][s], Q[t][s] for s = srow, t = ta*16 + 4g + i (slot i)
+          // and t = tb*16 + 4g + i (slot 4 + i)
+          Frag8<T> mf, kf;
+          float rw[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int t = (j < 4 ? ta : tb) * 16 + g * 4 + (j & 3);
+            const float gv = j < 4 ? gA[j] : gB[j - 4];
+            const float qv = j < 4 ? qA[j] : qB[j - 4];
+            const float dec = t >= srow ? __builtin_amdgcn_exp2f(lam[t] - lam_s) : 0.0f;
+            frag_set(mf, j, gv * dec);
+            frag_set(kf, j, qv * dec);
+            const float w = gv * qv * dec * dt_s;
+            rw[j] = w;
+            csum_l += w;
+          }
+          if (hf == 0) {
+            // row sums of W over this block's 16 s (lanes r16), per t
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) rw[j] += __shfl_xor(rw[j], off);
+            if (r16 == 0) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                rpart[blk * Q + (j < 4 ? ta : tb) * 16 + g * 4 + (j & 3)] = rw[j];
+            }
+          }
+          // u += M^T dy  (k = t in the slot order above), dB-part += K^T C
+#pragma unroll
+          for (int pp = 0; pp < TPH; ++pp) {
+            Frag8<T> yf;
+            const T* yr = YT + ((pb0 + pp) * 16 + r16) * TQ;
+            frag_load4x2(yf, yr + ta * 16 + g * 4, yr + tb * 16 + g * 4);
+            au[pp] = mma(mf, yf, au[pp]);
+          }
+          if (nlive) {
+#pragma unroll
+            for (int nn = 0; nn < TNH; ++nn) {
+              Frag8<T> cf;
+              const T* cr = CT + ((nb0 + nn) * 16 + r16) * TQ;
+              frag_load4x2(cf, cr + ta * 16 + g * 4, cr + tb * 16 + g * 4);
+              ab[nn] = mma(kf, cf, ab[nn]);
+            }
+          }
+        }
+        // column sums: over the 4 t-slots of each group, then the 4 groups
+        csum_l += __shfl_xor(csum_l, 16);
+        csum_l += __shfl_xor(csum_l, 32);
+        if (hf == 0 && g == 0) csum[srow] = csum_l;
+        // epilogue: dx = dt_s u + D dy, x_s . u_s and dy . x over this half's
+        // d_head columns, dB atomics over its d_state columns
+        float ex[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = s0 + g * 4 + i;
-          float v = 0.0f;
+          const float dts = dtv[s];
+          const bool live = s < len;
 #pragma unroll
-          for (int n2 = 0; n2 < TN; ++n2) v += ab[n2][i] * to_f32(Bn[s * NN + n2 * 16 + r16]);
-          e[i] = v;
+          for (int pp = 0; pp < TPH; ++pp) {
+            const int p = (pb0 + pp) * 16 + r16;
+            const float xv = to_f32(Xn[s * NP + p]), yv = to_f32(Yn[s * NP + p]);
+            ex[i] += xv * au[pp][i];
+            dd_acc += xv * yv;
+            if (live)
+              grad_store(DXp + (row0 + s) * k.dxs + (int64_t)h * P + p, dts * au[pp][i] + Dh * yv,
+                         k.accumulate);
+          }
+          if (live && nlive) {
+#pragma unroll
+            for (int nn = 0; nn < TNH; ++nn)
+              unsafeAtomicAdd(k.dB + (row0 + s) * k.dbs + (nb0 + nn) * 16 + r16, dts * ab[nn][i]);
+          }
         }
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) e[i] += __shfl_xor(e[i], off);
+          for (int i = 0; i < 4; ++i) ex[i] += __shfl_xor(ex[i], off);
         if (r16 == 0)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) esum[s0 + g * 4 + i] = e[i] * dtv[s0 + g * 4 + i];
+          for (int i = 0; i < 4; ++i) expl[hf * Q + s0 + g * 4 + i] = ex[i];
       }
-      // diagonal-block terms over t-block pairs (2ip, 2ip+1) with t >= s
-      const float lam_s = lam[srow], dt_s = dtv[srow];
-      float csum_l = 0.0f;
-#pragma unroll 1
-      for (int ip = sb / 2; ip < NBLK / 2; ++ip) {
-        const int ta = 2 * ip, tb = 2 * ip + 1;
-        const bool doa = ta >= sb;  // block ta has t >= s somewhere (wave-uniform)
-        f32x4 gA = {0, 0, 0, 0}, gB = {0, 0, 0, 0}, qA = {0, 0, 0, 0}, qB = {0, 0, 0, 0};
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          Frag8<T> bs, ca, cb;
-          frag_row(bs, Bn + srow * NN, kb * 32 + g * 8, N);
-          frag_row(cb, Cn + (tb * 16 + r16) * NN, kb * 32 + g * 8, N);
-          gB = mma(cb, bs, gB);
-          if (doa) {
-            frag_row(ca, Cn + (ta * 16 + r16) * NN, kb * 32 + g * 8, N);
-            gA = mma(ca, bs, gA);
-          }
-        }
-#pragma unroll
-        for (int kp = 0; kp < PKB; ++kp) {
-          Frag8<T> xs, ya, yb;
-          frag_load8(xs, Xn + srow * NP + kp * 32 + g * 8);
-          frag_load8(yb, Yn + (tb * 16 + r16) * NP + kp * 32 + g * 8);
-          qB = mma(yb, xs, qB);
-          if (doa) {
-            frag_load8(ya, Yn + (ta * 16 + r16) * NP + kp * 32 + g * 8);
-            qA = mma(ya, xs, qA);
-          }
-        }
-        // lane: G[t][s], Q[t][s] for s = srow, t = ta*16 + 4g + i (slot i)
-        // and t = tb*16 + 4g + i (slot 4 + i)
-        Frag8<T> mf, kf;
-        float rw[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = (j < 4 ? ta : tb) * 16 + g * 4 + (j & 3);
-          const float gv = j < 4 ? gA[j] : gB[j - 4];
-          const float qv = j < 4 ? qA[j] : qB[j - 4];
-          const float dec = t >= srow ? __builtin_amdgcn_exp2f(lam[t] - lam_s) : 0.0f;
-          frag_set(mf, j, gv * dec);
-          frag_set(kf, j, qv * dec);
-          const float w = gv * qv * dec * dt_s;
-          rw[j] = w;
-          csum_l += w;
-        }
-        // row sums of W over this block's 16 s (lanes r16), per t
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) rw[j] += __shfl_xor(rw[j], off);
-        if (r16 == 0) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) rpart[sb * Q + (j < 4 ? ta : tb) * 16 + g * 4 + (j & 3)] = rw[j];
-        }
-        // u += M^T dy  (k = t in the slot order above), dB-part += K^T C
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          Frag8<T> yf;
-          const T* yr = YT + (pt * 16 + r16) * TQ;
-          frag_load4x2(yf, yr + ta * 16 + g * 4, yr + tb * 16 + g * 4);
-          au[pt] = mma(mf, yf, au[pt]);
-        }
-#pragma unroll
-        for (int n2 = 0; n2 < TN; ++n2) {
-          Frag8<T> cf;
-          const T* cr = CT + (n2 * 16 + r16) * TQ;
-          frag_load4x2(cf, cr + ta * 16 + g * 4, cr + tb * 16 + g * 4);
-          ab[n2] = mma(kf, cf, ab[n2]);
-        }
-      }
-      // column sums: over the 4 t-slots of each group, then the 4 groups
-      csum_l += __shfl_xor(csum_l, 16);
-      csum_l += __shfl_xor(csum_l, 32);
-      if (g == 0) csum[srow] = csum_l;
-      // epilogue: dx = dt_s u + D dy, x_s . u_s, dy . x, dB atomics
-      float ex[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = s0 + g * 4 + i;
-        const float dts = dtv[s];
-        const bool live = s < len;
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          const int p = pt * 16 + r16;
-          const float xv = to_f32(Xn[s * NP + p]), yv = to_f32(Yn[s * NP + p]);
-          ex[i] += xv * au[pt][i];
-          dd_acc += xv * yv;
-          if (live)
-            grad_store(DXp + (row0 + s) * k.dxs + (int64_t)h * P + p, dts * au[pt][i] + Dh * yv,
-                       k.accumulate);
-        }
-        if (live) {
-#pragma unroll
-          for (int n2 = 0; n2 < TN; ++n2)
-            unsafeAtomicAdd(k.dB + (row0 + s) * k.dbs + n2 * 16 + r16, dts * ab[n2][i]);
-        }
-      }
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ex[i] += __shfl_xor(ex[i], off);
-      if (r16 == 0)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) expl[s0 + g * 4 + i] = ex[i];
-    } else {
-      // ---- t-side: rows t of one 16-token block: dC and the Hp term ----
-      const int tb = wave - NBLK, t0 = tb * 16;
-      const int trow = t0 + r16;
-      const float lam_t = lam[trow];
-      f32x4 ac[TN];
-#pragma unroll
-      for (int i = 0; i < TN; ++i) ac[i] = f32x4{0, 0, 0, 0};
-      // off-diagonal output term: exp(Lambda_t) dy_t Hp
-#pragma unroll
-      for (int kp = 0; kp < PKB; ++kp) {
-        Frag8<T> yf;
-        frag_row_scaled(yf, Yn + trow * NP, kp * 32 + g * 8, P, eL[trow]);
-#pragma unroll
-        for (int n2 = 0; n2 < TN; ++n2) {
-          Frag8<T> hf;
-          frag_load8(hf, HT + (n2 * 16 + r16) * TP2 + kp * 32 + g * 8);
-          ac[n2] = mma(yf, hf, ac[n2]);
-        }
-      }
+
+      // ---- t-side: rows t of the block: dC (this half's columns), Hp term ----
       {
-        float e[4];
+        const int t0 = blk * 16, trow = t0 + r16;
+        const float lam_t = lam[trow];
+        f32x4 ac[TNH];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = t0 + g * 4 + i;
-          float v = 0.0f;
-#pragma unroll
-          for (int n2 = 0; n2 < TN; ++n2) v += ac[n2][i] * to_f32(Cn[t * NN + n2 * 16 + r16]);
-          e[i] = v;
-        }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) e[i] += __shfl_xor(e[i], off);
-        if (r16 == 0)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) t1[t0 + g * 4 + i] = e[i];
-      }
-      // diagonal-block term over s-block pairs (2jp, 2jp+1) with s <= t
+        for (int i = 0; i < TNH; ++i) ac[i] = f32x4{0, 0, 0, 0};
+        if (nlive) {
+          // off-diagonal output term: exp(Lambda_t) dy_t Hp
 #pragma unroll 1
-      for (int jp = 0; jp <= tb / 2; ++jp) {
-        const int sa = 2 * jp, sb2 = 2 * jp + 1;
-        const bool dob = sb2 <= tb;  // wave-uniform
-        f32x4 rA = {0, 0, 0, 0}, rB = {0, 0, 0, 0};
+          for (int kp = 0; kp < PKB; ++kp) {
+            Frag8<T> yf;
+            frag_row_scaled(yf, Yn + trow * NP, kp * 32 + g * 8, P, eL[trow]);
 #pragma unroll
-        for (int kp = 0; kp < PKB; ++kp) {
-          Frag8<T> yt, xa, xb;
-          frag_load8(yt, Yn + trow * NP + kp * 32 + g * 8);
-          frag_load8(xa, Xn + (sa * 16 + r16) * NP + kp * 32 + g * 8);
-          rA = mma(xa, yt, rA);
-          if (dob) {
-            frag_load8(xb, Xn + (sb2 * 16 + r16) * NP + kp * 32 + g * 8);
-            rB = mma(xb, yt, rB);
+            for (int nn = 0; nn < TNH; ++nn) {
+              Frag8<T> hfr;
+              frag_load8(hfr, HT + ((nb0 + nn) * 16 + r16) * TP2 + kp * 32 + g * 8);
+              ac[nn] = mma(yf, hfr, ac[nn]);
+            }
           }
         }
-        // lane: (x_s . dy_t) for t = trow, s = sa*16 + 4g + i (slot i), sb2*16 + 4g + i (slot 4+i)
-        Frag8<T> kf;
+        {
+          float e[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int s = (j < 4 ? sa : sb2) * 16 + g * 4 + (j & 3);
-          const float rv = j < 4 ? rA[j] : rB[j - 4];
-          const float f = s <= trow ? __builtin_amdgcn_exp2f(lam_t - lam[s]) * dtv[s] : 0.0f;
-          frag_set(kf, j, rv * f);
+          for (int i = 0; i < 4; ++i) {
+            const int t = t0 + g * 4 + i;
+            float v = 0.0f;
+            if (nlive)
+#pragma unroll
+              for (int nn = 0; nn < TNH; ++nn)
+                v += ac[nn][i] * to_f32(Cn[t * NN + (nb0 + nn) * 16 + r16]);
+            e[i] = v;
+          }
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[i] += __shfl_xor(e[i], off);
+          if (r16 == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t1[hf * Q + t0 + g * 4 + i] = e[i];
         }
+        if (nlive) {
+          // diagonal-block term over s-block pairs (2jp, 2jp+1) with s <= t
+#pragma unroll 1
+          for (int jp = 0; jp <= blk / 2; ++jp) {
+            const int sa = 2 * jp, sb2 = 2 * jp + 1;
+            const bool dob = sb2 <= blk;  // wave-uniform
+            f32x4 rA = {0, 0, 0, 0}, rB = {0, 0, 0, 0};
 #pragma unroll
-        for (int n2 = 0; n2 < TN; ++n2) {
-          Frag8<T> bf;
-          const T* br = BT + (n2 * 16 + r16) * TQ;
-          frag_load4x2(bf, br + sa * 16 + g * 4, br + sb2 * 16 + g * 4);
-          ac[n2] = mma(kf, bf, ac[n2]);
-        }
-      }
+            for (int kp = 0; kp < PKB; ++kp) {
+              Frag8<T> yt, xa, xb;
+              frag_load8(yt, Yn + trow * NP + kp * 32 + g * 8);
+              frag_load8(xa, Xn + (sa * 16 + r16) * NP + kp * 32 + g * 8);
+              rA = mma(xa, yt, rA);
+              if (dob) {
+                frag_load8(xb, Xn + (sb2 * 16 + r16) * NP + kp * 32 + g * 8);
+                rB = mma(xb, yt, rB);
+              }
+            }
+            // lane: (x_s . dy_t) for t = trow, s = sa*16 + 4g + i (slot i),
+            // sb2*16 + 4g + i (slot 4 + i)
+            Frag8<T> kf;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + g * 4 + i;
-        if (t < len) {
+            for (int j = 0; j < 8; ++j) {
+              const int s = (j < 4 ? sa : sb2) * 16 + g * 4 + (j & 3);
+              const float rv = j < 4 ? rA[j] : rB[j - 4];
+              const float f = s <= trow ? __builtin_amdgcn_exp2f(lam_t - lam[s]) * dtv[s] : 0.0f;
+              frag_set(kf, j, rv * f);
+            }
 #pragma unroll
-          for (int n2 = 0; n2 < TN; ++n2)
-            unsafeAtomicAdd(k.dC + (row0 + t) * k.dcs + n2 * 16 + r16, ac[n2][i]);
+            for (int nn = 0; nn < TNH; ++nn) {
+              Frag8<T> bf;
+              const T* br = BT + ((nb0 + nn) * 16 + r16) * TQ;
+              frag_load4x2(bf, br + sa * 16 + g * 4, br + sb2 * 16 + g * 4);
+              ac[nn] = mma(kf, bf, ac[nn]);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = t0 + g * 4 + i;
+            if (t < len) {
+#pragma unroll
+              for (int nn = 0; nn < TNH; ++nn)
+                unsafeAtomicAdd(k.dC + (row0 + t) * k.dcs + (nb0 + nn) * 16 + r16, ac[nn][i]);
+            }
+          }
         }
       }
     }
 
     // ---- every wave: <Gc, H_e> over its tiles, then dGp ----
     if (owns) {
-      const T* he = Hst + (int64_t)(c + 1) * (P * N);
-      float dot = 0.0f;
-#pragma unroll
-      for (int t = 0; t < TPW; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dot += gacc[t][i] * to_f32(he[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16]);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) dot += __shfl_xor(dot, off);
-      if (lane == 0) hgw[wave] = dot;
       const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
@@ -672,12 +753,13 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
     if (wave == 0) {
       const int t = lane;
       // fixed summation order: the result does not depend on wave timing
-      float dl = t1[t] + (((rpart[t] + rpart[Q + t]) + rpart[2 * Q + t]) + rpart[3 * Q + t]) -
-                 csum[t] - esum[t];
+      float dl = (t1[t] + t1[Q + t]) +
+                 (((rpart[t] + rpart[Q + t]) + rpart[2 * Q + t]) + rpart[3 * Q + t]) - csum[t] -
+                 (esum[t] + esum[Q + t]);
       if (t == Q - 1) {
         float hg = 0.0f;
 #pragma unroll
-        for (int j = 0; j < kBWaves; ++j) hg += hgw[j];
+        for (int j = 0; j < kBWaves; ++j) hg += hgw[(c & 1) * kBWaves + j];
         dl += hg;
       }
       // suffix sum over t' >= t
@@ -688,11 +770,11 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
         if (lane + off < 64) suf += v;
       }
       if (t < len) {
-        grad_store(DDTp + (row0 + t) * k.ddts + h, expl[t] + Ah * suf, k.accumulate);
+        grad_store(DDTp + (row0 + t) * k.ddts + h, (expl[t] + expl[Q + t]) + Ah * suf, k.accumulate);
         da_acc += dtv[t] * suf;
       }
     }
-    // wave 0 rewrites lam/dtv/eL/sc/rpart/hgw only after its own reads above;
+    // wave 0 rewrites lam/dtv/eL/sc/rpart only after its own reads above;
     // every other array is rewritten after the next barrier
   }
 
@@ -712,7 +794,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
     for (int off = 1; off < 64; off <<= 1) da_acc += __shfl_xor(da_acc, off);
     if (lane == 0) unsafeAtomicAdd(k.dA + h, da_acc);
   }
-  if (k.dD && wave < NBLK) {
+  if (k.dD) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) dd_acc += __shfl_xor(dd_acc, off);
     if (lane == 0) unsafeAtomicAdd(k.dD + h, dd_acc);

@@ -386,4 +386,46 @@ int validate_ssd_backward(const void* x, int64_t x_row_stride, const void* dt,
   return MM_OK;
 }
 
+int validate_conv_backward(const void* xbc_in, int64_t in_row_stride, const void* dout,
+                           int64_t dout_row_stride, const void* dxbc_in, int64_t din_row_stride,
+                           const float* w, const float* bias, const float* conv_state,
+                           const float* dw, const float* dbias, const float* dconv_state,
+                           int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_head,
+                           int64_t d_state, int64_t ngroups, int64_t n_heads_active, int dtype,
+                           int accumulate) {
+  if (!dout || !dw) return MM_ERR_NULL;
+  // the forward's checks with dxbc_in in the output's place (it must not
+  // overlap the input either)
+  const int st = validate_conv(xbc_in, in_row_stride, dxbc_in, din_row_stride, w, bias, conv_state,
+                               batch, seqlen, d_inner, d_head, d_state, ngroups, n_heads_active,
+                               dtype);
+  if (st != MM_OK) return st;
+  if (accumulate != 0 && accumulate != 1) return MM_ERR_SHAPE;
+  const int64_t el = dtype_bytes(dtype);
+  const int64_t conv_dim = d_inner + 2 * ngroups * d_state;
+  const int64_t rows = batch * seqlen;
+  if (dout_row_stride < conv_dim || !mul_ok(rows, dout_row_stride)) return MM_ERR_SHAPE;
+  if ((seqlen + 63) / 64 > kMaxGridYZ) return MM_ERR_SHAPE;
+  if (!rows_aligned(dout, dout_row_stride, el)) return MM_ERR_ALIGN;
+  const void* f32s[] = {dw, dbias, dconv_state};
+  for (const void* p : f32s)
+    if (reinterpret_cast<uintptr_t>(p) % 4 != 0) return MM_ERR_ALIGN;
+  const int64_t sdin = ((rows - 1) * din_row_stride + conv_dim) * el;
+  const int64_t sdout = ((rows - 1) * dout_row_stride + conv_dim) * el;
+  const int64_t sin = ((rows - 1) * in_row_stride + conv_dim) * el;
+  const int64_t sst = batch * 3 * conv_dim * 4;
+  struct R { const void* p; int64_t n; };
+  const R outs[] = {{dxbc_in, sdin}, {dw, conv_dim * 16}, {dbias, conv_dim * 4},
+                    {dconv_state, sst}};
+  const R ins[] = {{xbc_in, sin}, {dout, sdout}, {w, conv_dim * 16}, {bias, conv_dim * 4},
+                   {conv_state, sst}};
+  for (const R& o : outs) {
+    for (const R& i : ins)
+      if (ranges_overlap(o.p, o.n, i.p, i.n)) return MM_ERR_SHAPE;
+    for (const R& o2 : outs)
+      if (&o2 != &o && ranges_overlap(o.p, o.n, o2.p, o2.n)) return MM_ERR_SHAPE;
+  }
+  return MM_OK;
+}
+
 }  // namespace mmssd

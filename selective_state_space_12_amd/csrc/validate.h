@@ -91,6 +91,17 @@ int validate_ssd_step(const float* state, const void* x_t, int64_t x_row_stride,
                       int64_t d_head, int64_t d_state, int64_t ngroups,
                       int64_t n_heads_active, int dtype);
 
+// mm_conv1d_silu_backward: validate_conv's checks with dxbc_in as the
+// output, dout's stride and alignment, accumulate 0 or 1, and no gradient
+// overlapping an input or another gradient.
+int validate_conv_backward(const void* xbc_in, int64_t in_row_stride, const void* dout,
+                           int64_t dout_row_stride, const void* dxbc_in, int64_t din_row_stride,
+                           const float* w, const float* bias, const float* conv_state,
+                           const float* dw, const float* dbias, const float* dconv_state,
+                           int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_head,
+                           int64_t d_state, int64_t ngroups, int64_t n_heads_active, int dtype,
+                           int accumulate);
+
 // Shape part of the backward checks (used by its workspace query too).
 int validate_ssd_backward_shape(int64_t batch, int64_t seqlen, int64_t n_heads, int64_t d_head,
                                 int64_t d_state, int64_t ngroups, int64_t n_heads_active,

@@ -200,6 +200,29 @@ int main() {
            validate_ssd_backward_shape(4, 8192, 64, 64, 64, 1, 64, MM_F32), MM_ERR_UNSUPPORTED);
   }
 
+  // conv backward: 4 x 8192 rows of 4352 channels, bf16
+  {
+    const void* D1 = reinterpret_cast<const void*>(uintptr_t(0x2000000000ull));
+    void* G1 = reinterpret_cast<void*>(uintptr_t(0x3000000000ull));
+    float* DW = reinterpret_cast<float*>(uintptr_t(0x4000000000ull));
+    float* DS = reinterpret_cast<float*>(uintptr_t(0x5000000000ull));
+    auto cb = [&](const void* dout, void* din, float* dw, int64_t ds, int acc) {
+      return validate_conv_backward(P, cd, dout, ds, din, cd, F, nullptr, nullptr, dw, nullptr, DS,
+                                    4, 8192, 4096, 64, 128, 1, 64, MM_BF16, acc);
+    };
+    expect("conv bwd ok", cb(D1, G1, DW, cd, 0), MM_OK);
+    expect("conv bwd accumulate", cb(D1, G1, DW, cd, 1), MM_OK);
+    expect("conv bwd null dout", cb(nullptr, G1, DW, cd, 0), MM_ERR_NULL);
+    expect("conv bwd null dw", cb(D1, G1, nullptr, cd, 0), MM_ERR_NULL);
+    expect("conv bwd din over dout", cb(D1, const_cast<void*>(D1), DW, cd, 0), MM_ERR_SHAPE);
+    expect("conv bwd din over input", cb(D1, const_cast<void*>(P), DW, cd, 0), MM_ERR_SHAPE);
+    expect("conv bwd dout stride short", cb(D1, G1, DW, cd - 8, 0), MM_ERR_SHAPE);
+    expect("conv bwd accumulate 2", cb(D1, G1, DW, cd, 2), MM_ERR_SHAPE);
+    expect("conv bwd dw misaligned", cb(D1, G1, reinterpret_cast<float*>(uintptr_t(0x4000000002ull)),
+                                        cd, 0), MM_ERR_ALIGN);
+    expect("conv bwd dw over dstate", cb(D1, G1, DS, cd, 0), MM_ERR_SHAPE);
+  }
+
   std::printf("%d failure(s)\n", failures);
   return failures == 0 ? 0 : 1;
 }
