@@ -121,16 +121,73 @@ __device__ __forceinline__ void frag_row_scaled(Frag8<T>& f, const T* p, int k0,
   }
 }
 
+// Sum over the 16 lanes of a DPP row (lanes 16r..16r+15), in every lane of
+// the row: rotate-and-add by 8 and 4 within the row, then quad swaps of 2
+// and 1.  Four VALU adds with DPP operands instead of four LDS permutes.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl,
+                                                               0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0x128>(v);  // row_ror:8
+  v += dpp_f32<0x124>(v);  // row_ror:4
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  return v;
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_rows(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl,
+                                                               kRowMask, 0xF, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// within each row of 16 (a lane whose source is outside its row adds 0),
+// then rows 1 and 3 add lane 15 of the row before and rows 2 and 3 add lane
+// 31 (the running total of rows 0-1).  Six DPP adds, no LDS permutes.
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  v += dpp_rows<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_rows<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_rows<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_rows<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_rows<0x142, 0xA>(v);  // row_bcast:15
+  v += dpp_rows<0x143, 0xC>(v);  // row_bcast:31
+  return v;
+}
+
 // Inclusive cumsum of dt*A*log2(e) over the chunk (wave 0, one token per
 // lane; tokens >= len take dt = 0 so Lambda stays at its end value).
-__device__ __forceinline__ float chunk_cumsum(float a, int lane) {
-  float incl = a;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
+__device__ __forceinline__ float chunk_cumsum(float a, int) { return wave_incl_scan(a); }
+
+// Four consecutive storage elements (8 bytes of bf16, 16 of fp32).
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16 v[4] = {from_f32<bf16>(a), from_f32<bf16>(b), from_f32<bf16>(c), from_f32<bf16>(d)};
+    *reinterpret_cast<uint2*>(p) = *reinterpret_cast<const uint2*>(v);
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
   }
-  return incl;
+}
+
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float (&o)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    o[0] = __builtin_bit_cast(float, u.x << 16);
+    o[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
+    o[2] = __builtin_bit_cast(float, u.y << 16);
+    o[3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
+  } else {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x;
+    o[1] = v.y;
+    o[2] = v.z;
+    o[3] = v.w;
+  }
 }
 
 template <typename T, int P, int N>
@@ -355,16 +412,12 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
       for (int i = 0; i < 4; ++i)
         gacc[t][i] = (gin && owns) ? gin[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] : 0.0f;
   }
-  float da_acc = 0.0f;  // wave 0: sum_r dt_r da_r of this lane's tokens
-  float dd_acc = 0.0f;  // sum dy . x over this lane's entries
-
-  for (int c = k.nchunks - 1; c >= 0; --c) {
+  // Global rows of a chunk, into registers (all issued before any is used).
+  Vec16<T> vx[NXV], vy[NXV], vb[NBV], vc[NBV];
+  float pdt = 0.0f;
+  auto load_rows = [&](int c) {
     const int64_t row0 = rowb + (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
-
-    // ---- stage: every global load of the chunk first (one round trip), then
-    // token rows (zero past len), transposed copies, Hp^T and Gc into LDS ----
-    Vec16<T> vx[NXV], vy[NXV], vb[NBV], vc[NBV], vh[NHV];
 #pragma unroll
     for (int v = 0; v < NXV; ++v) {
       const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
@@ -379,25 +432,47 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
       vb[v] = ld ? load16(Bp + (row0 + s) * k.bs + n0) : zero16<T>();
       vc[v] = ld ? load16(Cp + (row0 + s) * k.cs + n0) : zero16<T>();
     }
-    const T* hp = Hst + (int64_t)c * (P * N);
-#pragma unroll
-    for (int v = 0; v < NHV; ++v) {
-      const int idx = tid + v * kBThreads, p = idx % P, n0 = (idx / P) * VB;
-      vh[v] = idx < P * (N / VB) ? load16(hp + p * N + n0) : zero16<T>();
-    }
-    // <Gc, H_e> on this wave's tiles (H_e: the state after this chunk; gacc
-    // still holds Gc), into this chunk's half of the per-wave slots
+    pdt = (wave == 0 && lane < len) ? to_f32(DTp[(row0 + lane) * k.dts + h]) : 0.0f;
+  };
+  // <Gc, H_e> of the last chunk: Gc = dL/dh_final, H_e = the final state;
+  // for every other chunk it is formed at the end of the chunk after it,
+  // from the operand copy of that chunk's start state in LDS
+  {
+    const int cl = k.nchunks - 1;
+    const T* hn = Hst + (int64_t)k.nchunks * (P * N);
     float hdot = 0.0f;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        hdot += owns ? gacc[t][i] * to_f32(hn[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16])
+                     : 0.0f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) hdot += __shfl_xor(hdot, off);
+    if (lane == 0) hgw[(cl & 1) * kBWaves + wave] = hdot;
+  }
+  float da_acc = 0.0f;  // wave 0: sum_r dt_r da_r of this lane's tokens
+  float dd_acc = 0.0f;  // sum dy . x over this lane's entries
+
+  for (int c = k.nchunks - 1; c >= 0; --c) {
+    const int64_t row0 = rowb + (int64_t)c * Q;
+    const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
+
+    // ---- stage: the chunk's rows into LDS (every global load first: one
+    // round trip): token rows (zero past len), transposed copies, Hp^T and
+    // Gc.  (Loading the next chunk during this one's compute measured no
+    // faster and spills registers.) ----
+    load_rows(c);
+    const float dtl = pdt;
+    Vec16<T> vh[NHV];
     {
-      const T* hn = Hst + (int64_t)(c + 1) * (P * N);
+      const T* hp = Hst + (int64_t)c * (P * N);
 #pragma unroll
-      for (int t = 0; t < TPW; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          hdot += owns ? gacc[t][i] * to_f32(hn[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16])
-                       : 0.0f;
+      for (int v = 0; v < NHV; ++v) {
+        const int idx = tid + v * kBThreads, p = idx % P, n0 = (idx / P) * VB;
+        vh[v] = idx < P * (N / VB) ? load16(hp + p * N + n0) : zero16<T>();
+      }
     }
-    const float dtl = (wave == 0 && lane < len) ? to_f32(DTp[(row0 + lane) * k.dts + h]) : 0.0f;
 #pragma unroll
     for (int v = 0; v < NXV; ++v) {
       const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
@@ -428,21 +503,14 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
 #pragma unroll
         for (int j = 0; j < VB; ++j) HT[(n0 + j) * TP2 + p] = vh[v].v[j];
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) hdot += __shfl_xor(hdot, off);
-    // two halves by chunk parity: wave 0 may still read the other chunk's
-    // half (after the last barrier) while a faster wave writes this one
-    if (lane == 0) hgw[(c & 1) * kBWaves + wave] = hdot;
     if (owns) {
 #pragma unroll
-      for (int t = 0; t < TPW; ++t)
+      for (int t = 0; t < TPW; ++t) {
+        const int p0 = (pt0 + t) * 16 + g * 4, n = nt * 16 + r16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int p = (pt0 + t) * 16 + g * 4 + i, n = nt * 16 + r16;
-          const T v = from_f32<T>(gacc[t][i]);
-          Gs[p * NN + n] = v;
-          GT[n * TP2 + p] = v;
-        }
+        for (int i = 0; i < 4; ++i) Gs[(p0 + i) * NN + n] = from_f32<T>(gacc[t][i]);
+        store4(GT + n * TP2 + p0, gacc[t][0], gacc[t][1], gacc[t][2], gacc[t][3]);
+      }
     }
     if (wave == 0) {
       const float d = dtl;
@@ -513,9 +581,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
             e[i] = v;
           }
 #pragma unroll
-          for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) e[i] += __shfl_xor(e[i], off);
+          for (int i = 0; i < 4; ++i) e[i] = row16_sum(e[i]);
           if (r16 == 0)
 #pragma unroll
             for (int i = 0; i < 4; ++i) esum[hf * Q + s0 + g * 4 + i] = e[i] * dtv[s0 + g * 4 + i];
@@ -528,7 +594,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
           const int ta = 2 * ip, tb = 2 * ip + 1;
           const bool doa = ta >= blk;  // block ta has t >= s somewhere (wave-uniform)
           f32x4 gA = {0, 0, 0, 0}, gB = {0, 0, 0, 0}, qA = {0, 0, 0, 0}, qB = {0, 0, 0, 0};
-#pragma unroll
+#pragma unroll 2
           for (int kb = 0; kb < NKB; ++kb) {
             Frag8<T> bs, ca, cb;
             frag_row(bs, Bn + srow * NN, kb * 32 + g * 8, N);
@@ -569,9 +635,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
           if (hf == 0) {
             // row sums of W over this block's 16 s (lanes r16), per t
 #pragma unroll
-            for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-              for (int j = 0; j < 8; ++j) rw[j] += __shfl_xor(rw[j], off);
+            for (int j = 0; j < 8; ++j) rw[j] = row16_sum(rw[j]);
             if (r16 == 0) {
 #pragma unroll
               for (int j = 0; j < 8; ++j)
@@ -625,9 +689,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
           }
         }
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ex[i] += __shfl_xor(ex[i], off);
+        for (int i = 0; i < 4; ++i) ex[i] = row16_sum(ex[i]);
         if (r16 == 0)
 #pragma unroll
           for (int i = 0; i < 4; ++i) expl[hf * Q + s0 + g * 4 + i] = ex[i];
@@ -667,9 +729,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
             e[i] = v;
           }
 #pragma unroll
-          for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) e[i] += __shfl_xor(e[i], off);
+          for (int i = 0; i < 4; ++i) e[i] = row16_sum(e[i]);
           if (r16 == 0)
 #pragma unroll
             for (int i = 0; i < 4; ++i) t1[hf * Q + t0 + g * 4 + i] = e[i];
@@ -723,7 +783,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
       }
     }
 
-    // ---- every wave: <Gc, H_e> over its tiles, then dGp ----
+    // ---- every wave: dGp = exp(Lambda_e) Gc + sum_t exp(Lambda_t) dy_t C_t^T on
+    // its tiles, then <dGp, Hp> for the chunk before (Hp^T is in LDS) ----
     if (owns) {
       const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
 #pragma unroll
@@ -735,17 +796,35 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
         const int tq = ks * 32 + g * 8;
         const f32x4 e0 = *reinterpret_cast<const f32x4*>(eL + tq);
         const f32x4 e1 = *reinterpret_cast<const f32x4*>(eL + tq + 4);
-        Frag8<T> cf;
-        frag_load8(cf, CT + (nt * 16 + r16) * TQ + tq);
+        Frag8<T> cr, cf;
+        frag_load8(cr, CT + (nt * 16 + r16) * TQ + tq);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) frag_set(cf, j, to_f32(cr.v[j]) * (j < 4 ? e0[j] : e1[j - 4]));
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-          Frag8<T> yr, yf;
-          frag_load8(yr, YT + ((pt0 + t) * 16 + r16) * TQ + tq);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) frag_set(yf, j, to_f32(yr.v[j]) * (j < 4 ? e0[j] : e1[j - 4]));
+          Frag8<T> yf;
+          frag_load8(yf, YT + ((pt0 + t) * 16 + r16) * TQ + tq);
           gacc[t] = mma(yf, cf, gacc[t]);
         }
       }
+    }
+    if (c > 0) {
+      float hdot = 0.0f;
+      if (owns) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          float hv[4];
+          load4(HT + (nt * 16 + r16) * TP2 + (pt0 + t) * 16 + g * 4, hv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hdot += gacc[t][i] * hv[i];
+        }
+      }
+      hdot = row16_sum(hdot);
+      hdot += __shfl_xor(hdot, 16);
+      hdot += __shfl_xor(hdot, 32);
+      // two halves by chunk parity: wave 0 reads chunk c's half below while
+      // this writes chunk c-1's
+      if (lane == 0) hgw[((c - 1) & 1) * kBWaves + wave] = hdot;
     }
     __syncthreads();
 
@@ -762,13 +841,11 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
         for (int j = 0; j < kBWaves; ++j) hg += hgw[(c & 1) * kBWaves + j];
         dl += hg;
       }
-      // suffix sum over t' >= t
-      float suf = dl;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float v = __shfl_down(suf, off);
-        if (lane + off < 64) suf += v;
-      }
+      // suffix sum over t' >= t: the total minus the prefix before t
+      const float incl = wave_incl_scan(dl);
+      const float tot = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
+      const float suf = (tot - incl) + dl;
       if (t < len) {
         grad_store(DDTp + (row0 + t) * k.ddts + h, (expl[t] + expl[Q + t]) + Ah * suf, k.accumulate);
         da_acc += dtv[t] * suf;
