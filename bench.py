@@ -27,7 +27,8 @@ Also reported on the same JSON line:
     d_i) on the 1.4B-scale rows at every width, timed as the slices are;
   - ``backward``: the scan's backward pass (mm_ssd_backward: dx, ddt, dA,
     dB, dC, dD from the cotangent of y) on the same inputs at every width,
-    timed as the slices are, with its HBM fraction;
+    and the conv's backward (mm_conv1d_silu_backward) at full width, timed as
+    the slices are, with their HBM fractions;
   - ``decode``: the recurrent decode step (conv state roll + scan step) for a
     batch of 256 sequences at mixed widths, 1024 tokens captured in a HIP graph;
   - ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample
@@ -221,10 +222,11 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the scan-only timings of the 130M and long-context workloads")
-    ap.add_argument("--mode", choices=["step", "fused", "scan", "backward", "copy"],
+    ap.add_argument("--mode", choices=["step", "fused", "scan", "backward", "conv_backward", "copy"],
                     default="step",
-                    help="fused / scan / backward: only the full-width fused call / scan call / "
-                         "scan backward call (for counter runs); copy: a 1 GiB device copy that calibrates the HBM "
+                    help="fused / scan / backward / conv_backward: only the full-width fused "
+                         "call / scan call / scan backward / conv backward (for counter and "
+                         "trace runs); copy: a 1 GiB device copy that calibrates the HBM "
                          "byte counters")
     ap.add_argument("--summarize-pmc", nargs=5,
                     metavar=("WHICH", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -306,6 +308,15 @@ def main():
             g = mm.ssd_backward(xv, dt, A, Bv, Cv, D, dy, grads=g, workspace=bws)
         torch.cuda.synchronize()
         print(f"# backward-only: {args.warmup + args.steps} launches", file=sys.stderr)
+        return
+    if args.mode == "conv_backward":  # trace runs: the full-width conv backward alone
+        dout = synth.conv_cotangent(w).to(dev)
+        cg = {"dxbc": torch.empty_like(xbc_raw), "dw": torch.empty((w.conv_dim, 4), device=dev)}
+        for _ in range(args.warmup + args.steps):
+            mm.conv1d_silu_backward(xbc_raw, conv_w, dout, d_inner=w.d_inner, d_head=P, d_state=N,
+                                    grads=cg)
+        torch.cuda.synchronize()
+        print(f"# conv-backward-only: {args.warmup + args.steps} launches", file=sys.stderr)
         return
     if args.mode == "copy":  # counter calibration: a plain copy of known size
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -495,6 +506,20 @@ def bench_backward(torch, mm, synth, w, dev, flush, xv, dt, A, Bv, Cv, D, slices
                        "tokens_per_s": tokens / (t["median"] * 1e-3),
                        "hbm_frac": ab / (t["median"] * 1e-3) / (HBM_PEAK_GBS * 1e9)}
     del dy, g, ws
+    # the conv's backward on the 1.4B-scale rows at full width
+    xi = synth.xbc_inputs(w)
+    xbc, cw = xi["xbc"].to(dev), xi["w"].to(dev)
+    del xi
+    dout = synth.conv_cotangent(w).to(dev)
+    cg = {"dxbc": torch.empty_like(xbc), "dw": torch.empty((w.conv_dim, 4), device=dev)}
+    t = timed_calls(torch, lambda: mm.conv1d_silu_backward(
+        xbc, cw, dout, d_inner=w.d_inner, d_head=P, d_state=N, grads=cg), flush)
+    cb = 3 * tokens * w.conv_dim * 2
+    res["conv"] = {"ms": t["median"], "ms_p10": t["p10"], "ms_p90": t["p90"],
+                   "tokens_per_s": tokens / (t["median"] * 1e-3),
+                   "gb_per_s": cb / (t["median"] * 1e-3) / 1e9,
+                   "hbm_frac": cb / (t["median"] * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+    del xbc, cw, dout, cg
     return res
 
 

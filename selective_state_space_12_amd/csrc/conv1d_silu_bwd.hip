@@ -7,13 +7,16 @@
 //   du[tau]   = sum_k w_k dpre[tau + 3 - k]       (tau = -3..-1: the conv state rows)
 //   dw_k     += sum_t dpre[t] u[t - 3 + k],  dbias += sum_t dpre[t]
 //
-// Design: HBM-bound streaming, as the forward conv.  A thread owns 16 bytes
-// of channels and a run of tokens; it slides a window of three inputs and
+// Design: HBM-bound streaming, as the forward conv.  A thread owns four
+// channels and a run of tokens; it slides a window of three inputs and
 // three dpre values, so du[t-3] is complete once dpre[t] is known: the run
 // reads three tokens past its end (the halo whose dpre reaches back into the
 // run) and three before it.  The run that starts at token 0 also emits the
-// conv-state rows' gradient.  dw and dbias are summed over the run in
-// registers and added with one fp32 atomic per value and run.
+// conv-state rows' gradient.  A workgroup is 4 waves over 4 consecutive
+// runs of the same 64 channel groups; dw and dbias are summed over each run
+// in registers, over the 4 runs through LDS, and added with one fp32 atomic
+// per value and workgroup (atomics on the same few thousand addresses from
+// every run had made the kernel atomic-bound).
 #include "device_common.h"
 #include "kernels.h"
 #include "../../include/mm_ssd.h"
@@ -22,22 +25,52 @@ namespace mmssd {
 
 namespace {
 
-constexpr int kThreads = 64;
-constexpr int kRun = 64;  // tokens per thread
+constexpr int kLanes = 64;   // channel groups per workgroup
+constexpr int kRuns = 4;     // token runs per workgroup (one wave each)
+constexpr int kThreads = kLanes * kRuns;
+constexpr int kRun = 64;     // tokens per thread
+
+// Four consecutive channels of one token (8 bytes of bf16, 16 of fp32): a
+// thread's share.  Four rather than a 16-byte vector of bf16 keeps the
+// per-thread windows and sums small enough for several waves per SIMD.
+constexpr int V = 4;
 
 template <typename T>
-__device__ __forceinline__ void add_store16(T* p, const float (&v)[Vec16<T>::kN], int accumulate) {
-  constexpr int V = Vec16<T>::kN;
-  Vec16<T> o;
+__device__ __forceinline__ void load4f(const T* p, float (&o)[V]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    o[0] = __builtin_bit_cast(float, u.x << 16);
+    o[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
+    o[2] = __builtin_bit_cast(float, u.y << 16);
+    o[3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
+  } else {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x;
+    o[1] = v.y;
+    o[2] = v.z;
+    o[3] = v.w;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void add_store4(T* p, const float (&v)[V], int accumulate) {
+  float o[V];
   if (accumulate) {
-    const Vec16<T> old = load16(p);
+    float old[V];
+    load4f(p, old);
 #pragma unroll
-    for (int j = 0; j < V; ++j) o.v[j] = from_f32<T>(to_f32(old.v[j]) + v[j]);
+    for (int j = 0; j < V; ++j) o[j] = old[j] + v[j];
   } else {
 #pragma unroll
-    for (int j = 0; j < V; ++j) o.v[j] = from_f32<T>(v[j]);
+    for (int j = 0; j < V; ++j) o[j] = v[j];
   }
-  store16(p, o);
+  if constexpr (sizeof(T) == 2) {
+    const bf16 b[4] = {from_f32<bf16>(o[0]), from_f32<bf16>(o[1]), from_f32<bf16>(o[2]),
+                       from_f32<bf16>(o[3])};
+    *reinterpret_cast<uint2*>(p) = *reinterpret_cast<const uint2*>(b);
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+  }
 }
 
 template <typename T>
@@ -47,16 +80,20 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_bwd_kernel(
     const float* __restrict__ bias, const float* __restrict__ conv_state, float* __restrict__ dw,
     float* __restrict__ dbias, float* __restrict__ dstate, int seqlen, int d_inner, int xw,
     int bc_dim, int accumulate) {
-  constexpr int V = Vec16<T>::kN;
+  __shared__ float red[kRuns - 1][5 * V][kLanes];
   const int b = blockIdx.z;
-  const int t0 = blockIdx.y * kRun;
-  const int cg = blockIdx.x * kThreads + threadIdx.x;
+  const int run = threadIdx.x / kLanes, ln = threadIdx.x % kLanes;
+  const int t0 = (blockIdx.y * kRuns + run) * kRun;
+  const int cg = blockIdx.x * kLanes + ln;
   const int ngx = xw / V;
-  if (cg >= ngx + bc_dim / V || t0 >= seqlen) return;
-  const int c = cg < ngx ? cg * V : d_inner + (cg - ngx) * V;
+  // a thread past the channels or the sequence has no run but still takes
+  // part in the reduction (with zeros)
+  const bool active = cg < ngx + bc_dim / V && t0 < seqlen;
+  const int cgc = active ? cg : 0;
+  const int c = cgc < ngx ? cgc * V : d_inner + (cgc - ngx) * V;
   const int conv_dim = d_inner + bc_dim;
-  const int t1 = min(seqlen, t0 + kRun);
-  const int tend = min(seqlen, t1 + 3);  // tokens whose dpre is needed
+  const int t1 = active ? min(seqlen, t0 + kRun) : t0;
+  const int tend = active ? min(seqlen, t1 + 3) : t0;  // tokens whose dpre is needed
 
   float wk[4][V], bv[V];
 #pragma unroll
@@ -74,10 +111,11 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_bwd_kernel(
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     const int tau = t0 - 3 + k;
-    if (tau >= 0) {
-      const Vec16<T> v = load16(in + (row0 + tau) * in_stride + c);
+    if (!active) {
 #pragma unroll
-      for (int j = 0; j < V; ++j) h[k][j] = to_f32(v.v[j]);
+      for (int j = 0; j < V; ++j) h[k][j] = 0.0f;
+    } else if (tau >= 0) {
+      load4f(in + (row0 + tau) * in_stride + c, h[k]);
     } else if (conv_state) {
       const float* sp = conv_state + ((int64_t)b * 3 + (tau + 3)) * conv_dim + c;
 #pragma unroll
@@ -103,31 +141,32 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_bwd_kernel(
   // rows when the run starts the sequence (dpre before token 0 is zero).
   // Tokens past the sequence end have dpre = 0.
   constexpr int kGroup = 4;
-  for (int tg = t0; tg < t1 + 3; tg += kGroup) {
-    Vec16<T> u[kGroup], go[kGroup];
+  const int tstop = active ? t1 + 3 : t0;
+  for (int tg = t0; tg < tstop; tg += kGroup) {
+    float u[kGroup][V], go[kGroup][V];
 #pragma unroll
     for (int i = 0; i < kGroup; ++i)
       if (tg + i < tend) {
-        u[i] = load16(in + (row0 + tg + i) * in_stride + c);
-        go[i] = load16(dout + (row0 + tg + i) * dout_stride + c);
+        load4f(in + (row0 + tg + i) * in_stride + c, u[i]);
+        load4f(dout + (row0 + tg + i) * dout_stride + c, go[i]);
       }
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
       const int t = tg + i;
-      if (t >= t1 + 3) break;
+      if (t >= tstop) break;
       float dcur[V];
 #pragma unroll
       for (int j = 0; j < V; ++j) {
         float d = 0.0f;
         if (t < tend) {
-          const float ut = to_f32(u[i].v[j]);
+          const float ut = u[i][j];
           float pre = bv[j];
           pre = fmaf(wk[0][j], h[0][j], pre);
           pre = fmaf(wk[1][j], h[1][j], pre);
           pre = fmaf(wk[2][j], h[2][j], pre);
           pre = fmaf(wk[3][j], ut, pre);
           const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-pre * kLog2e));
-          d = to_f32(go[i].v[j]) * s * (1.0f + pre * (1.0f - s));
+          d = go[i][j] * s * (1.0f + pre * (1.0f - s));
           if (t < t1) {
             sw[0][j] = fmaf(d, h[0][j], sw[0][j]);
             sw[1][j] = fmaf(d, h[1][j], sw[1][j]);
@@ -149,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_bwd_kernel(
         for (int j = 0; j < V; ++j)
           g[j] = wk[0][j] * dcur[j] + wk[1][j] * dp[2][j] + wk[2][j] * dp[1][j] + wk[3][j] * dp[0][j];
         if (tau >= t0) {
-          add_store16(din + (row0 + tau) * din_stride + c, g, accumulate);
+          add_store4(din + (row0 + tau) * din_stride + c, g, accumulate);
         } else {  // tau = -3..-1: conv state row tau + 3 (the run starts the sequence)
           float* sp = dstate + ((int64_t)b * 3 + (tau + 3)) * conv_dim + c;
 #pragma unroll
@@ -164,11 +203,31 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_bwd_kernel(
       }
     }
   }
+  // sums over the workgroup's runs: runs 1.. park theirs in LDS, run 0 adds
+  if (run > 0) {
 #pragma unroll
-  for (int j = 0; j < V; ++j) {
+    for (int j = 0; j < V; ++j) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) unsafeAtomicAdd(dw + (int64_t)(c + j) * 4 + k, sw[k][j]);
-    if (dbias) unsafeAtomicAdd(dbias + c + j, sb[j]);
+      for (int k = 0; k < 4; ++k) red[run - 1][k * V + j][ln] = sw[k][j];
+      red[run - 1][4 * V + j][ln] = sb[j];
+    }
+  }
+  __syncthreads();
+  if (run == 0 && cg < ngx + bc_dim / V) {
+#pragma unroll
+    for (int r = 0; r < kRuns - 1; ++r)
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sw[k][j] += red[r][k * V + j][ln];
+        sb[j] += red[r][4 * V + j][ln];
+      }
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) unsafeAtomicAdd(dw + (int64_t)(c + j) * 4 + k, sw[k][j]);
+      if (dbias) unsafeAtomicAdd(dbias + c + j, sb[j]);
+    }
   }
 }
 
@@ -185,10 +244,9 @@ __global__ __launch_bounds__(256) void zero_channels_kernel(float* p, int width,
 
 template <typename T>
 void launch_typed(const ConvBwdArgs& a, hipStream_t s) {
-  constexpr int V = Vec16<T>::kN;
   const int groups = (a.xw + a.bc_dim) / V;
-  const dim3 grid((unsigned)((groups + kThreads - 1) / kThreads),
-                  (unsigned)((a.seqlen + kRun - 1) / kRun), (unsigned)a.batch);
+  const dim3 grid((unsigned)((groups + kLanes - 1) / kLanes),
+                  (unsigned)((a.seqlen + kRun * kRuns - 1) / (kRun * kRuns)), (unsigned)a.batch);
   hipLaunchKernelGGL(conv1d_silu_bwd_kernel<T>, grid, dim3(kThreads), 0, s,
                      static_cast<const T*>(a.in), a.in_stride, static_cast<const T*>(a.dout),
                      a.dout_stride, static_cast<T*>(a.din), a.din_stride, a.w, a.bias,
