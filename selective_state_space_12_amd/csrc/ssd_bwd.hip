@@ -45,6 +45,8 @@
 //  - dB and dC are sums over heads: fp32 atomics into the caller's buffers
 //    (zeroed by a fill kernel unless the call accumulates); dA and dD are sums
 //    over sequences, one atomic per workgroup.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "../../include/mm_ssd.h"
@@ -244,57 +246,68 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
         dst[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] = from_f32<T>(hacc[t][i]);
   };
 
-  // The next chunk's x, B rows and dt are loaded into registers while this
-  // chunk's update runs (every thread's vector slots are fixed, so the
-  // loads of a chunk are all in flight at once).
+  // The x, B rows and dt of the chunk two ahead are loaded into registers
+  // while this chunk's update runs (two register sets, used alternately; a
+  // thread's vector slots are fixed, so a chunk's loads are all in flight at
+  // once and have two chunks of time to land).
   constexpr int NXV = (Q * (P / VB) + kBThreads - 1) / kBThreads;
   constexpr int NBV = (Q * (N / VB) + kBThreads - 1) / kBThreads;
-  Vec16<T> px[NXV], pb[NBV];
-  float pdt = 0.0f;
-  auto prefetch = [&](int c) {
+  Vec16<T> px[2][NXV], pb[2][NBV];
+  float pdt[2] = {0.0f, 0.0f};
+  int plen[2] = {0, 0};
+  auto prefetch = [&](int c, auto set) {
+    constexpr int S = decltype(set)::value;
     const int64_t row0 = rowb + (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
+    // Every load is issued unconditionally at a clamped address and the
+    // rows past the end are zeroed afterwards: a load under a lane condition
+    // is followed by a wait for it at the branch's end, which serialises
+    // the whole batch.
 #pragma unroll
     for (int v = 0; v < NXV; ++v) {
-      const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
-      px[v] = (idx < Q * (P / VB) && s < len) ? load16(Xp + (row0 + s) * k.xs + (int64_t)h * P + p0)
-                                              : zero16<T>();
+      const int idx = min(tid + v * kBThreads, Q * (P / VB) - 1), s = idx % Q;
+      const int p0 = (idx / Q) * VB;
+      px[S][v] = load16(Xp + (row0 + min(s, len - 1)) * k.xs + (int64_t)h * P + p0);
     }
 #pragma unroll
     for (int v = 0; v < NBV; ++v) {
-      const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
-      pb[v] = (idx < Q * (N / VB) && s < len) ? load16(Bp + (row0 + s) * k.bs + n0) : zero16<T>();
+      const int idx = min(tid + v * kBThreads, Q * (N / VB) - 1), s = idx % Q;
+      const int n0 = (idx / Q) * VB;
+      pb[S][v] = load16(Bp + (row0 + min(s, len - 1)) * k.bs + n0);
     }
-    if (wave == 0) pdt = lane < len ? to_f32(DTp[(row0 + lane) * k.dts + h]) : 0.0f;
+    pdt[S] = to_f32(DTp[(row0 + min(lane, len - 1)) * k.dts + h]);
+    plen[S] = len;
   };
-  if (k.nchunks > 0) prefetch(0);
-
-  for (int c = 0; c < k.nchunks; ++c) {
+  auto step = [&](int c, auto set) {
+    constexpr int S = decltype(set)::value;
     store_state(c);
     // x^T and B^T: consecutive lanes take consecutive tokens (distinct banks)
+    const int len = plen[S];
 #pragma unroll
     for (int v = 0; v < NXV; ++v) {
       const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
+      const Vec16<T> xv = s < len ? px[S][v] : zero16<T>();
       if (idx < Q * (P / VB))
 #pragma unroll
-        for (int j = 0; j < VB; ++j) XT[(p0 + j) * TQ + s] = px[v].v[j];
+        for (int j = 0; j < VB; ++j) XT[(p0 + j) * TQ + s] = xv.v[j];
     }
 #pragma unroll
     for (int v = 0; v < NBV; ++v) {
       const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
+      const Vec16<T> bv = s < len ? pb[S][v] : zero16<T>();
       if (idx < Q * (N / VB))
 #pragma unroll
-        for (int j = 0; j < VB; ++j) BT[(n0 + j) * TQ + s] = pb[v].v[j];
+        for (int j = 0; j < VB; ++j) BT[(n0 + j) * TQ + s] = bv.v[j];
     }
     if (wave == 0) {
-      const float d = pdt;
+      const float d = lane < len ? pdt[S] : 0.0f;
       const float lv = chunk_cumsum(d * Ah2, lane);
       const float le = __shfl(lv, 63);
       lam[lane] = lv;
       wsc[lane] = __builtin_amdgcn_exp2f(le - lv) * d;
     }
     __syncthreads();
-    if (c + 1 < k.nchunks) prefetch(c + 1);
+    if (c + 2 < k.nchunks) prefetch(c + 2, set);
     if (owns) {
       const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
 #pragma unroll
@@ -319,6 +332,14 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
       }
     }
     __syncthreads();
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (k.nchunks > 0) prefetch(0, S0{});
+  if (k.nchunks > 1) prefetch(1, S1{});
+  for (int c = 0; c < k.nchunks; c += 2) {
+    step(c, S0{});
+    if (c + 1 < k.nchunks) step(c + 1, S1{});
   }
   store_state(k.nchunks);
 }
@@ -418,21 +439,23 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
   auto load_rows = [&](int c) {
     const int64_t row0 = rowb + (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
+    // unconditional loads at clamped addresses (a lane-conditional load is
+    // waited for at its branch's end); rows past len are zeroed at staging
 #pragma unroll
     for (int v = 0; v < NXV; ++v) {
-      const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
-      const bool ld = idx < Q * (P / VB) && s < len;
-      vx[v] = ld ? load16(Xp + (row0 + s) * k.xs + (int64_t)h * P + p0) : zero16<T>();
-      vy[v] = ld ? load16(DYp + (row0 + s) * k.dys + (int64_t)h * P + p0) : zero16<T>();
+      const int idx = min(tid + v * kBThreads, Q * (P / VB) - 1), s = min(idx % Q, len - 1);
+      const int p0 = (idx / Q) * VB;
+      vx[v] = load16(Xp + (row0 + s) * k.xs + (int64_t)h * P + p0);
+      vy[v] = load16(DYp + (row0 + s) * k.dys + (int64_t)h * P + p0);
     }
 #pragma unroll
     for (int v = 0; v < NBV; ++v) {
-      const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
-      const bool ld = idx < Q * (N / VB) && s < len;
-      vb[v] = ld ? load16(Bp + (row0 + s) * k.bs + n0) : zero16<T>();
-      vc[v] = ld ? load16(Cp + (row0 + s) * k.cs + n0) : zero16<T>();
+      const int idx = min(tid + v * kBThreads, Q * (N / VB) - 1), s = min(idx % Q, len - 1);
+      const int n0 = (idx / Q) * VB;
+      vb[v] = load16(Bp + (row0 + s) * k.bs + n0);
+      vc[v] = load16(Cp + (row0 + s) * k.cs + n0);
     }
-    pdt = (wave == 0 && lane < len) ? to_f32(DTp[(row0 + lane) * k.dts + h]) : 0.0f;
+    pdt = to_f32(DTp[(row0 + min(lane, len - 1)) * k.dts + h]);
   };
   // <Gc, H_e> of the last chunk: Gc = dL/dh_final, H_e = the final state;
   // for every other chunk it is formed at the end of the chunk after it,
@@ -463,36 +486,38 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
     // Gc.  (Loading the next chunk during this one's compute measured no
     // faster and spills registers.) ----
     load_rows(c);
-    const float dtl = pdt;
     Vec16<T> vh[NHV];
     {
       const T* hp = Hst + (int64_t)c * (P * N);
 #pragma unroll
       for (int v = 0; v < NHV; ++v) {
-        const int idx = tid + v * kBThreads, p = idx % P, n0 = (idx / P) * VB;
-        vh[v] = idx < P * (N / VB) ? load16(hp + p * N + n0) : zero16<T>();
+        const int idx = min(tid + v * kBThreads, P * (N / VB) - 1), p = idx % P;
+        vh[v] = load16(hp + p * N + (idx / P) * VB);
       }
     }
+    const float dtl = lane < len ? pdt : 0.0f;
 #pragma unroll
     for (int v = 0; v < NXV; ++v) {
       const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
+      const Vec16<T> xv = s < len ? vx[v] : zero16<T>(), yv = s < len ? vy[v] : zero16<T>();
       if (idx < Q * (P / VB)) {
-        store16(Xn + s * NP + p0, vx[v]);
-        store16(Yn + s * NP + p0, vy[v]);
+        store16(Xn + s * NP + p0, xv);
+        store16(Yn + s * NP + p0, yv);
 #pragma unroll
-        for (int j = 0; j < VB; ++j) YT[(p0 + j) * TQ + s] = vy[v].v[j];
+        for (int j = 0; j < VB; ++j) YT[(p0 + j) * TQ + s] = yv.v[j];
       }
     }
 #pragma unroll
     for (int v = 0; v < NBV; ++v) {
       const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
+      const Vec16<T> bv = s < len ? vb[v] : zero16<T>(), cv = s < len ? vc[v] : zero16<T>();
       if (idx < Q * (N / VB)) {
-        store16(Bn + s * NN + n0, vb[v]);
-        store16(Cn + s * NN + n0, vc[v]);
+        store16(Bn + s * NN + n0, bv);
+        store16(Cn + s * NN + n0, cv);
 #pragma unroll
         for (int j = 0; j < VB; ++j) {
-          BT[(n0 + j) * TQ + s] = vb[v].v[j];
-          CT[(n0 + j) * TQ + s] = vc[v].v[j];
+          BT[(n0 + j) * TQ + s] = bv.v[j];
+          CT[(n0 + j) * TQ + s] = cv.v[j];
         }
       }
     }
