@@ -418,12 +418,24 @@ int mm_conv1d_silu_backward(const void* xbc_in, int64_t in_row_stride,
 /*
  * Bytes of device workspace mm_ssd_backward needs: the state before every
  * 64-token chunk and the final state of each active (sequence, head), in the
- * storage dtype.  Same argument meaning and errors as mm_ssd_backward.
+ * storage dtype, and, when the sequences are split, fp32 segment states and
+ * gradients (see mm_ssd_backward_segments).  Same argument meaning and errors as mm_ssd_backward.
  * Host only.
  */
 int mm_ssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
                                    int64_t d_head, int64_t d_state, int64_t ngroups,
                                    int64_t n_heads_active, int dtype, size_t* bytes_out);
+
+/*
+ * Segments per sequence a mm_ssd_backward call with these sizes uses: with
+ * fewer than 256 active (sequence, head) walks, the sequences are split into
+ * segments of at least 256 tokens walked in parallel (a prepass and a
+ * combine chain them; the workspace size includes their data).  Same
+ * argument meaning and errors as mm_ssd_backward.  Host only.
+ */
+int mm_ssd_backward_segments(int64_t batch, int64_t seqlen, int64_t n_heads,
+                             int64_t d_head, int64_t d_state, int64_t ngroups,
+                             int64_t n_heads_active, int dtype, int* nseg_out);
 
 /*
  * Backward pass of mm_ssd_forward ("MatMamba", training paragraph: the

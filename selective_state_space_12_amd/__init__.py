@@ -114,6 +114,8 @@ def lib() -> ctypes.CDLL:
                                            _i64, _vp, _i64, _vp, _vp] + [_i64] * 7
                                           + [_int, _int, _vp, ctypes.c_size_t, _vp])
             L.mm_ssd_backward.restype = _int
+            L.mm_ssd_backward_segments.argtypes = [_i64] * 7 + [_int, ctypes.POINTER(_int)]
+            L.mm_ssd_backward_segments.restype = _int
             L.mm_conv1d_silu_backward.argtypes = ([_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
                                                    _vp, _vp, _vp] + [_i64] * 7
                                                   + [_int, _int, _vp])
@@ -326,6 +328,16 @@ def ssd_backward_workspace_size(batch: int, seqlen: int, n_heads: int, d_head: i
     _check("mm_ssd_backward_workspace_size",
            lib().mm_ssd_backward_workspace_size(batch, seqlen, n_heads, d_head, d_state, ngroups,
                                                 n_heads_active, code, ctypes.byref(out)))
+    return out.value
+
+
+def ssd_backward_segments(batch: int, seqlen: int, n_heads: int, d_head: int, d_state: int,
+                          ngroups: int, n_heads_active: int, dtype: torch.dtype) -> int:
+    out = _int(0)
+    code = MM_F32 if dtype == torch.float32 else MM_BF16
+    _check("mm_ssd_backward_segments",
+           lib().mm_ssd_backward_segments(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                          n_heads_active, code, ctypes.byref(out)))
     return out.value
 
 

@@ -380,6 +380,18 @@ int mm_ssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t n_head
   return MM_OK;
 }
 
+int mm_ssd_backward_segments(int64_t batch, int64_t seqlen, int64_t n_heads, int64_t d_head,
+                             int64_t d_state, int64_t ngroups, int64_t n_heads_active, int dtype,
+                             int* nseg_out) {
+  if (!nseg_out) return MM_ERR_NULL;
+  const int st = validate_ssd_backward_shape(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                             n_heads_active, dtype);
+  if (st != MM_OK) return st;
+  int nc, sc;
+  bwd_plan(batch, seqlen, n_heads_active, &nc, nseg_out, &sc);
+  return MM_OK;
+}
+
 int mm_ssd_backward(const void* x, int64_t x_row_stride, const void* dt, int64_t dt_row_stride,
                     const float* A, const void* B, int64_t b_row_stride, const void* C,
                     int64_t c_row_stride, const float* D, const float* initial_state,

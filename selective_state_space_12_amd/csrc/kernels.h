@@ -255,6 +255,10 @@ bool bwd_shape_supported(int64_t d_head, int64_t d_state, int dtype);
 size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
                            int64_t d_state, int dtype);
 hipError_t launch_ssd_backward(const BwdArgs& a, void* workspace, hipStream_t s);
+// Chunks per sequence, segments per sequence and chunks per segment of a
+// backward call (the split the launch, the workspace and the query share).
+void bwd_plan(int64_t batch, int64_t seqlen, int64_t heads, int* nchunks, int* nseg,
+              int* seg_chunks);
 
 // Conv backward (conv1d_silu_bwd.hip): gradients of sum dout * conv1d_silu(in).
 struct ConvBwdArgs {

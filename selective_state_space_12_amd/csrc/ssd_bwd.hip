@@ -45,6 +45,7 @@
 //  - dB and dC are sums over heads: fp32 atomics into the caller's buffers
 //    (zeroed by a fill kernel unless the call accumulates); dA and dD are sums
 //    over sequences, one atomic per workgroup.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -87,20 +88,31 @@ struct BwdK {
   float* dD;
   float* dh0;
   void* hst;  // (batch, heads, nchunks + 1, P, N) storage type
+  // sequence split (nseg > 1): per (unit, segment) fp32 P x N blocks and
+  // log2 decays; see the launch for what each holds when
+  float* seg_h;
+  float* seg_hd;
+  float* seg_g;
+  float* seg_gd;
   int64_t seqlen;
   int n_heads, heads, nchunks, accumulate;
+  int nseg, seg_chunks;
 };
 
 template <typename T> constexpr int bpad() { return 16 / (int)sizeof(T); }
 
 // (sequence, head) of this workgroup: consecutive units on one XCD so that
 // the heads of a sequence share its B and C rows in that XCD's L2.
-__device__ __forceinline__ void unit_of(int heads, int* b, int* h) {
+// With nsk segments per unit in the grid (segment fastest), *seg is this
+// workgroup's segment among them.
+__device__ __forceinline__ void unit_of(int heads, int nsk, int* b, int* h, int* seg) {
   const int total = gridDim.x;
   const int pid = blockIdx.x;
   const int uid = total % kXcds == 0 ? (pid % kXcds) * (total / kXcds) + pid / kXcds : pid;
-  *b = uid / heads;
-  *h = uid % heads;
+  const int unit = uid / nsk;
+  *seg = uid % nsk;
+  *b = unit / heads;
+  *h = unit % heads;
 }
 
 // Eight consecutive elements at p[k0..k0+7] when k0 < K, else zeros.
@@ -199,7 +211,10 @@ struct StateLds {
 };
 
 // Forward walk storing the state before every chunk and the final state.
-template <typename T, int P, int N>
+// With the sequence split, PRE walks segments 0..nseg-2 from a zero state and
+// writes each one's end state and log2 decay (seg_h, seg_hd); the main walk
+// of segment s > 0 then starts from the combined state in seg_h slot s-1.
+template <typename T, int P, int N, bool PRE>
 __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
   using L = StateLds<T, P, N>;
   constexpr int Q = kBQ, TQ = L::TQ;
@@ -214,14 +229,16 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
   float* lam = reinterpret_cast<float*>(BT + N * TQ);
   float* wsc = lam + Q;
 
-  int b, h;
-  unit_of(k.heads, &b, &h);
+  int b, h, seg;
+  unit_of(k.heads, PRE ? k.nseg - 1 : k.nseg, &b, &h, &seg);
+  const int64_t unit = (int64_t)b * k.heads + h;
+  const int c0 = seg * k.seg_chunks, c1 = min(c0 + k.seg_chunks, k.nchunks);
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int r16 = lane % 16, g = lane / 16;
   const T* __restrict__ Xp = static_cast<const T*>(k.x);
   const T* __restrict__ DTp = static_cast<const T*>(k.dt);
   const T* __restrict__ Bp = static_cast<const T*>(k.B);
-  T* __restrict__ Hst = static_cast<T*>(k.hst) + ((int64_t)b * k.heads + h) * (k.nchunks + 1) * (P * N);
+  T* __restrict__ Hst = static_cast<T*>(k.hst) + unit * (k.nchunks + 1) * (P * N);
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Ah2 = k.A[h] * kLog2e;
 
@@ -229,7 +246,11 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
   const bool owns = tile0 < NTILE;
   const int nt = tile0 / TP, pt0 = tile0 % TP;
   f32x4 hacc[TPW];
-  const float* hin = k.h0 ? k.h0 + ((int64_t)b * k.n_heads + h) * (P * N) : nullptr;
+  const float* hin = PRE ? nullptr
+                     : seg > 0 ? k.seg_h + (unit * k.nseg + seg - 1) * (P * N)
+                     : k.h0 ? k.h0 + ((int64_t)b * k.n_heads + h) * (P * N)
+                            : nullptr;
+  float lam_seg = 0.0f;  // log2 decay over the walked chunks
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -237,7 +258,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
       hacc[t][i] = (hin && owns) ? hin[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] : 0.0f;
 
   auto store_state = [&](int c) {
-    if (!owns) return;
+    if (PRE || !owns) return;
     T* dst = Hst + (int64_t)c * (P * N);
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
@@ -307,7 +328,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
       wsc[lane] = __builtin_amdgcn_exp2f(le - lv) * d;
     }
     __syncthreads();
-    if (c + 2 < k.nchunks) prefetch(c + 2, set);
+    if (c + 2 < c1) prefetch(c + 2, set);
+    lam_seg += lam[Q - 1];
     if (owns) {
       const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
 #pragma unroll
@@ -335,13 +357,160 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  if (k.nchunks > 0) prefetch(0, S0{});
-  if (k.nchunks > 1) prefetch(1, S1{});
-  for (int c = 0; c < k.nchunks; c += 2) {
+  if (c0 < c1) prefetch(c0, S0{});
+  if (c0 + 1 < c1) prefetch(c0 + 1, S1{});
+  for (int c = c0; c < c1; c += 2) {
     step(c, S0{});
-    if (c + 1 < k.nchunks) step(c + 1, S1{});
+    if (c + 1 < c1) step(c + 1, S1{});
   }
-  store_state(k.nchunks);
+  if (PRE) {
+    float* dst = k.seg_h + (unit * k.nseg + seg) * (P * N);
+    if (owns)
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] = hacc[t][i];
+    if (tid == 0) k.seg_hd[unit * k.nseg + seg] = lam_seg;
+  } else if (c1 == k.nchunks) {
+    store_state(k.nchunks);
+  }
+}
+
+// Reverse prepass of the sequence split: segments 1..nseg-1 walk their
+// chunks backwards from dL/dH = 0 at their end with the dL/dH update alone
+// (dGp = exp(Lambda_e) Gc + sum_t exp(Lambda_t) dy_t C_t^T) and write the
+// result at their start and their log2 decay (seg_g, seg_gd).
+template <typename T, int P, int N>
+__global__ __launch_bounds__(kBThreads) void bwd_gprep_kernel(BwdK k) {
+  using L = StateLds<T, P, N>;
+  constexpr int Q = kBQ, TQ = L::TQ;
+  constexpr int TP = P / 16, TN = N / 16, NTILE = TP * TN;
+  constexpr int TPW = NTILE >= kBWaves ? NTILE / kBWaves : 1;
+  constexpr int VB = 16 / (int)sizeof(T);
+  constexpr int NYV = (Q * (P / VB) + kBThreads - 1) / kBThreads;
+  constexpr int NCV = (Q * (N / VB) + kBThreads - 1) / kBThreads;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* YT = reinterpret_cast<T*>(smem);  // dy^T [P][TQ]
+  T* CT = YT + P * TQ;                 // C^T [N][TQ]
+  float* lam = reinterpret_cast<float*>(CT + N * TQ);
+  float* eL = lam + Q;
+
+  int b, h, sg;
+  unit_of(k.heads, k.nseg - 1, &b, &h, &sg);
+  const int seg = sg + 1;
+  const int64_t unit = (int64_t)b * k.heads + h;
+  const int c0 = seg * k.seg_chunks, c1 = min(c0 + k.seg_chunks, k.nchunks);
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int r16 = lane % 16, g = lane / 16;
+  const T* __restrict__ DYp = static_cast<const T*>(k.dy);
+  const T* __restrict__ DTp = static_cast<const T*>(k.dt);
+  const T* __restrict__ Cp = static_cast<const T*>(k.C);
+  const int64_t rowb = (int64_t)b * k.seqlen;
+  const float Ah2 = k.A[h] * kLog2e;
+  const int tile0 = wave * TPW;
+  const bool owns = tile0 < NTILE;
+  const int nt = tile0 / TP, pt0 = tile0 % TP;
+  f32x4 gacc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) gacc[t] = f32x4{0, 0, 0, 0};
+  float lam_seg = 0.0f;
+  for (int c = c1 - 1; c >= c0; --c) {
+    const int64_t row0 = rowb + (int64_t)c * Q;
+    const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
+    Vec16<T> vy[NYV], vc[NCV];
+#pragma unroll
+    for (int v = 0; v < NYV; ++v) {
+      const int idx = min(tid + v * kBThreads, Q * (P / VB) - 1), s = min(idx % Q, len - 1);
+      vy[v] = load16(DYp + (row0 + s) * k.dys + (int64_t)h * P + (idx / Q) * VB);
+    }
+#pragma unroll
+    for (int v = 0; v < NCV; ++v) {
+      const int idx = min(tid + v * kBThreads, Q * (N / VB) - 1), s = min(idx % Q, len - 1);
+      vc[v] = load16(Cp + (row0 + s) * k.cs + (idx / Q) * VB);
+    }
+    const float dtl = to_f32(DTp[(row0 + min(lane, len - 1)) * k.dts + h]);
+#pragma unroll
+    for (int v = 0; v < NYV; ++v) {
+      const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
+      const Vec16<T> yv = s < len ? vy[v] : zero16<T>();
+      if (idx < Q * (P / VB))
+#pragma unroll
+        for (int j = 0; j < VB; ++j) YT[(p0 + j) * TQ + s] = yv.v[j];
+    }
+#pragma unroll
+    for (int v = 0; v < NCV; ++v) {
+      const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
+      const Vec16<T> cv = s < len ? vc[v] : zero16<T>();
+      if (idx < Q * (N / VB))
+#pragma unroll
+        for (int j = 0; j < VB; ++j) CT[(n0 + j) * TQ + s] = cv.v[j];
+    }
+    if (wave == 0) {
+      const float d = lane < len ? dtl : 0.0f;
+      const float lv = chunk_cumsum(d * Ah2, lane);
+      lam[lane] = lv;
+      eL[lane] = __builtin_amdgcn_exp2f(lv);
+    }
+    __syncthreads();
+    lam_seg += lam[Q - 1];
+    if (owns) {
+      const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gacc[t][i] *= dec;
+#pragma unroll
+      for (int ks = 0; ks < Q / 32; ++ks) {
+        const int tq = ks * 32 + g * 8;
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(eL + tq);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(eL + tq + 4);
+        Frag8<T> cr, cf;
+        frag_load8(cr, CT + (nt * 16 + r16) * TQ + tq);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) frag_set(cf, j, to_f32(cr.v[j]) * (j < 4 ? e0[j] : e1[j - 4]));
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          Frag8<T> yf;
+          frag_load8(yf, YT + ((pt0 + t) * 16 + r16) * TQ + tq);
+          gacc[t] = mma(yf, cf, gacc[t]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  float* dst = k.seg_g + (unit * k.nseg + seg) * (P * N);
+  if (owns)
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] = gacc[t][i];
+  if (tid == 0) k.seg_gd[unit * k.nseg + seg] = lam_seg;
+}
+
+// Chains the segments of every unit, one thread per state element.
+// Forward (seg_h): slot s <- exp2(hd_s) * start_s + end_s, the start of
+// segment s+1 (start_0 = h0).  Backward (seg_g): from dL/dH = dhT at the end
+// of the last segment, slot s <- exp2(gd_s) * G + slot s for s = nseg-1..1,
+// the gradient at the end of segment s-1.
+template <int PN>
+__global__ __launch_bounds__(256) void bwd_combine_kernel(BwdK k) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int64_t unit = blockIdx.y;
+  const int b = (int)(unit / k.heads), h = (int)(unit % k.heads);
+  if (e >= PN) return;
+  const int64_t base = ((int64_t)b * k.n_heads + h) * PN + e;
+  float st = k.h0 ? k.h0[base] : 0.0f;
+  for (int s = 0; s + 1 < k.nseg; ++s) {
+    float* slot = k.seg_h + (unit * k.nseg + s) * PN + e;
+    st = __builtin_amdgcn_exp2f(k.seg_hd[unit * k.nseg + s]) * st + *slot;
+    *slot = st;
+  }
+  float gr = k.dhT ? k.dhT[base] : 0.0f;
+  for (int s = k.nseg - 1; s >= 1; --s) {
+    float* slot = k.seg_g + (unit * k.nseg + s) * PN + e;
+    gr = __builtin_amdgcn_exp2f(k.seg_gd[unit * k.nseg + s]) * gr + *slot;
+    *slot = gr;
+  }
 }
 
 template <typename T, int P, int N>
@@ -402,8 +571,10 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
   float* expl = t1 + 2 * Q;   // x_s . u_s, per column half: [2][Q]
   float* hgw = expl + 2 * Q;  // <Gc, H_e> over each wave's tiles: [2][8] by chunk parity
 
-  int b, h;
-  unit_of(k.heads, &b, &h);
+  int b, h, seg;
+  unit_of(k.heads, k.nseg, &b, &h, &seg);
+  const int64_t unit = (int64_t)b * k.heads + h;
+  const int c0 = seg * k.seg_chunks, c1 = min(c0 + k.seg_chunks, k.nchunks);
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int r16 = lane % 16, g = lane / 16;
   const T* __restrict__ Xp = static_cast<const T*>(k.x);
@@ -414,7 +585,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
   T* __restrict__ DXp = static_cast<T*>(k.dx);
   T* __restrict__ DDTp = static_cast<T*>(k.ddt);
   const T* __restrict__ Hst =
-      static_cast<const T*>(k.hst) + ((int64_t)b * k.heads + h) * (k.nchunks + 1) * (P * N);
+      static_cast<const T*>(k.hst) + unit * (k.nchunks + 1) * (P * N);
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Ah = k.A[h];
   const float Ah2 = Ah * kLog2e;
@@ -426,7 +597,11 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
   const int nt = tile0 / TP, pt0 = tile0 % TP;
   f32x4 gacc[TPW];
   {
-    const float* gin = k.dhT ? k.dhT + ((int64_t)b * k.n_heads + h) * (P * N) : nullptr;
+    // dL/dH at the end of this walk: the final state's cotangent, or (split
+    // sequence) the combined gradient at the end of this segment
+    const float* gin = seg + 1 < k.nseg ? k.seg_g + (unit * k.nseg + seg + 1) * (P * N)
+                       : k.dhT          ? k.dhT + ((int64_t)b * k.n_heads + h) * (P * N)
+                                        : nullptr;
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -461,8 +636,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
   // for every other chunk it is formed at the end of the chunk after it,
   // from the operand copy of that chunk's start state in LDS
   {
-    const int cl = k.nchunks - 1;
-    const T* hn = Hst + (int64_t)k.nchunks * (P * N);
+    const int cl = c1 - 1;
+    const T* hn = Hst + (int64_t)c1 * (P * N);
     float hdot = 0.0f;
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
@@ -477,7 +652,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
   float da_acc = 0.0f;  // wave 0: sum_r dt_r da_r of this lane's tokens
   float dd_acc = 0.0f;  // sum dy . x over this lane's entries
 
-  for (int c = k.nchunks - 1; c >= 0; --c) {
+  for (int c = c1 - 1; c >= c0; --c) {
     const int64_t row0 = rowb + (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
 
@@ -833,7 +1008,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
         }
       }
     }
-    if (c > 0) {
+    if (c > c0) {
       float hdot = 0.0f;
       if (owns) {
 #pragma unroll
@@ -881,7 +1056,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
   }
 
   // ---- per-unit results: dh0, dA, dD ----
-  if (k.dh0 && owns) {
+  if (k.dh0 && owns && seg == 0) {
     float* dst = k.dh0 + ((int64_t)b * k.n_heads + h) * (P * N);
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
@@ -921,19 +1096,36 @@ template <typename T, int P, int N>
 hipError_t launch_shape(const BwdK& k, int64_t batch, hipStream_t s) {
   const unsigned units = (unsigned)(batch * k.heads);
   const size_t lds1 = StateLds<T, P, N>::bytes, lds2 = ChunkLds<T, P, N>::bytes;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_state_kernel<T, P, N>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
-  if (e != hipSuccess) return e;
   static_assert(ChunkLds<T, P, N>::bytes <= 160 * 1024, "chunk tiles fit one CU's LDS");
-  hipLaunchKernelGGL((bwd_state_kernel<T, P, N>), dim3(units), dim3(kBThreads), lds1, s, k);
-  e = hipGetLastError();
+  const void* fns[] = {reinterpret_cast<const void*>(&bwd_state_kernel<T, P, N, false>),
+                       reinterpret_cast<const void*>(&bwd_state_kernel<T, P, N, true>),
+                       reinterpret_cast<const void*>(&bwd_gprep_kernel<T, P, N>),
+                       reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N>)};
+  const size_t ldss[] = {lds1, lds1, lds1, lds2};
+  for (int i = 0; i < 4; ++i) {
+    const hipError_t e =
+        hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldss[i]);
+    if (e != hipSuccess) return e;
+  }
+  if (k.nseg > 1) {
+    // segment prepasses (forward states, reverse dL/dH), then the combine
+    const unsigned pre = units * (unsigned)(k.nseg - 1);
+    hipLaunchKernelGGL((bwd_state_kernel<T, P, N, true>), dim3(pre), dim3(kBThreads), lds1, s, k);
+    hipLaunchKernelGGL((bwd_gprep_kernel<T, P, N>), dim3(pre), dim3(kBThreads), lds1, s, k);
+    hipLaunchKernelGGL((bwd_combine_kernel<P * N>), dim3((P * N + 255) / 256, units), dim3(256), 0,
+                       s, k);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const unsigned grid = units * (unsigned)k.nseg;
+  hipLaunchKernelGGL((bwd_state_kernel<T, P, N, false>), dim3(grid), dim3(kBThreads), lds1, s, k);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N>), dim3(units), dim3(kBThreads), lds2, s, k);
+  hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N>), dim3(grid), dim3(kBThreads), lds2, s, k);
   return hipGetLastError();
 }
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -942,11 +1134,31 @@ bool bwd_shape_supported(int64_t d_head, int64_t d_state, int dtype) {
   return d_head == 32 && d_state == 16;
 }
 
+void bwd_plan(int64_t batch, int64_t seqlen, int64_t heads, int* nchunks, int* nseg,
+              int* seg_chunks) {
+  const int nc = (int)((seqlen + kBQ - 1) / kBQ);
+  const int64_t units = batch * heads;
+  // Each (sequence, head) walk is one latency-bound workgroup per CU; with
+  // fewer than 256 walks, split the sequences into segments (at least four
+  // chunks each) so that about 256 workgroups run.
+  int64_t ns = 1;
+  if (units < 256) ns = std::min<int64_t>((256 + units - 1) / units, nc / 4);
+  if (ns < 1) ns = 1;
+  const int sc = (int)((nc + ns - 1) / ns);
+  *nchunks = nc;
+  *seg_chunks = sc;
+  *nseg = (nc + sc - 1) / sc;
+}
+
 size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
                            int64_t d_state, int dtype) {
-  const int64_t nchunks = (seqlen + kBQ - 1) / kBQ;
+  int nc, ns, sc;
+  bwd_plan(batch, seqlen, heads, &nc, &ns, &sc);
   const size_t el = dtype == MM_BF16 ? 2 : 4;
-  return (size_t)(batch * heads) * (size_t)(nchunks + 1) * (size_t)(d_head * d_state) * el;
+  const size_t units = (size_t)(batch * heads), pn = (size_t)(d_head * d_state);
+  size_t bytes = align256(units * (size_t)(nc + 1) * pn * el);
+  if (ns > 1) bytes += 2 * align256(units * ns * pn * 4) + 2 * align256(units * ns * 4);
+  return bytes;
 }
 
 hipError_t launch_ssd_backward(const BwdArgs& a, void* workspace, hipStream_t s) {
@@ -976,12 +1188,28 @@ hipError_t launch_ssd_backward(const BwdArgs& a, void* workspace, hipStream_t s)
   k.dcs = a.dcs;
   k.dD = a.dD;
   k.dh0 = a.dh0;
-  k.hst = workspace;
   k.seqlen = a.seqlen;
   k.n_heads = a.n_heads;
   k.heads = a.heads;
-  k.nchunks = (int)((a.seqlen + kBQ - 1) / kBQ);
+  bwd_plan(a.batch, a.seqlen, a.heads, &k.nchunks, &k.nseg, &k.seg_chunks);
   k.accumulate = a.accumulate;
+  {
+    const size_t el = a.dtype == MM_BF16 ? 2 : 4;
+    const size_t units = (size_t)(a.batch * a.heads), pn = (size_t)(a.d_head * a.d_state);
+    unsigned char* w = static_cast<unsigned char*>(workspace);
+    k.hst = w;
+    w += align256(units * (size_t)(k.nchunks + 1) * pn * el);
+    k.seg_h = k.seg_g = k.seg_hd = k.seg_gd = nullptr;
+    if (k.nseg > 1) {
+      k.seg_h = reinterpret_cast<float*>(w);
+      w += align256(units * k.nseg * pn * 4);
+      k.seg_g = reinterpret_cast<float*>(w);
+      w += align256(units * k.nseg * pn * 4);
+      k.seg_hd = reinterpret_cast<float*>(w);
+      w += align256(units * k.nseg * 4);
+      k.seg_gd = reinterpret_cast<float*>(w);
+    }
+  }
   if (!a.accumulate) {
     const int64_t rows = a.batch * a.seqlen;
     zero_rows(a.dB, a.dbs, a.d_state, rows, s);

@@ -110,6 +110,19 @@ def test_backward_130m_bf16(seqlen):
         _check(_run(w, inp, h), _oracle(inp, h), h, TOL[torch.bfloat16])
 
 
+@pytest.mark.parametrize("w,b,l,h", [(M130, 1, 2048, 3), (M130, 2, 1000, 24), (TINY, 1, 1024, 1)])
+def test_backward_split_sequences(w, b, l, h):
+    """Few (sequence, head) walks: the sequences are split into segments
+    walked in parallel, chained by a forward-state prepass, a reverse dL/dH
+    prepass and a combine; the result matches the oracle as an unsplit call
+    does."""
+    nseg = mm.ssd_backward_segments(b, l, w.n_heads, w.d_head, w.d_state, 1, h, w.dtype)
+    assert nseg > 1
+    inp = _inputs(w, b, l, salt=7)
+    say(f"backward split {w.name} b={b} l={l} heads={h} segments={nseg}")
+    _check(_run(w, inp, h), _oracle(inp, h), h, TOL[w.dtype])
+
+
 def test_backward_dstate64_bf16():
     """bf16 with d_state 64 (the other supported bf16 shape)."""
     w = M130_N64
