@@ -41,6 +41,43 @@ __device__ __forceinline__ void load8f(const T* p, float (&v)[8]) {
   }
 }
 
+// Eight storage elements as raw 16-byte words (one for bf16, two for fp32),
+// so that several rows' loads can be issued before any value is converted.
+struct Raw8 {
+  uint4 a, b;
+};
+
+template <typename T>
+__device__ __forceinline__ Raw8 load8raw(const T* p) {
+  Raw8 r;
+  r.a = *reinterpret_cast<const uint4*>(p);
+  if constexpr (sizeof(T) == 4) r.b = *reinterpret_cast<const uint4*>(p + 4);
+  else r.b = r.a;
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ void raw8f(const Raw8& r, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    // a bf16 is the high half of its fp32
+    const unsigned w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __builtin_bit_cast(float, w[j] << 16);
+      v[2 * j + 1] = __builtin_bit_cast(float, w[j] & 0xffff0000u);
+    }
+  } else {
+    v[0] = __builtin_bit_cast(float, r.a.x);
+    v[1] = __builtin_bit_cast(float, r.a.y);
+    v[2] = __builtin_bit_cast(float, r.a.z);
+    v[3] = __builtin_bit_cast(float, r.a.w);
+    v[4] = __builtin_bit_cast(float, r.b.x);
+    v[5] = __builtin_bit_cast(float, r.b.y);
+    v[6] = __builtin_bit_cast(float, r.b.z);
+    v[7] = __builtin_bit_cast(float, r.b.w);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void store8f(T* p, const float (&v)[8]) {
   if constexpr (sizeof(T) == 2) {
@@ -69,8 +106,10 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
   if (kRT == 64 && r >= rows) return;  // whole wave; no workgroup barrier below
   // (wider rows share a barrier: a row past the end only skips its memory)
   const int nch = r < rows ? d / 8 : 0;
-  const T* yr = y + r * ys;
-  const T* zr = z + r * zs;
+  // a row past the end reads the last row (its values are never used)
+  const int64_t rc = r < rows ? r : rows - 1;
+  const T* yr = y + rc * ys;
+  const T* zr = z + rc * zs;
   T* orow = out + r * os;
   const int tid = threadIdx.x % kRT;
   float g[kCached][8];
@@ -82,13 +121,30 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) gv[j] = yv[j] * silu(zv[j]);
   };
+  {
+    // The cached chunks' loads are issued together, unconditionally at a
+    // clamped chunk index, and masked afterwards: a load under a lane
+    // condition is waited for at the end of its branch, which serialised
+    // them.
+    const int last = d / 8 - 1;
+    Raw8 ry[kCached], rz[kCached];
 #pragma unroll
-  for (int i = 0; i < kCached; ++i) {
-    const int ch = tid + i * kRT;
-    if (ch < nch) {
-      gate(ch, g[i]);
+    for (int i = 0; i < kCached; ++i) {
+      const int ch = min(tid + i * kRT, last);
+      ry[i] = load8raw(yr + ch * 8);
+      rz[i] = load8raw(zr + ch * 8);
+    }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ss = fmaf(g[i][j], g[i][j], ss);
+    for (int i = 0; i < kCached; ++i) {
+      float yv[8], zv[8];
+      raw8f<T>(ry[i], yv);
+      raw8f<T>(rz[i], zv);
+      const bool live = tid + i * kRT < nch;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        g[i][j] = live ? yv[j] * silu(zv[j]) : 0.0f;
+        ss = fmaf(g[i][j], g[i][j], ss);
+      }
     }
   }
   for (int ch = tid + kCached * kRT; ch < nch; ch += kRT) {

@@ -59,30 +59,30 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(
   T* yrow = y + (int64_t)b * ys + (int64_t)h * P;
 
   for (int p0 = 0; p0 < P; p0 += kRowsPerPass * kUnroll) {
+    // Loads at clamped rows, unconditionally; only the stores are guarded.
+    // (A load under a lane condition is waited for at the end of its branch,
+    // and then every row block waited for the previous block's stores.)
     f32x4 s[kUnroll];
     float xv[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int p = p0 + u * kRowsPerPass + row_in_pass;
-      if (p < P) {
-        s[u] = *reinterpret_cast<const f32x4*>(sbase + (int64_t)p * N + n0);
-        xv[u] = to_f32(xrow[p]);
-      }
+      const int p = min(p0 + u * kRowsPerPass + row_in_pass, P - 1);
+      s[u] = *reinterpret_cast<const f32x4*>(sbase + (int64_t)p * N + n0);
+      xv[u] = to_f32(xrow[p]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int p = p0 + u * kRowsPerPass + row_in_pass;
-      if (p < P) {
-        const float xd = dtv * xv[u];
-        f32x4 hn;
+      const float xd = dtv * xv[u];
+      f32x4 hn;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) hn[j] = fmaf(alpha, s[u][j], xd * bv[j]);
+      for (int j = 0; j < 4; ++j) hn[j] = fmaf(alpha, s[u][j], xd * bv[j]);
+      if (p < P)
         __builtin_nontemporal_store(hn, reinterpret_cast<f32x4*>(sbase + (int64_t)p * N + n0));
-        float part = hn[0] * cv[0] + hn[1] * cv[1] + hn[2] * cv[2] + hn[3] * cv[3];
+      float part = hn[0] * cv[0] + hn[1] * cv[1] + hn[2] * cv[2] + hn[3] * cv[3];
 #pragma unroll
-        for (int m = LPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, LPR);
-        if (lane_in_row == 0) yrow[p] = from_f32<T>(part + Dh * xv[u]);
-      }
+      for (int m = LPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, LPR);
+      if (p < P && lane_in_row == 0) yrow[p] = from_f32<T>(part + Dh * xv[u]);
     }
   }
 }
@@ -126,9 +126,9 @@ __global__ __launch_bounds__(kStepThreads) void ssd_steps_kernel(
 
   f32x4 s[kUnroll];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int p = u * kRowsPerPass + row_in_pass;
-    if (p < P) s[u] = *reinterpret_cast<const f32x4*>(state_in + soff + (int64_t)p * N + n0);
+  for (int u = 0; u < kUnroll; ++u) {  // clamped rows, loaded unconditionally
+    const int p = min(u * kRowsPerPass + row_in_pass, P - 1);
+    s[u] = *reinterpret_cast<const f32x4*>(state_in + soff + (int64_t)p * N + n0);
   }
   auto load_tok = [&](int t, float (&bv)[4], float (&cv)[4], float& dtv, float (&xv)[kUnroll]) {
     const int64_t row = (int64_t)b * k + t;
@@ -142,7 +142,8 @@ __global__ __launch_bounds__(kStepThreads) void ssd_steps_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int p = u * kRowsPerPass + row_in_pass;
-      xv[u] = p < P ? to_f32(xrow[p]) : 0.0f;
+      const float v = to_f32(xrow[min(p, P - 1)]);
+      xv[u] = p < P ? v : 0.0f;
     }
   };
   // one token's update with the single step's arithmetic, in its order; the
