@@ -123,6 +123,20 @@ def test_backward_split_sequences(w, b, l, h):
     _check(_run(w, inp, h), _oracle(inp, h), h, TOL[w.dtype])
 
 
+def test_backward_long_context_many_segments():
+    """Long-context shape (32 heads of 64, d_state 128) at its narrowest slice,
+    one 16384-token sequence: 8 walks, split into 32 segments of 512 tokens
+    (the oracle keeps every state of a walk, so the sequence is a 16384-token
+    prefix of the workload's 131072)."""
+    w = synth.WORKLOADS["long"]
+    h, l = w.heads(w.slices[0]), 16384
+    nseg = mm.ssd_backward_segments(1, l, w.n_heads, w.d_head, w.d_state, 1, h, w.dtype)
+    assert nseg == 32
+    inp = _inputs(w, 1, l, salt=8)
+    say(f"backward long bf16 l={l} heads={h} segments={nseg}")
+    _check(_run(w, inp, h), _oracle(inp, h), h, TOL[torch.bfloat16])
+
+
 def test_backward_dstate64_bf16():
     """bf16 with d_state 64 (the other supported bf16 shape)."""
     w = M130_N64
