@@ -400,7 +400,7 @@ int mm_conv_state_advance(float* conv_state, const void* xbc, int64_t xbc_row_st
  *       channels written.
  *   accumulate: 0 overwrites the outputs above, 1 adds into them.
  * dw and dbias are sums formed with fp32 atomics (last bits may vary between
- * runs).  The updated conv state the forward returns is not differentiated.
+ * runs) and must be ordinary device allocations (hipMalloc, coarse-grained).  The updated conv state the forward returns is not differentiated.
  * Preconditions: those of mm_conv1d_silu (heads_active_per_seq aside);
  * seqlen <= 64*65535; dout rows 16-byte aligned; fp32 outputs 4-byte aligned;
  * accumulate 0 or 1 and no output overlapping an input or another output
@@ -463,7 +463,9 @@ int mm_ssd_backward_segments(int64_t batch, int64_t seqlen, int64_t n_heads,
  *   workspace: at least mm_ssd_backward_workspace_size() bytes, 16-byte
  *       aligned, not used concurrently by another call.
  * dB, dC, dA and dD are sums formed with fp32 atomics, so their last bits can
- * differ between runs; dx, ddt and dinitial_state are deterministic.
+ * differ between runs; dx, ddt and dinitial_state are deterministic.  Those
+ * four must be ordinary device allocations (hipMalloc, coarse-grained): the
+ * hardware fp32 atomics used are not defined on fine-grained host memory.
  * Preconditions: those of mm_ssd_forward except chunk (the backward cuts
  * 64-token chunks itself); (d_head, d_state) = (64, 64) or (64, 128) with
  * MM_BF16, (32, 16) with MM_F32 (MM_ERR_UNSUPPORTED otherwise); row strides
