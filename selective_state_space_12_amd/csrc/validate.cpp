@@ -325,6 +325,8 @@ int validate_ssd_backward_shape(int64_t batch, int64_t seqlen, int64_t n_heads, 
   const int st = validate_ssd_shape(batch, seqlen, n_heads, d_head, d_state, ngroups,
                                     n_heads_active, 64, dtype);
   if (st != MM_OK) return st;
+  // one workgroup per (sequence, head) walk, numbered in a 32-bit grid
+  if (batch * n_heads_active >= (int64_t(1) << 31)) return MM_ERR_UNSUPPORTED;
   return bwd_supported(d_head, d_state, dtype) ? MM_OK : MM_ERR_UNSUPPORTED;
 }
 
