@@ -214,6 +214,23 @@ struct StateLds {
 // With the sequence split, PRE walks segments 0..nseg-2 from a zero state and
 // writes each one's end state and log2 decay (seg_h, seg_hd); the main walk
 // of segment s > 0 then starts from the combined state in seg_h slot s-1.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Returns v unchanged, but the compiler can no longer see where it came
+// from.  Values loaded ahead pass through it where they are used, so that
+// unpacking or converting them is not moved up to their load: work placed
+// there makes the wave wait for the load at once, and loading ahead is lost.
+template <typename V> __device__ __forceinline__ V opaque(V v) {
+  if constexpr (sizeof(V) == 2) {
+    unsigned u = __builtin_bit_cast(unsigned short, v);
+    asm volatile("" : "+v"(u));
+    return __builtin_bit_cast(V, static_cast<unsigned short>(u));
+  } else {
+    asm volatile("" : "+v"(v));
+    return v;
+  }
+}
+
 template <typename T, int P, int N, bool PRE>
 __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
   using L = StateLds<T, P, N>;
@@ -243,7 +260,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
   const float Ah2 = k.A[h] * kLog2e;
 
   const int tile0 = wave * TPW;
-  const bool owns = tile0 < NTILE;
+  const bool owns = NTILE >= kBWaves || tile0 < NTILE;  // every wave when tiles >= waves
   const int nt = tile0 / TP, pt0 = tile0 % TP;
   f32x4 hacc[TPW];
   const float* hin = PRE ? nullptr
@@ -256,6 +273,9 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       hacc[t][i] = (hin && owns) ? hin[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] : 0.0f;
+  // the start state's loads complete here, before any chunk is loaded ahead
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) hacc[t] = opaque(hacc[t]);
 
   auto store_state = [&](int c) {
     if (PRE || !owns) return;
@@ -273,8 +293,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
   // once and have two chunks of time to land).
   constexpr int NXV = (Q * (P / VB) + kBThreads - 1) / kBThreads;
   constexpr int NBV = (Q * (N / VB) + kBThreads - 1) / kBThreads;
-  Vec16<T> px[2][NXV], pb[2][NBV];
-  float pdt[2] = {0.0f, 0.0f};
+  u32x4 px[2][NXV], pb[2][NBV];
+  T pdt[2];
   int plen[2] = {0, 0};
   auto prefetch = [&](int c, auto set) {
     constexpr int S = decltype(set)::value;
@@ -288,15 +308,15 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
     for (int v = 0; v < NXV; ++v) {
       const int idx = min(tid + v * kBThreads, Q * (P / VB) - 1), s = idx % Q;
       const int p0 = (idx / Q) * VB;
-      px[S][v] = load16(Xp + (row0 + min(s, len - 1)) * k.xs + (int64_t)h * P + p0);
+      px[S][v] = *reinterpret_cast<const u32x4*>(Xp + (row0 + min(s, len - 1)) * k.xs + (int64_t)h * P + p0);
     }
 #pragma unroll
     for (int v = 0; v < NBV; ++v) {
       const int idx = min(tid + v * kBThreads, Q * (N / VB) - 1), s = idx % Q;
       const int n0 = (idx / Q) * VB;
-      pb[S][v] = load16(Bp + (row0 + min(s, len - 1)) * k.bs + n0);
+      pb[S][v] = *reinterpret_cast<const u32x4*>(Bp + (row0 + min(s, len - 1)) * k.bs + n0);
     }
-    pdt[S] = to_f32(DTp[(row0 + min(lane, len - 1)) * k.dts + h]);
+    pdt[S] = DTp[(row0 + min(lane, len - 1)) * k.dts + h];
     plen[S] = len;
   };
   auto step = [&](int c, auto set) {
@@ -307,7 +327,9 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
 #pragma unroll
     for (int v = 0; v < NXV; ++v) {
       const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
-      const Vec16<T> xv = s < len ? px[S][v] : zero16<T>();
+      const u32x4 raw = opaque(px[S][v]);
+      Vec16<T> xv;
+      *reinterpret_cast<u32x4*>(xv.v) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
       if (idx < Q * (P / VB))
 #pragma unroll
         for (int j = 0; j < VB; ++j) XT[(p0 + j) * TQ + s] = xv.v[j];
@@ -315,20 +337,24 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
 #pragma unroll
     for (int v = 0; v < NBV; ++v) {
       const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
-      const Vec16<T> bv = s < len ? pb[S][v] : zero16<T>();
+      const u32x4 raw = opaque(pb[S][v]);
+      Vec16<T> bv;
+      *reinterpret_cast<u32x4*>(bv.v) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
       if (idx < Q * (N / VB))
 #pragma unroll
         for (int j = 0; j < VB; ++j) BT[(n0 + j) * TQ + s] = bv.v[j];
     }
     if (wave == 0) {
-      const float d = lane < len ? pdt[S] : 0.0f;
+      const float d = lane < len ? to_f32(opaque(pdt[S])) : 0.0f;
       const float lv = chunk_cumsum(d * Ah2, lane);
       const float le = __shfl(lv, 63);
       lam[lane] = lv;
       wsc[lane] = __builtin_amdgcn_exp2f(le - lv) * d;
     }
     __syncthreads();
-    if (c + 2 < c1) prefetch(c + 2, set);
+    // issued on every step (the last two reload the final chunk) so that the
+    // loop has one path and each load is waited for exactly where it is used
+    prefetch(min(c + 2, c1 - 1), set);
     lam_seg += lam[Q - 1];
     if (owns) {
       const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
@@ -357,12 +383,16 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  if (c0 < c1) prefetch(c0, S0{});
-  if (c0 + 1 < c1) prefetch(c0 + 1, S1{});
-  for (int c = c0; c < c1; c += 2) {
+  // c1 - 1 is a valid chunk whenever there is one (c1 = min(c0 + seg_chunks,
+  // nchunks) and nchunks >= 1), so the clamped loads stay in bounds
+  prefetch(min(c0, c1 - 1), S0{});
+  prefetch(min(c0 + 1, c1 - 1), S1{});
+  int c = c0;
+  for (; c + 1 < c1; c += 2) {
     step(c, S0{});
-    if (c + 1 < c1) step(c + 1, S1{});
+    step(c + 1, S1{});
   }
+  if (c < c1) step(c, S0{});
   if (PRE) {
     float* dst = k.seg_h + (unit * k.nseg + seg) * (P * N);
     if (owns)
