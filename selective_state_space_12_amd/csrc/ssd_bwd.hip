@@ -897,6 +897,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
         // epilogue: dx = dt_s u + D dy, x_s . u_s and dy . x over this half's
         // d_head columns, dB atomics over its d_state columns
         float ex[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float dxv[4][TPH];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = s0 + g * 4 + i;
@@ -908,15 +909,41 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
             const float xv = to_f32(Xn[s * NP + p]), yv = to_f32(Yn[s * NP + p]);
             ex[i] += xv * au[pp][i];
             dd_acc += xv * yv;
-            if (live)
-              grad_store(DXp + (row0 + s) * k.dxs + (int64_t)h * P + p, dts * au[pp][i] + Dh * yv,
-                         k.accumulate);
+            dxv[i][pp] = dts * au[pp][i] + Dh * yv;
           }
           if (live && nlive) {
 #pragma unroll
             for (int nn = 0; nn < TNH; ++nn)
               unsafeAtomicAdd(k.dB + (row0 + s) * k.dbs + (nb0 + nn) * 16 + r16, dts * ab[nn][i]);
           }
+        }
+        // dx rows: when adding into the caller's dx, all of this lane's old
+        // values are read (at clamped rows, under the wave-uniform flag only)
+        // before any is written, so the reads are in flight together
+        T* const dxrow = DXp + row0 * k.dxs + (int64_t)h * P;
+        if (k.accumulate) {
+          float old[4][TPH];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int pp = 0; pp < TPH; ++pp)
+              old[i][pp] = to_f32(dxrow[(int64_t)min(s0 + g * 4 + i, len - 1) * k.dxs +
+                                        (pb0 + pp) * 16 + r16]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (s0 + g * 4 + i < len)
+#pragma unroll
+              for (int pp = 0; pp < TPH; ++pp)
+                dxrow[(int64_t)(s0 + g * 4 + i) * k.dxs + (pb0 + pp) * 16 + r16] =
+                    from_f32<T>(old[i][pp] + dxv[i][pp]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (s0 + g * 4 + i < len)
+#pragma unroll
+              for (int pp = 0; pp < TPH; ++pp)
+                dxrow[(int64_t)(s0 + g * 4 + i) * k.dxs + (pb0 + pp) * 16 + r16] =
+                    from_f32<T>(dxv[i][pp]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) ex[i] = row16_sum(ex[i]);
