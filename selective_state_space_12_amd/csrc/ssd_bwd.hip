@@ -438,31 +438,44 @@ __global__ __launch_bounds__(kBThreads) void bwd_gprep_kernel(BwdK k) {
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Ah2 = k.A[h] * kLog2e;
   const int tile0 = wave * TPW;
-  const bool owns = tile0 < NTILE;
+  const bool owns = NTILE >= kBWaves || tile0 < NTILE;  // every wave when tiles >= waves
   const int nt = tile0 / TP, pt0 = tile0 % TP;
   f32x4 gacc[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) gacc[t] = f32x4{0, 0, 0, 0};
   float lam_seg = 0.0f;
-  for (int c = c1 - 1; c >= c0; --c) {
+  // As in the forward state walk: dy, C rows and dt of the chunk two behind
+  // (in walk order) are loaded while this chunk runs, into two register sets
+  // used alternately, and pass through opaque() where they are used.
+  u32x4 py[2][NYV], pc[2][NCV];
+  T pdt[2];
+  int plen[2];
+  auto prefetch = [&](int c, auto set) {
+    constexpr int S = decltype(set)::value;
     const int64_t row0 = rowb + (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
-    Vec16<T> vy[NYV], vc[NCV];
 #pragma unroll
     for (int v = 0; v < NYV; ++v) {
       const int idx = min(tid + v * kBThreads, Q * (P / VB) - 1), s = min(idx % Q, len - 1);
-      vy[v] = load16(DYp + (row0 + s) * k.dys + (int64_t)h * P + (idx / Q) * VB);
+      py[S][v] = *reinterpret_cast<const u32x4*>(DYp + (row0 + s) * k.dys + (int64_t)h * P + (idx / Q) * VB);
     }
 #pragma unroll
     for (int v = 0; v < NCV; ++v) {
       const int idx = min(tid + v * kBThreads, Q * (N / VB) - 1), s = min(idx % Q, len - 1);
-      vc[v] = load16(Cp + (row0 + s) * k.cs + (idx / Q) * VB);
+      pc[S][v] = *reinterpret_cast<const u32x4*>(Cp + (row0 + s) * k.cs + (idx / Q) * VB);
     }
-    const float dtl = to_f32(DTp[(row0 + min(lane, len - 1)) * k.dts + h]);
+    pdt[S] = DTp[(row0 + min(lane, len - 1)) * k.dts + h];
+    plen[S] = len;
+  };
+  auto step = [&](int c, auto set) {
+    constexpr int S = decltype(set)::value;
+    const int len = plen[S];
 #pragma unroll
     for (int v = 0; v < NYV; ++v) {
       const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
-      const Vec16<T> yv = s < len ? vy[v] : zero16<T>();
+      const u32x4 raw = opaque(py[S][v]);
+      Vec16<T> yv;
+      *reinterpret_cast<u32x4*>(yv.v) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
       if (idx < Q * (P / VB))
 #pragma unroll
         for (int j = 0; j < VB; ++j) YT[(p0 + j) * TQ + s] = yv.v[j];
@@ -470,18 +483,22 @@ __global__ __launch_bounds__(kBThreads) void bwd_gprep_kernel(BwdK k) {
 #pragma unroll
     for (int v = 0; v < NCV; ++v) {
       const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
-      const Vec16<T> cv = s < len ? vc[v] : zero16<T>();
+      const u32x4 raw = opaque(pc[S][v]);
+      Vec16<T> cv;
+      *reinterpret_cast<u32x4*>(cv.v) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
       if (idx < Q * (N / VB))
 #pragma unroll
         for (int j = 0; j < VB; ++j) CT[(n0 + j) * TQ + s] = cv.v[j];
     }
     if (wave == 0) {
-      const float d = lane < len ? dtl : 0.0f;
+      const float d = lane < len ? to_f32(opaque(pdt[S])) : 0.0f;
       const float lv = chunk_cumsum(d * Ah2, lane);
       lam[lane] = lv;
       eL[lane] = __builtin_amdgcn_exp2f(lv);
     }
     __syncthreads();
+    // issued on every step, clamped at the segment's first chunk
+    prefetch(max(c - 2, c0), set);
     lam_seg += lam[Q - 1];
     if (owns) {
       const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
@@ -507,7 +524,19 @@ __global__ __launch_bounds__(kBThreads) void bwd_gprep_kernel(BwdK k) {
       }
     }
     __syncthreads();
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // segments 1..nseg-1 each hold at least one chunk (c0 < c1), so every
+  // clamped chunk index below is a valid one
+  prefetch(c1 - 1, S0{});
+  prefetch(max(c1 - 2, c0), S1{});
+  int c = c1 - 1;
+  for (; c - 1 >= c0; c -= 2) {
+    step(c, S0{});
+    step(c - 1, S1{});
   }
+  if (c >= c0) step(c, S0{});
   float* dst = k.seg_g + (unit * k.nseg + seg) * (P * N);
   if (owns)
 #pragma unroll
@@ -1135,18 +1164,23 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
   }
 }
 
-// rows x width fp32 values at p (row stride ld) set to zero
-__global__ __launch_bounds__(256) void zero_rows_kernel(float* p, int64_t ld, int width, int64_t rows) {
+// The summed gradients set to zero in one launch: dB and dC (rows x width
+// fp32 values with their own row strides), dA and dD (heads values; dD may
+// be null).
+__global__ __launch_bounds__(256) void zero_grads_kernel(float* dB, int64_t dbs, float* dC, int64_t dcs,
+                                                         int width, int64_t rows, float* dA, float* dD,
+                                                         int heads) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * width) return;
-  p[(i / width) * ld + i % width] = 0.0f;
-}
-
-void zero_rows(float* p, int64_t ld, int width, int64_t rows, hipStream_t s) {
-  const int64_t n = rows * width;
-  if (n == 0) return;
-  hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, ld,
-                     width, rows);
+  if (i < rows * width) {
+    const int64_t r = i / width;
+    const int col = (int)(i % width);
+    dB[r * dbs + col] = 0.0f;
+    dC[r * dcs + col] = 0.0f;
+  }
+  if (i < heads) {
+    dA[i] = 0.0f;
+    if (dD) dD[i] = 0.0f;
+  }
 }
 
 template <typename T, int P, int N>
@@ -1269,10 +1303,9 @@ hipError_t launch_ssd_backward(const BwdArgs& a, void* workspace, hipStream_t s)
   }
   if (!a.accumulate) {
     const int64_t rows = a.batch * a.seqlen;
-    zero_rows(a.dB, a.dbs, a.d_state, rows, s);
-    zero_rows(a.dC, a.dcs, a.d_state, rows, s);
-    zero_rows(a.dA, a.heads, a.heads, 1, s);
-    if (a.dD) zero_rows(a.dD, a.heads, a.heads, 1, s);
+    const int64_t n = std::max<int64_t>(rows * a.d_state, a.heads);
+    hipLaunchKernelGGL(zero_grads_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.dB, a.dbs,
+                       a.dC, a.dcs, a.d_state, rows, a.dA, a.dD, a.heads);
   }
   if (a.dtype == MM_BF16) {
     if (a.d_state == 128) return launch_shape<bf16, 64, 128>(k, a.batch, s);
