@@ -140,16 +140,20 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_bwd_kernel(
   // at zero and nothing is emitted for those tokens, except the conv-state
   // rows when the run starts the sequence (dpre before token 0 is zero).
   // Tokens past the sequence end have dpre = 0.
-  constexpr int kGroup = 4;
+  constexpr int kGroup = 8;  // tokens whose loads are in flight together (measured: 8 > 4, 16)
   const int tstop = active ? t1 + 3 : t0;
+  // A group's loads are issued with no lane condition, at rows clamped to a
+  // valid token (a load under a lane condition is waited for at the end of
+  // its branch, which would serialise them); only tokens below tend are used.
+  const int tlast = max(0, min(tend, seqlen) - 1);
   for (int tg = t0; tg < tstop; tg += kGroup) {
     float u[kGroup][V], go[kGroup][V];
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i)
-      if (tg + i < tend) {
-        load4f(in + (row0 + tg + i) * in_stride + c, u[i]);
-        load4f(dout + (row0 + tg + i) * dout_stride + c, go[i]);
-      }
+    for (int i = 0; i < kGroup; ++i) {
+      const int tc = min(tg + i, tlast);
+      load4f(in + (row0 + tc) * in_stride + c, u[i]);
+      load4f(dout + (row0 + tc) * dout_stride + c, go[i]);
+    }
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
       const int t = tg + i;
