@@ -23,7 +23,7 @@ namespace mmssd {
 namespace {
 
 constexpr int kNormThreads = 256;
-constexpr int kCached = 4;  // chunks of 8 values held per thread
+constexpr int kMaxCached = 4;  // at most this many chunks of 8 values held per thread
 
 template <typename T>
 __device__ __forceinline__ void load8f(const T* p, float (&v)[8]) {
@@ -97,7 +97,10 @@ __device__ __forceinline__ void store8f(T* p, const float (&v)[8]) {
   }
 }
 
-template <typename T, int kRT>  // kRT threads per row: 64 or 256 (128 also works)
+// kRT threads per row (64, 128 or 256), each holding kCached chunks of 8
+// values in registers between the sum of squares and the scaled write; a
+// row longer than kRT * kCached chunks reloads the rest.
+template <typename T, int kRT, int kCached>
 __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
     const T* __restrict__ y, int64_t ys, const T* __restrict__ z, int64_t zs,
     const float* __restrict__ w, float eps, T* out, int64_t os, int d, int64_t rows) {
@@ -188,11 +191,12 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
   }
 }
 
-template <typename T, int kRT>
+template <typename T, int kRT, int kCached>
 void launch_rt(const NormArgs& a, hipStream_t s) {
+  static_assert(kCached >= 1 && kCached <= kMaxCached, "chunks held per thread");
   constexpr int kRows = kNormThreads / kRT;
   const dim3 grid((unsigned)((a.rows + kRows - 1) / kRows));
-  hipLaunchKernelGGL((gated_rmsnorm_kernel<T, kRT>), grid, dim3(kNormThreads), 0, s,
+  hipLaunchKernelGGL((gated_rmsnorm_kernel<T, kRT, kCached>), grid, dim3(kNormThreads), 0, s,
                      static_cast<const T*>(a.y), a.ys, static_cast<const T*>(a.z), a.zs, a.w, a.eps,
                      static_cast<T*>(a.out), a.os, (int)a.d, a.rows);
 }
@@ -201,9 +205,19 @@ void launch_rt(const NormArgs& a, hipStream_t s) {
 
 template <typename T>
 void launch_typed(const NormArgs& a, hipStream_t s) {
-  // (128 threads per row measured slower than 256 at d = 1024: 0.068 vs 0.060 ms)
-  if (a.d <= 64 * 8) launch_rt<T, 64>(a, s);
-  else launch_rt<T, kNormThreads>(a, s);
+  // Threads per row and chunks per thread sized to the row, so that every
+  // cached load a thread issues is one the row needs (the loads are issued
+  // unconditionally; with more slots than chunks they would repeat the
+  // last chunk and crowd the memory pipeline).
+  // Measured at 32768 rows: one wave per row up to d = 1024 (1024: 0.072 ms
+  // against 0.079 with 256 threads, half of them idle), four waves per row
+  // from there (2048: one wave holding 4 chunks took 0.106 ms against 0.101).
+  const int64_t nch = a.d / 8;
+  if (nch <= 64) launch_rt<T, 64, 1>(a, s);
+  else if (nch <= 128) launch_rt<T, 64, 2>(a, s);
+  else if (nch <= 256) launch_rt<T, kNormThreads, 1>(a, s);
+  else if (nch <= 512) launch_rt<T, kNormThreads, 2>(a, s);
+  else launch_rt<T, kNormThreads, kMaxCached>(a, s);
 }
 
 hipError_t launch_gated_rmsnorm(const NormArgs& a, int dtype, hipStream_t s) {

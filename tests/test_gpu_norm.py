@@ -43,12 +43,13 @@ def test_gated_rmsnorm_full_size_bf16():
     assert e < TOL[torch.bfloat16]
 
 
-@pytest.mark.parametrize("d", [8, 512, 520, 2048, 8192, 8200, 12288])
+@pytest.mark.parametrize("d", [8, 512, 520, 1024, 1032, 2048, 2056, 4096, 4104, 8192, 8200, 12288])
 def test_gated_rmsnorm_widths_and_cache_edge(d):
-    """Row widths on both sides of the one-wave-per-row limit (512; an odd
-    row count leaves a wave of the last workgroup without a row) and around
-    the 4 x 256 x 8 values the kernel keeps in registers (wider rows
-    recompute the gate in a second pass)."""
+    """Row widths on both sides of every launch-shape limit: one wave per row
+    holding 1 or 2 chunks of 8 values (up to 512, 1024), then four waves per
+    row holding 1, 2 or 4 (up to 2048, 4096, 8192; wider rows recompute the
+    gate in a second pass).  Five rows leave rows of the last workgroup
+    empty for the one-wave shapes."""
     g = torch.Generator().manual_seed(d)
     y = torch.randn(5, d, generator=g).to(torch.bfloat16)
     z = torch.randn(5, d, generator=g).to(torch.bfloat16)
