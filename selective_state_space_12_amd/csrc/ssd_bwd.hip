@@ -105,14 +105,17 @@ template <typename T> constexpr int bpad() { return 16 / (int)sizeof(T); }
 // the heads of a sequence share its B and C rows in that XCD's L2.
 // With nsk segments per unit in the grid (segment fastest), *seg is this
 // workgroup's segment among them.
-__device__ __forceinline__ void unit_of(int heads, int nsk, int* b, int* h, int* seg) {
-  const int total = gridDim.x;
-  const int pid = blockIdx.x;
+__device__ __forceinline__ void unit_of_idx(int pid, int total, int heads, int nsk, int* b, int* h,
+                                            int* seg) {
   const int uid = total % kXcds == 0 ? (pid % kXcds) * (total / kXcds) + pid / kXcds : pid;
   const int unit = uid / nsk;
   *seg = uid % nsk;
   *b = unit / heads;
   *h = unit % heads;
+}
+
+__device__ __forceinline__ void unit_of(int heads, int nsk, int* b, int* h, int* seg) {
+  unit_of_idx(blockIdx.x, gridDim.x, heads, nsk, b, h, seg);
 }
 
 // Eight consecutive elements at p[k0..k0+7] when k0 < K, else zeros.
@@ -232,7 +235,7 @@ template <typename V> __device__ __forceinline__ V opaque(V v) {
 }
 
 template <typename T, int P, int N, bool PRE>
-__global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
+__device__ __forceinline__ void state_walk(const BwdK& k, int pid, int total) {
   using L = StateLds<T, P, N>;
   constexpr int Q = kBQ, TQ = L::TQ;
   constexpr int TP = P / 16, TN = N / 16, NTILE = TP * TN;
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
   float* wsc = lam + Q;
 
   int b, h, seg;
-  unit_of(k.heads, PRE ? k.nseg - 1 : k.nseg, &b, &h, &seg);
+  unit_of_idx(pid, total, k.heads, PRE ? k.nseg - 1 : k.nseg, &b, &h, &seg);
   const int64_t unit = (int64_t)b * k.heads + h;
   const int c0 = seg * k.seg_chunks, c1 = min(c0 + k.seg_chunks, k.nchunks);
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
@@ -406,12 +409,17 @@ __global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
   }
 }
 
+template <typename T, int P, int N>
+__global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
+  state_walk<T, P, N, false>(k, blockIdx.x, gridDim.x);
+}
+
 // Reverse prepass of the sequence split: segments 1..nseg-1 walk their
 // chunks backwards from dL/dH = 0 at their end with the dL/dH update alone
 // (dGp = exp(Lambda_e) Gc + sum_t exp(Lambda_t) dy_t C_t^T) and write the
 // result at their start and their log2 decay (seg_g, seg_gd).
 template <typename T, int P, int N>
-__global__ __launch_bounds__(kBThreads) void bwd_gprep_kernel(BwdK k) {
+__device__ __forceinline__ void gprep_walk(const BwdK& k, int pid, int total) {
   using L = StateLds<T, P, N>;
   constexpr int Q = kBQ, TQ = L::TQ;
   constexpr int TP = P / 16, TN = N / 16, NTILE = TP * TN;
@@ -426,7 +434,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_gprep_kernel(BwdK k) {
   float* eL = lam + Q;
 
   int b, h, sg;
-  unit_of(k.heads, k.nseg - 1, &b, &h, &sg);
+  unit_of_idx(pid, total, k.heads, k.nseg - 1, &b, &h, &sg);
   const int seg = sg + 1;
   const int64_t unit = (int64_t)b * k.heads + h;
   const int c0 = seg * k.seg_chunks, c1 = min(c0 + k.seg_chunks, k.nchunks);
@@ -544,6 +552,16 @@ __global__ __launch_bounds__(kBThreads) void bwd_gprep_kernel(BwdK k) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] = gacc[t][i];
   if (tid == 0) k.seg_gd[unit * k.nseg + seg] = lam_seg;
+}
+
+// Both prepasses of the sequence split in one launch: they are independent
+// and each fills fewer than all CUs.  Workgroups [0, total/2) walk segments
+// 0..nseg-2 forward, the rest segments 1..nseg-1 backward.
+template <typename T, int P, int N>
+__global__ __launch_bounds__(kBThreads) void bwd_prepass_kernel(BwdK k) {
+  const int half = gridDim.x / 2;
+  if ((int)blockIdx.x < half) state_walk<T, P, N, true>(k, blockIdx.x, half);
+  else gprep_walk<T, P, N>(k, blockIdx.x - half, half);
 }
 
 // Chains the segments of every unit, one thread per state element.
@@ -1188,12 +1206,11 @@ hipError_t launch_shape(const BwdK& k, int64_t batch, hipStream_t s) {
   const unsigned units = (unsigned)(batch * k.heads);
   const size_t lds1 = StateLds<T, P, N>::bytes, lds2 = ChunkLds<T, P, N>::bytes;
   static_assert(ChunkLds<T, P, N>::bytes <= 160 * 1024, "chunk tiles fit one CU's LDS");
-  const void* fns[] = {reinterpret_cast<const void*>(&bwd_state_kernel<T, P, N, false>),
-                       reinterpret_cast<const void*>(&bwd_state_kernel<T, P, N, true>),
-                       reinterpret_cast<const void*>(&bwd_gprep_kernel<T, P, N>),
+  const void* fns[] = {reinterpret_cast<const void*>(&bwd_state_kernel<T, P, N>),
+                       reinterpret_cast<const void*>(&bwd_prepass_kernel<T, P, N>),
                        reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N>)};
-  const size_t ldss[] = {lds1, lds1, lds1, lds2};
-  for (int i = 0; i < 4; ++i) {
+  const size_t ldss[] = {lds1, lds1, lds2};
+  for (int i = 0; i < 3; ++i) {
     const hipError_t e =
         hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldss[i]);
     if (e != hipSuccess) return e;
@@ -1201,15 +1218,14 @@ hipError_t launch_shape(const BwdK& k, int64_t batch, hipStream_t s) {
   if (k.nseg > 1) {
     // segment prepasses (forward states, reverse dL/dH), then the combine
     const unsigned pre = units * (unsigned)(k.nseg - 1);
-    hipLaunchKernelGGL((bwd_state_kernel<T, P, N, true>), dim3(pre), dim3(kBThreads), lds1, s, k);
-    hipLaunchKernelGGL((bwd_gprep_kernel<T, P, N>), dim3(pre), dim3(kBThreads), lds1, s, k);
+    hipLaunchKernelGGL((bwd_prepass_kernel<T, P, N>), dim3(2 * pre), dim3(kBThreads), lds1, s, k);
     hipLaunchKernelGGL((bwd_combine_kernel<P * N>), dim3((P * N + 255) / 256, units), dim3(256), 0,
                        s, k);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const unsigned grid = units * (unsigned)k.nseg;
-  hipLaunchKernelGGL((bwd_state_kernel<T, P, N, false>), dim3(grid), dim3(kBThreads), lds1, s, k);
+  hipLaunchKernelGGL((bwd_state_kernel<T, P, N>), dim3(grid), dim3(kBThreads), lds1, s, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N>), dim3(grid), dim3(kBThreads), lds2, s, k);
