@@ -67,6 +67,29 @@ __device__ __forceinline__ Vec16<T> zero16() {
   return r;
 }
 
+// ---- range-checked stores ------------------------------------------------
+// 16 bytes per lane at byte offset `off` of [base, base + bytes), through a
+// buffer resource: the hardware drops lanes whose offset lies outside the
+// range, so a ragged tail needs no lane-conditional branch.  (A branch around
+// a store leaves the store count of later code unknown, and the compiler then
+// makes every later wait for a load also wait for all stores.)  Nontemporal:
+// data written once.  Offsets are 32-bit: callers keep `bytes` below 2^32.
+// `base` and `bytes` must be the same in every lane (the resource lives in
+// scalar registers).
+__device__ __forceinline__ void store16_nt_ranged(void* base, uint32_t bytes, uint32_t off,
+                                                  uint4 v) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  const int nb = __builtin_amdgcn_readfirstlane((int)bytes);
+  // word 3 of a gfx9 raw buffer resource: 32-bit data format, no swizzle
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(ub, 0, nb, 0x00020000);
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)off, 0,
+                                         2 /* nt */);
+}
+
 // ---- MFMA fragments -----------------------------------------------------
 // A 16x16 output tile computed from a K=32 slice.  Lane l (0..63) with
 // row/col index r = l % 16 and group g = l / 16 holds, for the A operand,

@@ -89,7 +89,11 @@ constexpr int kHF = kP * kN;   // elements of the operand copy of H (16 fragment
 constexpr int kStgRows = 4 + 32;
 constexpr int kStg = 4 * kStgRows * kP;
 constexpr size_t kDec = 3 * kQ;  // floats: Lambda, dt, block-end factor
-constexpr size_t kLds = (size_t)(2 * kXBuf + 2 * kHF + kStg) * sizeof(bf16) + 3 * kDec * sizeof(float);
+// Output staging: each output wave's 16 tokens x 64 channels (rows laid out
+// as the staged x rows, soff), so that y leaves in whole 128-byte lines.
+constexpr int kYRows = 16;
+constexpr size_t kYOff = (size_t)(2 * kXBuf + 2 * kHF + kStg) * sizeof(bf16) + 3 * kDec * sizeof(float);
+constexpr size_t kLds = kYOff + (size_t)8 * kYRows * kP * sizeof(bf16);
 
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -394,6 +398,7 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
   const bf16* xbuf = reinterpret_cast<const bf16*>(smem);
   const bf16* hbuf = xbuf + 2 * kXBuf;
   const float* dbuf = reinterpret_cast<const float*>(hbuf + 2 * kHF + kStg);
+  bf16* ybuf = reinterpret_cast<bf16*>(smem + kYOff) + (threadIdx.x >> 6) * kYRows * kP;
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Dh = k.D ? k.D[h] : 0.0f;
   const int t = tb * 16 + r16;  // this lane's token within a tile
@@ -413,6 +418,12 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
 
   load_c(c0);
   load_g(c0);
+  // Two stores with an empty range (dropped by the hardware) after the
+  // prologue loads, as each tile issues its two y stores after its loads:
+  // the compiler's wait at the top of the loop then lets the previous tile's
+  // stores stay in flight on every path into it.
+  store16_nt_ranged(k.y, 0u, 0u, make_uint4(0u, 0u, 0u, 0u));
+  store16_nt_ranged(k.y, 0u, 0u, make_uint4(0u, 0u, 0u, 0u));
   __syncthreads();  // decay cumsums and H_prev copy of the first tile
   __syncthreads();  // x copies of the first tile
 
@@ -489,15 +500,34 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
       acc[pb] = mma(xf, m, acc[pb] * sc);
     }
 
-    if (t < len) {
-      bf16* yb = k.y + (r0 + t) * k.ys + (int64_t)h * kP + g * 8;
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const uint2 lo = pack4(acc[2 * a]), hi = pack4(acc[2 * a + 1]);
-        *reinterpret_cast<uint4*>(yb + a * 32) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
-    }
+    // The next tile's G fragments are requested before the y stores: the
+    // vmcnt counter retires in order, so a load issued after the stores
+    // would make its wait (early in the next tile) wait for the stores too.
     load_g(cn);
+    // y through the wave's LDS rows: lane (r, g) holds chunks g and 4 + g
+    // (16 bytes each) of token r; read back, lane (i, j) = (lane / 8, lane % 8)
+    // holds chunk j of token 8k + i, so each store instruction writes eight
+    // whole 128-byte lines.  Whole-line nontemporal stores let the L2 hand
+    // the lines to HBM without interleaving with the fragment loads that
+    // every head repeats (measured: half-line stores cost ~20% of the
+    // kernel).  One wave's LDS operations complete in order, so the reads see
+    // the writes and the next tile's writes follow this tile's reads.
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const uint2 lo = pack4(acc[2 * a]), hi = pack4(acc[2 * a + 1]);
+      *reinterpret_cast<uint4*>(ybuf + soff(r16, a * 4 + g)) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int row = kk * 8 + (lane >> 3);
+      const uint4 v = *reinterpret_cast<const uint4*>(ybuf + soff(row, lane & 7));
+      // rows tb*16 + 8kk .. +7; those at or past the sequence end are dropped
+      const int first = tb * 16 + kk * 8;
+      const int nrows = min(max(len - first, 0), 8);
+      store16_nt_ranged(k.y + (r0 + first) * k.ys + (int64_t)h * kP,
+                        (uint32_t)(nrows * k.ys * (int64_t)sizeof(bf16)),
+                        (uint32_t)((lane >> 3) * k.ys * (int64_t)sizeof(bf16) + (lane & 7) * 16), v);
+    }
     __syncthreads();
   }
 }

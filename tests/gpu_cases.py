@@ -70,3 +70,32 @@ def oracle_forward(inp, heads, h0=True, head_idx=None):
     D = f64(inp["D"])[idx]
     hh = f64(inp["h0"])[:, idx] if (h0 and "h0" in inp) else None
     return oracle.ssd_forward(x, dt, A, f64(inp["B"]), f64(inp["C"]), D, hh)
+
+
+def tile_rel_l2(got: np.ndarray, want: np.ndarray, tile: int = 128) -> np.ndarray:
+    """Relative L2 of every 128-token tile of every (sequence, head) unit:
+    ``got``/``want`` are (b, l, heads, ...) arrays; returns (b, ceil(l/tile),
+    heads).  One wrong tile, segment seam or first token of a tile is then
+    visible on its own instead of being diluted by a norm over the whole
+    sequence."""
+    b, l, h = want.shape[:3]
+    nt = (l + tile - 1) // tile
+    out = np.zeros((b, nt, h))
+    for c in range(nt):
+        g = got[:, c * tile:(c + 1) * tile].reshape(b, -1, h, int(np.prod(want.shape[3:], dtype=int)))
+        w = want[:, c * tile:(c + 1) * tile].reshape(g.shape)
+        num = np.sqrt(((g - w) ** 2).sum(axis=(1, 3)))
+        den = np.sqrt((w ** 2).sum(axis=(1, 3)))
+        out[:, c] = num / np.maximum(den, 1e-300)
+    return out
+
+
+def assert_tiles(got: np.ndarray, want: np.ndarray, tol: float, what: str = "y") -> float:
+    """Every 128-token tile of every sampled unit within ``tol`` (relative L2);
+    returns the worst tile's error."""
+    e = tile_rel_l2(got, want)
+    worst = float(e.max())
+    bi, ci, hi = np.unravel_index(int(e.argmax()), e.shape)
+    say(f"  worst {what} tile: seq {bi} tile {ci} head {hi}: {worst:.3e}")
+    assert worst < tol, (what, bi, ci, hi, worst)
+    return worst

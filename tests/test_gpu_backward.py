@@ -221,3 +221,36 @@ def test_backward_rejects_bad_arguments():
     with pytest.raises(mm.MMError):  # fp32 with d_head 64 is not a backward shape
         f = {k: (v.float() if v.dtype == torch.bfloat16 else v) for k, v in inp.items()}
         mm.ssd_backward(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], f["dy"])
+
+
+def test_backward_accumulates_on_split_sequences():
+    """Accumulating over granularities where the calls split the sequence:
+    the second call's combined prepass, chained segment states, segment-
+    parallel dx read-modify-writes and the dinitial_state written only by the
+    first segment must add into the first call's gradients."""
+    w = M130
+    b, l = 1, 2048
+    hs = (24, 3)
+    nseg = [mm.ssd_backward_segments(b, l, w.n_heads, w.d_head, w.d_state, 1, h, w.dtype)
+            for h in hs]
+    assert max(nseg) > 1, nseg
+    inp = _inputs(w, b, l, salt=11)
+    g = None
+    total = None
+    for i, h in enumerate(hs):
+        say(f"backward accumulate split heads={h} segments={nseg[i]}")
+        g = _run(w, inp, h, grads=g, accumulate=i > 0)
+        r = _oracle(inp, h)
+        if total is None:
+            total = r
+        else:
+            for k in NAMES:
+                if k in ("dB", "dC"):
+                    total[k] = total[k] + r[k]
+                elif k in ("dA", "dD"):
+                    total[k][:h] += r[k][:h]
+                elif k == "dinitial_state":
+                    total[k][:, :h] += r[k][:, :h]
+                else:
+                    total[k][:, :, :h] += r[k][:, :, :h]
+    _check(g, total, max(hs), TOL[torch.bfloat16])
