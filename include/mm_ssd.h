@@ -35,8 +35,11 @@
  *     (x, dt, B, C, y, conv input/output).  A, D, conv weights and every state
  *     are fp32.  All arithmetic is fp32; bf16 stores round to nearest even.
  *   - Ownership: the caller owns every buffer.  The library allocates no
- *     memory, keeps no pointer after returning and holds no mutable global
- *     state; scratch memory comes in through `workspace`.  Calls are
+ *     memory and keeps no pointer after returning; scratch memory comes in
+ *     through `workspace`.  Its only global state: a per-device flag noting
+ *     that the scan kernels' LDS limit has been raised (set once per device,
+ *     idempotent, safe from any thread), and the device array that
+ *     mm_ssd_forward_noalloc uses instead of a workspace (see there).  Calls are
  *     asynchronous on `stream` (a hipStream_t; NULL = the null stream); buffers
  *     must stay valid until the stream has passed the call.  No entry point
  *     synchronises the host, so calls may be captured into a HIP graph.
@@ -192,6 +195,36 @@ int mm_ssd_forward(const void* x, int64_t x_row_stride,
                    int64_t d_head, int64_t d_state, int64_t ngroups,
                    int64_t n_heads_active, int64_t chunk, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the device array mm_ssd_forward_noalloc takes its workspace from. */
+#define MM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * mm_ssd_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops that forbid allocation, harnesses that
+ * forbid hipMalloc.  Same arguments, results and errors as mm_ssd_forward,
+ * without `workspace`: the workspace is a device array of
+ * MM_NOALLOC_SCRATCH_BYTES (64 MiB) compiled into the library, one per GPU,
+ * held from the first call on that GPU until the process ends.  Calls whose
+ * mm_ssd_forward_workspace_size() exceeds that return MM_ERR_WORKSPACE before
+ * anything is enqueued (64 MiB covers, e.g., 32768 tokens at 64 heads of
+ * d_head 64 / d_state 128).  The call allocates nothing and never frees.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams or other host threads) race and must not be
+ * issued; calls in order on one stream are safe.
+ */
+int mm_ssd_forward_noalloc(const void* x, int64_t x_row_stride,
+                           const void* dt, int64_t dt_row_stride,
+                           const float* A,
+                           const void* B, int64_t b_row_stride,
+                           const void* C, int64_t c_row_stride,
+                           const float* D,
+                           void* y, int64_t y_row_stride,
+                           const float* initial_state, float* final_state,
+                           int64_t batch, int64_t seqlen, int64_t n_heads,
+                           int64_t d_head, int64_t d_state, int64_t ngroups,
+                           int64_t n_heads_active, int64_t chunk, int dtype,
+                           void* stream);
 
 /*
  * Bytes of device workspace mm_ssd_forward_mixed needs for these sizes and

@@ -75,6 +75,10 @@ def lib() -> ctypes.CDLL:
                                          _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                          _i64, _i64, _i64, _int, _vp, ctypes.c_size_t, _vp]
             L.mm_ssd_forward.restype = _int
+            L.mm_ssd_forward_noalloc.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64,
+                                                 _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64,
+                                                 _i64, _i64, _i64, _i64, _int, _vp]
+            L.mm_ssd_forward_noalloc.restype = _int
             L.mm_ssd_forward_fused_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64,
                                                               _i64, _i64, _int,
                                                               ctypes.POINTER(ctypes.c_size_t)]
@@ -273,6 +277,42 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
                               batch, seqlen, n_heads, d_head, d_state, ngroups, h_act, chunk,
                               code, _ptr(workspace), wbytes, _stream())
     _check("mm_ssd_forward", st)
+    return y
+
+
+def ssd_forward_noalloc(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                        C: torch.Tensor, D: Optional[torch.Tensor] = None, *,
+                        n_heads_active: Optional[int] = None, chunk: int = 256,
+                        initial_state: Optional[torch.Tensor] = None,
+                        final_state: Optional[torch.Tensor] = None,
+                        y: torch.Tensor) -> torch.Tensor:
+    """ssd_forward through mm_ssd_forward_noalloc: no workspace argument and
+    no device allocation anywhere in the call (the library's fixed device
+    array serves as workspace), so ``y`` must be given.  Same layouts as
+    ssd_forward."""
+    batch, seqlen, n_heads, d_head = x.shape
+    if B.dim() == 3:
+        B = B.unsqueeze(2)
+        C = C.unsqueeze(2)
+    ngroups, d_state = B.shape[2], B.shape[3]
+    h_act = n_heads if n_heads_active is None else int(n_heads_active)
+    code = _dtype_code(x)
+    for name, t in (("dt", dt), ("B", B), ("C", C), ("y", y)):
+        if t.dtype != x.dtype:
+            raise TypeError(f"{name} must have x's dtype")
+    xs = _row_stride(x, "x", (n_heads, d_head))
+    ys = _row_stride(y, "y", (y.shape[2], d_head))
+    dts = _row_stride(dt, "dt", (n_heads,))
+    bs = _row_stride(B, "B", (ngroups, d_state))
+    cs = _row_stride(C, "C", (ngroups, d_state))
+    for name, t in (("A", A), ("D", D), ("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 tensor")
+    st = lib().mm_ssd_forward_noalloc(_ptr(x), xs, _ptr(dt), dts, _ptr(A), _ptr(B), bs, _ptr(C),
+                                      cs, _ptr(D), _ptr(y), ys, _ptr(initial_state),
+                                      _ptr(final_state), batch, seqlen, n_heads, d_head, d_state,
+                                      ngroups, h_act, chunk, code, _stream())
+    _check("mm_ssd_forward_noalloc", st)
     return y
 
 
