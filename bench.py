@@ -228,6 +228,10 @@ def main():
                          "call / scan call / scan backward / conv backward (for counter and "
                          "trace runs); copy: a 1 GiB device copy that calibrates the HBM "
                          "byte counters")
+    ap.add_argument("--workload", choices=["1.4b", "long", "130m"], default="1.4b",
+                    help="with --mode scan: the workload whose scan call is repeated")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="with --mode scan: active heads (default: all)")
     ap.add_argument("--summarize-pmc", nargs=5,
                     metavar=("WHICH", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="WHICH = scan or fused, then rocprofv3 --pmc output dirs (csv); writes "
@@ -247,6 +251,9 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.mode == "scan" and (args.workload != "1.4b" or args.heads):
+        scan_only(torch, mm, synth, dev, synth.WORKLOADS[args.workload], args)
+        return
     w = synth.WORKLOADS["1.4b"]
     b, l, H, P, N = w.batch, w.seqlen, w.n_heads, w.d_head, w.d_state
     tokens = b * l
@@ -482,6 +489,24 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w)
 
     print(json.dumps(out), flush=True)
+
+
+def scan_only(torch, mm, synth, dev, w, args):
+    """Trace and counter runs: the scan call of one workload at one width,
+    repeated (inputs drawn as in the slice timings)."""
+    h = args.heads or w.n_heads
+    inp = synth.forward_inputs(w)
+    d = {k: v.to(dev) for k, v in inp.items()}
+    b, l = w.batch, w.seqlen
+    y = torch.empty((b, l, w.n_heads, w.d_head), dtype=w.dtype, device=dev)
+    ws = torch.empty(max(mm.ssd_forward_workspace_size(b, l, w.n_heads, w.d_head, w.d_state, 1,
+                                                       h, w.chunk, w.dtype), 1),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup + args.steps):
+        mm.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], n_heads_active=h,
+                       chunk=w.chunk, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    print(f"# scan-only {w.name} heads={h}: {args.warmup + args.steps} launches", file=sys.stderr)
 
 
 def bench_backward(torch, mm, synth, w, dev, flush, xv, dt, A, Bv, Cv, D, slices=None):

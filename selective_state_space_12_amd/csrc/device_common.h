@@ -74,20 +74,44 @@ __device__ __forceinline__ Vec16<T> zero16() {
 // a store leaves the store count of later code unknown, and the compiler then
 // makes every later wait for a load also wait for all stores.)  Nontemporal:
 // data written once.  Offsets are 32-bit: callers keep `bytes` below 2^32.
-// `base` and `bytes` must be the same in every lane (the resource lives in
-// scalar registers).
-__device__ __forceinline__ void store16_nt_ranged(void* base, uint32_t bytes, uint32_t off,
-                                                  uint4 v) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+// Buffer resource over the byte range [addr, addr + bytes), forced uniform
+// (it lives in scalar registers; `addr` and `bytes` must be the same in every
+// lane).  Loads through it at an offset outside the range return 0 and stores
+// there are dropped.  Buffer loads and stores address with a scalar base and
+// a 32-bit per-lane offset; on gfx950 they measured ~10% faster than 64-bit
+// per-lane global addressing for the scan's mix of shared-fragment loads and
+// streamed rows.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(uint64_t addr, uint32_t bytes) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
   void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
   const int nb = __builtin_amdgcn_readfirstlane((int)bytes);
   // word 3 of a gfx9 raw buffer resource: 32-bit data format, no swizzle
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(ub, 0, nb, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, nb, 0x00020000);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
+  return uniform_rsrc(reinterpret_cast<uint64_t>(base), bytes);
+}
+
+// Cache policies of the buffer operations (gfx950): 0 = default, 2 = nontemporal.
+constexpr int kPolicyDefault = 0;
+constexpr int kPolicyNT = 2;
+
+template <int POLICY>
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)off, 0,
-                                         2 /* nt */);
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POLICY));
+}
+template <int POLICY>
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, POLICY);
+}
+
+__device__ __forceinline__ void store16_nt_ranged(void* base, uint32_t bytes, uint32_t off,
+                                                  uint4 v) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), uniform_rsrc(base, bytes),
+                                         (int)off, 0, kPolicyNT);
 }
 
 // ---- MFMA fragments -----------------------------------------------------

@@ -25,14 +25,18 @@
 //    (lane-major, 16 bytes per lane), so every operand read is a linear,
 //    conflict-free 16-byte load.  Each staging wave transposes its 32 tokens
 //    once per tile (raw rows to LDS, LDS transpose loads back) and writes two
-//    x copies: plain, and times the block-end decay.
-//  - off-diagonal 32-token blocks factor the decay as
-//    exp(Lambda_t - Lambda_e) * exp(Lambda_e - Lambda_s) dt_s (e = block end,
-//    both factors <= 1); the first factor is applied to the accumulator in
-//    Horner form (one scalar per block), so G enters the MFMA unscaled.  The
-//    state update uses the same block-scaled copy with the same Horner
-//    factors on its accumulators.  The diagonal block takes the direct masked
-//    form, with D folded into the diagonal of the mask.
+//    x copies: plain, and times the tile-end factor exp(Lambda_end -
+//    Lambda_s) dt_s (<= dt_s) for the state update.
+//  - the state is decayed to the tile end once per tile, after which its
+//    four 32-token MFMA blocks accumulate with no rescaling in between (a
+//    per-block rescale had put a VALU step between dependent MFMAs on the
+//    waves that bounded the tile time).
+//  - every output block takes the plain x copy: off-diagonal 32-token blocks
+//    split the factor exp(Lambda_t - Lambda_s) dt_s into exp(Lambda_t -
+//    Lambda_e) (one scalar per lane, e = block end) times the block-end
+//    factor exp(Lambda_e - Lambda_s) dt_s, both <= 1, applied to the G
+//    fragment in registers; the diagonal block takes the direct masked form,
+//    with D folded into the diagonal of the mask.
 //  - output rows are dealt to the A operand in an order that leaves each lane
 //    eight consecutive channels of a token, stored as one 16-byte write;
 //  - LDS tiles are double-buffered and the decay cumsums triple-buffered, so
@@ -80,15 +84,17 @@ constexpr size_t kFragBytes = 64 * 16;           // one wave-wide fragment
 //   x fragment (q, pb):   lane (r, g) holds x[q*32 + g*8 + j][column pb*16 + r]
 //   H fragment (pb, kb):  lane (r, g) holds H[chan(pb, r)][kb*32 + g*8 + j]
 constexpr int kXE = kQ * kP;   // elements of one x tile (16 fragments)
-// Per buffer two x tiles: plain (diagonal blocks) and scaled by the block-end
-// factor (off-diagonal blocks and the state update).
+// Per buffer two x tiles: plain (output blocks) and scaled by the tile-end
+// factor (the state update).
 constexpr int kXBuf = 2 * kXE;
 constexpr int kHF = kP * kN;   // elements of the operand copy of H (16 fragments)
 // Raw token-major rows per staging wave: 4 rows before its 32 tokens (the
 // conv window of a fused call) and the 32 rows themselves.
 constexpr int kStgRows = 4 + 32;
 constexpr int kStg = 4 * kStgRows * kP;
-constexpr size_t kDec = 3 * kQ;  // floats: Lambda, dt, block-end factor
+// floats: Lambda, dt, block-end factor exp2(Lambda_e - Lambda_s) dt_s (e the
+// end of s's 32-token block), tile-end factor exp2(Lambda_end - Lambda_s) dt_s
+constexpr size_t kDec = 4 * kQ;
 // Output staging: each output wave's 16 tokens x 64 channels (rows laid out
 // as the staged x rows, soff), so that y leaves in whole 128-byte lines.
 constexpr int kYRows = 16;
@@ -384,6 +390,13 @@ struct BK {
   UnitMap um;
 };
 
+// Buffer range over the fragments of tile c of sequence b, and the byte
+// offset of lane `lane`'s 16 bytes of fragment f in it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_frags(const BK& k, int b, int c) {
+  return uniform_rsrc(k.frags + ((int64_t)b * k.ntiles + c) * kNFR * 64, (uint32_t)(kNFR * kFragBytes));
+}
+__device__ __forceinline__ uint32_t frag_off(int f, int lane) { return (uint32_t)(f * 64 + lane) * 16; }
+
 // ---------------------------------------------------------------------------
 // Output waves (OUT only).  Each produces one 16-token block tb of every tile
 // for all 64 channels of the head; L = tb/2 is the number of 32-token blocks
@@ -406,14 +419,16 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
   Frag8<bf16> cf[kKB];
   Frag8<bf16> gf[L + 1];
   auto load_c = [&](int c) {
-    const uint4* f = k.frags + (((int64_t)b * k.ntiles + c) * kNFR + kC0 + tb * kKB) * 64 + lane;
+    const auto r = tile_frags(k, b, c);
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) cf[kb] = as_frag(f[kb * 64]);
+    for (int kb = 0; kb < kKB; ++kb)
+      cf[kb] = as_frag(buffer_load16<kPolicyDefault>(r, frag_off(kC0 + tb * kKB + kb, lane)));
   };
   auto load_g = [&](int c) {
-    const uint4* f = k.frags + (((int64_t)b * k.ntiles + c) * kNFR + gbase(tb)) * 64 + lane;
+    const auto r = tile_frags(k, b, c);
 #pragma unroll
-    for (int q = 0; q <= L; ++q) gf[q] = as_frag(f[q * 64]);
+    for (int q = 0; q <= L; ++q)
+      gf[q] = as_frag(buffer_load16<kPolicyDefault>(r, frag_off(gbase(tb) + q, lane)));
   };
 
   load_c(c0);
@@ -432,9 +447,9 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
     const int64_t r0 = rowb + (int64_t)c * kQ;
     const bf16* Hs = hbuf + (c & 1) * kHF;
     const bf16* XT = xbuf + (c & 1) * kXBuf;
-    const bf16* XE = XT + kXE;
     const float* lam = dbuf + (c % 3) * kDec;
     const float* dtv = lam + kQ;
+    const float* bef = lam + 2 * kQ;  // block-end factors
 
     f32x4 acc[kPB];
 #pragma unroll
@@ -476,28 +491,37 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
     const int cn = min(c + 1, c1 - 1);
     load_c(cn);
 
-    // Off-diagonal blocks in Horner form.  Before block q the accumulator is
-    // referred to the end e(q-1) of the previous block (the tile start for
-    // q = 0) and is moved to e(q) by exp2(lam[e(q)] - lam[e(q-1)]) <= 1; the
-    // block's own terms carry exp2(lam[e(q)] - lam_s) dt_s inside x (XE).
-    float prev = 0.0f;
+    // The state's contribution decays from the tile start to the token.
+    {
+      const float st = __builtin_amdgcn_exp2f(lt);
+#pragma unroll
+      for (int pb = 0; pb < kPB; ++pb) acc[pb] *= st;
+    }
+    // Off-diagonal blocks q < L: the exact factor exp2(lam_t - lam_s) dt_s
+    // is split as exp2(lam_t - lam_e) (e = end of block q, one scalar per
+    // lane, <= 1) times the block-end factor of s, and applied to the G
+    // fragment in registers, so these blocks take the plain x copy.
 #pragma unroll
     for (int q = 0; q < L; ++q) {
-      const float eq = lam[q * 32 + 31];
-      const float r = __builtin_amdgcn_exp2f(eq - prev);
-      prev = eq;
+      const float f = __builtin_amdgcn_exp2f(lt - lam[q * 32 + 31]);
+      const f32x4 ga = *reinterpret_cast<const f32x4*>(bef + q * 32 + g * 8);
+      const f32x4 gb = *reinterpret_cast<const f32x4*>(bef + q * 32 + g * 8 + 4);
+      Frag8<bf16> mq;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        mq.v[j] = static_cast<bf16>(static_cast<float>(gf[q].v[j]) * (f * ga[j]));
+        mq.v[j + 4] = static_cast<bf16>(static_cast<float>(gf[q].v[j + 4]) * (f * gb[j]));
+      }
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
-        const Frag8<bf16> xf = lds_frag(XE + foff(q * kPB + pb, lane));
-        acc[pb] = mma(xf, gf[q], acc[pb] * r);
+        const Frag8<bf16> xf = lds_frag(XT + foff(q * kPB + pb, lane));
+        acc[pb] = mma(xf, mq, acc[pb]);
       }
     }
-    // from the last block end (tile start if none) to the token: <= 1
-    const float sc = __builtin_amdgcn_exp2f(lt - prev);
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb) {
       const Frag8<bf16> xf = lds_frag(XT + foff(L * kPB + pb, lane));
-      acc[pb] = mma(xf, m, acc[pb] * sc);
+      acc[pb] = mma(xf, m, acc[pb]);
     }
 
     // The next tile's G fragments are requested before the y stores: the
@@ -564,9 +588,11 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
   }
   Frag8<bf16> bt[kNBW][kSB];
   auto load_bt = [&](int c, int ks) {  // one 32-token slice of this wave's B^T columns
-    const uint4* f = k.frags + (((int64_t)b * k.ntiles + c) * kNFR + kBT0) * 64 + lane;
+    const auto r = tile_frags(k, b, c);
 #pragma unroll
-    for (int j = 0; j < kNBW; ++j) bt[j][ks] = as_frag(f[((u * kNBW + j) * kSB + ks) * 64]);
+    for (int j = 0; j < kNBW; ++j)
+      bt[j][ks] = as_frag(
+          buffer_load16<kPolicyDefault>(r, frag_off(kBT0 + (u * kNBW + j) * kSB + ks, lane)));
   };
   // this wave's columns are exactly the H fragments (pb, kb = u)
   auto write_hs = [&](int buf) {
@@ -589,26 +615,28 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
   __syncthreads();  // x copies of the first tile
 
   for (int c = c0; c < c1; ++c) {
-    // H <- exp2(Lambda_end) H + sum_s exp2(Lambda_end - Lambda_s) dt_s x_s B_s^T
-    // in Horner form over the four 32-token blocks: the state is moved from
-    // the previous block end (tile start for the first) to the end e(q) of
-    // block q by exp2(lam[e(q)] - lam[e(q-1)]) <= 1, then block q adds B^T
-    // times the x copy scaled by exp2(lam[e(q)] - lam_s) dt_s (the copy the
-    // output waves use).  A operand B^T rows, B operand x; each B^T slice is
-    // reloaded for the next tile as soon as its MFMAs are issued.
+    // H <- exp2(Lambda_end) H + sum_s exp2(Lambda_end - Lambda_s) dt_s x_s B_s^T:
+    // the state is decayed to the tile end once, then the four 32-token
+    // blocks add B^T times the x copy that carries the tile-end factor
+    // exp2(lam_end - lam_s) dt_s (<= dt_s), with no rescaling between them.
+    // A operand B^T rows, B operand x; each B^T slice is reloaded for the
+    // next tile as soon as its MFMAs are issued.
     const float* d = dbuf + (c % 3) * kDec;
-    const bf16* XE = xbuf + (c & 1) * kXBuf + kXE;
-    float prev = 0.0f;
+    const bf16* XF = xbuf + (c & 1) * kXBuf + kXE;
+    {
+      const float rt = __builtin_amdgcn_exp2f(d[kQ - 1]);
+#pragma unroll
+      for (int j = 0; j < kNBW; ++j)
+#pragma unroll
+        for (int pb = 0; pb < kPB; ++pb) hacc[j][pb] *= rt;
+    }
 #pragma unroll
     for (int ks = 0; ks < kSB; ++ks) {
-      const float e = d[ks * 32 + 31];
-      const float rq = __builtin_amdgcn_exp2f(e - prev);
-      prev = e;
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
-        const Frag8<bf16> xf = lds_frag(XE + foff(ks * kPB + pb, lane));
+        const Frag8<bf16> xf = lds_frag(XF + foff(ks * kPB + pb, lane));
 #pragma unroll
-        for (int j = 0; j < kNBW; ++j) hacc[j][pb] = mma(bt[j][ks], xf, hacc[j][pb] * rq);
+        for (int j = 0; j < kNBW; ++j) hacc[j][pb] = mma(bt[j][ks], xf, hacc[j][pb]);
       }
       load_bt(min(c + 1, cl), ks);
     }
@@ -635,14 +663,14 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
 // ---------------------------------------------------------------------------
 // Stage waves.  Wave v turns tokens 32v..32v+31 of each tile, one tile ahead,
 // into the x fragments (v, pb) of both LDS x tiles (plain and times the
-// block-end factor): its raw rows go to its own staging rows (layout at soff)
+// tile-end factor): its raw rows go to its own staging rows (layout at soff)
 // and come back transposed, as operand fragments, from LDS transpose loads.
 // In a fused call the wave also stages the 4 rows before its tokens and
 // applies the causal conv (kernel 4) + SiLU to the transposed fragments, where
 // each lane holds 8 consecutive tokens of one channel: the same fp32
 // operation order and rounding as the conv kernel.
 // All four also form the decay cumsum two tiles ahead (a few DPP steps) and
-// waves 12, 13, 14 write its three arrays.
+// each writes one of its four arrays.
 template <bool OUT, bool FUSED>
 __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int seg, int c0,
                             int c1, int v) {
@@ -661,26 +689,31 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
   // rows r0..r3 (tokens 32v + 8i + lane/8) and, fused, the halo row
   struct XSet { uint4 r0, r1, r2, r3, h; };
   XSet xs;
+  // Rows at or past the sequence end lie outside the tile's buffer range and
+  // read as 0 (finite values that the scan multiplies by dt = 0 or never
+  // stores), so every iteration issues the same loads with no lane condition.
+  const uint32_t rowbytes = (uint32_t)(k.xs * (int64_t)sizeof(bf16));
   auto load_x = [&](int c) {
-    const int64_t r0 = rowb + (int64_t)c * kQ;
-    const int last = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ) - 1;
+    const int len = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ);
+    const uint64_t tile0 = reinterpret_cast<uint64_t>(k.x) +
+                           (uint64_t)(((rowb + (int64_t)c * kQ) * k.xs + (int64_t)h * kP) * sizeof(bf16));
+    const auto r = uniform_rsrc(tile0, (uint32_t)len * rowbytes);
     auto row = [&](int i) {
-      const int s = min(v * 32 + i * 8 + (lane >> 3), last);
-      return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                                           k.x + (r0 + s) * k.xs + (int64_t)h * kP + pc * 8)));
+      const int s = v * 32 + i * 8 + (lane >> 3);
+      return buffer_load16<kPolicyNT>(r, (uint32_t)s * rowbytes + pc * 16);
     };
     xs.r0 = row(0);
     xs.r1 = row(1);
     xs.r2 = row(2);
     xs.r3 = row(3);
     if (FUSED) {
-      // the 4 tokens before the wave's first (lanes 32-63 repeat lanes 0-31);
-      // before the sequence start: 0 (a conv state enters in fp32 below)
+      // the 4 tokens before the wave's first (lanes 32-63 repeat lanes 0-31),
+      // through a range that starts 4 rows before the tile; before the
+      // sequence start they read 0 (a conv state enters in fp32 below)
       const int s = v * 32 - 4 + ((lane >> 3) & 3);
-      xs.h = make_uint4(0u, 0u, 0u, 0u);
-      if (s >= 0 || c > 0)
-        xs.h = *reinterpret_cast<const uint4*>(k.x + (r0 + (s >= 0 ? min(s, last) : s)) * k.xs +
-                                               (int64_t)h * kP + pc * 8);
+      const auto rh = uniform_rsrc(tile0 - 4 * (uint64_t)rowbytes, (uint32_t)(len + 4) * rowbytes);
+      const uint32_t off = (s >= 0 || c > 0) ? (uint32_t)(s + 4) * rowbytes + pc * 16 : 0xfffffff0u;
+      xs.h = buffer_load16<kPolicyDefault>(rh, off);
     }
   };
   // conv weights and bias of the lane's channels h*64 + chan(pb, r)
@@ -747,7 +780,7 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
         }
       }
     }
-    const float* ef = d + 2 * kQ + v * 32 + (lane >> 4) * 8;
+    const float* ef = d + 3 * kQ + v * 32 + (lane >> 4) * 8;
     const f32x4 e0 = *reinterpret_cast<const f32x4*>(ef);
     const f32x4 e1 = *reinterpret_cast<const f32x4*>(ef + 4);
 #pragma unroll
@@ -760,13 +793,14 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
   // dt of tokens 2*lane, 2*lane + 1 of a tile (head-major copy), kept raw
   // until make_dec (a conversion here would make the wave wait for the load)
   auto load_dt = [&](int c) -> uint32_t {
-    return reinterpret_cast<const uint32_t*>(
-        k.dtT + (((int64_t)b * k.ntiles + c) * k.heads + h) * kQ)[lane];
+    const auto r = uniform_rsrc(k.dtT + (((int64_t)b * k.ntiles + c) * k.heads + h) * kQ,
+                                (uint32_t)(kQ * sizeof(bf16)));
+    return buffer_load4<kPolicyDefault>(r, (uint32_t)lane * 4);
   };
   uint32_t dtr_raw;
-  // Lambda (inclusive cumsum of dt*A, log2 units), dt and block-end factor
-  // exp2(Lambda_e - Lambda_s) dt_s of tile c (dt = 0 past the end of the
-  // sequence).
+  // Lambda (inclusive cumsum of dt*A, log2 units), dt, block-end factor
+  // exp2(Lambda_e - Lambda_s) dt_s and tile-end factor exp2(Lambda_end -
+  // Lambda_s) dt_s of tile c (dt = 0 past the end of the sequence).
   auto make_dec = [&](int c, int buf, uint32_t raw) {
     const int len = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ);
     float dtr[2];
@@ -797,6 +831,9 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
     } else if (v == 2) {
       *reinterpret_cast<float2*>(d + 2 * kQ + 2 * lane) =
           make_float2(__builtin_amdgcn_exp2f(lblk - l0) * dtr[0], __builtin_amdgcn_exp2f(lblk - l1) * dtr[1]);
+    } else {
+      *reinterpret_cast<float2*>(d + 3 * kQ + 2 * lane) =
+          make_float2(__builtin_amdgcn_exp2f(lend - l0) * dtr[0], __builtin_amdgcn_exp2f(lend - l1) * dtr[1]);
     }
     return lend;
   };
