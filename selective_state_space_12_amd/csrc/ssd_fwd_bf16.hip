@@ -239,18 +239,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void t
   // a fused call, 0 otherwise); the rows before the sequence start are 0 (a
   // given conv state enters the conv below in fp32).
   constexpr int kH = FUSED ? 3 : 0;
-  for (int v = tid; v < (kQ + kH) * (kN / 8); v += 512) {
-    const int sr = v / (kN / 8), col = (v % (kN / 8)) * 8;
-    const int s = sr - kH;
-    u32x4 bq = {0u, 0u, 0u, 0u}, cq = {0u, 0u, 0u, 0u};
-    if (s >= 0 || c > 0) {
-      const int64_t r = row0 + (s >= 0 ? min(s, last) : s);
-      // B and C rows are read once here (nontemporal: prep 12.0 vs 13.7 us)
-      bq = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Bp + r * bs + col));
-      cq = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cp + r * cs + col));
+  // Every row load of the tile is issued before any is written to LDS (a
+  // loop that stored each pair before loading the next waited for one HBM
+  // round trip per iteration).  Through buffer ranges that start kH rows
+  // before the tile: rows at or past the sequence end read as 0 (finite
+  // values that the scan multiplies by dt = 0 or never stores), and so do
+  // the rows before the sequence start (a given conv state enters the conv
+  // below in fp32).  B and C rows are read once here: nontemporal.
+  {
+    constexpr int kRowChunks = (kQ + kH) * (kN / 8);
+    constexpr int kIt = (kRowChunks + 511) / 512;
+    const int len = last + 1;
+    const int64_t first = row0 - kH;  // row of staged row 0
+    const uint64_t bb = reinterpret_cast<uint64_t>(Bp) + (uint64_t)(first * bs * (int64_t)sizeof(bf16));
+    const uint64_t cb = reinterpret_cast<uint64_t>(Cp) + (uint64_t)(first * cs * (int64_t)sizeof(bf16));
+    const uint32_t bstep = (uint32_t)(bs * sizeof(bf16)), cstep = (uint32_t)(cs * sizeof(bf16));
+    const auto rb = uniform_rsrc(bb, (uint32_t)(len + kH) * bstep);
+    const auto rc = uniform_rsrc(cb, (uint32_t)(len + kH) * cstep);
+    uint4 bq[kIt], cq[kIt];
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int v = tid + i * 512;
+      const int sr = min(v, kRowChunks - 1) / (kN / 8), col = (v % (kN / 8)) * 8;
+      // staged row sr; before the sequence start only in a fused call's first tile
+      const bool before = c == 0 && sr < kH;
+      bq[i] = buffer_load16<kPolicyNT>(rb, before ? 0xfffffff0u : (uint32_t)sr * bstep + col * 2);
+      cq[i] = buffer_load16<kPolicyNT>(rc, before ? 0xfffffff0u : (uint32_t)sr * cstep + col * 2);
     }
-    *reinterpret_cast<u32x4*>(&Bs[sr][col]) = bq;
-    *reinterpret_cast<u32x4*>(&Cs[sr][col]) = cq;
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int v = tid + i * 512;
+      if (v < kRowChunks) {
+        const int sr = v / (kN / 8), col = (v % (kN / 8)) * 8;
+        *reinterpret_cast<uint4*>(&Bs[sr][col]) = bq[i];
+        *reinterpret_cast<uint4*>(&Cs[sr][col]) = cq[i];
+      }
+    }
   }
   __syncthreads();
   if (FUSED) {
