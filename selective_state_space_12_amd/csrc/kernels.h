@@ -171,6 +171,14 @@ size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_
 // that a split adds.
 void fwd_plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int* ntiles, int* nseg,
                    int* seg_tiles, int64_t units = 0);
+// The full plan: main segments of seg_tiles tiles; for a split call, each
+// segment but the last is cut into ppseg pieces of piece_tiles tiles (the
+// last piece may be shorter, none empty) for the state-only pass.
+struct Bf16Plan {
+  int ntiles = 0, nseg = 1, seg_tiles = 1, ppseg = 1, piece_tiles = 1;
+  int nslot() const { return nseg > 1 ? (nseg - 1) * ppseg + 1 : 1; }
+};
+Bf16Plan plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int64_t units = 0);
 hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* workspace, hipStream_t s);
 // The same with the conv and dt transform fused in: a.x, a.B, a.C are the raw
 // conv input's x, B and C columns and a.dt the raw dt.  The conv state, if

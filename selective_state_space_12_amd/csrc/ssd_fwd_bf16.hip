@@ -100,6 +100,15 @@ constexpr size_t kDec = 4 * kQ;
 constexpr int kYRows = 16;
 constexpr size_t kYOff = (size_t)(2 * kXBuf + 2 * kHF + kStg) * sizeof(bf16) + 3 * kDec * sizeof(float);
 constexpr size_t kLds = kYOff + (size_t)8 * kYRows * kP * sizeof(bf16);
+// The state-only pass (segment end states, no outputs) keeps only the scaled
+// x copy and no H copies or output rows: a compact layout, so that several
+// of its 512-thread workgroups share a CU.
+template <bool OUT> constexpr int kXBufL = OUT ? kXBuf : kXE;   // elements per x buffer
+template <bool OUT> constexpr int kXFOff = OUT ? kXE : 0;       // scaled copy within a buffer
+template <bool OUT> constexpr int kStgOff = 2 * kXBufL<OUT> + (OUT ? 2 * kHF : 0);  // elements
+template <bool OUT> constexpr size_t kDecOff = (size_t)(kStgOff<OUT> + kStg) * sizeof(bf16);  // bytes
+static_assert(kDecOff<true> + 3 * kDec * sizeof(float) == kYOff, "main layout");
+constexpr size_t kLdsSeg = kDecOff<false> + 3 * kDec * sizeof(float);
 
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -409,6 +418,10 @@ struct BK {
   int64_t conv_dim;
   int64_t seqlen;
   int n_heads, heads, nseg, seg_chunks, ntiles;
+  // split calls: each main segment but the last is cut into ppseg pieces of
+  // piece_tiles tiles for the state-only pass; state slot i of a unit holds
+  // the state entering piece i (nslot = (nseg - 1) * ppseg + 1 per unit)
+  int ppseg, piece_tiles, nslot;
   // mixed calls: the grid is (segments x active units) on x, units numbered
   // sequence-major (heads of one sequence adjacent)
   UnitMap um;
@@ -434,7 +447,7 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
   const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
   const bf16* xbuf = reinterpret_cast<const bf16*>(smem);
   const bf16* hbuf = xbuf + 2 * kXBuf;
-  const float* dbuf = reinterpret_cast<const float*>(hbuf + 2 * kHF + kStg);
+  const float* dbuf = reinterpret_cast<const float*>(smem + kDecOff<true>);
   bf16* ybuf = reinterpret_cast<bf16*>(smem + kYOff) + (threadIdx.x >> 6) * kYRows * kP;
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Dh = k.D ? k.D[h] : 0.0f;
@@ -590,15 +603,15 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
                             int c1, int u) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
   const bf16* xbuf = reinterpret_cast<const bf16*>(smem);
-  bf16* hbuf = reinterpret_cast<bf16*>(smem) + 2 * kXBuf;
-  const float* dbuf = reinterpret_cast<const float*>(hbuf + 2 * kHF + kStg);
+  bf16* hbuf = reinterpret_cast<bf16*>(smem) + 2 * kXBuf;  // (OUT only)
+  const float* dbuf = reinterpret_cast<const float*>(smem + kDecOff<OUT>);
 
   f32x4 hacc[kNBW][kPB];
   {
     const float* hin = nullptr;
     if (OUT) {
       if (k.nseg > 1)
-        hin = k.seg_state + (((int64_t)b * k.heads + h) * k.nseg + seg) * (kP * kN);
+        hin = k.seg_state + (((int64_t)b * k.heads + h) * k.nslot + seg * k.ppseg) * (kP * kN);
       else if (k.h0)
         hin = k.h0 + ((int64_t)b * k.n_heads + h) * (kP * kN);
     }
@@ -646,7 +659,7 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
     // A operand B^T rows, B operand x; each B^T slice is reloaded for the
     // next tile as soon as its MFMAs are issued.
     const float* d = dbuf + (c % 3) * kDec;
-    const bf16* XF = xbuf + (c & 1) * kXBuf + kXE;
+    const bf16* XF = xbuf + (c & 1) * kXBufL<OUT> + kXFOff<OUT>;
     {
       const float rt = __builtin_amdgcn_exp2f(d[kQ - 1]);
 #pragma unroll
@@ -672,7 +685,7 @@ __device__ void state_waves(const BK& k, unsigned char* smem, int b, int h, int 
   if (OUT) {
     if (k.hT && seg == k.nseg - 1) hout = k.hT + ((int64_t)b * k.n_heads + h) * (kP * kN);
   } else {
-    hout = k.seg_state + (((int64_t)b * k.heads + h) * k.nseg + seg) * (kP * kN);
+    hout = k.seg_state + (((int64_t)b * k.heads + h) * k.nslot + seg) * (kP * kN);  // seg: piece
   }
   if (hout) {
 #pragma unroll
@@ -700,8 +713,8 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
                             int c1, int v) {
   const int lane = threadIdx.x & 63;
   bf16* xbuf = reinterpret_cast<bf16*>(smem);
-  bf16* stg = xbuf + 2 * kXBuf + 2 * kHF + v * kStgRows * kP;  // this wave's staged rows
-  float* dbuf = reinterpret_cast<float*>(xbuf + 2 * kXBuf + 2 * kHF + kStg);
+  bf16* stg = xbuf + kStgOff<OUT> + v * kStgRows * kP;  // this wave's staged rows
+  float* dbuf = reinterpret_cast<float*>(smem + kDecOff<OUT>);
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Ah2 = k.A[h] * kLog2e;
 
@@ -756,7 +769,8 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
   // fragments and the ones scaled by exp2(lam[e] - lam_s) dt_s, e the end of
   // the token's 32-token block (lane (r, g) holds tokens 32v + g*8 + j).
   auto commit = [&](int c) {
-    bf16* XT = xbuf + (c & 1) * kXBuf;
+    bf16* XT = xbuf + (c & 1) * kXBufL<OUT>;  // (plain copy: OUT only)
+    bf16* XF = XT + kXFOff<OUT>;
     const float* d = dbuf + (c % 3) * kDec;
     *reinterpret_cast<uint4*>(stg + soff(4 + (lane >> 3), pc)) = xs.r0;
     *reinterpret_cast<uint4*>(stg + soff(12 + (lane >> 3), pc)) = xs.r1;
@@ -810,7 +824,7 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb) {
       if (OUT) *reinterpret_cast<uint4*>(XT + foff(v * kPB + pb, lane)) = __builtin_bit_cast(uint4, f[pb].v);
-      *reinterpret_cast<uint4*>(XT + kXE + foff(v * kPB + pb, lane)) =
+      *reinterpret_cast<uint4*>(XF + foff(v * kPB + pb, lane)) =
           __builtin_bit_cast(uint4, scale8(f[pb], e0, e1).v);
     }
   };
@@ -885,39 +899,43 @@ __device__ void stage_waves(const BK& k, unsigned char* smem, int b, int h, int 
     __syncthreads();
   }
   if (!OUT && v == 0 && lane == 0)
-    k.seg_decay[((int64_t)b * k.heads + h) * k.nseg + seg] = lam_seg;
+    k.seg_decay[((int64_t)b * k.heads + h) * k.nslot + seg] = lam_seg;  // seg: piece
 }
 
-template <bool OUT, bool FUSED>
-__global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(BK k) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  // XCD-aware unit mapping: consecutive workgroups go to different XCDs, so
-  // give each XCD a contiguous block of units numbered head fastest; the heads
-  // that walk the same tiles (same sequence and segment) then share one L2 for
-  // the fragments.
+// XCD-aware unit mapping: consecutive workgroups go to different XCDs, so
+// give each XCD a contiguous block of units numbered head fastest; the heads
+// that walk the same tiles (same sequence and segment) then share one L2 for
+// the fragments.  Grid (parts, heads, batch), or (parts * units) for mixed
+// calls; returns the part (segment or piece) index.
+__device__ __forceinline__ int unit_of_block(const BK& k, int* b, int* h) {
   const int gx = gridDim.x, gy = gridDim.y;
   const int total = gx * gy * gridDim.z;
   const int pid = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
   const int uid = total % kXcds == 0 ? (pid % kXcds) * (total / kXcds) + pid / kXcds : pid;
-  int h, seg, b;
   if (k.um.mixed) {
-    seg = uid / k.um.units;
-    unit_to_bh(k.um, uid % k.um.units, &b, &h);
-  } else {
-    h = uid % gy;
-    seg = (uid / gy) % gx;
-    b = uid / (gx * gy);
+    unit_to_bh(k.um, uid % k.um.units, b, h);
+    return uid / k.um.units;
   }
+  *h = uid % gy;
+  *b = uid / (gx * gy);
+  return (uid / gy) % gx;
+}
+
+template <bool FUSED>
+__global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(BK k) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int b, h;
+  const int seg = unit_of_block(k, &b, &h);
   const int c0 = seg * k.seg_chunks;
   const int c1 = min(c0 + k.seg_chunks, k.ntiles);
   if (c0 >= c1) return;  // whole workgroup
   // wave index as a scalar, so the role branch below is uniform per wave
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave >= 12) {
-    stage_waves<OUT, FUSED>(k, smem, b, h, seg, c0, c1, wave - 12);
+    stage_waves<true, FUSED>(k, smem, b, h, seg, c0, c1, wave - 12);
   } else if (wave >= 8) {
-    state_waves<OUT>(k, smem, b, h, seg, c0, c1, wave - 8);
-  } else if (OUT) {
+    state_waves<true>(k, smem, b, h, seg, c0, c1, wave - 8);
+  } else {
     const int tb = wave < 4 ? wave : kTB + 3 - wave;  // 0 1 2 3 7 6 5 4
     switch (tb >> 1) {
       case 0: output_wave<0>(k, smem, b, h, c0, c1, tb); break;
@@ -925,21 +943,40 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(BK k) {
       case 2: output_wave<2>(k, smem, b, h, c0, c1, tb); break;
       default: output_wave<3>(k, smem, b, h, c0, c1, tb); break;
     }
-  } else {
-    // no outputs in the prepass: keep the barrier count of the state waves
-    for (int i = 0; i < c1 - c0 + 2; ++i) __syncthreads();
   }
 }
 
-// Chains segment states: slot s receives the state entering segment s,
-//   H_in[0] = h0, H_in[s+1] = exp2(decay_s) H_in[s] + S_s,
-// where slot s held the local end state S_s written by the prepass.  One
-// thread per state element; the slot loads of eight segments are issued
-// together.
+// State-only pass of a split call: for each unit and each piece of the
+// segments before the last, the state at the piece end starting from zero
+// (slot = piece) and the piece's total log2 decay.  Eight waves (four stage
+// x, four update the state) in a compact LDS layout (56 KB); the pieces may
+// be finer than the segments so that these workgroups fill the GPU.
+template <bool FUSED>
+__global__ __launch_bounds__(512) void ssd_bf16_seg_kernel(BK k) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int b, h;
+  const int piece = unit_of_block(k, &b, &h);
+  const int seg = piece / k.ppseg;
+  const int c0 = seg * k.seg_chunks + (piece % k.ppseg) * k.piece_tiles;
+  const int c1 = min(min(c0 + k.piece_tiles, (seg + 1) * k.seg_chunks), k.ntiles);
+  if (c0 >= c1) return;  // whole workgroup (the planner makes no empty piece)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave >= 4)
+    state_waves<false>(k, smem, b, h, piece, c0, c1, wave - 4);
+  else
+    stage_waves<false, FUSED>(k, smem, b, h, piece, c0, c1, wave);
+}
+
+// Chains the pieces' states: slot i receives the state entering piece i,
+//   H_in[0] = h0, H_in[i+1] = exp2(decay_i) H_in[i] + S_i,
+// where slot i held the piece's own end state S_i from the state-only pass.
+// One thread per state element; the loads of eight slots are issued together
+// before their part of the chain.
+constexpr int kCombineRegs = 8;
 __global__ __launch_bounds__(256) void seg_combine_bf16_kernel(float* __restrict__ seg_state,
                                                                const float* __restrict__ seg_decay,
                                                                const float* __restrict__ h0,
-                                                               int n_heads, int heads, int nseg,
+                                                               int n_heads, int heads, int nslot,
                                                                UnitMap um) {
   constexpr int PN = kP * kN;
   const int e = blockIdx.x * 256 + threadIdx.x;
@@ -947,25 +984,24 @@ __global__ __launch_bounds__(256) void seg_combine_bf16_kernel(float* __restrict
   if (um.mixed) unit_to_bh(um, blockIdx.y, &b, &h);
   const int64_t unit = (int64_t)b * heads + h;
   float H = h0 ? h0[((int64_t)b * n_heads + h) * PN + e] : 0.0f;
-  float* base = seg_state + unit * nseg * PN + e;
-  const float* dec = seg_decay + unit * nseg;
-  constexpr int kU = 8;
-  for (int s0 = 0; s0 < nseg; s0 += kU) {
-    float S[kU];
+  float* base = seg_state + unit * nslot * PN + e;
+  const float* dec = seg_decay + unit * nslot;
+  const int npre = nslot - 1;
+  for (int s0 = 0; s0 < npre; s0 += kCombineRegs) {
+    float S[kCombineRegs];
 #pragma unroll
-    for (int i = 0; i < kU; ++i) {
-      const int sg = s0 + i;
-      S[i] = sg < nseg - 1 ? base[(int64_t)sg * PN] : 0.0f;
-    }
+    for (int i = 0; i < kCombineRegs; ++i)  // (slot index clamped: every load valid)
+      S[i] = base[(int64_t)min(s0 + i, npre - 1) * PN];
 #pragma unroll
-    for (int i = 0; i < kU; ++i) {
+    for (int i = 0; i < kCombineRegs; ++i) {
       const int sg = s0 + i;
-      if (sg < nseg) {
+      if (sg < npre) {
         base[(int64_t)sg * PN] = H;
-        if (sg < nseg - 1) H = exp2f(dec[sg]) * H + S[i];
+        H = exp2f(dec[sg]) * H + S[i];
       }
     }
   }
+  base[(int64_t)npre * PN] = H;
 }
 
 size_t frag_region_bytes(int64_t batch, int64_t seqlen) {
@@ -985,40 +1021,66 @@ bool bf16_path(int64_t d_head, int64_t d_state, int64_t chunk, int dtype) {
   return dtype == MM_BF16 && d_head == kP && d_state == kN && (chunk == 128 || chunk == 256);
 }
 
-void fwd_plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int* ntiles, int* nseg,
-                   int* seg_tiles, int64_t units_in) {
-  // Cost in units of one tile step of a workgroup (about 2.7 us on MI355X):
-  // each round of up to kCus workgroups costs its walk plus ~2.5 tiles of
-  // start-up (first loads from HBM, state in, pipeline fill and drain); the
-  // prepass walks at about half the main kernel's rate per tile; the combine
-  // and the two extra launches add ~3 tiles.
-  constexpr int64_t kCus = 256;
+Bf16Plan plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int64_t units_in) {
+  // Cost in units of one tile step of a main workgroup (about 2.5 us on
+  // MI355X).  Each round of up to kCus main workgroups costs its walk plus
+  // ~2.5 tiles of start-up (first loads from HBM, state in, pipeline fill and
+  // drain).  A split adds the state-only pass, whose workgroups walk a piece
+  // at ~0.6 of a main tile step per tile plus ~2.5 of start-up (one per CU:
+  // two sharing a CU measured slower per CU than one), and the combine and
+  // its launch (~2, plus ~0.3 per piece: each piece's state is written and
+  // read back once more).  Pieces finer than the segments pay where the
+  // segments alone leave CUs idle in the state-only pass.
+  constexpr int64_t kCus = 256, kSegPerCu = 1, kMaxPieces = 8;
+  Bf16Plan pl;
   const int64_t n = (seqlen + kQ - 1) / kQ;
   const int64_t units = units_in > 0 ? units_in : batch * heads;
-  int64_t best_per = n > 0 ? n : 1, best_seg = 1;
+  pl.ntiles = (int)n;
+  pl.nseg = 1;
+  pl.seg_tiles = (int)(n > 0 ? n : 1);
+  pl.ppseg = 1;
+  pl.piece_tiles = pl.seg_tiles;
   double best = 1e300;
   for (int64_t want = 1; want <= n; ++want) {
     const int64_t per = (n + want - 1) / want;
     const int64_t seg = (n + per - 1) / per;
     if (seg != want) continue;  // the same cut as a smaller count
     const int64_t r_main = (units * seg + kCus - 1) / kCus;
-    double cost = (double)r_main * ((double)per + 2.5);
-    if (seg > 1) {
-      const int64_t r_pre = (units * (seg - 1) + kCus - 1) / kCus;
-      cost += (double)r_pre * (0.5 * (double)per + 2.5) + 3.0;
+    const double main_cost = (double)r_main * ((double)per + 2.5);
+    if (seg == 1) {
+      if (main_cost < best) {
+        best = main_cost;
+        pl.nseg = 1; pl.seg_tiles = (int)per; pl.ppseg = 1; pl.piece_tiles = (int)per;
+      }
+      continue;
     }
-    if (cost < best) { best = cost; best_per = per; best_seg = seg; }
+    for (int64_t pp = 1; pp <= kMaxPieces && pp <= per; ++pp) {
+      const int64_t pt = (per + pp - 1) / pp;
+      if ((pp - 1) * pt >= per) continue;  // an empty piece
+      const int64_t npre = (seg - 1) * pp;
+      const int64_t r_pre = (units * npre + kCus * kSegPerCu - 1) / (kCus * kSegPerCu);
+      const double cost = main_cost + (double)r_pre * (0.6 * (double)pt + 2.5) + 2.0 + 0.3 * (double)npre;
+      if (cost < best) {
+        best = cost;
+        pl.nseg = (int)seg; pl.seg_tiles = (int)per; pl.ppseg = (int)pp; pl.piece_tiles = (int)pt;
+      }
+    }
   }
-  *ntiles = (int)n;
-  *seg_tiles = (int)best_per;
-  *nseg = (int)best_seg;
+  return pl;
+}
+
+void fwd_plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int* ntiles, int* nseg,
+                   int* seg_tiles, int64_t units_in) {
+  const Bf16Plan pl = plan_bf16(batch, seqlen, heads, units_in);
+  *ntiles = pl.ntiles;
+  *seg_tiles = pl.seg_tiles;
+  *nseg = pl.nseg;
 }
 
 size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t units) {
-  int nt, nseg, per;
-  fwd_plan_bf16(batch, seqlen, heads, &nt, &nseg, &per, units);
+  const Bf16Plan pl = plan_bf16(batch, seqlen, heads, units);
   size_t bytes = frag_region_bytes(batch, seqlen) + dt_region_bytes(batch, seqlen, heads);
-  if (nseg > 1) bytes += (size_t)(batch * heads * nseg) * (size_t)(kP * kN + 1) * sizeof(float);
+  if (pl.nseg > 1) bytes += (size_t)(batch * heads * pl.nslot()) * (size_t)(kP * kN + 1) * sizeof(float);
   return bytes;
 }
 
@@ -1034,10 +1096,10 @@ hipError_t set_lds_attributes() {
   const std::pair<const void*, size_t> attrs[] = {
       {reinterpret_cast<const void*>(tile_prep_kernel<false>), kPrepLds},
       {reinterpret_cast<const void*>(tile_prep_kernel<true>), kPrepLds},
-      {reinterpret_cast<const void*>(ssd_bf16_kernel<false, false>), kLds},
-      {reinterpret_cast<const void*>(ssd_bf16_kernel<true, false>), kLds},
-      {reinterpret_cast<const void*>(ssd_bf16_kernel<false, true>), kLds},
-      {reinterpret_cast<const void*>(ssd_bf16_kernel<true, true>), kLds}};
+      {reinterpret_cast<const void*>(ssd_bf16_kernel<false>), kLds},
+      {reinterpret_cast<const void*>(ssd_bf16_kernel<true>), kLds},
+      {reinterpret_cast<const void*>(ssd_bf16_seg_kernel<false>), kLdsSeg},
+      {reinterpret_cast<const void*>(ssd_bf16_seg_kernel<true>), kLdsSeg}};
   for (const auto& fa : attrs) {
     e = hipFuncSetAttribute(fa.first, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fa.second);
     if (e != hipSuccess) return e;
@@ -1059,8 +1121,13 @@ hipError_t launch_bf16(const FwdArgs& a, const FuseArgs& fu, void* ws, hipStream
   k.cw = fu.w; k.cbias = fu.bias; k.cstate = fu.state; k.conv_dim = fu.conv_dim;
   k.seqlen = a.seqlen; k.n_heads = a.n_heads; k.heads = a.heads;
   k.um = make_unit_map(a);
-  fwd_plan_bf16(a.batch, a.seqlen, a.heads, &k.ntiles, &k.nseg, &k.seg_chunks,
-                k.um.mixed ? k.um.units : 0);
+  const Bf16Plan pl = plan_bf16(a.batch, a.seqlen, a.heads, k.um.mixed ? k.um.units : 0);
+  k.ntiles = pl.ntiles;
+  k.nseg = pl.nseg;
+  k.seg_chunks = pl.seg_tiles;
+  k.ppseg = pl.ppseg;
+  k.piece_tiles = pl.piece_tiles;
+  k.nslot = pl.nslot();
   if (k.um.mixed && k.um.units == 0) return hipSuccess;  // no active head anywhere
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   uint4* frags = reinterpret_cast<uint4*>(wsb);
@@ -1072,7 +1139,7 @@ hipError_t launch_bf16(const FwdArgs& a, const FuseArgs& fu, void* ws, hipStream
   if (k.nseg > 1) {
     k.seg_state = reinterpret_cast<float*>(wsb + frag_region_bytes(a.batch, a.seqlen) +
                                            dt_region_bytes(a.batch, a.seqlen, a.heads));
-    k.seg_decay = k.seg_state + (size_t)a.batch * a.heads * k.nseg * kP * kN;
+    k.seg_decay = k.seg_state + (size_t)a.batch * a.heads * k.nslot * kP * kN;
   }
   hipError_t e = set_lds_attributes();
   if (e != hipSuccess) return e;
@@ -1081,19 +1148,20 @@ hipError_t launch_bf16(const FwdArgs& a, const FuseArgs& fu, void* ws, hipStream
                      frags, dtT, a.seqlen, k.ntiles, a.heads, fu);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (k.nseg > 1) {
-    auto pre = ssd_bf16_kernel<false, FUSED>;
-    const dim3 gpre = k.um.mixed ? dim3((unsigned)((k.nseg - 1) * k.um.units))
-                                 : dim3(k.nseg - 1, a.heads, (unsigned)a.batch);
-    hipLaunchKernelGGL(pre, gpre, dim3(kThreads), kLds, s, k);
+    const int npre = k.nslot - 1;
+    auto pre = ssd_bf16_seg_kernel<FUSED>;
+    const dim3 gpre = k.um.mixed ? dim3((unsigned)(npre * k.um.units))
+                                 : dim3(npre, a.heads, (unsigned)a.batch);
+    hipLaunchKernelGGL(pre, gpre, dim3(512), kLdsSeg, s, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     static_assert((kP * kN) % 256 == 0, "state elements split over 256-thread blocks");
     const dim3 gcomb = k.um.mixed ? dim3(kP * kN / 256, (unsigned)k.um.units)
                                   : dim3(kP * kN / 256, a.heads, (unsigned)a.batch);
     hipLaunchKernelGGL(seg_combine_bf16_kernel, gcomb, dim3(256), 0, s, k.seg_state, k.seg_decay,
-                       a.h0, a.n_heads, a.heads, k.nseg, k.um);
+                       a.h0, a.n_heads, a.heads, k.nslot, k.um);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  auto main_k = ssd_bf16_kernel<true, FUSED>;
+  auto main_k = ssd_bf16_kernel<FUSED>;
   const dim3 gmain = k.um.mixed ? dim3((unsigned)(k.nseg * k.um.units))
                                 : dim3(k.nseg, a.heads, (unsigned)a.batch);
   hipLaunchKernelGGL(main_k, gmain, dim3(kThreads), kLds, s, k);
