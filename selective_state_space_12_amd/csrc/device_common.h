@@ -99,7 +99,6 @@ constexpr int kPolicyNT = 2;
 
 template <int POLICY>
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POLICY));
 }
 template <int POLICY>

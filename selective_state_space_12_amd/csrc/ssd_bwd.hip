@@ -57,8 +57,10 @@ namespace mmssd {
 namespace {
 
 constexpr int kBQ = 64;  // tokens per backward chunk
-constexpr int kBWaves = 8;
+constexpr int kBWaves = 8;  // state walks
 constexpr int kBThreads = kBWaves * 64;
+constexpr int kCWaves = 16;  // chunk walk
+constexpr int kCThreads = kCWaves * 64;
 constexpr int kXcds = 8;
 
 struct BwdK {
@@ -100,6 +102,23 @@ struct BwdK {
 };
 
 template <typename T> constexpr int bpad() { return 16 / (int)sizeof(T); }
+
+// State tiles (16 x 16 of P x N) come in pairs 2j, 2j+1 that together cover
+// d_head rows 32j .. 32j+31, interleaved so that the accumulators of a pair
+// are an MFMA operand fragment with K = d_head: row m of tile T is d_head row
+//   prow(T, m) = 32 (T/2) + 4 (T%2) + 8 (m/4) + m%4,
+// so lane (r, g) holds rows 32j + 8g + 0..7 of column r across the pair
+// (slots 0-3 from tile 2j, 4-7 from tile 2j+1).  The stored chunk states use
+// that fragment order: fragment (kp, nb) of a P x N state is 64 lanes x 8
+// consecutive elements at ((kp * N/16 + nb) * 64 + lane) * 8.
+__device__ __forceinline__ int prow(int T, int m) {
+  return (T >> 1) * 32 + (T & 1) * 4 + (m >> 2) * 8 + (m & 3);
+}
+
+template <int N>
+__device__ __forceinline__ int64_t state_frag(int kp, int nb, int lane) {
+  return ((int64_t)(kp * (N / 16) + nb) * 64 + lane) * 8;
+}
 
 // (sequence, head) of this workgroup: consecutive units on one XCD so that
 // the heads of a sequence share its B and C rows in that XCD's L2.
@@ -190,6 +209,24 @@ __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d)
   }
 }
 
+// Eight consecutive storage elements from two accumulator quads (16 B of
+// bf16, 32 of fp32).
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const f32x4& a, const f32x4& b) {
+  if constexpr (sizeof(T) == 2) {
+    bf16 v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = from_f32<bf16>(a[i]);
+      v[i + 4] = from_f32<bf16>(b[i]);
+    }
+    *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(v);
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(a[0], a[1], a[2], a[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(b[0], b[1], b[2], b[3]);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void load4(const T* p, float (&o)[4]) {
   if constexpr (sizeof(T) == 2) {
@@ -239,9 +276,9 @@ __device__ __forceinline__ void state_walk(const BwdK& k, int pid, int total) {
   using L = StateLds<T, P, N>;
   constexpr int Q = kBQ, TQ = L::TQ;
   constexpr int TP = P / 16, TN = N / 16, NTILE = TP * TN;
-  constexpr int TPW = NTILE >= kBWaves ? NTILE / kBWaves : 1;
-  static_assert(NTILE < kBWaves || NTILE % kBWaves == 0, "state tiles must split evenly");
-  static_assert(TP % TPW == 0, "a wave's state tiles share one column block");
+  constexpr int TPW = NTILE >= 2 * kBWaves ? NTILE / kBWaves : 2;
+  static_assert(NTILE < 2 * kBWaves || NTILE % kBWaves == 0, "state tiles must split evenly");
+  static_assert(TP % TPW == 0 && TPW % 2 == 0, "a wave's state tiles are whole pairs of one column block");
   constexpr int VB = 16 / (int)sizeof(T);
   extern __shared__ __align__(16) unsigned char smem[];
   T* XT = reinterpret_cast<T*>(smem);
@@ -253,7 +290,7 @@ __device__ __forceinline__ void state_walk(const BwdK& k, int pid, int total) {
   unit_of_idx(pid, total, k.heads, PRE ? k.nseg - 1 : k.nseg, &b, &h, &seg);
   const int64_t unit = (int64_t)b * k.heads + h;
   const int c0 = seg * k.seg_chunks, c1 = min(c0 + k.seg_chunks, k.nchunks);
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int r16 = lane % 16, g = lane / 16;
   const T* __restrict__ Xp = static_cast<const T*>(k.x);
   const T* __restrict__ DTp = static_cast<const T*>(k.dt);
@@ -262,8 +299,9 @@ __device__ __forceinline__ void state_walk(const BwdK& k, int pid, int total) {
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Ah2 = k.A[h] * kLog2e;
 
+  // this wave's state tiles (pt0 + t, nt), rows in the paired order of prow()
   const int tile0 = wave * TPW;
-  const bool owns = NTILE >= kBWaves || tile0 < NTILE;  // every wave when tiles >= waves
+  const bool owns = tile0 < NTILE;
   const int nt = tile0 / TP, pt0 = tile0 % TP;
   f32x4 hacc[TPW];
   const float* hin = PRE ? nullptr
@@ -275,19 +313,17 @@ __device__ __forceinline__ void state_walk(const BwdK& k, int pid, int total) {
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      hacc[t][i] = (hin && owns) ? hin[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] : 0.0f;
+      hacc[t][i] = (hin && owns) ? hin[prow(pt0 + t, g * 4 + i) * N + nt * 16 + r16] : 0.0f;
   // the start state's loads complete here, before any chunk is loaded ahead
 #pragma unroll
   for (int t = 0; t < TPW; ++t) hacc[t] = opaque(hacc[t]);
 
+  // the state in fragment order: one 8-element run per lane and tile pair
   auto store_state = [&](int c) {
     if (PRE || !owns) return;
     T* dst = Hst + (int64_t)c * (P * N);
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dst[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] = from_f32<T>(hacc[t][i]);
+    for (int t = 0; t < TPW; t += 2) store8(dst + state_frag<N>((pt0 + t) / 2, nt, lane), hacc[t], hacc[t + 1]);
   };
 
   // The x, B rows and dt of the chunk two ahead are loaded into registers
@@ -375,7 +411,7 @@ __device__ __forceinline__ void state_walk(const BwdK& k, int pid, int total) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
           Frag8<T> xr, xf;
-          frag_load8(xr, XT + ((pt0 + t) * 16 + r16) * TQ + s0);
+          frag_load8(xr, XT + prow(pt0 + t, r16) * TQ + s0);
 #pragma unroll
           for (int j = 0; j < 8; ++j) frag_set(xf, j, to_f32(xr.v[j]) * (j < 4 ? w0[j] : w1[j - 4]));
           hacc[t] = mma(xf, bf, hacc[t]);
@@ -402,7 +438,7 @@ __device__ __forceinline__ void state_walk(const BwdK& k, int pid, int total) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] = hacc[t][i];
+        for (int i = 0; i < 4; ++i) dst[prow(pt0 + t, g * 4 + i) * N + nt * 16 + r16] = hacc[t][i];
     if (tid == 0) k.seg_hd[unit * k.nseg + seg] = lam_seg;
   } else if (c1 == k.nchunks) {
     store_state(k.nchunks);
@@ -438,7 +474,7 @@ __device__ __forceinline__ void gprep_walk(const BwdK& k, int pid, int total) {
   const int seg = sg + 1;
   const int64_t unit = (int64_t)b * k.heads + h;
   const int c0 = seg * k.seg_chunks, c1 = min(c0 + k.seg_chunks, k.nchunks);
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int r16 = lane % 16, g = lane / 16;
   const T* __restrict__ DYp = static_cast<const T*>(k.dy);
   const T* __restrict__ DTp = static_cast<const T*>(k.dt);
@@ -590,69 +626,156 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdK k) {
   }
 }
 
+// LDS of the chunk kernel: the chunk's x, dy, B, C rows token-major, Gc
+// n-major, the start state Hp as stored (fragment order) and the masked Q x Q
+// matrices M, K (rows s) and Kd (rows t); products that need another
+// orientation read columns with transpose loads (frag_cols), so no
+// transposed copy is kept (119 KB at d_head 64, d_state 128 in bf16).
 template <typename T, int P, int N>
 struct ChunkLds {
-  static constexpr int NP = P + bpad<T>();   // token-major x and dy rows
-  static constexpr int NN = N + bpad<T>();   // token-major B and C rows, Gc rows (p-major)
-  static constexpr int TQ = kBQ + bpad<T>(); // transposed dy, B, C rows
-  static constexpr int TP2 = P + bpad<T>();  // Gc^T and Hp^T rows (n-major)
-  static constexpr size_t elems = (size_t)2 * kBQ * NP + (size_t)P * TQ + (size_t)2 * kBQ * NN +
-                                  (size_t)2 * N * TQ + (size_t)P * NN + (size_t)2 * N * TP2;
-  static constexpr int kFloats = 15 * kBQ + 2 * kBWaves;
+  static constexpr int NP = P + bpad<T>();    // token-major x and dy rows
+  static constexpr int NN = N + bpad<T>();    // token-major B and C rows
+  static constexpr int TP2 = P + bpad<T>();   // Gc^T rows (n-major)
+  static constexpr int QP = kBQ + bpad<T>();  // M, K, Kd rows
+  static constexpr size_t elems = (size_t)2 * kBQ * NP + (size_t)2 * kBQ * NN + (size_t)N * TP2 +
+                                  (size_t)P * N + (size_t)3 * kBQ * QP;
+  static constexpr int kFloats = 4 * kBQ + 2 * 4 * kBQ + 3 * 4 * kBQ + 2 * kCWaves;
   static constexpr size_t bytes = elems * sizeof(T) + kFloats * sizeof(float);
 };
 
+// Operand fragment from columns of a row-major LDS tile M (row pitch ld):
+// lane (r, g) gets M[ra + j][c(r)] in slots j = 0..3 and M[rb + j][c(r)] in
+// slots 4..7, where ra, rb are the row bases of its 16-lane group and
+// c(r) = c0 + cs (r/4) + r%4 (cs = 4: sixteen consecutive columns; cs = 8:
+// the paired d_head rows of prow()).  16-bit elements: two LDS transpose
+// loads, in which lane q of a group addresses the four elements at row
+// base + q/4, columns c0 + cs (q%4) .. +3, and receives in element k element
+// q%4 of what lane 4k + q/4 addressed (tiles of whole K=32 slices only).
+// 32-bit elements: eight element reads, zeros where live is false.
 template <typename T>
-__device__ __forceinline__ void grad_store(T* p, float v, int accumulate) {
-  *p = from_f32<T>(accumulate ? to_f32(*p) + v : v);
+__device__ __forceinline__ void frag_cols(Frag8<T>& f, const T* M, int ld, int ra, int rb, int c0,
+                                          int cs, int lane, bool live = true) {
+  const int q = lane & 15;
+  if constexpr (sizeof(T) == 2) {
+    typedef short short4v __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) short4v lds_short4;
+    const int col = c0 + (q & 3) * cs;
+    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_short4*)(const_cast<T*>(M) + (ra + (q >> 2)) * ld + col));
+    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_short4*)(const_cast<T*>(M) + (rb + (q >> 2)) * ld + col));
+    f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else {
+    const int col = c0 + (q >> 2) * cs + (q & 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.v[j] = live ? M[(ra + j) * ld + col] : 0.0f;
+      f.v[j + 4] = live ? M[(rb + j) * ld + col] : 0.0f;
+    }
+  }
 }
 
-template <typename T, int P, int N>
-__global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
+// Sum over the 64 lanes, in every lane: row sums by DPP, then the four rows'
+// sums read from lanes 0, 16, 32, 48.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  auto rl = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
+  return (rl(0) + rl(16)) + (rl(32) + rl(48));
+}
+
+// v of lane ^ m (an LDS permute whose address is formed from the caller's
+// lane index, so that it is formed where used)
+__device__ __forceinline__ float xor_lane(float v, int lane, int m) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __builtin_bit_cast(int, v)));
+}
+
+// One storage element through a buffer resource: loads outside the range
+// read 0, stores there are dropped.
+template <typename T>
+__device__ __forceinline__ float buffer_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(T) == 2) {
+    const unsigned short u = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    return __builtin_bit_cast(float, (uint32_t)u << 16);
+  } else {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+  }
+}
+template <typename T>
+__device__ __forceinline__ void buffer_store_elem(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  if constexpr (sizeof(T) == 2) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f32<bf16>(v)), r,
+                                          (int)off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+  }
+}
+
+// ACC: add into the caller's dx and ddt (else overwrite them).
+//
+// One workgroup of 16 waves walks the chunks of one (sequence, head) (or
+// segment) backwards with dL/dH in accumulators.  Per chunk, after staging:
+//  phase 1: the Q x Q blocks on and below the diagonal, once each (waves
+//    0-9, one 16 x 16 block each): C_t . B_s and dy_t . x_s, the masked decay,
+//    and from them M = G dec, K = Q dec (both [s][t]) and Kd = K dt_s ([t][s])
+//    in LDS plus the row and column sums of W; every wave: its dL/dH tile
+//    pair (decay, + dy^T exp(Lambda) C, then <dGp, Hp> for the chunk before),
+//    its u tile's end-state term exp(Lambda_e - Lambda_s) B_s Gc^T, its dB
+//    tiles' exp(..) x_s Gc and its dC tiles' exp(Lambda_t) dy_t Hp;
+//  phase 2: the causal products u += M dy, dB += K C, dC += Kd B into the
+//    same accumulators, then dx, the dB and dC atomics;
+//  tail (wave 0): dLambda from the partial sums, its suffix sum, ddt, dA.
+// Every partial sum is written by one wave and summed in a fixed order, so
+// the results do not depend on wave timing.
+template <typename T, int P, int N, bool ACC>
+__global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
   using L = ChunkLds<T, P, N>;
-  constexpr int Q = kBQ, NP = L::NP, NN = L::NN, TQ = L::TQ, TP2 = L::TP2;
-  constexpr int TP = P / 16, TN = N / 16, NTILE = TP * TN;
-  constexpr int TPW = NTILE >= kBWaves ? NTILE / kBWaves : 1;
+  constexpr int Q = kBQ, NP = L::NP, NN = L::NN, TP2 = L::TP2, QP = L::QP;
+  constexpr int TP = P / 16, TN = N / 16;
   constexpr int NKB = (N + 31) / 32;  // K=32 slices over d_state
   constexpr int PKB = P / 32;         // K=32 slices over d_head
   constexpr int VB = 16 / (int)sizeof(T);
   constexpr int NBLK = Q / 16;        // 16-token blocks per chunk
-  static_assert(NBLK == 4, "four s-blocks and four t-blocks, one per wave");
-  static_assert(P % 32 == 0, "d_head is a whole number of K=32 slices");
-  constexpr int NXV = (Q * (P / VB) + kBThreads - 1) / kBThreads;  // x, dy vectors per thread
-  constexpr int NBV = (Q * (N / VB) + kBThreads - 1) / kBThreads;  // B, C vectors per thread
-  constexpr int NHV = (P * (N / VB) + kBThreads - 1) / kBThreads;  // Hp vectors per thread
-  constexpr int TPH = TP / 2;                  // d_head tiles per column half
-  constexpr int TNH = TN >= 2 ? TN / 2 : 1;    // d_state tiles per column half
-  static_assert(TP % 2 == 0 && (TN == 1 || TN % 2 == 0), "columns split in two halves");
+  static_assert(NBLK == 4 && Q % 32 == 0, "four 16-token blocks per chunk");
+  static_assert(P % 32 == 0 && TP % 2 == 0, "d_head is a whole number of K=32 slices");
+  static_assert(sizeof(T) == 4 || N % 32 == 0, "16-bit tiles are read in whole K=32 slices");
+  constexpr int NU = NBLK * TP, UPW = (NU + kCWaves - 1) / kCWaves;  // u tiles, per wave
+  constexpr int ND = NBLK * TN, DPW = (ND + kCWaves - 1) / kCWaves;  // dB (and dC) tiles, per wave
+  static_assert(UPW == 1 && TN % DPW == 0, "one u tile per wave; a wave's dB tiles share a block");
+  constexpr int NQ = TN / DPW;       // dB / dC partials per 16-token block
+  constexpr int NGP = (TP / 2) * TN;  // dL/dH tile pairs
+  static_assert(NGP <= kCWaves, "at most one dL/dH tile pair per wave");
+  constexpr int NQQ = NBLK * (NBLK + 1) / 2;  // Q x Q blocks on and below the diagonal
+  static_assert(NQQ <= kCWaves, "one Q x Q block per wave");
+  constexpr int NXY = (2 * Q * (P / VB) + kCThreads - 1) / kCThreads;  // x, dy vectors per thread
+  constexpr int NBC = (2 * Q * (N / VB) + kCThreads - 1) / kCThreads;  // B, C vectors per thread
+  constexpr int NHV = (P * (N / VB) + kCThreads - 1) / kCThreads;      // Hp vectors per thread
 
   extern __shared__ __align__(16) unsigned char smem[];
   T* Xn = reinterpret_cast<T*>(smem);  // [Q][NP]
   T* Yn = Xn + Q * NP;                 // dy [Q][NP]
-  T* YT = Yn + Q * NP;                 // dy^T [P][TQ]
-  T* Bn = YT + P * TQ;                 // [Q][NN]
+  T* Bn = Yn + Q * NP;                 // [Q][NN]
   T* Cn = Bn + Q * NN;                 // [Q][NN]
-  T* BT = Cn + Q * NN;                 // [N][TQ]
-  T* CT = BT + N * TQ;                 // [N][TQ]
-  T* Gs = CT + N * TQ;                 // Gc [P][NN]
-  T* GT = Gs + P * NN;                 // Gc^T [N][TP2]
-  T* HT = GT + N * TP2;                // Hp^T [N][TP2]
-  float* lam = reinterpret_cast<float*>(HT + N * TP2);  // log2-scaled Lambda
+  T* GT = Cn + Q * NN;                 // Gc^T [N][TP2]
+  T* HpF = GT + N * TP2;               // Hp, fragment order [P * N]
+  T* Mq = HpF + P * N;                 // M [s][t]
+  T* Kq = Mq + Q * QP;                 // K [s][t]
+  T* Kd = Kq + Q * QP;                 // K dt_s, [t][s]
+  float* lam = reinterpret_cast<float*>(Kd + Q * QP);  // log2-scaled Lambda
   float* dtv = lam + Q;
-  float* eL = dtv + Q;    // exp(Lambda_t)
-  float* sc = eL + Q;     // exp(Lambda_e - Lambda_s)
-  float* rpart = sc + Q;  // sum_s W[t,s] over each s-block: [4][Q]
-  float* csum = rpart + 4 * Q;  // sum_t W[t,s]
-  float* esum = csum + Q;     // dt_s exp(..) x_s^T Gc B_s, per column half: [2][Q]
-  float* t1 = esum + 2 * Q;   // exp(Lambda_t) dy_t . Hp C_t, per column half: [2][Q]
-  float* expl = t1 + 2 * Q;   // x_s . u_s, per column half: [2][Q]
-  float* hgw = expl + 2 * Q;  // <Gc, H_e> over each wave's tiles: [2][8] by chunk parity
+  float* eL = dtv + Q;      // exp(Lambda_t)
+  float* sc = eL + Q;       // exp(Lambda_e - Lambda_s)
+  float* rpart = sc + Q;    // [sb][t]: sum over s in block sb of W[t][s]
+  float* cpart = rpart + NBLK * Q;  // [tb][s]: sum over t in block tb of W[t][s]
+  float* t1p = cpart + NBLK * Q;    // [q][t]: exp(Lambda_t) dy_t . Hp C_t over d_state part q
+  float* esp = t1p + 4 * Q;         // [q][s]: dt_s exp(..) x_s^T Gc B_s over d_state part q
+  float* expl = esp + 4 * Q;        // [pt][s]: x_s . u_s over d_head tile pt
+  float* hgw = expl + 4 * Q;        // [2][16]: <Gc, H_e> per wave, by chunk parity
 
   int b, h, seg;
   unit_of(k.heads, k.nseg, &b, &h, &seg);
   const int64_t unit = (int64_t)b * k.heads + h;
   const int c0 = seg * k.seg_chunks, c1 = min(c0 + k.seg_chunks, k.nchunks);
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int r16 = lane % 16, g = lane / 16;
   const T* __restrict__ Xp = static_cast<const T*>(k.x);
   const T* __restrict__ DTp = static_cast<const T*>(k.dt);
@@ -661,18 +784,21 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
   const T* __restrict__ DYp = static_cast<const T*>(k.dy);
   T* __restrict__ DXp = static_cast<T*>(k.dx);
   T* __restrict__ DDTp = static_cast<T*>(k.ddt);
-  const T* __restrict__ Hst =
-      static_cast<const T*>(k.hst) + unit * (k.nchunks + 1) * (P * N);
+  const T* __restrict__ Hst = static_cast<const T*>(k.hst) + unit * (k.nchunks + 1) * (P * N);
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Ah = k.A[h];
   const float Ah2 = Ah * kLog2e;
   const float Dh = k.D ? k.D[h] : 0.0f;
 
-  // tiles of dL/dH owned by this wave: G[pt*16 + g*4 + i][nt*16 + r16]
-  const int tile0 = wave * TPW;
-  const bool owns = tile0 < NTILE;
-  const int nt = tile0 / TP, pt0 = tile0 % TP;
-  f32x4 gacc[TPW];
+  // this wave's tiles (wave-uniform; known when the tiles divide evenly)
+  const bool gown = NGP >= kCWaves || wave < NGP;  // dL/dH pair: n tile gnt, d_head tiles 2gpr, 2gpr+1
+  const int gnt = wave / (TP / 2), gpr = wave % (TP / 2);
+  const bool uown = NU >= kCWaves || wave < NU;    // u tile: s block usb, d_head tile upt
+  const int usb = wave / TP, upt = wave % TP;
+  const bool down = ND >= kCWaves * DPW || wave * DPW < ND;  // dB, dC tiles: block dsb, n tiles dnt0 + j
+  const int dsb = (wave * DPW) / TN, dnt0 = (wave * DPW) % TN, dq = dnt0 / DPW;
+
+  f32x4 gacc[2];
   {
     // dL/dH at the end of this walk: the final state's cotangent, or (split
     // sequence) the combined gradient at the end of this segment
@@ -680,419 +806,181 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
                        : k.dhT          ? k.dhT + ((int64_t)b * k.n_heads + h) * (P * N)
                                         : nullptr;
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        gacc[t][i] = (gin && owns) ? gin[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] : 0.0f;
+        gacc[t][i] = (gin && gown) ? gin[prow(2 * gpr + t, g * 4 + i) * N + gnt * 16 + r16] : 0.0f;
   }
-  // Global rows of a chunk, into registers (all issued before any is used).
-  Vec16<T> vx[NXV], vy[NXV], vb[NBV], vc[NBV];
-  float pdt = 0.0f;
-  auto load_rows = [&](int c) {
-    const int64_t row0 = rowb + (int64_t)c * Q;
-    const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
-    // unconditional loads at clamped addresses (a lane-conditional load is
-    // waited for at its branch's end); rows past len are zeroed at staging
-#pragma unroll
-    for (int v = 0; v < NXV; ++v) {
-      const int idx = min(tid + v * kBThreads, Q * (P / VB) - 1), s = min(idx % Q, len - 1);
-      const int p0 = (idx / Q) * VB;
-      vx[v] = load16(Xp + (row0 + s) * k.xs + (int64_t)h * P + p0);
-      vy[v] = load16(DYp + (row0 + s) * k.dys + (int64_t)h * P + p0);
-    }
-#pragma unroll
-    for (int v = 0; v < NBV; ++v) {
-      const int idx = min(tid + v * kBThreads, Q * (N / VB) - 1), s = min(idx % Q, len - 1);
-      const int n0 = (idx / Q) * VB;
-      vb[v] = load16(Bp + (row0 + s) * k.bs + n0);
-      vc[v] = load16(Cp + (row0 + s) * k.cs + n0);
-    }
-    pdt = to_f32(DTp[(row0 + min(lane, len - 1)) * k.dts + h]);
-  };
   // <Gc, H_e> of the last chunk: Gc = dL/dh_final, H_e = the final state;
   // for every other chunk it is formed at the end of the chunk after it,
-  // from the operand copy of that chunk's start state in LDS
+  // from that chunk's start state (the accumulators of a tile pair and a
+  // stored state fragment hold the same elements in the same slots)
   {
     const int cl = c1 - 1;
-    const T* hn = Hst + (int64_t)c1 * (P * N);
     float hdot = 0.0f;
+    if (gown) {
+      Frag8<T> hf;
+      frag_load8(hf, Hst + (int64_t)c1 * (P * N) + state_frag<N>(gpr, gnt, lane));
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        hdot += owns ? gacc[t][i] * to_f32(hn[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16])
-                     : 0.0f;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) hdot += __shfl_xor(hdot, off);
-    if (lane == 0) hgw[(cl & 1) * kBWaves + wave] = hdot;
+      for (int i = 0; i < 4; ++i) hdot += gacc[0][i] * to_f32(hf.v[i]) + gacc[1][i] * to_f32(hf.v[i + 4]);
+    }
+    hdot = wave_sum(hdot);
+    if (lane == 0) hgw[(cl & 1) * kCWaves + wave] = hdot;
   }
+  // M, K, Kd above the diagonal blocks are never written: zero them once
+  for (int i = tid; i < 3 * Q * QP; i += kCThreads) Mq[i] = from_f32<T>(0.0f);
+
+  // Global rows of a chunk and its start state, into registers (all issued
+  // before any is used): loaded during the chunk before it in the walk.
+  Vec16<T> vxy[NXY], vbc[NBC], vh[NHV];
+  float pdt = 0.0f;
+  auto load_rows = [&](int c, int tid, int lane) {
+    const int64_t row0 = rowb + (int64_t)c * Q;
+    const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
+    // unconditional loads at clamped addresses; rows past len are zeroed at staging
+#pragma unroll
+    for (int v = 0; v < NXY; ++v) {
+      const int idx = min(tid + v * kCThreads, 2 * Q * (P / VB) - 1);
+      const int which = idx / (Q * (P / VB)), r = idx % (Q * (P / VB));
+      const int s = min(r % Q, len - 1), p0 = (r / Q) * VB;
+      const T* src = which ? DYp + (row0 + s) * k.dys : Xp + (row0 + s) * k.xs;
+      vxy[v] = load16(src + (int64_t)h * P + p0);
+    }
+#pragma unroll
+    for (int v = 0; v < NBC; ++v) {
+      const int idx = min(tid + v * kCThreads, 2 * Q * (N / VB) - 1);
+      const int which = idx / (Q * (N / VB)), r = idx % (Q * (N / VB));
+      const int s = min(r % Q, len - 1), n0 = (r / Q) * VB;
+      const T* src = which ? Cp + (row0 + s) * k.cs : Bp + (row0 + s) * k.bs;
+      vbc[v] = load16(src + n0);
+    }
+    pdt = to_f32(DTp[(row0 + min(lane, len - 1)) * k.dts + h]);
+    const T* hp = Hst + (int64_t)c * (P * N);
+#pragma unroll
+    for (int v = 0; v < NHV; ++v) vh[v] = load16(hp + min(tid + v * kCThreads, P * (N / VB) - 1) * VB);
+  };
   float da_acc = 0.0f;  // wave 0: sum_r dt_r da_r of this lane's tokens
   float dd_acc = 0.0f;  // sum dy . x over this lane's entries
 
+  const int tid_o = tid;
+  load_rows(c1 - 1, opaque(tid_o), opaque(tid_o) % 64);
+  // Every chunk issues its stores and atomics after the next chunk's loads,
+  // and the staging waits for those loads with the stores still in flight.
+  // The loop is entered with nothing issued after the first loads; the
+  // compiler merges the two entries and would wait for every store.  So the
+  // entry issues as many memory operations after them: stores through an
+  // empty range, which the hardware drops.
+  {
+    constexpr int kOps = (ACC ? 8 : 4) * UPW + 8 * DPW + (ACC ? 2 : 1);
+    const auto none = uniform_rsrc(k.dB, 0u);
+#pragma unroll
+    for (int i = 0; i < kOps; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, 0);
+  }
   for (int c = c1 - 1; c >= c0; --c) {
     const int64_t row0 = rowb + (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
+    // The lane indices, re-derived every chunk from an opaque copy: the LDS
+    // and global addresses built from them are then formed inside the loop
+    // rather than hoisted out of it and held across the walk.
+    const int tid = opaque(tid_o), lane = tid % 64, r16 = lane % 16, g = lane / 16;
 
-    // ---- stage: the chunk's rows into LDS (every global load first: one
-    // round trip): token rows (zero past len), transposed copies, Hp^T and
-    // Gc.  (Loading the next chunk during this one's compute measured no
-    // faster and spills registers.) ----
-    load_rows(c);
-    Vec16<T> vh[NHV];
-    {
-      const T* hp = Hst + (int64_t)c * (P * N);
-#pragma unroll
-      for (int v = 0; v < NHV; ++v) {
-        const int idx = min(tid + v * kBThreads, P * (N / VB) - 1), p = idx % P;
-        vh[v] = load16(hp + p * N + (idx / P) * VB);
-      }
-    }
+    // ---- stage: the chunk's rows (loaded during the chunk before) into
+    // LDS token-major, zero past len; its start state as stored; Gc n-major ----
     const float dtl = lane < len ? pdt : 0.0f;
 #pragma unroll
-    for (int v = 0; v < NXV; ++v) {
-      const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
-      const Vec16<T> xv = s < len ? vx[v] : zero16<T>(), yv = s < len ? vy[v] : zero16<T>();
-      if (idx < Q * (P / VB)) {
-        store16(Xn + s * NP + p0, xv);
-        store16(Yn + s * NP + p0, yv);
-#pragma unroll
-        for (int j = 0; j < VB; ++j) YT[(p0 + j) * TQ + s] = yv.v[j];
-      }
+    for (int v = 0; v < NXY; ++v) {
+      const int idx = tid + v * kCThreads;
+      const int which = idx / (Q * (P / VB)), r = idx % (Q * (P / VB));
+      const int s = r % Q, p0 = (r / Q) * VB;
+      const Vec16<T> xv = s < len ? vxy[v] : zero16<T>();
+      if (idx < 2 * Q * (P / VB)) store16((which ? Yn : Xn) + s * NP + p0, xv);
     }
 #pragma unroll
-    for (int v = 0; v < NBV; ++v) {
-      const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
-      const Vec16<T> bv = s < len ? vb[v] : zero16<T>(), cv = s < len ? vc[v] : zero16<T>();
-      if (idx < Q * (N / VB)) {
-        store16(Bn + s * NN + n0, bv);
-        store16(Cn + s * NN + n0, cv);
-#pragma unroll
-        for (int j = 0; j < VB; ++j) {
-          BT[(n0 + j) * TQ + s] = bv.v[j];
-          CT[(n0 + j) * TQ + s] = cv.v[j];
-        }
-      }
+    for (int v = 0; v < NBC; ++v) {
+      const int idx = tid + v * kCThreads;
+      const int which = idx / (Q * (N / VB)), r = idx % (Q * (N / VB));
+      const int s = r % Q, n0 = (r / Q) * VB;
+      const Vec16<T> bv = s < len ? vbc[v] : zero16<T>();
+      if (idx < 2 * Q * (N / VB)) store16((which ? Cn : Bn) + s * NN + n0, bv);
     }
 #pragma unroll
-    for (int v = 0; v < NHV; ++v) {
-      const int idx = tid + v * kBThreads, p = idx % P, n0 = (idx / P) * VB;
-      if (idx < P * (N / VB))
-#pragma unroll
-        for (int j = 0; j < VB; ++j) HT[(n0 + j) * TP2 + p] = vh[v].v[j];
-    }
-    if (owns) {
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const int p0 = (pt0 + t) * 16 + g * 4, n = nt * 16 + r16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Gs[(p0 + i) * NN + n] = from_f32<T>(gacc[t][i]);
-        store4(GT + n * TP2 + p0, gacc[t][0], gacc[t][1], gacc[t][2], gacc[t][3]);
-      }
-    }
+    for (int v = 0; v < NHV; ++v)
+      if (tid + v * kCThreads < P * (N / VB)) store16(HpF + (tid + v * kCThreads) * VB, vh[v]);
+    // Gc^T: a tile pair's accumulators are eight consecutive d_head rows
+    if (gown) store8(GT + (gnt * 16 + r16) * TP2 + gpr * 32 + g * 8, gacc[0], gacc[1]);
     if (wave == 0) {
-      const float d = dtl;
-      const float lv = chunk_cumsum(d * Ah2, lane);
-      const float le = __shfl(lv, 63);
+      const float lv = chunk_cumsum(dtl * Ah2, lane);
+      const float le = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), 63));
       lam[lane] = lv;
-      dtv[lane] = d;
+      dtv[lane] = dtl;
       eL[lane] = __builtin_amdgcn_exp2f(lv);
       sc[lane] = __builtin_amdgcn_exp2f(le - lv);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) rpart[j * Q + lane] = 0.0f;
     }
     __syncthreads();
+    // the next chunk in the walk (this one again at the segment's start),
+    // in flight while this one is computed
+    load_rows(max(c - 1, c0), tid, lane);
 
-    {
-      // ---- this wave: s-block and t-block `blk`, column half `hf` (d_head
-      // tiles [pb0, pb0+TPH), d_state tiles [nb0, nb0+TNH)); the two waves of
-      // a block share its Q x Q products and split the outputs' columns ----
-      const int blk = wave % NBLK, hf = wave / NBLK;
-      const int pb0 = hf * TPH, nb0 = hf * TNH;
-      const bool nlive = nb0 < TN;  // this half has d_state tiles (wave-uniform)
-
-      // ---- s-side: rows s of the block: dx, dB, column sums of W ----
-      {
-        const int s0 = blk * 16, srow = s0 + r16;  // A-operand row of this lane
-        const float scs = sc[srow];
-        f32x4 au[TPH], ab[TNH];
-#pragma unroll
-        for (int i = 0; i < TPH; ++i) au[i] = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < TNH; ++i) ab[i] = f32x4{0, 0, 0, 0};
-        // end-state terms: u += exp(..) B_s Gc^T,  dB-part += exp(..) x_s Gc
-#pragma unroll 1
-        for (int kb = 0; kb < NKB; ++kb) {
-          Frag8<T> bf;
-          frag_row_scaled(bf, Bn + srow * NN, kb * 32 + g * 8, N, scs);
-#pragma unroll
-          for (int pp = 0; pp < TPH; ++pp) {
-            Frag8<T> gf;
-            frag_row(gf, Gs + ((pb0 + pp) * 16 + r16) * NN, kb * 32 + g * 8, N);
-            au[pp] = mma(bf, gf, au[pp]);
-          }
-        }
-        if (nlive) {
-#pragma unroll 1
-          for (int kp = 0; kp < PKB; ++kp) {
-            Frag8<T> xf;
-            frag_row_scaled(xf, Xn + srow * NP, kp * 32 + g * 8, P, scs);
-#pragma unroll
-            for (int nn = 0; nn < TNH; ++nn) {
-              Frag8<T> gf;
-              frag_load8(gf, GT + ((nb0 + nn) * 16 + r16) * TP2 + kp * 32 + g * 8);
-              ab[nn] = mma(xf, gf, ab[nn]);
-            }
-          }
-        }
-        // esum_s (this half) = dt_s sum_n ab[s][n] B[s][n]  (rows s = s0 + 4g + i)
-        {
-          float e[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int s = s0 + g * 4 + i;
-            float v = 0.0f;
-            if (nlive)
-#pragma unroll
-              for (int nn = 0; nn < TNH; ++nn)
-                v += ab[nn][i] * to_f32(Bn[s * NN + (nb0 + nn) * 16 + r16]);
-            e[i] = v;
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) e[i] = row16_sum(e[i]);
-          if (r16 == 0)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) esum[hf * Q + s0 + g * 4 + i] = e[i] * dtv[s0 + g * 4 + i];
-        }
-        // diagonal-block terms over t-block pairs (2ip, 2ip+1) with t >= s
-        const float lam_s = lam[srow], dt_s = dtv[srow];
-        float csum_l = 0.0f;
-#pragma unroll 1
-        for (int ip = blk / 2; ip < NBLK / 2; ++ip) {
-          const int ta = 2 * ip, tb = 2 * ip + 1;
-          const bool doa = ta >= blk;  // block ta has t >= s somewhere (wave-uniform)
-          f32x4 gA = {0, 0, 0, 0}, gB = {0, 0, 0, 0}, qA = {0, 0, 0, 0}, qB = {0, 0, 0, 0};
-#pragma unroll 2
-          for (int kb = 0; kb < NKB; ++kb) {
-            Frag8<T> bs, ca, cb;
-            frag_row(bs, Bn + srow * NN, kb * 32 + g * 8, N);
-            frag_row(cb, Cn + (tb * 16 + r16) * NN, kb * 32 + g * 8, N);
-            gB = mma(cb, bs, gB);
-            if (doa) {
-              frag_row(ca, Cn + (ta * 16 + r16) * NN, kb * 32 + g * 8, N);
-              gA = mma(ca, bs, gA);
-            }
-          }
-#pragma unroll
-          for (int kp = 0; kp < PKB; ++kp) {
-            Frag8<T> xs, ya, yb;
-            frag_load8(xs, Xn + srow * NP + kp * 32 + g * 8);
-            frag_load8(yb, Yn + (tb * 16 + r16) * NP + kp * 32 + g * 8);
-            qB = mma(yb, xs, qB);
-            if (doa) {
-              frag_load8(ya, Yn + (ta * 16 + r16) * NP + kp * 32 + g * 8);
-              qA = mma(ya, xs, qA);
-            }
-          }
-          // lane: G[t][s], Q[t][s] for s = srow, t = ta*16 + 4g + i (slot i)
-          // and t = tb*16 + 4g + i (slot 4 + i)
-          Frag8<T> mf, kf;
-          float rw[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int t = (j < 4 ? ta : tb) * 16 + g * 4 + (j & 3);
-            const float gv = j < 4 ? gA[j] : gB[j - 4];
-            const float qv = j < 4 ? qA[j] : qB[j - 4];
-            const float dec = t >= srow ? __builtin_amdgcn_exp2f(lam[t] - lam_s) : 0.0f;
-            frag_set(mf, j, gv * dec);
-            frag_set(kf, j, qv * dec);
-            const float w = gv * qv * dec * dt_s;
-            rw[j] = w;
-            csum_l += w;
-          }
-          if (hf == 0) {
-            // row sums of W over this block's 16 s (lanes r16), per t
-#pragma unroll
-            for (int j = 0; j < 8; ++j) rw[j] = row16_sum(rw[j]);
-            if (r16 == 0) {
-#pragma unroll
-              for (int j = 0; j < 8; ++j)
-                rpart[blk * Q + (j < 4 ? ta : tb) * 16 + g * 4 + (j & 3)] = rw[j];
-            }
-          }
-          // u += M^T dy  (k = t in the slot order above), dB-part += K^T C
-#pragma unroll
-          for (int pp = 0; pp < TPH; ++pp) {
-            Frag8<T> yf;
-            const T* yr = YT + ((pb0 + pp) * 16 + r16) * TQ;
-            frag_load4x2(yf, yr + ta * 16 + g * 4, yr + tb * 16 + g * 4);
-            au[pp] = mma(mf, yf, au[pp]);
-          }
-          if (nlive) {
-#pragma unroll
-            for (int nn = 0; nn < TNH; ++nn) {
-              Frag8<T> cf;
-              const T* cr = CT + ((nb0 + nn) * 16 + r16) * TQ;
-              frag_load4x2(cf, cr + ta * 16 + g * 4, cr + tb * 16 + g * 4);
-              ab[nn] = mma(kf, cf, ab[nn]);
-            }
-          }
-        }
-        // column sums: over the 4 t-slots of each group, then the 4 groups
-        csum_l += __shfl_xor(csum_l, 16);
-        csum_l += __shfl_xor(csum_l, 32);
-        if (hf == 0 && g == 0) csum[srow] = csum_l;
-        // epilogue: dx = dt_s u + D dy, x_s . u_s and dy . x over this half's
-        // d_head columns, dB atomics over its d_state columns
-        float ex[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        float dxv[4][TPH];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = s0 + g * 4 + i;
-          const float dts = dtv[s];
-          const bool live = s < len;
-#pragma unroll
-          for (int pp = 0; pp < TPH; ++pp) {
-            const int p = (pb0 + pp) * 16 + r16;
-            const float xv = to_f32(Xn[s * NP + p]), yv = to_f32(Yn[s * NP + p]);
-            ex[i] += xv * au[pp][i];
-            dd_acc += xv * yv;
-            dxv[i][pp] = dts * au[pp][i] + Dh * yv;
-          }
-          if (live && nlive) {
-#pragma unroll
-            for (int nn = 0; nn < TNH; ++nn)
-              unsafeAtomicAdd(k.dB + (row0 + s) * k.dbs + (nb0 + nn) * 16 + r16, dts * ab[nn][i]);
-          }
-        }
-        // dx rows: when adding into the caller's dx, all of this lane's old
-        // values are read (at clamped rows, under the wave-uniform flag only)
-        // before any is written, so the reads are in flight together
-        T* const dxrow = DXp + row0 * k.dxs + (int64_t)h * P;
-        if (k.accumulate) {
-          float old[4][TPH];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int pp = 0; pp < TPH; ++pp)
-              old[i][pp] = to_f32(dxrow[(int64_t)min(s0 + g * 4 + i, len - 1) * k.dxs +
-                                        (pb0 + pp) * 16 + r16]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (s0 + g * 4 + i < len)
-#pragma unroll
-              for (int pp = 0; pp < TPH; ++pp)
-                dxrow[(int64_t)(s0 + g * 4 + i) * k.dxs + (pb0 + pp) * 16 + r16] =
-                    from_f32<T>(old[i][pp] + dxv[i][pp]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (s0 + g * 4 + i < len)
-#pragma unroll
-              for (int pp = 0; pp < TPH; ++pp)
-                dxrow[(int64_t)(s0 + g * 4 + i) * k.dxs + (pb0 + pp) * 16 + r16] =
-                    from_f32<T>(dxv[i][pp]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ex[i] = row16_sum(ex[i]);
-        if (r16 == 0)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) expl[hf * Q + s0 + g * 4 + i] = ex[i];
+    // ================= phase 1 =================
+    // ---- one Q x Q block (sb, tb), tb >= sb: lane slot i is s = sb*16 + 4g + i,
+    // t = tb*16 + r16 ----
+    if (wave < NQQ) {
+      int sb = 0, tb = wave;
+      while (tb >= NBLK - sb) {
+        tb -= NBLK - sb;
+        ++sb;
       }
-
-      // ---- t-side: rows t of the block: dC (this half's columns), Hp term ----
-      {
-        const int t0 = blk * 16, trow = t0 + r16;
-        const float lam_t = lam[trow];
-        f32x4 ac[TNH];
+      tb += sb;
+      f32x4 gq = {0, 0, 0, 0}, qq = {0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < TNH; ++i) ac[i] = f32x4{0, 0, 0, 0};
-        if (nlive) {
-          // off-diagonal output term: exp(Lambda_t) dy_t Hp
-#pragma unroll 1
-          for (int kp = 0; kp < PKB; ++kp) {
-            Frag8<T> yf;
-            frag_row_scaled(yf, Yn + trow * NP, kp * 32 + g * 8, P, eL[trow]);
-#pragma unroll
-            for (int nn = 0; nn < TNH; ++nn) {
-              Frag8<T> hfr;
-              frag_load8(hfr, HT + ((nb0 + nn) * 16 + r16) * TP2 + kp * 32 + g * 8);
-              ac[nn] = mma(yf, hfr, ac[nn]);
-            }
-          }
-        }
-        {
-          float e[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = t0 + g * 4 + i;
-            float v = 0.0f;
-            if (nlive)
-#pragma unroll
-              for (int nn = 0; nn < TNH; ++nn)
-                v += ac[nn][i] * to_f32(Cn[t * NN + (nb0 + nn) * 16 + r16]);
-            e[i] = v;
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) e[i] = row16_sum(e[i]);
-          if (r16 == 0)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) t1[hf * Q + t0 + g * 4 + i] = e[i];
-        }
-        if (nlive) {
-          // diagonal-block term over s-block pairs (2jp, 2jp+1) with s <= t
-#pragma unroll 1
-          for (int jp = 0; jp <= blk / 2; ++jp) {
-            const int sa = 2 * jp, sb2 = 2 * jp + 1;
-            const bool dob = sb2 <= blk;  // wave-uniform
-            f32x4 rA = {0, 0, 0, 0}, rB = {0, 0, 0, 0};
-#pragma unroll
-            for (int kp = 0; kp < PKB; ++kp) {
-              Frag8<T> yt, xa, xb;
-              frag_load8(yt, Yn + trow * NP + kp * 32 + g * 8);
-              frag_load8(xa, Xn + (sa * 16 + r16) * NP + kp * 32 + g * 8);
-              rA = mma(xa, yt, rA);
-              if (dob) {
-                frag_load8(xb, Xn + (sb2 * 16 + r16) * NP + kp * 32 + g * 8);
-                rB = mma(xb, yt, rB);
-              }
-            }
-            // lane: (x_s . dy_t) for t = trow, s = sa*16 + 4g + i (slot i),
-            // sb2*16 + 4g + i (slot 4 + i)
-            Frag8<T> kf;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int s = (j < 4 ? sa : sb2) * 16 + g * 4 + (j & 3);
-              const float rv = j < 4 ? rA[j] : rB[j - 4];
-              const float f = s <= trow ? __builtin_amdgcn_exp2f(lam_t - lam[s]) * dtv[s] : 0.0f;
-              frag_set(kf, j, rv * f);
-            }
-#pragma unroll
-            for (int nn = 0; nn < TNH; ++nn) {
-              Frag8<T> bf;
-              const T* br = BT + ((nb0 + nn) * 16 + r16) * TQ;
-              frag_load4x2(bf, br + sa * 16 + g * 4, br + sb2 * 16 + g * 4);
-              ac[nn] = mma(kf, bf, ac[nn]);
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = t0 + g * 4 + i;
-            if (t < len) {
-#pragma unroll
-              for (int nn = 0; nn < TNH; ++nn)
-                unsafeAtomicAdd(k.dC + (row0 + t) * k.dcs + (nb0 + nn) * 16 + r16, ac[nn][i]);
-            }
-          }
-        }
+      for (int kb = 0; kb < NKB; ++kb) {
+        Frag8<T> bs, ct;
+        frag_row(bs, Bn + (sb * 16 + r16) * NN, kb * 32 + g * 8, N);
+        frag_row(ct, Cn + (tb * 16 + r16) * NN, kb * 32 + g * 8, N);
+        gq = mma(bs, ct, gq);  // B_s . C_t
       }
+#pragma unroll
+      for (int kp = 0; kp < PKB; ++kp) {
+        Frag8<T> xs, yt;
+        frag_load8(xs, Xn + (sb * 16 + r16) * NP + kp * 32 + g * 8);
+        frag_load8(yt, Yn + (tb * 16 + r16) * NP + kp * 32 + g * 8);
+        qq = mma(xs, yt, qq);  // x_s . dy_t
+      }
+      const int t = tb * 16 + r16, s4 = sb * 16 + g * 4;
+      const float lam_t = lam[t];
+      const f32x4 lam_s = *reinterpret_cast<const f32x4*>(lam + s4);
+      const f32x4 dt_s = *reinterpret_cast<const f32x4*>(dtv + s4);
+      float w[4], kd[4], rs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float dec = t >= s4 + i ? __builtin_amdgcn_exp2f(lam_t - lam_s[i]) : 0.0f;
+        const float m = gq[i] * dec, kk = qq[i] * dec;
+        Mq[(s4 + i) * QP + t] = from_f32<T>(m);
+        Kq[(s4 + i) * QP + t] = from_f32<T>(kk);
+        kd[i] = kk * dt_s[i];
+        w[i] = m * qq[i] * dt_s[i];
+        rs += w[i];
+      }
+      store4(Kd + t * QP + s4, kd[0], kd[1], kd[2], kd[3]);
+      // row sums (over s, per t): over the 4 slots, then the 4 groups
+      rs += xor_lane(rs, lane, 16);
+      rs += xor_lane(rs, lane, 32);
+      if (g == 0) rpart[sb * Q + t] = rs;
+      // column sums (over t, per s): over the 16 lanes of each group
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = row16_sum(w[i]);
+      if (r16 == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cpart[tb * Q + s4 + i] = w[i];
     }
 
-    // ---- every wave: dGp = exp(Lambda_e) Gc + sum_t exp(Lambda_t) dy_t C_t^T on
-    // its tiles, then <dGp, Hp> for the chunk before (Hp^T is in LDS) ----
-    if (owns) {
+    // ---- dL/dH tile pair: dGp = exp(Lambda_e) Gc + sum_t exp(Lambda_t) dy_t C_t^T
+    // (A operand rows in the paired order of prow()), then <dGp, Hp> for the
+    // chunk before ----
+    if (gown) {
       const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
 #pragma unroll
-      for (int t = 0; t < TPW; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) gacc[t][i] *= dec;
 #pragma unroll
@@ -1101,48 +989,201 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
         const f32x4 e0 = *reinterpret_cast<const f32x4*>(eL + tq);
         const f32x4 e1 = *reinterpret_cast<const f32x4*>(eL + tq + 4);
         Frag8<T> cr, cf;
-        frag_load8(cr, CT + (nt * 16 + r16) * TQ + tq);
+        frag_cols(cr, Cn, NN, tq, tq + 4, gnt * 16, 4, lane);
 #pragma unroll
         for (int j = 0; j < 8; ++j) frag_set(cf, j, to_f32(cr.v[j]) * (j < 4 ? e0[j] : e1[j - 4]));
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
+        for (int t = 0; t < 2; ++t) {
           Frag8<T> yf;
-          frag_load8(yf, YT + ((pt0 + t) * 16 + r16) * TQ + tq);
+          frag_cols(yf, Yn, NP, tq, tq + 4, gpr * 32 + t * 4, 8, lane);
           gacc[t] = mma(yf, cf, gacc[t]);
         }
       }
+      if (c > c0) {
+        Frag8<T> hd;
+        frag_load8(hd, HpF + state_frag<N>(gpr, gnt, lane));
+        float hdot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hdot += gacc[0][i] * to_f32(hd.v[i]) + gacc[1][i] * to_f32(hd.v[i + 4]);
+        hdot = wave_sum(hdot);
+        // two halves by chunk parity: wave 0 reads chunk c's half in the
+        // tail while this writes chunk c-1's
+        if (lane == 0) hgw[((c - 1) & 1) * kCWaves + wave] = hdot;
+      }
     }
-    if (c > c0) {
-      float hdot = 0.0f;
-      if (owns) {
+
+    // ---- u tile (usb, upt): exp(Lambda_e - Lambda_s) B_s Gc^T ----
+    f32x4 au = {0, 0, 0, 0};
+    if (uown) {
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-          float hv[4];
-          load4(HT + (nt * 16 + r16) * TP2 + (pt0 + t) * 16 + g * 4, hv);
+      for (int kb = 0; kb < NKB; ++kb) {
+        Frag8<T> bf, gf;
+        frag_row(bf, Bn + (usb * 16 + r16) * NN, kb * 32 + g * 8, N);
+        frag_cols(gf, GT, TP2, kb * 32 + g * 8, kb * 32 + g * 8 + 4, upt * 16, 4, lane, kb * 32 + g * 8 < N);
+        au = mma(bf, gf, au);
+      }
+      const f32x4 s4 = *reinterpret_cast<const f32x4*>(sc + usb * 16 + g * 4);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) hdot += gacc[t][i] * hv[i];
+      for (int i = 0; i < 4; ++i) au[i] *= s4[i];
+    }
+    // ---- dB tiles (dsb, dnt0 + j): exp(..) x_s Gc, and its part of esum ----
+    f32x4 ab[DPW], ac[DPW];
+#pragma unroll
+    for (int j = 0; j < DPW; ++j) ab[j] = ac[j] = f32x4{0, 0, 0, 0};
+    if (down) {
+#pragma unroll
+      for (int kp = 0; kp < PKB; ++kp) {
+        Frag8<T> xf;
+        frag_load8(xf, Xn + (dsb * 16 + r16) * NP + kp * 32 + g * 8);
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) {
+          Frag8<T> gf;
+          frag_load8(gf, GT + ((dnt0 + j) * 16 + r16) * TP2 + kp * 32 + g * 8);
+          ab[j] = mma(xf, gf, ab[j]);
         }
       }
-      hdot = row16_sum(hdot);
-      hdot += __shfl_xor(hdot, 16);
-      hdot += __shfl_xor(hdot, 32);
-      // two halves by chunk parity: wave 0 reads chunk c's half below while
-      // this writes chunk c-1's
-      if (lane == 0) hgw[((c - 1) & 1) * kBWaves + wave] = hdot;
+      const int s4 = dsb * 16 + g * 4;
+      const f32x4 scs = *reinterpret_cast<const f32x4*>(sc + s4);
+      const f32x4 dts = *reinterpret_cast<const f32x4*>(dtv + s4);
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = 0.0f;
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) {
+          ab[j][i] *= scs[i];
+          v += ab[j][i] * to_f32(Bn[(s4 + i) * NN + (dnt0 + j) * 16 + r16]);
+        }
+        e[i] = row16_sum(v) * dts[i];
+      }
+      if (r16 == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) esp[dq * Q + s4 + i] = e[i];
+      // ---- dC tiles (same block index as t block, same n tiles):
+      // exp(Lambda_t) dy_t Hp, and its part of t1 ----
+#pragma unroll
+      for (int kp = 0; kp < PKB; ++kp) {
+        Frag8<T> yf;
+        frag_load8(yf, Yn + (dsb * 16 + r16) * NP + kp * 32 + g * 8);
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) {
+          Frag8<T> hfr;
+          frag_load8(hfr, HpF + state_frag<N>(kp, dnt0 + j, lane));
+          ac[j] = mma(yf, hfr, ac[j]);
+        }
+      }
+      const f32x4 et = *reinterpret_cast<const f32x4*>(eL + s4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = 0.0f;
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) {
+          ac[j][i] *= et[i];
+          v += ac[j][i] * to_f32(Cn[(s4 + i) * NN + (dnt0 + j) * 16 + r16]);
+        }
+        e[i] = row16_sum(v);
+      }
+      if (r16 == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t1p[dq * Q + s4 + i] = e[i];
     }
     __syncthreads();
 
-    // ---- wave 0: dLambda -> da (suffix sum) -> ddt, dA ----
+    // ================= phase 2 =================
+    // Outputs leave through buffer resources over this chunk's rows: lanes at
+    // rows past len fall outside the range and are dropped, so no store or
+    // atomic sits under a lane condition (which would make every later wait
+    // for a load also wait for all earlier stores).
+    const auto rdx = uniform_rsrc(DXp + row0 * k.dxs + (int64_t)h * P, (uint32_t)(len * k.dxs * sizeof(T)));
+    const auto rdb = uniform_rsrc(k.dB + row0 * k.dbs, (uint32_t)(len * k.dbs * sizeof(float)));
+    const auto rdc = uniform_rsrc(k.dC + row0 * k.dcs, (uint32_t)(len * k.dcs * sizeof(float)));
+    // ---- u += M dy over t >= s (K = t slices from the block's own) ----
+    if (uown) {
+#pragma unroll 1
+      for (int ks = usb / 2; ks < Q / 32; ++ks) {
+        Frag8<T> mf, yf;
+        frag_load8(mf, Mq + (usb * 16 + r16) * QP + ks * 32 + g * 8);
+        frag_cols(yf, Yn, NP, ks * 32 + g * 8, ks * 32 + g * 8 + 4, upt * 16, 4, lane);
+        au = mma(mf, yf, au);
+      }
+      // dx = dt_s u + D dy; x_s . u_s over this d_head tile; dy . x
+      const int s4 = usb * 16 + g * 4, p = upt * 16 + r16;
+      const f32x4 dts = *reinterpret_cast<const f32x4*>(dtv + s4);
+      float ex[4], dxv[4], old[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        old[i] = ACC ? buffer_elem<T>(rdx, (uint32_t)(((s4 + i) * k.dxs + p) * sizeof(T))) : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float xv = to_f32(Xn[(s4 + i) * NP + p]), yv = to_f32(Yn[(s4 + i) * NP + p]);
+        ex[i] = xv * au[i];
+        dd_acc += xv * yv;
+        dxv[i] = dts[i] * au[i] + Dh * yv;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        buffer_store_elem<T>(rdx, (uint32_t)(((s4 + i) * k.dxs + p) * sizeof(T)), old[i] + dxv[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ex[i] = row16_sum(ex[i]);
+      if (r16 == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) expl[upt * Q + s4 + i] = ex[i];
+    }
+    if (down) {
+      // ---- dB += K C over t >= s; dB = dt_s (...) ----
+#pragma unroll 1
+      for (int ks = dsb / 2; ks < Q / 32; ++ks) {
+        Frag8<T> kf;
+        frag_load8(kf, Kq + (dsb * 16 + r16) * QP + ks * 32 + g * 8);
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) {
+          Frag8<T> cf;
+          frag_cols(cf, Cn, NN, ks * 32 + g * 8, ks * 32 + g * 8 + 4, (dnt0 + j) * 16, 4, lane);
+          ab[j] = mma(kf, cf, ab[j]);
+        }
+      }
+      // ---- dC += Kd B over s <= t ----
+#pragma unroll 1
+      for (int ks = 0; ks <= dsb / 2; ++ks) {
+        Frag8<T> kf;
+        frag_load8(kf, Kd + (dsb * 16 + r16) * QP + ks * 32 + g * 8);
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) {
+          Frag8<T> bf;
+          frag_cols(bf, Bn, NN, ks * 32 + g * 8, ks * 32 + g * 8 + 4, (dnt0 + j) * 16, 4, lane);
+          ac[j] = mma(kf, bf, ac[j]);
+        }
+      }
+      const int s4 = dsb * 16 + g * 4;
+      const f32x4 dts = *reinterpret_cast<const f32x4*>(dtv + s4);
+#pragma unroll
+      for (int j = 0; j < DPW; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = (dnt0 + j) * 16 + r16;
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+              dts[i] * ab[j][i], rdb, (int)(((s4 + i) * k.dbs + col) * sizeof(float)), 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+              ac[j][i], rdc, (int)(((s4 + i) * k.dcs + col) * sizeof(float)), 0, 0);
+        }
+    }
+    __syncthreads();
+
+    // ---- tail (wave 0): dLambda -> da (suffix sum) -> ddt, dA ----
     if (wave == 0) {
-      const int t = lane;
+      const int t = lane, tb = t / 16;
       // fixed summation order: the result does not depend on wave timing
-      float dl = (t1[t] + t1[Q + t]) +
-                 (((rpart[t] + rpart[Q + t]) + rpart[2 * Q + t]) + rpart[3 * Q + t]) - csum[t] -
-                 (esum[t] + esum[Q + t]);
+      float dl = 0.0f;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) dl += t1p[q * Q + t] - esp[q * Q + t];
+#pragma unroll
+      for (int sb = 0; sb < NBLK; ++sb) dl += sb <= tb ? rpart[sb * Q + t] : 0.0f;
+#pragma unroll
+      for (int b2 = 0; b2 < NBLK; ++b2) dl -= b2 >= tb ? cpart[b2 * Q + t] : 0.0f;
       if (t == Q - 1) {
         float hg = 0.0f;
 #pragma unroll
-        for (int j = 0; j < kBWaves; ++j) hg += hgw[(c & 1) * kBWaves + j];
+        for (int j = 0; j < NGP; ++j) hg += hgw[(c & 1) * kCWaves + j];
         dl += hg;
       }
       // suffix sum over t' >= t: the total minus the prefix before t
@@ -1150,34 +1191,41 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdK k) {
       const float tot = __builtin_bit_cast(
           float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
       const float suf = (tot - incl) + dl;
-      if (t < len) {
-        grad_store(DDTp + (row0 + t) * k.ddts + h, (expl[t] + expl[Q + t]) + Ah * suf, k.accumulate);
-        da_acc += dtv[t] * suf;
-      }
+      float xu = 0.0f;
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) xu += expl[pt * Q + t];
+      // ddt through a range over this chunk's rows (tokens past len dropped);
+      // dt is 0 past len, so da_acc takes nothing from them
+      const auto rdt = uniform_rsrc(DDTp + row0 * k.ddts + h, (uint32_t)(len * k.ddts * sizeof(T)));
+      const uint32_t off = (uint32_t)(t * k.ddts * sizeof(T));
+      const float old = ACC ? buffer_elem<T>(rdt, off) : 0.0f;
+      buffer_store_elem<T>(rdt, off, old + xu + Ah * suf);
+      da_acc += dtv[t] * suf;
     }
-    // wave 0 rewrites lam/dtv/eL/sc/rpart only after its own reads above;
-    // every other array is rewritten after the next barrier
+    // wave 0 rewrites lam/dtv/eL/sc only after its own reads above; every
+    // other array is rewritten after the next barrier
   }
 
   // ---- per-unit results: dh0, dA, dD ----
-  if (k.dh0 && owns && seg == 0) {
+  if (k.dh0 && gown && seg == 0) {
+    // (lane indices re-derived here, as in the loop, so that these addresses
+    // are not formed before the walk and held across it)
+    const int ln = opaque(lane), r16 = ln % 16, g = ln / 16;
     float* dst = k.dh0 + ((int64_t)b * k.n_heads + h) * (P * N);
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float* q = dst + ((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16;
+        float* q = dst + prow(2 * gpr + t, g * 4 + i) * N + gnt * 16 + r16;
         *q = k.accumulate ? *q + gacc[t][i] : gacc[t][i];
       }
   }
   if (wave == 0) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) da_acc += __shfl_xor(da_acc, off);
+    da_acc = wave_sum(da_acc);
     if (lane == 0) unsafeAtomicAdd(k.dA + h, da_acc);
   }
   if (k.dD) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) dd_acc += __shfl_xor(dd_acc, off);
+    dd_acc = wave_sum(dd_acc);
     if (lane == 0) unsafeAtomicAdd(k.dD + h, dd_acc);
   }
 }
@@ -1208,9 +1256,10 @@ hipError_t launch_shape(const BwdK& k, int64_t batch, hipStream_t s) {
   static_assert(ChunkLds<T, P, N>::bytes <= 160 * 1024, "chunk tiles fit one CU's LDS");
   const void* fns[] = {reinterpret_cast<const void*>(&bwd_state_kernel<T, P, N>),
                        reinterpret_cast<const void*>(&bwd_prepass_kernel<T, P, N>),
-                       reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N>)};
-  const size_t ldss[] = {lds1, lds1, lds2};
-  for (int i = 0; i < 3; ++i) {
+                       reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N, false>),
+                       reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N, true>)};
+  const size_t ldss[] = {lds1, lds1, lds2, lds2};
+  for (int i = 0; i < 4; ++i) {
     const hipError_t e =
         hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldss[i]);
     if (e != hipSuccess) return e;
@@ -1228,7 +1277,10 @@ hipError_t launch_shape(const BwdK& k, int64_t batch, hipStream_t s) {
   hipLaunchKernelGGL((bwd_state_kernel<T, P, N>), dim3(grid), dim3(kBThreads), lds1, s, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N>), dim3(grid), dim3(kBThreads), lds2, s, k);
+  if (k.accumulate)
+    hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N, true>), dim3(grid), dim3(kCThreads), lds2, s, k);
+  else
+    hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N, false>), dim3(grid), dim3(kCThreads), lds2, s, k);
   return hipGetLastError();
 }
 
