@@ -450,9 +450,10 @@ int mm_conv1d_silu_backward(const void* xbc_in, int64_t in_row_stride,
 
 /*
  * Bytes of device workspace mm_ssd_backward needs: the state before every
- * 64-token chunk and the final state of each active (sequence, head), in the
- * storage dtype, and, when the sequences are split, fp32 segment states and
- * gradients (see mm_ssd_backward_segments).  Same argument meaning and errors as mm_ssd_backward.
+ * 64-token chunk and the final state of each active (sequence, head), and
+ * dL/dH at the end of every chunk, in the storage dtype, and, when the
+ * sequences are split, fp32 segment states and gradients (see
+ * mm_ssd_backward_segments).  Same argument meaning and errors as mm_ssd_backward.
  * Host only.
  */
 int mm_ssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
@@ -460,10 +461,12 @@ int mm_ssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t n_head
                                    int64_t n_heads_active, int dtype, size_t* bytes_out);
 
 /*
- * Segments per sequence a mm_ssd_backward call with these sizes uses: with
+ * Segments per sequence a mm_ssd_backward call with these sizes uses for its
+ * two walks over the chunks (the states forwards, dL/dH backwards): with
  * fewer than 256 active (sequence, head) walks, the sequences are split into
  * segments of at least 256 tokens walked in parallel (a prepass and a
- * combine chain them; the workspace size includes their data).  Same
+ * combine chain them; the workspace size includes their data).  The
+ * gradients themselves are then formed for all chunks in parallel.  Same
  * argument meaning and errors as mm_ssd_backward.  Host only.
  */
 int mm_ssd_backward_segments(int64_t batch, int64_t seqlen, int64_t n_heads,
@@ -495,10 +498,11 @@ int mm_ssd_backward_segments(int64_t batch, int64_t seqlen, int64_t n_heads,
  *       granularity with its n_heads_active and the cotangents of its pass).
  *   workspace: at least mm_ssd_backward_workspace_size() bytes, 16-byte
  *       aligned, not used concurrently by another call.
- * dB, dC, dA and dD are sums formed with fp32 atomics, so their last bits can
- * differ between runs; dx, ddt and dinitial_state are deterministic.  Those
- * four must be ordinary device allocations (hipMalloc, coarse-grained): the
- * hardware fp32 atomics used are not defined on fine-grained host memory.
+ * dA and dD are sums formed with fp32 atomics, so their last bits can differ
+ * between runs; dx, ddt, dB, dC (summed over the heads in a fixed order) and
+ * dinitial_state are deterministic.  dA and dD must be ordinary device
+ * allocations (hipMalloc, coarse-grained): the hardware fp32 atomics used are
+ * not defined on fine-grained host memory.
  * Preconditions: those of mm_ssd_forward except chunk (the backward cuts
  * 64-token chunks itself); (d_head, d_state) = (64, 64) or (64, 128) with
  * MM_BF16, (32, 16) with MM_F32 (MM_ERR_UNSUPPORTED otherwise); row strides

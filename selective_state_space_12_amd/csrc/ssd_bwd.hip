@@ -89,7 +89,8 @@ struct BwdK {
   int64_t dcs;
   float* dD;
   float* dh0;
-  void* hst;  // (batch, heads, nchunks + 1, P, N) storage type
+  void* hst;  // (batch, heads, nchunks + 1, P, N) storage type, fragment order
+  void* gst;  // (batch, heads, nchunks, N, P) storage type: dL/dH at each chunk's end
   // sequence split (nseg > 1): per (unit, segment) fp32 P x N blocks and
   // log2 decays; see the launch for what each holds when
   float* seg_h;
@@ -301,7 +302,7 @@ __device__ __forceinline__ void state_walk(const BwdK& k, int pid, int total) {
 
   // this wave's state tiles (pt0 + t, nt), rows in the paired order of prow()
   const int tile0 = wave * TPW;
-  const bool owns = tile0 < NTILE;
+  const bool owns = NTILE >= kBWaves * TPW || tile0 < NTILE;  // known true when every wave owns
   const int nt = tile0 / TP, pt0 = tile0 % TP;
   f32x4 hacc[TPW];
   const float* hin = PRE ? nullptr
@@ -445,21 +446,22 @@ __device__ __forceinline__ void state_walk(const BwdK& k, int pid, int total) {
   }
 }
 
-template <typename T, int P, int N>
-__global__ __launch_bounds__(kBThreads) void bwd_state_kernel(BwdK k) {
-  state_walk<T, P, N, false>(k, blockIdx.x, gridDim.x);
-}
 
-// Reverse prepass of the sequence split: segments 1..nseg-1 walk their
-// chunks backwards from dL/dH = 0 at their end with the dL/dH update alone
-// (dGp = exp(Lambda_e) Gc + sum_t exp(Lambda_t) dy_t C_t^T) and write the
-// result at their start and their log2 decay (seg_g, seg_gd).
-template <typename T, int P, int N>
+// Reverse walk of dL/dH alone, chunk by chunk backwards:
+//   dGp = exp(Lambda_e) Gc + sum_t exp(Lambda_t) dy_t C_t^T.
+// MAIN = false (prepass of the sequence split): segments 1..nseg-1 walk from
+// dL/dH = 0 at their end and write the result at their start and their log2
+// decay (seg_g, seg_gd).  MAIN = true: every segment walks from the combined
+// gradient at its end (dhT for the last one) and stores Gc, the gradient at
+// the end of each chunk, n-major ([N][P], gst) for the chunk kernel; the
+// first segment writes dh0.  Tile rows in the paired order of prow().
+template <typename T, int P, int N, bool MAIN>
 __device__ __forceinline__ void gprep_walk(const BwdK& k, int pid, int total) {
   using L = StateLds<T, P, N>;
   constexpr int Q = kBQ, TQ = L::TQ;
   constexpr int TP = P / 16, TN = N / 16, NTILE = TP * TN;
-  constexpr int TPW = NTILE >= kBWaves ? NTILE / kBWaves : 1;
+  constexpr int TPW = NTILE >= 2 * kBWaves ? NTILE / kBWaves : 2;
+  static_assert(TP % TPW == 0 && TPW % 2 == 0, "a wave's tiles are whole pairs of one column block");
   constexpr int VB = 16 / (int)sizeof(T);
   constexpr int NYV = (Q * (P / VB) + kBThreads - 1) / kBThreads;
   constexpr int NCV = (Q * (N / VB) + kBThreads - 1) / kBThreads;
@@ -470,8 +472,8 @@ __device__ __forceinline__ void gprep_walk(const BwdK& k, int pid, int total) {
   float* eL = lam + Q;
 
   int b, h, sg;
-  unit_of_idx(pid, total, k.heads, k.nseg - 1, &b, &h, &sg);
-  const int seg = sg + 1;
+  unit_of_idx(pid, total, k.heads, MAIN ? k.nseg : k.nseg - 1, &b, &h, &sg);
+  const int seg = MAIN ? sg : sg + 1;
   const int64_t unit = (int64_t)b * k.heads + h;
   const int c0 = seg * k.seg_chunks, c1 = min(c0 + k.seg_chunks, k.nchunks);
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
@@ -482,11 +484,23 @@ __device__ __forceinline__ void gprep_walk(const BwdK& k, int pid, int total) {
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Ah2 = k.A[h] * kLog2e;
   const int tile0 = wave * TPW;
-  const bool owns = NTILE >= kBWaves || tile0 < NTILE;  // every wave when tiles >= waves
+  const bool owns = NTILE >= kBWaves * TPW || tile0 < NTILE;  // known true when every wave owns
   const int nt = tile0 / TP, pt0 = tile0 % TP;
   f32x4 gacc[TPW];
+  {
+    const float* gin = !MAIN                 ? nullptr
+                       : seg + 1 < k.nseg ? k.seg_g + (unit * k.nseg + seg + 1) * (P * N)
+                       : k.dhT             ? k.dhT + ((int64_t)b * k.n_heads + h) * (P * N)
+                                           : nullptr;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) gacc[t] = f32x4{0, 0, 0, 0};
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        gacc[t][i] = (gin && owns) ? gin[prow(pt0 + t, g * 4 + i) * N + nt * 16 + r16] : 0.0f;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) gacc[t] = opaque(gacc[t]);
+  }
+  T* __restrict__ Gst = static_cast<T*>(k.gst) + unit * k.nchunks * (P * N);
   float lam_seg = 0.0f;
   // As in the forward state walk: dy, C rows and dt of the chunk two behind
   // (in walk order) are loaded while this chunk runs, into two register sets
@@ -514,6 +528,14 @@ __device__ __forceinline__ void gprep_walk(const BwdK& k, int pid, int total) {
   auto step = [&](int c, auto set) {
     constexpr int S = decltype(set)::value;
     const int len = plen[S];
+    // Gc of this chunk, n-major: a tile pair's accumulators are eight
+    // consecutive d_head rows
+    if (MAIN && owns) {
+      T* dst = Gst + (int64_t)c * (P * N);
+#pragma unroll
+      for (int t = 0; t < TPW; t += 2)
+        store8(dst + (nt * 16 + r16) * P + ((pt0 + t) / 2) * 32 + g * 8, gacc[t], gacc[t + 1]);
+    }
 #pragma unroll
     for (int v = 0; v < NYV; ++v) {
       const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
@@ -562,7 +584,7 @@ __device__ __forceinline__ void gprep_walk(const BwdK& k, int pid, int total) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
           Frag8<T> yf;
-          frag_load8(yf, YT + ((pt0 + t) * 16 + r16) * TQ + tq);
+          frag_load8(yf, YT + prow(pt0 + t, r16) * TQ + tq);
           gacc[t] = mma(yf, cf, gacc[t]);
         }
       }
@@ -581,13 +603,24 @@ __device__ __forceinline__ void gprep_walk(const BwdK& k, int pid, int total) {
     step(c - 1, S1{});
   }
   if (c >= c0) step(c, S0{});
-  float* dst = k.seg_g + (unit * k.nseg + seg) * (P * N);
-  if (owns)
+  if (!MAIN) {
+    float* dst = k.seg_g + (unit * k.nseg + seg) * (P * N);
+    if (owns)
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[prow(pt0 + t, g * 4 + i) * N + nt * 16 + r16] = gacc[t][i];
+    if (tid == 0) k.seg_gd[unit * k.nseg + seg] = lam_seg;
+  } else if (seg == 0 && k.dh0 && owns) {
+    float* dst = k.dh0 + ((int64_t)b * k.n_heads + h) * (P * N);
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[((pt0 + t) * 16 + g * 4 + i) * N + nt * 16 + r16] = gacc[t][i];
-  if (tid == 0) k.seg_gd[unit * k.nseg + seg] = lam_seg;
+      for (int i = 0; i < 4; ++i) {
+        float* q = dst + prow(pt0 + t, g * 4 + i) * N + nt * 16 + r16;
+        *q = k.accumulate ? *q + gacc[t][i] : gacc[t][i];
+      }
+  }
 }
 
 // Both prepasses of the sequence split in one launch: they are independent
@@ -597,7 +630,17 @@ template <typename T, int P, int N>
 __global__ __launch_bounds__(kBThreads) void bwd_prepass_kernel(BwdK k) {
   const int half = gridDim.x / 2;
   if ((int)blockIdx.x < half) state_walk<T, P, N, true>(k, blockIdx.x, half);
-  else gprep_walk<T, P, N>(k, blockIdx.x - half, half);
+  else gprep_walk<T, P, N, false>(k, blockIdx.x - half, half);
+}
+
+// Both walks of the call in one launch, independent of each other:
+// workgroups [0, total/2) walk forward storing the state before every chunk,
+// the rest walk backwards storing dL/dH at the end of every chunk.
+template <typename T, int P, int N>
+__global__ __launch_bounds__(kBThreads) void bwd_walks_kernel(BwdK k) {
+  const int half = gridDim.x / 2;
+  if ((int)blockIdx.x < half) state_walk<T, P, N, false>(k, blockIdx.x, half);
+  else gprep_walk<T, P, N, true>(k, blockIdx.x - half, half);
 }
 
 // Chains the segments of every unit, one thread per state element.
@@ -639,7 +682,8 @@ struct ChunkLds {
   static constexpr int QP = kBQ + bpad<T>();  // M, K, Kd rows
   static constexpr size_t elems = (size_t)2 * kBQ * NP + (size_t)2 * kBQ * NN + (size_t)N * TP2 +
                                   (size_t)P * N + (size_t)3 * kBQ * QP;
-  static constexpr int kFloats = 4 * kBQ + 2 * 4 * kBQ + 3 * 4 * kBQ + 2 * kCWaves;
+  static constexpr int kHeadFloats = 4 * kBQ + 2 * 4 * kBQ + 3 * 4 * kBQ + 2 * kCWaves;
+  static constexpr int kFloats = 2 * kHeadFloats;  // by head parity
   static constexpr size_t bytes = elems * sizeof(T) + kFloats * sizeof(float);
 };
 
@@ -710,22 +754,27 @@ __device__ __forceinline__ void buffer_store_elem(__amdgpu_buffer_rsrc_t r, uint
   }
 }
 
-// ACC: add into the caller's dx and ddt (else overwrite them).
+// ACC: add into the caller's dx, ddt, dB and dC (else overwrite them).
 //
-// One workgroup of 16 waves walks the chunks of one (sequence, head) (or
-// segment) backwards with dL/dH in accumulators.  Per chunk, after staging:
-//  phase 1: the Q x Q blocks on and below the diagonal, once each (waves
-//    0-9, one 16 x 16 block each): C_t . B_s and dy_t . x_s, the masked decay,
-//    and from them M = G dec, K = Q dec (both [s][t]) and Kd = K dt_s ([t][s])
-//    in LDS plus the row and column sums of W; every wave: its dL/dH tile
-//    pair (decay, + dy^T exp(Lambda) C, then <dGp, Hp> for the chunk before),
-//    its u tile's end-state term exp(Lambda_e - Lambda_s) B_s Gc^T, its dB
-//    tiles' exp(..) x_s Gc and its dC tiles' exp(Lambda_t) dy_t Hp;
-//  phase 2: the causal products u += M dy, dB += K C, dC += Kd B into the
-//    same accumulators, then dx, the dB and dC atomics;
+// One workgroup of 16 waves per (sequence, chunk) loops over the heads; the
+// walks have stored, per head, the state before the chunk (Hp) and dL/dH at
+// its end (Gc).  Once per chunk: the B and C rows are staged and the Q x Q
+// blocks of B_s . C_t on and below the diagonal formed (waves 0-9, one
+// 16 x 16 block each, kept in registers: they do not depend on the head).
+// Per head, after staging its x, dy, dt, Hp and Gc:
+//  phase 1: dy_t . x_s on the same blocks, the masked decay, and from them
+//    M = G dec, K = Q dec (both [s][t]) and Kd = K dt_s ([t][s]) in LDS with
+//    the row and column sums of W; the wave's u tile's end-state term
+//    exp(Lambda_e - Lambda_s) B_s Gc^T, its dB tiles' exp(..) x_s Gc, its dC
+//    tiles' exp(Lambda_t) dy_t Hp, and part of <Gc, Hp>;
+//  phase 2: u += M dy, dB += K C, dC += Kd B; dx; dB and dC added to their
+//    sums over the heads (registers);
 //  tail (wave 0): dLambda from the partial sums, its suffix sum, ddt, dA.
-// Every partial sum is written by one wave and summed in a fixed order, so
-// the results do not depend on wave timing.
+// The chunk's end state is H_e = exp(Lambda_e) Hp + sum_s exp(Lambda_e -
+// Lambda_s) dt_s x_s B_s^T, so <Gc, H_e> = exp(Lambda_e) <Gc, Hp> + the sum
+// over s of the end-state dLambda terms.  dB and dC are written once per
+// chunk after the loop: no atomics.  Every partial sum is written by one
+// wave and summed in a fixed order: the results do not depend on timing.
 template <typename T, int P, int N, bool ACC>
 __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
   using L = ChunkLds<T, P, N>;
@@ -741,14 +790,14 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
   constexpr int NU = NBLK * TP, UPW = (NU + kCWaves - 1) / kCWaves;  // u tiles, per wave
   constexpr int ND = NBLK * TN, DPW = (ND + kCWaves - 1) / kCWaves;  // dB (and dC) tiles, per wave
   static_assert(UPW == 1 && TN % DPW == 0, "one u tile per wave; a wave's dB tiles share a block");
-  constexpr int NQ = TN / DPW;       // dB / dC partials per 16-token block
-  constexpr int NGP = (TP / 2) * TN;  // dL/dH tile pairs
-  static_assert(NGP <= kCWaves, "at most one dL/dH tile pair per wave");
+  constexpr int NQ = TN / DPW;                 // dB / dC partials per 16-token block
+  constexpr int NFR = (P / 32) * TN;           // state fragments (for <Gc, Hp>)
+  static_assert(NFR <= kCWaves, "at most one state fragment per wave");
   constexpr int NQQ = NBLK * (NBLK + 1) / 2;  // Q x Q blocks on and below the diagonal
   static_assert(NQQ <= kCWaves, "one Q x Q block per wave");
   constexpr int NXY = (2 * Q * (P / VB) + kCThreads - 1) / kCThreads;  // x, dy vectors per thread
   constexpr int NBC = (2 * Q * (N / VB) + kCThreads - 1) / kCThreads;  // B, C vectors per thread
-  constexpr int NHV = (P * (N / VB) + kCThreads - 1) / kCThreads;      // Hp vectors per thread
+  constexpr int NHV = (P * (N / VB) + kCThreads - 1) / kCThreads;      // Hp (and Gc) vectors per thread
 
   extern __shared__ __align__(16) unsigned char smem[];
   T* Xn = reinterpret_cast<T*>(smem);  // [Q][NP]
@@ -760,132 +809,192 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
   T* Mq = HpF + P * N;                 // M [s][t]
   T* Kq = Mq + Q * QP;                 // K [s][t]
   T* Kd = Kq + Q * QP;                 // K dt_s, [t][s]
-  float* lam = reinterpret_cast<float*>(Kd + Q * QP);  // log2-scaled Lambda
-  float* dtv = lam + Q;
-  float* eL = dtv + Q;      // exp(Lambda_t)
-  float* sc = eL + Q;       // exp(Lambda_e - Lambda_s)
-  float* rpart = sc + Q;    // [sb][t]: sum over s in block sb of W[t][s]
-  float* cpart = rpart + NBLK * Q;  // [tb][s]: sum over t in block tb of W[t][s]
-  float* t1p = cpart + NBLK * Q;    // [q][t]: exp(Lambda_t) dy_t . Hp C_t over d_state part q
-  float* esp = t1p + 4 * Q;         // [q][s]: dt_s exp(..) x_s^T Gc B_s over d_state part q
-  float* expl = esp + 4 * Q;        // [pt][s]: x_s . u_s over d_head tile pt
-  float* hgw = expl + 4 * Q;        // [2][16]: <Gc, H_e> per wave, by chunk parity
+  // Per-head values, two sets by head parity: the tail of a head runs
+  // during phase 1 of the next one.
+  float* const fbase = reinterpret_cast<float*>(Kd + Q * QP);
+  struct HeadF {
+    float *lam, *dtv, *eL, *sc, *rpart, *cpart, *t1p, *esp, *expl, *hgw, *ddw;
+  };
+  auto head_floats = [&](int parity) {
+    HeadF f;
+    f.lam = fbase + parity * L::kHeadFloats;  // log2-scaled Lambda
+    f.dtv = f.lam + Q;
+    f.eL = f.dtv + Q;              // exp(Lambda_t)
+    f.sc = f.eL + Q;               // exp(Lambda_e - Lambda_s)
+    f.rpart = f.sc + Q;            // [sb][t]: sum over s in block sb of W[t][s]
+    f.cpart = f.rpart + NBLK * Q;  // [tb][s]: sum over t in block tb of W[t][s]
+    f.t1p = f.cpart + NBLK * Q;    // [q][t]: exp(Lambda_t) dy_t . Hp C_t over d_state part q
+    f.esp = f.t1p + 4 * Q;         // [q][s]: dt_s exp(..) x_s^T Gc B_s over d_state part q
+    f.expl = f.esp + 4 * Q;        // [pt][s]: x_s . u_s over d_head tile pt
+    f.hgw = f.expl + 4 * Q;        // [16]: <Gc, Hp> per wave
+    f.ddw = f.hgw + kCWaves;       // [16]: dy . x per wave
+    return f;
+  };
 
-  int b, h, seg;
-  unit_of(k.heads, k.nseg, &b, &h, &seg);
-  const int64_t unit = (int64_t)b * k.heads + h;
-  const int c0 = seg * k.seg_chunks, c1 = min(c0 + k.seg_chunks, k.nchunks);
+  const int c = (int)(blockIdx.x % (unsigned)k.nchunks), b = (int)(blockIdx.x / (unsigned)k.nchunks);
+  const int64_t row0 = (int64_t)b * k.seqlen + (int64_t)c * Q;
+  const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int r16 = lane % 16, g = lane / 16;
   const T* __restrict__ Xp = static_cast<const T*>(k.x);
   const T* __restrict__ DTp = static_cast<const T*>(k.dt);
-  const T* __restrict__ Bp = static_cast<const T*>(k.B);
-  const T* __restrict__ Cp = static_cast<const T*>(k.C);
   const T* __restrict__ DYp = static_cast<const T*>(k.dy);
   T* __restrict__ DXp = static_cast<T*>(k.dx);
   T* __restrict__ DDTp = static_cast<T*>(k.ddt);
-  const T* __restrict__ Hst = static_cast<const T*>(k.hst) + unit * (k.nchunks + 1) * (P * N);
-  const int64_t rowb = (int64_t)b * k.seqlen;
-  const float Ah = k.A[h];
-  const float Ah2 = Ah * kLog2e;
-  const float Dh = k.D ? k.D[h] : 0.0f;
+  const int64_t ubase = (int64_t)b * k.heads;  // unit of head 0 of this sequence
 
   // this wave's tiles (wave-uniform; known when the tiles divide evenly)
-  const bool gown = NGP >= kCWaves || wave < NGP;  // dL/dH pair: n tile gnt, d_head tiles 2gpr, 2gpr+1
-  const int gnt = wave / (TP / 2), gpr = wave % (TP / 2);
-  const bool uown = NU >= kCWaves || wave < NU;    // u tile: s block usb, d_head tile upt
+  const bool uown = NU >= kCWaves || wave < NU;  // u tile: s block usb, d_head tile upt
   const int usb = wave / TP, upt = wave % TP;
   const bool down = ND >= kCWaves * DPW || wave * DPW < ND;  // dB, dC tiles: block dsb, n tiles dnt0 + j
   const int dsb = (wave * DPW) / TN, dnt0 = (wave * DPW) % TN, dq = dnt0 / DPW;
 
-  f32x4 gacc[2];
-  {
-    // dL/dH at the end of this walk: the final state's cotangent, or (split
-    // sequence) the combined gradient at the end of this segment
-    const float* gin = seg + 1 < k.nseg ? k.seg_g + (unit * k.nseg + seg + 1) * (P * N)
-                       : k.dhT          ? k.dhT + ((int64_t)b * k.n_heads + h) * (P * N)
-                                        : nullptr;
+  // ---- once per chunk: B and C rows (zero past len); M, K, Kd zeroed (the
+  // blocks above the diagonal are never written) ----
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        gacc[t][i] = (gin && gown) ? gin[prow(2 * gpr + t, g * 4 + i) * N + gnt * 16 + r16] : 0.0f;
-  }
-  // <Gc, H_e> of the last chunk: Gc = dL/dh_final, H_e = the final state;
-  // for every other chunk it is formed at the end of the chunk after it,
-  // from that chunk's start state (the accumulators of a tile pair and a
-  // stored state fragment hold the same elements in the same slots)
-  {
-    const int cl = c1 - 1;
-    float hdot = 0.0f;
-    if (gown) {
-      Frag8<T> hf;
-      frag_load8(hf, Hst + (int64_t)c1 * (P * N) + state_frag<N>(gpr, gnt, lane));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hdot += gacc[0][i] * to_f32(hf.v[i]) + gacc[1][i] * to_f32(hf.v[i + 4]);
+  for (int v = 0; v < NBC; ++v) {
+    const int idx = tid + v * kCThreads;
+    const int which = idx / (Q * (N / VB)), r = idx % (Q * (N / VB));
+    const int s = r % Q, n0 = (r / Q) * VB;
+    if (idx < 2 * Q * (N / VB)) {
+      const T* src = static_cast<const T*>(which ? k.C : k.B) + (row0 + min(s, len - 1)) * (which ? k.cs : k.bs);
+      const Vec16<T> bv = load16(src + n0);
+      store16((which ? Cn : Bn) + s * NN + n0, s < len ? bv : zero16<T>());
     }
-    hdot = wave_sum(hdot);
-    if (lane == 0) hgw[(cl & 1) * kCWaves + wave] = hdot;
   }
-  // M, K, Kd above the diagonal blocks are never written: zero them once
   for (int i = tid; i < 3 * Q * QP; i += kCThreads) Mq[i] = from_f32<T>(0.0f);
+  __syncthreads();
+  // this wave's Q x Q block (sb, tb), tb >= sb: lane slot i is s = sb*16 + 4g + i,
+  // t = tb*16 + r16; gq = B_s . C_t
+  int qsb = 0, qtb = wave < NQQ ? wave : 0;
+  while (qtb >= NBLK - qsb) {
+    qtb -= NBLK - qsb;
+    ++qsb;
+  }
+  qtb += qsb;
+  f32x4 gq = {0, 0, 0, 0};
+  if (wave < NQQ) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      Frag8<T> bs, ct;
+      frag_row(bs, Bn + (qsb * 16 + r16) * NN, kb * 32 + g * 8, N);
+      frag_row(ct, Cn + (qtb * 16 + r16) * NN, kb * 32 + g * 8, N);
+      gq = mma(bs, ct, gq);
+    }
+  }
 
-  // Global rows of a chunk and its start state, into registers (all issued
-  // before any is used): loaded during the chunk before it in the walk.
-  Vec16<T> vxy[NXY], vbc[NBC], vh[NHV];
+  // Per-head rows (x, dy), dt, Hp and Gc into registers (all issued before
+  // any is used): loaded during the head before.
+  Vec16<T> vxy[NXY], vh[NHV], vg[NHV];
   float pdt = 0.0f;
-  auto load_rows = [&](int c, int tid, int lane) {
-    const int64_t row0 = rowb + (int64_t)c * Q;
-    const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
-    // unconditional loads at clamped addresses; rows past len are zeroed at staging
+  auto load_head = [&](int hh, int tid, int lane) {
+    const int64_t unit = ubase + hh;
 #pragma unroll
     for (int v = 0; v < NXY; ++v) {
       const int idx = min(tid + v * kCThreads, 2 * Q * (P / VB) - 1);
       const int which = idx / (Q * (P / VB)), r = idx % (Q * (P / VB));
       const int s = min(r % Q, len - 1), p0 = (r / Q) * VB;
       const T* src = which ? DYp + (row0 + s) * k.dys : Xp + (row0 + s) * k.xs;
-      vxy[v] = load16(src + (int64_t)h * P + p0);
+      vxy[v] = load16(src + (int64_t)hh * P + p0);
     }
+    // dt: wave 0 only (the other waves' range is empty); tokens past len read 0
+    pdt = buffer_elem<T>(uniform_rsrc(DTp + row0 * k.dts + hh, wave == 0 ? (uint32_t)(len * k.dts * sizeof(T)) : 0u),
+                         (uint32_t)(lane * k.dts * sizeof(T)));
+    const T* hp = static_cast<const T*>(k.hst) + (unit * (k.nchunks + 1) + c) * (P * N);
+    const T* gp = static_cast<const T*>(k.gst) + (unit * k.nchunks + c) * (P * N);
 #pragma unroll
-    for (int v = 0; v < NBC; ++v) {
-      const int idx = min(tid + v * kCThreads, 2 * Q * (N / VB) - 1);
-      const int which = idx / (Q * (N / VB)), r = idx % (Q * (N / VB));
-      const int s = min(r % Q, len - 1), n0 = (r / Q) * VB;
-      const T* src = which ? Cp + (row0 + s) * k.cs : Bp + (row0 + s) * k.bs;
-      vbc[v] = load16(src + n0);
+    for (int v = 0; v < NHV; ++v) {
+      const int idx = min(tid + v * kCThreads, P * (N / VB) - 1) * VB;
+      vh[v] = load16(hp + idx);
+      vg[v] = load16(gp + idx);
     }
-    pdt = to_f32(DTp[(row0 + min(lane, len - 1)) * k.dts + h]);
-    const T* hp = Hst + (int64_t)c * (P * N);
-#pragma unroll
-    for (int v = 0; v < NHV; ++v) vh[v] = load16(hp + min(tid + v * kCThreads, P * (N / VB) - 1) * VB);
   };
-  float da_acc = 0.0f;  // wave 0: sum_r dt_r da_r of this lane's tokens
-  float dd_acc = 0.0f;  // sum dy . x over this lane's entries
+  f32x4 abt[DPW], act[DPW];  // dB, dC summed over the heads
+#pragma unroll
+  for (int j = 0; j < DPW; ++j) abt[j] = act[j] = f32x4{0, 0, 0, 0};
 
   const int tid_o = tid;
-  load_rows(c1 - 1, opaque(tid_o), opaque(tid_o) % 64);
-  // Every chunk issues its stores and atomics after the next chunk's loads,
-  // and the staging waits for those loads with the stores still in flight.
-  // The loop is entered with nothing issued after the first loads; the
-  // compiler merges the two entries and would wait for every store.  So the
-  // entry issues as many memory operations after them: stores through an
-  // empty range, which the hardware drops.
+  load_head(0, opaque(tid_o), opaque(tid_o) % 64);
+  // Every head issues its stores after the next head's loads, and the
+  // staging waits for those loads with the stores still in flight.  The loop
+  // is entered with nothing issued after the first loads; the compiler merges
+  // the two entries and would wait for every store.  So the entry issues as
+  // many memory operations after them: stores through an empty range, which
+  // the hardware drops.
   {
-    constexpr int kOps = (ACC ? 8 : 4) * UPW + 8 * DPW + (ACC ? 2 : 1);
-    const auto none = uniform_rsrc(k.dB, 0u);
+    constexpr int kOps = (ACC ? 8 : 4) * UPW + (ACC ? 2 : 1) + 2;
+    const auto none = uniform_rsrc(k.dA, 0u);
 #pragma unroll
     for (int i = 0; i < kOps; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, 0);
   }
-  for (int c = c1 - 1; c >= c0; --c) {
-    const int64_t row0 = rowb + (int64_t)c * Q;
-    const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
-    // The lane indices, re-derived every chunk from an opaque copy: the LDS
-    // and global addresses built from them are then formed inside the loop
-    // rather than hoisted out of it and held across the walk.
-    const int tid = opaque(tid_o), lane = tid % 64, r16 = lane % 16, g = lane / 16;
+  // outputs of this chunk through buffer resources over its rows: lanes at
+  // rows past len fall outside the range and are dropped, so no store sits
+  // under a lane condition (which would make every later wait for a load
+  // also wait for all earlier stores)
+  const auto rdb = uniform_rsrc(k.dB + row0 * k.dbs, (uint32_t)(len * k.dbs * sizeof(float)));
+  const auto rdc = uniform_rsrc(k.dC + row0 * k.dcs, (uint32_t)(len * k.dcs * sizeof(float)));
+  const auto rdA = uniform_rsrc(k.dA, (uint32_t)(k.n_heads * sizeof(float)));
+  const auto rdD = uniform_rsrc(k.dD, k.dD ? (uint32_t)(k.n_heads * sizeof(float)) : 0u);
 
-    // ---- stage: the chunk's rows (loaded during the chunk before) into
-    // LDS token-major, zero past len; its start state as stored; Gc n-major ----
+  // ---- tail of head th (one wave): dLambda -> da (suffix sum) -> ddt, dA, dD ----
+  auto run_tail = [&](int th, int lane) {
+    const HeadF F = head_floats(th & 1);
+    const float Ah = k.A[th];
+    {
+      const int t = lane, tb = t / 16;
+      // fixed summation order: the result does not depend on wave timing
+      float t1 = 0.0f, es = 0.0f;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        t1 += F.t1p[q * Q + t];
+        es += F.esp[q * Q + t];
+      }
+      float dl = t1 - es;
+#pragma unroll
+      for (int sb = 0; sb < NBLK; ++sb) dl += sb <= tb ? F.rpart[sb * Q + t] : 0.0f;
+#pragma unroll
+      for (int b2 = 0; b2 < NBLK; ++b2) dl -= b2 >= tb ? F.cpart[b2 * Q + t] : 0.0f;
+      // <Gc, H_e> at the chunk's last token
+      float hp = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NFR; ++j) hp += F.hgw[j];
+      const float hg = F.eL[Q - 1] * hp + wave_sum(es);
+      if (t == Q - 1) dl += hg;
+      // suffix sum over t' >= t: the total minus the prefix before t
+      const float incl = wave_incl_scan(dl);
+      const float tot = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
+      const float suf = (tot - incl) + dl;
+      float xu = 0.0f;
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) xu += F.expl[pt * Q + t];
+      // ddt through a range over this chunk's rows (tokens past len dropped);
+      // dt is 0 past len, so dA takes nothing from them
+      const auto rdt = uniform_rsrc(DDTp + row0 * k.ddts + th, (uint32_t)(len * k.ddts * sizeof(T)));
+      const uint32_t off = (uint32_t)(t * k.ddts * sizeof(T));
+      const float old = ACC ? buffer_elem<T>(rdt, off) : 0.0f;
+      buffer_store_elem<T>(rdt, off, old + xu + Ah * suf);
+      const float da = wave_sum(F.dtv[t] * suf);
+      float ddh = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kCWaves; ++j) ddh += F.ddw[j];
+      // one lane adds each (offsets of the others lie outside the ranges)
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(da, rdA, lane == 0 ? th * 4 : 0x7ffffff0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(ddh, rdD, lane == 0 ? th * 4 : 0x7ffffff0, 0, 0);
+    }
+  };
+
+  for (int hh = 0; hh < k.heads; ++hh) {
+    // The lane indices, re-derived every head from an opaque copy: the LDS
+    // and global addresses built from them are then formed inside the loop
+    // rather than hoisted out of it and held across it.
+    const int tid = opaque(tid_o), lane = tid % 64, r16 = lane % 16, g = lane / 16;
+    const float Ah = k.A[hh];
+    const float Dh = k.D ? k.D[hh] : 0.0f;
+    const HeadF F = head_floats(hh & 1);
+
+    // ---- stage this head: x, dy rows token-major (zero past len), Hp as
+    // stored, Gc n-major; wave 0: Lambda and its factors ----
     const float dtl = lane < len ? pdt : 0.0f;
 #pragma unroll
     for (int v = 0; v < NXY; ++v) {
@@ -896,60 +1005,43 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
       if (idx < 2 * Q * (P / VB)) store16((which ? Yn : Xn) + s * NP + p0, xv);
     }
 #pragma unroll
-    for (int v = 0; v < NBC; ++v) {
+    for (int v = 0; v < NHV; ++v) {
       const int idx = tid + v * kCThreads;
-      const int which = idx / (Q * (N / VB)), r = idx % (Q * (N / VB));
-      const int s = r % Q, n0 = (r / Q) * VB;
-      const Vec16<T> bv = s < len ? vbc[v] : zero16<T>();
-      if (idx < 2 * Q * (N / VB)) store16((which ? Cn : Bn) + s * NN + n0, bv);
+      if (idx < P * (N / VB)) {
+        store16(HpF + idx * VB, vh[v]);
+        store16(GT + (idx / (P / VB)) * TP2 + (idx % (P / VB)) * VB, vg[v]);
+      }
     }
-#pragma unroll
-    for (int v = 0; v < NHV; ++v)
-      if (tid + v * kCThreads < P * (N / VB)) store16(HpF + (tid + v * kCThreads) * VB, vh[v]);
-    // Gc^T: a tile pair's accumulators are eight consecutive d_head rows
-    if (gown) store8(GT + (gnt * 16 + r16) * TP2 + gpr * 32 + g * 8, gacc[0], gacc[1]);
     if (wave == 0) {
-      const float lv = chunk_cumsum(dtl * Ah2, lane);
+      const float lv = chunk_cumsum(dtl * Ah * kLog2e, lane);
       const float le = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), 63));
-      lam[lane] = lv;
-      dtv[lane] = dtl;
-      eL[lane] = __builtin_amdgcn_exp2f(lv);
-      sc[lane] = __builtin_amdgcn_exp2f(le - lv);
+      F.lam[lane] = lv;
+      F.dtv[lane] = dtl;
+      F.eL[lane] = __builtin_amdgcn_exp2f(lv);
+      F.sc[lane] = __builtin_amdgcn_exp2f(le - lv);
     }
     __syncthreads();
-    // the next chunk in the walk (this one again at the segment's start),
-    // in flight while this one is computed
-    load_rows(max(c - 1, c0), tid, lane);
+    // the next head's inputs (this one's again at the last), in flight
+    // while this one is computed
+    load_head(min(hh + 1, k.heads - 1), tid, lane);
 
     // ================= phase 1 =================
-    // ---- one Q x Q block (sb, tb), tb >= sb: lane slot i is s = sb*16 + 4g + i,
-    // t = tb*16 + r16 ----
+    // the previous head's tail, on a wave without a Q x Q block
+    if (wave == kCWaves - 1 && hh > 0) run_tail(hh - 1, lane);
+    // ---- the wave's Q x Q block: x_s . dy_t, masked decay, M, K, Kd, W sums ----
     if (wave < NQQ) {
-      int sb = 0, tb = wave;
-      while (tb >= NBLK - sb) {
-        tb -= NBLK - sb;
-        ++sb;
-      }
-      tb += sb;
-      f32x4 gq = {0, 0, 0, 0}, qq = {0, 0, 0, 0};
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        Frag8<T> bs, ct;
-        frag_row(bs, Bn + (sb * 16 + r16) * NN, kb * 32 + g * 8, N);
-        frag_row(ct, Cn + (tb * 16 + r16) * NN, kb * 32 + g * 8, N);
-        gq = mma(bs, ct, gq);  // B_s . C_t
-      }
+      f32x4 qq = {0, 0, 0, 0};
 #pragma unroll
       for (int kp = 0; kp < PKB; ++kp) {
         Frag8<T> xs, yt;
-        frag_load8(xs, Xn + (sb * 16 + r16) * NP + kp * 32 + g * 8);
-        frag_load8(yt, Yn + (tb * 16 + r16) * NP + kp * 32 + g * 8);
-        qq = mma(xs, yt, qq);  // x_s . dy_t
+        frag_load8(xs, Xn + (qsb * 16 + r16) * NP + kp * 32 + g * 8);
+        frag_load8(yt, Yn + (qtb * 16 + r16) * NP + kp * 32 + g * 8);
+        qq = mma(xs, yt, qq);
       }
-      const int t = tb * 16 + r16, s4 = sb * 16 + g * 4;
-      const float lam_t = lam[t];
-      const f32x4 lam_s = *reinterpret_cast<const f32x4*>(lam + s4);
-      const f32x4 dt_s = *reinterpret_cast<const f32x4*>(dtv + s4);
+      const int t = qtb * 16 + r16, s4 = qsb * 16 + g * 4;
+      const float lam_t = F.lam[t];
+      const f32x4 lam_s = *reinterpret_cast<const f32x4*>(F.lam + s4);
+      const f32x4 dt_s = *reinterpret_cast<const f32x4*>(F.dtv + s4);
       float w[4], kd[4], rs = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -965,53 +1057,26 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
       // row sums (over s, per t): over the 4 slots, then the 4 groups
       rs += xor_lane(rs, lane, 16);
       rs += xor_lane(rs, lane, 32);
-      if (g == 0) rpart[sb * Q + t] = rs;
+      if (g == 0) F.rpart[qsb * Q + t] = rs;
       // column sums (over t, per s): over the 16 lanes of each group
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[i] = row16_sum(w[i]);
       if (r16 == 0)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cpart[tb * Q + s4 + i] = w[i];
+        for (int i = 0; i < 4; ++i) F.cpart[qtb * Q + s4 + i] = w[i];
     }
-
-    // ---- dL/dH tile pair: dGp = exp(Lambda_e) Gc + sum_t exp(Lambda_t) dy_t C_t^T
-    // (A operand rows in the paired order of prow()), then <dGp, Hp> for the
-    // chunk before ----
-    if (gown) {
-      const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
+    // ---- <Gc, Hp> over the wave's state fragment (kp, nb) ----
+    if (NFR >= kCWaves || wave < NFR) {
+      const int kp = wave / TN, nb = wave % TN;
+      Frag8<T> hf, gf;
+      frag_load8(hf, HpF + state_frag<N>(kp, nb, lane));
+      frag_load8(gf, GT + (nb * 16 + r16) * TP2 + kp * 32 + g * 8);
+      float v = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gacc[t][i] *= dec;
-#pragma unroll
-      for (int ks = 0; ks < Q / 32; ++ks) {
-        const int tq = ks * 32 + g * 8;
-        const f32x4 e0 = *reinterpret_cast<const f32x4*>(eL + tq);
-        const f32x4 e1 = *reinterpret_cast<const f32x4*>(eL + tq + 4);
-        Frag8<T> cr, cf;
-        frag_cols(cr, Cn, NN, tq, tq + 4, gnt * 16, 4, lane);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) frag_set(cf, j, to_f32(cr.v[j]) * (j < 4 ? e0[j] : e1[j - 4]));
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          Frag8<T> yf;
-          frag_cols(yf, Yn, NP, tq, tq + 4, gpr * 32 + t * 4, 8, lane);
-          gacc[t] = mma(yf, cf, gacc[t]);
-        }
-      }
-      if (c > c0) {
-        Frag8<T> hd;
-        frag_load8(hd, HpF + state_frag<N>(gpr, gnt, lane));
-        float hdot = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hdot += gacc[0][i] * to_f32(hd.v[i]) + gacc[1][i] * to_f32(hd.v[i + 4]);
-        hdot = wave_sum(hdot);
-        // two halves by chunk parity: wave 0 reads chunk c's half in the
-        // tail while this writes chunk c-1's
-        if (lane == 0) hgw[((c - 1) & 1) * kCWaves + wave] = hdot;
-      }
+      for (int j = 0; j < 8; ++j) v += to_f32(hf.v[j]) * to_f32(gf.v[j]);
+      v = wave_sum(v);
+      if (lane == 0) F.hgw[wave] = v;
     }
-
     // ---- u tile (usb, upt): exp(Lambda_e - Lambda_s) B_s Gc^T ----
     f32x4 au = {0, 0, 0, 0};
     if (uown) {
@@ -1022,81 +1087,60 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
         frag_cols(gf, GT, TP2, kb * 32 + g * 8, kb * 32 + g * 8 + 4, upt * 16, 4, lane, kb * 32 + g * 8 < N);
         au = mma(bf, gf, au);
       }
-      const f32x4 s4 = *reinterpret_cast<const f32x4*>(sc + usb * 16 + g * 4);
+      const f32x4 s4 = *reinterpret_cast<const f32x4*>(F.sc + usb * 16 + g * 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) au[i] *= s4[i];
     }
-    // ---- dB tiles (dsb, dnt0 + j): exp(..) x_s Gc, and its part of esum ----
+    // ---- dB tiles (dsb, dnt0 + j): exp(..) x_s Gc, and its part of esum;
+    // dC tiles (same block index as t block): exp(Lambda_t) dy_t Hp, and its
+    // part of t1 ----
     f32x4 ab[DPW], ac[DPW];
 #pragma unroll
     for (int j = 0; j < DPW; ++j) ab[j] = ac[j] = f32x4{0, 0, 0, 0};
     if (down) {
 #pragma unroll
       for (int kp = 0; kp < PKB; ++kp) {
-        Frag8<T> xf;
+        Frag8<T> xf, yf;
         frag_load8(xf, Xn + (dsb * 16 + r16) * NP + kp * 32 + g * 8);
-#pragma unroll
-        for (int j = 0; j < DPW; ++j) {
-          Frag8<T> gf;
-          frag_load8(gf, GT + ((dnt0 + j) * 16 + r16) * TP2 + kp * 32 + g * 8);
-          ab[j] = mma(xf, gf, ab[j]);
-        }
-      }
-      const int s4 = dsb * 16 + g * 4;
-      const f32x4 scs = *reinterpret_cast<const f32x4*>(sc + s4);
-      const f32x4 dts = *reinterpret_cast<const f32x4*>(dtv + s4);
-      float e[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = 0.0f;
-#pragma unroll
-        for (int j = 0; j < DPW; ++j) {
-          ab[j][i] *= scs[i];
-          v += ab[j][i] * to_f32(Bn[(s4 + i) * NN + (dnt0 + j) * 16 + r16]);
-        }
-        e[i] = row16_sum(v) * dts[i];
-      }
-      if (r16 == 0)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) esp[dq * Q + s4 + i] = e[i];
-      // ---- dC tiles (same block index as t block, same n tiles):
-      // exp(Lambda_t) dy_t Hp, and its part of t1 ----
-#pragma unroll
-      for (int kp = 0; kp < PKB; ++kp) {
-        Frag8<T> yf;
         frag_load8(yf, Yn + (dsb * 16 + r16) * NP + kp * 32 + g * 8);
 #pragma unroll
         for (int j = 0; j < DPW; ++j) {
-          Frag8<T> hfr;
+          Frag8<T> gf, hfr;
+          frag_load8(gf, GT + ((dnt0 + j) * 16 + r16) * TP2 + kp * 32 + g * 8);
           frag_load8(hfr, HpF + state_frag<N>(kp, dnt0 + j, lane));
+          ab[j] = mma(xf, gf, ab[j]);
           ac[j] = mma(yf, hfr, ac[j]);
         }
       }
-      const f32x4 et = *reinterpret_cast<const f32x4*>(eL + s4);
+      const int s4 = dsb * 16 + g * 4;
+      const f32x4 scs = *reinterpret_cast<const f32x4*>(F.sc + s4);
+      const f32x4 dts = *reinterpret_cast<const f32x4*>(F.dtv + s4);
+      const f32x4 et = *reinterpret_cast<const f32x4*>(F.eL + s4);
+      float e[4], f[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float v = 0.0f;
+        float v = 0.0f, u = 0.0f;
 #pragma unroll
         for (int j = 0; j < DPW; ++j) {
+          ab[j][i] *= scs[i];
           ac[j][i] *= et[i];
-          v += ac[j][i] * to_f32(Cn[(s4 + i) * NN + (dnt0 + j) * 16 + r16]);
+          v += ab[j][i] * to_f32(Bn[(s4 + i) * NN + (dnt0 + j) * 16 + r16]);
+          u += ac[j][i] * to_f32(Cn[(s4 + i) * NN + (dnt0 + j) * 16 + r16]);
         }
-        e[i] = row16_sum(v);
+        e[i] = row16_sum(v) * dts[i];
+        f[i] = row16_sum(u);
       }
       if (r16 == 0)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) t1p[dq * Q + s4 + i] = e[i];
+        for (int i = 0; i < 4; ++i) {
+          F.esp[dq * Q + s4 + i] = e[i];
+          F.t1p[dq * Q + s4 + i] = f[i];
+        }
     }
     __syncthreads();
 
     // ================= phase 2 =================
-    // Outputs leave through buffer resources over this chunk's rows: lanes at
-    // rows past len fall outside the range and are dropped, so no store or
-    // atomic sits under a lane condition (which would make every later wait
-    // for a load also wait for all earlier stores).
-    const auto rdx = uniform_rsrc(DXp + row0 * k.dxs + (int64_t)h * P, (uint32_t)(len * k.dxs * sizeof(T)));
-    const auto rdb = uniform_rsrc(k.dB + row0 * k.dbs, (uint32_t)(len * k.dbs * sizeof(float)));
-    const auto rdc = uniform_rsrc(k.dC + row0 * k.dcs, (uint32_t)(len * k.dcs * sizeof(float)));
+    float dd = 0.0f;
     // ---- u += M dy over t >= s (K = t slices from the block's own) ----
     if (uown) {
 #pragma unroll 1
@@ -1107,8 +1151,9 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
         au = mma(mf, yf, au);
       }
       // dx = dt_s u + D dy; x_s . u_s over this d_head tile; dy . x
+      const auto rdx = uniform_rsrc(DXp + row0 * k.dxs + (int64_t)hh * P, (uint32_t)(len * k.dxs * sizeof(T)));
       const int s4 = usb * 16 + g * 4, p = upt * 16 + r16;
-      const f32x4 dts = *reinterpret_cast<const f32x4*>(dtv + s4);
+      const f32x4 dts = *reinterpret_cast<const f32x4*>(F.dtv + s4);
       float ex[4], dxv[4], old[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -1117,7 +1162,7 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
       for (int i = 0; i < 4; ++i) {
         const float xv = to_f32(Xn[(s4 + i) * NP + p]), yv = to_f32(Yn[(s4 + i) * NP + p]);
         ex[i] = xv * au[i];
-        dd_acc += xv * yv;
+        dd += xv * yv;
         dxv[i] = dts[i] * au[i] + Dh * yv;
       }
 #pragma unroll
@@ -1127,10 +1172,12 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
       for (int i = 0; i < 4; ++i) ex[i] = row16_sum(ex[i]);
       if (r16 == 0)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) expl[upt * Q + s4 + i] = ex[i];
+        for (int i = 0; i < 4; ++i) F.expl[upt * Q + s4 + i] = ex[i];
     }
+    dd = wave_sum(dd);
+    if (lane == 0) F.ddw[wave] = dd;
     if (down) {
-      // ---- dB += K C over t >= s; dB = dt_s (...) ----
+      // ---- dB += K C over t >= s; dB summed over heads with dt_s ----
 #pragma unroll 1
       for (int ks = dsb / 2; ks < Q / 32; ++ks) {
         Frag8<T> kf;
@@ -1154,96 +1201,45 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
           ac[j] = mma(kf, bf, ac[j]);
         }
       }
-      const int s4 = dsb * 16 + g * 4;
-      const f32x4 dts = *reinterpret_cast<const f32x4*>(dtv + s4);
+      const f32x4 dts = *reinterpret_cast<const f32x4*>(F.dtv + dsb * 16 + g * 4);
 #pragma unroll
       for (int j = 0; j < DPW; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int col = (dnt0 + j) * 16 + r16;
-          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
-              dts[i] * ab[j][i], rdb, (int)(((s4 + i) * k.dbs + col) * sizeof(float)), 0, 0);
-          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
-              ac[j][i], rdc, (int)(((s4 + i) * k.dcs + col) * sizeof(float)), 0, 0);
+          abt[j][i] += dts[i] * ab[j][i];
+          act[j][i] += ac[j][i];
         }
     }
     __syncthreads();
 
-    // ---- tail (wave 0): dLambda -> da (suffix sum) -> ddt, dA ----
-    if (wave == 0) {
-      const int t = lane, tb = t / 16;
-      // fixed summation order: the result does not depend on wave timing
-      float dl = 0.0f;
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) dl += t1p[q * Q + t] - esp[q * Q + t];
-#pragma unroll
-      for (int sb = 0; sb < NBLK; ++sb) dl += sb <= tb ? rpart[sb * Q + t] : 0.0f;
-#pragma unroll
-      for (int b2 = 0; b2 < NBLK; ++b2) dl -= b2 >= tb ? cpart[b2 * Q + t] : 0.0f;
-      if (t == Q - 1) {
-        float hg = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NGP; ++j) hg += hgw[(c & 1) * kCWaves + j];
-        dl += hg;
-      }
-      // suffix sum over t' >= t: the total minus the prefix before t
-      const float incl = wave_incl_scan(dl);
-      const float tot = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
-      const float suf = (tot - incl) + dl;
-      float xu = 0.0f;
-#pragma unroll
-      for (int pt = 0; pt < TP; ++pt) xu += expl[pt * Q + t];
-      // ddt through a range over this chunk's rows (tokens past len dropped);
-      // dt is 0 past len, so da_acc takes nothing from them
-      const auto rdt = uniform_rsrc(DDTp + row0 * k.ddts + h, (uint32_t)(len * k.ddts * sizeof(T)));
-      const uint32_t off = (uint32_t)(t * k.ddts * sizeof(T));
-      const float old = ACC ? buffer_elem<T>(rdt, off) : 0.0f;
-      buffer_store_elem<T>(rdt, off, old + xu + Ah * suf);
-      da_acc += dtv[t] * suf;
-    }
-    // wave 0 rewrites lam/dtv/eL/sc only after its own reads above; every
-    // other array is rewritten after the next barrier
+    // (the tail of this head reads its values during the next head's phase 1;
+    // they are rewritten two heads later)
   }
 
-  // ---- per-unit results: dh0, dA, dD ----
-  if (k.dh0 && gown && seg == 0) {
-    // (lane indices re-derived here, as in the loop, so that these addresses
-    // are not formed before the walk and held across it)
-    const int ln = opaque(lane), r16 = ln % 16, g = ln / 16;
-    float* dst = k.dh0 + ((int64_t)b * k.n_heads + h) * (P * N);
+  if (wave == kCWaves - 1) run_tail(k.heads - 1, opaque(lane));
+
+  // ---- dB and dC of this chunk, summed over the heads ----
+  if (down) {
+    const int s4 = dsb * 16 + g * 4;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int j = 0; j < DPW; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float* q = dst + prow(2 * gpr + t, g * 4 + i) * N + gnt * 16 + r16;
-        *q = k.accumulate ? *q + gacc[t][i] : gacc[t][i];
+        const int col = (dnt0 + j) * 16 + r16;
+        const uint32_t ob = (uint32_t)(((s4 + i) * k.dbs + col) * sizeof(float));
+        const uint32_t oc = (uint32_t)(((s4 + i) * k.dcs + col) * sizeof(float));
+        const float pb = ACC ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdb, (int)ob, 0, 0)) : 0.0f;
+        const float pc = ACC ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdc, (int)oc, 0, 0)) : 0.0f;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pb + abt[j][i]), rdb, (int)ob, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pc + act[j][i]), rdc, (int)oc, 0, 0);
       }
-  }
-  if (wave == 0) {
-    da_acc = wave_sum(da_acc);
-    if (lane == 0) unsafeAtomicAdd(k.dA + h, da_acc);
-  }
-  if (k.dD) {
-    dd_acc = wave_sum(dd_acc);
-    if (lane == 0) unsafeAtomicAdd(k.dD + h, dd_acc);
   }
 }
 
-// The summed gradients set to zero in one launch: dB and dC (rows x width
-// fp32 values with their own row strides), dA and dD (heads values; dD may
-// be null).
-__global__ __launch_bounds__(256) void zero_grads_kernel(float* dB, int64_t dbs, float* dC, int64_t dcs,
-                                                         int width, int64_t rows, float* dA, float* dD,
-                                                         int heads) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < rows * width) {
-    const int64_t r = i / width;
-    const int col = (int)(i % width);
-    dB[r * dbs + col] = 0.0f;
-    dC[r * dcs + col] = 0.0f;
-  }
-  if (i < heads) {
+// dA and dD (heads values; dD may be null) set to zero: the only outputs the
+// calls add into from several workgroups.
+__global__ __launch_bounds__(64) void zero_heads_kernel(float* dA, float* dD, int heads) {
+  for (int i = threadIdx.x; i < heads; i += 64) {
     dA[i] = 0.0f;
     if (dD) dD[i] = 0.0f;
   }
@@ -1254,7 +1250,7 @@ hipError_t launch_shape(const BwdK& k, int64_t batch, hipStream_t s) {
   const unsigned units = (unsigned)(batch * k.heads);
   const size_t lds1 = StateLds<T, P, N>::bytes, lds2 = ChunkLds<T, P, N>::bytes;
   static_assert(ChunkLds<T, P, N>::bytes <= 160 * 1024, "chunk tiles fit one CU's LDS");
-  const void* fns[] = {reinterpret_cast<const void*>(&bwd_state_kernel<T, P, N>),
+  const void* fns[] = {reinterpret_cast<const void*>(&bwd_walks_kernel<T, P, N>),
                        reinterpret_cast<const void*>(&bwd_prepass_kernel<T, P, N>),
                        reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N, false>),
                        reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N, true>)};
@@ -1273,10 +1269,13 @@ hipError_t launch_shape(const BwdK& k, int64_t batch, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const unsigned grid = units * (unsigned)k.nseg;
-  hipLaunchKernelGGL((bwd_state_kernel<T, P, N>), dim3(grid), dim3(kBThreads), lds1, s, k);
+  // the two walks (states before each chunk, dL/dH after each), then the
+  // chunks in parallel
+  const unsigned walks = units * (unsigned)k.nseg;
+  hipLaunchKernelGGL((bwd_walks_kernel<T, P, N>), dim3(2 * walks), dim3(kBThreads), lds1, s, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)(batch * k.nchunks);
   if (k.accumulate)
     hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N, true>), dim3(grid), dim3(kCThreads), lds2, s, k);
   else
@@ -1315,7 +1314,7 @@ size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t
   bwd_plan(batch, seqlen, heads, &nc, &ns, &sc);
   const size_t el = dtype == MM_BF16 ? 2 : 4;
   const size_t units = (size_t)(batch * heads), pn = (size_t)(d_head * d_state);
-  size_t bytes = align256(units * (size_t)(nc + 1) * pn * el);
+  size_t bytes = align256(units * (size_t)(nc + 1) * pn * el) + align256(units * (size_t)nc * pn * el);
   if (ns > 1) bytes += 2 * align256(units * ns * pn * 4) + 2 * align256(units * ns * 4);
   return bytes;
 }
@@ -1358,6 +1357,8 @@ hipError_t launch_ssd_backward(const BwdArgs& a, void* workspace, hipStream_t s)
     unsigned char* w = static_cast<unsigned char*>(workspace);
     k.hst = w;
     w += align256(units * (size_t)(k.nchunks + 1) * pn * el);
+    k.gst = w;
+    w += align256(units * (size_t)k.nchunks * pn * el);
     k.seg_h = k.seg_g = k.seg_hd = k.seg_gd = nullptr;
     if (k.nseg > 1) {
       k.seg_h = reinterpret_cast<float*>(w);
@@ -1369,12 +1370,9 @@ hipError_t launch_ssd_backward(const BwdArgs& a, void* workspace, hipStream_t s)
       k.seg_gd = reinterpret_cast<float*>(w);
     }
   }
-  if (!a.accumulate) {
-    const int64_t rows = a.batch * a.seqlen;
-    const int64_t n = std::max<int64_t>(rows * a.d_state, a.heads);
-    hipLaunchKernelGGL(zero_grads_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.dB, a.dbs,
-                       a.dC, a.dcs, a.d_state, rows, a.dA, a.dD, a.heads);
-  }
+  // dB and dC are written whole by the chunk kernel; dA and dD are sums
+  // over workgroups
+  if (!a.accumulate) hipLaunchKernelGGL(zero_heads_kernel, dim3(1), dim3(64), 0, s, a.dA, a.dD, (int)a.heads);
   if (a.dtype == MM_BF16) {
     if (a.d_state == 128) return launch_shape<bf16, 64, 128>(k, a.batch, s);
     return launch_shape<bf16, 64, 64>(k, a.batch, s);
