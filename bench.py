@@ -51,9 +51,19 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILES = {"scan": os.path.join(ROOT, "profiles", "traffic_ssd_scan_1p4b_m2048.json"),
                  "fused": os.path.join(ROOT, "profiles", "traffic_fused_prefill_1p4b_m2048.json")}
+
+
+def traffic_file(which: str, workload: str = "1.4b", m: int = 0) -> str:
+    """Record of the measured HBM bytes of one scan (or fused) call of a
+    workload at width m (0 = the 1.4B full-width records above)."""
+    if not m or (workload == "1.4b" and m == 2048):
+        return TRAFFIC_FILES[which]
+    return os.path.join(ROOT, "profiles", f"traffic_ssd_scan_{workload.replace('.', 'p')}_m{m}.json")
 SCAN_SRCS = [os.path.join(ROOT, "selective_state_space_12_amd", "csrc", f)
              for f in ("ssd_fwd_bf16.hip", "device_common.h")]
-SCAN_KERNELS = ("tile_prep_kernel", "ssd_bf16_kernel")  # the two kernels of one call
+# the kernels of one call: tile prep, and with the sequences split the
+# state-only pass and the combine, then the scan (absent ones are skipped)
+SCAN_KERNELS = ("tile_prep_kernel", "ssd_bf16_seg_kernel", "seg_combine_bf16_kernel", "ssd_bf16_kernel")
 
 
 COPY_BYTES = 1 << 30
@@ -78,42 +88,51 @@ def _pmc_per_dispatch(dirname: str, counter: str, kernel_substr: str, min_grid: 
     return sum(vals.values()) / len(vals), len(vals)
 
 
-def summarize_pmc(which, scan_fetch, scan_write, copy_fetch, copy_write):
+def summarize_pmc(which, scan_fetch, scan_write, copy_fetch, copy_write, workload="1.4b", heads=0):
     """HBM bytes per scan call or fused prefill call (``which``: counter runs
-    of ``--mode scan`` / ``--mode fused``): FETCH_SIZE + WRITE_SIZE of its two
-    kernels (mean per dispatch of each, summed), each counter scaled by what
-    it reads for a copy of known size."""
+    of ``--mode scan`` / ``--mode fused``, with ``--workload`` / ``--heads``):
+    FETCH_SIZE + WRITE_SIZE of its kernels (mean per dispatch of each,
+    summed), each counter scaled by what it reads for a copy of known size."""
+    import synth
+    w = synth.WORKLOADS[workload]
+    h = heads or w.n_heads
+    m = next(mm for mm in w.slices if w.heads(mm) == h)
     sf = sw = 0.0
-    nsf, nsw = [], []
+    nsf, nsw, per = [], [], {}
     for kname in SCAN_KERNELS:
-        f1, n1 = _pmc_per_dispatch(scan_fetch, "FETCH_SIZE", kname)
-        w1, n2 = _pmc_per_dispatch(scan_write, "WRITE_SIZE", kname)
+        try:
+            f1, n1 = _pmc_per_dispatch(scan_fetch, "FETCH_SIZE", kname)
+            w1, n2 = _pmc_per_dispatch(scan_write, "WRITE_SIZE", kname)
+        except SystemExit:
+            continue
         sf += f1
         sw += w1
         nsf.append(n1)
         nsw.append(n2)
+        per[kname] = {"fetch_kib": f1, "write_kib": w1}
     # the calibration copy is the only large copy dispatch of its run
     cf, _ = _pmc_per_dispatch(copy_fetch, "FETCH_SIZE", "copyBuffer", min_grid=1 << 16)
     cw, _ = _pmc_per_dispatch(copy_write, "WRITE_SIZE", "copyBuffer", min_grid=1 << 16)
     kf = COPY_BYTES / (cf * 1024.0)
     kw = COPY_BYTES / (cw * 1024.0)
     total = sf * 1024.0 * kf + sw * 1024.0 * kw
-    import synth
-    w = synth.WORKLOADS["1.4b"]
-    alg = scan_bytes(w.batch * w.seqlen, w.n_heads, w.d_head, w.d_state, 2)
-    rec = {"kernel": ("fused prefill call: tile_prep_kernel<true> + ssd_bf16_kernel<true, true> "
-                      "(conv + scan" if which == "fused" else
-                      "scan call: tile_prep_kernel<false> + ssd_bf16_kernel<true, false> (scan") +
-                     ", bf16, d_head 64, d_state 128, 128-token tiles)",
-           "workload": "1.4B-scale prefill, b=4 l=8192, 64 heads, chunk 256, inputs as in bench.py",
+    alg = scan_bytes(w.batch * w.seqlen, h, w.d_head, w.d_state, 2)
+    for v in per.values():
+        v["hbm_bytes"] = v["fetch_kib"] * 1024.0 * kf + v["write_kib"] * 1024.0 * kw
+    rec = {"kernel": ("fused prefill call (conv + scan" if which == "fused" else "scan call (scan") +
+                     ", bf16, d_head 64, d_state 128, 128-token tiles): " + " + ".join(per),
+           "workload": f"{workload} prefill, b={w.batch} l={w.seqlen}, {h} of {w.n_heads} heads "
+                       f"(m={m}), chunk {w.chunk}, inputs as in bench.py",
            "kernel_source_sha256_16": src_hash(),
            "fetch_kib_per_dispatch": sf, "write_kib_per_dispatch": sw,
+           "per_kernel": per,
            "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
                                 "fetch_scale": kf, "write_scale": kw},
            "hbm_bytes_per_launch": total, "alg_bytes_per_launch": alg,
            "traffic_over_alg": total / alg, "dispatches": [nsf, nsw]}
-    os.makedirs(os.path.dirname(TRAFFIC_FILES[which]), exist_ok=True)
-    json.dump(rec, open(TRAFFIC_FILES[which], "w"), indent=1)
+    path = traffic_file(which, workload, m)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    json.dump(rec, open(path, "w"), indent=1)
     print(json.dumps(rec))
 
 
@@ -163,15 +182,20 @@ def timed_calls(torch, fn, flush, iters: int = 50, warmup: int = 5):
     return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9)}
 
 
-def scan_entry(tokens, h, P, N, Q, t):
-    """JSON fields of one scan timing ``t`` (median/p10/p90 in ms)."""
+def scan_entry(tokens, h, P, N, Q, t, elem=2, traffic=None):
+    """JSON fields of one scan timing ``t`` (median/p10/p90 in ms); ``traffic``:
+    the measured HBM bytes of the call (rocprofv3 record), if any."""
     ms = t["median"]
-    ab = scan_bytes(tokens, h, P, N, 2)
+    ab = scan_bytes(tokens, h, P, N, elem)
     fl = scan_flops(tokens, h, P, N, Q)
-    return {"heads": h, "scan_ms": ms, "scan_ms_p10": t["p10"], "scan_ms_p90": t["p90"],
-            "tokens_per_s": tokens / (ms * 1e-3),
-            "hbm_frac": ab / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
-            "mfma_frac": fl / (ms * 1e-3) / (MFMA_PEAK_TFLOPS * 1e12)}
+    e = {"heads": h, "scan_ms": ms, "scan_ms_p10": t["p10"], "scan_ms_p90": t["p90"],
+         "tokens_per_s": tokens / (ms * 1e-3), "alg_bytes": ab,
+         "hbm_frac": ab / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+         "mfma_frac": fl / (ms * 1e-3) / (MFMA_PEAK_TFLOPS * 1e12)}
+    if traffic:
+        e["traffic"] = traffic
+        e["traffic_over_alg"] = traffic / ab
+    return e
 
 
 def conv_bytes(tokens: int, channels: int, elem: int) -> int:
@@ -199,11 +223,11 @@ def src_hash() -> str:
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def load_traffic(which):
+def load_traffic(which, workload="1.4b", m=0):
     """HBM bytes per scan / fused call measured with rocprofv3 (FETCH_SIZE and
     WRITE_SIZE, calibrated on a copy kernel), if taken on this kernel source."""
     try:
-        d = json.load(open(TRAFFIC_FILES[which]))
+        d = json.load(open(traffic_file(which, workload, m)))
     except (OSError, ValueError):
         return None
     if d.get("kernel_source_sha256_16") != src_hash():
@@ -228,7 +252,7 @@ def main():
                          "call / scan call / scan backward / conv backward (for counter and "
                          "trace runs); copy: a 1 GiB device copy that calibrates the HBM "
                          "byte counters")
-    ap.add_argument("--workload", choices=["1.4b", "long", "130m"], default="1.4b",
+    ap.add_argument("--workload", choices=["1.4b", "long", "130m", "tiny"], default="1.4b",
                     help="with --mode scan: the workload whose scan call is repeated")
     ap.add_argument("--heads", type=int, default=0,
                     help="with --mode scan: active heads (default: all)")
@@ -238,7 +262,7 @@ def main():
                          "the traffic record under profiles/")
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
+        summarize_pmc(*args.summarize_pmc, workload=args.workload, heads=args.heads)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -251,7 +275,7 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    if args.mode == "scan" and (args.workload != "1.4b" or args.heads):
+    if args.mode == "scan":
         scan_only(torch, mm, synth, dev, synth.WORKLOADS[args.workload], args)
         return
     w = synth.WORKLOADS["1.4b"]
@@ -291,13 +315,6 @@ def main():
         mm.conv1d_silu(xbc_raw, conv_w, None, None, d_inner=w.d_inner, d_head=P,
                        d_state=N, n_heads_active=heads, out=xbc)
 
-    if args.mode == "scan":  # counter runs: the full-width scan alone
-        conv(H)
-        for _ in range(args.warmup + args.steps):
-            scan(H)
-        torch.cuda.synchronize()
-        print(f"# scan-only: {args.warmup + args.steps} launches", file=sys.stderr)
-        return
     if args.mode == "fused":  # counter runs: the full-width fused call alone
         for _ in range(args.warmup + args.steps):
             fused(H)
@@ -417,7 +434,8 @@ def main():
         for m in w.slices:
             h = w.heads(m)
             slices[str(m)] = scan_entry(tokens, h, P, N, w.chunk,
-                                        timed_calls(torch, lambda: scan(h), flush))
+                                        timed_calls(torch, lambda: scan(h), flush),
+                                        traffic=load_traffic("scan", "1.4b", m))
             fused_slices[str(m)] = scan_entry(tokens, h, P, N, w.chunk,
                                               timed_calls(torch, lambda: fused(h), flush))
         # conv alone at full width, and a plain device copy of the same bytes
@@ -493,11 +511,27 @@ def main():
 
 def scan_only(torch, mm, synth, dev, w, args):
     """Trace and counter runs: the scan call of one workload at one width,
-    repeated (inputs drawn as in the slice timings)."""
+    repeated, on inputs as in the timings: the 1.4B scan reads strided views
+    of the conv output (as in the step), the others dense seeded tensors."""
     h = args.heads or w.n_heads
-    inp = synth.forward_inputs(w)
-    d = {k: v.to(dev) for k, v in inp.items()}
     b, l = w.batch, w.seqlen
+    if w.name == "1.4b":
+        P, N = w.d_head, w.d_state
+        xi = synth.xbc_inputs(w)
+        raw, cw = xi["xbc"].to(dev), xi["w"].to(dev)
+        del xi
+        xbc = torch.empty_like(raw)
+        mm.conv1d_silu(raw, cw, None, None, d_inner=w.d_inner, d_head=P, d_state=N,
+                       n_heads_active=w.n_heads, out=xbc)
+        del raw
+        d = {"x": xbc[..., :w.d_inner].view(b, l, w.n_heads, P),
+             "B": xbc[..., w.d_inner:w.d_inner + N].unsqueeze(2),
+             "C": xbc[..., w.d_inner + N:].unsqueeze(2),
+             "dt": synth.pipeline_dt(w).to(dev), "A": synth.draw_A(w).to(dev),
+             "D": synth.draw_D(w).to(dev)}
+    else:
+        inp = synth.forward_inputs(w)
+        d = {k: v.to(dev) for k, v in inp.items()}
     y = torch.empty((b, l, w.n_heads, w.d_head), dtype=w.dtype, device=dev)
     ws = torch.empty(max(mm.ssd_forward_workspace_size(b, l, w.n_heads, w.d_head, w.d_state, 1,
                                                        h, w.chunk, w.dtype), 1),
@@ -549,12 +583,13 @@ def bench_backward(torch, mm, synth, w, dev, flush, xv, dt, A, Bv, Cv, D, slices
 
 
 def bench_configs(torch, mm, synth, dev, flush):
-    """Scan-only tokens/s, HBM and MFMA fractions at every slice of the
-    130M-scale (b=8, l=2048, 24 heads) and long-context (b=1, l=131072, 32
-    heads) workloads: dense seeded inputs (x, dt, B, C as separate tensors),
-    no initial state, timed as the 1.4B slices are (``timed_calls``)."""
+    """Scan-only tokens/s, HBM and MFMA fractions at every slice of the tiny
+    fp32 (b=1, l=256, 4 heads of 32, d_state 16, chunk 64), 130M-scale (b=8,
+    l=2048, 24 heads) and long-context (b=1, l=131072, 32 heads) workloads:
+    dense seeded inputs (x, dt, B, C as separate tensors), no initial state,
+    timed as the 1.4B slices are (``timed_calls``)."""
     res = {}
-    for name in ("130m", "long"):
+    for name in ("tiny", "130m", "long"):
         w = synth.WORKLOADS[name]
         print(f"# generating inputs for {name}: b={w.batch} l={w.seqlen}", file=sys.stderr, flush=True)
         inp = synth.forward_inputs(w)
@@ -573,9 +608,12 @@ def bench_configs(torch, mm, synth, dev, flush):
                 mm.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], n_heads_active=h,
                                chunk=w.chunk, y=y, workspace=ws)
             per[str(m)] = scan_entry(tokens, h, w.d_head, w.d_state, w.chunk,
-                                     timed_calls(torch, call, flush))
+                                     timed_calls(torch, call, flush),
+                                     elem=torch.finfo(w.dtype).bits // 8,
+                                     traffic=load_traffic("scan", name, m))
             del ws
-        res[name] = {"batch": w.batch, "seq_len": w.seqlen, "n_heads": w.n_heads, "slices": per}
+        res[name] = {"batch": w.batch, "seq_len": w.seqlen, "n_heads": w.n_heads,
+                     "dtype": str(w.dtype).replace("torch.", ""), "slices": per}
         del d, y
         torch.cuda.empty_cache()
     return res
@@ -682,10 +720,26 @@ def bench_decode(torch, mm, synth, dev):
                             "verify_plus_commit_vs_steps": s_us / (v_us + c_us)}}
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w):
-    """The fp64 oracle as it stands, on the host cores, over one full step of the
-    same workload (conv over all 4352 channels, then the scan for all 64 heads
-    of the 4 sequences of 8192 tokens) -- about 86 GFLOP of fp64 work."""
+    """The fp64 oracle as it stands, on the host cores.  ``value``: one full
+    step of the benchmarked workload (conv over all 4352 channels, then the
+    scan for all 64 heads of the 4 sequences of 8192 tokens; ~86 GFLOP of
+    fp64 work).  ``per_config``: the oracle's scan alone at the smallest and
+    the full slice of every forward workload (the long-context one on its
+    first 32768 tokens: the oracle's time is linear in them), and 64 decode
+    steps (conv state roll + state update) of 32 of the decode batch's 256
+    sequences at its mixed widths, each on that workload's seeded inputs."""
     import oracle
     import synth
 
@@ -709,10 +763,53 @@ def cpu_baseline(w):
     Cm = xo[..., w.d_inner + N:]
     oracle.ssd_forward(x, dt, A, Bm, Cm, D, return_state=False)
     t2 = time.perf_counter()
-    return {"value": b * l / (t2 - t0), "unit": "tokens/s", "cores": int(os.environ["OMP_NUM_THREADS"]),
-            "kind": "oracle",
+    del xo, x, Bm, Cm
+    per = {}
+    for name in ("tiny", "130m", "1.4b", "long"):
+        wl = synth.WORKLOADS[name]
+        sl = min(wl.seqlen, 32768)
+        inp = {k: v.double().numpy() for k, v in synth.forward_inputs(wl, seqlen=sl).items()}
+        toks = wl.batch * sl
+        for m in (wl.slices[0], wl.slices[-1]):
+            h = wl.heads(m)
+            ta = time.perf_counter()
+            oracle.ssd_forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                               heads_active=h, return_state=False)
+            tb = time.perf_counter()
+            per[f"{name} m={m}"] = {"heads": h, "tokens": toks, "seconds": tb - ta,
+                                    "tokens_per_s": toks / (tb - ta)}
+            if sl < wl.seqlen:
+                per[f"{name} m={m}"]["sample"] = f"first {sl} of {wl.seqlen} tokens"
+        del inp
+    dw = synth.WORKLOADS["decode"]
+    nb = 32  # sequences of the decode batch timed
+    pool = synth.decode_pool(dw, pool=64, batch=nb)
+    xs = pool["xbc_t"].double().numpy()
+    dts = pool["dt_t"].double().numpy()
+    hv = synth.decode_heads(dw, batch=nb).numpy()
+    Ad, Dd = synth.draw_A(dw).double().numpy(), synth.draw_D(dw).double().numpy()
+    cwd = synth.draw_conv_w(dw).double().numpy()
+    import numpy as np
+    st = np.zeros((nb, dw.n_heads, dw.d_head, dw.d_state))
+    cst = np.zeros((nb, dw.conv_dim, 3))
+    di, Nd = dw.d_inner, dw.d_state
+    ta = time.perf_counter()
+    for k in range(64):
+        uo, cst = oracle.conv1d_silu(xs[k][:, None, :], cwd, None, cst, d_inner=di, d_head=dw.d_head,
+                                     heads_active=hv)
+        uo = uo[:, 0]
+        _, st = oracle.ssd_step(st, uo[:, :di].reshape(nb, dw.n_heads, dw.d_head), dts[k], Ad,
+                                uo[:, di:di + Nd], uo[:, di + Nd:], Dd, heads_active=hv)
+    tb = time.perf_counter()
+    per["decode 64 steps"] = {"sequences": nb, "seconds": tb - ta,
+                              "tokens_per_s": nb * 64 / (tb - ta),
+                              "sample": f"{nb} of the {dw.batch} sequences, widths round-robin"}
+    nthr = int(os.environ["OMP_NUM_THREADS"])
+    return {"value": b * l / (t2 - t0), "unit": "tokens/s", "cores": nthr,
+            "kind": "oracle", "cpu_model": _cpu_model(), "omp_num_threads": nthr,
             "sample": f"one full step (b={b}, l={l}): fp64 conv {t1 - t0:.1f}s + scan {t2 - t1:.1f}s "
-                      f"on {os.environ['OMP_NUM_THREADS']} threads"}
+                      f"on {nthr} threads",
+            "per_config": per}
 
 
 if __name__ == "__main__":

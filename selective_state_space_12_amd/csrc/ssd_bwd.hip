@@ -26,25 +26,29 @@
 // da_r = sum_{t>=r} dLambda_t, ddt_r gets A da_r, dA_h = sum_r dt_r da_r.
 //
 // MI355X design (gfx950, 64-wide waves, 16x16x32 bf16 / 16x16x4 fp32 MFMA):
-//  - bwd_state_kernel: one workgroup per (sequence, head) walks the chunks
-//    forward with the fp32 state in MFMA accumulators and stores the state
-//    before every chunk (and the final one) in the storage type to the
-//    workspace: the backward walk needs them in reverse order.
-//  - bwd_chunk_kernel: one workgroup of 8 waves per (sequence, head) walks the
-//    chunks backwards with dL/dH (P x N fp32) in accumulators.  Per chunk the
-//    x, dy, B, C rows are staged in LDS in token-major form plus the
-//    transposed copies the K = token products need, Hp (from the workspace)
-//    and the bf16/fp32 operand copies of Gc.  Waves 0-3 own one 16-token
-//    s-block each (dx, dB, the column sums of W), waves 4-7 one 16-token
-//    t-block each (dC, the first dLambda term); the causal work of an
-//    s-block grows as that of the matching t-block shrinks, and wave w and
-//    w+4 share a SIMD.  Every wave updates its tiles of dL/dH.  The Q x Q
-//    products are formed transposed where needed so that their accumulators
-//    are directly the A operand of the next product (the masked decay applied
-//    in registers), as in the forward kernel.
-//  - dB and dC are sums over heads: fp32 atomics into the caller's buffers
-//    (zeroed by a fill kernel unless the call accumulates); dA and dD are sums
-//    over sequences, one atomic per workgroup.
+//  - bwd_walks_kernel: two independent walks per (sequence, head) in one
+//    launch, one workgroup of 8 waves each, the fp32 P x N value in MFMA
+//    accumulators: forwards, storing the state before every chunk (and the
+//    final one); backwards, storing Gc, dL/dH at the end of every chunk.
+//    Both are stored in the storage type in layouts the chunk kernel reads
+//    directly (states in MFMA fragment order, Gc n-major).  With few walks the
+//    sequences are split into segments: a prepass walks each segment from
+//    zero, a combine chains the segments, and the walks start from the
+//    chained values.
+//  - bwd_chunk_kernel: one workgroup of 16 waves per (sequence, chunk), every
+//    chunk in parallel, looping over the heads.  The B, C rows and the Q x Q
+//    blocks of C_t . B_s (the same for every head) are formed once; per head
+//    the x, dy rows, dt, Hp and Gc are staged (the next head's loaded during
+//    this one), then phase 1 forms the head's Q x Q blocks (one block per
+//    wave on waves 0-9) and the end-state and Hp terms (each wave its own
+//    u, dB and dC tiles) and phase 2 the causal products into the same
+//    accumulators, with dx written and dB, dC added to their sums over the
+//    heads in registers.  Products that need a tile's transpose read its
+//    columns with LDS transpose loads.  A wave without a Q x Q block forms
+//    the previous head's dLambda, ddt and dA during phase 1.
+//  - dB and dC (sums over the heads) are written once per chunk, no atomics;
+//    dA and dD (sums over the sequences and chunks) are one fp32 atomic per
+//    (workgroup, head).
 #include <algorithm>
 #include <type_traits>
 

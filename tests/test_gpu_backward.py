@@ -184,13 +184,14 @@ def test_backward_accumulates_over_granularities():
 
 
 def test_backward_deterministic_parts_repeat_bitwise():
-    """dx, ddt and dinitial_state come from one workgroup each, in a fixed
-    order: two calls give the same bits."""
+    """dx, ddt, dB, dC and dinitial_state are each formed by one workgroup in
+    a fixed order (dB and dC summed over the heads in registers): two calls
+    give the same bits."""
     w = M130
     inp = _inputs(w, 2, 300, salt=5)
     g1 = _run(w, inp, 24)
     g2 = _run(w, inp, 24)
-    for k in ("dx", "ddt", "dinitial_state"):
+    for k in ("dx", "ddt", "dB", "dC", "dinitial_state"):
         a, b = g1[k], g2[k]
         assert torch.equal(torch.nan_to_num(a, nan=7.0), torch.nan_to_num(b, nan=7.0)), k
 
