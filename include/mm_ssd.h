@@ -464,8 +464,9 @@ int mm_ssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t n_head
  * Segments per sequence a mm_ssd_backward call with these sizes uses for its
  * two walks over the chunks (the states forwards, dL/dH backwards): with
  * fewer than 256 active (sequence, head) walks, the sequences are split into
- * segments of at least 256 tokens walked in parallel (a prepass and a
- * combine chain them; the workspace size includes their data).  The
+ * segments walked in parallel, every one but the last at least 256 tokens
+ * long (a prepass and a combine chain them; the workspace size includes
+ * their data).  The
  * gradients themselves are then formed for all chunks in parallel.  Same
  * argument meaning and errors as mm_ssd_backward.  Host only.
  */

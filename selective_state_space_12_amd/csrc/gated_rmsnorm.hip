@@ -12,7 +12,7 @@
 // workgroups, 16-byte loads and stores, the row's gated values kept in
 // registers between the sum of squares and the scaling (up to 4 chunks of 8
 // per thread; wider rows recompute the gate in a second pass).  Rows of up
-// to 512 values take one wave each (four rows per workgroup, a wave-only
+// to 1024 values take one wave each (four rows per workgroup, a wave-only
 // sum), wider rows a whole workgroup.
 #include "device_common.h"
 #include "kernels.h"
