@@ -232,6 +232,27 @@ __device__ __forceinline__ void store8(T* p, const f32x4& a, const f32x4& b) {
   }
 }
 
+// One storage element through a buffer resource: loads outside the range
+// read 0, stores there are dropped.
+template <typename T>
+__device__ __forceinline__ float buffer_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(T) == 2) {
+    const unsigned short u = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    return __builtin_bit_cast(float, (uint32_t)u << 16);
+  } else {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+  }
+}
+template <typename T>
+__device__ __forceinline__ void buffer_store_elem(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  if constexpr (sizeof(T) == 2) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f32<bf16>(v)), r,
+                                          (int)off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void load4(const T* p, float (&o)[4]) {
   if constexpr (sizeof(T) == 2) {
@@ -249,16 +270,6 @@ __device__ __forceinline__ void load4(const T* p, float (&o)[4]) {
   }
 }
 
-template <typename T, int P, int N>
-struct StateLds {
-  static constexpr int TQ = kBQ + bpad<T>();  // pitch of the transposed x and B rows
-  static constexpr size_t bytes = (size_t)(P + N) * TQ * sizeof(T) + 2 * kBQ * sizeof(float);
-};
-
-// Forward walk storing the state before every chunk and the final state.
-// With the sequence split, PRE walks segments 0..nseg-2 from a zero state and
-// writes each one's end state and log2 decay (seg_h, seg_hd); the main walk
-// of segment s > 0 then starts from the combined state in seg_h slot s-1.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Returns v unchanged, but the compiler can no longer see where it came
@@ -276,345 +287,258 @@ template <typename V> __device__ __forceinline__ V opaque(V v) {
   }
 }
 
-template <typename T, int P, int N, bool PRE>
-__device__ __forceinline__ void state_walk(const BwdK& k, int pid, int total) {
-  using L = StateLds<T, P, N>;
-  constexpr int Q = kBQ, TQ = L::TQ;
+// Operand fragment from columns of a row-major LDS tile M (row pitch ld):
+// lane (r, g) gets M[ra + j][c(r)] in slots j = 0..3 and M[rb + j][c(r)] in
+// slots 4..7, where ra, rb are the row bases of its 16-lane group and
+// c(r) = c0 + cs (r/4) + r%4 (cs = 4: sixteen consecutive columns; cs = 8:
+// the paired d_head rows of prow()).  16-bit elements: two LDS transpose
+// loads, in which lane q of a group addresses the four elements at row
+// base + q/4, columns c0 + cs (q%4) .. +3, and receives in element k element
+// q%4 of what lane 4k + q/4 addressed (tiles of whole K=32 slices only).
+// 32-bit elements: eight element reads, zeros where live is false.
+template <typename T>
+__device__ __forceinline__ void frag_cols(Frag8<T>& f, const T* M, int ld, int ra, int rb, int c0,
+                                          int cs, int lane, bool live = true) {
+  const int q = lane & 15;
+  if constexpr (sizeof(T) == 2) {
+    typedef short short4v __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) short4v lds_short4;
+    const int col = c0 + (q & 3) * cs;
+    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_short4*)(const_cast<T*>(M) + (ra + (q >> 2)) * ld + col));
+    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_short4*)(const_cast<T*>(M) + (rb + (q >> 2)) * ld + col));
+    f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else {
+    const int col = c0 + (q >> 2) * cs + (q & 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.v[j] = live ? M[(ra + j) * ld + col] : 0.0f;
+      f.v[j + 4] = live ? M[(rb + j) * ld + col] : 0.0f;
+    }
+  }
+}
+
+// LDS of a walk: two buffers (by chunk parity), each the chunk's rows of the
+// d_head stream (x forwards, dy backwards) and of the d_state stream (B
+// forwards, C backwards) token-major, with Lambda and the per-token weights.
+template <typename T, int P, int N>
+struct WalkLds {
+  static constexpr int NP = P + bpad<T>();
+  static constexpr int NN = N + bpad<T>();
+  static constexpr size_t buf_elems = (size_t)kBQ * NP + (size_t)kBQ * NN;
+  static constexpr size_t buf_bytes = buf_elems * sizeof(T) + 2 * kBQ * sizeof(float);
+  static constexpr size_t bytes = 2 * buf_bytes;
+};
+
+// One walk over the chunks of a (sequence, head) segment with the fp32 P x N
+// value V in MFMA accumulators, V <- exp2(Lambda_e) V + sum_t a_t w_t b_t^T
+// per chunk:
+//   REV = false (states): chunks ascending, a = x, b = B, w_s = exp2(Lambda_e -
+//     Lambda_s) dt_s: V is the state.  MAIN stores it before every chunk
+//     (and after the last one) in fragment order; PRE (segments 0..nseg-2,
+//     from zero) writes the segment's end state and log2 decay.
+//   REV = true (gradients): chunks descending, a = dy, b = C, w_t =
+//     exp2(Lambda_t): V is dL/dH.  MAIN stores it at the end of every chunk
+//     n-major, before the chunk's update, and the first segment writes dh0;
+//     PRE (segments 1..nseg-1, from zero) writes the result at the segment's
+//     start and its log2 decay.
+// MAIN segments start from the combined value of the split (or h0 / dhT).
+// The a and b rows are staged token-major and read as operand columns with
+// transpose loads; the rows of the chunk two ahead are loaded into registers
+// (two sets, used alternately) and the LDS buffers alternate by chunk, so a
+// chunk needs one barrier.  Tile rows in the paired order of prow().
+template <typename T, int P, int N, bool REV, bool MAIN>
+__device__ __forceinline__ void walk(const BwdK& k, int pid, int total) {
+  using L = WalkLds<T, P, N>;
+  constexpr int Q = kBQ, NP = L::NP, NN = L::NN;
   constexpr int TP = P / 16, TN = N / 16, NTILE = TP * TN;
   constexpr int TPW = NTILE >= 2 * kBWaves ? NTILE / kBWaves : 2;
   static_assert(NTILE < 2 * kBWaves || NTILE % kBWaves == 0, "state tiles must split evenly");
-  static_assert(TP % TPW == 0 && TPW % 2 == 0, "a wave's state tiles are whole pairs of one column block");
+  static_assert(TP % TPW == 0 && TPW % 2 == 0, "a wave's tiles are whole pairs of one column block");
   constexpr int VB = 16 / (int)sizeof(T);
+  constexpr int NAV = (Q * (P / VB) + kBThreads - 1) / kBThreads;  // a vectors per thread
+  constexpr int NBV = (Q * (N / VB) + kBThreads - 1) / kBThreads;  // b vectors per thread
   extern __shared__ __align__(16) unsigned char smem[];
-  T* XT = reinterpret_cast<T*>(smem);
-  T* BT = XT + P * TQ;
-  float* lam = reinterpret_cast<float*>(BT + N * TQ);
-  float* wsc = lam + Q;
+  auto buf = [&](int parity, T*& an, T*& bn, float*& lam, float*& wt) {
+    unsigned char* base = smem + parity * L::buf_bytes;
+    an = reinterpret_cast<T*>(base);
+    bn = an + Q * NP;
+    lam = reinterpret_cast<float*>(bn + Q * NN);
+    wt = lam + Q;
+  };
 
-  int b, h, seg;
-  unit_of_idx(pid, total, k.heads, PRE ? k.nseg - 1 : k.nseg, &b, &h, &seg);
+  int b, h, sg;
+  unit_of_idx(pid, total, k.heads, MAIN ? k.nseg : k.nseg - 1, &b, &h, &sg);
+  const int seg = (REV && !MAIN) ? sg + 1 : sg;
   const int64_t unit = (int64_t)b * k.heads + h;
   const int c0 = seg * k.seg_chunks, c1 = min(c0 + k.seg_chunks, k.nchunks);
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int r16 = lane % 16, g = lane / 16;
-  const T* __restrict__ Xp = static_cast<const T*>(k.x);
+  const T* __restrict__ Ap = static_cast<const T*>(REV ? k.dy : k.x);
+  const int64_t as = REV ? k.dys : k.xs;
+  const T* __restrict__ Bp = static_cast<const T*>(REV ? k.C : k.B);
+  const int64_t bs = REV ? k.cs : k.bs;
   const T* __restrict__ DTp = static_cast<const T*>(k.dt);
-  const T* __restrict__ Bp = static_cast<const T*>(k.B);
-  T* __restrict__ Hst = static_cast<T*>(k.hst) + unit * (k.nchunks + 1) * (P * N);
   const int64_t rowb = (int64_t)b * k.seqlen;
   const float Ah2 = k.A[h] * kLog2e;
 
-  // this wave's state tiles (pt0 + t, nt), rows in the paired order of prow()
+  // this wave's tiles (pt0 + t, nt), rows in the paired order of prow()
   const int tile0 = wave * TPW;
   const bool owns = NTILE >= kBWaves * TPW || tile0 < NTILE;  // known true when every wave owns
   const int nt = tile0 / TP, pt0 = tile0 % TP;
-  f32x4 hacc[TPW];
-  const float* hin = PRE ? nullptr
-                     : seg > 0 ? k.seg_h + (unit * k.nseg + seg - 1) * (P * N)
-                     : k.h0 ? k.h0 + ((int64_t)b * k.n_heads + h) * (P * N)
-                            : nullptr;
+  f32x4 acc[TPW];
+  {
+    const float* vin = nullptr;
+    if (MAIN) {
+      if (!REV)
+        vin = seg > 0 ? k.seg_h + (unit * k.nseg + seg - 1) * (P * N)
+              : k.h0  ? k.h0 + ((int64_t)b * k.n_heads + h) * (P * N)
+                      : nullptr;
+      else
+        vin = seg + 1 < k.nseg ? k.seg_g + (unit * k.nseg + seg + 1) * (P * N)
+              : k.dhT          ? k.dhT + ((int64_t)b * k.n_heads + h) * (P * N)
+                               : nullptr;
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[t][i] = (vin && owns) ? vin[prow(pt0 + t, g * 4 + i) * N + nt * 16 + r16] : 0.0f;
+    // the start value's loads complete here, before any chunk is loaded ahead
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) acc[t] = opaque(acc[t]);
+  }
   float lam_seg = 0.0f;  // log2 decay over the walked chunks
+  T* __restrict__ Vst = static_cast<T*>(REV ? k.gst : k.hst) +
+                        unit * (REV ? k.nchunks : k.nchunks + 1) * (P * N);
+  // V after chunk c (REV: before the update with chunk c), in its stored layout
+  auto store_v = [&](int c) {
+    if (!MAIN || !owns) return;
+    T* dst = Vst + (int64_t)c * (P * N);
 #pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      hacc[t][i] = (hin && owns) ? hin[prow(pt0 + t, g * 4 + i) * N + nt * 16 + r16] : 0.0f;
-  // the start state's loads complete here, before any chunk is loaded ahead
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) hacc[t] = opaque(hacc[t]);
-
-  // the state in fragment order: one 8-element run per lane and tile pair
-  auto store_state = [&](int c) {
-    if (PRE || !owns) return;
-    T* dst = Hst + (int64_t)c * (P * N);
-#pragma unroll
-    for (int t = 0; t < TPW; t += 2) store8(dst + state_frag<N>((pt0 + t) / 2, nt, lane), hacc[t], hacc[t + 1]);
+    for (int t = 0; t < TPW; t += 2) {
+      if (REV) store8(dst + (nt * 16 + r16) * P + ((pt0 + t) / 2) * 32 + g * 8, acc[t], acc[t + 1]);
+      else store8(dst + state_frag<N>((pt0 + t) / 2, nt, lane), acc[t], acc[t + 1]);
+    }
   };
 
-  // The x, B rows and dt of the chunk two ahead are loaded into registers
-  // while this chunk's update runs (two register sets, used alternately; a
-  // thread's vector slots are fixed, so a chunk's loads are all in flight at
-  // once and have two chunks of time to land).
-  constexpr int NXV = (Q * (P / VB) + kBThreads - 1) / kBThreads;
-  constexpr int NBV = (Q * (N / VB) + kBThreads - 1) / kBThreads;
-  u32x4 px[2][NXV], pb[2][NBV];
-  T pdt[2];
+  u32x4 pa[2][NAV], pb[2][NBV];
+  float pdt[2];
   int plen[2] = {0, 0};
   auto prefetch = [&](int c, auto set) {
     constexpr int S = decltype(set)::value;
     const int64_t row0 = rowb + (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
-    // Every load is issued unconditionally at a clamped address and the
-    // rows past the end are zeroed afterwards: a load under a lane condition
-    // is followed by a wait for it at the branch's end, which serialises
-    // the whole batch.
+    // every load unconditional, at a clamped row (rows past len are zeroed
+    // at staging): a load under a lane condition is waited for at its branch
 #pragma unroll
-    for (int v = 0; v < NXV; ++v) {
-      const int idx = min(tid + v * kBThreads, Q * (P / VB) - 1), s = idx % Q;
-      const int p0 = (idx / Q) * VB;
-      px[S][v] = *reinterpret_cast<const u32x4*>(Xp + (row0 + min(s, len - 1)) * k.xs + (int64_t)h * P + p0);
-    }
-#pragma unroll
-    for (int v = 0; v < NBV; ++v) {
-      const int idx = min(tid + v * kBThreads, Q * (N / VB) - 1), s = idx % Q;
-      const int n0 = (idx / Q) * VB;
-      pb[S][v] = *reinterpret_cast<const u32x4*>(Bp + (row0 + min(s, len - 1)) * k.bs + n0);
-    }
-    pdt[S] = DTp[(row0 + min(lane, len - 1)) * k.dts + h];
-    plen[S] = len;
-  };
-  auto step = [&](int c, auto set) {
-    constexpr int S = decltype(set)::value;
-    store_state(c);
-    // x^T and B^T: consecutive lanes take consecutive tokens (distinct banks)
-    const int len = plen[S];
-#pragma unroll
-    for (int v = 0; v < NXV; ++v) {
-      const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
-      const u32x4 raw = opaque(px[S][v]);
-      Vec16<T> xv;
-      *reinterpret_cast<u32x4*>(xv.v) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
-      if (idx < Q * (P / VB))
-#pragma unroll
-        for (int j = 0; j < VB; ++j) XT[(p0 + j) * TQ + s] = xv.v[j];
-    }
-#pragma unroll
-    for (int v = 0; v < NBV; ++v) {
-      const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
-      const u32x4 raw = opaque(pb[S][v]);
-      Vec16<T> bv;
-      *reinterpret_cast<u32x4*>(bv.v) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
-      if (idx < Q * (N / VB))
-#pragma unroll
-        for (int j = 0; j < VB; ++j) BT[(n0 + j) * TQ + s] = bv.v[j];
-    }
-    if (wave == 0) {
-      const float d = lane < len ? to_f32(opaque(pdt[S])) : 0.0f;
-      const float lv = chunk_cumsum(d * Ah2, lane);
-      const float le = __shfl(lv, 63);
-      lam[lane] = lv;
-      wsc[lane] = __builtin_amdgcn_exp2f(le - lv) * d;
-    }
-    __syncthreads();
-    // issued on every step (the last two reload the final chunk) so that the
-    // loop has one path and each load is waited for exactly where it is used
-    prefetch(min(c + 2, c1 - 1), set);
-    lam_seg += lam[Q - 1];
-    if (owns) {
-      const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
-#pragma unroll
-      for (int t = 0; t < TPW; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hacc[t][i] *= dec;
-#pragma unroll
-      for (int ks = 0; ks < Q / 32; ++ks) {
-        const int s0 = ks * 32 + g * 8;
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(wsc + s0);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wsc + s0 + 4);
-        Frag8<T> bf;
-        frag_load8(bf, BT + (nt * 16 + r16) * TQ + s0);
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-          Frag8<T> xr, xf;
-          frag_load8(xr, XT + prow(pt0 + t, r16) * TQ + s0);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) frag_set(xf, j, to_f32(xr.v[j]) * (j < 4 ? w0[j] : w1[j - 4]));
-          hacc[t] = mma(xf, bf, hacc[t]);
-        }
-      }
-    }
-    __syncthreads();
-  };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  // c1 - 1 is a valid chunk whenever there is one (c1 = min(c0 + seg_chunks,
-  // nchunks) and nchunks >= 1), so the clamped loads stay in bounds
-  prefetch(min(c0, c1 - 1), S0{});
-  prefetch(min(c0 + 1, c1 - 1), S1{});
-  int c = c0;
-  for (; c + 1 < c1; c += 2) {
-    step(c, S0{});
-    step(c + 1, S1{});
-  }
-  if (c < c1) step(c, S0{});
-  if (PRE) {
-    float* dst = k.seg_h + (unit * k.nseg + seg) * (P * N);
-    if (owns)
-#pragma unroll
-      for (int t = 0; t < TPW; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[prow(pt0 + t, g * 4 + i) * N + nt * 16 + r16] = hacc[t][i];
-    if (tid == 0) k.seg_hd[unit * k.nseg + seg] = lam_seg;
-  } else if (c1 == k.nchunks) {
-    store_state(k.nchunks);
-  }
-}
-
-
-// Reverse walk of dL/dH alone, chunk by chunk backwards:
-//   dGp = exp(Lambda_e) Gc + sum_t exp(Lambda_t) dy_t C_t^T.
-// MAIN = false (prepass of the sequence split): segments 1..nseg-1 walk from
-// dL/dH = 0 at their end and write the result at their start and their log2
-// decay (seg_g, seg_gd).  MAIN = true: every segment walks from the combined
-// gradient at its end (dhT for the last one) and stores Gc, the gradient at
-// the end of each chunk, n-major ([N][P], gst) for the chunk kernel; the
-// first segment writes dh0.  Tile rows in the paired order of prow().
-template <typename T, int P, int N, bool MAIN>
-__device__ __forceinline__ void gprep_walk(const BwdK& k, int pid, int total) {
-  using L = StateLds<T, P, N>;
-  constexpr int Q = kBQ, TQ = L::TQ;
-  constexpr int TP = P / 16, TN = N / 16, NTILE = TP * TN;
-  constexpr int TPW = NTILE >= 2 * kBWaves ? NTILE / kBWaves : 2;
-  static_assert(TP % TPW == 0 && TPW % 2 == 0, "a wave's tiles are whole pairs of one column block");
-  constexpr int VB = 16 / (int)sizeof(T);
-  constexpr int NYV = (Q * (P / VB) + kBThreads - 1) / kBThreads;
-  constexpr int NCV = (Q * (N / VB) + kBThreads - 1) / kBThreads;
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* YT = reinterpret_cast<T*>(smem);  // dy^T [P][TQ]
-  T* CT = YT + P * TQ;                 // C^T [N][TQ]
-  float* lam = reinterpret_cast<float*>(CT + N * TQ);
-  float* eL = lam + Q;
-
-  int b, h, sg;
-  unit_of_idx(pid, total, k.heads, MAIN ? k.nseg : k.nseg - 1, &b, &h, &sg);
-  const int seg = MAIN ? sg : sg + 1;
-  const int64_t unit = (int64_t)b * k.heads + h;
-  const int c0 = seg * k.seg_chunks, c1 = min(c0 + k.seg_chunks, k.nchunks);
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
-  const int r16 = lane % 16, g = lane / 16;
-  const T* __restrict__ DYp = static_cast<const T*>(k.dy);
-  const T* __restrict__ DTp = static_cast<const T*>(k.dt);
-  const T* __restrict__ Cp = static_cast<const T*>(k.C);
-  const int64_t rowb = (int64_t)b * k.seqlen;
-  const float Ah2 = k.A[h] * kLog2e;
-  const int tile0 = wave * TPW;
-  const bool owns = NTILE >= kBWaves * TPW || tile0 < NTILE;  // known true when every wave owns
-  const int nt = tile0 / TP, pt0 = tile0 % TP;
-  f32x4 gacc[TPW];
-  {
-    const float* gin = !MAIN                 ? nullptr
-                       : seg + 1 < k.nseg ? k.seg_g + (unit * k.nseg + seg + 1) * (P * N)
-                       : k.dhT             ? k.dhT + ((int64_t)b * k.n_heads + h) * (P * N)
-                                           : nullptr;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        gacc[t][i] = (gin && owns) ? gin[prow(pt0 + t, g * 4 + i) * N + nt * 16 + r16] : 0.0f;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) gacc[t] = opaque(gacc[t]);
-  }
-  T* __restrict__ Gst = static_cast<T*>(k.gst) + unit * k.nchunks * (P * N);
-  float lam_seg = 0.0f;
-  // As in the forward state walk: dy, C rows and dt of the chunk two behind
-  // (in walk order) are loaded while this chunk runs, into two register sets
-  // used alternately, and pass through opaque() where they are used.
-  u32x4 py[2][NYV], pc[2][NCV];
-  T pdt[2];
-  int plen[2];
-  auto prefetch = [&](int c, auto set) {
-    constexpr int S = decltype(set)::value;
-    const int64_t row0 = rowb + (int64_t)c * Q;
-    const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
-#pragma unroll
-    for (int v = 0; v < NYV; ++v) {
+    for (int v = 0; v < NAV; ++v) {
       const int idx = min(tid + v * kBThreads, Q * (P / VB) - 1), s = min(idx % Q, len - 1);
-      py[S][v] = *reinterpret_cast<const u32x4*>(DYp + (row0 + s) * k.dys + (int64_t)h * P + (idx / Q) * VB);
+      pa[S][v] = *reinterpret_cast<const u32x4*>(Ap + (row0 + s) * as + (int64_t)h * P + (idx / Q) * VB);
     }
 #pragma unroll
-    for (int v = 0; v < NCV; ++v) {
+    for (int v = 0; v < NBV; ++v) {
       const int idx = min(tid + v * kBThreads, Q * (N / VB) - 1), s = min(idx % Q, len - 1);
-      pc[S][v] = *reinterpret_cast<const u32x4*>(Cp + (row0 + s) * k.cs + (idx / Q) * VB);
+      pb[S][v] = *reinterpret_cast<const u32x4*>(Bp + (row0 + s) * bs + (idx / Q) * VB);
     }
-    pdt[S] = DTp[(row0 + min(lane, len - 1)) * k.dts + h];
+    // dt: wave 0 only (the other waves' range is empty); tokens past len read 0
+    pdt[S] = buffer_elem<T>(uniform_rsrc(DTp + row0 * k.dts + h, wave == 0 ? (uint32_t)(len * k.dts * sizeof(T)) : 0u),
+                            (uint32_t)(lane * k.dts * sizeof(T)));
     plen[S] = len;
   };
-  auto step = [&](int c, auto set) {
+  auto step = [&](int c, int parity, auto set) {
     constexpr int S = decltype(set)::value;
+    T *an, *bn;
+    float *lam, *wt;
+    buf(parity, an, bn, lam, wt);
+    store_v(c);  // the state before chunk c, or dL/dH at its end
     const int len = plen[S];
-    // Gc of this chunk, n-major: a tile pair's accumulators are eight
-    // consecutive d_head rows
-    if (MAIN && owns) {
-      T* dst = Gst + (int64_t)c * (P * N);
 #pragma unroll
-      for (int t = 0; t < TPW; t += 2)
-        store8(dst + (nt * 16 + r16) * P + ((pt0 + t) / 2) * 32 + g * 8, gacc[t], gacc[t + 1]);
-    }
-#pragma unroll
-    for (int v = 0; v < NYV; ++v) {
-      const int idx = tid + v * kBThreads, s = idx % Q, p0 = (idx / Q) * VB;
-      const u32x4 raw = opaque(py[S][v]);
-      Vec16<T> yv;
-      *reinterpret_cast<u32x4*>(yv.v) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
+    for (int v = 0; v < NAV; ++v) {
+      const int idx = tid + v * kBThreads, s = idx % Q;
+      const u32x4 raw = opaque(pa[S][v]);
       if (idx < Q * (P / VB))
-#pragma unroll
-        for (int j = 0; j < VB; ++j) YT[(p0 + j) * TQ + s] = yv.v[j];
+        *reinterpret_cast<u32x4*>(an + s * NP + (idx / Q) * VB) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int v = 0; v < NCV; ++v) {
-      const int idx = tid + v * kBThreads, s = idx % Q, n0 = (idx / Q) * VB;
-      const u32x4 raw = opaque(pc[S][v]);
-      Vec16<T> cv;
-      *reinterpret_cast<u32x4*>(cv.v) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
+    for (int v = 0; v < NBV; ++v) {
+      const int idx = tid + v * kBThreads, s = idx % Q;
+      const u32x4 raw = opaque(pb[S][v]);
       if (idx < Q * (N / VB))
-#pragma unroll
-        for (int j = 0; j < VB; ++j) CT[(n0 + j) * TQ + s] = cv.v[j];
+        *reinterpret_cast<u32x4*>(bn + s * NN + (idx / Q) * VB) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
     }
     if (wave == 0) {
-      const float d = lane < len ? to_f32(opaque(pdt[S])) : 0.0f;
+      const float d = opaque(pdt[S]);
       const float lv = chunk_cumsum(d * Ah2, lane);
+      const float le = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), 63));
       lam[lane] = lv;
-      eL[lane] = __builtin_amdgcn_exp2f(lv);
+      wt[lane] = REV ? __builtin_amdgcn_exp2f(lv) : __builtin_amdgcn_exp2f(le - lv) * d;
     }
+    // one barrier per chunk: this buffer is staged, and every wave is done
+    // with the other one (read by the chunk before), which the next chunk
+    // stages
     __syncthreads();
-    // issued on every step, clamped at the segment's first chunk
-    prefetch(max(c - 2, c0), set);
+    // issued on every step, clamped at the segment's last chunk in walk order
+    prefetch(REV ? max(c - 2, c0) : min(c + 2, c1 - 1), set);
     lam_seg += lam[Q - 1];
     if (owns) {
       const float dec = __builtin_amdgcn_exp2f(lam[Q - 1]);
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) gacc[t][i] *= dec;
+        for (int i = 0; i < 4; ++i) acc[t][i] *= dec;
 #pragma unroll
       for (int ks = 0; ks < Q / 32; ++ks) {
         const int tq = ks * 32 + g * 8;
-        const f32x4 e0 = *reinterpret_cast<const f32x4*>(eL + tq);
-        const f32x4 e1 = *reinterpret_cast<const f32x4*>(eL + tq + 4);
-        Frag8<T> cr, cf;
-        frag_load8(cr, CT + (nt * 16 + r16) * TQ + tq);
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(wt + tq);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wt + tq + 4);
+        Frag8<T> br, bf;
+        frag_cols(br, bn, NN, tq, tq + 4, nt * 16, 4, lane);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) frag_set(cf, j, to_f32(cr.v[j]) * (j < 4 ? e0[j] : e1[j - 4]));
+        for (int j = 0; j < 8; ++j) frag_set(bf, j, to_f32(br.v[j]) * (j < 4 ? w0[j] : w1[j - 4]));
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-          Frag8<T> yf;
-          frag_load8(yf, YT + prow(pt0 + t, r16) * TQ + tq);
-          gacc[t] = mma(yf, cf, gacc[t]);
+          Frag8<T> af;
+          frag_cols(af, an, NP, tq, tq + 4, ((pt0 + t) >> 1) * 32 + ((pt0 + t) & 1) * 4, 8, lane);
+          acc[t] = mma(af, bf, acc[t]);
         }
       }
     }
-    __syncthreads();
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  // segments 1..nseg-1 each hold at least one chunk (c0 < c1), so every
+  // every segment walked here holds at least one chunk (c0 < c1), so every
   // clamped chunk index below is a valid one
-  prefetch(c1 - 1, S0{});
-  prefetch(max(c1 - 2, c0), S1{});
-  int c = c1 - 1;
-  for (; c - 1 >= c0; c -= 2) {
-    step(c, S0{});
-    step(c - 1, S1{});
+  if (!REV) {
+    prefetch(min(c0, c1 - 1), S0{});
+    prefetch(min(c0 + 1, c1 - 1), S1{});
+    int c = c0;
+    for (; c + 1 < c1; c += 2) {
+      step(c, 0, S0{});
+      step(c + 1, 1, S1{});
+    }
+    if (c < c1) step(c, 0, S0{});
+  } else {
+    prefetch(c1 - 1, S0{});
+    prefetch(max(c1 - 2, c0), S1{});
+    int c = c1 - 1;
+    for (; c - 1 >= c0; c -= 2) {
+      step(c, 0, S0{});
+      step(c - 1, 1, S1{});
+    }
+    if (c >= c0) step(c, 0, S0{});
   }
-  if (c >= c0) step(c, S0{});
   if (!MAIN) {
-    float* dst = k.seg_g + (unit * k.nseg + seg) * (P * N);
+    float* dst = (REV ? k.seg_g : k.seg_h) + (unit * k.nseg + seg) * (P * N);
     if (owns)
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[prow(pt0 + t, g * 4 + i) * N + nt * 16 + r16] = gacc[t][i];
-    if (tid == 0) k.seg_gd[unit * k.nseg + seg] = lam_seg;
+        for (int i = 0; i < 4; ++i) dst[prow(pt0 + t, g * 4 + i) * N + nt * 16 + r16] = acc[t][i];
+    if (tid == 0) (REV ? k.seg_gd : k.seg_hd)[unit * k.nseg + seg] = lam_seg;
+  } else if (!REV) {
+    if (c1 == k.nchunks) store_v(k.nchunks);
   } else if (seg == 0 && k.dh0 && owns) {
     float* dst = k.dh0 + ((int64_t)b * k.n_heads + h) * (P * N);
 #pragma unroll
@@ -622,7 +546,7 @@ __device__ __forceinline__ void gprep_walk(const BwdK& k, int pid, int total) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float* q = dst + prow(pt0 + t, g * 4 + i) * N + nt * 16 + r16;
-        *q = k.accumulate ? *q + gacc[t][i] : gacc[t][i];
+        *q = k.accumulate ? *q + acc[t][i] : acc[t][i];
       }
   }
 }
@@ -633,8 +557,8 @@ __device__ __forceinline__ void gprep_walk(const BwdK& k, int pid, int total) {
 template <typename T, int P, int N>
 __global__ __launch_bounds__(kBThreads) void bwd_prepass_kernel(BwdK k) {
   const int half = gridDim.x / 2;
-  if ((int)blockIdx.x < half) state_walk<T, P, N, true>(k, blockIdx.x, half);
-  else gprep_walk<T, P, N, false>(k, blockIdx.x - half, half);
+  if ((int)blockIdx.x < half) walk<T, P, N, false, false>(k, blockIdx.x, half);
+  else walk<T, P, N, true, false>(k, blockIdx.x - half, half);
 }
 
 // Both walks of the call in one launch, independent of each other:
@@ -643,8 +567,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_prepass_kernel(BwdK k) {
 template <typename T, int P, int N>
 __global__ __launch_bounds__(kBThreads) void bwd_walks_kernel(BwdK k) {
   const int half = gridDim.x / 2;
-  if ((int)blockIdx.x < half) state_walk<T, P, N, false>(k, blockIdx.x, half);
-  else gprep_walk<T, P, N, true>(k, blockIdx.x - half, half);
+  if ((int)blockIdx.x < half) walk<T, P, N, false, true>(k, blockIdx.x, half);
+  else walk<T, P, N, true, true>(k, blockIdx.x - half, half);
 }
 
 // Chains the segments of every unit, one thread per state element.
@@ -691,38 +615,6 @@ struct ChunkLds {
   static constexpr size_t bytes = elems * sizeof(T) + kFloats * sizeof(float);
 };
 
-// Operand fragment from columns of a row-major LDS tile M (row pitch ld):
-// lane (r, g) gets M[ra + j][c(r)] in slots j = 0..3 and M[rb + j][c(r)] in
-// slots 4..7, where ra, rb are the row bases of its 16-lane group and
-// c(r) = c0 + cs (r/4) + r%4 (cs = 4: sixteen consecutive columns; cs = 8:
-// the paired d_head rows of prow()).  16-bit elements: two LDS transpose
-// loads, in which lane q of a group addresses the four elements at row
-// base + q/4, columns c0 + cs (q%4) .. +3, and receives in element k element
-// q%4 of what lane 4k + q/4 addressed (tiles of whole K=32 slices only).
-// 32-bit elements: eight element reads, zeros where live is false.
-template <typename T>
-__device__ __forceinline__ void frag_cols(Frag8<T>& f, const T* M, int ld, int ra, int rb, int c0,
-                                          int cs, int lane, bool live = true) {
-  const int q = lane & 15;
-  if constexpr (sizeof(T) == 2) {
-    typedef short short4v __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) short4v lds_short4;
-    const int col = c0 + (q & 3) * cs;
-    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_short4*)(const_cast<T*>(M) + (ra + (q >> 2)) * ld + col));
-    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_short4*)(const_cast<T*>(M) + (rb + (q >> 2)) * ld + col));
-    f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  } else {
-    const int col = c0 + (q >> 2) * cs + (q & 3);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f.v[j] = live ? M[(ra + j) * ld + col] : 0.0f;
-      f.v[j + 4] = live ? M[(rb + j) * ld + col] : 0.0f;
-    }
-  }
-}
-
 // Sum over the 64 lanes, in every lane: row sums by DPP, then the four rows'
 // sums read from lanes 0, 16, 32, 48.
 __device__ __forceinline__ float wave_sum(float v) {
@@ -735,27 +627,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 // lane index, so that it is formed where used)
 __device__ __forceinline__ float xor_lane(float v, int lane, int m) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __builtin_bit_cast(int, v)));
-}
-
-// One storage element through a buffer resource: loads outside the range
-// read 0, stores there are dropped.
-template <typename T>
-__device__ __forceinline__ float buffer_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if constexpr (sizeof(T) == 2) {
-    const unsigned short u = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
-    return __builtin_bit_cast(float, (uint32_t)u << 16);
-  } else {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
-  }
-}
-template <typename T>
-__device__ __forceinline__ void buffer_store_elem(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-  if constexpr (sizeof(T) == 2) {
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f32<bf16>(v)), r,
-                                          (int)off, 0, 0);
-  } else {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
-  }
 }
 
 // ACC: add into the caller's dx, ddt, dB and dC (else overwrite them).
@@ -1252,7 +1123,7 @@ __global__ __launch_bounds__(64) void zero_heads_kernel(float* dA, float* dD, in
 template <typename T, int P, int N>
 hipError_t launch_shape(const BwdK& k, int64_t batch, hipStream_t s) {
   const unsigned units = (unsigned)(batch * k.heads);
-  const size_t lds1 = StateLds<T, P, N>::bytes, lds2 = ChunkLds<T, P, N>::bytes;
+  const size_t lds1 = WalkLds<T, P, N>::bytes, lds2 = ChunkLds<T, P, N>::bytes;
   static_assert(ChunkLds<T, P, N>::bytes <= 160 * 1024, "chunk tiles fit one CU's LDS");
   const void* fns[] = {reinterpret_cast<const void*>(&bwd_walks_kernel<T, P, N>),
                        reinterpret_cast<const void*>(&bwd_prepass_kernel<T, P, N>),
