@@ -255,7 +255,7 @@ def main():
     ap.add_argument("--workload", choices=["1.4b", "long", "130m", "tiny"], default="1.4b",
                     help="with --mode scan: the workload whose scan call is repeated")
     ap.add_argument("--heads", type=int, default=0,
-                    help="with --mode scan: active heads (default: all)")
+                    help="with --mode scan or backward: active heads (default: all)")
     ap.add_argument("--summarize-pmc", nargs=5,
                     metavar=("WHICH", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="WHICH = scan or fused, then rocprofv3 --pmc output dirs (csv); writes "
@@ -321,15 +321,16 @@ def main():
         torch.cuda.synchronize()
         print(f"# fused-only: {args.warmup + args.steps} launches", file=sys.stderr)
         return
-    if args.mode == "backward":  # counter runs: the full-width scan backward alone
+    if args.mode == "backward":  # counter runs: the scan backward alone (full width by default)
         conv(H)
+        hb = args.heads or H
         dy = synth.cotangents(w)["dy"].to(dev)
         g = {"dx": torch.empty((b, l, H, P), dtype=w.dtype, device=dev),
              "ddt": torch.empty((b, l, H), dtype=w.dtype, device=dev)}
-        bws = torch.empty(mm.ssd_backward_workspace_size(b, l, H, P, N, 1, H, w.dtype),
+        bws = torch.empty(mm.ssd_backward_workspace_size(b, l, H, P, N, 1, hb, w.dtype),
                           dtype=torch.uint8, device=dev)
         for _ in range(args.warmup + args.steps):
-            g = mm.ssd_backward(xv, dt, A, Bv, Cv, D, dy, grads=g, workspace=bws)
+            g = mm.ssd_backward(xv, dt, A, Bv, Cv, D, dy, n_heads_active=hb, grads=g, workspace=bws)
         torch.cuda.synchronize()
         print(f"# backward-only: {args.warmup + args.steps} launches", file=sys.stderr)
         return

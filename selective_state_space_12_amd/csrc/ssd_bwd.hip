@@ -759,30 +759,37 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
   }
 
   // Per-head rows (x, dy), dt, Hp and Gc into registers (all issued before
-  // any is used): loaded during the head before.
+  // any is used): loaded during the head before.  Waves 0-7 read x rows,
+  // waves 8-15 dy rows, one 16-byte vector per thread, through a range over
+  // the chunk's rows of the head (rows past len read 0); Hp and Gc through
+  // ranges over their blocks (threads past a block's end read 0).  Offsets
+  // are 32-bit: a load costs one address add, not 64-bit row arithmetic.
+  static_assert(NXY == 1 && 2 * Q * (P / VB) == kCThreads, "one x or dy vector per thread");
+  static_assert(NHV == 1, "at most one Hp and one Gc vector per thread");
   Vec16<T> vxy[NXY], vh[NHV], vg[NHV];
   float pdt = 0.0f;
+  const bool is_dy = wave >= kCWaves / 2;
+  const uint32_t xy_rb = (uint32_t)((is_dy ? k.dys : k.xs) * (int64_t)sizeof(T));  // row bytes
+  const T* const xy0 = is_dy ? DYp + row0 * k.dys : Xp + row0 * k.xs;
+  const uint32_t dt_rb = (uint32_t)(k.dts * (int64_t)sizeof(T));
+  auto vec_at = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    Vec16<T> v;
+    *reinterpret_cast<uint4*>(v.v) = buffer_load16<kPolicyDefault>(r, off);
+    return v;
+  };
   auto load_head = [&](int hh, int tid, int lane) {
     const int64_t unit = ubase + hh;
-#pragma unroll
-    for (int v = 0; v < NXY; ++v) {
-      const int idx = min(tid + v * kCThreads, 2 * Q * (P / VB) - 1);
-      const int which = idx / (Q * (P / VB)), r = idx % (Q * (P / VB));
-      const int s = min(r % Q, len - 1), p0 = (r / Q) * VB;
-      const T* src = which ? DYp + (row0 + s) * k.dys : Xp + (row0 + s) * k.xs;
-      vxy[v] = load16(src + (int64_t)hh * P + p0);
-    }
+    const unsigned r = (unsigned)tid % (Q * (P / VB)), s = r % Q, p0 = (r / Q) * VB;
+    vxy[0] = vec_at(uniform_rsrc(xy0 + (int64_t)hh * P, (uint32_t)len * xy_rb),
+                    s * xy_rb + p0 * (unsigned)sizeof(T));
     // dt: wave 0 only (the other waves' range is empty); tokens past len read 0
-    pdt = buffer_elem<T>(uniform_rsrc(DTp + row0 * k.dts + hh, wave == 0 ? (uint32_t)(len * k.dts * sizeof(T)) : 0u),
-                         (uint32_t)(lane * k.dts * sizeof(T)));
+    pdt = buffer_elem<T>(uniform_rsrc(DTp + row0 * k.dts + hh, wave == 0 ? (uint32_t)len * dt_rb : 0u),
+                         (uint32_t)lane * dt_rb);
+    constexpr uint32_t kHB = (uint32_t)(P * N * sizeof(T));
     const T* hp = static_cast<const T*>(k.hst) + (unit * (k.nchunks + 1) + c) * (P * N);
     const T* gp = static_cast<const T*>(k.gst) + (unit * k.nchunks + c) * (P * N);
-#pragma unroll
-    for (int v = 0; v < NHV; ++v) {
-      const int idx = min(tid + v * kCThreads, P * (N / VB) - 1) * VB;
-      vh[v] = load16(hp + idx);
-      vg[v] = load16(gp + idx);
-    }
+    vh[0] = vec_at(uniform_rsrc(hp, kHB), (uint32_t)tid * 16u);
+    vg[0] = vec_at(uniform_rsrc(gp, kHB), (uint32_t)tid * 16u);
   };
   f32x4 abt[DPW], act[DPW];  // dB, dC summed over the heads
 #pragma unroll
@@ -863,29 +870,22 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
     // The lane indices, re-derived every head from an opaque copy: the LDS
     // and global addresses built from them are then formed inside the loop
     // rather than hoisted out of it and held across it.
-    const int tid = opaque(tid_o), lane = tid % 64, r16 = lane % 16, g = lane / 16;
+    const int tid = opaque(tid_o), lane = tid & 63, r16 = lane & 15, g = lane >> 4;
     const float Ah = k.A[hh];
     const float Dh = k.D ? k.D[hh] : 0.0f;
     const HeadF F = head_floats(hh & 1);
 
     // ---- stage this head: x, dy rows token-major (zero past len), Hp as
     // stored, Gc n-major; wave 0: Lambda and its factors ----
-    const float dtl = lane < len ? pdt : 0.0f;
-#pragma unroll
-    for (int v = 0; v < NXY; ++v) {
-      const int idx = tid + v * kCThreads;
-      const int which = idx / (Q * (P / VB)), r = idx % (Q * (P / VB));
-      const int s = r % Q, p0 = (r / Q) * VB;
-      const Vec16<T> xv = s < len ? vxy[v] : zero16<T>();
-      if (idx < 2 * Q * (P / VB)) store16((which ? Yn : Xn) + s * NP + p0, xv);
+    const float dtl = pdt;  // 0 past len
+    {
+      const unsigned r = (unsigned)tid % (Q * (P / VB)), s = r % Q, p0 = (r / Q) * VB;
+      store16((is_dy ? Yn : Xn) + s * NP + p0, vxy[0]);
     }
-#pragma unroll
-    for (int v = 0; v < NHV; ++v) {
-      const int idx = tid + v * kCThreads;
-      if (idx < P * (N / VB)) {
-        store16(HpF + idx * VB, vh[v]);
-        store16(GT + (idx / (P / VB)) * TP2 + (idx % (P / VB)) * VB, vg[v]);
-      }
+    if ((unsigned)tid < P * (N / VB)) {
+      const unsigned idx = tid;
+      store16(HpF + idx * VB, vh[0]);
+      store16(GT + (idx / (P / VB)) * TP2 + (idx % (P / VB)) * VB, vg[0]);
     }
     if (wave == 0) {
       const float lv = chunk_cumsum(dtl * Ah * kLog2e, lane);
