@@ -30,8 +30,10 @@
 //    launch, one workgroup of 8 waves each, the fp32 P x N value in MFMA
 //    accumulators: forwards, storing the state before every chunk (and the
 //    final one); backwards, storing Gc, dL/dH at the end of every chunk.
-//    Both are stored in the storage type in layouts the chunk kernel reads
-//    directly (states in MFMA fragment order, Gc n-major).  With few walks the
+//    Both are stored in the storage type in MFMA fragment order: each lane
+//    writes its 16 bytes of a 1 KB fragment, so a store covers whole cache
+//    lines (an n-major dL/dH store, half lines, had made the backward walk
+//    twice as slow as the forward one).  With few walks the
 //    sequences are split into segments: a prepass walks each segment from
 //    zero, a combine chains the segments, and the walks start from the
 //    chained values.
@@ -94,7 +96,7 @@ struct BwdK {
   float* dD;
   float* dh0;
   void* hst;  // (batch, heads, nchunks + 1, P, N) storage type, fragment order
-  void* gst;  // (batch, heads, nchunks, N, P) storage type: dL/dH at each chunk's end
+  void* gst;  // (batch, heads, nchunks, P, N) storage type, fragment order: dL/dH at each chunk's end
   // sequence split (nseg > 1): per (unit, segment) fp32 P x N blocks and
   // log2 decays; see the launch for what each holds when
   float* seg_h;
@@ -340,7 +342,8 @@ struct WalkLds {
 //     from zero) writes the segment's end state and log2 decay.
 //   REV = true (gradients): chunks descending, a = dy, b = C, w_t =
 //     exp2(Lambda_t): V is dL/dH.  MAIN stores it at the end of every chunk
-//     n-major, before the chunk's update, and the first segment writes dh0;
+//     in fragment order, before the chunk's update, and the first segment
+//     writes dh0;
 //     PRE (segments 1..nseg-1, from zero) writes the result at the segment's
 //     start and its log2 decay.
 // MAIN segments start from the combined value of the split (or h0 / dhT).
@@ -417,10 +420,7 @@ __device__ __forceinline__ void walk(const BwdK& k, int pid, int total) {
     if (!MAIN || !owns) return;
     T* dst = Vst + (int64_t)c * (P * N);
 #pragma unroll
-    for (int t = 0; t < TPW; t += 2) {
-      if (REV) store8(dst + (nt * 16 + r16) * P + ((pt0 + t) / 2) * 32 + g * 8, acc[t], acc[t + 1]);
-      else store8(dst + state_frag<N>((pt0 + t) / 2, nt, lane), acc[t], acc[t + 1]);
-    }
+    for (int t = 0; t < TPW; t += 2) store8(dst + state_frag<N>((pt0 + t) / 2, nt, lane), acc[t], acc[t + 1]);
   };
 
   u32x4 pa[2][NAV], pb[2][NBV];
@@ -876,7 +876,7 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
     const HeadF F = head_floats(hh & 1);
 
     // ---- stage this head: x, dy rows token-major (zero past len), Hp as
-    // stored, Gc n-major; wave 0: Lambda and its factors ----
+    // stored, Gc as n-major rows; wave 0: Lambda and its factors ----
     const float dtl = pdt;  // 0 past len
     {
       const unsigned r = (unsigned)tid % (Q * (P / VB)), s = r % Q, p0 = (r / Q) * VB;
@@ -885,7 +885,12 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
     if ((unsigned)tid < P * (N / VB)) {
       const unsigned idx = tid;
       store16(HpF + idx * VB, vh[0]);
-      store16(GT + (idx / (P / VB)) * TP2 + (idx % (P / VB)) * VB, vg[0]);
+      // Gc in fragment order: element e of the block is lane ln's value j0
+      // of fragment (kp, nb), i.e. row n = nb*16 + ln%16, column
+      // p = kp*32 + (ln/16)*8 + j0 of Gc^T
+      const unsigned e = idx * VB, fid = e / 512, ln = (e / 8) % 64, j0 = e % 8;
+      const unsigned n = (fid % TN) * 16 + ln % 16, p = (fid / TN) * 32 + (ln / 16) * 8 + j0;
+      store16(GT + n * TP2 + p, vg[0]);
     }
     if (wave == 0) {
       const float lv = chunk_cumsum(dtl * Ah * kLog2e, lane);
