@@ -106,6 +106,9 @@ struct BwdK {
   int64_t seqlen;
   int n_heads, heads, nchunks, accumulate;
   int nseg, seg_chunks;
+  // chunk kernel: heads [h0g, h0g + hg) of this launch; bc_acc: add dB, dC
+  // into the values an earlier launch (heads before h0g) wrote
+  int h0g, hg, bc_acc;
 };
 
 template <typename T> constexpr int bpad() { return 16 / (int)sizeof(T); }
@@ -431,16 +434,17 @@ __device__ __forceinline__ void walk(const BwdK& k, int pid, int total) {
     const int64_t row0 = rowb + (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
     // every load unconditional, at a clamped row (rows past len are zeroed
-    // at staging): a load under a lane condition is waited for at its branch
+    // at staging): a load under a lane condition is waited for at its branch.
+    // Consecutive lanes read along a row, so a wave reads whole rows.
 #pragma unroll
     for (int v = 0; v < NAV; ++v) {
-      const int idx = min(tid + v * kBThreads, Q * (P / VB) - 1), s = min(idx % Q, len - 1);
-      pa[S][v] = *reinterpret_cast<const u32x4*>(Ap + (row0 + s) * as + (int64_t)h * P + (idx / Q) * VB);
+      const int idx = min(tid + v * kBThreads, Q * (P / VB) - 1), s = min(idx / (P / VB), len - 1);
+      pa[S][v] = *reinterpret_cast<const u32x4*>(Ap + (row0 + s) * as + (int64_t)h * P + (idx % (P / VB)) * VB);
     }
 #pragma unroll
     for (int v = 0; v < NBV; ++v) {
-      const int idx = min(tid + v * kBThreads, Q * (N / VB) - 1), s = min(idx % Q, len - 1);
-      pb[S][v] = *reinterpret_cast<const u32x4*>(Bp + (row0 + s) * bs + (idx / Q) * VB);
+      const int idx = min(tid + v * kBThreads, Q * (N / VB) - 1), s = min(idx / (N / VB), len - 1);
+      pb[S][v] = *reinterpret_cast<const u32x4*>(Bp + (row0 + s) * bs + (idx % (N / VB)) * VB);
     }
     // dt: wave 0 only (the other waves' range is empty); tokens past len read 0
     pdt[S] = buffer_elem<T>(uniform_rsrc(DTp + row0 * k.dts + h, wave == 0 ? (uint32_t)(len * k.dts * sizeof(T)) : 0u),
@@ -456,17 +460,17 @@ __device__ __forceinline__ void walk(const BwdK& k, int pid, int total) {
     const int len = plen[S];
 #pragma unroll
     for (int v = 0; v < NAV; ++v) {
-      const int idx = tid + v * kBThreads, s = idx % Q;
+      const int idx = tid + v * kBThreads, s = idx / (P / VB);
       const u32x4 raw = opaque(pa[S][v]);
       if (idx < Q * (P / VB))
-        *reinterpret_cast<u32x4*>(an + s * NP + (idx / Q) * VB) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(an + s * NP + (idx % (P / VB)) * VB) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int v = 0; v < NBV; ++v) {
-      const int idx = tid + v * kBThreads, s = idx % Q;
+      const int idx = tid + v * kBThreads, s = idx / (N / VB);
       const u32x4 raw = opaque(pb[S][v]);
       if (idx < Q * (N / VB))
-        *reinterpret_cast<u32x4*>(bn + s * NN + (idx / Q) * VB) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(bn + s * NN + (idx % (N / VB)) * VB) = s < len ? raw : u32x4{0u, 0u, 0u, 0u};
     }
     if (wave == 0) {
       const float d = opaque(pdt[S]);
@@ -612,7 +616,13 @@ struct ChunkLds {
                                   (size_t)P * N + (size_t)3 * kBQ * QP;
   static constexpr int kHeadFloats = 4 * kBQ + 2 * 4 * kBQ + 3 * 4 * kBQ + 2 * kCWaves;
   static constexpr int kFloats = 2 * kHeadFloats;  // by head parity
-  static constexpr size_t bytes = elems * sizeof(T) + kFloats * sizeof(float);
+  // per launch (at most kGH heads): dt of the chunk [head][token] in the
+  // storage type, ddt [head][token] fp32, and per head A, D, dA, dD
+  static constexpr int kGH = 64;
+  static constexpr int DTP = kBQ + 2, DDP = kBQ + 1;
+  static constexpr size_t bytes = elems * sizeof(T) + kFloats * sizeof(float) +
+                                  ((size_t)kGH * DTP * sizeof(T) + 3) / 4 * 4 +
+                                  ((size_t)kGH * DDP + 4 * kGH) * sizeof(float);
 };
 
 // Sum over the 64 lanes, in every lane: row sums by DPP, then the four rows'
@@ -687,6 +697,10 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
   // Per-head values, two sets by head parity: the tail of a head runs
   // during phase 1 of the next one.
   float* const fbase = reinterpret_cast<float*>(Kd + Q * QP);
+  constexpr int kGH = L::kGH, DTP = L::DTP, DDP = L::DDP;
+  T* const dtS = reinterpret_cast<T*>(fbase + L::kFloats);  // [kGH][DTP]
+  float* const ddtS = reinterpret_cast<float*>(dtS) + ((size_t)kGH * DTP * sizeof(T) + 3) / 4;  // [kGH][DDP]
+  float* const ADs = ddtS + kGH * DDP;  // A, D, dA, dD of the launch's heads
   struct HeadF {
     float *lam, *dtv, *eL, *sc, *rpart, *cpart, *t1p, *esp, *expl, *hgw, *ddw;
   };
@@ -730,7 +744,7 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
   for (int v = 0; v < NBC; ++v) {
     const int idx = tid + v * kCThreads;
     const int which = idx / (Q * (N / VB)), r = idx % (Q * (N / VB));
-    const int s = r % Q, n0 = (r / Q) * VB;
+    const int s = r / (N / VB), n0 = (r % (N / VB)) * VB;
     if (idx < 2 * Q * (N / VB)) {
       const T* src = static_cast<const T*>(which ? k.C : k.B) + (row0 + min(s, len - 1)) * (which ? k.cs : k.bs);
       const Vec16<T> bv = load16(src + n0);
@@ -738,6 +752,21 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
     }
   }
   for (int i = tid; i < 3 * Q * QP; i += kCThreads) Mq[i] = from_f32<T>(0.0f);
+  // dt of the launch's heads over the chunk, one 2- or 4-byte element per
+  // lane, 64 consecutive heads of a token per wave (rows past len and heads
+  // past hg read 0); A and D of the heads
+  {
+    const auto rdt = uniform_rsrc(DTp + row0 * k.dts + k.h0g, (uint32_t)(len * k.dts * sizeof(T)));
+    for (int i = tid; i < Q * kGH; i += kCThreads) {
+      const int t = i / kGH, hl = i % kGH;
+      const uint32_t off = hl < k.hg ? (uint32_t)((t * k.dts + hl) * sizeof(T)) : 0x7ffffff0u;
+      dtS[hl * DTP + t] = from_f32<T>(buffer_elem<T>(rdt, off));
+    }
+    if (tid < k.hg) {
+      ADs[tid] = k.A[k.h0g + tid];
+      ADs[kGH + tid] = k.D ? k.D[k.h0g + tid] : 0.0f;
+    }
+  }
   __syncthreads();
   // this wave's Q x Q block (sb, tb), tb >= sb: lane slot i is s = sb*16 + 4g + i,
   // t = tb*16 + r16; gq = B_s . C_t
@@ -760,18 +789,19 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
 
   // Per-head rows (x, dy), dt, Hp and Gc into registers (all issued before
   // any is used): loaded during the head before.  Waves 0-7 read x rows,
-  // waves 8-15 dy rows, one 16-byte vector per thread, through a range over
+  // waves 8-15 dy rows, one 16-byte vector per thread, consecutive lanes
+  // along a row (a wave reads whole rows: a lane per row had made every load
+  // touch 64 cache lines and the vector memory unit the bottleneck of the
+  // head boundary), through a range over
   // the chunk's rows of the head (rows past len read 0); Hp and Gc through
   // ranges over their blocks (threads past a block's end read 0).  Offsets
   // are 32-bit: a load costs one address add, not 64-bit row arithmetic.
   static_assert(NXY == 1 && 2 * Q * (P / VB) == kCThreads, "one x or dy vector per thread");
   static_assert(NHV == 1, "at most one Hp and one Gc vector per thread");
   Vec16<T> vxy[NXY], vh[NHV], vg[NHV];
-  float pdt = 0.0f;
   const bool is_dy = wave >= kCWaves / 2;
   const uint32_t xy_rb = (uint32_t)((is_dy ? k.dys : k.xs) * (int64_t)sizeof(T));  // row bytes
   const T* const xy0 = is_dy ? DYp + row0 * k.dys : Xp + row0 * k.xs;
-  const uint32_t dt_rb = (uint32_t)(k.dts * (int64_t)sizeof(T));
   auto vec_at = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
     Vec16<T> v;
     *reinterpret_cast<uint4*>(v.v) = buffer_load16<kPolicyDefault>(r, off);
@@ -779,12 +809,9 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
   };
   auto load_head = [&](int hh, int tid, int lane) {
     const int64_t unit = ubase + hh;
-    const unsigned r = (unsigned)tid % (Q * (P / VB)), s = r % Q, p0 = (r / Q) * VB;
+    const unsigned r = (unsigned)tid % (Q * (P / VB)), s = r / (P / VB), p0 = (r % (P / VB)) * VB;
     vxy[0] = vec_at(uniform_rsrc(xy0 + (int64_t)hh * P, (uint32_t)len * xy_rb),
                     s * xy_rb + p0 * (unsigned)sizeof(T));
-    // dt: wave 0 only (the other waves' range is empty); tokens past len read 0
-    pdt = buffer_elem<T>(uniform_rsrc(DTp + row0 * k.dts + hh, wave == 0 ? (uint32_t)len * dt_rb : 0u),
-                         (uint32_t)lane * dt_rb);
     constexpr uint32_t kHB = (uint32_t)(P * N * sizeof(T));
     const T* hp = static_cast<const T*>(k.hst) + (unit * (k.nchunks + 1) + c) * (P * N);
     const T* gp = static_cast<const T*>(k.gst) + (unit * k.nchunks + c) * (P * N);
@@ -796,18 +823,18 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
   for (int j = 0; j < DPW; ++j) abt[j] = act[j] = f32x4{0, 0, 0, 0};
 
   const int tid_o = tid;
-  load_head(0, opaque(tid_o), opaque(tid_o) % 64);
-  // Every head issues its stores after the next head's loads, and the
+  load_head(k.h0g, opaque(tid_o), opaque(tid_o) % 64);
+  // Every head issues its dx stores after the next head's loads, and the
   // staging waits for those loads with the stores still in flight.  The loop
   // is entered with nothing issued after the first loads; the compiler merges
   // the two entries and would wait for every store.  So the entry issues as
   // many memory operations after them: stores through an empty range, which
-  // the hardware drops.
+  // the hardware drops (at offsets far apart, so that they are not merged).
   {
-    constexpr int kOps = (ACC ? 8 : 4) * UPW + (ACC ? 2 : 1) + 2;
+    constexpr int kOps = (ACC ? 8 : 4) * UPW;
     const auto none = uniform_rsrc(k.dA, 0u);
 #pragma unroll
-    for (int i = 0; i < kOps; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, 0);
+    for (int i = 0; i < kOps; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, i * 256, 0, 0);
   }
   // outputs of this chunk through buffer resources over its rows: lanes at
   // rows past len fall outside the range and are dropped, so no store sits
@@ -815,13 +842,13 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
   // also wait for all earlier stores)
   const auto rdb = uniform_rsrc(k.dB + row0 * k.dbs, (uint32_t)(len * k.dbs * sizeof(float)));
   const auto rdc = uniform_rsrc(k.dC + row0 * k.dcs, (uint32_t)(len * k.dcs * sizeof(float)));
-  const auto rdA = uniform_rsrc(k.dA, (uint32_t)(k.n_heads * sizeof(float)));
-  const auto rdD = uniform_rsrc(k.dD, k.dD ? (uint32_t)(k.n_heads * sizeof(float)) : 0u);
 
-  // ---- tail of head th (one wave): dLambda -> da (suffix sum) -> ddt, dA, dD ----
+  // ---- tail of head th (one wave): dLambda -> da (suffix sum) -> ddt, dA, dD
+  // of the head into LDS (written out once per chunk) ----
   auto run_tail = [&](int th, int lane) {
     const HeadF F = head_floats(th & 1);
-    const float Ah = k.A[th];
+    const int thl = th - k.h0g;
+    const float Ah = ADs[thl];
     {
       const int t = lane, tb = t / 16;
       // fixed summation order: the result does not depend on wave timing
@@ -850,36 +877,33 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
       float xu = 0.0f;
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt) xu += F.expl[pt * Q + t];
-      // ddt through a range over this chunk's rows (tokens past len dropped);
-      // dt is 0 past len, so dA takes nothing from them
-      const auto rdt = uniform_rsrc(DDTp + row0 * k.ddts + th, (uint32_t)(len * k.ddts * sizeof(T)));
-      const uint32_t off = (uint32_t)(t * k.ddts * sizeof(T));
-      const float old = ACC ? buffer_elem<T>(rdt, off) : 0.0f;
-      buffer_store_elem<T>(rdt, off, old + xu + Ah * suf);
+      // dt is 0 past len, so dA takes nothing from those tokens
+      ddtS[thl * DDP + t] = xu + Ah * suf;
       const float da = wave_sum(F.dtv[t] * suf);
       float ddh = 0.0f;
 #pragma unroll
       for (int j = 0; j < kCWaves; ++j) ddh += F.ddw[j];
-      // one lane adds each (offsets of the others lie outside the ranges)
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(da, rdA, lane == 0 ? th * 4 : 0x7ffffff0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(ddh, rdD, lane == 0 ? th * 4 : 0x7ffffff0, 0, 0);
+      if (lane == 0) {
+        ADs[2 * kGH + thl] = da;
+        ADs[3 * kGH + thl] = ddh;
+      }
     }
   };
 
-  for (int hh = 0; hh < k.heads; ++hh) {
+  const int hend = k.h0g + k.hg;
+  for (int hh = k.h0g; hh < hend; ++hh) {
     // The lane indices, re-derived every head from an opaque copy: the LDS
     // and global addresses built from them are then formed inside the loop
     // rather than hoisted out of it and held across it.
     const int tid = opaque(tid_o), lane = tid & 63, r16 = lane & 15, g = lane >> 4;
-    const float Ah = k.A[hh];
-    const float Dh = k.D ? k.D[hh] : 0.0f;
+    const float Ah = ADs[hh - k.h0g];
+    const float Dh = ADs[kGH + hh - k.h0g];
     const HeadF F = head_floats(hh & 1);
 
     // ---- stage this head: x, dy rows token-major (zero past len), Hp as
     // stored, Gc as n-major rows; wave 0: Lambda and its factors ----
-    const float dtl = pdt;  // 0 past len
     {
-      const unsigned r = (unsigned)tid % (Q * (P / VB)), s = r % Q, p0 = (r / Q) * VB;
+      const unsigned r = (unsigned)tid % (Q * (P / VB)), s = r / (P / VB), p0 = (r % (P / VB)) * VB;
       store16((is_dy ? Yn : Xn) + s * NP + p0, vxy[0]);
     }
     if ((unsigned)tid < P * (N / VB)) {
@@ -893,6 +917,7 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
       store16(GT + n * TP2 + p, vg[0]);
     }
     if (wave == 0) {
+      const float dtl = to_f32(dtS[(hh - k.h0g) * DTP + lane]);  // 0 past len
       const float lv = chunk_cumsum(dtl * Ah * kLog2e, lane);
       const float le = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), 63));
       F.lam[lane] = lv;
@@ -903,11 +928,11 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
     __syncthreads();
     // the next head's inputs (this one's again at the last), in flight
     // while this one is computed
-    load_head(min(hh + 1, k.heads - 1), tid, lane);
+    load_head(min(hh + 1, hend - 1), tid, lane);
 
     // ================= phase 1 =================
     // the previous head's tail, on a wave without a Q x Q block
-    if (wave == kCWaves - 1 && hh > 0) run_tail(hh - 1, lane);
+    if (wave == kCWaves - 1 && hh > k.h0g) run_tail(hh - 1, lane);
     // ---- the wave's Q x Q block: x_s . dy_t, masked decay, M, K, Kd, W sums ----
     if (wave < NQQ) {
       f32x4 qq = {0, 0, 0, 0};
@@ -1096,9 +1121,31 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
     // they are rewritten two heads later)
   }
 
-  if (wave == kCWaves - 1) run_tail(k.heads - 1, opaque(lane));
+  if (wave == kCWaves - 1) run_tail(hend - 1, opaque(lane));
+  __syncthreads();
+  // ---- ddt of the launch's heads (64 consecutive heads of a token per wave,
+  // rows past len and heads past hg dropped), then dA and dD, one head per
+  // lane ----
+  {
+    const auto rdt = uniform_rsrc(DDTp + row0 * k.ddts + k.h0g, (uint32_t)(len * k.ddts * sizeof(T)));
+    for (int i = tid; i < Q * kGH; i += kCThreads) {
+      const int t = i / kGH, hl = i % kGH;
+      const uint32_t off = hl < k.hg ? (uint32_t)((t * k.ddts + hl) * sizeof(T)) : 0x7ffffff0u;
+      const float old = ACC ? buffer_elem<T>(rdt, off) : 0.0f;
+      buffer_store_elem<T>(rdt, off, old + ddtS[hl * DDP + t]);
+    }
+    static_assert(kGH == 64, "one head per lane");
+    if (wave == 0) {
+      const auto rdA = uniform_rsrc(k.dA + k.h0g, (uint32_t)(k.hg * sizeof(float)));
+      const auto rdD = uniform_rsrc(k.dD + k.h0g, k.dD ? (uint32_t)(k.hg * sizeof(float)) : 0u);
+      const int off = lane < k.hg ? lane * 4 : 0x7ffffff0;
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(ADs[2 * kGH + lane], rdA, off, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(ADs[3 * kGH + lane], rdD, off, 0, 0);
+    }
+  }
 
   // ---- dB and dC of this chunk, summed over the heads ----
+  const bool acc_bc = ACC || k.bc_acc;
   if (down) {
     const int s4 = dsb * 16 + g * 4;
 #pragma unroll
@@ -1108,8 +1155,8 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
         const int col = (dnt0 + j) * 16 + r16;
         const uint32_t ob = (uint32_t)(((s4 + i) * k.dbs + col) * sizeof(float));
         const uint32_t oc = (uint32_t)(((s4 + i) * k.dcs + col) * sizeof(float));
-        const float pb = ACC ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdb, (int)ob, 0, 0)) : 0.0f;
-        const float pc = ACC ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdc, (int)oc, 0, 0)) : 0.0f;
+        const float pb = acc_bc ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdb, (int)ob, 0, 0)) : 0.0f;
+        const float pc = acc_bc ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdc, (int)oc, 0, 0)) : 0.0f;
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pb + abt[j][i]), rdb, (int)ob, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pc + act[j][i]), rdc, (int)oc, 0, 0);
       }
@@ -1155,12 +1202,24 @@ hipError_t launch_shape(const BwdK& k, int64_t batch, hipStream_t s) {
   hipLaunchKernelGGL((bwd_walks_kernel<T, P, N>), dim3(2 * walks), dim3(kBThreads), lds1, s, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // the chunks in parallel, one launch per group of at most kGH heads (the
+  // per-head dt, ddt, A, D, dA, dD of a launch live in LDS); later groups
+  // add their dB, dC to the earlier ones'
   const unsigned grid = (unsigned)(batch * k.nchunks);
-  if (k.accumulate)
-    hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N, true>), dim3(grid), dim3(kCThreads), lds2, s, k);
-  else
-    hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N, false>), dim3(grid), dim3(kCThreads), lds2, s, k);
-  return hipGetLastError();
+  constexpr int kGH = ChunkLds<T, P, N>::kGH;
+  for (int g0 = 0; g0 < k.heads; g0 += kGH) {
+    BwdK kg = k;
+    kg.h0g = g0;
+    kg.hg = std::min(kGH, k.heads - g0);
+    kg.bc_acc = g0 > 0;
+    if (k.accumulate)
+      hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N, true>), dim3(grid), dim3(kCThreads), lds2, s, kg);
+    else
+      hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N, false>), dim3(grid), dim3(kCThreads), lds2, s, kg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -1200,7 +1259,7 @@ size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t
 }
 
 hipError_t launch_ssd_backward(const BwdArgs& a, void* workspace, hipStream_t s) {
-  BwdK k;
+  BwdK k{};
   k.x = a.x;
   k.xs = a.xs;
   k.dt = a.dt;

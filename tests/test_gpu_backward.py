@@ -23,6 +23,8 @@ TINY = synth.WORKLOADS["tiny"]
 M130 = synth.WORKLOADS["130m"]
 B14 = synth.WORKLOADS["1.4b"]
 M130_N64 = dataclasses.replace(M130, name="130m-n64", d_state=64)
+# 80 heads: more than one launch's worth (64) of heads in the chunk kernel
+M130_H80 = dataclasses.replace(M130, name="130m-h80", d_model=2560, d_inner=5120)
 
 NAMES = ("dx", "ddt", "dA", "dB", "dC", "dD", "dinitial_state")
 
@@ -144,6 +146,17 @@ def test_backward_dstate64_bf16():
     for h in (3, 24):
         say(f"backward 130m d_state=64 bf16 heads={h}")
         _check(_run(w, inp, h), _oracle(inp, h), h, TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("h", [64, 70, 80])
+def test_backward_more_heads_than_one_launch(h):
+    """80 heads of 64: the chunk kernel takes at most 64 heads per launch
+    (their per-head values live in LDS), so 70 and 80 active heads run as
+    two launches whose dB, dC add up; 64 is exactly one."""
+    w = M130_H80
+    inp = _inputs(w, 1, 300, salt=9)
+    say(f"backward 80-head bf16 l=300 heads={h}")
+    _check(_run(w, inp, h), _oracle(inp, h), h, TOL[torch.bfloat16])
 
 
 def test_backward_without_optional_inputs():
