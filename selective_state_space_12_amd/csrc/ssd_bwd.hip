@@ -324,6 +324,26 @@ __device__ __forceinline__ void frag_cols(Frag8<T>& f, const T* M, int ld, int r
   }
 }
 
+// Rows ra..ra+3 of column c0 + lane%16 of a row-major LDS tile M (pitch
+// ld), as fp32: one transpose load in 16-bit storage (frag_cols' first
+// half with column step 4), four element loads in fp32.
+template <typename T>
+__device__ __forceinline__ f32x4 col4(const T* M, int ld, int ra, int c0, int lane) {
+  const int q = lane & 15;
+  if constexpr (sizeof(T) == 2) {
+    typedef short short4v __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) short4v lds_short4;
+    const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_short4*)(const_cast<T*>(M) + (ra + (q >> 2)) * ld + c0 + (q & 3) * 4));
+    const uint2 u = __builtin_bit_cast(uint2, v);
+    return f32x4{__builtin_bit_cast(float, u.x << 16), __builtin_bit_cast(float, u.x & 0xffff0000u),
+                 __builtin_bit_cast(float, u.y << 16), __builtin_bit_cast(float, u.y & 0xffff0000u)};
+  } else {
+    return f32x4{M[ra * ld + c0 + q], M[(ra + 1) * ld + c0 + q], M[(ra + 2) * ld + c0 + q],
+                 M[(ra + 3) * ld + c0 + q]};
+  }
+}
+
 // LDS of a walk: two buffers (by chunk parity), each the chunk's rows of the
 // d_head stream (x forwards, dy backwards) and of the d_state stream (B
 // forwards, C backwards) token-major, with Lambda and the per-token weights.
@@ -966,9 +986,7 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
       // column sums (over t, per s): over the 16 lanes of each group
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[i] = row16_sum(w[i]);
-      if (r16 == 0)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) F.cpart[qtb * Q + s4 + i] = w[i];
+      if (r16 == 0) *reinterpret_cast<f32x4*>(F.cpart + qtb * Q + s4) = f32x4{w[0], w[1], w[2], w[3]};
     }
     // ---- <Gc, Hp> over the wave's state fragment (kp, nb) ----
     if (NFR >= kCWaves || wave < NFR) {
@@ -1022,6 +1040,12 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
       const f32x4 dts = *reinterpret_cast<const f32x4*>(F.dtv + s4);
       const f32x4 et = *reinterpret_cast<const f32x4*>(F.eL + s4);
       float e[4], f[4];
+      f32x4 bc[DPW], cc[DPW];  // B, C at rows s4 + i, columns of the wave's tiles
+#pragma unroll
+      for (int j = 0; j < DPW; ++j) {
+        bc[j] = col4(Bn, NN, s4, (dnt0 + j) * 16, lane);
+        cc[j] = col4(Cn, NN, s4, (dnt0 + j) * 16, lane);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float v = 0.0f, u = 0.0f;
@@ -1029,18 +1053,16 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
         for (int j = 0; j < DPW; ++j) {
           ab[j][i] *= scs[i];
           ac[j][i] *= et[i];
-          v += ab[j][i] * to_f32(Bn[(s4 + i) * NN + (dnt0 + j) * 16 + r16]);
-          u += ac[j][i] * to_f32(Cn[(s4 + i) * NN + (dnt0 + j) * 16 + r16]);
+          v += ab[j][i] * bc[j][i];
+          u += ac[j][i] * cc[j][i];
         }
         e[i] = row16_sum(v) * dts[i];
         f[i] = row16_sum(u);
       }
-      if (r16 == 0)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          F.esp[dq * Q + s4 + i] = e[i];
-          F.t1p[dq * Q + s4 + i] = f[i];
-        }
+      if (r16 == 0) {
+        *reinterpret_cast<f32x4*>(F.esp + dq * Q + s4) = f32x4{e[0], e[1], e[2], e[3]};
+        *reinterpret_cast<f32x4*>(F.t1p + dq * Q + s4) = f32x4{f[0], f[1], f[2], f[3]};
+      }
     }
     __syncthreads();
 
@@ -1063,9 +1085,10 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         old[i] = ACC ? buffer_elem<T>(rdx, (uint32_t)(((s4 + i) * k.dxs + p) * sizeof(T))) : 0.0f;
+      const f32x4 xc = col4(Xn, NP, s4, upt * 16, lane), yc = col4(Yn, NP, s4, upt * 16, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float xv = to_f32(Xn[(s4 + i) * NP + p]), yv = to_f32(Yn[(s4 + i) * NP + p]);
+        const float xv = xc[i], yv = yc[i];
         ex[i] = xv * au[i];
         dd += xv * yv;
         dxv[i] = dts[i] * au[i] + Dh * yv;
@@ -1075,9 +1098,7 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
         buffer_store_elem<T>(rdx, (uint32_t)(((s4 + i) * k.dxs + p) * sizeof(T)), old[i] + dxv[i]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) ex[i] = row16_sum(ex[i]);
-      if (r16 == 0)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) F.expl[upt * Q + s4 + i] = ex[i];
+      if (r16 == 0) *reinterpret_cast<f32x4*>(F.expl + upt * Q + s4) = f32x4{ex[0], ex[1], ex[2], ex[3]};
     }
     dd = wave_sum(dd);
     if (lane == 0) F.ddw[wave] = dd;
