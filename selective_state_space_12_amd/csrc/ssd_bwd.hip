@@ -628,9 +628,11 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdK k) {
 // transposed copy is kept (119 KB at d_head 64, d_state 128 in bf16).
 template <typename T, int P, int N>
 struct ChunkLds {
-  static constexpr int NP = P + bpad<T>();    // token-major x and dy rows
-  static constexpr int NN = N + bpad<T>();    // token-major B and C rows
-  static constexpr int TP2 = P + bpad<T>();   // Gc^T rows (n-major)
+  // row pitches: 16-bit x, dy and Gc^T rows padded by 32 bytes rather than
+  // 16 (fewer bank conflicts in their transpose loads: about 1% of the call)
+  static constexpr int NP = P + (sizeof(T) == 2 ? 16 : bpad<T>());   // token-major x and dy rows
+  static constexpr int NN = N + bpad<T>();                           // token-major B and C rows
+  static constexpr int TP2 = P + (sizeof(T) == 2 ? 16 : bpad<T>());  // Gc^T rows (n-major)
   static constexpr int QP = kBQ + bpad<T>();  // M, K, Kd rows
   static constexpr size_t elems = (size_t)2 * kBQ * NP + (size_t)2 * kBQ * NN + (size_t)N * TP2 +
                                   (size_t)P * N + (size_t)3 * kBQ * QP;
