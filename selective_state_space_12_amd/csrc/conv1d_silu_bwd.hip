@@ -8,10 +8,12 @@
 //   dw_k     += sum_t dpre[t] u[t - 3 + k],  dbias += sum_t dpre[t]
 //
 // Design: HBM-bound streaming, as the forward conv.  A thread owns four
-// channels and a run of tokens; it slides a window of three inputs and
+// channels and a run of 128 tokens; it slides a window of three inputs and
 // three dpre values, so du[t-3] is complete once dpre[t] is known: the run
 // reads three tokens past its end (the halo whose dpre reaches back into the
-// run) and three before it.  The run that starts at token 0 also emits the
+// run) and three before it.  The streamed rows (inputs and dout) are read
+// with nontemporal loads (measured: 0.286 -> 0.258 ms at the 1.4B full
+// width; runs of 128 tokens rather than 64, 0.247 ms).  The run that starts at token 0 also emits the
 // conv-state rows' gradient.  A workgroup is 4 waves over 4 consecutive
 // runs of the same 64 channel groups; dw and dbias are summed over each run
 // in registers, over the 4 runs through LDS, and added with one fp32 atomic
@@ -28,7 +30,7 @@ namespace {
 constexpr int kLanes = 64;   // channel groups per workgroup
 constexpr int kRuns = 4;     // token runs per workgroup (one wave each)
 constexpr int kThreads = kLanes * kRuns;
-constexpr int kRun = 64;     // tokens per thread
+constexpr int kRun = 128;    // tokens per thread
 
 // Four consecutive channels of one token (8 bytes of bf16, 16 of fp32): a
 // thread's share.  Four rather than a 16-byte vector of bf16 keeps the
@@ -49,6 +51,24 @@ __device__ __forceinline__ void load4f(const T* p, float (&o)[V]) {
     o[1] = v.y;
     o[2] = v.z;
     o[3] = v.w;
+  }
+}
+
+
+// The same for rows streamed once: a nontemporal load.
+template <typename T>
+__device__ __forceinline__ void load4f_nt(const T* p, float (&o)[V]) {
+  if constexpr (sizeof(T) == 2) {
+    typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t u = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    o[0] = __builtin_bit_cast(float, u[0] << 16);
+    o[1] = __builtin_bit_cast(float, u[0] & 0xffff0000u);
+    o[2] = __builtin_bit_cast(float, u[1] << 16);
+    o[3] = __builtin_bit_cast(float, u[1] & 0xffff0000u);
+  } else {
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
   }
 }
 
@@ -151,8 +171,8 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_bwd_kernel(
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
       const int tc = min(tg + i, tlast);
-      load4f(in + (row0 + tc) * in_stride + c, u[i]);
-      load4f(dout + (row0 + tc) * dout_stride + c, go[i]);
+      load4f_nt(in + (row0 + tc) * in_stride + c, u[i]);
+      load4f_nt(dout + (row0 + tc) * dout_stride + c, go[i]);
     }
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
