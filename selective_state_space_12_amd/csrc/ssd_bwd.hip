@@ -459,7 +459,10 @@ __device__ __forceinline__ void walk(const BwdK& k, int pid, int total) {
 #pragma unroll
     for (int v = 0; v < NAV; ++v) {
       const int idx = min(tid + v * kBThreads, Q * (P / VB) - 1), s = min(idx / (P / VB), len - 1);
-      pa[S][v] = *reinterpret_cast<const u32x4*>(Ap + (row0 + s) * as + (int64_t)h * P + (idx % (P / VB)) * VB);
+      // this head's rows, not read again by the walk: nontemporal (about 1.5%
+      // of the call; the B and C rows, shared by the heads, stay cached)
+      pa[S][v] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(Ap + (row0 + s) * as + (int64_t)h * P + (idx % (P / VB)) * VB));
     }
 #pragma unroll
     for (int v = 0; v < NBV; ++v) {
