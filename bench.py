@@ -63,7 +63,8 @@ SCAN_SRCS = [os.path.join(ROOT, "selective_state_space_12_amd", "csrc", f)
              for f in ("ssd_fwd_bf16.hip", "device_common.h")]
 # the kernels of one call: tile prep, and with the sequences split the
 # state-only pass and the combine, then the scan (absent ones are skipped)
-SCAN_KERNELS = ("tile_prep_kernel", "ssd_bf16_seg_kernel", "seg_combine_bf16_kernel", "ssd_bf16_kernel")
+SCAN_KERNELS = ("tile_prep_kernel", "ssd_bf16_seg_kernel", "ssd_bf16_seg2_kernel", "seg_combine_bf16_kernel",
+                "ssd_bf16_kernel")
 
 
 COPY_BYTES = 1 << 30

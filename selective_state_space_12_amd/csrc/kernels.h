@@ -164,21 +164,27 @@ struct FuseArgs {
 
 // bf16, d_head 64, d_state 128, chunk 128 or 256 (ssd_fwd_bf16.hip).
 bool bf16_path(int64_t d_head, int64_t d_state, int64_t chunk, int dtype);
-size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t units = 0);
+// allow_pairs: the call may run its state-only pass two heads per workgroup
+// (calls without the fused conv and without per-sequence widths).
+size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t units = 0,
+                            bool allow_pairs = false);
 // The bf16 path's cut (128-token tiles): the segment count that minimises an
 // estimate of the call's time in tile-walk units, counting workgroup rounds
 // of one workgroup per CU, the per-walk start-up and the prepass and combine
 // that a split adds.
 void fwd_plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int* ntiles, int* nseg,
-                   int* seg_tiles, int64_t units = 0);
+                   int* seg_tiles, int64_t units = 0, bool allow_pairs = false);
 // The full plan: main segments of seg_tiles tiles; for a split call, each
 // segment but the last is cut into ppseg pieces of piece_tiles tiles (the
-// last piece may be shorter, none empty) for the state-only pass.
+// last piece may be shorter, none empty) for the state-only pass, which
+// takes two heads per workgroup when pairs is set.
 struct Bf16Plan {
   int ntiles = 0, nseg = 1, seg_tiles = 1, ppseg = 1, piece_tiles = 1;
+  bool pairs = false;
   int nslot() const { return nseg > 1 ? (nseg - 1) * ppseg + 1 : 1; }
 };
-Bf16Plan plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int64_t units = 0);
+Bf16Plan plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int64_t units = 0,
+                   bool allow_pairs = false);
 hipError_t launch_ssd_forward_bf16(const FwdArgs& a, void* workspace, hipStream_t s);
 // The same with the conv and dt transform fused in: a.x, a.B, a.C are the raw
 // conv input's x, B and C columns and a.dt the raw dt.  The conv state, if

@@ -730,7 +730,7 @@ int fwd_segments(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
                  int64_t d_state, int64_t chunk, int dtype, int64_t units) {
   int nc, nseg, per;
   if (bf16_path(d_head, d_state, chunk, dtype))
-    fwd_plan_bf16(batch, seqlen, heads, &nc, &nseg, &per, units);
+    fwd_plan_bf16(batch, seqlen, heads, &nc, &nseg, &per, units, units == 0);
   else
     fwd_plan(batch, seqlen, heads, chunk, &nc, &nseg, &per, units);
   return nseg;
@@ -739,7 +739,7 @@ int fwd_segments(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
 size_t fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t d_head,
                            int64_t d_state, int64_t chunk, int dtype, int64_t units) {
   if (bf16_path(d_head, d_state, chunk, dtype))
-    return bf16_workspace_bytes(batch, seqlen, heads, units);
+    return bf16_workspace_bytes(batch, seqlen, heads, units, units == 0);
   int nc, nseg, per;
   fwd_plan(batch, seqlen, heads, chunk, &nc, &nseg, &per, units);
   if (nseg <= 1) return 0;

@@ -967,6 +967,241 @@ __global__ __launch_bounds__(512) void ssd_bf16_seg_kernel(BK k) {
     stage_waves<false, FUSED>(k, smem, b, h, piece, c0, c1, wave);
 }
 
+// ---------------------------------------------------------------------------
+// State-only pass over two heads of a sequence per workgroup (calls without
+// the fused conv and without per-sequence widths).  The state waves load
+// each tile's B^T fragments once and update both heads' states with them, so
+// the bytes the CU reads per head and tile fall from 48 KB (16 KB of x, 32
+// KB of B^T) to 32 KB; the staging waves stage both heads' x.  Same
+// arithmetic per head as the one-head pass.  With an odd head count the last
+// workgroup repeats its head as the second and stores it once.
+constexpr int kXBuf2 = 2 * kXE;  // per parity: head 0's scaled x, then head 1's
+constexpr size_t kDecOff2 = (size_t)(2 * kXBuf2 + kStg) * sizeof(bf16);
+constexpr size_t kLdsSeg2 = kDecOff2 + 2 * 3 * kDec * sizeof(float);  // per head: three decay sets
+
+__device__ void state_waves2(const BK& k, unsigned char* smem, int b, int h0, int nh, int piece,
+                             int c0, int c1, int u) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+  const bf16* xbuf = reinterpret_cast<const bf16*>(smem);
+  const float* dbuf = reinterpret_cast<const float*>(smem + kDecOff2);
+  f32x4 hacc[2][kNBW][kPB];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int j = 0; j < kNBW; ++j)
+#pragma unroll
+      for (int pb = 0; pb < kPB; ++pb) hacc[e][j][pb] = f32x4{0, 0, 0, 0};
+  Frag8<bf16> bt[kNBW][kSB];
+  auto load_bt = [&](int c, int ks) {
+    const auto r = tile_frags(k, b, c);
+#pragma unroll
+    for (int j = 0; j < kNBW; ++j)
+      bt[j][ks] = as_frag(
+          buffer_load16<kPolicyDefault>(r, frag_off(kBT0 + (u * kNBW + j) * kSB + ks, lane)));
+  };
+  const int cl = c1 - 1;
+#pragma unroll
+  for (int ks = 0; ks < kSB; ++ks) load_bt(c0, ks);
+  __syncthreads();  // decay cumsums of the first tiles
+  __syncthreads();  // x copies of the first tile
+
+  for (int c = c0; c < c1; ++c) {
+    const bf16* XF = xbuf + (c & 1) * kXBuf2;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float rt = __builtin_amdgcn_exp2f(dbuf[(e * 3 + c % 3) * kDec + kQ - 1]);
+#pragma unroll
+      for (int j = 0; j < kNBW; ++j)
+#pragma unroll
+        for (int pb = 0; pb < kPB; ++pb) hacc[e][j][pb] *= rt;
+    }
+#pragma unroll
+    for (int ks = 0; ks < kSB; ++ks) {
+#pragma unroll
+      for (int pb = 0; pb < kPB; ++pb) {
+        const Frag8<bf16> x0 = lds_frag(XF + foff(ks * kPB + pb, lane));
+        const Frag8<bf16> x1 = lds_frag(XF + kXE + foff(ks * kPB + pb, lane));
+#pragma unroll
+        for (int j = 0; j < kNBW; ++j) {
+          hacc[0][j][pb] = mma(bt[j][ks], x0, hacc[0][j][pb]);
+          hacc[1][j][pb] = mma(bt[j][ks], x1, hacc[1][j][pb]);
+        }
+      }
+      load_bt(min(c + 1, cl), ks);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    if (e >= nh) break;
+    float* hout = k.seg_state + (((int64_t)b * k.heads + h0 + e) * k.nslot + piece) * (kP * kN);
+#pragma unroll
+    for (int j = 0; j < kNBW; ++j)
+#pragma unroll
+      for (int pb = 0; pb < kPB; ++pb)
+        *reinterpret_cast<f32x4*>(hout + chan(pb, r16) * kN + u * 32 + g * 8 + j * 4) = hacc[e][j][pb];
+  }
+}
+
+__device__ void stage_waves2(const BK& k, unsigned char* smem, int b, int h0, int nh, int piece,
+                             int c0, int c1, int v) {
+  const int lane = threadIdx.x & 63;
+  bf16* xbuf = reinterpret_cast<bf16*>(smem);
+  bf16* stg = xbuf + 2 * kXBuf2 + v * kStgRows * kP;  // this wave's staged rows
+  float* dbuf = reinterpret_cast<float*>(smem + kDecOff2);
+  const int64_t rowb = (int64_t)b * k.seqlen;
+  const int hs[2] = {h0, h0 + nh - 1};
+  const float Ah2[2] = {k.A[hs[0]] * kLog2e, k.A[hs[1]] * kLog2e};
+  const int pc = lane & 7;
+  // rows of both heads: (head 0: r0..r3, head 1: r4..r7), four named
+  // registers per head (an array was placed in scratch in the one-head pass)
+  struct XSet { uint4 r0, r1, r2, r3; };
+  XSet xs0, xs1;
+  const uint32_t rowbytes = (uint32_t)(k.xs * (int64_t)sizeof(bf16));
+  auto load_x = [&](int c) {
+    const int len = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ);
+    auto head_rows = [&](int hh, XSet& xs) {
+      const uint64_t tile0 = reinterpret_cast<uint64_t>(k.x) +
+                             (uint64_t)(((rowb + (int64_t)c * kQ) * k.xs + (int64_t)hh * kP) * sizeof(bf16));
+      const auto r = uniform_rsrc(tile0, (uint32_t)len * rowbytes);
+      auto row = [&](int i) {
+        const int s = v * 32 + i * 8 + (lane >> 3);
+        return buffer_load16<kPolicyNT>(r, (uint32_t)s * rowbytes + pc * 16);
+      };
+      xs.r0 = row(0);
+      xs.r1 = row(1);
+      xs.r2 = row(2);
+      xs.r3 = row(3);
+    };
+    head_rows(hs[0], xs0);
+    head_rows(hs[1], xs1);
+  };
+  // raw rows out, fragments back, times the tile-end factor, for each head
+  // (LDS operations of one wave complete in order: head 1's rows are written
+  // after head 0's transposed reads)
+  auto commit = [&](int c) {
+    auto one = [&](const XSet& xs, int e) {
+      bf16* XF = xbuf + (c & 1) * kXBuf2 + e * kXE;
+      const float* d = dbuf + (e * 3 + c % 3) * kDec;
+      *reinterpret_cast<uint4*>(stg + soff(4 + (lane >> 3), pc)) = xs.r0;
+      *reinterpret_cast<uint4*>(stg + soff(12 + (lane >> 3), pc)) = xs.r1;
+      *reinterpret_cast<uint4*>(stg + soff(20 + (lane >> 3), pc)) = xs.r2;
+      *reinterpret_cast<uint4*>(stg + soff(28 + (lane >> 3), pc)) = xs.r3;
+      Frag8<bf16> f[kPB];
+#pragma unroll
+      for (int pb = 0; pb < kPB; ++pb) f[pb] = stg_frag(stg, 4 + (lane >> 4) * 8, pb, lane);
+      const float* ef = d + 3 * kQ + v * 32 + (lane >> 4) * 8;
+      const f32x4 e0 = *reinterpret_cast<const f32x4*>(ef);
+      const f32x4 e1 = *reinterpret_cast<const f32x4*>(ef + 4);
+#pragma unroll
+      for (int pb = 0; pb < kPB; ++pb)
+        *reinterpret_cast<uint4*>(XF + foff(v * kPB + pb, lane)) =
+            __builtin_bit_cast(uint4, scale8(f[pb], e0, e1).v);
+    };
+    one(xs0, 0);
+    one(xs1, 1);
+  };
+  auto load_dt = [&](int c, int hh) -> uint32_t {
+    const auto r = uniform_rsrc(k.dtT + (((int64_t)b * k.ntiles + c) * k.heads + hh) * kQ,
+                                (uint32_t)(kQ * sizeof(bf16)));
+    return buffer_load4<kPolicyDefault>(r, (uint32_t)lane * 4);
+  };
+  // the one-head pass's decay arrays (Lambda, dt, block-end and tile-end
+  // factors), each stage wave writing one, for head e
+  auto make_dec = [&](int c, int buf, uint32_t raw, int e) {
+    const int len = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ);
+    float dtr[2];
+    dtr[0] = 2 * lane < len ? __builtin_bit_cast(float, raw << 16) : 0.0f;
+    dtr[1] = 2 * lane + 1 < len ? __builtin_bit_cast(float, raw & 0xffff0000u) : 0.0f;
+    float* d = dbuf + (e * 3 + buf) * kDec;
+    const float v0 = dtr[0] * Ah2[e], v1 = dtr[1] * Ah2[e];
+    float incl = v0 + v1;
+    incl += dpp_f<0x111, 0xf>(incl);  // row_shr:1
+    incl += dpp_f<0x112, 0xf>(incl);  // row_shr:2
+    incl += dpp_f<0x114, 0xf>(incl);  // row_shr:4
+    incl += dpp_f<0x118, 0xf>(incl);  // row_shr:8
+    incl += dpp_f<0x142, 0xa>(incl);  // row_bcast:15 into rows 1 and 3
+    incl += dpp_f<0x143, 0xc>(incl);  // row_bcast:31 into rows 2 and 3
+    const float l0 = incl - v1, l1 = incl;
+    const float lend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
+    const float e0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 15));
+    const float e1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 31));
+    const float e2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 47));
+    const int row = lane >> 4;
+    const float lblk = row == 0 ? e0 : row == 1 ? e1 : row == 2 ? e2 : lend;
+    if (v == 0) {
+      *reinterpret_cast<float2*>(d + 2 * lane) = make_float2(l0, l1);
+    } else if (v == 1) {
+      *reinterpret_cast<float2*>(d + kQ + 2 * lane) = make_float2(dtr[0], dtr[1]);
+    } else if (v == 2) {
+      *reinterpret_cast<float2*>(d + 2 * kQ + 2 * lane) =
+          make_float2(__builtin_amdgcn_exp2f(lblk - l0) * dtr[0], __builtin_amdgcn_exp2f(lblk - l1) * dtr[1]);
+    } else {
+      *reinterpret_cast<float2*>(d + 3 * kQ + 2 * lane) =
+          make_float2(__builtin_amdgcn_exp2f(lend - l0) * dtr[0], __builtin_amdgcn_exp2f(lend - l1) * dtr[1]);
+    }
+    return lend;
+  };
+
+  // the one-head pass's schedule, for two heads
+  const int cl = c1 - 1;
+  float lam_seg[2] = {0.0f, 0.0f};
+  uint32_t dtr_raw[2];
+  load_x(c0);
+  {
+    uint32_t d0[2], d1[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      d0[e] = load_dt(c0, hs[e]);
+      d1[e] = load_dt(min(c0 + 1, cl), hs[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      lam_seg[e] += make_dec(c0, c0 % 3, d0[e], e);
+      if (c0 + 1 < c1) lam_seg[e] += make_dec(c0 + 1, (c0 + 1) % 3, d1[e], e);
+    }
+  }
+  __syncthreads();
+  commit(c0);
+  load_x(min(c0 + 1, cl));
+#pragma unroll
+  for (int e = 0; e < 2; ++e) dtr_raw[e] = load_dt(min(c0 + 2, cl), hs[e]);
+  __syncthreads();
+
+  for (int c = c0; c < c1; ++c) {
+    if (c + 1 < c1) commit(c + 1);
+    load_x(min(c + 2, cl));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (c + 2 < c1) lam_seg[e] += make_dec(c + 2, (c + 2) % 3, dtr_raw[e], e);
+      dtr_raw[e] = load_dt(min(c + 3, cl), hs[e]);
+    }
+    __syncthreads();
+  }
+  if (v == 0 && lane == 0) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      if (e < nh) k.seg_decay[((int64_t)b * k.heads + hs[e]) * k.nslot + piece] = lam_seg[e];
+  }
+}
+
+__global__ __launch_bounds__(512) void ssd_bf16_seg2_kernel(BK k) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int b, hp;
+  const int piece = unit_of_block(k, &b, &hp);  // grid (pieces, head pairs, batch)
+  const int h0 = 2 * hp, nh = min(2, k.heads - h0);
+  const int seg = piece / k.ppseg;
+  const int c0 = seg * k.seg_chunks + (piece % k.ppseg) * k.piece_tiles;
+  const int c1 = min(min(c0 + k.piece_tiles, (seg + 1) * k.seg_chunks), k.ntiles);
+  if (c0 >= c1) return;  // whole workgroup (the planner makes no empty piece)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave >= 4)
+    state_waves2(k, smem, b, h0, nh, piece, c0, c1, wave - 4);
+  else
+    stage_waves2(k, smem, b, h0, nh, piece, c0, c1, wave);
+}
+
 // Chains the pieces' states: slot i receives the state entering piece i,
 //   H_in[0] = h0, H_in[i+1] = exp2(decay_i) H_in[i] + S_i,
 // where slot i held the piece's own end state S_i from the state-only pass.
@@ -1021,7 +1256,8 @@ bool bf16_path(int64_t d_head, int64_t d_state, int64_t chunk, int dtype) {
   return dtype == MM_BF16 && d_head == kP && d_state == kN && (chunk == 128 || chunk == 256);
 }
 
-Bf16Plan plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int64_t units_in) {
+Bf16Plan plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int64_t units_in,
+                   bool allow_pairs) {
   // Cost in units of one tile step of a main workgroup (about 2.5 us on
   // MI355X).  Each round of up to kCus main workgroups costs its walk plus
   // ~2.5 tiles of start-up (first loads from HBM, state in, pipeline fill and
@@ -1030,8 +1266,12 @@ Bf16Plan plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int64_t units_i
   // two sharing a CU measured slower per CU than one), and the combine and
   // its launch (~2, plus ~0.3 per piece: each piece's state is written and
   // read back once more).  Pieces finer than the segments pay where the
-  // segments alone leave CUs idle in the state-only pass.
-  constexpr int64_t kCus = 256, kSegPerCu = 1, kMaxPieces = 8;
+  // segments alone leave CUs idle in the state-only pass.  Two heads per
+  // state-only workgroup (pairs: the B^T fragments are read once for the
+  // two) take ~1.0 of a main tile step per tile for both (measured at long
+  // context: 0.6 for one head), in half as many workgroups: they pay where
+  // the pieces can be made fine enough to fill the CUs.
+  constexpr int64_t kCus = 256, kSegPerCu = 1, kMaxPieces = 16;
   Bf16Plan pl;
   const int64_t n = (seqlen + kQ - 1) / kQ;
   const int64_t units = units_in > 0 ? units_in : batch * heads;
@@ -1058,11 +1298,17 @@ Bf16Plan plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int64_t units_i
       const int64_t pt = (per + pp - 1) / pp;
       if ((pp - 1) * pt >= per) continue;  // an empty piece
       const int64_t npre = (seg - 1) * pp;
-      const int64_t r_pre = (units * npre + kCus * kSegPerCu - 1) / (kCus * kSegPerCu);
-      const double cost = main_cost + (double)r_pre * (0.6 * (double)pt + 2.5) + 2.0 + 0.3 * (double)npre;
-      if (cost < best) {
-        best = cost;
-        pl.nseg = (int)seg; pl.seg_tiles = (int)per; pl.ppseg = (int)pp; pl.piece_tiles = (int)pt;
+      for (int pr = 0; pr < (allow_pairs ? 2 : 1); ++pr) {
+        if (!pr && pp > 8) continue;  // one head per workgroup: at most 8 pieces
+        const int64_t pu = pr ? batch * ((heads + 1) / 2) : units;  // state-only workgroups per piece
+        const int64_t r_pre = (pu * npre + kCus * kSegPerCu - 1) / (kCus * kSegPerCu);
+        const double cost = main_cost + (double)r_pre * ((pr ? 1.0 : 0.6) * (double)pt + 2.5) + 2.0 +
+                            0.3 * (double)npre;
+        if (cost < best) {
+          best = cost;
+          pl.nseg = (int)seg; pl.seg_tiles = (int)per; pl.ppseg = (int)pp; pl.piece_tiles = (int)pt;
+          pl.pairs = pr != 0;
+        }
       }
     }
   }
@@ -1070,15 +1316,16 @@ Bf16Plan plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int64_t units_i
 }
 
 void fwd_plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int* ntiles, int* nseg,
-                   int* seg_tiles, int64_t units_in) {
-  const Bf16Plan pl = plan_bf16(batch, seqlen, heads, units_in);
+                   int* seg_tiles, int64_t units_in, bool allow_pairs) {
+  const Bf16Plan pl = plan_bf16(batch, seqlen, heads, units_in, allow_pairs);
   *ntiles = pl.ntiles;
   *seg_tiles = pl.seg_tiles;
   *nseg = pl.nseg;
 }
 
-size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t units) {
-  const Bf16Plan pl = plan_bf16(batch, seqlen, heads, units);
+size_t bf16_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t units,
+                            bool allow_pairs) {
+  const Bf16Plan pl = plan_bf16(batch, seqlen, heads, units, allow_pairs);
   size_t bytes = frag_region_bytes(batch, seqlen) + dt_region_bytes(batch, seqlen, heads);
   if (pl.nseg > 1) bytes += (size_t)(batch * heads * pl.nslot()) * (size_t)(kP * kN + 1) * sizeof(float);
   return bytes;
@@ -1099,7 +1346,8 @@ hipError_t set_lds_attributes() {
       {reinterpret_cast<const void*>(ssd_bf16_kernel<false>), kLds},
       {reinterpret_cast<const void*>(ssd_bf16_kernel<true>), kLds},
       {reinterpret_cast<const void*>(ssd_bf16_seg_kernel<false>), kLdsSeg},
-      {reinterpret_cast<const void*>(ssd_bf16_seg_kernel<true>), kLdsSeg}};
+      {reinterpret_cast<const void*>(ssd_bf16_seg_kernel<true>), kLdsSeg},
+      {reinterpret_cast<const void*>(ssd_bf16_seg2_kernel), kLdsSeg2}};
   for (const auto& fa : attrs) {
     e = hipFuncSetAttribute(fa.first, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fa.second);
     if (e != hipSuccess) return e;
@@ -1121,7 +1369,8 @@ hipError_t launch_bf16(const FwdArgs& a, const FuseArgs& fu, void* ws, hipStream
   k.cw = fu.w; k.cbias = fu.bias; k.cstate = fu.state; k.conv_dim = fu.conv_dim;
   k.seqlen = a.seqlen; k.n_heads = a.n_heads; k.heads = a.heads;
   k.um = make_unit_map(a);
-  const Bf16Plan pl = plan_bf16(a.batch, a.seqlen, a.heads, k.um.mixed ? k.um.units : 0);
+  const Bf16Plan pl = plan_bf16(a.batch, a.seqlen, a.heads, k.um.mixed ? k.um.units : 0,
+                                !FUSED && !k.um.mixed);
   k.ntiles = pl.ntiles;
   k.nseg = pl.nseg;
   k.seg_chunks = pl.seg_tiles;
@@ -1149,10 +1398,16 @@ hipError_t launch_bf16(const FwdArgs& a, const FuseArgs& fu, void* ws, hipStream
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (k.nseg > 1) {
     const int npre = k.nslot - 1;
-    auto pre = ssd_bf16_seg_kernel<FUSED>;
-    const dim3 gpre = k.um.mixed ? dim3((unsigned)(npre * k.um.units))
-                                 : dim3(npre, a.heads, (unsigned)a.batch);
-    hipLaunchKernelGGL(pre, gpre, dim3(512), kLdsSeg, s, k);
+    if (pl.pairs) {
+      // two heads per workgroup, sharing the B^T fragments
+      hipLaunchKernelGGL(ssd_bf16_seg2_kernel, dim3(npre, (unsigned)((a.heads + 1) / 2), (unsigned)a.batch),
+                         dim3(512), kLdsSeg2, s, k);
+    } else {
+      auto pre = ssd_bf16_seg_kernel<FUSED>;
+      const dim3 gpre = k.um.mixed ? dim3((unsigned)(npre * k.um.units))
+                                   : dim3(npre, a.heads, (unsigned)a.batch);
+      hipLaunchKernelGGL(pre, gpre, dim3(512), kLdsSeg, s, k);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     static_assert((kP * kN) % 256 == 0, "state elements split over 256-thread blocks");
     const dim3 gcomb = k.um.mixed ? dim3(kP * kN / 256, (unsigned)k.um.units)
