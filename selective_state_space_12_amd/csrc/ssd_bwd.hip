@@ -32,25 +32,25 @@
 //    final one); backwards, storing Gc, dL/dH at the end of every chunk.
 //    Both are stored in the storage type in MFMA fragment order: each lane
 //    writes its 16 bytes of a 1 KB fragment, so a store covers whole cache
-//    lines (an n-major dL/dH store, half lines, had made the backward walk
-//    twice as slow as the forward one).  With few walks the
-//    sequences are split into segments: a prepass walks each segment from
-//    zero, a combine chains the segments, and the walks start from the
-//    chained values.
+//    lines.  Token rows are read by consecutive lanes along a row.  With few
+//    walks the sequences are split into segments: a prepass walks each
+//    segment from zero, a combine chains the segments, and the walks start
+//    from the chained values.
 //  - bwd_chunk_kernel: one workgroup of 16 waves per (sequence, chunk), every
-//    chunk in parallel, looping over the heads.  The B, C rows and the Q x Q
-//    blocks of C_t . B_s (the same for every head) are formed once; per head
-//    the x, dy rows, dt, Hp and Gc are staged (the next head's loaded during
-//    this one), then phase 1 forms the head's Q x Q blocks (one block per
-//    wave on waves 0-9) and the end-state and Hp terms (each wave its own
-//    u, dB and dC tiles) and phase 2 the causal products into the same
-//    accumulators, with dx written and dB, dC added to their sums over the
-//    heads in registers.  Products that need a tile's transpose read its
-//    columns with LDS transpose loads.  A wave without a Q x Q block forms
-//    the previous head's dLambda, ddt and dA during phase 1.
+//    chunk in parallel, looping over up to 64 heads per launch.  The B, C
+//    rows, the Q x Q blocks of C_t . B_s (the same for every head) and the
+//    chunk's dt, A and D of the heads are loaded once; per head the x, dy
+//    rows, Hp and Gc are staged (the next head's loaded during this one),
+//    then phase 1 forms the head's Q x Q blocks (one block per wave on waves
+//    0-9) and the end-state and Hp terms (each wave its own u, dB and dC
+//    tiles) and phase 2 the causal products into the same accumulators, with
+//    dx written and dB, dC added to their sums over the heads in registers.
+//    Products that need a tile's transpose read its columns with LDS
+//    transpose loads.  A wave without a Q x Q block forms the previous head's
+//    dLambda, ddt, dA and dD during phase 1 and leaves them in LDS.
 //  - dB and dC (sums over the heads) are written once per chunk, no atomics;
-//    dA and dD (sums over the sequences and chunks) are one fp32 atomic per
-//    (workgroup, head).
+//    ddt once per chunk for all its heads; dA and dD (sums over the sequences
+//    and chunks) are one fp32 atomic per (workgroup, head).
 #include <algorithm>
 #include <type_traits>
 
@@ -666,12 +666,13 @@ __device__ __forceinline__ float xor_lane(float v, int lane, int m) {
 
 // ACC: add into the caller's dx, ddt, dB and dC (else overwrite them).
 //
-// One workgroup of 16 waves per (sequence, chunk) loops over the heads; the
-// walks have stored, per head, the state before the chunk (Hp) and dL/dH at
-// its end (Gc).  Once per chunk: the B and C rows are staged and the Q x Q
-// blocks of B_s . C_t on and below the diagonal formed (waves 0-9, one
-// 16 x 16 block each, kept in registers: they do not depend on the head).
-// Per head, after staging its x, dy, dt, Hp and Gc:
+// One workgroup of 16 waves per (sequence, chunk) loops over heads
+// [h0g, h0g + hg), at most 64; the walks have stored, per head, the state
+// before the chunk (Hp) and dL/dH at its end (Gc).  Once per chunk: the B and
+// C rows and the dt, A and D of the heads are staged and the Q x Q blocks of
+// B_s . C_t on and below the diagonal formed (waves 0-9, one 16 x 16 block
+// each, kept in registers: they do not depend on the head).
+// Per head, after staging its x, dy, Hp and Gc:
 //  phase 1: dy_t . x_s on the same blocks, the masked decay, and from them
 //    M = G dec, K = Q dec (both [s][t]) and Kd = K dt_s ([t][s]) in LDS with
 //    the row and column sums of W; the wave's u tile's end-state term
@@ -679,11 +680,13 @@ __device__ __forceinline__ float xor_lane(float v, int lane, int m) {
 //    tiles' exp(Lambda_t) dy_t Hp, and part of <Gc, Hp>;
 //  phase 2: u += M dy, dB += K C, dC += Kd B; dx; dB and dC added to their
 //    sums over the heads (registers);
-//  tail (wave 0): dLambda from the partial sums, its suffix sum, ddt, dA.
+//  tail (wave 0): dLambda from the partial sums, its suffix sum, ddt, dA and
+//    dD, left in LDS.
 // The chunk's end state is H_e = exp(Lambda_e) Hp + sum_s exp(Lambda_e -
 // Lambda_s) dt_s x_s B_s^T, so <Gc, H_e> = exp(Lambda_e) <Gc, Hp> + the sum
-// over s of the end-state dLambda terms.  dB and dC are written once per
-// chunk after the loop: no atomics.  Every partial sum is written by one
+// over s of the end-state dLambda terms.  After the loop: ddt is written as
+// whole token rows of the group's heads, dA and dD one atomic per head, dB
+// and dC once (a later group's launch adds into them): no dB/dC atomics.  Every partial sum is written by one
 // wave and summed in a fixed order: the results do not depend on timing.
 template <typename T, int P, int N, bool ACC>
 __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {

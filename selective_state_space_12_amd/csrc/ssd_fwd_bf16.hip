@@ -41,6 +41,10 @@
 //    eight consecutive channels of a token, stored as one 16-byte write;
 //  - LDS tiles are double-buffered and the decay cumsums triple-buffered, so
 //    each tile costs one workgroup barrier.
+//  - long sequences with few heads are split into segments: a state-only pass
+//    (one or two heads per workgroup, pieces finer than the segments) forms
+//    each piece's end state from zero, a combine chains them, and the main
+//    kernel walks every segment from its chained start state.
 #include <atomic>
 #include <utility>
 
