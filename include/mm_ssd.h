@@ -462,9 +462,9 @@ int mm_ssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t n_head
 
 /*
  * Segments per sequence a mm_ssd_backward call with these sizes uses for its
- * two walks over the chunks (the states forwards, dL/dH backwards): with
- * fewer than 256 active (sequence, head) walks, the sequences are split into
- * segments walked in parallel, every one but the last at least 256 tokens
+ * two walks over the chunks (the states forwards, dL/dH backwards): with at
+ * most 32 active (sequence, head) walks, the sequences are split into
+ * segments walked in parallel, every one but the last at least 512 tokens
  * long (a prepass and a combine chain them; the workspace size includes
  * their data).  The
  * gradients themselves are then formed for all chunks in parallel.  Same
