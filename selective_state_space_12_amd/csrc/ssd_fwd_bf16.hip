@@ -1268,8 +1268,8 @@ Bf16Plan plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int64_t units_i
   // drain).  A split adds the state-only pass, whose workgroups walk a piece
   // at ~0.6 of a main tile step per tile plus ~2.5 of start-up (one per CU:
   // two sharing a CU measured slower per CU than one), and the combine and
-  // its launch (~2, plus ~0.3 per piece: each piece's state is written and
-  // read back once more).  Pieces finer than the segments pay where the
+  // its launch (~3, plus ~0.3 per piece: each piece's state is written and
+  // read back once more; traces put the combine alone at 5-9 us).  Pieces finer than the segments pay where the
   // segments alone leave CUs idle in the state-only pass.  Two heads per
   // state-only workgroup (pairs: the B^T fragments are read once for the
   // two) take ~1.0 of a main tile step per tile for both (measured at long
@@ -1306,7 +1306,7 @@ Bf16Plan plan_bf16(int64_t batch, int64_t seqlen, int64_t heads, int64_t units_i
         if (!pr && pp > 8) continue;  // one head per workgroup: at most 8 pieces
         const int64_t pu = pr ? batch * ((heads + 1) / 2) : units;  // state-only workgroups per piece
         const int64_t r_pre = (pu * npre + kCus * kSegPerCu - 1) / (kCus * kSegPerCu);
-        const double cost = main_cost + (double)r_pre * ((pr ? 1.0 : 0.6) * (double)pt + 2.5) + 2.0 +
+        const double cost = main_cost + (double)r_pre * ((pr ? 1.0 : 0.6) * (double)pt + 2.5) + 3.0 +
                             0.3 * (double)npre;
         if (cost < best) {
           best = cost;
