@@ -590,10 +590,18 @@ __global__ __launch_bounds__(kBThreads) void bwd_prepass_kernel(BwdK k) {
 
 // Both walks of the call in one launch, independent of each other:
 // workgroups [0, total/2) walk forward storing the state before every chunk,
-// the rest walk backwards storing dL/dH at the end of every chunk.
+// the rest walk backwards storing dL/dH at the end of every chunk.  dA and dD
+// are sums that the chunk kernel (launched after this one) adds into with
+// fp32 atomics: unless the call accumulates, the first workgroup clears them.
 template <typename T, int P, int N>
 __global__ __launch_bounds__(kBThreads) void bwd_walks_kernel(BwdK k) {
   const int half = gridDim.x / 2;
+  if (blockIdx.x == 0 && !k.accumulate) {
+    for (int i = threadIdx.x; i < k.heads; i += kBThreads) {
+      k.dA[i] = 0.0f;
+      if (k.dD) k.dD[i] = 0.0f;
+    }
+  }
   if ((int)blockIdx.x < half) walk<T, P, N, false, true>(k, blockIdx.x, half);
   else walk<T, P, N, true, true>(k, blockIdx.x - half, half);
 }
@@ -1192,15 +1200,6 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
   }
 }
 
-// dA and dD (heads values; dD may be null) set to zero: the only outputs the
-// calls add into from several workgroups.
-__global__ __launch_bounds__(64) void zero_heads_kernel(float* dA, float* dD, int heads) {
-  for (int i = threadIdx.x; i < heads; i += 64) {
-    dA[i] = 0.0f;
-    if (dD) dD[i] = 0.0f;
-  }
-}
-
 template <typename T, int P, int N>
 hipError_t launch_shape(const BwdK& k, int64_t batch, hipStream_t s) {
   const unsigned units = (unsigned)(batch * k.heads);
@@ -1342,8 +1341,7 @@ hipError_t launch_ssd_backward(const BwdArgs& a, void* workspace, hipStream_t s)
     }
   }
   // dB and dC are written whole by the chunk kernel; dA and dD are sums
-  // over workgroups
-  if (!a.accumulate) hipLaunchKernelGGL(zero_heads_kernel, dim3(1), dim3(64), 0, s, a.dA, a.dD, (int)a.heads);
+  // over workgroups, cleared by the walks kernel
   if (a.dtype == MM_BF16) {
     if (a.d_state == 128) return launch_shape<bf16, 64, 128>(k, a.batch, s);
     return launch_shape<bf16, 64, 64>(k, a.batch, s);
