@@ -610,25 +610,42 @@ __global__ __launch_bounds__(kBThreads) void bwd_walks_kernel(BwdK k) {
 // Forward (seg_h): slot s <- exp2(hd_s) * start_s + end_s, the start of
 // segment s+1 (start_0 = h0).  Backward (seg_g): from dL/dH = dhT at the end
 // of the last segment, slot s <- exp2(gd_s) * G + slot s for s = nseg-1..1,
-// the gradient at the end of segment s-1.
+// the gradient at the end of segment s-1.  The slots of both chains are
+// loaded eight at a time before their part of the chains (one load round
+// trip per eight segments rather than one per segment).
 template <int PN>
 __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdK k) {
+  constexpr int kG = 8;
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int64_t unit = blockIdx.y;
   const int b = (int)(unit / k.heads), h = (int)(unit % k.heads);
   if (e >= PN) return;
   const int64_t base = ((int64_t)b * k.n_heads + h) * PN + e;
   float st = k.h0 ? k.h0[base] : 0.0f;
-  for (int s = 0; s + 1 < k.nseg; ++s) {
-    float* slot = k.seg_h + (unit * k.nseg + s) * PN + e;
-    st = __builtin_amdgcn_exp2f(k.seg_hd[unit * k.nseg + s]) * st + *slot;
-    *slot = st;
-  }
   float gr = k.dhT ? k.dhT[base] : 0.0f;
-  for (int s = k.nseg - 1; s >= 1; --s) {
-    float* slot = k.seg_g + (unit * k.nseg + s) * PN + e;
-    gr = __builtin_amdgcn_exp2f(k.seg_gd[unit * k.nseg + s]) * gr + *slot;
-    *slot = gr;
+  float* hs = k.seg_h + unit * k.nseg * PN + e;
+  float* gs = k.seg_g + unit * k.nseg * PN + e;
+  const float* hd = k.seg_hd + unit * k.nseg;
+  const float* gd = k.seg_gd + unit * k.nseg;
+  const int npre = k.nseg - 1;  // forward slots 0..npre-1, backward slots npre..1
+  for (int i0 = 0; i0 < npre; i0 += kG) {
+    float Hs[kG], Gs[kG];
+#pragma unroll
+    for (int i = 0; i < kG; ++i) {  // (slot index clamped: every load valid)
+      const int s = min(i0 + i, npre - 1);
+      Hs[i] = hs[(int64_t)s * PN];
+      Gs[i] = gs[(int64_t)(npre - s) * PN];
+    }
+#pragma unroll
+    for (int i = 0; i < kG; ++i) {
+      const int s = i0 + i;
+      if (s < npre) {
+        st = __builtin_amdgcn_exp2f(hd[s]) * st + Hs[i];
+        hs[(int64_t)s * PN] = st;
+        gr = __builtin_amdgcn_exp2f(gd[npre - s]) * gr + Gs[i];
+        gs[(int64_t)(npre - s) * PN] = gr;
+      }
+    }
   }
 }
 
