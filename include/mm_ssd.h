@@ -452,8 +452,10 @@ int mm_conv1d_silu_backward(const void* xbc_in, int64_t in_row_stride,
  * Bytes of device workspace mm_ssd_backward needs: the state before every
  * 64-token chunk and the final state of each active (sequence, head), and
  * dL/dH at the end of every chunk, in the storage dtype, and, when the
- * sequences are split, fp32 segment states and gradients (see
- * mm_ssd_backward_segments).  Same argument meaning and errors as mm_ssd_backward.
+ * sequences are split, each segment's own end values (fp32) and chained
+ * boundary values (storage dtype) and one fp32 decay per chunk and direction
+ * (see mm_ssd_backward_segments).  Same argument meaning and errors as
+ * mm_ssd_backward.
  * Host only.
  */
 int mm_ssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
@@ -462,11 +464,11 @@ int mm_ssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t n_head
 
 /*
  * Segments per sequence a mm_ssd_backward call with these sizes uses for its
- * two walks over the chunks (the states forwards, dL/dH backwards): with at
- * most 32 active (sequence, head) walks, the sequences are split into
- * segments walked in parallel, every one but the last at least 512 tokens
- * long (a prepass and a combine chain them; the workspace size includes
- * their data).  The
+ * two walks over the chunks (the states forwards, dL/dH backwards): with
+ * fewer than 128 active (sequence, head) pairs, the sequences are split into
+ * segments walked in parallel, about 128 pairs in all, every segment but the
+ * last at least 512 tokens long (a combine chains them; the workspace size
+ * includes its data).  The
  * gradients themselves are then formed for all chunks in parallel.  Same
  * argument meaning and errors as mm_ssd_backward.  Host only.
  */

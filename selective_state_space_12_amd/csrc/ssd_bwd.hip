@@ -33,9 +33,11 @@
 //    Both are stored in the storage type in MFMA fragment order: each lane
 //    writes its 16 bytes of a 1 KB fragment, so a store covers whole cache
 //    lines.  Token rows are read by consecutive lanes along a row.  With few
-//    walks the sequences are split into segments: a prepass walks each
-//    segment from zero, a combine chains the segments, and the walks start
-//    from the chained values.
+//    walks the sequences are split into segments walked in parallel, each
+//    from its own start (h0 or dL/dH of the final state at the sequence's
+//    ends, zero elsewhere); a combine chains the segments' end values, and
+//    the chunk kernel adds to each stored value the chained value at its
+//    segment's boundary, decayed to the chunk (the recurrence is linear).
 //  - bwd_chunk_kernel: one workgroup of 16 waves per (sequence, chunk), every
 //    chunk in parallel, looping over up to 64 heads per launch.  The B, C
 //    rows, the Q x Q blocks of C_t . B_s (the same for every head) and the
@@ -97,12 +99,22 @@ struct BwdK {
   float* dh0;
   void* hst;  // (batch, heads, nchunks + 1, P, N) storage type, fragment order
   void* gst;  // (batch, heads, nchunks, P, N) storage type, fragment order: dL/dH at each chunk's end
-  // sequence split (nseg > 1): per (unit, segment) fp32 P x N blocks and
-  // log2 decays; see the launch for what each holds when
+  // sequence split (nseg > 1): per (unit, segment) fp32 P x N blocks,
+  // n-major ([N][P]), and the segments' log2 decays (the combine describes
+  // what each holds); the chained boundary values in the storage type,
+  // n-major: hb slot s the state at the start of segment s+1, gb slot s
+  // dL/dH at the end of segment s-1; per (unit, chunk) the log2 decay
+  // between the chunk's stored value and its segment's boundary: lamh from
+  // the segment start to the chunk start, lamg from the chunk end to the
+  // segment end
   float* seg_h;
   float* seg_hd;
   float* seg_g;
   float* seg_gd;
+  void* seg_hb;
+  void* seg_gb;
+  float* lamh;
+  float* lamg;
   int64_t seqlen;
   int n_heads, heads, nchunks, accumulate;
   int nseg, seg_chunks;
@@ -360,21 +372,23 @@ struct WalkLds {
 // value V in MFMA accumulators, V <- exp2(Lambda_e) V + sum_t a_t w_t b_t^T
 // per chunk:
 //   REV = false (states): chunks ascending, a = x, b = B, w_s = exp2(Lambda_e -
-//     Lambda_s) dt_s: V is the state.  MAIN stores it before every chunk
-//     (and after the last one) in fragment order; PRE (segments 0..nseg-2,
-//     from zero) writes the segment's end state and log2 decay.
+//     Lambda_s) dt_s: V is the state, stored before every chunk (and after
+//     the last one) in fragment order.  Starts from h0 in the first segment,
+//     from zero in the others.
 //   REV = true (gradients): chunks descending, a = dy, b = C, w_t =
-//     exp2(Lambda_t): V is dL/dH.  MAIN stores it at the end of every chunk
-//     in fragment order, before the chunk's update, and the first segment
-//     writes dh0;
-//     PRE (segments 1..nseg-1, from zero) writes the result at the segment's
-//     start and its log2 decay.
-// MAIN segments start from the combined value of the split (or h0 / dhT).
+//     exp2(Lambda_t): V is dL/dH, stored at the end of every chunk in
+//     fragment order, before the chunk's update.  Starts from dL/dH of the
+//     final state in the last segment, from zero in the others; an unsplit
+//     walk writes dh0.
+// In a split call every walk also stores, per chunk, the log2 decay between
+// the stored value and the segment boundary it started from, and writes its
+// own end value (forward, all segments but the last) or start value
+// (backward, every segment) with the segment's log2 decay, for the combine.
 // The a and b rows are staged token-major and read as operand columns with
 // transpose loads; the rows of the chunk two ahead are loaded into registers
 // (two sets, used alternately) and the LDS buffers alternate by chunk, so a
 // chunk needs one barrier.  Tile rows in the paired order of prow().
-template <typename T, int P, int N, bool REV, bool MAIN>
+template <typename T, int P, int N, bool REV>
 __device__ __forceinline__ void walk(const BwdK& k, int pid, int total) {
   using L = WalkLds<T, P, N>;
   constexpr int Q = kBQ, NP = L::NP, NN = L::NN;
@@ -394,9 +408,8 @@ __device__ __forceinline__ void walk(const BwdK& k, int pid, int total) {
     wt = lam + Q;
   };
 
-  int b, h, sg;
-  unit_of_idx(pid, total, k.heads, MAIN ? k.nseg : k.nseg - 1, &b, &h, &sg);
-  const int seg = (REV && !MAIN) ? sg + 1 : sg;
+  int b, h, seg;
+  unit_of_idx(pid, total, k.heads, k.nseg, &b, &h, &seg);
   const int64_t unit = (int64_t)b * k.heads + h;
   const int c0 = seg * k.seg_chunks, c1 = min(c0 + k.seg_chunks, k.nchunks);
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
@@ -416,16 +429,8 @@ __device__ __forceinline__ void walk(const BwdK& k, int pid, int total) {
   f32x4 acc[TPW];
   {
     const float* vin = nullptr;
-    if (MAIN) {
-      if (!REV)
-        vin = seg > 0 ? k.seg_h + (unit * k.nseg + seg - 1) * (P * N)
-              : k.h0  ? k.h0 + ((int64_t)b * k.n_heads + h) * (P * N)
-                      : nullptr;
-      else
-        vin = seg + 1 < k.nseg ? k.seg_g + (unit * k.nseg + seg + 1) * (P * N)
-              : k.dhT          ? k.dhT + ((int64_t)b * k.n_heads + h) * (P * N)
-                               : nullptr;
-    }
+    if (!REV && seg == 0 && k.h0) vin = k.h0 + ((int64_t)b * k.n_heads + h) * (P * N);
+    if (REV && seg + 1 == k.nseg && k.dhT) vin = k.dhT + ((int64_t)b * k.n_heads + h) * (P * N);
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -436,11 +441,12 @@ __device__ __forceinline__ void walk(const BwdK& k, int pid, int total) {
     for (int t = 0; t < TPW; ++t) acc[t] = opaque(acc[t]);
   }
   float lam_seg = 0.0f;  // log2 decay over the walked chunks
+  float* const lamc = k.nseg > 1 ? (REV ? k.lamg : k.lamh) : nullptr;
   T* __restrict__ Vst = static_cast<T*>(REV ? k.gst : k.hst) +
                         unit * (REV ? k.nchunks : k.nchunks + 1) * (P * N);
   // V after chunk c (REV: before the update with chunk c), in its stored layout
   auto store_v = [&](int c) {
-    if (!MAIN || !owns) return;
+    if (!owns) return;
     T* dst = Vst + (int64_t)c * (P * N);
 #pragma unroll
     for (int t = 0; t < TPW; t += 2) store8(dst + state_frag<N>((pt0 + t) / 2, nt, lane), acc[t], acc[t + 1]);
@@ -480,6 +486,7 @@ __device__ __forceinline__ void walk(const BwdK& k, int pid, int total) {
     float *lam, *wt;
     buf(parity, an, bn, lam, wt);
     store_v(c);  // the state before chunk c, or dL/dH at its end
+    if (lamc && tid == 0) lamc[unit * k.nchunks + c] = lam_seg;
     const int len = plen[S];
 #pragma unroll
     for (int v = 0; v < NAV; ++v) {
@@ -556,17 +563,18 @@ __device__ __forceinline__ void walk(const BwdK& k, int pid, int total) {
     }
     if (c >= c0) step(c, 0, S0{});
   }
-  if (!MAIN) {
-    float* dst = (REV ? k.seg_g : k.seg_h) + (unit * k.nseg + seg) * (P * N);
-    if (owns)
+  if (!REV && c1 == k.nchunks) store_v(k.nchunks);
+  if (k.nseg > 1) {
+    if (REV || seg + 1 < k.nseg) {
+      float* dst = (REV ? k.seg_g : k.seg_h) + (unit * k.nseg + seg) * (P * N);
+      if (owns)
 #pragma unroll
-      for (int t = 0; t < TPW; ++t)
+        for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[prow(pt0 + t, g * 4 + i) * N + nt * 16 + r16] = acc[t][i];
-    if (tid == 0) (REV ? k.seg_gd : k.seg_hd)[unit * k.nseg + seg] = lam_seg;
-  } else if (!REV) {
-    if (c1 == k.nchunks) store_v(k.nchunks);
-  } else if (seg == 0 && k.dh0 && owns) {
+          for (int i = 0; i < 4; ++i) dst[(nt * 16 + r16) * P + prow(pt0 + t, g * 4 + i)] = acc[t][i];
+      if (tid == 0) (REV ? k.seg_gd : k.seg_hd)[unit * k.nseg + seg] = lam_seg;
+    }
+  } else if (REV && k.dh0 && owns) {
     float* dst = k.dh0 + ((int64_t)b * k.n_heads + h) * (P * N);
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
@@ -576,16 +584,6 @@ __device__ __forceinline__ void walk(const BwdK& k, int pid, int total) {
         *q = k.accumulate ? *q + acc[t][i] : acc[t][i];
       }
   }
-}
-
-// Both prepasses of the sequence split in one launch: they are independent
-// and each fills fewer than all CUs.  Workgroups [0, total/2) walk segments
-// 0..nseg-2 forward, the rest segments 1..nseg-1 backward.
-template <typename T, int P, int N>
-__global__ __launch_bounds__(kBThreads) void bwd_prepass_kernel(BwdK k) {
-  const int half = gridDim.x / 2;
-  if ((int)blockIdx.x < half) walk<T, P, N, false, false>(k, blockIdx.x, half);
-  else walk<T, P, N, true, false>(k, blockIdx.x - half, half);
 }
 
 // Both walks of the call in one launch, independent of each other:
@@ -602,29 +600,34 @@ __global__ __launch_bounds__(kBThreads) void bwd_walks_kernel(BwdK k) {
       if (k.dD) k.dD[i] = 0.0f;
     }
   }
-  if ((int)blockIdx.x < half) walk<T, P, N, false, true>(k, blockIdx.x, half);
-  else walk<T, P, N, true, true>(k, blockIdx.x - half, half);
+  if ((int)blockIdx.x < half) walk<T, P, N, false>(k, blockIdx.x, half);
+  else walk<T, P, N, true>(k, blockIdx.x - half, half);
 }
 
-// Chains the segments of every unit, one thread per state element.
-// Forward (seg_h): slot s <- exp2(hd_s) * start_s + end_s, the start of
-// segment s+1 (start_0 = h0).  Backward (seg_g): from dL/dH = dhT at the end
-// of the last segment, slot s <- exp2(gd_s) * G + slot s for s = nseg-1..1,
-// the gradient at the end of segment s-1.  The slots of both chains are
+// Chains the segments of every unit, one thread per state element (n-major
+// index e = n P + p).  Forward: slot s holds segment s's end state from its
+// own start (h0 for segment 0, zero after); the start of segment s+1 is
+// exp2(hd_s) (start of s) + slot s, written to slot s of seg_hb.  Backward:
+// slot s holds dL/dH at segment s's start from its own end value (dL/dH of
+// the final state for the last segment, zero before); dL/dH at the end of
+// segment s-1 is exp2(gd_s) (that at the end of s) + slot s, written to
+// slot s of seg_gb, and dh0 is exp2(gd_0) (dL/dH at the end of segment 0) +
+// slot 0.  The chains run in fp32; the boundary values are stored in the
+// storage type, as the walks store theirs.  The slots of both chains are
 // loaded eight at a time before their part of the chains (one load round
-// trip per eight segments rather than one per segment).
-template <int PN>
+// trip per eight segments, not one per segment).
+template <typename T, int P, int N>
 __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdK k) {
-  constexpr int kG = 8;
+  constexpr int kG = 8, PN = P * N;
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int64_t unit = blockIdx.y;
   const int b = (int)(unit / k.heads), h = (int)(unit % k.heads);
   if (e >= PN) return;
-  const int64_t base = ((int64_t)b * k.n_heads + h) * PN + e;
-  float st = k.h0 ? k.h0[base] : 0.0f;
-  float gr = k.dhT ? k.dhT[base] : 0.0f;
-  float* hs = k.seg_h + unit * k.nseg * PN + e;
-  float* gs = k.seg_g + unit * k.nseg * PN + e;
+  float st = 0.0f, gr = 0.0f;
+  const float* hs = k.seg_h + unit * k.nseg * PN + e;
+  const float* gs = k.seg_g + unit * k.nseg * PN + e;
+  T* hb = static_cast<T*>(k.seg_hb) + unit * k.nseg * PN + e;
+  T* gb = static_cast<T*>(k.seg_gb) + unit * k.nseg * PN + e;
   const float* hd = k.seg_hd + unit * k.nseg;
   const float* gd = k.seg_gd + unit * k.nseg;
   const int npre = k.nseg - 1;  // forward slots 0..npre-1, backward slots npre..1
@@ -641,11 +644,16 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdK k) {
       const int s = i0 + i;
       if (s < npre) {
         st = __builtin_amdgcn_exp2f(hd[s]) * st + Hs[i];
-        hs[(int64_t)s * PN] = st;
+        hb[(int64_t)s * PN] = from_f32<T>(st);
         gr = __builtin_amdgcn_exp2f(gd[npre - s]) * gr + Gs[i];
-        gs[(int64_t)(npre - s) * PN] = gr;
+        gb[(int64_t)(npre - s) * PN] = from_f32<T>(gr);
       }
     }
+  }
+  if (k.dh0) {
+    const float v = __builtin_amdgcn_exp2f(gd[0]) * gr + gs[0];
+    float* q = k.dh0 + ((int64_t)b * k.n_heads + h) * PN + (e % P) * N + e / P;
+    *q = k.accumulate ? *q + v : v;
   }
 }
 
@@ -713,7 +721,7 @@ __device__ __forceinline__ float xor_lane(float v, int lane, int m) {
 // whole token rows of the group's heads, dA and dD one atomic per head, dB
 // and dC once (a later group's launch adds into them): no dB/dC atomics.  Every partial sum is written by one
 // wave and summed in a fixed order: the results do not depend on timing.
-template <typename T, int P, int N, bool ACC>
+template <typename T, int P, int N, bool ACC, bool SPLIT>
 __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
   using L = ChunkLds<T, P, N>;
   constexpr int Q = kBQ, NP = L::NP, NN = L::NN, TP2 = L::TP2, QP = L::QP;
@@ -773,7 +781,12 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
     return f;
   };
 
-  const int c = (int)(blockIdx.x % (unsigned)k.nchunks), b = (int)(blockIdx.x / (unsigned)k.nchunks);
+  // (sequence, chunk) of this workgroup: consecutive chunks on one XCD, so
+  // that the chunks of a segment share its boundary values in that XCD's L2
+  // (split calls)
+  const int total = (int)gridDim.x, pid = (int)blockIdx.x;
+  const int uid = total % kXcds == 0 ? (pid % kXcds) * (total / kXcds) + pid / kXcds : pid;
+  const int c = uid % k.nchunks, b = uid / k.nchunks;
   const int64_t row0 = (int64_t)b * k.seqlen + (int64_t)c * Q;
   const int len = (int)min((int64_t)Q, k.seqlen - (int64_t)c * Q);
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
@@ -852,6 +865,10 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
   static_assert(NXY == 1 && 2 * Q * (P / VB) == kCThreads, "one x or dy vector per thread");
   static_assert(NHV == 1, "at most one Hp and one Gc vector per thread");
   Vec16<T> vxy[NXY], vh[NHV], vg[NHV];
+  // split calls: the chained values at the chunk's segment boundaries at
+  // this thread's Hp and Gc elements, and the log2 decays from them
+  Vec16<T> vsh, vsg;
+  float lsh = 0.0f, lsg = 0.0f;
   const bool is_dy = wave >= kCWaves / 2;
   const uint32_t xy_rb = (uint32_t)((is_dy ? k.dys : k.xs) * (int64_t)sizeof(T));  // row bytes
   const T* const xy0 = is_dy ? DYp + row0 * k.dys : Xp + row0 * k.xs;
@@ -870,6 +887,23 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
     const T* gp = static_cast<const T*>(k.gst) + (unit * k.nchunks + c) * (P * N);
     vh[0] = vec_at(uniform_rsrc(hp, kHB), (uint32_t)tid * 16u);
     vg[0] = vec_at(uniform_rsrc(gp, kHB), (uint32_t)tid * 16u);
+    if constexpr (SPLIT) {
+      // the walks of a split call start each segment from its own boundary
+      // value (zero inside the sequence); the recurrence being linear, the
+      // chained value at that boundary (n-major, from the combine) decayed
+      // to the chunk is added here.  At the sequence's ends there is none:
+      // the empty ranges read 0.
+      const int sg = c / k.seg_chunks;
+      const unsigned e = (unsigned)tid * VB, fid = e / 512, ln = (e / 8) % 64, j0 = e % 8;
+      const unsigned n = (fid % TN) * 16 + ln % 16, p = (fid / TN) * 32 + (ln / 16) * 8 + j0;
+      const uint32_t off = (n * P + p) * (uint32_t)sizeof(T);
+      const T* hb = static_cast<const T*>(k.seg_hb) + (unit * k.nseg + max(sg - 1, 0)) * (P * N);
+      const T* gb = static_cast<const T*>(k.seg_gb) + (unit * k.nseg + min(sg + 1, k.nseg - 1)) * (P * N);
+      vsh = vec_at(uniform_rsrc(hb, sg > 0 ? kHB : 0u), off);
+      vsg = vec_at(uniform_rsrc(gb, sg + 1 < k.nseg ? kHB : 0u), off);
+      lsh = k.lamh[unit * k.nchunks + c];
+      lsg = k.lamg[unit * k.nchunks + c];
+    }
   };
   f32x4 abt[DPW], act[DPW];  // dB, dC summed over the heads
 #pragma unroll
@@ -961,13 +995,22 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
     }
     if ((unsigned)tid < P * (N / VB)) {
       const unsigned idx = tid;
-      store16(HpF + idx * VB, vh[0]);
+      Vec16<T> hv = vh[0], gv = vg[0];
+      if constexpr (SPLIT) {
+        const float eh = __builtin_amdgcn_exp2f(lsh), eg = __builtin_amdgcn_exp2f(lsg);
+#pragma unroll
+        for (int j = 0; j < VB; ++j) {
+          hv.v[j] = from_f32<T>(to_f32(hv.v[j]) + eh * to_f32(vsh.v[j]));
+          gv.v[j] = from_f32<T>(to_f32(gv.v[j]) + eg * to_f32(vsg.v[j]));
+        }
+      }
+      store16(HpF + idx * VB, hv);
       // Gc in fragment order: element e of the block is lane ln's value j0
       // of fragment (kp, nb), i.e. row n = nb*16 + ln%16, column
       // p = kp*32 + (ln/16)*8 + j0 of Gc^T
       const unsigned e = idx * VB, fid = e / 512, ln = (e / 8) % 64, j0 = e % 8;
       const unsigned n = (fid % TN) * 16 + ln % 16, p = (fid / TN) * 32 + (ln / 16) * 8 + j0;
-      store16(GT + n * TP2 + p, vg[0]);
+      store16(GT + n * TP2 + p, gv);
     }
     if (wave == 0) {
       const float dtl = to_f32(dtS[(hh - k.h0g) * DTP + lane]);  // 0 past len
@@ -1223,28 +1266,22 @@ hipError_t launch_shape(const BwdK& k, int64_t batch, hipStream_t s) {
   const size_t lds1 = WalkLds<T, P, N>::bytes, lds2 = ChunkLds<T, P, N>::bytes;
   static_assert(ChunkLds<T, P, N>::bytes <= 160 * 1024, "chunk tiles fit one CU's LDS");
   const void* fns[] = {reinterpret_cast<const void*>(&bwd_walks_kernel<T, P, N>),
-                       reinterpret_cast<const void*>(&bwd_prepass_kernel<T, P, N>),
-                       reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N, false>),
-                       reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N, true>)};
-  const size_t ldss[] = {lds1, lds1, lds2, lds2};
-  for (int i = 0; i < 4; ++i) {
+                       reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N, false, false>),
+                       reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N, true, false>),
+                       reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N, false, true>),
+                       reinterpret_cast<const void*>(&bwd_chunk_kernel<T, P, N, true, true>)};
+  const size_t ldss[] = {lds1, lds2, lds2, lds2, lds2};
+  for (int i = 0; i < 5; ++i) {
     const hipError_t e =
         hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldss[i]);
     if (e != hipSuccess) return e;
   }
-  if (k.nseg > 1) {
-    // segment prepasses (forward states, reverse dL/dH), then the combine
-    const unsigned pre = units * (unsigned)(k.nseg - 1);
-    hipLaunchKernelGGL((bwd_prepass_kernel<T, P, N>), dim3(2 * pre), dim3(kBThreads), lds1, s, k);
-    hipLaunchKernelGGL((bwd_combine_kernel<P * N>), dim3((P * N + 255) / 256, units), dim3(256), 0,
-                       s, k);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  // the two walks (states before each chunk, dL/dH after each), then the
-  // chunks in parallel
+  // the two walks (states before each chunk, dL/dH after each), each segment
+  // from its own start; with a split, the combine chains the segments
   const unsigned walks = units * (unsigned)k.nseg;
   hipLaunchKernelGGL((bwd_walks_kernel<T, P, N>), dim3(2 * walks), dim3(kBThreads), lds1, s, k);
+  if (k.nseg > 1)
+    hipLaunchKernelGGL((bwd_combine_kernel<T, P, N>), dim3((P * N + 255) / 256, units), dim3(256), 0, s, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the chunks in parallel, one launch per group of at most kGH heads (the
@@ -1252,16 +1289,15 @@ hipError_t launch_shape(const BwdK& k, int64_t batch, hipStream_t s) {
   // add their dB, dC to the earlier ones'
   const unsigned grid = (unsigned)(batch * k.nchunks);
   constexpr int kGH = ChunkLds<T, P, N>::kGH;
+  const bool split = k.nseg > 1;
   for (int g0 = 0; g0 < k.heads; g0 += kGH) {
     BwdK kg = k;
     kg.h0g = g0;
     kg.hg = std::min(kGH, k.heads - g0);
     kg.bc_acc = g0 > 0;
-    if (k.accumulate)
-      hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N, true>), dim3(grid), dim3(kCThreads), lds2, s, kg);
-    else
-      hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N, false>), dim3(grid), dim3(kCThreads), lds2, s, kg);
-    e = hipGetLastError();
+    const void* fn = fns[1 + (k.accumulate ? 1 : 0) + (split ? 2 : 0)];
+    void* args[] = {&kg};
+    e = hipLaunchKernel(fn, dim3(grid), dim3(kCThreads), args, lds2, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1280,14 +1316,14 @@ void bwd_plan(int64_t batch, int64_t seqlen, int64_t heads, int* nchunks, int* n
               int* seg_chunks) {
   const int nc = (int)((seqlen + kBQ - 1) / kBQ);
   const int64_t units = batch * heads;
-  // Each (sequence, head) walk is a latency-bound chain over the chunks.  A
-  // split walks the segments twice (the prepass, then the walks) and adds a
-  // combine, so it pays only with very few walks: with at most 32, the
-  // sequences are cut into segments of at least 8 chunks so that about 256
-  // walks run; with more, the walks stay whole (at 48 to 128 walks a split
-  // measured 5-15% slower over the whole call).
+  // Each (sequence, head) walk is a latency-bound chain over the chunks, one
+  // workgroup per direction.  With fewer than 128 (sequence, head) units the
+  // sequences are cut into segments (at least 8 chunks each) so that about
+  // 128 units run, one walk workgroup per CU; more segments, with walks
+  // sharing CUs, measured slower (the split also adds a combine and the
+  // boundary correction in the chunk kernel).
   int64_t ns = 1;
-  if (units <= 32) ns = std::min<int64_t>((256 + units - 1) / units, nc / 8);
+  if (units < 128) ns = std::min<int64_t>(128 / units, nc / 8);
   if (ns < 1) ns = 1;
   const int sc = (int)((nc + ns - 1) / ns);
   *nchunks = nc;
@@ -1302,7 +1338,9 @@ size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t
   const size_t el = dtype == MM_BF16 ? 2 : 4;
   const size_t units = (size_t)(batch * heads), pn = (size_t)(d_head * d_state);
   size_t bytes = align256(units * (size_t)(nc + 1) * pn * el) + align256(units * (size_t)nc * pn * el);
-  if (ns > 1) bytes += 2 * align256(units * ns * pn * 4) + 2 * align256(units * ns * 4);
+  if (ns > 1)
+    bytes += 2 * align256(units * ns * pn * 4) + 2 * align256(units * ns * 4) +
+             2 * align256(units * ns * pn * el) + 2 * align256(units * (size_t)nc * 4);
   return bytes;
 }
 
@@ -1346,7 +1384,8 @@ hipError_t launch_ssd_backward(const BwdArgs& a, void* workspace, hipStream_t s)
     w += align256(units * (size_t)(k.nchunks + 1) * pn * el);
     k.gst = w;
     w += align256(units * (size_t)k.nchunks * pn * el);
-    k.seg_h = k.seg_g = k.seg_hd = k.seg_gd = nullptr;
+    k.seg_h = k.seg_g = k.seg_hd = k.seg_gd = k.lamh = k.lamg = nullptr;
+    k.seg_hb = k.seg_gb = nullptr;
     if (k.nseg > 1) {
       k.seg_h = reinterpret_cast<float*>(w);
       w += align256(units * k.nseg * pn * 4);
@@ -1355,6 +1394,14 @@ hipError_t launch_ssd_backward(const BwdArgs& a, void* workspace, hipStream_t s)
       k.seg_hd = reinterpret_cast<float*>(w);
       w += align256(units * k.nseg * 4);
       k.seg_gd = reinterpret_cast<float*>(w);
+      w += align256(units * k.nseg * 4);
+      k.seg_hb = w;
+      w += align256(units * k.nseg * pn * el);
+      k.seg_gb = w;
+      w += align256(units * k.nseg * pn * el);
+      k.lamh = reinterpret_cast<float*>(w);
+      w += align256(units * (size_t)k.nchunks * 4);
+      k.lamg = reinterpret_cast<float*>(w);
     }
   }
   // dB and dC are written whole by the chunk kernel; dA and dD are sums

@@ -115,9 +115,9 @@ def test_backward_130m_bf16(seqlen):
 @pytest.mark.parametrize("w,b,l,h", [(M130, 1, 2048, 3), (M130, 2, 1000, 12), (TINY, 1, 1024, 1)])
 def test_backward_split_sequences(w, b, l, h):
     """Few (sequence, head) walks: the sequences are split into segments
-    walked in parallel, chained by a forward-state prepass, a reverse dL/dH
-    prepass and a combine; the result matches the oracle as an unsplit call
-    does."""
+    walked in parallel, each from its own boundary value, chained by a
+    combine and corrected in the chunk kernel; the result matches the oracle
+    as an unsplit call does."""
     nseg = mm.ssd_backward_segments(b, l, w.n_heads, w.d_head, w.d_state, 1, h, w.dtype)
     assert nseg > 1
     inp = _inputs(w, b, l, salt=7)
@@ -127,13 +127,13 @@ def test_backward_split_sequences(w, b, l, h):
 
 def test_backward_long_context_many_segments():
     """Long-context shape (32 heads of 64, d_state 128) at its narrowest slice,
-    one 16384-token sequence: 8 walks, split into 32 segments of 512 tokens
+    one 16384-token sequence: 8 walks, split into 16 segments of 1024 tokens
     (the oracle keeps every state of a walk, so the sequence is a 16384-token
     prefix of the workload's 131072)."""
     w = synth.WORKLOADS["long"]
     h, l = w.heads(w.slices[0]), 16384
     nseg = mm.ssd_backward_segments(1, l, w.n_heads, w.d_head, w.d_state, 1, h, w.dtype)
-    assert nseg == 32
+    assert nseg == 16
     inp = _inputs(w, 1, l, salt=8)
     say(f"backward long bf16 l={l} heads={h} segments={nseg}")
     _check(_run(w, inp, h), _oracle(inp, h), h, TOL[torch.bfloat16])
@@ -239,9 +239,9 @@ def test_backward_rejects_bad_arguments():
 
 def test_backward_accumulates_on_split_sequences():
     """Accumulating over granularities where the calls split the sequence:
-    the second call's combined prepass, chained segment states, segment-
-    parallel dx read-modify-writes and the dinitial_state written only by the
-    first segment must add into the first call's gradients."""
+    the second call's segment walks, combine (which writes dinitial_state),
+    boundary corrections and segment-parallel dx read-modify-writes must add
+    into the first call's gradients."""
     w = M130
     b, l = 1, 2048
     hs = (24, 3)
