@@ -46,6 +46,7 @@
 //    each piece's end state from zero, a combine chains them, and the main
 //    kernel walks every segment from its chained start state.
 #include <atomic>
+#include <type_traits>
 #include <utility>
 
 #include "device_common.h"
@@ -203,6 +204,8 @@ __device__ __forceinline__ float dpp_f(float v) {
 // B and C channels in LDS, in the same fp32 operation order and rounding as
 // the conv kernel, and turns raw dt into dt = softplus(dt + dt_bias) (or
 // dt + dt_bias), rounded to bf16 as a stored dt would be.
+// Byte offset of lane `lane`'s 16 bytes of fragment f in a tile's block.
+__device__ __forceinline__ uint32_t frag_off(int f, int lane) { return (uint32_t)(f * 64 + lane) * 16; }
 constexpr int kBCP = kN + 8;  // LDS row pitch (elements) of the staged B and C rows
 constexpr int kBCRows = kQ + 3;  // the tile's rows and, for a fused call, three before it
 // B and C rows; the dt transpose buffer reuses the C rows once the G and C
@@ -343,39 +346,71 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void t
   // G^T tiles: A operand row m takes B row k*32 + (m/4)*8 + m%4 (tile a) or
   // that + 4 (tile b), B operand column n is C row tb*16 + n, so output slot
   // i of lane (r, g) is G[tb*16 + r][k*32 + g*8 + i] (a) and [.. + 4 + i] (b).
-  for (int f = wave; f < kNG; f += 8) {
-    int tb = 0;
-    while (gbase(tb + 1) <= f) ++tb;
-    const int k = f - gbase(tb);
-    const int sa = k * 32 + (r16 >> 2) * 8 + (r16 & 3);
-    f32x4 da = {0, 0, 0, 0}, db = {0, 0, 0, 0};
+  // Waves 0-3 form three fragments, waves 4-7 two (f = wave + 8i), each
+  // wave's fragments in one unrolled pass so that the LDS reads of all of them
+  // are in flight together (one fragment at a time waited for its reads).
+  // Fragments leave with nontemporal stores: they are read back from HBM by
+  // the scan kernels, and streaming them out shortens the kernel's drain.
+  const uint32_t fbytes = (uint32_t)(kNFR * kFragBytes);
+  auto g_frags = [&](auto nf) {
+    constexpr int NF = decltype(nf)::value;
+    int tbs[NF], sas[NF];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int f = wave + 8 * i;
+      int tb = 0;
+      while (gbase(tb + 1) <= f) ++tb;
+      tbs[i] = tb;
+      sas[i] = (f - gbase(tb)) * 32 + (r16 >> 2) * 8 + (r16 & 3);
+    }
+    f32x4 da[NF], db[NF];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) da[i] = db[i] = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
       const int n = kb * 32 + g * 8;
-      da = mma(lds_frag(&Bs[sa][n]), lds_frag(&Cs[tb * 16 + r16][n]), da);
-      db = mma(lds_frag(&Bs[sa + 4][n]), lds_frag(&Cs[tb * 16 + r16][n]), db);
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        const Frag8<bf16> cfr = lds_frag(&Cs[tbs[i] * 16 + r16][n]);
+        da[i] = mma(lds_frag(&Bs[sas[i]][n]), cfr, da[i]);
+        db[i] = mma(lds_frag(&Bs[sas[i] + 4][n]), cfr, db[i]);
+      }
     }
-    const uint2 lo = pack4(da), hi = pack4(db);
-    out[f * 64 + lane] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-  }
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const uint2 lo = pack4(da[i]), hi = pack4(db[i]);
+      store16_nt_ranged(out, fbytes, frag_off(wave + 8 * i, lane), make_uint4(lo.x, lo.y, hi.x, hi.y));
+    }
+  };
+  static_assert(kNG == 20, "three G fragments for waves 0-3, two for waves 4-7");
+  if (wave < 4)
+    g_frags(std::integral_constant<int, 3>{});
+  else
+    g_frags(std::integral_constant<int, 2>{});
   // B^T fragments with LDS transpose loads: within each 16-lane group lane i
   // receives element i%4 of the 8 bytes lane 4k + i/4 addresses (k = 0..3),
   // so lane src addresses row ks*32 + g*8 + src/4 (+4), columns
   // np*32 + (src%4)*8 + e*4 .. +3.
   typedef __attribute__((address_space(3))) short4v lds_short4;
-  for (int f = wave; f < kNB * kSB; f += 8) {
+  static_assert(kNB * kSB == 32 && kTB * kKB == 32, "four B^T and four C fragments per wave");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int f = wave + 8 * i;
     const int npe = f / kSB, ks = f % kSB;  // npe = np*2 + e
     const int src = lane & 15;
     const int col = (npe >> 1) * 32 + (src & 3) * 8 + (npe & 1) * 4;
     const int s1 = ks * 32 + g * 8 + (src >> 2);
     const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)&Bs[s1][col]);
     const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)&Bs[s1 + 4][col]);
-    out[(kBT0 + f) * 64 + lane] =
-        __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    store16_nt_ranged(out, fbytes, frag_off(kBT0 + f, lane),
+                      __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
   }
-  for (int f = wave; f < kTB * kKB; f += 8) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int f = wave + 8 * i;
     const int tb = f / kKB, kb = f % kKB;
-    out[(kC0 + f) * 64 + lane] = *reinterpret_cast<const uint4*>(&Cs[tb * 16 + r16][kb * 32 + g * 8]);
+    store16_nt_ranged(out, fbytes, frag_off(kC0 + f, lane),
+                      *reinterpret_cast<const uint4*>(&Cs[tb * 16 + r16][kb * 32 + g * 8]));
   }
 
   // dt, 64 heads at a time: [token][head] -> LDS -> [head][token]
@@ -436,7 +471,6 @@ struct BK {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_frags(const BK& k, int b, int c) {
   return uniform_rsrc(k.frags + ((int64_t)b * k.ntiles + c) * kNFR * 64, (uint32_t)(kNFR * kFragBytes));
 }
-__device__ __forceinline__ uint32_t frag_off(int f, int lane) { return (uint32_t)(f * 64 + lane) * 16; }
 
 // ---------------------------------------------------------------------------
 // Output waves (OUT only).  Each produces one 16-token block tb of every tile
