@@ -31,6 +31,8 @@ Also reported on the same JSON line:
     the slices are, with their HBM fractions;
   - ``decode``: the recurrent decode step (conv state roll + scan step) for a
     batch of 256 sequences at mixed widths, 1024 tokens captured in a HIP graph;
+    ``decode.fused_vs_two_launches``: microseconds per token of those two
+    launches against the one-launch mm_ssd_step_fused at batch 1, 16, 64, 256;
   - ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample
     of the same workload, scaled to the step.
 
@@ -621,6 +623,64 @@ def bench_configs(torch, mm, synth, dev, flush):
     return res
 
 
+def decode_batch_sweep(torch, mm, synth, dev, batches=(1, 16, 64, 256)):
+    """Decode step of the decode workload's model (mixed widths) at several
+    batch sizes: the conv step and mm_ssd_step as two launches per token
+    against mm_ssd_step_fused (one launch, two conv-state buffers in turn),
+    each in HIP graphs of 64 tokens, best of two timings of 16 replays;
+    microseconds per token."""
+    d = synth.WORKLOADS["decode"]
+    H, P, N, cd = d.n_heads, d.d_head, d.d_state, d.conv_dim
+    out = {}
+    for bsz in batches:
+        pool = synth.decode_pool(d, pool=64, batch=bsz)
+        xbc_t, dt_t = pool["xbc_t"].to(dev), pool["dt_t"].to(dev)
+        hv = synth.decode_heads(d, batch=bsz).to(dev)
+        A, D, cw = synth.draw_A(d).to(dev), synth.draw_D(d).to(dev), synth.draw_conv_w(d).to(dev)
+        state = torch.zeros((bsz, H, P, N), device=dev)
+        csb = (torch.zeros((bsz, 3, cd), device=dev), torch.zeros((bsz, 3, cd), device=dev))
+        u = torch.empty((bsz, 1, cd), device=dev)
+        yt = torch.empty((bsz, H, P), device=dev)
+
+        def two(k):
+            mm.conv1d_silu(xbc_t[k].unsqueeze(1), cw, None, csb[0], d_inner=d.d_inner, d_head=P,
+                           d_state=N, n_heads_active=H, heads_per_seq=hv, out=u)
+            u2 = u[:, 0]
+            mm.ssd_step(state, u2[:, :d.d_inner].view(bsz, H, P), dt_t[k], A,
+                        u2[:, d.d_inner:d.d_inner + N], u2[:, d.d_inner + N:], D,
+                        n_heads_active=H, heads_per_seq=hv, y=yt)
+
+        def fused(k):
+            mm.ssd_step_fused(state, csb[k % 2], csb[(k + 1) % 2], xbc_t[k], cw, dt_t[k], A, D,
+                              n_heads_active=H, heads_per_seq=hv, y=yt)
+
+        best = {}
+        for name, fn in (("two_launches_us", two), ("fused_us", fused)) * 2:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for k in range(4):
+                    fn(k)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for k in range(64):
+                    fn(k)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(16):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            best[name] = min(best.get(name, 1e30), e0.elapsed_time(e1) * 1e3 / (16 * 64))
+            del g
+        out[str(bsz)] = best
+    return out
+
+
 def bench_decode(torch, mm, synth, dev):
     d = synth.WORKLOADS["decode"]
     bsz, H, P, N, cd = d.batch, d.n_heads, d.d_head, d.d_state, d.conv_dim
@@ -670,6 +730,7 @@ def bench_decode(torch, mm, synth, dev):
     steps = reps * 64
     per_step_us = ms * 1e3 / steps
     by = decode_bytes(hv_cpu.tolist(), P, N, d.d_inner)
+    sweep = decode_batch_sweep(torch, mm, synth, dev)
     # speculative decoding at full width (64 heads, every sequence): verify 4
     # draft tokens in one pass over the states (conv of the 4 tokens on a copy
     # of the conv state, then mm_ssd_step_multi with no state write), commit
@@ -717,6 +778,7 @@ def bench_decode(torch, mm, synth, dev):
                         "round-robin {16,32,64} heads, 1024 tokens in a HIP graph",
             "tokens_per_s": bsz * steps / (ms * 1e-3), "us_per_step": per_step_us,
             "bytes_per_step": by, "hbm_frac": by / (per_step_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+            "fused_vs_two_launches": sweep,
             "spec_decode": {"draft_tokens": kd, "heads": H, "verify_us": v_us, "commit_us": c_us,
                             "four_single_steps_us": s_us,
                             "verify_plus_commit_vs_steps": s_us / (v_us + c_us)}}

@@ -369,6 +369,44 @@ int mm_ssd_step(float* state,
                 const int32_t* heads_active_per_seq, int dtype, void* stream);
 
 /*
+ * One decode token with the conv folded in: mm_conv1d_silu's decode step
+ * ("MatMamba", block paragraph: the conv and SiLU over [x | B | C] come before
+ * the SSM) followed by mm_ssd_step (Mamba page, Strengths: linear-time
+ * recurrent inference), in one launch.  The results equal that pair of calls
+ * bit for bit: y_t, state and the advanced conv state.  The conv outputs are
+ * rounded to dtype, as a stored conv output would be, and are not written
+ * out.
+ *   state (batch, n_heads, d_head, d_state) fp32, read and written in place
+ *        for heads [0, h_b) of sequence b (h_b as in mm_conv1d_silu).
+ *   conv_state_in (batch, 3, conv_dim) fp32: the history, laid out as in
+ *        mm_conv1d_silu; read only.
+ *   conv_state_out (batch, 3, conv_dim) fp32: receives the advanced history.
+ *        Active channels (the x slice and every B/C channel) hold the last
+ *        three raw inputs; every other channel is copied from conv_state_in.
+ *        It must overlap neither conv_state_in nor state.  A decode loop
+ *        alternates two such buffers.
+ *   xbc_t (batch rows, xbc_row_stride) dtype: the token's raw [x | B | C]
+ *        row, conv_dim = n_heads*d_head + 2*d_state.
+ *   conv_w (conv_dim, 4) fp32; conv_bias (conv_dim) fp32 or NULL.
+ *   dt_t, A, D, y_t: as in mm_ssd_step (dt_t post-softplus).
+ * Ownership: the caller owns every buffer; nothing is allocated or kept.
+ * Errors: those of mm_ssd_step and mm_conv1d_silu.  In addition:
+ *   - MM_ERR_UNSUPPORTED unless d_head is a multiple of 8 and
+ *     d_head + 2*d_state <= 768;
+ *   - MM_ERR_ALIGN unless both conv states are 16-byte aligned;
+ *   - MM_ERR_SHAPE if conv_state_out overlaps conv_state_in or state.
+ */
+int mm_ssd_step_fused(float* state, const float* conv_state_in, float* conv_state_out,
+                      const void* xbc_t, int64_t xbc_row_stride,
+                      const float* conv_w, const float* conv_bias,
+                      const void* dt_t, int64_t dt_row_stride,
+                      const float* A, const float* D,
+                      void* y_t, int64_t y_row_stride,
+                      int64_t batch, int64_t n_heads, int64_t d_head,
+                      int64_t d_state, int64_t ngroups, int64_t n_heads_active,
+                      const int32_t* heads_active_per_seq, int dtype, void* stream);
+
+/*
  * ntok tokens per sequence in one pass over the states, for nested-draft
  * speculative decoding ("MatMamba", deployment paragraph: a smaller nested
  * slice drafts tokens that the larger model verifies).  For each active

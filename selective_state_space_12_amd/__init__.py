@@ -100,6 +100,12 @@ def lib() -> ctypes.CDLL:
                                             _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                             _i64, _i64, _vp, _vp, _int, _vp]
             L.mm_ssd_step_multi.restype = _int
+            # state, cs_in, cs_out, xbc, xbcs, w, bias, dt, dts, A, D, y, ys,
+            # batch, n_heads, d_head, d_state, ngroups, active, per_seq, dtype, stream
+            L.mm_ssd_step_fused.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp,
+                                            _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                            _vp, _int, _vp]
+            L.mm_ssd_step_fused.restype = _int
             L.mm_conv_state_advance.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                                                 _i64, _i64, _int, _vp]
             L.mm_conv_state_advance.restype = _int
@@ -164,6 +170,19 @@ def _row_stride(t: torch.Tensor, name: str, inner: Tuple[int, ...]) -> int:
     if t.shape[0] > 1 and t.shape[1] > 1 and t.stride(0) != t.shape[1] * t.stride(1):
         raise ValueError(f"{name}: batches must be seqlen rows apart")
     return rs
+
+
+def _batch_row_stride(t: torch.Tensor, name: str, inner: Tuple[int, ...]) -> int:
+    """Row stride of a (batch, *inner) view of one token per sequence whose
+    inner block is contiguous."""
+    if tuple(t.shape[1:]) != tuple(inner):
+        raise ValueError(f"{name}: expected (batch, {inner}), got {tuple(t.shape)}")
+    expect = 1
+    for d in range(t.dim() - 1, 0, -1):
+        if t.shape[d] > 1 and t.stride(d) != expect:
+            raise ValueError(f"{name}: inner dimensions must be contiguous")
+        expect *= t.shape[d]
+    return t.stride(0) if t.shape[0] > 1 else expect
 
 
 def abi_version() -> int:
@@ -715,25 +734,51 @@ def ssd_step(state: torch.Tensor, x_t: torch.Tensor, dt_t: torch.Tensor, A: torc
     if state.dtype != torch.float32 or not state.is_contiguous():
         raise ValueError("state must be a contiguous fp32 tensor")
 
-    def rows(t, name, inner):
-        if tuple(t.shape[1:]) != tuple(inner):
-            raise ValueError(f"{name}: expected (batch, {inner}), got {tuple(t.shape)}")
-        expect = 1
-        for d in range(t.dim() - 1, 0, -1):
-            if t.shape[d] > 1 and t.stride(d) != expect:
-                raise ValueError(f"{name}: inner dimensions must be contiguous")
-            expect *= t.shape[d]
-        return t.stride(0) if t.shape[0] > 1 else expect
-
-    xs = rows(x_t, "x_t", (n_heads, d_head))
-    ys = rows(y, "y", (n_heads, d_head))
-    dts = rows(dt_t, "dt_t", (n_heads,))
-    bs = rows(B_t, "B_t", (ngroups, d_state))
-    cs = rows(C_t, "C_t", (ngroups, d_state))
+    xs = _batch_row_stride(x_t, "x_t", (n_heads, d_head))
+    ys = _batch_row_stride(y, "y", (n_heads, d_head))
+    dts = _batch_row_stride(dt_t, "dt_t", (n_heads,))
+    bs = _batch_row_stride(B_t, "B_t", (ngroups, d_state))
+    cs = _batch_row_stride(C_t, "C_t", (ngroups, d_state))
     if heads_per_seq is not None and (heads_per_seq.dtype != torch.int32 or not heads_per_seq.is_contiguous()):
         raise ValueError("heads_per_seq must be a contiguous int32 tensor")
     st = lib().mm_ssd_step(_ptr(state), _ptr(x_t), xs, _ptr(dt_t), dts, _ptr(A), _ptr(B_t), bs,
                            _ptr(C_t), cs, _ptr(D), _ptr(y), ys, batch, n_heads, d_head, d_state,
                            ngroups, h_act, _ptr(heads_per_seq), _dtype_code(x_t), _stream())
     _check("mm_ssd_step", st)
+    return y
+
+
+def ssd_step_fused(state: torch.Tensor, conv_state_in: torch.Tensor, conv_state_out: torch.Tensor,
+                   xbc_t: torch.Tensor, conv_w: torch.Tensor, dt_t: torch.Tensor, A: torch.Tensor,
+                   D: Optional[torch.Tensor] = None, conv_bias: Optional[torch.Tensor] = None, *,
+                   n_heads_active: Optional[int] = None,
+                   heads_per_seq: Optional[torch.Tensor] = None,
+                   y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode token with the conv folded in (mm_ssd_step_fused): the
+    token's raw [x | B | C] row xbc_t (batch, conv_dim); the conv history is
+    read from conv_state_in and the advanced one written to conv_state_out
+    (both (batch, 3, conv_dim) fp32, disjoint); state (batch, n_heads, d_head,
+    d_state) fp32 is updated in place.  Returns y_t (batch, n_heads, d_head)."""
+    batch, n_heads, d_head, d_state = state.shape
+    conv_dim = n_heads * d_head + 2 * d_state
+    h_act = n_heads if n_heads_active is None else int(n_heads_active)
+    if state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError("state must be a contiguous fp32 tensor")
+    for name, t in (("conv_state_in", conv_state_in), ("conv_state_out", conv_state_out)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (batch, 3, conv_dim):
+            raise ValueError(f"{name} must be a contiguous fp32 (batch, 3, conv_dim) tensor")
+    if conv_w.dtype != torch.float32 or not conv_w.is_contiguous() or conv_w.numel() != conv_dim * 4:
+        raise ValueError("conv_w must be a contiguous fp32 (conv_dim, 4) tensor")
+    if y is None:
+        y = torch.empty((batch, n_heads, d_head), dtype=xbc_t.dtype, device=xbc_t.device)
+    xs = _batch_row_stride(xbc_t, "xbc_t", (conv_dim,))
+    ys = _batch_row_stride(y, "y", (n_heads, d_head))
+    dts = _batch_row_stride(dt_t, "dt_t", (n_heads,))
+    if heads_per_seq is not None and (heads_per_seq.dtype != torch.int32 or not heads_per_seq.is_contiguous()):
+        raise ValueError("heads_per_seq must be a contiguous int32 tensor")
+    st = lib().mm_ssd_step_fused(_ptr(state), _ptr(conv_state_in), _ptr(conv_state_out), _ptr(xbc_t),
+                                 xs, _ptr(conv_w), _ptr(conv_bias), _ptr(dt_t), dts, _ptr(A), _ptr(D),
+                                 _ptr(y), ys, batch, n_heads, d_head, d_state, 1, h_act,
+                                 _ptr(heads_per_seq), _dtype_code(xbc_t), _stream())
+    _check("mm_ssd_step_fused", st)
     return y

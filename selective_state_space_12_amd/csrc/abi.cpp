@@ -483,4 +483,39 @@ int mm_ssd_step(float* state, const void* x_t, int64_t x_row_stride, const void*
   return hip_status(launch_ssd_step(a, dtype, as_stream(stream)));
 }
 
+int mm_ssd_step_fused(float* state, const float* conv_state_in, float* conv_state_out,
+                      const void* xbc_t, int64_t xbc_row_stride, const float* conv_w,
+                      const float* conv_bias, const void* dt_t, int64_t dt_row_stride,
+                      const float* A, const float* D, void* y_t, int64_t y_row_stride,
+                      int64_t batch, int64_t n_heads, int64_t d_head, int64_t d_state,
+                      int64_t ngroups, int64_t n_heads_active,
+                      const int32_t* heads_active_per_seq, int dtype, void* stream) {
+  const int st = validate_ssd_step_fused(state, conv_state_in, conv_state_out, xbc_t,
+                                         xbc_row_stride, conv_w, conv_bias, dt_t, dt_row_stride,
+                                         A, y_t, y_row_stride, batch, n_heads, d_head, d_state,
+                                         ngroups, n_heads_active, dtype);
+  if (st != MM_OK) return st;
+  StepFusedArgs a;
+  a.state = state;
+  a.cs_in = conv_state_in;
+  a.cs_out = conv_state_out;
+  a.xbc = xbc_t;
+  a.xbcs = xbc_row_stride;
+  a.w = conv_w;
+  a.bias = conv_bias;
+  a.dt = dt_t;
+  a.dts = dt_row_stride;
+  a.A = A;
+  a.D = D;
+  a.y = y_t;
+  a.ys = y_row_stride;
+  a.batch = batch;
+  a.n_heads = (int)n_heads;
+  a.d_head = (int)d_head;
+  a.d_state = (int)d_state;
+  a.heads_cap = (int)n_heads_active;
+  a.heads_per_seq = heads_active_per_seq;
+  return hip_status(launch_ssd_step_fused(a, dtype, as_stream(stream)));
+}
+
 }  // extern "C"

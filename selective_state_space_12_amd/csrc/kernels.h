@@ -47,6 +47,30 @@ struct StepArgs {
 
 hipError_t launch_ssd_step(const StepArgs& a, int dtype, hipStream_t s);
 
+// One decode token with the conv folded in (ssd_step.hip): raw [x | B | C]
+// row in, conv state read from cs_in and the advanced one written to cs_out.
+struct StepFusedArgs {
+  float* state;
+  const float* cs_in;
+  float* cs_out;
+  const void* xbc;
+  int64_t xbcs;
+  const float* w;
+  const float* bias;
+  const void* dt;
+  int64_t dts;
+  const float* A;
+  const float* D;
+  void* y;
+  int64_t ys;
+  int64_t batch;
+  int n_heads, d_head, d_state;
+  int heads_cap;
+  const int32_t* heads_per_seq;
+};
+
+hipError_t launch_ssd_step_fused(const StepFusedArgs& a, int dtype, hipStream_t s);
+
 // ntok tokens per sequence in one pass over the states (ssd_step.hip).
 struct StepMultiArgs {
   const float* state_in;

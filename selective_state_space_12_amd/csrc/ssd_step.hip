@@ -87,6 +87,154 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(
   }
 }
 
+// One decode token with the causal conv (kernel 4) + SiLU folded in.  The
+// workgroup of (head h, sequence b) reads the token's raw [x | B | C] row and
+// applies the conv to its head's x channels and to the B and C channels, in
+// the conv step's fp32 order, rounding each output to the storage type (as a
+// conv output stored in HBM would be).  It then updates the state exactly as
+// ssd_step_kernel does.  The conv state is read from cs_in, and the advanced
+// state is written to cs_out, a separate buffer, so no workgroup can overwrite
+// taps that another is still reading.
+//  - Head h's workgroup writes the taps of its x channels.
+//  - Head 0's workgroup writes the B and C taps.
+//  - Workgroups of heads outside the sequence's slice copy their x channels'
+//    taps unchanged.
+// So cs_out ends up exactly as the in-place conv step would leave cs_in.
+// Order of work: each thread first issues the loads of one or two of the
+// workgroup's d_head + 2*d_state conv channels, then its state rows, so the
+// conv's inputs and the state are in flight together.  The conv outputs go
+// through LDS (one barrier) to the lanes that use them.  The B and C inputs,
+// taps and weights are re-read by every head of a sequence: a few KB, L2
+// hits after the first head.
+constexpr int kFusedConvCh = 3;  // conv channels per thread: d_head + 2*d_state <= 768
+
+template <typename T, int LPR, bool kBias>
+__global__ __launch_bounds__(kStepThreads) void ssd_step_fused_kernel(
+    float* __restrict__ state, const float* __restrict__ cs_in, float* __restrict__ cs_out,
+    const T* __restrict__ xbc, int64_t xbcs, const float* __restrict__ w,
+    const float* __restrict__ bias, const T* __restrict__ dt, int64_t dts,
+    const float* __restrict__ A, const float* __restrict__ D, T* __restrict__ y, int64_t ys,
+    int n_heads, int P, int heads_cap, const int32_t* __restrict__ heads_per_seq) {
+  constexpr int N = LPR * 4;
+  constexpr int kRowsPerPass = kStepThreads / LPR;
+  constexpr int kUnroll = 8;
+  __shared__ float conv_out[kFusedConvCh * kStepThreads];  // x channels, then B, then C
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int64_t d_inner = (int64_t)n_heads * P;
+  const int64_t cd = d_inner + 2 * N;  // conv_dim
+  const float* ci = cs_in + (int64_t)b * 3 * cd;
+  float* co = cs_out + (int64_t)b * 3 * cd;
+  const T* urow = xbc + (int64_t)b * xbcs;
+  const int nch = P + 2 * N;
+
+  if (h >= clamp_heads(heads_per_seq, b, heads_cap)) {
+    // Outside the slice: the x channels' taps pass through unchanged.  Head
+    // 0 still advances the B and C taps (the conv step always runs them).
+    for (int i = threadIdx.x; i < 3 * P; i += kStepThreads) {
+      const int k = i / P;
+      const int64_t c = (int64_t)h * P + (i - k * P);
+      co[k * cd + c] = ci[k * cd + c];
+    }
+    if (h == 0) {
+      for (int i = threadIdx.x; i < 2 * N; i += kStepThreads) {
+        const int64_t c = d_inner + i;
+        const float u = to_f32(urow[c]), t1 = ci[cd + c], t2 = ci[2 * cd + c];
+        co[c] = t1;
+        co[cd + c] = t2;
+        co[2 * cd + c] = u;
+      }
+    }
+    return;
+  }
+
+  // conv channel i of the workgroup: x channel h*P + i, then B and C
+  auto chan = [&](int i) -> int64_t { return i < P ? (int64_t)h * P + i : d_inner + (i - P); };
+  float cu[kFusedConvCh], t0[kFusedConvCh], t1[kFusedConvCh], t2[kFusedConvCh], cb[kFusedConvCh];
+  float4 wk[kFusedConvCh];
+#pragma unroll
+  for (int q = 0; q < kFusedConvCh; ++q) {
+    if (q > 0 && q * kStepThreads >= nch) break;  // uniform: no channel in this slot
+    const int i = min((int)threadIdx.x + q * kStepThreads, nch - 1);  // clamped: every load valid
+    const int64_t c = chan(i);
+    cu[q] = to_f32(urow[c]);
+    t0[q] = ci[c];
+    t1[q] = ci[cd + c];
+    t2[q] = ci[2 * cd + c];
+    wk[q] = *reinterpret_cast<const float4*>(w + c * 4);
+    cb[q] = kBias ? bias[c] : 0.0f;
+  }
+
+  const int lane_in_row = threadIdx.x % LPR;
+  const int row_in_pass = threadIdx.x / LPR;
+  const int n0 = lane_in_row * 4;
+  const float dtv = to_f32(dt[(int64_t)b * dts + h]);
+  const float alpha = exp2f(dtv * A[h] * kLog2e);
+  const float Dh = D ? D[h] : 0.0f;
+  float* sbase = state + ((int64_t)b * n_heads + h) * (int64_t)P * N;
+  T* yrow = y + (int64_t)b * ys + (int64_t)h * P;
+
+  // first pass of state rows in flight before the conv is formed
+  f32x4 s[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int p = min(u * kRowsPerPass + row_in_pass, P - 1);
+    s[u] = *reinterpret_cast<const f32x4*>(sbase + (int64_t)p * N + n0);
+  }
+
+#pragma unroll
+  for (int q = 0; q < kFusedConvCh; ++q) {
+    const int i = threadIdx.x + q * kStepThreads;
+    if (q > 0 && q * kStepThreads >= nch) break;
+    if (i < nch) {
+      float pre = cb[q];
+      pre = fmaf(wk[q].x, t0[q], pre);
+      pre = fmaf(wk[q].y, t1[q], pre);
+      pre = fmaf(wk[q].z, t2[q], pre);
+      pre = fmaf(wk[q].w, cu[q], pre);
+      conv_out[i] = to_f32(from_f32<T>(silu(pre)));
+      if (i < P || h == 0) {  // taps of the channels this workgroup owns
+        const int64_t c = chan(i);
+        co[c] = t1[q];
+        co[cd + c] = t2[q];
+        co[2 * cd + c] = cu[q];
+      }
+    }
+  }
+  __syncthreads();
+
+  float bv[4], cv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bv[j] = conv_out[P + n0 + j];
+    cv[j] = conv_out[P + N + n0 + j];
+  }
+  for (int p0 = 0; p0 < P; p0 += kRowsPerPass * kUnroll) {
+    if (p0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int p = min(p0 + u * kRowsPerPass + row_in_pass, P - 1);
+        s[u] = *reinterpret_cast<const f32x4*>(sbase + (int64_t)p * N + n0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int p = p0 + u * kRowsPerPass + row_in_pass;
+      const float xv = conv_out[min(p, P - 1)];
+      const float xd = dtv * xv;
+      f32x4 hn;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hn[j] = fmaf(alpha, s[u][j], xd * bv[j]);
+      if (p < P)
+        __builtin_nontemporal_store(hn, reinterpret_cast<f32x4*>(sbase + (int64_t)p * N + n0));
+      float part = hn[0] * cv[0] + hn[1] * cv[1] + hn[2] * cv[2] + hn[3] * cv[3];
+#pragma unroll
+      for (int m = LPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, LPR);
+      if (p < P && lane_in_row == 0) yrow[p] = from_f32<T>(part + Dh * xv);
+    }
+  }
+}
+
 // k tokens per sequence in one pass over the states (speculative decoding:
 // verify a draft, then commit its accepted prefix): each workgroup reads its
 // (head, sequence) state once, applies the sequence's first ntok_b tokens in
@@ -302,6 +450,29 @@ hipError_t launch_lpr(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int LPR>
+hipError_t launch_fused_lpr(const StepFusedArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)a.n_heads, (unsigned)a.batch);
+  auto kern = a.bias ? ssd_step_fused_kernel<T, LPR, true> : ssd_step_fused_kernel<T, LPR, false>;
+  hipLaunchKernelGGL(kern, grid, dim3(kStepThreads), 0, s, a.state, a.cs_in, a.cs_out,
+                     static_cast<const T*>(a.xbc), a.xbcs, a.w, a.bias,
+                     static_cast<const T*>(a.dt), a.dts, a.A, a.D, static_cast<T*>(a.y), a.ys,
+                     a.n_heads, a.d_head, a.heads_cap, a.heads_per_seq);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_fused_typed(const StepFusedArgs& a, hipStream_t s) {
+  switch (a.d_state) {
+    case 16: return launch_fused_lpr<T, 4>(a, s);
+    case 32: return launch_fused_lpr<T, 8>(a, s);
+    case 64: return launch_fused_lpr<T, 16>(a, s);
+    case 128: return launch_fused_lpr<T, 32>(a, s);
+    case 256: return launch_fused_lpr<T, 64>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T>
 hipError_t launch_typed(const StepArgs& a, hipStream_t s) {
   switch (a.d_state) {
@@ -319,6 +490,11 @@ hipError_t launch_typed(const StepArgs& a, hipStream_t s) {
 hipError_t launch_ssd_step(const StepArgs& a, int dtype, hipStream_t s) {
   if (dtype == MM_BF16) return launch_typed<bf16>(a, s);
   return launch_typed<float>(a, s);
+}
+
+hipError_t launch_ssd_step_fused(const StepFusedArgs& a, int dtype, hipStream_t s) {
+  if (dtype == MM_BF16) return launch_fused_typed<bf16>(a, s);
+  return launch_fused_typed<float>(a, s);
 }
 
 hipError_t launch_ssd_step_multi(const StepMultiArgs& a, int dtype, hipStream_t s) {

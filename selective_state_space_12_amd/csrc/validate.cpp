@@ -319,6 +319,51 @@ int validate_ssd_step(const float* state, const void* x_t, int64_t x_row_stride,
   return MM_OK;
 }
 
+int validate_ssd_step_fused(const float* state, const float* cs_in, const float* cs_out,
+                            const void* xbc_t, int64_t xbc_row_stride, const float* w,
+                            const float* bias, const void* dt_t, int64_t dt_row_stride,
+                            const float* A, const void* y_t, int64_t y_row_stride, int64_t batch,
+                            int64_t n_heads, int64_t d_head, int64_t d_state, int64_t ngroups,
+                            int64_t n_heads_active, int dtype) {
+  if (!state || !cs_in || !cs_out || !xbc_t || !w || !dt_t || !A || !y_t) return MM_ERR_NULL;
+  const int64_t el = dtype_bytes(dtype);
+  if (el == 0) return MM_ERR_DTYPE;
+  if (!pos(batch) || !pos(n_heads) || !pos(d_head) || !pos(d_state) || !pos(ngroups))
+    return MM_ERR_SHAPE;
+  if (n_heads_active < 1 || n_heads_active > n_heads) return MM_ERR_SLICE;
+  if (n_heads % ngroups != 0) return MM_ERR_SHAPE;
+  if (batch > kMaxGridYZ || n_heads >= (int64_t(1) << 31)) return MM_ERR_SHAPE;
+  if (ngroups != 1) return MM_ERR_UNSUPPORTED;
+  if (d_state != 16 && d_state != 32 && d_state != 64 && d_state != 128 && d_state != 256)
+    return MM_ERR_UNSUPPORTED;
+  if (d_head % 8 != 0) return MM_ERR_UNSUPPORTED;  // the conv's channel groups
+  if (d_head + 2 * d_state > 768) return MM_ERR_UNSUPPORTED;  // three conv channels per thread
+  if (!mul_ok(n_heads, d_head)) return MM_ERR_SHAPE;
+  const int64_t conv_dim = n_heads * d_head + 2 * d_state;
+  const int64_t xw = n_heads_active * d_head;
+  if (xbc_row_stride < conv_dim || y_row_stride < xw || dt_row_stride < n_heads_active)
+    return MM_ERR_SHAPE;
+  if (!mul_ok(batch, xbc_row_stride) || !mul_ok(batch, y_row_stride) ||
+      !mul_ok(batch, dt_row_stride) || !mul_ok(batch * 3, conv_dim) ||
+      !mul_ok(batch * n_heads, d_head * d_state))
+    return MM_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(state) % 16 != 0 || reinterpret_cast<uintptr_t>(cs_in) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(cs_out) % 16 != 0 || reinterpret_cast<uintptr_t>(w) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(bias) % 4 != 0)
+    return MM_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(xbc_t) % el != 0 || reinterpret_cast<uintptr_t>(y_t) % el != 0 ||
+      reinterpret_cast<uintptr_t>(dt_t) % el != 0)
+    return MM_ERR_ALIGN;
+  // The advanced conv state goes to a buffer of its own: it may overlap
+  // neither the state it is advanced from nor the SSD state.
+  const uintptr_t cb = uintptr_t(batch * 3 * conv_dim * 4);
+  const uintptr_t i0 = reinterpret_cast<uintptr_t>(cs_in), o0 = reinterpret_cast<uintptr_t>(cs_out);
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(state);
+  const uintptr_t sb = uintptr_t(batch * n_heads * d_head * d_state * 4);
+  if ((i0 < o0 + cb && o0 < i0 + cb) || (s0 < o0 + cb && o0 < s0 + sb)) return MM_ERR_SHAPE;
+  return MM_OK;
+}
+
 int validate_ssd_backward_shape(int64_t batch, int64_t seqlen, int64_t n_heads, int64_t d_head,
                                 int64_t d_state, int64_t ngroups, int64_t n_heads_active,
                                 int dtype) {

@@ -91,6 +91,17 @@ int validate_ssd_step(const float* state, const void* x_t, int64_t x_row_stride,
                       int64_t d_head, int64_t d_state, int64_t ngroups,
                       int64_t n_heads_active, int dtype);
 
+// mm_ssd_step_fused: validate_ssd_step's checks for the state, dt and y,
+// validate_conv's for the raw row and the weights (d_head a multiple of 8),
+// 16-byte aligned conv states, and conv_state_out overlapping neither
+// conv_state_in nor the state.
+int validate_ssd_step_fused(const float* state, const float* cs_in, const float* cs_out,
+                            const void* xbc_t, int64_t xbc_row_stride, const float* w,
+                            const float* bias, const void* dt_t, int64_t dt_row_stride,
+                            const float* A, const void* y_t, int64_t y_row_stride, int64_t batch,
+                            int64_t n_heads, int64_t d_head, int64_t d_state, int64_t ngroups,
+                            int64_t n_heads_active, int dtype);
+
 // mm_conv1d_silu_backward: validate_conv's checks with dxbc_in as the
 // output, dout's stride and alignment, accumulate 0 or 1, and no gradient
 // overlapping an input or another gradient.

@@ -223,6 +223,36 @@ int main() {
     expect("conv bwd dw over dstate", cb(D1, G1, DS, cd, 0), MM_ERR_SHAPE);
   }
 
+  // fused decode step: 256 sequences, 64 heads x 64 x 128, raw rows of 4352
+  // channels at P; state at F, conv states at CI / CO, y at P2
+  {
+    const float* CI = reinterpret_cast<const float*>(uintptr_t(0x6000000000ull));
+    const float* CO = reinterpret_cast<const float*>(uintptr_t(0x7000000000ull));
+    auto sf = [&](const float* st, const float* ci, const float* co, const float* w, int64_t xs,
+                  int64_t P_, int64_t N_, int64_t ha, int dt_code) {
+      return validate_ssd_step_fused(st, ci, co, P, xs, w, nullptr, P, 64, F, P2, 64 * P_, 256, 64,
+                                     P_, N_, 1, ha, dt_code);
+    };
+    expect("step fused ok", sf(F, CI, CO, F, cd, 64, 128, 64, MM_BF16), MM_OK);
+    expect("step fused null conv out", sf(F, CI, nullptr, F, cd, 64, 128, 64, MM_BF16), MM_ERR_NULL);
+    expect("step fused null conv w", sf(F, CI, CO, nullptr, cd, 64, 128, 64, MM_BF16), MM_ERR_NULL);
+    expect("step fused in place", sf(F, CI, CI, F, cd, 64, 128, 64, MM_BF16), MM_ERR_SHAPE);
+    expect("step fused out over state", sf(CO, CI, CO, F, cd, 64, 128, 64, MM_BF16), MM_ERR_SHAPE);
+    expect("step fused out overlaps in",
+           sf(F, CI, reinterpret_cast<const float*>(uintptr_t(0x6000000100ull)), F, cd, 64, 128, 64,
+              MM_BF16), MM_ERR_SHAPE);
+    expect("step fused stride < conv_dim", sf(F, CI, CO, F, cd - 8, 64, 128, 64, MM_BF16), MM_ERR_SHAPE);
+    expect("step fused d_head 60", sf(F, CI, CO, F, cd, 60, 128, 64, MM_BF16), MM_ERR_UNSUPPORTED);
+    expect("step fused N=96", sf(F, CI, CO, F, cd, 64, 96, 64, MM_BF16), MM_ERR_UNSUPPORTED);
+    expect("step fused d_head 512 N=256", sf(F, CI, CO, F, 512 * 64 + 512, 512, 256, 64, MM_BF16),
+           MM_ERR_UNSUPPORTED);
+    expect("step fused heads 0", sf(F, CI, CO, F, cd, 64, 128, 0, MM_BF16), MM_ERR_SLICE);
+    expect("step fused conv in misaligned",
+           sf(F, reinterpret_cast<const float*>(uintptr_t(0x6000000004ull)), CO, F, cd, 64, 128, 64,
+              MM_BF16), MM_ERR_ALIGN);
+    expect("step fused dtype", sf(F, CI, CO, F, cd, 64, 128, 64, 3), MM_ERR_DTYPE);
+  }
+
   std::printf("%d failure(s)\n", failures);
   return failures == 0 ? 0 : 1;
 }
