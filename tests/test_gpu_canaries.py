@@ -166,3 +166,29 @@ def test_decode_conv_norm_guards():
     out = Guarded(tuple(gy.shape), gy.dtype)
     mm.gated_rmsnorm(gy, gz, gw, 1e-5, d=gy.shape[-1], out=out.t)
     out.check("gated_rmsnorm out")
+
+
+def test_fused_decode_guards():
+    """mm_ssd_step_fused: state, both conv-state buffers (the one read must
+    stay unchanged) and y, at mixed widths including sequences with no active
+    head, over two tokens with the buffers swapped."""
+    d = synth.WORKLOADS["decode"]
+    bsz, H, P, N, cd = 24, d.n_heads, d.d_head, d.d_state, d.conv_dim
+    pool = synth.decode_pool(d, pool=2, batch=bsz)
+    hv = synth.decode_heads(d, batch=bsz)
+    hv[::5] = 0
+    hv = hv.to(DEV)
+    A, D, cw = synth.draw_A(d).to(DEV), synth.draw_D(d).to(DEV), synth.draw_conv_w(d).to(DEV)
+    st = Guarded((bsz, H, P, N), torch.float32, fill=torch.zeros((bsz, H, P, N)))
+    cs = [Guarded((bsz, 3, cd), torch.float32, fill=torch.randn(bsz, 3, cd)),
+          Guarded((bsz, 3, cd), torch.float32, fill=torch.full((bsz, 3, cd), float("nan")))]
+    yt = Guarded((bsz, H, P), torch.float32)
+    for k in range(2):
+        before = cs[k % 2].t.clone()
+        mm.ssd_step_fused(st.t, cs[k % 2].t, cs[(k + 1) % 2].t, pool["xbc_t"][k].to(DEV), cw,
+                          pool["dt_t"][k].to(DEV), A, D, n_heads_active=H, heads_per_seq=hv, y=yt.t)
+        torch.cuda.synchronize()
+        assert torch.equal(cs[k % 2].t, before), "conv_state_in written"
+        assert bool(torch.isfinite(cs[(k + 1) % 2].t).all()), "conv_state_out not fully written"
+    for g, name in ((st, "state"), (cs[0], "conv_state a"), (cs[1], "conv_state b"), (yt, "y")):
+        g.check(name)
