@@ -17,6 +17,9 @@
 // step 110 vs 114 us; nontemporal loads are slower).  A row of the state
 // (d_state floats) is spread over d_state/4 lanes; y's dot product is a
 // butterfly over those lanes.
+// Also here: the same step with the causal conv folded in (one launch per
+// token), the multi-token pass of speculative decoding, and the conv-state
+// advance that commits its accepted tokens.
 #include "device_common.h"
 #include "kernels.h"
 #include "../../include/mm_ssd.h"
