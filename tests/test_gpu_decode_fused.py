@@ -7,6 +7,7 @@ the SSD step in one launch.
 - Against the fp64 oracle's conv step followed by its recurrent step over
   64 tokens, on sequences covering every width class of the decode workload.
 - Sequences with no active head still advance their B and C taps.
+- Replays of a HIP graph of fused tokens equal the eager run.
 """
 from __future__ import annotations
 
@@ -158,3 +159,54 @@ def test_fused_step_64_tokens_against_oracle(dtype):
         act[:int(hv[bb]) * P] = True
         act[w.d_inner:] = True
         assert oracle.rel_l2(gcs[bb][:, act], ocs_t[bb][:, act]) < 1e-6
+
+
+def test_fused_step_in_a_graph_replays():
+    """Four fused tokens captured in a HIP graph (conv-state buffers in
+    turn), replayed three times with eager work between the replays: every
+    replay equals the same four tokens run eagerly from the same start."""
+    w, steps, b = DEC, 4, 48
+    hv = synth.decode_heads(w, batch=b)
+    inp = _inputs(w, steps, torch.float32, b, hv, True, seed=5)
+    say(f"fused decode in a graph: batch={b} steps={steps}")
+    want_y, want_st, want_cs = _fused(w, inp, steps, torch.float32)
+    H, P = w.n_heads, w.d_head
+    st = torch.empty_like(want_st)
+    cs = [torch.empty_like(want_cs), torch.empty_like(want_cs)]
+    ys = [torch.empty((b, H, P), device=DEV) for _ in range(steps)]
+    xbc = [inp["xbc"][k].to(DEV) for k in range(steps)]
+    dts = [inp["dt"][k].to(DEV) for k in range(steps)]
+    hvd = hv.to(DEV)
+    cw, A, D, cb = inp["cw"].to(DEV), inp["A"].to(DEV), inp["D"].to(DEV), inp["cb"].to(DEV)
+
+    def reset():
+        st.copy_(inp["st0"])
+        cs[0].copy_(inp["cs0"])
+        for y in ys:
+            y.fill_(float("nan"))
+
+    def run():
+        for k in range(steps):
+            mm.ssd_step_fused(st, cs[k % 2], cs[(k + 1) % 2], xbc[k], cw, dts[k], A, D, cb,
+                              n_heads_active=H, heads_per_seq=hvd, y=ys[k])
+
+    reset()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in range(steps):
+            assert _same_nan(ys[k], want_y[k]), (rep, k)
+        assert torch.equal(st, want_st), rep
+        assert torch.equal(cs[steps % 2], want_cs), rep
+        _ = (st * 2).sum().item()  # eager work between replays
