@@ -492,22 +492,26 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
   const int t = tb * 16 + r16;  // this lane's token within a tile
 
   Frag8<bf16> cf[kKB];
-  Frag8<bf16> gf[L + 1];
+  // G fragments in two register sets used in turn: tile c+1's are requested
+  // at the start of tile c, a whole tile before its diagonal mask needs them
+  // (requested at the end of tile c they arrived last, and the waves with the
+  // most G blocks waited on them while the other roles idled at the barrier)
+  Frag8<bf16> g0[L + 1], g1[L + 1];
   auto load_c = [&](int c) {
     const auto r = tile_frags(k, b, c);
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
       cf[kb] = as_frag(buffer_load16<kPolicyDefault>(r, frag_off(kC0 + tb * kKB + kb, lane)));
   };
-  auto load_g = [&](int c) {
+  auto load_g = [&](Frag8<bf16> (&g)[L + 1], int c) {
     const auto r = tile_frags(k, b, c);
 #pragma unroll
     for (int q = 0; q <= L; ++q)
-      gf[q] = as_frag(buffer_load16<kPolicyDefault>(r, frag_off(gbase(tb) + q, lane)));
+      g[q] = as_frag(buffer_load16<kPolicyDefault>(r, frag_off(gbase(tb) + q, lane)));
   };
 
   load_c(c0);
-  load_g(c0);
+  load_g(g0, c0);
   // Two stores with an empty range (dropped by the hardware) after the
   // prologue loads, as each tile issues its two y stores after its loads:
   // the compiler's wait at the top of the loop then lets the previous tile's
@@ -517,7 +521,13 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
   __syncthreads();  // decay cumsums and H_prev copy of the first tile
   __syncthreads();  // x copies of the first tile
 
-  for (int c = c0; c < c1; ++c) {
+  // one tile: G fragments of tile c in gf, tile c+1's requested into gn
+  auto tile = [&](const int c, Frag8<bf16> (&gf)[L + 1], Frag8<bf16> (&gn)[L + 1]) {
+    // Prefetches are unconditional (the last tile reloads itself): with a
+    // fixed number of loads per tile the compiler's vmcnt waits stay exact
+    // instead of draining loads that were just issued.
+    const int cn = min(c + 1, c1 - 1);
+    load_g(gn, cn);
     const int len = (int)min((int64_t)kQ, k.seqlen - (int64_t)c * kQ);
     const int64_t r0 = rowb + (int64_t)c * kQ;
     const bf16* Hs = hbuf + (c & 1) * kHF;
@@ -560,10 +570,6 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
       if (kb == 1) mask4(0);
       if (kb == 3) mask4(4);
     }
-    // Prefetches are unconditional (the last tile reloads itself): with a
-    // fixed number of loads per iteration the compiler's vmcnt waits stay
-    // exact instead of draining loads that were just issued.
-    const int cn = min(c + 1, c1 - 1);
     load_c(cn);
 
     // The state's contribution decays from the tile start to the token.
@@ -599,10 +605,9 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
       acc[pb] = mma(xf, m, acc[pb]);
     }
 
-    // The next tile's G fragments are requested before the y stores: the
-    // vmcnt counter retires in order, so a load issued after the stores
-    // would make its wait (early in the next tile) wait for the stores too.
-    load_g(cn);
+    // Every load of the tile is issued before the y stores: the vmcnt
+    // counter retires in order, so a load issued after the stores would make
+    // its wait (early in the next tile) wait for the stores too.
     // y through the wave's LDS rows: lane (r, g) holds chunks g and 4 + g
     // (16 bytes each) of token r; read back, lane (i, j) = (lane / 8, lane % 8)
     // holds chunk j of token 8k + i, so each store instruction writes eight
@@ -628,6 +633,10 @@ __device__ void output_wave(const BK& k, unsigned char* smem, int b, int h, int 
                         (uint32_t)((lane >> 3) * k.ys * (int64_t)sizeof(bf16) + (lane & 7) * 16), v);
     }
     __syncthreads();
+  };
+  for (int c = c0; c < c1; c += 2) {
+    tile(c, g0, g1);
+    if (c + 1 < c1) tile(c + 1, g1, g0);
   }
 }
 
