@@ -40,7 +40,8 @@
 //  - output rows are dealt to the A operand in an order that leaves each lane
 //    eight consecutive channels of a token, stored as one 16-byte write;
 //  - LDS tiles are double-buffered and the decay cumsums triple-buffered, so
-//    each tile costs one workgroup barrier.
+//    each tile costs one workgroup barrier; an output wave's G fragments sit
+//    in two register sets, the next tile's requested a whole tile ahead.
 //  - long sequences with few heads are split into segments: a state-only pass
 //    (one or two heads per workgroup, pieces finer than the segments) forms
 //    each piece's end state from zero, a combine chains them, and the main
