@@ -196,6 +196,37 @@ int mm_ssd_forward(const void* x, int64_t x_row_stride,
                    int64_t n_heads_active, int64_t chunk, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * mm_ssd_forward with the sequences cut as for plan_heads active heads
+ * ("MatMamba", nesting paragraph: every parameter of a sub-block M_i is part
+ * of M_g, so M_i's output should equal the first h_i heads of M_g's).  The
+ * segment plan of a call depends on its active (sequence, head) count, and
+ * a sub-block run alone with a different plan than the full block chains the
+ * states at other seams: equal within rounding, not bit for bit.  Calls with
+ * the same plan_heads (n_heads_active <= plan_heads <= n_heads) cut the
+ * sequences alike.  So a sub-block with plan_heads = the full block's head
+ * count gives exactly the full call's first n_heads_active heads of y and of
+ * final_state, bit for bit, at the cost of the full block's plan at the
+ * narrow width (fewer segments than its own plan would use).
+ *   plan_heads: as above; MM_ERR_SLICE outside [n_heads_active, n_heads].
+ *   workspace: at least mm_ssd_forward_workspace_size(..., n_heads_active =
+ *              plan_heads, ...) bytes, 16-byte aligned.
+ * Every other argument, the layouts, ownership and errors as mm_ssd_forward.
+ */
+int mm_ssd_forward_nested(const void* x, int64_t x_row_stride,
+                          const void* dt, int64_t dt_row_stride,
+                          const float* A,
+                          const void* B, int64_t b_row_stride,
+                          const void* C, int64_t c_row_stride,
+                          const float* D,
+                          void* y, int64_t y_row_stride,
+                          const float* initial_state, float* final_state,
+                          int64_t batch, int64_t seqlen, int64_t n_heads,
+                          int64_t d_head, int64_t d_state, int64_t ngroups,
+                          int64_t n_heads_active, int64_t plan_heads,
+                          int64_t chunk, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Size of the device array mm_ssd_forward_noalloc takes its workspace from. */
 #define MM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 

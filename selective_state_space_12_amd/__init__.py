@@ -75,6 +75,11 @@ def lib() -> ctypes.CDLL:
                                          _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                          _i64, _i64, _i64, _int, _vp, ctypes.c_size_t, _vp]
             L.mm_ssd_forward.restype = _int
+            L.mm_ssd_forward_nested.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64,
+                                                _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64,
+                                                _i64, _i64, _i64, _i64, _i64, _int, _vp,
+                                                ctypes.c_size_t, _vp]
+            L.mm_ssd_forward_nested.restype = _int
             L.mm_ssd_forward_noalloc.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64,
                                                  _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64,
                                                  _i64, _i64, _i64, _i64, _int, _vp]
@@ -256,7 +261,8 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
                 initial_state: Optional[torch.Tensor] = None,
                 final_state: Optional[torch.Tensor] = None,
                 y: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                workspace: Optional[torch.Tensor] = None,
+                plan_heads: Optional[int] = None) -> torch.Tensor:
     """Chunked selective scan over heads [0, n_heads_active).
 
     x (batch, seqlen, n_heads, d_head), dt (batch, seqlen, n_heads),
@@ -265,7 +271,9 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
     Returns y: the given buffer (batch, seqlen, n_heads, d_head) with the
     active prefix written, or a new (batch, seqlen, n_heads_active, d_head)
     tensor.  final_state (batch, n_heads, d_head, d_state) fp32, if given, is
-    written for the active heads."""
+    written for the active heads.  plan_heads (mm_ssd_forward_nested): cut
+    the sequences as for that many active heads, so that calls with the same
+    plan_heads agree bit for bit on their common heads."""
     batch, seqlen, n_heads, d_head = x.shape
     if B.dim() == 3:
         B = B.unsqueeze(2)
@@ -286,16 +294,25 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
     for name, t in (("A", A), ("D", D), ("initial_state", initial_state), ("final_state", final_state)):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous fp32 tensor")
-    need = ssd_forward_workspace_size(batch, seqlen, n_heads, d_head, d_state, ngroups, h_act,
-                                      chunk, x.dtype)
+    need = ssd_forward_workspace_size(batch, seqlen, n_heads, d_head, d_state, ngroups,
+                                      h_act if plan_heads is None else int(plan_heads), chunk,
+                                      x.dtype)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().mm_ssd_forward(_ptr(x), xs, _ptr(dt), dts, _ptr(A), _ptr(B), bs, _ptr(C), cs,
-                              _ptr(D), _ptr(y), ys, _ptr(initial_state), _ptr(final_state),
-                              batch, seqlen, n_heads, d_head, d_state, ngroups, h_act, chunk,
-                              code, _ptr(workspace), wbytes, _stream())
-    _check("mm_ssd_forward", st)
+    if plan_heads is None:
+        st = lib().mm_ssd_forward(_ptr(x), xs, _ptr(dt), dts, _ptr(A), _ptr(B), bs, _ptr(C), cs,
+                                  _ptr(D), _ptr(y), ys, _ptr(initial_state), _ptr(final_state),
+                                  batch, seqlen, n_heads, d_head, d_state, ngroups, h_act, chunk,
+                                  code, _ptr(workspace), wbytes, _stream())
+        _check("mm_ssd_forward", st)
+    else:
+        st = lib().mm_ssd_forward_nested(_ptr(x), xs, _ptr(dt), dts, _ptr(A), _ptr(B), bs, _ptr(C),
+                                         cs, _ptr(D), _ptr(y), ys, _ptr(initial_state),
+                                         _ptr(final_state), batch, seqlen, n_heads, d_head, d_state,
+                                         ngroups, h_act, int(plan_heads), chunk, code,
+                                         _ptr(workspace), wbytes, _stream())
+        _check("mm_ssd_forward_nested", st)
     return y
 
 

@@ -152,6 +152,9 @@ struct FwdArgs {
   int n_heads, d_head, d_state, heads;  // heads: active heads (the widest sequence's, if mixed)
   int chunk;
   const int32_t* heads_per_seq = nullptr;  // host array (batch entries) for a mixed call
+  // heads the segment plan is chosen for (>= heads; 0: heads).  Calls planned
+  // for the same count cut the sequences alike, whatever their active heads.
+  int plan_heads = 0;
 };
 
 // The unit map of a call (mixed when a.heads_per_seq is set).

@@ -648,8 +648,8 @@ hipError_t launch_shape(const FwdArgs& a, void* ws, hipStream_t s) {
   k.y = a.y; k.ys = a.ys; k.h0 = a.h0; k.hT = a.hT;
   k.seqlen = a.seqlen; k.n_heads = a.n_heads; k.heads = a.heads;
   k.um = make_unit_map(a);
-  fwd_plan(a.batch, a.seqlen, a.heads, Q, &k.nchunks, &k.nseg, &k.seg_chunks,
-           k.um.mixed ? k.um.units : 0);
+  fwd_plan(a.batch, a.seqlen, a.plan_heads > 0 ? a.plan_heads : a.heads, Q, &k.nchunks, &k.nseg,
+           &k.seg_chunks, k.um.mixed ? k.um.units : 0);
   k.seg_state = nullptr;
   k.seg_decay = nullptr;
   if (k.nseg > 1) {

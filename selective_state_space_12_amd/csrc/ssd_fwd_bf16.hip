@@ -1417,7 +1417,8 @@ hipError_t launch_bf16(const FwdArgs& a, const FuseArgs& fu, void* ws, hipStream
   k.cw = fu.w; k.cbias = fu.bias; k.cstate = fu.state; k.conv_dim = fu.conv_dim;
   k.seqlen = a.seqlen; k.n_heads = a.n_heads; k.heads = a.heads;
   k.um = make_unit_map(a);
-  const Bf16Plan pl = plan_bf16(a.batch, a.seqlen, a.heads, k.um.mixed ? k.um.units : 0,
+  const Bf16Plan pl = plan_bf16(a.batch, a.seqlen, a.plan_heads > 0 ? a.plan_heads : a.heads,
+                                k.um.mixed ? k.um.units : 0,
                                 !FUSED && !k.um.mixed);
   k.ntiles = pl.ntiles;
   k.nseg = pl.nseg;

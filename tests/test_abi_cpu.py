@@ -141,6 +141,35 @@ def test_entry_points_reject_before_enqueueing(lib):
     assert call(a5=P + 8) == -6         # B misaligned
 
 
+@pytest.mark.skipif(not _no_gpu(), reason="fake device pointers are only passed where no GPU exists")
+def test_nested_forward_rejects_before_enqueueing(lib):
+    """mm_ssd_forward_nested: a plan head count outside [n_heads_active,
+    n_heads] and a workspace sized for the active heads instead of the plan's
+    are refused before any launch."""
+    P = 0x100000
+    i64 = ctypes.c_int64
+    fn = lib.mm_ssd_forward_nested
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, i64, ctypes.c_void_p, i64, ctypes.c_void_p, ctypes.c_void_p, i64,
+                   ctypes.c_void_p, i64, ctypes.c_void_p, ctypes.c_void_p, i64, ctypes.c_void_p,
+                   ctypes.c_void_p, i64, i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    # 1.4B shape, bf16, 8 active heads planned as 64
+    args = [P, 4096, P, 64, P, P, 128, P, 128, None, P, 4096, None, None,
+            4, 8192, 64, 64, 128, 1, 8, 64, 256, 1, P, 1 << 34, None]
+    assert fn(*args[:21], 7, *args[22:]) == -3        # plan below the active heads
+    assert fn(*args[:21], 65, *args[22:]) == -3       # plan beyond n_heads
+    q = ctypes.c_size_t(0)
+    lib.mm_ssd_forward_workspace_size.restype = ctypes.c_int
+    lib.mm_ssd_forward_workspace_size.argtypes = [i64] * 8 + [ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    assert lib.mm_ssd_forward_workspace_size(4, 8192, 64, 64, 128, 1, 8, 256, 1, ctypes.byref(q)) == 0
+    own = q.value
+    assert lib.mm_ssd_forward_workspace_size(4, 8192, 64, 64, 128, 1, 64, 256, 1, ctypes.byref(q)) == 0
+    planned = q.value
+    if own < planned:  # the 8-head call's own workspace does not cover the 64-head plan
+        assert fn(*args[:25], own, None) == -7
+
+
 def test_validation_cases_under_sanitizers(tmp_path):
     src = os.path.join(ROOT, "tests", "native", "validate_cases.cpp")
     val = os.path.join(ROOT, "selective_state_space_12_amd", "csrc", "validate.cpp")

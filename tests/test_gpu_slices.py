@@ -118,6 +118,38 @@ def test_nesting_across_different_segment_plans(w, b, l, hs):
         assert_tiles(f64(got[:, :, sample]), yr, BF)
 
 
+TINY = synth.WORKLOADS["tiny"]
+
+
+@pytest.mark.parametrize("w,b,l,hs", [(B14, 4, 8192, (8, 64)), (M130, 8, 2048, (3, 24)),
+                                      (LONG, 1, 32768, (8, 32)), (TINY, 1, 8192, (1, 4))])
+def test_nested_plan_gives_the_full_blocks_heads_bit_for_bit(w, b, l, hs):
+    """mm_ssd_forward_nested: the sub-block planned for the full block's head
+    count returns exactly the full call's first h_i heads of y and of the
+    final state, although its own plan would cut the sequences differently
+    (MatMamba page, nesting paragraph).  bf16 fast path and the fp32 general
+    path (tiny)."""
+    h_small, h_full = hs
+    assert _segments(w, b, l, h_small) != _segments(w, b, l, h_full)
+    inp = synth.forward_inputs(w, batch=b, seqlen=l, with_state=True, salt=13)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    H, P, N = w.n_heads, w.d_head, w.d_state
+    say(f"nested plan {w.name} b={b} l={l}: heads {h_small} planned as {h_full}")
+    outs = []
+    for h, plan in ((h_full, None), (h_small, h_full)):
+        y = torch.full((b, l, H, P), float("nan"), dtype=w.dtype, device=DEV)
+        hT = torch.full((b, H, P, N), float("nan"), device=DEV)
+        mm.ssd_forward(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"],
+                       n_heads_active=h, chunk=w.chunk, initial_state=dev["h0"], final_state=hT,
+                       y=y, plan_heads=plan)
+        torch.cuda.synchronize()
+        outs.append((y, hT))
+    (yf, hf), (ys, hs_) = outs
+    assert torch.equal(ys[:, :, :h_small], yf[:, :, :h_small])
+    assert torch.equal(hs_[:, :h_small], hf[:, :h_small])
+    assert torch.isnan(ys[:, :, h_small:].float()).all()  # heads past the slice untouched
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_decode_64_steps_every_width_class(dtype):
     """Decode over 64 steps (conv step + scan step per token) for 24
