@@ -48,7 +48,7 @@
 //    tiles) and phase 2 the causal products into the same accumulators, with
 //    dx written and dB, dC added to their sums over the heads in registers.
 //    Products that need a tile's transpose read its columns with LDS
-//    transpose loads.  A wave without a Q x Q block forms the previous head's
+//    transpose loads.  Wave kTailWave forms the previous head's
 //    dLambda, ddt, dA and dD during phase 1 and leaves them in LDS.
 //  - dB and dC (sums over the heads) are written once per chunk, no atomics;
 //    ddt once per chunk for all its heads; dA and dD (sums over the sequences
@@ -69,6 +69,7 @@ constexpr int kBWaves = 8;  // state walks
 constexpr int kBThreads = kBWaves * 64;
 constexpr int kCWaves = 16;  // chunk walk
 constexpr int kCThreads = kCWaves * 64;
+constexpr int kTailWave = 2;  // runs each head's dLambda / ddt / dA / dD tail
 constexpr int kXcds = 8;
 
 struct BwdK {
@@ -1027,8 +1028,11 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
     load_head(min(hh + 1, hend - 1), tid, lane);
 
     // ================= phase 1 =================
-    // the previous head's tail, on a wave without a Q x Q block
-    if (wave == kCWaves - 1 && hh > k.h0g) run_tail(hh - 1, lane);
+    // the previous head's tail on wave kTailWave: its Q x Q block leaves it
+    // the most slack before the phase-1 barrier (a barrier-wait probe: waves
+    // 0-3 waited ~20% of the loop there, and the tail on the last wave, whose
+    // tiles fill phase 1, made that wave the one every other waited for)
+    if (wave == kTailWave && hh > k.h0g) run_tail(hh - 1, lane);
     // ---- the wave's Q x Q block: x_s . dy_t, masked decay, M, K, Kd, W sums ----
     if (wave < NQQ) {
       f32x4 qq = {0, 0, 0, 0};
@@ -1218,7 +1222,7 @@ __global__ __launch_bounds__(kCThreads) void bwd_chunk_kernel(BwdK k) {
     // they are rewritten two heads later)
   }
 
-  if (wave == kCWaves - 1) run_tail(hend - 1, opaque(lane));
+  if (wave == kTailWave) run_tail(hend - 1, opaque(lane));
   __syncthreads();
   // ---- ddt of the launch's heads (64 consecutive heads of a token per wave,
   // rows past len and heads past hg dropped), then dA and dD, one head per
